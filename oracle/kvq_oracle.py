@@ -1,0 +1,294 @@
+"""fp64 CPU oracle for rotation-based 2-bit KV-cache quantization with fused
+decode attention (the OmniKVQuant method).
+
+TEST INFRASTRUCTURE.  Only the tests, the smoke check and the benchmark's CPU
+baseline leg may import this module.  The library's product path never calls
+it, and it shares no code, constant or helper with the HIP path.
+
+Sources (the OmniKVQuant page, paperlayer.ai summary of arXiv 2609.11582):
+  * Sec. 2 Method, "TurboQuant" bullet: rotate toward Gaussian-like
+    coordinates with a randomized Hadamard transform, separate magnitude from
+    direction, quantize rotated coordinates with a fixed codebook, reconstruct.
+  * Sec. 2 Method, first "OmniKVQuant" bullet: min-max scale rotated keys in
+    short consecutive-token groups, store the group statistics, apply the
+    shared fixed codebook; the statistics restore the range on reconstruction;
+    the Hadamard basis is kept.
+  * Sec. 2 Method, second "OmniKVQuant" bullet: a value rotation per modality;
+    reconstructed values use their modality's rotation.
+  * Sec. 1 Introduction, "Implementation" bullet: decode unpacks the 2-bit
+    cache inside attention, rotates one query per head, and applies the inverse
+    value rotations once, after aggregation.
+
+Everything is float64.  Inputs are exact float64 images of the fp32/bf16
+data.  Stored statistics (key min/max, value norms) are rounded once to fp16
+with round-to-nearest-even (numpy's direct double->half conversion).
+
+Readings where the pages are silent (each repeated in the design notes):
+  * Hadamard: Sylvester natural order, signs applied first,
+    y = (1/sqrt(d)) * H_d (s * x); the 1/sqrt(d) is one fp64 multiply after
+    the unnormalised transform.
+  * Key statistics are per (32-token group, rotated channel): lo/hi = min/max
+    over the group's present tokens, stored as fp16.
+  * The group range [LO, HI] maps affinely onto [c0, c3]; a value's code is
+    the number of decision thresholds (midpoints of adjacent levels) it
+    reaches (ties go up); HI == LO gives code 0.
+  * Values: n = ||v||, r = R_m^T v, z = sqrt(d) * r / n, nearest level; the
+    stored norm is fp16(n); reconstruction is R_m (N / sqrt(d)) c[code].
+  * Query head i uses KV head floor(i / G); scores use scale 1/sqrt(d) unless
+    given; an empty context attends to nothing and yields zeros.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+GROUP_TOKENS = 32
+N_MODALITIES = 3
+
+
+# ------------------------------------------------------------------ inputs
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact float64 value of bfloat16 data given as raw uint16 bits."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
+
+
+def as_f64(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return bf16_to_f64(x)
+    return np.asarray(x, dtype=np.float32).astype(np.float64)
+
+
+# ------------------------------------------------------- Hadamard rotation
+
+def walsh_hadamard(x: np.ndarray) -> np.ndarray:
+    """Unnormalised Walsh-Hadamard transform along the last axis (Sylvester
+    natural order: H_1 = [1], H_2n = [[H, H], [H, -H]]), by butterflies."""
+    x = np.array(x, dtype=np.float64, copy=True)
+    d = x.shape[-1]
+    if d & (d - 1):
+        raise ValueError("head dimension must be a power of two")
+    lead = x.shape[:-1]
+    h = 1
+    while h < d:
+        y = x.reshape(lead + (d // (2 * h), 2, h))
+        a = y[..., 0, :].copy()
+        b = y[..., 1, :].copy()
+        y[..., 0, :] = a + b
+        y[..., 1, :] = a - b
+        x = y.reshape(lead + (d,))
+        h *= 2
+    return x
+
+
+def randomized_hadamard(x: np.ndarray, signs: np.ndarray) -> np.ndarray:
+    """y = (1/sqrt(d)) H_d (s * x) over the last axis: the randomized Hadamard
+    rotation (Method, TurboQuant bullet; kept for keys by OmniKVQuant)."""
+    d = x.shape[-1]
+    return walsh_hadamard(np.asarray(x, np.float64) * np.asarray(signs, np.float64)) * (1.0 / np.sqrt(d))
+
+
+def inverse_randomized_hadamard(y: np.ndarray, signs: np.ndarray) -> np.ndarray:
+    """x = s * (1/sqrt(d)) H_d y (H_d is symmetric and H_d H_d = d I)."""
+    d = y.shape[-1]
+    return walsh_hadamard(y) * (1.0 / np.sqrt(d)) * np.asarray(signs, np.float64)
+
+
+# ------------------------------------------------------------------ codebook
+
+def decision_thresholds(codebook: np.ndarray) -> np.ndarray:
+    """Midpoints between adjacent levels, in fp64 from the fp32 levels."""
+    c = np.asarray(codebook, dtype=np.float32).astype(np.float64)
+    return (c[:-1] + c[1:]) / 2.0
+
+
+def nearest_level(z: np.ndarray, codebook: np.ndarray) -> np.ndarray:
+    """Index of the nearest codebook level: the number of thresholds z reaches
+    (a value exactly on a threshold takes the upper level)."""
+    b = decision_thresholds(codebook)
+    return (np.asarray(z)[..., None] >= b).sum(axis=-1).astype(np.uint8)
+
+
+# ------------------------------------------------------------------- keys
+
+def quantize_keys(k: np.ndarray, signs: np.ndarray, codebook: np.ndarray,
+                  group: int = GROUP_TOKENS):
+    """Quantize one KV head's keys.
+
+    k: [L, d] float64 raw keys.  Returns codes [L, d] uint8, lo/hi
+    [ceil(L/group), d] float16 (the stored group statistics).
+    Method, OmniKVQuant key bullet: rotate, min-max scale within short
+    consecutive-token groups, store the statistics, apply the fixed codebook.
+    """
+    y = randomized_hadamard(k, signs)
+    L, d = y.shape
+    ng = -(-L // group)
+    c = np.asarray(codebook, np.float32).astype(np.float64)
+    c0, c3 = c[0], c[-1]
+    codes = np.zeros((L, d), np.uint8)
+    lo16 = np.zeros((ng, d), np.float16)
+    hi16 = np.zeros((ng, d), np.float16)
+    for g in range(ng):
+        yg = y[g * group:(g + 1) * group]
+        lo16[g] = yg.min(axis=0).astype(np.float16)
+        hi16[g] = yg.max(axis=0).astype(np.float16)
+        LO = lo16[g].astype(np.float64)
+        HI = hi16[g].astype(np.float64)
+        span = HI - LO
+        ok = span > 0
+        z = np.zeros_like(yg)
+        z[:, ok] = c0 + (yg[:, ok] - LO[ok]) * (c3 - c0) / span[ok]
+        cg = nearest_level(z, codebook)
+        cg[:, ~ok] = 0
+        codes[g * group:(g + 1) * group] = cg
+    return codes, lo16, hi16
+
+
+def key_normalized_values(k: np.ndarray, signs: np.ndarray, lo16: np.ndarray,
+                          hi16: np.ndarray, codebook: np.ndarray,
+                          group: int = GROUP_TOKENS) -> np.ndarray:
+    """The fp64 value z each key element's code is decided on (NaN where the
+    group range is empty).  Used to find elements near a decision threshold."""
+    y = randomized_hadamard(k, signs)
+    c = np.asarray(codebook, np.float32).astype(np.float64)
+    c0, c3 = c[0], c[-1]
+    gi = np.arange(y.shape[0]) // group
+    LO = lo16.astype(np.float64)[gi]
+    HI = hi16.astype(np.float64)[gi]
+    span = HI - LO
+    with np.errstate(divide="ignore", invalid="ignore"):
+        z = c0 + (y - LO) * (c3 - c0) / span
+    z[span == 0] = np.nan
+    return z
+
+
+def dequantize_keys(codes: np.ndarray, lo16: np.ndarray, hi16: np.ndarray,
+                    codebook: np.ndarray, group: int = GROUP_TOKENS) -> np.ndarray:
+    """Rotated-domain key reconstruction k_hat = LO + (c[code]-c0)(HI-LO)/(c3-c0):
+    code 0 gives LO and code 3 gives HI, restoring the group's range."""
+    c = np.asarray(codebook, np.float32).astype(np.float64)
+    gi = np.arange(codes.shape[0]) // group
+    LO = lo16.astype(np.float64)[gi]
+    HI = hi16.astype(np.float64)[gi]
+    return LO + (c[codes] - c[0]) * (HI - LO) / (c[-1] - c[0])
+
+
+# ------------------------------------------------------------------ values
+
+def quantize_values(v: np.ndarray, modality: np.ndarray, rot: np.ndarray,
+                    codebook: np.ndarray):
+    """Quantize one KV head's values with per-modality rotations.
+
+    v: [L, d] float64; modality: [L] in {0,1,2}; rot: [3, d, d] (R_m, columns
+    form the basis).  Returns codes [L, d] uint8 and norms [L] float16.
+    Method, TurboQuant bullet (magnitude/direction split, fixed codebook on
+    rotated coordinates) with the rotation replaced by the modality's R_m
+    (OmniKVQuant value bullet).
+    """
+    L, d = v.shape
+    R = np.asarray(rot, np.float32).astype(np.float64)
+    n = np.sqrt(np.sum(v * v, axis=1))
+    norms = n.astype(np.float16)
+    r = np.zeros_like(v)
+    for m in range(N_MODALITIES):
+        idx = modality == m
+        if idx.any():
+            r[idx] = v[idx] @ R[m]          # r_j = sum_i R_ij v_i, i.e. R_m^T v
+    codes = np.zeros((L, d), np.uint8)
+    ok = n > 0
+    z = np.sqrt(d) * r[ok] / n[ok][:, None]
+    codes[ok] = nearest_level(z, codebook)
+    return codes, norms
+
+
+def value_normalized_values(v: np.ndarray, modality: np.ndarray, rot: np.ndarray) -> np.ndarray:
+    """The fp64 value z each value element's code is decided on (NaN for n == 0)."""
+    L, d = v.shape
+    R = np.asarray(rot, np.float32).astype(np.float64)
+    n = np.sqrt(np.sum(v * v, axis=1))
+    r = np.zeros_like(v)
+    for m in range(N_MODALITIES):
+        idx = modality == m
+        if idx.any():
+            r[idx] = v[idx] @ R[m]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        z = np.sqrt(d) * r / n[:, None]
+    z[n == 0] = np.nan
+    return z
+
+
+def dequantize_values_rotated(codes: np.ndarray, norms16: np.ndarray,
+                              codebook: np.ndarray) -> np.ndarray:
+    """v_tilde = (N / sqrt(d)) c[code], still in the modality's rotated frame."""
+    d = codes.shape[1]
+    c = np.asarray(codebook, np.float32).astype(np.float64)
+    return (norms16.astype(np.float64) / np.sqrt(d))[:, None] * c[codes]
+
+
+# ------------------------------------------------------------------- decode
+
+def rotate_query(q: np.ndarray, signs: np.ndarray, n_kv_heads: int) -> np.ndarray:
+    """q: [Hq, d] float64 -> q_rot [Hq, d]: each query rotated once with the
+    Hadamard signs of its KV head (Introduction, Implementation bullet)."""
+    hq = q.shape[0]
+    g = hq // n_kv_heads
+    out = np.empty_like(np.asarray(q, np.float64))
+    for i in range(hq):
+        out[i] = randomized_hadamard(q[i], signs[i // g])
+    return out
+
+
+def decode_attention_head(q_rot: np.ndarray, k_codes, lo16, hi16, v_codes, norms16,
+                          modality, rot, codebook, scale: float) -> np.ndarray:
+    """One query head over one KV head's packed cache, in the rotated domain.
+
+    scores s_t = scale * <q_rot, k_hat_t>; p = softmax(s) over all cached
+    positions; A_m = sum over modality-m positions of p_t v_tilde_t; output
+    o = sum_m R_m A_m (the inverse value rotation applied once per modality,
+    after aggregation)."""
+    L = k_codes.shape[0]
+    d = q_rot.shape[-1]
+    if L == 0:
+        return np.zeros(d)
+    k_hat = dequantize_keys(k_codes, lo16, hi16, codebook)
+    s = scale * (k_hat @ q_rot)
+    p = np.exp(s - s.max())
+    p = p / p.sum()
+    v_t = dequantize_values_rotated(v_codes, norms16, codebook)
+    R = np.asarray(rot, np.float32).astype(np.float64)
+    o = np.zeros(d)
+    for m in range(N_MODALITIES):
+        idx = modality == m
+        if idx.any():
+            o += R[m] @ (p[idx] @ v_t[idx])
+    return o
+
+
+def decode_attention(q_rot: np.ndarray, caches: list, rot: np.ndarray, codebook,
+                     scale: float) -> np.ndarray:
+    """q_rot: [Hq, d]; caches: per KV head dicts with k_codes, lo, hi, v_codes,
+    norms and the shared modality; rot: [Hkv, 3, d, d].  Returns [Hq, d]."""
+    hq, d = q_rot.shape
+    hkv = len(caches)
+    g = hq // hkv
+    out = np.zeros((hq, d))
+    for i in range(hq):
+        c = caches[i // g]
+        out[i] = decode_attention_head(q_rot[i], c["k_codes"], c["lo"], c["hi"],
+                                       c["v_codes"], c["norms"], c["modality"],
+                                       rot[i // g], codebook, scale)
+    return out
+
+
+# --------------------------------------------------------- whole sessions
+
+def quantize_session(k: np.ndarray, v: np.ndarray, modality: np.ndarray,
+                     signs: np.ndarray, rot: np.ndarray, codebook) -> list:
+    """k, v: [L, Hkv, d] float64 -> per KV head packed-cache dicts (logical layout)."""
+    hkv = k.shape[1]
+    out = []
+    for h in range(hkv):
+        kc, lo, hi = quantize_keys(k[:, h], signs[h], codebook)
+        vc, nrm = quantize_values(v[:, h], modality, rot[h], codebook)
+        out.append(dict(k_codes=kc, lo=lo, hi=hi, v_codes=vc, norms=nrm, modality=modality))
+    return out
