@@ -1,0 +1,244 @@
+"""Benchmark: fused 2-bit decode attention on the packed KV cache at 80K context.
+
+One step = one decode step of one attention layer on the seeded synthetic
+omni stream (81,920 cached positions, 28 query / 4 KV heads, d = 128, bf16
+input): quantize-append the step's new key/value, rotate the query, and run
+the fused decode over the packed cache.  Steps cycle over R layer replicas
+(R x 27.8 MB > the 256 MB Infinity Cache) so that the cache is read from HBM.
+
+Prints one JSON line (rank 0).  `value` = KV positions attended per second
+(context length / time per step, inputs resident in HBM).  `roofline` is for
+the decode launch (partition + merge kernels), timed with HIP events on the
+stream it runs on.  `cpu_baseline` is the fp64 oracle decoding the same
+packed cache on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def algorithmic_decode_bytes(L: int, d: int, hq: int, hkv: int) -> int:
+    """Bytes one decode must move: per (position, KV head) the key codes
+    (d/4), value codes (d/4), key group statistics (2 d fp16 per 32
+    positions) and the value norm (fp16); one modality byte per position;
+    the value bases (3 d^2 fp32 per KV head); the rotated query and output."""
+    per_pos_head = d // 4 + d // 4 + (2 * d * 2) // 32 + 2
+    return L * hkv * per_pos_head + L + hkv * 3 * d * d * 4 + 2 * hq * d * 4
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--replicas", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the decode shards by KV head with no exchange; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import decode_attention_kvq_amd as K
+    from omnistream import generate
+    from tests import kvq_harness as H
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    L0 = 81920
+    extra = args.steps // args.replicas + args.warmup // args.replicas + 4
+    w = generate(2, length=L0 + extra)
+    c = w.cfg
+    d, hq, hkv = c.head_dim, c.n_q_heads, c.n_kv_heads
+    pt = w.page_tokens
+    max_pages = -(-(L0 + extra) // pt)
+    table = np.arange(max_pages, dtype=np.int32)[None, :]
+    cfg, params, cache0 = H.build(w, page_table=table, upto=[L0])
+    torch.cuda.synchronize()
+
+    # Layer replicas: identical packed caches in separate buffers.
+    caches = [cache0]
+    for _ in range(args.replicas - 1):
+        cc = K.Cache(cfg, torch.from_numpy(table), device=dev)
+        for name in ("k_codes", "k_stats", "v_codes", "v_norms", "modality", "k_tail", "seq_len"):
+            getattr(cc, name).copy_(getattr(cache0, name))
+        cc.set_lengths(cache0.lengths())
+        caches.append(cc)
+    torch.cuda.synchronize()
+
+    k_steps = H._kv_tensor(w.k[0][None, L0:L0 + extra], "bf16", dev)     # [1, extra, Hkv, d]
+    v_steps = H._kv_tensor(w.v[0][None, L0:L0 + extra], "bf16", dev)
+    m_steps = torch.from_numpy(np.ascontiguousarray(w.modality[0][None, L0:L0 + extra])).to(dev)
+    q = H.query_tensor(w, dev)
+    q_rot = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    ws = torch.empty(K.kvq_decode_workspace_bytes(cfg, L0 + extra), dtype=torch.uint8, device=dev)
+    scale = 1.0 / math.sqrt(d)
+
+    def one_step(r, j):
+        cache = caches[r]
+        K.kvq_quantize_append(cfg, cache, params, k_steps[:, j:j + 1], v_steps[:, j:j + 1], m_steps[:, j:j + 1])
+        K.kvq_rotate_query(cfg, params, q, q_rot)
+        K.kvq_decode_attention(cfg, cache, params, q_rot, scale, out, ws)
+
+    # Eager warm-up (also loads every kernel), then rewind the lengths.
+    for r in range(args.replicas):
+        one_step(r, 0)
+    torch.cuda.synchronize()
+    for cc in caches:
+        cc.set_lengths([L0])
+    torch.cuda.synchronize()
+
+    # One graph = one decode step on each of the R layer replicas.  Replays
+    # append the same new token again at the (device-side) current length, so
+    # every replay is a full decode step on a cache of L0 + replay positions.
+    g_step = torch.cuda.CUDAGraph()
+    s_cap = torch.cuda.Stream()
+    s_cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s_cap):
+        with torch.cuda.graph(g_step, stream=s_cap):
+            for r in range(args.replicas):
+                one_step(r, 0)
+    torch.cuda.synchronize()
+    for cc in caches:                       # capture advanced the host mirror only
+        cc.set_lengths([L0])
+    torch.cuda.synchronize()
+
+    g_dec = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s_cap):
+        with torch.cuda.graph(g_dec, stream=s_cap):
+            for r in range(args.replicas):
+                K.kvq_decode_attention(cfg, caches[r], params, q_rot, scale, out, ws)
+    torch.cuda.synchronize()
+
+    n_rep = max(1, args.steps // args.replicas)
+    n_warm = max(1, args.warmup // args.replicas)
+    stream = torch.cuda.current_stream()
+    for _ in range(n_warm):
+        g_step.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(n_rep):
+        g_step.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    steps = n_rep * args.replicas
+    ms_step = e0.elapsed_time(e1) / steps
+    lens = [int(x) for cc in caches for x in cc.seq_len.cpu().tolist()]
+    for cc, n in zip(caches, lens):
+        cc.set_lengths([n])
+    ctx_mean = float(np.mean(lens)) - (n_rep - 1) / 2.0      # mean context over the timed steps
+
+    # Decode launches alone: R back-to-back decodes per replay, HIP events on the stream.
+    for _ in range(2):
+        g_dec.replay()
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n_dec = max(5, (2 * args.steps) // args.replicas)
+    d0.record(stream)
+    for _ in range(n_dec):
+        g_dec.replay()
+    d1.record(stream)
+    torch.cuda.synchronize()
+    dec_ms = d0.elapsed_time(d1) / (n_dec * args.replicas)
+    Ld = int(np.mean(lens))
+    dec_bytes = algorithmic_decode_bytes(Ld, d, hq, hkv)
+    achieved = dec_bytes / (dec_ms * 1e-3) / 1e9
+
+    # Warm (Infinity-Cache resident) decode for context: one replica repeatedly.
+    g_warm = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s_cap):
+        with torch.cuda.graph(g_warm, stream=s_cap):
+            for _ in range(args.replicas):
+                K.kvq_decode_attention(cfg, caches[0], params, q_rot, scale, out, ws)
+    g_warm.replay()
+    ew0, ew1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ew0.record(stream)
+    for _ in range(10):
+        g_warm.replay()
+    ew1.record(stream)
+    torch.cuda.synchronize()
+    warm_ms = ew0.elapsed_time(ew1) / (10 * args.replicas)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, cfg, caches[0], args.cpu_seconds)
+
+    rec = {
+        "metric": "fused 2-bit decode attention: KV tokens/s + HBM GB/s (% peak) at 80K ctx",
+        "value": ctx_mean / (ms_step * 1e-3),
+        "unit": "KV tokens/s",
+        "n_gpus": 1, "steps": steps, "warmup": n_warm * args.replicas,
+        "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32 accumulate over 2-bit codes (bf16 input)",
+        "data": "synthetic seeded omni stream (video/audio/text chunks), random bases",
+        "config": {"workload": "decode step at 81,920-position context: append 1 token + rotate q + fused decode",
+                   "context": int(ctx_mean), "head_dim": d, "q_heads": hq, "kv_heads": hkv,
+                   "batch": 1, "layer_replicas": args.replicas, "page_tokens": pt},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "decode (partition + merge)", "bytes_per_launch": dec_bytes,
+                     "avg_launch_us": dec_ms * 1e3},
+        "cpu_baseline": cpu,
+        "extra": {"decode_us_hbm": dec_ms * 1e3, "decode_us_warm": warm_ms * 1e3,
+                  "decode_kv_tokens_per_s": Ld / (dec_ms * 1e-3),
+                  "step_wall_us": wall / steps * 1e6},
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(w, cfg, cache, budget_s: float) -> dict:
+    """The fp64 oracle (as it stands) decoding the same packed cache on the
+    host: rotate the queries, dequantize, attend, rotate back.  Sample: as many
+    KV heads of the 80K-position step as fit in the time budget."""
+    from threadpoolctl import threadpool_limits
+
+    from decode_attention_kvq_amd.layout import session_view
+    from oracle import kvq_oracle as O
+
+    host = cache.host_arrays()
+    n = int(host["seq_len"][0])
+    q64 = O.as_f64(w.q, w.dtype)[0]
+    q_rot = O.rotate_query(q64, w.signs, cfg.n_kv_heads)
+    g = cfg.n_q_heads // cfg.n_kv_heads
+    done_heads = 0
+    t_total = 0.0
+    with threadpool_limits(limits=1):
+        for h in range(cfg.n_kv_heads):
+            view = session_view(host, cfg, 0, n, h)
+            t = time.perf_counter()
+            for i in range(h * g, (h + 1) * g):
+                O.decode_attention_head(q_rot[i], view["k_codes"], view["lo"], view["hi"], view["v_codes"],
+                                        view["norms"], view["modality"], w.rot[h], w.codebook,
+                                        1.0 / math.sqrt(cfg.head_dim))
+            t_total += time.perf_counter() - t
+            done_heads += 1
+            if t_total > budget_s:
+                break
+    t_step = t_total * cfg.n_kv_heads / done_heads
+    return {"value": n / t_step, "unit": "KV tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"fp64 oracle decode of {done_heads}/{cfg.n_kv_heads} KV heads "
+                      f"({done_heads * g} query heads) over {n} positions, scaled to all heads; "
+                      f"{t_total:.1f} s on 1 thread"}
+
+
+if __name__ == "__main__":
+    main()

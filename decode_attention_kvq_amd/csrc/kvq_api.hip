@@ -1,0 +1,224 @@
+// Host side of the C ABI: argument validation, partition planning and kernel
+// dispatch.  Nothing here allocates device memory or synchronises.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "kvq_internal.h"
+
+namespace {
+
+using kvq::kGroupTokens;
+using kvq::kMaxGroupHeads;
+
+bool codebook_ok(const float c[4]) {
+  for (int k = 0; k < 4; ++k)
+    if (!isfinite(c[k])) return false;
+  return c[0] < c[1] && c[1] < c[2] && c[2] < c[3];
+}
+
+kvq_status check_config(const kvq_config* cfg) {
+  if (!cfg) return KVQ_ERR_INVALID;
+  if (cfg->head_dim != 64 && cfg->head_dim != 128) return KVQ_ERR_UNSUPPORTED;
+  if (cfg->n_q_heads <= 0 || cfg->n_kv_heads <= 0 || cfg->batch <= 0) return KVQ_ERR_INVALID;
+  if (cfg->n_q_heads % cfg->n_kv_heads != 0) return KVQ_ERR_INVALID;
+  if (cfg->n_q_heads / cfg->n_kv_heads > kMaxGroupHeads) return KVQ_ERR_UNSUPPORTED;
+  if (cfg->page_tokens <= 0 || cfg->page_tokens % kGroupTokens != 0) return KVQ_ERR_INVALID;
+  if (cfg->max_pages <= 0 || cfg->num_pages <= 0) return KVQ_ERR_INVALID;
+  if ((int64_t)cfg->max_pages * cfg->page_tokens > INT32_MAX) return KVQ_ERR_INVALID;
+  if (cfg->kv_dtype != KVQ_F32 && cfg->kv_dtype != KVQ_BF16) return KVQ_ERR_UNSUPPORTED;
+  return KVQ_OK;
+}
+
+kvq_status check_params(const kvq_params* p) {
+  if (!p || !p->signs || !p->rot) return KVQ_ERR_INVALID;
+  if (!codebook_ok(p->codebook)) return KVQ_ERR_INVALID;
+  return KVQ_OK;
+}
+
+kvq_status check_cache(const kvq_cache* c) {
+  if (!c || !c->k_codes || !c->k_stats || !c->v_codes || !c->v_norms || !c->modality ||
+      !c->page_table || !c->seq_len || !c->k_tail || !c->seq_len_host)
+    return KVQ_ERR_INVALID;
+  return KVQ_OK;
+}
+
+// Context partitions for the decode: about 4096 partition wavefronts over the
+// whole batch, at least 8 groups each, a multiple of 4 per (session, KV head).
+struct Plan {
+  int splits;
+  int split_tokens;
+};
+
+Plan plan_decode(const kvq_config* cfg, int32_t max_len) {
+  const int want = std::max(4, 4096 / std::max(1, cfg->batch * cfg->n_kv_heads));
+  int len = std::max(max_len, 1);
+  int per = (len + want - 1) / want;
+  per = std::max(256, ((per + kGroupTokens - 1) / kGroupTokens) * kGroupTokens);
+  int splits = (len + per - 1) / per;
+  splits = ((splits + 3) / 4) * 4;
+  while (splits > 4096) {  // very long contexts: widen the partitions
+    per *= 2;
+    splits = (((len + per - 1) / per) + 3) / 4 * 4;
+  }
+  return {splits, per};
+}
+
+size_t partial_floats(const kvq_config* cfg, const Plan& p) {
+  return (size_t)cfg->batch * cfg->n_q_heads * p.splits * (2 + 3 * cfg->head_dim);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvq_status_string(kvq_status s) {
+  switch (s) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_INVALID: return "invalid argument";
+    case KVQ_ERR_UNSUPPORTED: return "unsupported configuration";
+    case KVQ_ERR_CAPACITY: return "cache capacity exceeded";
+    case KVQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case KVQ_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+kvq_status kvq_cache_buffer_bytes(const kvq_config* cfg, size_t out[6]) {
+  kvq_status st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  if (!out) return KVQ_ERR_INVALID;
+  const size_t d = cfg->head_dim, hkv = cfg->n_kv_heads, pt = cfg->page_tokens, np = cfg->num_pages;
+  const size_t groups = np * hkv * (pt / kGroupTokens);
+  out[0] = groups * 8 * d;                 // k_codes
+  out[1] = groups * 2 * d * 2;             // k_stats (fp16)
+  out[2] = groups * 8 * d;                 // v_codes
+  out[3] = np * hkv * pt * 2;              // v_norms (fp16)
+  out[4] = np * pt;                        // modality
+  out[5] = (size_t)cfg->batch * hkv * kGroupTokens * d * (cfg->kv_dtype == KVQ_BF16 ? 2 : 4);
+  return KVQ_OK;
+}
+
+kvq_status kvq_quantize_append(const kvq_config* cfg, kvq_cache* cache, const kvq_params* params,
+                               int32_t b0, int32_t nb, int32_t n_new, const void* k_new,
+                               const void* v_new, const uint8_t* modality_new, hipStream_t stream) {
+  kvq_status st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  if ((st = check_params(params)) != KVQ_OK) return st;
+  if ((st = check_cache(cache)) != KVQ_OK) return st;
+  if (b0 < 0 || nb <= 0 || b0 + nb > cfg->batch || n_new < 0) return KVQ_ERR_INVALID;
+  if (n_new == 0) return KVQ_OK;
+  if (!k_new || !v_new || !modality_new) return KVQ_ERR_INVALID;
+  const int64_t cap = (int64_t)cfg->max_pages * cfg->page_tokens;
+  for (int b = b0; b < b0 + nb; ++b) {
+    if (cache->seq_len_host[b] < 0) return KVQ_ERR_INVALID;
+    if ((int64_t)cache->seq_len_host[b] + n_new > cap) return KVQ_ERR_CAPACITY;
+  }
+  const double sd = sqrt((double)cfg->head_dim);
+  kvq::AppendArgs a;
+  a.k_codes = cache->k_codes;
+  a.k_stats = cache->k_stats;
+  a.v_codes = cache->v_codes;
+  a.v_norms = cache->v_norms;
+  a.modality = cache->modality;
+  a.page_table = cache->page_table;
+  a.seq_len = cache->seq_len;
+  a.k_tail = cache->k_tail;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.modality_new = modality_new;
+  a.signs = params->signs;
+  a.rot = params->rot;
+  a.b0 = b0;
+  a.n_new = n_new;
+  a.hkv = cfg->n_kv_heads;
+  a.page_tokens = cfg->page_tokens;
+  a.max_pages = cfg->max_pages;
+  a.num_pages = cfg->num_pages;
+  a.inv_sqrt_d = 1.0 / sd;
+  a.sqrt_d = sd;
+  const double c[4] = {params->codebook[0], params->codebook[1], params->codebook[2], params->codebook[3]};
+  a.c0 = c[0];
+  a.c3 = c[3];
+  a.thr0 = (c[0] + c[1]) / 2.0;
+  a.thr1 = (c[1] + c[2]) / 2.0;
+  a.thr2 = (c[2] + c[3]) / 2.0;
+  hipError_t e = kvq::launch_append(cfg->head_dim, cfg->kv_dtype == KVQ_BF16, nb, a, stream);
+  if (e != hipSuccess) return KVQ_ERR_LAUNCH;
+  for (int b = b0; b < b0 + nb; ++b) cache->seq_len_host[b] += n_new;
+  return KVQ_OK;
+}
+
+kvq_status kvq_rotate_query(const kvq_config* cfg, const kvq_params* params, int32_t batch,
+                            const void* q, int32_t q_dtype, float* q_rot, hipStream_t stream) {
+  kvq_status st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  if (!params || !params->signs) return KVQ_ERR_INVALID;
+  if (batch <= 0 || !q || !q_rot) return KVQ_ERR_INVALID;
+  if (q_dtype != KVQ_F32 && q_dtype != KVQ_BF16) return KVQ_ERR_UNSUPPORTED;
+  kvq::RotateArgs a;
+  a.q = q;
+  a.q_rot = q_rot;
+  a.signs = params->signs;
+  a.hq = cfg->n_q_heads;
+  a.group = cfg->n_q_heads / cfg->n_kv_heads;
+  a.inv_sqrt_d = 1.0 / sqrt((double)cfg->head_dim);
+  hipError_t e = kvq::launch_rotate_query(cfg->head_dim, q_dtype == KVQ_BF16, batch, a, stream);
+  return e == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;
+}
+
+size_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t max_len) {
+  if (check_config(cfg) != KVQ_OK || max_len < 0) return 0;
+  return partial_floats(cfg, plan_decode(cfg, max_len)) * sizeof(float);
+}
+
+kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache,
+                                const kvq_params* params, const float* q_rot, float scale,
+                                float* out, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  kvq_status st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  if ((st = check_params(params)) != KVQ_OK) return st;
+  if ((st = check_cache(cache)) != KVQ_OK) return st;
+  if (!q_rot || !out || !isfinite(scale)) return KVQ_ERR_INVALID;
+  int32_t max_len = 0;
+  const int64_t cap = (int64_t)cfg->max_pages * cfg->page_tokens;
+  for (int b = 0; b < cfg->batch; ++b) {
+    if (cache->seq_len_host[b] < 0 || cache->seq_len_host[b] > cap) return KVQ_ERR_INVALID;
+    max_len = std::max(max_len, cache->seq_len_host[b]);
+  }
+  const Plan plan = plan_decode(cfg, max_len);
+  if (!workspace || workspace_bytes < partial_floats(cfg, plan) * sizeof(float)) return KVQ_ERR_WORKSPACE;
+  const double c0 = params->codebook[0], c3 = params->codebook[3];
+  kvq::DecodeArgs a;
+  a.k_codes = cache->k_codes;
+  a.k_stats = cache->k_stats;
+  a.v_codes = cache->v_codes;
+  a.v_norms = cache->v_norms;
+  a.modality = cache->modality;
+  a.page_table = cache->page_table;
+  a.seq_len = cache->seq_len;
+  a.q_rot = q_rot;
+  a.rot = params->rot;
+  a.out = out;
+  a.partials = static_cast<float*>(workspace);
+  a.hq = cfg->n_q_heads;
+  a.hkv = cfg->n_kv_heads;
+  a.group = cfg->n_q_heads / cfg->n_kv_heads;
+  a.page_tokens = cfg->page_tokens;
+  a.max_pages = cfg->max_pages;
+  a.num_pages = cfg->num_pages;
+  a.splits = plan.splits;
+  a.split_tokens = plan.split_tokens;
+  a.scale_log2e = (float)((double)scale * 1.4426950408889634);
+  a.value_scale = (float)(1.0 / sqrt((double)cfg->head_dim));
+  for (int k = 0; k < 4; ++k) {
+    a.lv[k] = (float)((params->codebook[k] - c0) / (c3 - c0));
+    a.cv[k] = params->codebook[k];
+  }
+  hipError_t e = kvq::launch_decode(cfg->head_dim, cfg->batch, a, stream);
+  return e == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,172 @@
+/*
+ * kvq.h - C ABI of the MI355X (gfx950) library for rotation-based 2-bit
+ * KV-cache quantization with fused decode attention over the packed cache.
+ *
+ * Method (OmniKVQuant page, paperlayer.ai summary of arXiv 2609.11582):
+ *   - keys: randomized Hadamard rotation, min-max scaling inside short
+ *     consecutive-token groups with the group statistics stored, and the
+ *     shared fixed codebook on the scaled values (Sec. 2 Method, key bullet);
+ *   - values: a separate rotation per modality, then the fixed codebook on
+ *     the magnitude-normalised rotated coordinates (Sec. 2 Method, TurboQuant
+ *     and value bullets);
+ *   - decode: one query rotation per head, attention computed directly on
+ *     the 2-bit codes, inverse value rotations applied once after the
+ *     aggregation; no dense FP16 cache is ever formed (Sec. 1, Implementation
+ *     bullet; Abstract).
+ *
+ * Conventions shared by every entry point
+ *   - All pointers named "device" are HIP device memory owned by the caller;
+ *     the library allocates nothing and keeps no global state.
+ *   - Every call is asynchronous on the given stream (0 = null stream).  No
+ *     call synchronises.
+ *   - Arguments are validated on the host before anything is launched; a
+ *     failed validation returns an error code and changes no state.
+ *   - Launch failures are reported as KVQ_ERR_LAUNCH.
+ *   - d (head_dim) is 64 or 128; G = n_q_heads / n_kv_heads is an integer in
+ *     [1, 16]; query head i reads KV head floor(i / G).
+ *   - Modalities: 0 video, 1 audio, 2 text.  Keys are grouped in 32-token
+ *     groups aligned to absolute positions 32g.
+ *
+ * Packed cache (paged; a contiguous cache is an identity page table).
+ * page_tokens is a multiple of 32; GP = page_tokens / 32 groups per page.
+ * Physical page p, KV head h, group-in-page j, position-in-page s:
+ *   k_codes  [num_pages][Hkv][GP][8d] bytes   2-bit key codes of one group
+ *   v_codes  [num_pages][Hkv][GP][8d] bytes   2-bit value codes of one group
+ *   k_stats  [num_pages][Hkv][GP][2][d] fp16  rotated-key group min (row 0) and max (row 1)
+ *   v_norms  [num_pages][Hkv][page_tokens] fp16  value norms
+ *   modality [num_pages][page_tokens] uint8
+ * Inside one 8d-byte group block the codes are laid out for the decode
+ * kernel's matrix-core operands ("lane-major").  With W = d/8 bytes per lane
+ * and lane L in [0, 64):
+ *   key   (token t in 0..31, channel c): L = ((c % 32) / 8) * 16 + t % 16,
+ *         byte = L*W + (t / 16)*(d/16) + (c / 32)*2 + (c % 8) / 4, bits 2*(c % 4)
+ *   value (token t, channel c):          L = ((t % 16) / 4) * 16 + c % 16,
+ *         byte = L*W + (c / 16)*2 + t / 16, bits 2*(t % 4)
+ * Slots past the session length hold unspecified codes and are never read
+ * as data.  The raw key tail keeps the keys of the open (partial) group:
+ *   k_tail   [batch][Hkv][32][d] in kv_dtype, slot = position % 32
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_ERR_INVALID = 1,      /* null pointer, bad shape, bad codebook, bad index range */
+  KVQ_ERR_UNSUPPORTED = 2,  /* d not in {64,128}, G > 16, dtype not supported */
+  KVQ_ERR_CAPACITY = 3,     /* append would exceed max_pages * page_tokens */
+  KVQ_ERR_WORKSPACE = 4,    /* decode workspace null or too small */
+  KVQ_ERR_LAUNCH = 5        /* a HIP launch failed */
+} kvq_status;
+
+typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype;
+
+typedef struct kvq_config {
+  int32_t head_dim;     /* d: 64 or 128 */
+  int32_t n_q_heads;    /* Hq */
+  int32_t n_kv_heads;   /* Hkv; Hq % Hkv == 0 and Hq / Hkv <= 16 */
+  int32_t batch;        /* sessions B */
+  int32_t page_tokens;  /* tokens per page, multiple of 32 */
+  int32_t max_pages;    /* page-table row length: capacity = max_pages * page_tokens */
+  int32_t num_pages;    /* physical pages in the pool */
+  int32_t kv_dtype;     /* kvq_dtype of appended K/V (and of the raw key tail) */
+} kvq_config;
+
+typedef struct kvq_cache {
+  uint8_t*       k_codes;     /* device */
+  uint16_t*      k_stats;     /* device, fp16 bits */
+  uint8_t*       v_codes;     /* device */
+  uint16_t*      v_norms;     /* device, fp16 bits */
+  uint8_t*       modality;    /* device */
+  const int32_t* page_table;  /* device [batch][max_pages]: physical page of each logical page */
+  int32_t*       seq_len;     /* device [batch]: cached positions per session */
+  void*          k_tail;      /* device [batch][Hkv][32][d] kv_dtype */
+  int32_t*       seq_len_host;/* host [batch]: mirror of seq_len kept by the library */
+} kvq_cache;
+
+typedef struct kvq_params {
+  const int8_t* signs;        /* device [Hkv][d], each +1 or -1: Hadamard signs per KV head */
+  const float*  rot;          /* device [Hkv][3][d][d] row-major R_{h,m}; columns are the basis */
+  float         codebook[4];  /* strictly increasing reconstruction levels c0 < c1 < c2 < c3 */
+} kvq_params;
+
+/* Bytes of each cache buffer for a configuration, in the order k_codes,
+ * k_stats, v_codes, v_norms, modality, k_tail.  Returns KVQ_ERR_INVALID /
+ * KVQ_ERR_UNSUPPORTED for a bad configuration. */
+kvq_status kvq_cache_buffer_bytes(const kvq_config* cfg, size_t bytes_out[6]);
+
+/*
+ * kvq_quantize_append - quantize n_new tokens per session and append them
+ * to sessions [b0, b0 + nb) of the packed cache (Sec. 2 Method: key and
+ * value bullets).
+ *
+ * k_new, v_new: device [nb][n_new][Hkv][d] in cfg->kv_dtype.
+ * modality_new: device [nb][n_new] uint8 in {0,1,2}.
+ * Keys: y = H_d (s_h * k) / sqrt(d) in fp64; the group touched by the append
+ * (including the open group, whose earlier keys come from k_tail) is
+ * re-quantized with lo/hi = min/max of y over its present tokens, stored as
+ * fp16 (round to nearest even); codes map [LO, HI] onto [c0, c3] and take
+ * the nearest level.  Values: n = ||v||, z = sqrt(d) (R_{h,m}^T v) / n in
+ * fp64, nearest level, norm stored as fp16.  seq_len and seq_len_host
+ * advance by n_new.  Three kernels are launched on `stream`.
+ * Errors: KVQ_ERR_INVALID (null pointers, b0/nb out of range, n_new < 0,
+ * codebook not increasing), KVQ_ERR_CAPACITY (some session would exceed
+ * max_pages * page_tokens, judged on seq_len_host), KVQ_ERR_UNSUPPORTED.
+ */
+kvq_status kvq_quantize_append(const kvq_config* cfg, kvq_cache* cache, const kvq_params* params,
+                               int32_t b0, int32_t nb, int32_t n_new,
+                               const void* k_new, const void* v_new,
+                               const uint8_t* modality_new, hipStream_t stream);
+
+/*
+ * kvq_rotate_query - rotate every query head once with its KV head's
+ * Hadamard signs (Sec. 1, Implementation bullet):
+ * q_rot[b][i] = H_d (s_{floor(i/G)} * q[b][i]) / sqrt(d), computed in fp64
+ * and rounded once to fp32.
+ * q: device [batch][Hq][d] in q_dtype (KVQ_F32 or KVQ_BF16); q_rot: device
+ * [batch][Hq][d] fp32.  Errors: KVQ_ERR_INVALID, KVQ_ERR_UNSUPPORTED.
+ */
+kvq_status kvq_rotate_query(const kvq_config* cfg, const kvq_params* params, int32_t batch,
+                            const void* q, int32_t q_dtype, float* q_rot, hipStream_t stream);
+
+/* Workspace bytes kvq_decode_attention needs when the longest session holds
+ * max_len positions (split-K partial results). */
+size_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t max_len);
+
+/*
+ * kvq_decode_attention - one decode step of every query head against the
+ * packed cache (Sec. 1, Implementation bullet; Abstract: no dense FP16 cache).
+ * For query head i of session b, over positions t < seq_len[b]:
+ *   s_t = scale * <q_rot[b][i], k_hat_t>,  k_hat_t = LO + (c[code]-c0)(HI-LO)/(c3-c0)
+ *   p = softmax(s);  A_m = sum_{t: modality m} p_t (N_t / sqrt(d)) c[vcode_t]
+ *   out[b][i] = sum_m R_{h,m} A_m
+ * The context is split into partitions processed in parallel (online
+ * softmax per partition); a second kernel merges them and applies R_{h,m}.
+ * q_rot: device [batch][Hq][d] fp32 (from kvq_rotate_query); out: device
+ * [batch][Hq][d] fp32; an empty session gives zeros.  The partition plan
+ * comes from max(seq_len_host).  workspace: device, at least
+ * kvq_decode_workspace_bytes(cfg, max(seq_len_host)) bytes.
+ * Errors: KVQ_ERR_INVALID, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE,
+ * KVQ_ERR_LAUNCH.
+ */
+kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache,
+                                const kvq_params* params, const float* q_rot, float scale,
+                                float* out, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+/* Static description of a status code. */
+const char* kvq_status_string(kvq_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -1,0 +1,147 @@
+"""Shared plumbing of the GPU parity tests: run a seeded workload through the
+HIP library and through the fp64 oracle, and compare them."""
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+from omnistream import Workload
+from oracle import kvq_oracle as O
+
+ATTN_TOL = 2e-3          # max normwise relative error per (session, query head)
+BOUNDARY_EPS = 1e-6      # |z - threshold| below which a code may differ
+BOUNDARY_FRAC = 1e-5     # allowed fraction of such elements
+
+
+def _kv_tensor(x: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    if dtype == "bf16":
+        t = t.view(torch.bfloat16)
+    return t.to(device)
+
+
+def build(w: Workload, page_table: Optional[np.ndarray] = None, chunks: Optional[Sequence[int]] = None,
+          upto: Optional[Sequence[int]] = None, device="cuda"):
+    """Create cfg/params/cache for workload w and append every session's stream
+    (split into `chunks` sized appends if given) up to `upto[b]` positions."""
+    import decode_attention_kvq_amd as K
+    c = w.cfg
+    kv_dtype = torch.bfloat16 if c.dtype == "bf16" else torch.float32
+    pt = w.page_table if page_table is None else page_table
+    num_pages = int(pt.max()) + 1
+    cfg = K.Config(c.head_dim, c.n_q_heads, c.n_kv_heads, c.batch, w.page_tokens, pt.shape[1],
+                   num_pages, kv_dtype)
+    params = K.Params(torch.from_numpy(w.signs).to(device), torch.from_numpy(w.rot).to(device),
+                      w.codebook.tolist())
+    cache = K.Cache(cfg, torch.from_numpy(pt), device=device)
+    for b in range(c.batch):
+        n = int(w.lengths[b] if upto is None else upto[b])
+        append_range(cfg, cache, params, w, b, 0, n, chunks)
+    return cfg, params, cache
+
+
+def append_range(cfg, cache, params, w: Workload, b: int, start: int, stop: int,
+                 chunks: Optional[Sequence[int]] = None):
+    import decode_attention_kvq_amd as K
+    pos = start
+    ci = 0
+    while pos < stop:
+        n = stop - pos if not chunks else min(int(chunks[ci % len(chunks)]), stop - pos)
+        ci += 1
+        k = _kv_tensor(w.k[b][None, pos:pos + n], w.dtype)
+        v = _kv_tensor(w.v[b][None, pos:pos + n], w.dtype)
+        m = torch.from_numpy(np.ascontiguousarray(w.modality[b][None, pos:pos + n])).to(k.device)
+        K.kvq_quantize_append(cfg, cache, params, k, v, m, b0=b)
+        pos += n
+
+
+def query_tensor(w: Workload, device="cuda") -> torch.Tensor:
+    return _kv_tensor(w.q, w.dtype, device)
+
+
+def oracle_session(w: Workload, b: int, length: Optional[int] = None) -> list:
+    n = int(w.lengths[b] if length is None else length)
+    k = O.as_f64(w.k[b][:n], w.dtype)
+    v = O.as_f64(w.v[b][:n], w.dtype)
+    return O.quantize_session(k, v, w.modality[b][:n], w.signs, w.rot, w.codebook)
+
+
+def _boundary_ok(z: np.ndarray, mism: np.ndarray, thresholds: np.ndarray) -> np.ndarray:
+    dist = np.min(np.abs(z[mism][:, None] - thresholds[None, :]), axis=1)
+    return dist < BOUNDARY_EPS
+
+
+def compare_session_codes(w: Workload, b: int, gpu: dict, ora: list, h: int, length: int) -> dict:
+    """Bit-exact comparison of one (session, KV head); returns counts."""
+    o = ora[h]
+    stats = {}
+    np.testing.assert_array_equal(gpu["lo"].view(np.uint16), o["lo"].view(np.uint16), err_msg=f"LO b={b} h={h}")
+    np.testing.assert_array_equal(gpu["hi"].view(np.uint16), o["hi"].view(np.uint16), err_msg=f"HI b={b} h={h}")
+    np.testing.assert_array_equal(gpu["modality"], w.modality[b][:length])
+    thr = O.decision_thresholds(w.codebook)
+    k = O.as_f64(w.k[b][:length, h], w.dtype)
+    v = O.as_f64(w.v[b][:length, h], w.dtype)
+    km = gpu["k_codes"] != o["k_codes"]
+    if km.any():
+        z = O.key_normalized_values(k, w.signs[h], o["lo"], o["hi"], w.codebook)
+        ok = _boundary_ok(z, km, thr)
+        assert ok.all(), f"key codes differ away from a threshold: b={b} h={h} n={int((~ok).sum())}"
+    vm = gpu["v_codes"] != o["v_codes"]
+    if vm.any():
+        z = O.value_normalized_values(v, w.modality[b][:length], w.rot[h])
+        ok = _boundary_ok(z, vm, thr)
+        assert ok.all(), f"value codes differ away from a threshold: b={b} h={h} n={int((~ok).sum())}"
+    nm = gpu["norms"].view(np.uint16) != o["norms"].view(np.uint16)
+    if nm.any():
+        n64 = np.sqrt(np.sum(v * v, axis=1))[nm]
+        lo_ = np.minimum(gpu["norms"][nm], o["norms"][nm]).astype(np.float64)
+        hi_ = np.maximum(gpu["norms"][nm], o["norms"][nm]).astype(np.float64)
+        mid = (lo_ + hi_) / 2
+        assert np.all(np.abs(n64 - mid) <= 1e-12 * n64), f"norms differ away from an fp16 midpoint b={b} h={h}"
+    stats["elements"] = 2 * k.size
+    stats["boundary_mismatches"] = int(km.sum() + vm.sum() + nm.sum())
+    return stats
+
+
+def check_codes(w: Workload, cfg, cache, sessions: Sequence[int], lengths: Optional[Sequence[int]] = None):
+    from decode_attention_kvq_amd.layout import session_view
+    host = cache.host_arrays()
+    total = mism = 0
+    for b in sessions:
+        n = int(w.lengths[b] if lengths is None else lengths[b])
+        assert int(host["seq_len"][b]) == n
+        ora = oracle_session(w, b, n)
+        for h in range(w.cfg.n_kv_heads):
+            gpu = session_view(host, cfg, b, n, h)
+            s = compare_session_codes(w, b, gpu, ora, h, n)
+            total += s["elements"]
+            mism += s["boundary_mismatches"]
+    assert mism <= BOUNDARY_FRAC * max(total, 1), f"{mism} boundary mismatches of {total}"
+    return total, mism
+
+
+def oracle_decode_over_gpu_codes(w: Workload, cfg, cache, q: np.ndarray, sessions: Sequence[int],
+                                 scale: float) -> dict:
+    """The oracle attending over the GPU's own packed cache (codes read back)."""
+    from decode_attention_kvq_amd.layout import session_view
+    host = cache.host_arrays()
+    out = {}
+    for b in sessions:
+        n = int(host["seq_len"][b])
+        caches = [session_view(host, cfg, b, n, h) for h in range(w.cfg.n_kv_heads)]
+        q_rot = O.rotate_query(q[b], w.signs, w.cfg.n_kv_heads)
+        out[b] = O.decode_attention(q_rot, caches, w.rot, w.codebook, scale)
+    return out
+
+
+def normwise_rel_err(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """Per row: max_j |got - ref| / max_j |ref|."""
+    den = np.maximum(np.abs(ref).max(axis=-1), 1e-30)
+    return np.abs(got - ref).max(axis=-1) / den
+
+
+def default_scale(w: Workload) -> float:
+    return 1.0 / math.sqrt(w.cfg.head_dim)

@@ -1,0 +1,132 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+and rejects bad arguments on the host before launching anything."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    import decode_attention_kvq_amd._lib as L
+    if not os.path.exists(L.LIB_PATH):
+        pytest.skip("libkvq.so not built")
+    return L, L.load()
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:kvq_status|size_t|const char\*)\s+(kvq_\w+)\s*\(", src, re.M)))
+
+
+def test_header_declares_the_three_entry_points():
+    names = _declared()
+    for n in ("kvq_quantize_append", "kvq_rotate_query", "kvq_decode_attention"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L, lib = _lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (kvq_\w+)", out))
+    for n in _declared():
+        assert n in exported, n
+        assert hasattr(lib, n)
+    assert set(L.EXPORTED) == set(_declared())
+
+
+def _cfg(L, **kw):
+    base = dict(head_dim=128, n_q_heads=16, n_kv_heads=2, batch=2, page_tokens=256, max_pages=4,
+                num_pages=8, kv_dtype=L.KVQ_BF16)
+    base.update(kw)
+    return L.KvqConfig(*[base[f] for f, _ in L.KvqConfig._fields_])
+
+
+def _fake_params(L, codebook=(-1.5104, -0.4528, 0.4528, 1.5104)):
+    return L.KvqParams(0x1000, 0x2000, (ctypes.c_float * 4)(*codebook))
+
+
+def _fake_cache(L, lengths):
+    arr = (ctypes.c_int32 * len(lengths))(*lengths)
+    c = L.KvqCache(*([0x1000] * 8), arr)
+    return c, arr
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), 2), (dict(head_dim=256), 2), (dict(n_q_heads=15), 1),
+    (dict(n_q_heads=34, n_kv_heads=2), 2), (dict(page_tokens=100), 1), (dict(batch=0), 1),
+    (dict(kv_dtype=7), 2), (dict(max_pages=0), 1),
+])
+def test_config_validation(kw, status):
+    L, lib = _lib()
+    out = (ctypes.c_size_t * 6)()
+    assert lib.kvq_cache_buffer_bytes(ctypes.byref(_cfg(L, **kw)), out) == status
+
+
+def test_buffer_sizes():
+    L, lib = _lib()
+    out = (ctypes.c_size_t * 6)()
+    assert lib.kvq_cache_buffer_bytes(ctypes.byref(_cfg(L)), out) == 0
+    groups = 8 * 2 * 8
+    assert list(out) == [groups * 1024, groups * 512, groups * 1024, 8 * 2 * 256 * 2, 8 * 256, 2 * 2 * 32 * 128 * 2]
+
+
+def test_append_rejects_bad_arguments_without_launching():
+    L, lib = _lib()
+    cfg = _cfg(L)
+    p = _fake_params(L)
+    c, lens = _fake_cache(L, [0, 1000])
+    args = lambda b0, nb, n: (ctypes.byref(cfg), ctypes.byref(c), ctypes.byref(p), b0, nb, n,
+                              ctypes.c_void_p(8), ctypes.c_void_p(8), ctypes.c_void_p(8), None)
+    assert lib.kvq_quantize_append(*args(0, 3, 1)) == L.KVQ_ERR_INVALID          # sessions out of range
+    assert lib.kvq_quantize_append(*args(-1, 1, 1)) == L.KVQ_ERR_INVALID
+    assert lib.kvq_quantize_append(*args(0, 1, -5)) == L.KVQ_ERR_INVALID
+    assert lib.kvq_quantize_append(*args(1, 1, 25)) == L.KVQ_ERR_CAPACITY        # 1000 + 25 > 4 * 256
+    assert list(lens) == [0, 1000]                                                # no state change
+    assert lib.kvq_quantize_append(*args(0, 2, 0)) == L.KVQ_OK                    # empty append: no-op
+    bad = _fake_params(L, (-1.0, 0.5, 0.2, 1.0))
+    assert lib.kvq_quantize_append(ctypes.byref(cfg), ctypes.byref(c), ctypes.byref(bad), 0, 1, 1,
+                                   ctypes.c_void_p(8), ctypes.c_void_p(8), ctypes.c_void_p(8), None) == 1
+    assert lib.kvq_quantize_append(ctypes.byref(cfg), ctypes.byref(c), ctypes.byref(p), 0, 1, 4,
+                                   None, ctypes.c_void_p(8), ctypes.c_void_p(8), None) == 1
+    nulls = L.KvqCache(0, *([0x1000] * 7), lens)
+    assert lib.kvq_quantize_append(ctypes.byref(cfg), ctypes.byref(nulls), ctypes.byref(p), 0, 1, 1,
+                                   ctypes.c_void_p(8), ctypes.c_void_p(8), ctypes.c_void_p(8), None) == 1
+
+
+def test_decode_and_rotate_reject_bad_arguments():
+    L, lib = _lib()
+    cfg = _cfg(L)
+    p = _fake_params(L)
+    c, lens = _fake_cache(L, [10, 1000])
+    need = lib.kvq_decode_workspace_bytes(ctypes.byref(cfg), 1000)
+    assert need > 0
+    dec = lambda ws, nbytes, scale=0.1: lib.kvq_decode_attention(
+        ctypes.byref(cfg), ctypes.byref(c), ctypes.byref(p), ctypes.c_void_p(8), ctypes.c_float(scale),
+        ctypes.c_void_p(8), ws, nbytes, None)
+    assert dec(None, need) == L.KVQ_ERR_WORKSPACE
+    assert dec(ctypes.c_void_p(8), need - 1) == L.KVQ_ERR_WORKSPACE
+    assert dec(ctypes.c_void_p(8), need, float("nan")) == L.KVQ_ERR_INVALID
+    lens[1] = 5000                                                                # beyond capacity
+    assert dec(ctypes.c_void_p(8), 1 << 30) == L.KVQ_ERR_INVALID
+    assert lib.kvq_rotate_query(ctypes.byref(cfg), ctypes.byref(p), 0, ctypes.c_void_p(8), 0,
+                                ctypes.c_void_p(8), None) == L.KVQ_ERR_INVALID
+    assert lib.kvq_rotate_query(ctypes.byref(cfg), ctypes.byref(p), 1, ctypes.c_void_p(8), 9,
+                                ctypes.c_void_p(8), None) == L.KVQ_ERR_UNSUPPORTED
+    assert lib.kvq_rotate_query(ctypes.byref(cfg), None, 1, ctypes.c_void_p(8), 0,
+                                ctypes.c_void_p(8), None) == L.KVQ_ERR_INVALID
+    for s in range(6):
+        assert lib.kvq_status_string(s)
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    import decode_attention_kvq_amd as K
+    _lib()
+    cfg = K.Config(64, 2, 1, 1, 256, 8, 8, torch.float32)
+    with pytest.raises(TypeError):
+        K.Params(torch.ones(1, 64, dtype=torch.int8), torch.zeros(1, 3, 64, 64), [-1.5, -0.5, 0.5, 1.5])

@@ -1,0 +1,177 @@
+"""GPU parity of the HIP path against the fp64 oracle, through the C ABI.
+
+Bar: key/value codes and fp16 statistics bit-exact (codes may differ only
+within 1e-6 of a decision threshold, counted, < 1e-5 of all elements);
+rotated queries bit-exact (one fp32 rounding of the fp64 transform);
+decode outputs within 2e-3 normwise relative error per (session, query head)
+of the oracle attending over the same packed codes.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from omnistream import generate
+from oracle import kvq_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import decode_attention_kvq_amd._lib as L
+    L.load()
+
+
+def H():
+    import tests.kvq_harness as h
+    return h
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+# ------------------------------------------------------------ query rotation
+
+@pytest.mark.parametrize("cfg_id", [0, 1, 2, 4])
+def test_rotate_query_bit_exact(cfg_id):
+    import decode_attention_kvq_amd as K
+    w = generate(cfg_id, length=64)
+    _say(f"rotate_query cfg{cfg_id}")
+    cfg, params, cache = H().build(w)
+    q_rot = K.kvq_rotate_query(cfg, params, H().query_tensor(w)).cpu().numpy()
+    q64 = O.as_f64(w.q, w.dtype)
+    for b in range(w.cfg.batch):
+        ref = O.rotate_query(q64[b], w.signs, w.cfg.n_kv_heads).astype(np.float32)
+        np.testing.assert_array_equal(q_rot[b], ref)
+
+
+# ----------------------------------------------------- quantize-append + decode
+
+CASES = [
+    # (cfg_id, overrides) -- several tiles and a ragged tail at each size
+    (0, dict()),
+    (1, dict(length=3001)),
+    (2, dict(length=5000)),
+    (3, dict(batch=3, len_range=(700, 2600))),
+    (4, dict(length=1500)),
+]
+
+
+@pytest.mark.parametrize("cfg_id,kw", CASES, ids=[f"cfg{c}" for c, _ in CASES])
+def test_append_and_decode_parity(cfg_id, kw):
+    import decode_attention_kvq_amd as K
+    h = H()
+    w = generate(cfg_id, **kw)
+    _say(f"append+decode cfg{cfg_id} {kw} lengths={w.lengths.tolist()}")
+    cfg, params, cache = h.build(w)
+    total, mism = h.check_codes(w, cfg, cache, range(w.cfg.batch))
+    _say(f"codes: {total} elements, {mism} boundary mismatches")
+    scale = h.default_scale(w)
+    q_rot = K.kvq_rotate_query(cfg, params, h.query_tensor(w))
+    out = K.kvq_decode_attention(cfg, cache, params, q_rot, scale).cpu().numpy()
+    ref = h.oracle_decode_over_gpu_codes(w, cfg, cache, O.as_f64(w.q, w.dtype), range(w.cfg.batch), scale)
+    worst = 0.0
+    for b in range(w.cfg.batch):
+        err = h.normwise_rel_err(out[b].astype(np.float64), ref[b])
+        worst = max(worst, float(err.max()))
+    _say(f"decode worst normwise rel err {worst:.3e}")
+    assert worst <= h.ATTN_TOL
+
+
+def test_chunked_append_equals_one_shot():
+    """Appends of ragged sizes (re-quantizing the open group from the raw key
+    tail each time) give the same cache bytes as one append of the stream."""
+    h = H()
+    w = generate(1, length=1111)
+    _say("chunked append cfg1 1111")
+    cfg, params, one = h.build(w)
+    _, _, many = h.build(w, chunks=[1, 7, 31, 33, 64, 5, 100, 2, 32])
+    a, b = one.host_arrays(), many.host_arrays()
+    for key in ("k_codes", "k_stats", "v_codes", "v_norms", "modality", "seq_len"):
+        np.testing.assert_array_equal(a[key], b[key], err_msg=key)
+    h.check_codes(w, cfg, many, [0])
+
+
+def test_paged_equals_contiguous():
+    """The same sessions under a shuffled page table decode to the same output."""
+    import decode_attention_kvq_amd as K
+    h = H()
+    w = generate(3, batch=4, len_range=(300, 1500))
+    _say("paged vs contiguous cfg3 b=4")
+    ident = np.full_like(w.page_table, -1)
+    off = 0
+    for b in range(4):
+        n = int((w.page_table[b] >= 0).sum())
+        ident[b, :n] = np.arange(off, off + n)
+        off += n
+    cfg_p, params, cache_p = h.build(w)
+    cfg_c, _, cache_c = h.build(w, page_table=ident)
+    q_rot = K.kvq_rotate_query(cfg_p, params, h.query_tensor(w))
+    out_p = K.kvq_decode_attention(cfg_p, cache_p, params, q_rot).cpu().numpy()
+    out_c = K.kvq_decode_attention(cfg_c, cache_c, params, q_rot).cpu().numpy()
+    np.testing.assert_array_equal(out_p, out_c)
+
+
+def test_empty_and_tiny_sessions():
+    """Session lengths 0, 1, 31, 32, 33: empty gives zeros, one position gives
+    that position's reconstructed value."""
+    import decode_attention_kvq_amd as K
+    h = H()
+    w = generate(3, batch=5, len_range=(40, 60))
+    upto = [0, 1, 31, 32, 33]
+    _say(f"tiny sessions {upto}")
+    cfg, params, cache = h.build(w, upto=upto)
+    h.check_codes(w, cfg, cache, [1, 2, 3, 4], lengths=upto)
+    q_rot = K.kvq_rotate_query(cfg, params, h.query_tensor(w))
+    out = K.kvq_decode_attention(cfg, cache, params, q_rot).cpu().numpy()
+    np.testing.assert_array_equal(out[0], 0.0)
+    ref = h.oracle_decode_over_gpu_codes(w, cfg, cache, O.as_f64(w.q, w.dtype), [1, 2, 3, 4],
+                                         h.default_scale(w))
+    for b in [1, 2, 3, 4]:
+        assert h.normwise_rel_err(out[b].astype(np.float64), ref[b]).max() <= h.ATTN_TOL
+
+
+def test_decode_is_repeatable_and_scale_respected():
+    import decode_attention_kvq_amd as K
+    h = H()
+    w = generate(1, length=2000)
+    cfg, params, cache = h.build(w)
+    q_rot = K.kvq_rotate_query(cfg, params, h.query_tensor(w))
+    a = K.kvq_decode_attention(cfg, cache, params, q_rot, 0.05).cpu().numpy()
+    b = K.kvq_decode_attention(cfg, cache, params, q_rot, 0.05).cpu().numpy()
+    np.testing.assert_array_equal(a, b)
+    ref = h.oracle_decode_over_gpu_codes(w, cfg, cache, O.as_f64(w.q, w.dtype), [0], 0.05)
+    assert h.normwise_rel_err(a[0].astype(np.float64), ref[0]).max() <= h.ATTN_TOL
+
+
+def test_graph_replays_match_eager():
+    """A captured decode (no memset nodes) replayed several times, with eager
+    work in between, reproduces the eager output on every replay."""
+    import decode_attention_kvq_amd as K
+    h = H()
+    w = generate(2, length=3000)
+    _say("graph replay cfg2 3000")
+    cfg, params, cache = h.build(w)
+    q_rot = K.kvq_rotate_query(cfg, params, h.query_tensor(w))
+    eager = K.kvq_decode_attention(cfg, cache, params, q_rot).clone()
+    out = torch.empty_like(eager)
+    ws = torch.empty(K.kvq_decode_workspace_bytes(cfg, 3000), dtype=torch.uint8, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            K.kvq_decode_attention(cfg, cache, params, q_rot, None, out, ws)
+    for i in range(4):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i}"
+        K.kvq_rotate_query(cfg, params, h.query_tensor(w), q_rot)   # eager work between replays
+        torch.cuda.synchronize()
