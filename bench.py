@@ -46,6 +46,9 @@ def main():
     ap.add_argument("--replicas", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB ten times (reference "
+                         "for the HBM byte counters) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -54,6 +57,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        x = torch.ones(n, dtype=torch.uint8, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(10):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "launches": 10}), flush=True)
+        return
     import decode_attention_kvq_amd as K
     from omnistream import generate
     from tests import kvq_harness as H

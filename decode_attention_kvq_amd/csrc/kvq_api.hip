@@ -44,29 +44,49 @@ kvq_status check_cache(const kvq_cache* c) {
   return KVQ_OK;
 }
 
-// Context partitions for the decode: about 4096 partition wavefronts over the
-// whole batch, at least 8 groups each, a multiple of 4 per (session, KV head).
+// Context partitions for the decode.  A partition is a multiple of
+// 32 * kDecodeWaves positions (every wavefront of the workgroup takes whole
+// groups).  Partitions are sized from the longest session so that a batch of
+// such sessions spreads over about one workgroup per compute unit (256 CUs),
+// or four per CU when that would make partitions longer than 4096 positions.
+// The plan depends only on (cfg, max_len), so the workspace size is known
+// before the call.
 struct Plan {
   int splits;
   int split_tokens;
 };
 
 Plan plan_decode(const kvq_config* cfg, int32_t max_len) {
-  const int want = std::max(4, 4096 / std::max(1, cfg->batch * cfg->n_kv_heads));
-  int len = std::max(max_len, 1);
-  int per = (len + want - 1) / want;
-  per = std::max(256, ((per + kGroupTokens - 1) / kGroupTokens) * kGroupTokens);
-  int splits = (len + per - 1) / per;
-  splits = ((splits + 3) / 4) * 4;
-  while (splits > 4096) {  // very long contexts: widen the partitions
+  constexpr int64_t kUnit = kGroupTokens * kvq::kDecodeWaves;
+  constexpr int64_t kCUs = 256;
+  const int64_t len = std::max<int32_t>(max_len, 1);
+  const int64_t total = len * cfg->batch * cfg->n_kv_heads;
+  int64_t per = (total + kCUs - 1) / kCUs;
+  if (per > 4096) per = (total + 4 * kCUs - 1) / (4 * kCUs);
+  per = std::max(kUnit, ((per + kUnit - 1) / kUnit) * kUnit);
+  int64_t splits = (len + per - 1) / per;
+  while (splits > 4096) {
     per *= 2;
-    splits = (((len + per - 1) / per) + 3) / 4 * 4;
+    splits = (len + per - 1) / per;
   }
-  return {splits, per};
+  return {(int)splits, (int)per};
 }
 
-size_t partial_floats(const kvq_config* cfg, const Plan& p) {
-  return (size_t)cfg->batch * cfg->n_q_heads * p.splits * (2 + 3 * cfg->head_dim);
+// Upper bound of plan_decode(cfg, len).splits over every len <= max_len, so a
+// workspace sized for max_len serves every shorter context too.
+int splits_bound(const kvq_config* cfg, int32_t max_len) {
+  constexpr int64_t kUnit = kGroupTokens * kvq::kDecodeWaves;
+  const int64_t heads = (int64_t)cfg->batch * cfg->n_kv_heads;
+  const int64_t by_len = (std::max<int32_t>(max_len, 1) + kUnit - 1) / kUnit;
+  const int64_t by_grid = (1024 + heads - 1) / heads + 1;
+  return (int)std::min<int64_t>(4096, std::max<int64_t>(1, std::min(by_len, by_grid)));
+}
+
+// Workspace: partials, then the rotated per-modality parts, then the merge
+// completion counters (one int per (session, query head)).
+size_t workspace_floats(const kvq_config* cfg, const Plan& p) {
+  const size_t heads = (size_t)cfg->batch * cfg->n_q_heads;
+  return heads * p.splits * (kvq::kPartialHeader + 3 * cfg->head_dim) + heads * 3 * cfg->head_dim + heads;
 }
 
 }  // namespace
@@ -170,7 +190,7 @@ kvq_status kvq_rotate_query(const kvq_config* cfg, const kvq_params* params, int
 
 size_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t max_len) {
   if (check_config(cfg) != KVQ_OK || max_len < 0) return 0;
-  return partial_floats(cfg, plan_decode(cfg, max_len)) * sizeof(float);
+  return workspace_floats(cfg, Plan{splits_bound(cfg, max_len), 0}) * sizeof(float);
 }
 
 kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache,
@@ -189,7 +209,7 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache,
     max_len = std::max(max_len, cache->seq_len_host[b]);
   }
   const Plan plan = plan_decode(cfg, max_len);
-  if (!workspace || workspace_bytes < partial_floats(cfg, plan) * sizeof(float)) return KVQ_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < workspace_floats(cfg, plan) * sizeof(float)) return KVQ_ERR_WORKSPACE;
   const double c0 = params->codebook[0], c3 = params->codebook[3];
   kvq::DecodeArgs a;
   a.k_codes = cache->k_codes;
@@ -203,6 +223,10 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache,
   a.rot = params->rot;
   a.out = out;
   a.partials = static_cast<float*>(workspace);
+  a.counters = reinterpret_cast<int32_t*>(static_cast<float*>(workspace) + workspace_floats(cfg, plan) -
+                                          (size_t)cfg->batch * cfg->n_q_heads);
+  a.counters_len = cfg->batch * cfg->n_q_heads;
+  a.batch = cfg->batch;
   a.hq = cfg->n_q_heads;
   a.hkv = cfg->n_kv_heads;
   a.group = cfg->n_q_heads / cfg->n_kv_heads;
@@ -213,10 +237,19 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache,
   a.split_tokens = plan.split_tokens;
   a.scale_log2e = (float)((double)scale * 1.4426950408889634);
   a.value_scale = (float)(1.0 / sqrt((double)cfg->head_dim));
+  uint16_t lv[4];
   for (int k = 0; k < 4; ++k) {
-    a.lv[k] = (float)((params->codebook[k] - c0) / (c3 - c0));
-    a.cv[k] = params->codebook[k];
+    const _Float16 v = (_Float16)((2.0 * params->codebook[k] - c0 - c3) / (c3 - c0));
+    lv[k] = __builtin_bit_cast(uint16_t, v);
   }
+  a.level_f16[0] = lv[0] | ((uint32_t)lv[1] << 16);
+  a.level_f16[1] = lv[2] | ((uint32_t)lv[3] << 16);
+  for (int e = 0; e < 256; ++e) {
+    a.byte_levels[e].x = lv[e & 3] | ((uint32_t)lv[(e >> 2) & 3] << 16);
+    a.byte_levels[e].y = lv[(e >> 4) & 3] | ((uint32_t)lv[(e >> 6) & 3] << 16);
+  }
+  a.cmid = (float)((c0 + c3) / 2.0);
+  a.chalf = (float)((c3 - c0) / 2.0);
   hipError_t e = kvq::launch_decode(cfg->head_dim, cfg->batch, a, stream);
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;
 }

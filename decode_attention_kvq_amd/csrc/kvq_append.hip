@@ -167,16 +167,20 @@ __global__ __launch_bounds__(256) void key_append_kernel(AppendArgs a) {
 
 // One workgroup quantizes the new positions of one 32-token group of values
 // (merging with the codes already stored for the group's earlier positions).
+// 256 threads = TQ parts x D output channels: part p accumulates
+// r_j = sum_i R_{h,m}[i][j] v_i over its slice of i for every new position,
+// so each element of R is read once per workgroup and the loads of a slice
+// are independent; the parts are then summed in a fixed order.
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void value_append_kernel(AppendArgs a) {
-  constexpr int TQ = 256 / D;       // positions sharing one output channel per pass
-  constexpr int NT = kGroupTokens / TQ;
+  constexpr int TQ = 256 / D;       // parts of the i range
+  constexpr int IQ = D / TQ;        // rows of R per part
   constexpr int W = D / 8;
   __shared__ double s_v[kGroupTokens][D];
+  __shared__ double s_r[TQ - 1][kGroupTokens][D];
   __shared__ double s_n[kGroupTokens];
   __shared__ uint8_t s_mod[kGroupTokens];
   __shared__ uint8_t s_code[kGroupTokens][D];
-  __shared__ int s_has[kModalities];
 
   const int b = blockIdx.z, h = blockIdx.y;
   const int sb = a.b0 + b;
@@ -190,7 +194,6 @@ __global__ __launch_bounds__(256) void value_append_kernel(AppendArgs a) {
   const int s_end = min(kGroupTokens, L_new - t0);
   const int tid = threadIdx.x;
 
-  if (tid < kModalities) s_has[tid] = 0;
   for (int idx = tid; idx < kGroupTokens * D; idx += 256) {
     const int s = idx / D, c = idx % D;
     if (s >= s_first && s < s_end) {
@@ -198,48 +201,64 @@ __global__ __launch_bounds__(256) void value_append_kernel(AppendArgs a) {
       s_v[s][c] = load_input<BF16>(a.v_new, src);
     }
   }
+  if (tid < kGroupTokens) {
+    const int s = tid;
+    if (s >= s_first && s < s_end) s_mod[s] = a.modality_new[static_cast<size_t>(b) * a.n_new + (t0 + s - L_old)];
+  }
   __syncthreads();
+  // Which modalities occur among the new positions (uniform across the block).
+  uint32_t present = 0;
+  for (int s = s_first; s < s_end; ++s) present |= (s_mod[s] < kModalities) ? (1u << s_mod[s]) : 0u;
   if (tid < kGroupTokens) {
     const int s = tid;
     if (s >= s_first && s < s_end) {
-      const uint8_t m = a.modality_new[static_cast<size_t>(b) * a.n_new + (t0 + s - L_old)];
-      s_mod[s] = m;
-      if (m < kModalities) s_has[m] = 1;
       double acc = 0.0;
       for (int c = 0; c < D; ++c) acc = acc + s_v[s][c] * s_v[s][c];
       s_n[s] = sqrt(acc);
     }
   }
-  __syncthreads();
 
-  // r_j = sum_i R_{h,m}[i][j] v_i  (R^T v), accumulated in fp64.
-  const int jc = tid % D, tq = tid / D;
-  double acc[NT];
+  const int jc = tid % D, part = tid / D;
+  const int i0 = part * IQ;
+  double acc[kGroupTokens];
 #pragma unroll
-  for (int k = 0; k < NT; ++k) acc[k] = 0.0;
+  for (int s = 0; s < kGroupTokens; ++s) acc[s] = 0.0;
   for (int m = 0; m < kModalities; ++m) {
-    if (!s_has[m]) continue;
-    const float* Rm = a.rot + (static_cast<size_t>(h) * kModalities + m) * D * D;
-    for (int i = 0; i < D; ++i) {
-      const double r = static_cast<double>(Rm[i * D + jc]);
+    if (!(present & (1u << m))) continue;
+    const float* Rm = a.rot + ((static_cast<size_t>(h) * kModalities + m) * D + i0) * D + jc;
+    for (int i = 0; i < IQ; i += 16) {
+      double r[16];
 #pragma unroll
-      for (int k = 0; k < NT; ++k) {
-        const int s = tq + k * TQ;
-        if (s >= s_first && s < s_end && s_mod[s] == m) acc[k] = fma(r, s_v[s][i], acc[k]);
+      for (int u = 0; u < 16; ++u) r[u] = static_cast<double>(Rm[(i + u) * D]);
+#pragma unroll
+      for (int s = 0; s < kGroupTokens; ++s) {
+        if (s >= s_first && s < s_end && s_mod[s] == m) {
+#pragma unroll
+          for (int u = 0; u < 16; ++u) acc[s] = fma(r[u], s_v[s][i0 + i + u], acc[s]);
+        }
       }
     }
   }
+  if (part > 0) {
 #pragma unroll
-  for (int k = 0; k < NT; ++k) {
-    const int s = tq + k * TQ;
-    if (s >= s_first && s < s_end) {
-      const double n = s_n[s];
-      uint32_t code = 0;
-      if (n > 0.0) {
-        const double z = (a.sqrt_d * acc[k]) / n;
-        code = (z >= a.thr0 ? 1u : 0u) + (z >= a.thr1 ? 1u : 0u) + (z >= a.thr2 ? 1u : 0u);
+    for (int s = 0; s < kGroupTokens; ++s)
+      if (s >= s_first && s < s_end) s_r[part - 1][s][jc] = acc[s];
+  }
+  __syncthreads();
+  if (part == 0) {
+#pragma unroll
+    for (int s = 0; s < kGroupTokens; ++s) {
+      if (s >= s_first && s < s_end) {
+        double r = acc[s];
+        for (int p = 1; p < TQ; ++p) r = r + s_r[p - 1][s][jc];
+        const double n = s_n[s];
+        uint32_t code = 0;
+        if (n > 0.0) {
+          const double z = (a.sqrt_d * r) / n;
+          code = (z >= a.thr0 ? 1u : 0u) + (z >= a.thr1 ? 1u : 0u) + (z >= a.thr2 ? 1u : 0u);
+        }
+        s_code[s][jc] = static_cast<uint8_t>(code);
       }
-      s_code[s][jc] = static_cast<uint8_t>(code);
     }
   }
   __syncthreads();

@@ -2,16 +2,35 @@
 // Sec. 1 Introduction, Implementation bullet; Abstract): the codes are
 // unpacked inside attention, scores use the already-rotated query, values are
 // aggregated per modality in their rotated frames, and the inverse value
-// rotations are applied once per modality after aggregation.
+// rotations are applied once per modality after aggregation.  No dense key or
+// value is ever written.
 //
-// Partition kernel: one wavefront per (session, KV head, context partition)
-// serves all G query heads of the KV head, streaming 32-position groups:
-//   score   s_t = scale * (sum_c q_c LO_c + sum_c (q_c (HI_c - LO_c)) l[code])
-//           with l[code] = (c[code] - c0) / (c3 - c0)
-//   softmax online (running max / sum per head, base-2 exponent)
-//   values  A_m += p_t (N_t / sqrt(d)) c[vcode]   (three accumulators per head)
-// Merge kernel: one workgroup per (session, query head) rescales and sums the
-// partitions, applies out = sum_m R_m A_m / l.
+// Partition kernel (one workgroup = NW wavefronts = one context partition of
+// one (session, KV head)).  Each wavefront takes one 32-position group at a
+// time and serves all G <= 16 query heads of the KV head on the matrix cores
+// (v_mfma_f32_16x16x32_f16):
+//
+//   codes -> fp16 operands through a 256-entry byte table in LDS (a copy per
+//            lane pair of banks, so lookups never conflict): one byte of four
+//            2-bit codes becomes four centred levels
+//            l = (2 c - c0 - c3) / (c3 - c0) in [-1, 1];
+//   keys    k_hat = mid + half * l with mid/half = (HI +- LO) / 2 per channel;
+//   scores  S^T[t][i] = sum_c mid_c q_ic + sum_c l_tc (q_ic half_c): rows = 16
+//           positions, columns = 16 query heads; the first sum from the stored
+//           fp16 LO/HI rows, the second with q~ = q * half split in two fp16
+//           halves, so the scores keep fp32-level accuracy;
+//   softmax online, base 2, per query head;
+//   values  A_m^T[c][.] += sum_t l_tc w_t (w = p * N_t): rows = 16 channels,
+//           columns = (modality slot, query head) pairs.  With G <= 5 the
+//           three modalities share one accumulator set, with G <= 8 two sets,
+//           else three: the score result already sits in the operand layout,
+//           and slot columns take their head's weights by a DPP row shift.
+// Value levels are c = cmid + chalf * l; sum_t w_t per modality is also kept
+// when the codebook is not symmetric (cmid != 0).
+//
+// Merge kernel: one workgroup per (session, query head, modality) rescales and
+// sums the partitions and applies R_m; the last of the three sums the three
+// rotated parts in fixed order (bitwise reproducible) and writes the output.
 #include "kvq_common.h"
 #include "kvq_internal.h"
 
@@ -19,235 +38,646 @@ namespace kvq {
 
 namespace {
 
-constexpr int kWaves = 4;
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTabCopies = 32;     // byte-table copies: lane l reads copy l % 32
 constexpr int kMaxSplits = 4096;
 
+__device__ __forceinline__ floatx4 mfma(const half8& a, const half8& b, const floatx4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Four fp16 levels of the four 2-bit codes of one byte of `word`.
+__device__ __forceinline__ uint2 lookup(const uint2* tab, uint32_t word, uint32_t sel, uint32_t lane_off) {
+  // v_perm_b32: result byte 0 = lane offset, byte 1 = the code byte, bytes 2..3 = 0
+  const uint32_t off = __builtin_amdgcn_perm(word, lane_off, sel);
+  return *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(tab) + off);
+}
+
+__device__ __forceinline__ half8 as_half8(uint2 lo, uint2 hi) {
+  uint4 v;
+  v.x = lo.x;
+  v.y = lo.y;
+  v.z = hi.x;
+  v.w = hi.y;
+  return __builtin_bit_cast(half8, v);
+}
+
+// Selector placing byte j (0..3) of the first operand at result byte 1.
+__device__ __forceinline__ constexpr uint32_t byte_sel(int j) { return 0x0C0C0000u | ((4u + j) << 8); }
+
+// Within each row of 16 lanes, lanes >= S take the value of lane - S.
+template <int S>
+__device__ __forceinline__ uint32_t row_shr(uint32_t old, uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(old), static_cast<int>(v),
+                                                           0x110 + S, 0xF, 0xF, false));
+}
+
+// Modality slots: the 16 value-accumulator columns are split into SLOTS slots
+// of GP columns; column c of set k holds head c % GP of modality k*SLOTS + c/GP.
+template <int SLOTS>
+struct Slots {
+  static constexpr int GP = SLOTS == 1 ? 16 : (SLOTS == 2 ? 8 : 5);
+  static constexpr int NSETS = (kModalities + SLOTS - 1) / SLOTS;
+};
+
+// Moves a value of score column (col % GP) to value column col.
+template <int SLOTS>
+__device__ __forceinline__ uint32_t to_value_column(uint32_t v) {
+  constexpr int GP = Slots<SLOTS>::GP;
+  if constexpr (SLOTS == 2) return row_shr<GP>(v, v);
+  if constexpr (SLOTS == 3) return row_shr<2 * GP>(row_shr<GP>(v, v), v);
+  return v;
+}
+
 template <int D>
-__global__ __launch_bounds__(256) void decode_partition_kernel(DecodeArgs a) {
-  constexpr int W = D / 8;
-  constexpr int CPL = D / 64;   // value channels per lane: c = lane + 64 k
-  constexpr int GM = kMaxGroupHeads;
-  __shared__ float s_q[GM][D];
-  __shared__ float s_qt[kWaves][GM][D];
-  __shared__ float s_w[kWaves][GM][kGroupTokens];
-  __shared__ __align__(16) uint8_t s_k[kWaves][8 * D];
-  __shared__ __align__(16) uint8_t s_v[kWaves][8 * D];
-  __shared__ float s_nrm[kWaves][kGroupTokens];
-  __shared__ uint8_t s_mod[kWaves][kGroupTokens];
+struct GroupLoad {
+  uint32_t kc[D / 32];   // lane-major key codes (D/8 bytes)
+  uint32_t vc[D / 32];   // lane-major value codes
+  uint32_t st[D / 64];   // this lane's share of the LO/HI rows (4D bytes per group)
+  uint2 nrm0, nrm1;      // fp16 norms of positions 4kg..4kg+3 and 16+4kg..16+4kg+3
+  uint32_t md0, md1;     // modality bytes of the same positions
+};
 
-  const int b = blockIdx.z, h = blockIdx.y;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int split = blockIdx.x * kWaves + wave;
-  const int G = a.group;
-  const int L = a.seq_len[b];
+// Issues the loads of the group at position t0 without branching (so the
+// compiler can count outstanding loads exactly): a group outside [0, te) or on
+// an unmapped page reads page 0 instead and is flagged invalid.
+template <int D>
+__device__ __forceinline__ void load_group(const DecodeArgs& a, int b, int h, int t0, int te, int lane, int kg,
+                                           GroupLoad<D>& g, bool& ok) {
+  const int page = t0 / a.page_tokens;
+  const int pg = min(page, a.max_pages - 1);
+  // The page table is read-only here: reading it through the constant address
+  // space makes this a scalar load, which does not wait on the vector loads
+  // already in flight.
+  const __attribute__((address_space(4))) int32_t* ptab =
+      (const __attribute__((address_space(4))) int32_t*)(a.page_table);
+  const int phys0 = ptab[static_cast<size_t>(b) * a.max_pages + pg];
+  ok = t0 < te && page < a.max_pages && phys0 >= 0 && phys0 < a.num_pages;
+  const int phys = ok ? phys0 : 0;
   const int gp = a.page_tokens / kGroupTokens;
+  const int tin = ok ? t0 % a.page_tokens : 0;
+  const size_t blk = (static_cast<size_t>(phys) * a.hkv + h) * gp + tin / kGroupTokens;
+  const uint32_t* kp = reinterpret_cast<const uint32_t*>(a.k_codes + blk * 8 * D) + lane * (D / 32);
+  const uint32_t* vp = reinterpret_cast<const uint32_t*>(a.v_codes + blk * 8 * D) + lane * (D / 32);
+  if constexpr (D == 128) {
+    const uint4 k4 = *reinterpret_cast<const uint4*>(kp);
+    const uint4 v4 = *reinterpret_cast<const uint4*>(vp);
+    g.kc[0] = k4.x; g.kc[1] = k4.y; g.kc[2] = k4.z; g.kc[3] = k4.w;
+    g.vc[0] = v4.x; g.vc[1] = v4.y; g.vc[2] = v4.z; g.vc[3] = v4.w;
+    const uint2 s2 = reinterpret_cast<const uint2*>(a.k_stats + blk * 2 * D)[lane];
+    g.st[0] = s2.x; g.st[1] = s2.y;
+  } else {
+    const uint2 k2 = *reinterpret_cast<const uint2*>(kp);
+    const uint2 v2 = *reinterpret_cast<const uint2*>(vp);
+    g.kc[0] = k2.x; g.kc[1] = k2.y;
+    g.vc[0] = v2.x; g.vc[1] = v2.y;
+    g.st[0] = reinterpret_cast<const uint32_t*>(a.k_stats + blk * 2 * D)[lane];
+  }
+  const uint16_t* np = a.v_norms + (static_cast<size_t>(phys) * a.hkv + h) * a.page_tokens + tin;
+  g.nrm0 = *reinterpret_cast<const uint2*>(np + 4 * kg);
+  g.nrm1 = *reinterpret_cast<const uint2*>(np + 16 + 4 * kg);
+  const uint8_t* mp = a.modality + static_cast<size_t>(phys) * a.page_tokens + tin;
+  g.md0 = *reinterpret_cast<const uint32_t*>(mp + 4 * kg);
+  g.md1 = *reinterpret_cast<const uint32_t*>(mp + 16 + 4 * kg);
+}
 
-  for (int idx = threadIdx.x; idx < G * D; idx += 256)
-    s_q[idx / D][idx % D] = a.q_rot[(static_cast<size_t>(b) * a.hq + h * G + idx / D) * D + idx % D];
-  __syncthreads();
+// Per-wavefront running state of one partition.
+template <int D, int SLOTS, bool ASYM>
+struct WaveState {
+  static constexpr int NSETS = Slots<SLOTS>::NSETS;
+  float m_run;                      // running max (base 2) of this lane's score head
+  float l_run;                      // this lane's share of the softmax denominator
+  floatx4 acc[NSETS][D / 16];       // value accumulators (columns = slot/head pairs)
+  floatx4 accs[ASYM ? NSETS : 1];   // sum of weights per column (non-symmetric codebook)
+  int mask;                         // modalities that received weight
+};
 
-  float m_run[GM], l_run[GM], acc[GM][kModalities][CPL];
+__device__ __forceinline__ int group_pos(int kg, int i) { return (i < 4) ? (4 * kg + i) : (16 + 4 * kg + i - 4); }
+
+// Exact fp32 difference of fp16 fields (low or high half) of two registers.
+__device__ __forceinline__ float f16_diff_lo(uint32_t a2, uint32_t b2) {
+  float d;
+  asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel_hi:[1,0,1]" : "=v"(d) : "v"(a2), "v"(b2));
+  return d;
+}
+__device__ __forceinline__ float f16_diff_hi(uint32_t a2, uint32_t b2) {
+  float d;
+  asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel:[1,0,1] op_sel_hi:[1,0,1]" : "=v"(d) : "v"(a2), "v"(b2));
+  return d;
+}
+
+// FULL: all 32 positions of the group are inside the partition.
+template <int D, int SLOTS, bool ASYM, bool FULL>
+__device__ __forceinline__ void process_group(const GroupLoad<D>& cur, int t0, int te, int kg, int col,
+                                              int lane, const uint2* tab, uint16_t* st_lds, uint32_t lane_off,
+                                              const float (&hq)[D / 32][8], const half8 (&bq_hi)[D / 32],
+                                              const half8 (&bq_lo)[D / 32], WaveState<D, SLOTS, ASYM>& ws) {
+  constexpr int KT = D / 32;
+  constexpr int CT = D / 16;
+  constexpr int GP = Slots<SLOTS>::GP;
+  constexpr int NSETS = Slots<SLOTS>::NSETS;
+
+  // Stage LO / HI rows; each lane then reads the 8-channel runs it needs.
+  if constexpr (D == 128) {
+    reinterpret_cast<uint2*>(st_lds)[lane] = uint2{cur.st[0], cur.st[1]};
+  } else {
+    reinterpret_cast<uint32_t*>(st_lds)[lane] = cur.st[0];
+  }
+  wave_sync();
+  // Group bias sum_c q_c (LO_c + HI_c) / 2 (identical in every row) and
+  // q~ = q (HI - LO) / 2 split into fp16 hi + lo, one K-tile at a time.
+  floatx4 b0 = {0.f, 0.f, 0.f, 0.f}, b1 = {0.f, 0.f, 0.f, 0.f};
+  half8 qt_hi[KT], qt_lo[KT];
 #pragma unroll
-  for (int hh = 0; hh < GM; ++hh) {
-    m_run[hh] = -__builtin_inff();
-    l_run[hh] = 0.f;
+  for (int kt = 0; kt < KT; ++kt) {
+    const uint4 lo4 = *reinterpret_cast<const uint4*>(st_lds + 32 * kt + 8 * kg);
+    const uint4 hi4 = *reinterpret_cast<const uint4*>(st_lds + D + 32 * kt + 8 * kg);
+    const half8 lo8 = __builtin_bit_cast(half8, lo4);
+    const half8 hi8 = __builtin_bit_cast(half8, hi4);
+    b0 = mfma(lo8, bq_hi[kt], b0);
+    b1 = mfma(lo8, bq_lo[kt], b1);
+    b0 = mfma(hi8, bq_hi[kt], b0);
+    b1 = mfma(hi8, bq_lo[kt], b1);
+    const uint32_t lw[4] = {lo4.x, lo4.y, lo4.z, lo4.w};
+    const uint32_t hw[4] = {hi4.x, hi4.y, hi4.z, hi4.w};
 #pragma unroll
-    for (int m = 0; m < kModalities; ++m)
+    for (int i = 0; i < 8; ++i) {
+      const float diff = (i & 1) ? f16_diff_hi(hw[i >> 1], lw[i >> 1]) : f16_diff_lo(hw[i >> 1], lw[i >> 1]);
+      const float qt = hq[kt][i] * diff;
+      const _Float16 h16 = static_cast<_Float16>(qt);
+      qt_hi[kt][i] = h16;
+      qt_lo[kt][i] = static_cast<_Float16>(qt - static_cast<float>(h16));
+    }
+  }
+  wave_sync();   // the LDS staging may be overwritten by the next group
+
+  // Scores for positions 16 mt + 4 kg + j of head `col`.
+  floatx4 sc[2];
 #pragma unroll
-      for (int k = 0; k < CPL; ++k) acc[hh][m][k] = 0.f;
+  for (int mt = 0; mt < 2; ++mt) {
+    floatx4 s_hi = b0, s_lo = b1;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      const int j0 = mt * (D / 16) + kt * 2;   // code bytes j0, j0 + 1 of this (mt, kt)
+      const uint2 x0 = lookup(tab, cur.kc[j0 >> 2], byte_sel(j0 & 3), lane_off);
+      const uint2 x1 = lookup(tab, cur.kc[(j0 + 1) >> 2], byte_sel((j0 + 1) & 3), lane_off);
+      const half8 ak = as_half8(x0, x1);
+      s_hi = mfma(ak, qt_hi[kt], s_hi);
+      s_lo = mfma(ak, qt_lo[kt], s_lo);
+    }
+    sc[mt] = s_hi + s_lo;
   }
 
-  // The last partition runs to the session's current length, so a launch
-  // planned for a shorter context (e.g. replayed from a captured graph while
-  // the cache grows) still covers every cached position.
-  const int tb = split * a.split_tokens;
-  const int te = (split == a.splits - 1) ? L : min(tb + a.split_tokens, L);
-  const int tok = lane & 31, half = lane >> 5;
-
-  for (int t0 = tb; t0 < te; t0 += kGroupTokens) {
-    const int page = t0 / a.page_tokens;
-    const int phys = page < a.max_pages ? a.page_table[static_cast<size_t>(b) * a.max_pages + page] : -1;
-    if (phys < 0 || phys >= a.num_pages) continue;   // unmapped page: nothing to read
-    const size_t blk = (static_cast<size_t>(phys) * a.hkv + h) * gp + (t0 % a.page_tokens) / kGroupTokens;
-    const size_t prow = (static_cast<size_t>(phys) * a.hkv + h) * a.page_tokens + (t0 % a.page_tokens);
-
-    // Stage the group's key / value code blocks, norms and modalities.
-    if (lane * 16 < 8 * D) {
-      reinterpret_cast<uint4*>(s_k[wave])[lane] = reinterpret_cast<const uint4*>(a.k_codes + blk * 8 * D)[lane];
-      reinterpret_cast<uint4*>(s_v[wave])[lane] = reinterpret_cast<const uint4*>(a.v_codes + blk * 8 * D)[lane];
+  // Online softmax (base 2) for head `col` over this group's positions.
+  bool valid[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) valid[i] = FULL || t0 + group_pos(kg, i) < te;
+  float mx = -__builtin_inff();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) mx = valid[i] ? fmaxf(mx, sc[i >> 2][i & 3]) : mx;
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(ws.m_run, mx);
+  if (__any(m_new > ws.m_run)) {
+    const float alpha = exp2f(ws.m_run - m_new);   // 0 on the first group
+    ws.l_run *= alpha;
+    const float alpha_v = __uint_as_float(to_value_column<SLOTS>(__float_as_uint(alpha)));
+#pragma unroll
+    for (int k = 0; k < NSETS; ++k) {
+      if constexpr (ASYM) ws.accs[k] *= alpha_v;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) ws.acc[k][ct] *= alpha_v;
     }
-    if (lane < kGroupTokens) {
-      const bool ok = t0 + lane < te;
-      s_nrm[wave][lane] = ok ? f16_bits_to_f32(a.v_norms[prow + lane]) * a.value_scale : 0.f;
-      s_mod[wave][lane] = ok ? a.modality[static_cast<size_t>(phys) * a.page_tokens + (t0 % a.page_tokens) + lane] : 0;
-    }
-
-    // Fold the group statistics into the query: q~ = q (HI - LO), bias = q . LO.
-    float lo[CPL], dl[CPL];
+    ws.m_run = m_new;
+  }
+  const uint32_t n4[4] = {cur.nrm0.x, cur.nrm0.y, cur.nrm1.x, cur.nrm1.y};
+  uint32_t wp[4];   // fp16 weights p * N of the lane's 8 positions, two per register
 #pragma unroll
-    for (int k = 0; k < CPL; ++k) {
-      const int c = lane + 64 * k;
-      const float LO = f16_bits_to_f32(a.k_stats[blk * 2 * D + c]);
-      const float HI = f16_bits_to_f32(a.k_stats[blk * 2 * D + D + c]);
-      lo[k] = LO;
-      dl[k] = HI - LO;
-    }
-    float bias[GM];
+  for (int r = 0; r < 4; ++r) {
+    float w2[2];
 #pragma unroll
-    for (int hh = 0; hh < GM; ++hh) {
-      bias[hh] = 0.f;
-      if (hh < G) {
-        float p = 0.f;
-#pragma unroll
-        for (int k = 0; k < CPL; ++k) {
-          const int c = lane + 64 * k;
-          p += s_q[hh][c] * lo[k];
-          s_qt[wave][hh][c] = s_q[hh][c] * dl[k];
-        }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) p += __shfl_xor(p, off);
-        bias[hh] = p;
+    for (int u = 0; u < 2; ++u) {
+      const int i = 2 * r + u;
+      // arguments are <= 0: the raw base-2 exponential flushes only results below 2^-126
+      const float p = __builtin_amdgcn_exp2f(sc[i >> 2][i & 3] - ws.m_run);
+      const float nrm = f16_bits_to_f32(static_cast<uint16_t>(n4[r] >> (16 * u)));
+      if constexpr (FULL) {
+        ws.l_run += p;
+        w2[u] = p * nrm;
+      } else {
+        ws.l_run += valid[i] ? p : 0.f;
+        w2[u] = valid[i] ? p * nrm : 0.f;
       }
     }
-    wave_sync();
-
-    // Scores: lane = (position tok, channel half).
-    float sc[GM];
-#pragma unroll
-    for (int hh = 0; hh < GM; ++hh) sc[hh] = 0.f;
-    for (int cc = 0; cc < D / 2; ++cc) {
-      const int c = half * (D / 2) + cc;
-      const uint32_t code = (s_k[wave][key_code_byte<D>(tok, c)] >> (2 * (c & 3))) & 3u;
-      const float lv = a.lv[code];
-#pragma unroll
-      for (int hh = 0; hh < GM; ++hh)
-        if (hh < G) sc[hh] += s_qt[wave][hh][c] * lv;
-    }
-    const bool valid = t0 + tok < te;
-#pragma unroll
-    for (int hh = 0; hh < GM; ++hh) {
-      if (hh < G) {
-        const float s = (sc[hh] + __shfl_xor(sc[hh], 32) + bias[hh]) * a.scale_log2e;
-        float mx = valid ? s : -__builtin_inff();
-#pragma unroll
-        for (int off = 16; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-        const float m_new = fmaxf(m_run[hh], mx);
-        const float alpha = exp2f(m_run[hh] - m_new);   // 0 when m_run is -inf
-        const float p = valid ? exp2f(s - m_new) : 0.f;
-        float ps = p;
-#pragma unroll
-        for (int off = 16; off > 0; off >>= 1) ps += __shfl_xor(ps, off);
-        l_run[hh] = l_run[hh] * alpha + ps;
-        m_run[hh] = m_new;
-#pragma unroll
-        for (int m = 0; m < kModalities; ++m)
-#pragma unroll
-          for (int k = 0; k < CPL; ++k) acc[hh][m][k] *= alpha;
-        if (lane < kGroupTokens) s_w[wave][hh][tok] = p * s_nrm[wave][tok];
-      }
-    }
-    wave_sync();
-
-    // Values: lane = channels lane + 64 k; loop over the group's positions.
-    const int nt = min(kGroupTokens, te - t0);
-    for (int tt = 0; tt < nt; ++tt) {
-      const int m = s_mod[wave][tt];
-      float cv[CPL];
-#pragma unroll
-      for (int k = 0; k < CPL; ++k) {
-        const int c = lane + 64 * k;
-        const uint32_t code = (s_v[wave][value_code_byte<D>(tt, c)] >> (2 * (tt & 3))) & 3u;
-        cv[k] = a.cv[code];
-      }
-#pragma unroll
-      for (int hh = 0; hh < GM; ++hh) {
-        if (hh < G) {
-          const float w = s_w[wave][hh][tt];
-#pragma unroll
-          for (int k = 0; k < CPL; ++k) {
-            if (m == 0) acc[hh][0][k] += w * cv[k];
-            else if (m == 1) acc[hh][1][k] += w * cv[k];
-            else acc[hh][2][k] += w * cv[k];
-          }
-        }
-      }
-    }
-    wave_sync();
+    const half2v hw2 = {static_cast<_Float16>(w2[0]), static_cast<_Float16>(w2[1])};
+    wp[r] = to_value_column<SLOTS>(__builtin_bit_cast(uint32_t, hw2));
   }
 
-  // Partial result of this partition for each query head of the group.
-  constexpr int PS = 2 + kModalities * D;
+  // Value operands: rows = channels 16 ct + col, k = the positions of the scores.
+  half8 av[CT];
 #pragma unroll
-  for (int hh = 0; hh < GM; ++hh) {
-    if (hh < G) {
-      float* part = a.partials + ((static_cast<size_t>(b) * a.hq + h * G + hh) * a.splits + split) * PS;
-      if (lane == 0) {
-        part[0] = m_run[hh];
-        part[1] = l_run[hh];
+  for (int ct = 0; ct < CT; ++ct) {
+    const int j0 = 2 * ct;
+    const uint2 x0 = lookup(tab, cur.vc[j0 >> 2], byte_sel(j0 & 3), lane_off);
+    const uint2 x1 = lookup(tab, cur.vc[(j0 + 1) >> 2], byte_sel((j0 + 1) & 3), lane_off);
+    av[ct] = as_half8(x0, x1);
+  }
+
+  // Accumulate each modality set whose modalities occur in the group.
+  const int slot = col / GP;
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(cur.md0 & 0xFFu);
+  const bool uniform = FULL && __all(cur.md0 == m0 * 0x01010101u && cur.md1 == m0 * 0x01010101u);
+  const uint32_t md[2] = {cur.md0, cur.md1};
+#pragma unroll
+  for (int k = 0; k < NSETS; ++k) {
+    const uint32_t lo_mod = static_cast<uint32_t>(k * SLOTS);
+    const uint32_t my_mod = lo_mod + static_cast<uint32_t>(slot);   // this column's modality
+    const bool col_ok = slot < SLOTS && my_mod < kModalities;
+    bool present;
+    uint32_t bm[4];
+    int got = 0;   // modalities of this set that receive weight
+    if (uniform) {
+      present = m0 >= lo_mod && m0 < lo_mod + SLOTS && m0 < kModalities;
+      got = present ? (1 << m0) : 0;
+      const bool take = col_ok && my_mod == m0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) bm[r] = take ? wp[r] : 0u;
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        uint32_t keep = 0;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int i = 2 * r + u;
+          const uint32_t tm = (md[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+          if (valid[i] && tm >= lo_mod && tm < lo_mod + SLOTS && tm < kModalities) got |= 1 << tm;
+          keep |= (col_ok && tm == my_mod) ? (0xFFFFu << (16 * u)) : 0u;
+        }
+        bm[r] = wp[r] & keep;
       }
+      present = __any(got != 0);
+    }
+    if (present) {
+      const half8 bw = __builtin_bit_cast(half8, uint4{bm[0], bm[1], bm[2], bm[3]});
 #pragma unroll
-      for (int m = 0; m < kModalities; ++m)
-#pragma unroll
-        for (int k = 0; k < CPL; ++k) part[2 + m * D + lane + 64 * k] = acc[hh][m][k];
+      for (int ct = 0; ct < CT; ++ct) ws.acc[k][ct] = mfma(av[ct], bw, ws.acc[k][ct]);
+      if constexpr (ASYM) {
+        const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
+        ws.accs[k] = mfma(ones, bw, ws.accs[k]);
+      }
+      ws.mask |= got;
     }
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
-  constexpr int PS = 2 + kModalities * D;
-  __shared__ float s_e[kMaxSplits];
-  __shared__ float s_A[kModalities][D];
-  __shared__ float s_red[256];
-  const int i = blockIdx.x, b = blockIdx.y;
-  const int h = i / a.group;
-  const int tid = threadIdx.x;
-  const float* P = a.partials + (static_cast<size_t>(b) * a.hq + i) * a.splits * PS;
+template <int D, int SLOTS, int NW, bool ASYM>
+__global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeArgs a) {
+  constexpr int KT = D / 32;
+  constexpr int CT = D / 16;
+  constexpr int GP = Slots<SLOTS>::GP;
+  constexpr int NSETS = Slots<SLOTS>::NSETS;
+  constexpr int PS = kPartialHeader + kModalities * D;
+  constexpr int kPrefetch = 2;     // groups in flight per wavefront
+  struct Merge {
+    float4 tree[NW / 2][NSETS][CT][64];   // wavefront accumulators handed down the reduction tree
+    float m[NW][kMaxGroupHeads];
+    float l[NW][kMaxGroupHeads];
+    float s[NW][kModalities][kMaxGroupHeads];
+    int mask;
+  };
+  union Smem {
+    struct {
+      uint2 tab[256 * kTabCopies];       // 64 KB: entry e, copy c at byte e*256 + c*8
+      uint16_t stats[NW][2][D];          // per-wave staging of one group's LO / HI rows
+    } s;
+    Merge merge;
+  };
+  __shared__ Smem sm;
 
-  float mx = -__builtin_inff();
-  for (int s = tid; s < a.splits; s += 256) mx = fmaxf(mx, P[static_cast<size_t>(s) * PS]);
-  s_red[tid] = mx;
-  __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
-    if (tid < off) s_red[tid] = fmaxf(s_red[tid], s_red[tid + off]);
-    __syncthreads();
-  }
-  const float M = s_red[0];
-  __syncthreads();
-  float ls = 0.f;
-  for (int s = tid; s < a.splits; s += 256) {
-    const float ms = P[static_cast<size_t>(s) * PS];
-    const float e = (ms == -__builtin_inff()) ? 0.f : exp2f(ms - M);
-    s_e[s] = e;
-    ls += e * P[static_cast<size_t>(s) * PS + 1];
-  }
-  s_red[tid] = ls;
-  __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
-    if (tid < off) s_red[tid] += s_red[tid + off];
-    __syncthreads();
-  }
-  const float l = s_red[0];
-  for (int idx = tid; idx < kModalities * D; idx += 256) {
-    float A = 0.f;
-    for (int s = 0; s < a.splits; ++s) A += s_e[s] * P[static_cast<size_t>(s) * PS + 2 + idx];
-    s_A[idx / D][idx % D] = A;
-  }
-  __syncthreads();
-  if (tid < D) {
-    float o = 0.f;
-    for (int m = 0; m < kModalities; ++m) {
-      const float* R = a.rot + ((static_cast<size_t>(h) * kModalities + m) * D + tid) * D;
-      for (int j = 0; j < D; ++j) o += R[j] * s_A[m][j];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar) index
+  const int kg = lane >> 4, col = lane & 15;
+  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int G = a.group;
+  const int L = a.seq_len[b];
+
+  // The merge kernel's completion counters start from zero every launch.
+  if (split == 0 && h == 0 && b == 0)
+    for (int i = tid; i < a.counters_len; i += NW * 64) a.counters[i] = 0;
+
+  // Byte table: one copy per lane of a 32-lane half wave.
+  for (int i = tid; i < 256 * kTabCopies; i += NW * 64) sm.s.tab[i] = a.byte_levels[i / kTabCopies];
+
+  // This lane's score head (padding columns reuse the last head; ignored):
+  // q * scale * log2(e) / 2 on channels 32kt + 8kg + i, in fp32 and as an
+  // fp16 pair hi + lo (the bias operand).
+  const int qh = h * G + min(col, G - 1);
+  const float* qp = a.q_rot + (static_cast<size_t>(b) * a.hq + qh) * D;
+  float hq[KT][8];
+  half8 bq_hi[KT], bq_lo[KT];
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float v = qp[32 * kt + 8 * kg + i] * a.scale_log2e * 0.5f;
+      hq[kt][i] = v;
+      const _Float16 hi = static_cast<_Float16>(v);
+      bq_hi[kt][i] = hi;
+      bq_lo[kt][i] = static_cast<_Float16>(v - static_cast<float>(hi));
     }
-    a.out[(static_cast<size_t>(b) * a.hq + i) * D + tid] = (l > 0.f) ? o / l : 0.f;
   }
+
+  const int tb = split * a.split_tokens;
+  const int te = (split == a.splits - 1) ? L : min(tb + a.split_tokens, L);
+  const uint32_t lane_off = static_cast<uint32_t>(lane & (kTabCopies - 1)) << 3;
+
+  WaveState<D, SLOTS, ASYM> ws;
+  ws.m_run = -__builtin_inff();
+  ws.l_run = 0.f;
+  ws.mask = 0;
+#pragma unroll
+  for (int k = 0; k < NSETS; ++k) {
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) ws.acc[k][ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int k = 0; k < (ASYM ? NSETS : 1); ++k) ws.accs[k] = floatx4{0.f, 0.f, 0.f, 0.f};
+  __syncthreads();
+
+  const uint2* tab = sm.s.tab;
+  uint16_t* st_lds = &sm.s.stats[wave][0][0];
+
+  // Prefetch ring over the partition's full groups: each wavefront keeps
+  // kPrefetch groups in flight.  The one partial group a partition can end
+  // with (the session's last) is handled after the loop.
+  const int te_full = te & ~(kGroupTokens - 1);   // tb is a multiple of 32
+  GroupLoad<D> buf[kPrefetch];
+  bool ok[kPrefetch];
+  const int stride = NW * kGroupTokens;
+  const int first = tb + wave * kGroupTokens;
+#pragma unroll
+  for (int k = 0; k < kPrefetch; ++k) load_group<D>(a, b, h, first + k * stride, te_full, lane, kg, buf[k], ok[k]);
+  for (int base = first; base < te_full; base += kPrefetch * stride) {
+#pragma unroll
+    for (int k = 0; k < kPrefetch; ++k) {
+      if (ok[k])
+        process_group<D, SLOTS, ASYM, true>(buf[k], base + k * stride, te, kg, col, lane, tab, st_lds, lane_off,
+                                            hq, bq_hi, bq_lo, ws);
+      load_group<D>(a, b, h, base + (k + kPrefetch) * stride, te_full, lane, kg, buf[k], ok[k]);
+    }
+  }
+  if (te_full >= tb && te_full < te && ((te_full - tb) / kGroupTokens) % NW == wave) {
+    load_group<D>(a, b, h, te_full, te, lane, kg, buf[0], ok[0]);
+    if (ok[0])
+      process_group<D, SLOTS, ASYM, false>(buf[0], te_full, te, kg, col, lane, tab, st_lds, lane_off, hq, bq_hi,
+                                           bq_lo, ws);
+  }
+
+  // ---- merge the wavefronts of the workgroup, write one partial per query head
+  ws.l_run += __shfl_xor(ws.l_run, 16);
+  ws.l_run += __shfl_xor(ws.l_run, 32);
+  __syncthreads();   // the byte table is dead from here on
+  Merge& ms = sm.merge;
+  if (tid == 0) ms.mask = 0;
+  const int slot = col / GP, hp = col % GP;
+  if (kg == 0) {
+    ms.m[wave][col] = ws.m_run;
+    ms.l[wave][col] = ws.l_run;
+    if (slot < SLOTS) {
+#pragma unroll
+      for (int k = 0; k < NSETS; ++k) {
+        const int m = k * SLOTS + slot;
+        if (m < kModalities) ms.s[wave][m][hp] = ASYM ? ws.accs[ASYM ? k : 0][0] : 0.f;
+      }
+    }
+  }
+  __syncthreads();
+  if (ws.mask) atomicOr(&ms.mask, ws.mask);
+  // Bring the value columns (head hp) to the workgroup max of that head, then
+  // sum the wavefronts pairwise down a fixed tree (bitwise reproducible).
+  float M = -__builtin_inff();
+  for (int w = 0; w < NW; ++w) M = fmaxf(M, ms.m[w][hp]);
+  const float mw = ms.m[wave][hp];
+  const float e = (mw == -__builtin_inff()) ? 0.f : exp2f(mw - M);
+#pragma unroll
+  for (int k = 0; k < NSETS; ++k)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) ws.acc[k][ct] *= e;
+#pragma unroll
+  for (int half = NW / 2; half >= 1; half >>= 1) {
+    if (wave >= half && wave < 2 * half) {
+#pragma unroll
+      for (int k = 0; k < NSETS; ++k)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          const floatx4 v = ws.acc[k][ct];
+          ms.tree[wave - half][k][ct][lane] = float4{v[0], v[1], v[2], v[3]};
+        }
+    }
+    __syncthreads();
+    if (wave < half) {
+#pragma unroll
+      for (int k = 0; k < NSETS; ++k)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          const float4 v = ms.tree[wave][k][ct][lane];
+          ws.acc[k][ct] += floatx4{v.x, v.y, v.z, v.w};
+        }
+    }
+    __syncthreads();
+  }
+  const int wmask = ms.mask;
+  if (wave == 0 && slot < SLOTS && hp < G) {
+    float* part = a.partials + ((static_cast<size_t>(b) * a.hq + h * G + hp) * a.splits + split) * PS;
+#pragma unroll
+    for (int k = 0; k < NSETS; ++k) {
+      const int m = k * SLOTS + slot;
+      if (m < kModalities && (wmask & (1 << m))) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          const floatx4 v = ws.acc[k][ct];
+          *reinterpret_cast<float4*>(part + kPartialHeader + m * D + 16 * ct + 4 * kg) = float4{v[0], v[1], v[2], v[3]};
+        }
+      }
+    }
+  }
+  if (tid < G * kPartialHeader) {
+    const int hh = tid / kPartialHeader, f = tid % kPartialHeader;
+    float* part = a.partials + ((static_cast<size_t>(b) * a.hq + h * G + hh) * a.splits + split) * PS;
+    float Mh = -__builtin_inff();
+    for (int w = 0; w < NW; ++w) Mh = fmaxf(Mh, ms.m[w][hh]);
+    float v = 0.f;
+    if (f == 0) {
+      v = Mh;
+    } else if (f == 1 || (f >= 4 && f < 4 + kModalities)) {
+      for (int w = 0; w < NW; ++w) {
+        const float mww = ms.m[w][hh];
+        if (mww != -__builtin_inff()) v += exp2f(mww - Mh) * (f == 1 ? ms.l[w][hh] : ms.s[w][f - 4][hh]);
+      }
+    } else if (f == 2) {
+      v = __int_as_float(wmask);
+    }
+    part[f] = v;
+  }
+}
+
+// One workgroup per (session, query head, modality m): weighted sum of the
+// partitions' modality-m accumulators, then R_m times it; the last of the
+// three workgroups of a head adds the three rotated parts in modality order.
+constexpr int kMergeThreads = 256;
+
+template <int D>
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs a) {
+  constexpr int PS = kPartialHeader + kModalities * D;
+  constexpr int F4 = D / 4;                      // float4 per accumulator block
+  constexpr int SG = kMergeThreads / F4;         // split subsets
+  constexpr int NQ = kMergeThreads / D;          // threads per output row
+  constexpr int JQ = D / NQ;                     // columns per thread
+  __shared__ float s_e[kMaxSplits];
+  __shared__ float4 s_part[SG][F4];
+  __shared__ float s_A[D];
+  __shared__ float s_red[kMergeThreads / 64][3];
+  __shared__ int s_mask;
+  __shared__ int s_last;
+  const int i = blockIdx.x, b = blockIdx.y, m = blockIdx.z;
+  const int h = i / a.group;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int S = a.splits;
+  const size_t head = static_cast<size_t>(b) * a.hq + i;
+  const float* P = a.partials + head * static_cast<size_t>(S) * PS;
+
+  // Headers: global max, weights, denominator, modality mask.
+  float mx = -__builtin_inff();
+  for (int s = tid; s < S; s += kMergeThreads) mx = fmaxf(mx, P[static_cast<size_t>(s) * PS]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if (lane == 0) s_red[wave][0] = mx;
+  if (tid == 0) s_mask = 0;
+  __syncthreads();
+  float M = -__builtin_inff();
+#pragma unroll
+  for (int w = 0; w < kMergeThreads / 64; ++w) M = fmaxf(M, s_red[w][0]);
+  __syncthreads();
+  float ls = 0.f, ss = 0.f;
+  int mk = 0;
+  for (int s = tid; s < S; s += kMergeThreads) {
+    const float* ph = P + static_cast<size_t>(s) * PS;
+    const float ms = ph[0];
+    const float e = (ms == -__builtin_inff()) ? 0.f : exp2f(ms - M);
+    const int pm = e > 0.f ? __float_as_int(ph[2]) : 0;
+    s_e[s] = (pm & (1 << m)) ? e : 0.f;
+    ls += e * ph[1];
+    ss += (pm & (1 << m)) ? e * ph[4 + m] : 0.f;
+    mk |= pm;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    ls += __shfl_xor(ls, off);
+    ss += __shfl_xor(ss, off);
+  }
+  if (mk) atomicOr(&s_mask, mk);
+  if (lane == 0) {
+    s_red[wave][1] = ls;
+    s_red[wave][2] = ss;
+  }
+  __syncthreads();
+  float l = 0.f, Sm = 0.f;
+#pragma unroll
+  for (int w = 0; w < kMergeThreads / 64; ++w) {
+    l += s_red[w][1];
+    Sm += s_red[w][2];
+  }
+  const bool have = (s_mask >> m) & 1;
+
+  float* out3 = a.partials + static_cast<size_t>(a.batch) * a.hq * S * PS;   // [B][Hq][3][D]
+  float* mine = out3 + (head * kModalities + m) * D;
+  if (have) {
+    // Weighted sum of the modality-m blocks: thread -> (float4 column, split subset).
+    {
+      const int f4 = tid % F4, sg = tid / F4;
+      float4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+      for (int s = sg; s < S; s += SG) {
+        const float e = s_e[s];
+        if (e > 0.f) {
+          const float4 v = reinterpret_cast<const float4*>(P + static_cast<size_t>(s) * PS + kPartialHeader +
+                                                           m * D)[f4];
+          acc.x += e * v.x;
+          acc.y += e * v.y;
+          acc.z += e * v.z;
+          acc.w += e * v.w;
+        }
+      }
+      s_part[sg][f4] = acc;
+    }
+    __syncthreads();
+    if (tid < F4) {
+      float4 v = s_part[0][tid];
+#pragma unroll
+      for (int g = 1; g < SG; ++g) {
+        v.x += s_part[g][tid].x;
+        v.y += s_part[g][tid].y;
+        v.z += s_part[g][tid].z;
+        v.w += s_part[g][tid].w;
+      }
+      s_A[4 * tid + 0] = v.x;
+      s_A[4 * tid + 1] = v.y;
+      s_A[4 * tid + 2] = v.z;
+      s_A[4 * tid + 3] = v.w;
+    }
+    __syncthreads();
+    // R_m times the accumulator: NQ threads per row, JQ columns each.
+    const int row = tid / NQ, q = tid % NQ;
+    const float4* R = reinterpret_cast<const float4*>(
+        a.rot + ((static_cast<size_t>(h) * kModalities + m) * D + row) * D + q * JQ);
+    float acc = 0.f, rs = 0.f;
+#pragma unroll
+    for (int j4 = 0; j4 < JQ / 4; ++j4) {
+      const float4 r = R[j4];
+      const float* A = &s_A[q * JQ + 4 * j4];
+      acc += r.x * A[0] + r.y * A[1] + r.z * A[2] + r.w * A[3];
+      rs += r.x + r.y + r.z + r.w;
+    }
+#pragma unroll
+    for (int off = 1; off < NQ; off <<= 1) {
+      acc += __shfl_xor(acc, off);
+      rs += __shfl_xor(rs, off);
+    }
+    if (q == 0) mine[row] = (l > 0.f) ? (a.chalf * acc + a.cmid * Sm * rs) * (a.value_scale / l) : 0.f;
+  } else {
+    for (int r = tid; r < D; r += kMergeThreads) mine[r] = 0.f;
+  }
+
+  // The last of the three modality workgroups writes out = part_0 + part_1 + part_2.
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) s_last = atomicAdd(&a.counters[head], 1) == kModalities - 1;
+  __syncthreads();
+  if (s_last) {
+    __threadfence();
+    const float* p3 = out3 + head * kModalities * D;
+    for (int r = tid; r < D; r += kMergeThreads) a.out[head * D + r] = (p3[r] + p3[D + r]) + p3[2 * D + r];
+  }
+}
+
+template <int D, int SLOTS, int NW>
+void launch_partition(int batch, const DecodeArgs& a, hipStream_t s) {
+  const dim3 grid(a.splits, a.hkv, batch);
+  if (a.cmid != 0.f)
+    hipLaunchKernelGGL((decode_partition_kernel<D, SLOTS, NW, true>), grid, dim3(NW * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_partition_kernel<D, SLOTS, NW, false>), grid, dim3(NW * 64), 0, s, a);
 }
 
 template <int D>
 hipError_t launch_decode_t(int batch, const DecodeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((decode_partition_kernel<D>), dim3(a.splits / kWaves, a.hkv, batch), dim3(256), 0, s, a);
-  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(a.hq, batch), dim3(256), 0, s, a);
+  if (a.group <= 5) launch_partition<D, 3, kDecodeWaves>(batch, a, s);
+  else if (a.group <= 8) launch_partition<D, 2, kDecodeWaves>(batch, a, s);
+  else launch_partition<D, 1, kDecodeWaves / 2>(batch, a, s);
+  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(a.hq, batch, kModalities), dim3(kMergeThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -42,6 +42,16 @@ struct RotateArgs {
   double inv_sqrt_d;
 };
 
+// Decode partitions: a workgroup of kDecodeWaves wavefronts streams one
+// contiguous range of 32-position groups of one (session, KV head) and writes
+// one partial result per query head of the group:
+//   [0] running max (base-2 units)  [1] softmax denominator
+//   [2] bit mask of modalities with value mass  [3] unused
+//   [4..6] per-modality weight sums (only needed for a non-symmetric codebook)
+//   [7] unused, then [3][d] per-modality value accumulators.
+constexpr int kDecodeWaves = 8;
+constexpr int kPartialHeader = 8;
+
 struct DecodeArgs {
   const uint8_t* k_codes;
   const uint16_t* k_stats;
@@ -53,14 +63,19 @@ struct DecodeArgs {
   const float* q_rot;
   const float* rot;
   float* out;
-  float* partials;        // [B][Hq][splits][2 + 3d]
+  float* partials;        // workspace: [B][Hq][splits][kPartialHeader + 3d] partials,
+                          // then [B][Hq][3][d] rotated per-modality parts
+  int32_t* counters;      // workspace tail: [B][Hq] completion counters of the merge
+  int32_t counters_len;
+  int32_t batch;
   int32_t hq, hkv, group, page_tokens, max_pages, num_pages;
   int32_t splits;         // partitions per (session, KV head)
-  int32_t split_tokens;   // positions per partition (multiple of 32)
+  int32_t split_tokens;   // positions per partition (multiple of 32 * kDecodeWaves)
   float scale_log2e;      // softmax scale * log2(e)
   float value_scale;      // 1 / sqrt(d)
-  float lv[4];            // key levels mapped to [0, 1]: (c_k - c0) / (c3 - c0)
-  float cv[4];            // value levels c_k
+  float cmid, chalf;      // codebook centre (c0 + c3) / 2 and half range (c3 - c0) / 2
+  uint32_t level_f16[2];  // normalized levels (2 c_k - c0 - c3) / (c3 - c0) as fp16 bits, k = 0..3
+  uint2 byte_levels[256]; // byte e of four 2-bit codes -> its four fp16 levels (code of bits 2i..2i+1 first)
 };
 
 hipError_t launch_append(int d, bool bf16, int nb, const AppendArgs& a, hipStream_t s);
