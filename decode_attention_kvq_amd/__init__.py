@@ -82,11 +82,12 @@ class Cache:
             raise ValueError("page_table must be [batch, max_pages]")
         self.page_table = page_table.to(device=device, dtype=torch.int32).contiguous()
         self.seq_len = torch.zeros(cfg.batch, dtype=torch.int32, device=device)
+        self.append_tickets = torch.zeros(cfg.batch, dtype=torch.int32, device=device)
         self.seq_len_host = (ctypes.c_int32 * cfg.batch)()
         self.struct = KvqCache(self.k_codes.data_ptr(), self.k_stats.data_ptr(), self.v_codes.data_ptr(),
                                self.v_norms.data_ptr(), self.modality.data_ptr(),
                                self.page_table.data_ptr(), self.seq_len.data_ptr(),
-                               self.k_tail.data_ptr(), self.seq_len_host)
+                               self.k_tail.data_ptr(), self.append_tickets.data_ptr(), self.seq_len_host)
 
     def lengths(self) -> list:
         return list(self.seq_len_host)

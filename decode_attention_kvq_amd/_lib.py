@@ -28,7 +28,7 @@ class KvqCache(ctypes.Structure):
                 ("v_codes", ctypes.c_void_p), ("v_norms", ctypes.c_void_p),
                 ("modality", ctypes.c_void_p), ("page_table", ctypes.c_void_p),
                 ("seq_len", ctypes.c_void_p), ("k_tail", ctypes.c_void_p),
-                ("seq_len_host", ctypes.POINTER(ctypes.c_int32))]
+                ("append_tickets", ctypes.c_void_p), ("seq_len_host", ctypes.POINTER(ctypes.c_int32))]
 
 
 class KvqParams(ctypes.Structure):

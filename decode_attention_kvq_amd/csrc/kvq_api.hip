@@ -39,7 +39,7 @@ kvq_status check_params(const kvq_params* p) {
 
 kvq_status check_cache(const kvq_cache* c) {
   if (!c || !c->k_codes || !c->k_stats || !c->v_codes || !c->v_norms || !c->modality ||
-      !c->page_table || !c->seq_len || !c->k_tail || !c->seq_len_host)
+      !c->page_table || !c->seq_len || !c->k_tail || !c->append_tickets || !c->seq_len_host)
     return KVQ_ERR_INVALID;
   return KVQ_OK;
 }
@@ -82,11 +82,10 @@ int splits_bound(const kvq_config* cfg, int32_t max_len) {
   return (int)std::min<int64_t>(4096, std::max<int64_t>(1, std::min(by_len, by_grid)));
 }
 
-// Workspace: partials, then the rotated per-modality parts, then the merge
-// completion counters (one int per (session, query head)).
+// Workspace: one partial result per (session, query head, partition).
 size_t workspace_floats(const kvq_config* cfg, const Plan& p) {
   const size_t heads = (size_t)cfg->batch * cfg->n_q_heads;
-  return heads * p.splits * (kvq::kPartialHeader + 3 * cfg->head_dim) + heads * 3 * cfg->head_dim + heads;
+  return heads * p.splits * (kvq::kPartialHeader + 3 * cfg->head_dim);
 }
 
 }  // namespace
@@ -145,6 +144,7 @@ kvq_status kvq_quantize_append(const kvq_config* cfg, kvq_cache* cache, const kv
   a.page_table = cache->page_table;
   a.seq_len = cache->seq_len;
   a.k_tail = cache->k_tail;
+  a.tickets = cache->append_tickets;
   a.k_new = k_new;
   a.v_new = v_new;
   a.modality_new = modality_new;
@@ -223,9 +223,6 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache,
   a.rot = params->rot;
   a.out = out;
   a.partials = static_cast<float*>(workspace);
-  a.counters = reinterpret_cast<int32_t*>(static_cast<float*>(workspace) + workspace_floats(cfg, plan) -
-                                          (size_t)cfg->batch * cfg->n_q_heads);
-  a.counters_len = cfg->batch * cfg->n_q_heads;
   a.batch = cfg->batch;
   a.hq = cfg->n_q_heads;
   a.hkv = cfg->n_kv_heads;

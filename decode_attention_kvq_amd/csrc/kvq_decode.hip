@@ -28,9 +28,9 @@
 // Value levels are c = cmid + chalf * l; sum_t w_t per modality is also kept
 // when the codebook is not symmetric (cmid != 0).
 //
-// Merge kernel: one workgroup per (session, query head, modality) rescales and
-// sums the partitions and applies R_m; the last of the three sums the three
-// rotated parts in fixed order (bitwise reproducible) and writes the output.
+// Merge kernel: workgroups of (session, query head, block of output rows)
+// rescale and sum the partitions and apply the three R_m in a fixed order
+// (bitwise reproducible).
 #include "kvq_common.h"
 #include "kvq_internal.h"
 
@@ -364,10 +364,6 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeArgs a)
   const int G = a.group;
   const int L = a.seq_len[b];
 
-  // The merge kernel's completion counters start from zero every launch.
-  if (split == 0 && h == 0 && b == 0)
-    for (int i = tid; i < a.counters_len; i += NW * 64) a.counters[i] = 0;
-
   // Byte table: one copy per lane of a 32-lane half wave.
   for (int i = tid; i < 256 * kTabCopies; i += NW * 64) sm.s.tab[i] = a.byte_levels[i / kTabCopies];
 
@@ -524,143 +520,202 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeArgs a)
   }
 }
 
-// One workgroup per (session, query head, modality m): weighted sum of the
-// partitions' modality-m accumulators, then R_m times it; the last of the
-// three workgroups of a head adds the three rotated parts in modality order.
-constexpr int kMergeThreads = 256;
+// Merge: workgroup (session, query head, row block) rescales every
+// partition's partial to the global max, sums them per modality, and applies
+// the rows [rb D/RB, (rb+1) D/RB) of the inverse value rotations,
+// out = sum_m R_m A_m / l.  Every global load (headers, accumulator blocks,
+// rotation rows) is issued before the first reduction, so the kernel costs
+// one memory round trip; all sums run in a fixed order (bitwise
+// reproducible).  The RB row blocks of one head are numbered so that they
+// land on the same XCD (workgroups are dealt to the 8 XCDs round robin) and
+// share the head's partials through that XCD's L2.
+constexpr int kMergeThreads = 512;
+constexpr int kMergeChunk = 16;    // partial blocks in flight per thread
+constexpr int kXcds = 8;
 
 template <int D>
+struct MergeShape {
+  static constexpr int RB = D / 32;                 // row blocks per head
+  static constexpr int RR = D / RB;                 // rows per block
+};
+
+template <int D, bool ASYM>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs a) {
   constexpr int PS = kPartialHeader + kModalities * D;
-  constexpr int F4 = D / 4;                      // float4 per accumulator block
-  constexpr int SG = kMergeThreads / F4;         // split subsets
-  constexpr int NQ = kMergeThreads / D;          // threads per output row
-  constexpr int JQ = D / NQ;                     // columns per thread
+  constexpr int F4 = D / 4;                        // float4 per accumulator block
+  constexpr int NCOL = kModalities * F4;           // (modality, float4) columns
+  constexpr int SG = kMergeThreads / NCOL;         // split subsets
+  constexpr int RB = MergeShape<D>::RB;
+  constexpr int RR = MergeShape<D>::RR;
+  constexpr int QT = kMergeThreads / RR;           // threads per output row
+  constexpr int JQ = D / QT;                       // columns of R per thread
+  constexpr int NW = kMergeThreads / 64;
+  static_assert(JQ % 4 == 0, "rotation columns per thread");
   __shared__ float s_e[kMaxSplits];
-  __shared__ float4 s_part[SG][F4];
-  __shared__ float s_A[D];
-  __shared__ float s_red[kMergeThreads / 64][3];
-  __shared__ int s_mask;
-  __shared__ int s_last;
-  const int i = blockIdx.x, b = blockIdx.y, m = blockIdx.z;
+  __shared__ uint8_t s_mk[kMaxSplits];
+  __shared__ float4 s_part[SG][NCOL];
+  __shared__ float s_A[kModalities][D];
+  __shared__ float s_red[NW][2 + kModalities];
+  __shared__ float s_M;
+
+  const int x = blockIdx.x % kXcds, y = blockIdx.x / kXcds;
+  const int rb = y % RB;
+  const int hi = (y / RB) * kXcds + x;             // b * Hq + i
+  if (hi >= a.batch * a.hq) return;
+  const int i = hi % a.hq;
   const int h = i / a.group;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = a.splits;
-  const size_t head = static_cast<size_t>(b) * a.hq + i;
+  const size_t head = static_cast<size_t>(hi);
   const float* P = a.partials + head * static_cast<size_t>(S) * PS;
 
-  // Headers: global max, weights, denominator, modality mask.
-  float mx = -__builtin_inff();
-  for (int s = tid; s < S; s += kMergeThreads) mx = fmaxf(mx, P[static_cast<size_t>(s) * PS]);
+  // Rotation rows: row rb RR + tid / QT, columns [q JQ, (q+1) JQ) of all three R_m.
+  const int rloc = tid / QT, q = tid % QT;
+  const int row = rb * RR + rloc;
+  float4 R[kModalities][JQ / 4];
+#pragma unroll
+  for (int m = 0; m < kModalities; ++m) {
+    const float4* Rp = reinterpret_cast<const float4*>(
+        a.rot + ((static_cast<size_t>(h) * kModalities + m) * D + row) * D + q * JQ);
+#pragma unroll
+    for (int j4 = 0; j4 < JQ / 4; ++j4) R[m][j4] = Rp[j4];
+  }
+  // First chunk of this thread's accumulator blocks: column (m, f4), splits
+  // g, g + SG, ... (indices past the last split re-read it: the loads stay
+  // branch-free, so they are all in flight at once; the extra values are
+  // never used).
+  const int col = tid % NCOL, g = tid / NCOL;
+  const bool loader = g < SG;
+  const int cm = col / F4, cf = col % F4;
+  float4 blk[kMergeChunk];
+#pragma unroll
+  for (int k = 0; k < kMergeChunk; ++k) {
+    const int s = min(g + k * SG, S - 1);
+    if (loader) blk[k] = reinterpret_cast<const float4*>(P + static_cast<size_t>(s) * PS + kPartialHeader + cm * D)[cf];
+  }
+  // Headers: [m, l, mask, -, S0, S1, S2, -] of splits tid, tid + 512, ...
+  // (the first one stays in registers).
+  const float4 ninf4 = {-__builtin_inff(), 0.f, 0.f, 0.f};
+  const float4 hd0 = tid < S ? reinterpret_cast<const float4*>(P + static_cast<size_t>(tid) * PS)[0] : ninf4;
+  float4 hd1 = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (ASYM) {
+    if (tid < S) hd1 = reinterpret_cast<const float4*>(P + static_cast<size_t>(tid) * PS)[1];
+  }
+  float mx = hd0.x;
+  for (int s = tid + kMergeThreads; s < S; s += kMergeThreads) mx = fmaxf(mx, P[static_cast<size_t>(s) * PS]);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
   if (lane == 0) s_red[wave][0] = mx;
-  if (tid == 0) s_mask = 0;
   __syncthreads();
-  float M = -__builtin_inff();
-#pragma unroll
-  for (int w = 0; w < kMergeThreads / 64; ++w) M = fmaxf(M, s_red[w][0]);
+  if (tid == 0) {
+    float M = s_red[0][0];
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, s_red[w][0]);
+    s_M = M;
+  }
   __syncthreads();
-  float ls = 0.f, ss = 0.f;
-  int mk = 0;
+  const float M = s_M;
+  float ls = 0.f, ss[kModalities] = {0.f, 0.f, 0.f};
   for (int s = tid; s < S; s += kMergeThreads) {
-    const float* ph = P + static_cast<size_t>(s) * PS;
-    const float ms = ph[0];
-    const float e = (ms == -__builtin_inff()) ? 0.f : exp2f(ms - M);
-    const int pm = e > 0.f ? __float_as_int(ph[2]) : 0;
-    s_e[s] = (pm & (1 << m)) ? e : 0.f;
-    ls += e * ph[1];
-    ss += (pm & (1 << m)) ? e * ph[4 + m] : 0.f;
-    mk |= pm;
+    const float4 h0 = s == tid ? hd0 : reinterpret_cast<const float4*>(P + static_cast<size_t>(s) * PS)[0];
+    const float e = (h0.x == -__builtin_inff()) ? 0.f : exp2f(h0.x - M);
+    const int pm = e > 0.f ? __float_as_int(h0.z) : 0;
+    s_e[s] = e;
+    s_mk[s] = static_cast<uint8_t>(pm);
+    ls += e * h0.y;
+    if constexpr (ASYM) {
+      const float4 h1 = s == tid ? hd1 : reinterpret_cast<const float4*>(P + static_cast<size_t>(s) * PS)[1];
+      ss[0] += (pm & 1) ? e * h1.x : 0.f;
+      ss[1] += (pm & 2) ? e * h1.y : 0.f;
+      ss[2] += (pm & 4) ? e * h1.z : 0.f;
+    }
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
     ls += __shfl_xor(ls, off);
-    ss += __shfl_xor(ss, off);
+    if constexpr (ASYM)
+#pragma unroll
+      for (int m = 0; m < kModalities; ++m) ss[m] += __shfl_xor(ss[m], off);
   }
-  if (mk) atomicOr(&s_mask, mk);
   if (lane == 0) {
     s_red[wave][1] = ls;
-    s_red[wave][2] = ss;
+#pragma unroll
+    for (int m = 0; m < kModalities; ++m) s_red[wave][2 + m] = ss[m];
   }
   __syncthreads();
-  float l = 0.f, Sm = 0.f;
-#pragma unroll
-  for (int w = 0; w < kMergeThreads / 64; ++w) {
-    l += s_red[w][1];
-    Sm += s_red[w][2];
-  }
-  const bool have = (s_mask >> m) & 1;
 
-  float* out3 = a.partials + static_cast<size_t>(a.batch) * a.hq * S * PS;   // [B][Hq][3][D]
-  float* mine = out3 + (head * kModalities + m) * D;
-  if (have) {
-    // Weighted sum of the modality-m blocks: thread -> (float4 column, split subset).
-    {
-      const int f4 = tid % F4, sg = tid / F4;
-      float4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-      for (int s = sg; s < S; s += SG) {
-        const float e = s_e[s];
-        if (e > 0.f) {
-          const float4 v = reinterpret_cast<const float4*>(P + static_cast<size_t>(s) * PS + kPartialHeader +
-                                                           m * D)[f4];
-          acc.x += e * v.x;
-          acc.y += e * v.y;
-          acc.z += e * v.z;
-          acc.w += e * v.w;
+  // Weighted sums of the accumulator blocks (absent modalities are selected
+  // away, never multiplied: their blocks hold stale data).
+  if (loader) {
+    float4 acc = {0.f, 0.f, 0.f, 0.f};
+    const uint8_t bit = static_cast<uint8_t>(1u << cm);
+    for (int base = 0; base < S; base += kMergeChunk * SG) {
+      if (base > 0) {
+#pragma unroll
+        for (int k = 0; k < kMergeChunk; ++k) {
+          const int s = min(base + g + k * SG, S - 1);
+          blk[k] = reinterpret_cast<const float4*>(P + static_cast<size_t>(s) * PS + kPartialHeader + cm * D)[cf];
         }
       }
-      s_part[sg][f4] = acc;
-    }
-    __syncthreads();
-    if (tid < F4) {
-      float4 v = s_part[0][tid];
 #pragma unroll
-      for (int g = 1; g < SG; ++g) {
-        v.x += s_part[g][tid].x;
-        v.y += s_part[g][tid].y;
-        v.z += s_part[g][tid].z;
-        v.w += s_part[g][tid].w;
+      for (int k = 0; k < kMergeChunk; ++k) {
+        const int s = base + g + k * SG;
+        if (s < S && (s_mk[s] & bit)) {
+          const float e = s_e[s];
+          acc.x += e * blk[k].x;
+          acc.y += e * blk[k].y;
+          acc.z += e * blk[k].z;
+          acc.w += e * blk[k].w;
+        }
       }
-      s_A[4 * tid + 0] = v.x;
-      s_A[4 * tid + 1] = v.y;
-      s_A[4 * tid + 2] = v.z;
-      s_A[4 * tid + 3] = v.w;
     }
-    __syncthreads();
-    // R_m times the accumulator: NQ threads per row, JQ columns each.
-    const int row = tid / NQ, q = tid % NQ;
-    const float4* R = reinterpret_cast<const float4*>(
-        a.rot + ((static_cast<size_t>(h) * kModalities + m) * D + row) * D + q * JQ);
-    float acc = 0.f, rs = 0.f;
+    s_part[g][col] = acc;
+  }
+  __syncthreads();
+  if (tid < NCOL) {
+    float4 v = s_part[0][tid];
+#pragma unroll
+    for (int gg = 1; gg < SG; ++gg) {
+      v.x += s_part[gg][tid].x;
+      v.y += s_part[gg][tid].y;
+      v.z += s_part[gg][tid].z;
+      v.w += s_part[gg][tid].w;
+    }
+    const int m = tid / F4, f = tid % F4;
+    s_A[m][4 * f + 0] = v.x;
+    s_A[m][4 * f + 1] = v.y;
+    s_A[m][4 * f + 2] = v.z;
+    s_A[m][4 * f + 3] = v.w;
+  }
+  __syncthreads();
+
+  // out[row] = (chalf sum_m R_m A_m + cmid sum_m S_m rowsum(R_m)) / (sqrt(d) l)
+  float l = 0.f, Sm[kModalities] = {0.f, 0.f, 0.f};
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    l += s_red[w][1];
+#pragma unroll
+    for (int m = 0; m < kModalities; ++m) Sm[m] += s_red[w][2 + m];
+  }
+  float acc = 0.f, rs = 0.f;
+#pragma unroll
+  for (int m = 0; m < kModalities; ++m) {
+    float am = 0.f, rm = 0.f;
 #pragma unroll
     for (int j4 = 0; j4 < JQ / 4; ++j4) {
-      const float4 r = R[j4];
-      const float* A = &s_A[q * JQ + 4 * j4];
-      acc += r.x * A[0] + r.y * A[1] + r.z * A[2] + r.w * A[3];
-      rs += r.x + r.y + r.z + r.w;
+      const float* A = &s_A[m][q * JQ + 4 * j4];
+      const float4 r = R[m][j4];
+      am += r.x * A[0] + r.y * A[1] + r.z * A[2] + r.w * A[3];
+      if constexpr (ASYM) rm += r.x + r.y + r.z + r.w;
     }
+    acc += am;
+    if constexpr (ASYM) rs += Sm[m] * rm;
+  }
 #pragma unroll
-    for (int off = 1; off < NQ; off <<= 1) {
-      acc += __shfl_xor(acc, off);
-      rs += __shfl_xor(rs, off);
-    }
-    if (q == 0) mine[row] = (l > 0.f) ? (a.chalf * acc + a.cmid * Sm * rs) * (a.value_scale / l) : 0.f;
-  } else {
-    for (int r = tid; r < D; r += kMergeThreads) mine[r] = 0.f;
+  for (int off = 1; off < QT; off <<= 1) {
+    acc += __shfl_xor(acc, off);
+    if constexpr (ASYM) rs += __shfl_xor(rs, off);
   }
-
-  // The last of the three modality workgroups writes out = part_0 + part_1 + part_2.
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_last = atomicAdd(&a.counters[head], 1) == kModalities - 1;
-  __syncthreads();
-  if (s_last) {
-    __threadfence();
-    const float* p3 = out3 + head * kModalities * D;
-    for (int r = tid; r < D; r += kMergeThreads) a.out[head * D + r] = (p3[r] + p3[D + r]) + p3[2 * D + r];
-  }
+  if (q == 0) a.out[head * D + row] = (l > 0.f) ? (a.chalf * acc + a.cmid * rs) * (a.value_scale / l) : 0.f;
 }
 
 template <int D, int SLOTS, int NW>
@@ -677,7 +732,12 @@ hipError_t launch_decode_t(int batch, const DecodeArgs& a, hipStream_t s) {
   if (a.group <= 5) launch_partition<D, 3, kDecodeWaves>(batch, a, s);
   else if (a.group <= 8) launch_partition<D, 2, kDecodeWaves>(batch, a, s);
   else launch_partition<D, 1, kDecodeWaves / 2>(batch, a, s);
-  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(a.hq, batch, kModalities), dim3(kMergeThreads), 0, s, a);
+  const int heads = a.hq * batch;
+  const dim3 mgrid(kXcds * MergeShape<D>::RB * ((heads + kXcds - 1) / kXcds));
+  if (a.cmid != 0.f)
+    hipLaunchKernelGGL((decode_merge_kernel<D, true>), mgrid, dim3(kMergeThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_merge_kernel<D, false>), mgrid, dim3(kMergeThreads), 0, s, a);
   return hipGetLastError();
 }
 

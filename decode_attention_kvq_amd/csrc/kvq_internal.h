@@ -12,7 +12,7 @@ constexpr int kGroupTokens = 32;   // key-statistics group length (positions 32g
 constexpr int kModalities = 3;     // video, audio, text
 constexpr int kMaxGroupHeads = 16; // query heads per KV head supported by the kernels
 
-// Arguments of the three append kernels (passed by value).
+// Arguments of the append kernel (passed by value).
 struct AppendArgs {
   uint8_t* k_codes;
   uint16_t* k_stats;
@@ -22,6 +22,7 @@ struct AppendArgs {
   const int32_t* page_table;
   int32_t* seq_len;
   void* k_tail;
+  int32_t* tickets;    // [batch] completion tickets, zero between appends
   const void* k_new;
   const void* v_new;
   const uint8_t* modality_new;
@@ -63,10 +64,7 @@ struct DecodeArgs {
   const float* q_rot;
   const float* rot;
   float* out;
-  float* partials;        // workspace: [B][Hq][splits][kPartialHeader + 3d] partials,
-                          // then [B][Hq][3][d] rotated per-modality parts
-  int32_t* counters;      // workspace tail: [B][Hq] completion counters of the merge
-  int32_t counters_len;
+  float* partials;        // workspace: [B][Hq][splits][kPartialHeader + 3d] partials
   int32_t batch;
   int32_t hq, hkv, group, page_tokens, max_pages, num_pages;
   int32_t splits;         // partitions per (session, KV head)

@@ -89,6 +89,9 @@ typedef struct kvq_cache {
   const int32_t* page_table;  /* device [batch][max_pages]: physical page of each logical page */
   int32_t*       seq_len;     /* device [batch]: cached positions per session */
   void*          k_tail;      /* device [batch][Hkv][32][d] kv_dtype */
+  int32_t*       append_tickets; /* device [batch], zero when the cache is created; the
+                                    append kernel's completion tickets (back to zero after
+                                    every append) */
   int32_t*       seq_len_host;/* host [batch]: mirror of seq_len kept by the library */
 } kvq_cache;
 
@@ -116,7 +119,9 @@ kvq_status kvq_cache_buffer_bytes(const kvq_config* cfg, size_t bytes_out[6]);
  * fp16 (round to nearest even); codes map [LO, HI] onto [c0, c3] and take
  * the nearest level.  Values: n = ||v||, z = sqrt(d) (R_{h,m}^T v) / n in
  * fp64, nearest level, norm stored as fp16.  seq_len and seq_len_host
- * advance by n_new.  Three kernels are launched on `stream`.
+ * advance by n_new (seq_len by the last workgroup to finish, through
+ * append_tickets).  One kernel is launched on `stream`; appends to the same
+ * cache must not overlap in time.
  * Errors: KVQ_ERR_INVALID (null pointers, b0/nb out of range, n_new < 0,
  * codebook not increasing), KVQ_ERR_CAPACITY (some session would exceed
  * max_pages * page_tokens, judged on seq_len_host), KVQ_ERR_UNSUPPORTED.

@@ -52,7 +52,7 @@ def _fake_params(L, codebook=(-1.5104, -0.4528, 0.4528, 1.5104)):
 
 def _fake_cache(L, lengths):
     arr = (ctypes.c_int32 * len(lengths))(*lengths)
-    c = L.KvqCache(*([0x1000] * 8), arr)
+    c = L.KvqCache(*([0x1000] * 9), arr)
     return c, arr
 
 
@@ -93,8 +93,11 @@ def test_append_rejects_bad_arguments_without_launching():
                                    ctypes.c_void_p(8), ctypes.c_void_p(8), ctypes.c_void_p(8), None) == 1
     assert lib.kvq_quantize_append(ctypes.byref(cfg), ctypes.byref(c), ctypes.byref(p), 0, 1, 4,
                                    None, ctypes.c_void_p(8), ctypes.c_void_p(8), None) == 1
-    nulls = L.KvqCache(0, *([0x1000] * 7), lens)
+    nulls = L.KvqCache(0, *([0x1000] * 8), lens)
     assert lib.kvq_quantize_append(ctypes.byref(cfg), ctypes.byref(nulls), ctypes.byref(p), 0, 1, 1,
+                                   ctypes.c_void_p(8), ctypes.c_void_p(8), ctypes.c_void_p(8), None) == 1
+    no_tickets = L.KvqCache(*([0x1000] * 8), 0, lens)
+    assert lib.kvq_quantize_append(ctypes.byref(cfg), ctypes.byref(no_tickets), ctypes.byref(p), 0, 1, 1,
                                    ctypes.c_void_p(8), ctypes.c_void_p(8), ctypes.c_void_p(8), None) == 1
 
 

@@ -175,3 +175,55 @@ def test_graph_replays_match_eager():
         assert torch.equal(out, eager), f"replay {i}"
         K.kvq_rotate_query(cfg, params, h.query_tensor(w), q_rot)   # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_many_partitions_merge():
+    """A context long enough for more partitions than the merge keeps in
+    flight at once (d = 64, one KV head: 70,000 positions)."""
+    import decode_attention_kvq_amd as K
+    h = H()
+    w = generate(0, length=70000)
+    _say("many partitions cfg0 70000")
+    cfg, params, cache = h.build(w, chunks=[4096])
+    scale = h.default_scale(w)
+    q_rot = K.kvq_rotate_query(cfg, params, h.query_tensor(w))
+    out = K.kvq_decode_attention(cfg, cache, params, q_rot, scale).cpu().numpy()
+    ref = h.oracle_decode_over_gpu_codes(w, cfg, cache, O.as_f64(w.q, w.dtype), [0], scale)
+    err = float(h.normwise_rel_err(out[0].astype(np.float64), ref[0]).max())
+    _say(f"decode worst normwise rel err {err:.3e}")
+    assert err <= h.ATTN_TOL
+
+
+def test_graph_replayed_single_token_appends():
+    """A captured one-position append replayed 70 times (the input buffer is
+    refilled eagerly between replays) advances the device length itself and
+    leaves the same cache as appending the stream directly."""
+    import decode_attention_kvq_amd as K
+    h = H()
+    w = generate(1, length=200)
+    _say("graph-replayed appends cfg1 130 -> 200")
+    cfg, params, cache = h.build(w, upto=[130])
+    k_in = h._kv_tensor(w.k[0][None, 130:131], w.dtype)
+    v_in = h._kv_tensor(w.v[0][None, 130:131], w.dtype)
+    m_in = torch.from_numpy(np.ascontiguousarray(w.modality[0][None, 130:131])).cuda()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            K.kvq_quantize_append(cfg, cache, params, k_in, v_in, m_in)
+    torch.cuda.synchronize()
+    assert int(cache.seq_len.cpu()[0]) == 130          # capture does not run the kernel
+    for t in range(130, 200):
+        k_in.copy_(h._kv_tensor(w.k[0][None, t:t + 1], w.dtype))
+        v_in.copy_(h._kv_tensor(w.v[0][None, t:t + 1], w.dtype))
+        m_in.copy_(torch.from_numpy(np.ascontiguousarray(w.modality[0][None, t:t + 1])).cuda())
+        g.replay()
+    torch.cuda.synchronize()
+    assert int(cache.seq_len.cpu()[0]) == 200
+    assert int(cache.append_tickets.cpu()[0]) == 0
+    cache.set_lengths([200])
+    _, _, ref = h.build(w)
+    a, b = cache.host_arrays(), ref.host_arrays()
+    for key in ("k_codes", "k_stats", "v_codes", "v_norms", "modality", "seq_len"):
+        np.testing.assert_array_equal(a[key], b[key], err_msg=key)
