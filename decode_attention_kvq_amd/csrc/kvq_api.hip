@@ -48,16 +48,23 @@ kvq_status check_cache(const kvq_cache* c) {
 // 32 * kDecodeWaves positions (every wavefront of the workgroup takes whole
 // groups).  Partitions are sized from the longest session so that a batch of
 // such sessions spreads over about one workgroup per compute unit (256 CUs),
-// or four per CU when that would make partitions longer than 4096 positions.
-// The plan depends only on (cfg, max_len), so the workspace size is known
-// before the call.
+// or four per CU when that would make partitions longer than 4096 positions,
+// and never span more than kPartitionPages - 2 pages (the kernel keeps a
+// partition's page-table entries in LDS).  The plan depends only on
+// (cfg, max_len), so the workspace size is known before the call.
 struct Plan {
   int splits;
   int split_tokens;
 };
 
+constexpr int64_t kUnit = kGroupTokens * kvq::kDecodeWaves;
+constexpr int64_t kMaxPlanSplits = 4096;
+
+int64_t max_split_tokens(const kvq_config* cfg) {
+  return ((int64_t)(kvq::kPartitionPages - 2) * cfg->page_tokens / kUnit) * kUnit;
+}
+
 Plan plan_decode(const kvq_config* cfg, int32_t max_len) {
-  constexpr int64_t kUnit = kGroupTokens * kvq::kDecodeWaves;
   constexpr int64_t kCUs = 256;
   const int64_t len = std::max<int32_t>(max_len, 1);
   const int64_t total = len * cfg->batch * cfg->n_kv_heads;
@@ -65,21 +72,32 @@ Plan plan_decode(const kvq_config* cfg, int32_t max_len) {
   if (per > 4096) per = (total + 4 * kCUs - 1) / (4 * kCUs);
   per = std::max(kUnit, ((per + kUnit - 1) / kUnit) * kUnit);
   int64_t splits = (len + per - 1) / per;
-  while (splits > 4096) {
+  while (splits > kMaxPlanSplits) {
     per *= 2;
+    splits = (len + per - 1) / per;
+  }
+  const int64_t cap = max_split_tokens(cfg);
+  if (per > cap) {
+    per = cap;
     splits = (len + per - 1) / per;
   }
   return {(int)splits, (int)per};
 }
 
+// Longest context the plan supports (splits stay within kMaxPlanSplits).
+bool plan_supported(const kvq_config* cfg, int32_t max_len) {
+  return (int64_t)max_len <= kMaxPlanSplits * max_split_tokens(cfg);
+}
+
 // Upper bound of plan_decode(cfg, len).splits over every len <= max_len, so a
 // workspace sized for max_len serves every shorter context too.
 int splits_bound(const kvq_config* cfg, int32_t max_len) {
-  constexpr int64_t kUnit = kGroupTokens * kvq::kDecodeWaves;
   const int64_t heads = (int64_t)cfg->batch * cfg->n_kv_heads;
-  const int64_t by_len = (std::max<int32_t>(max_len, 1) + kUnit - 1) / kUnit;
+  const int64_t len = std::max<int32_t>(max_len, 1);
+  const int64_t by_len = (len + kUnit - 1) / kUnit;
   const int64_t by_grid = (1024 + heads - 1) / heads + 1;
-  return (int)std::min<int64_t>(4096, std::max<int64_t>(1, std::min(by_len, by_grid)));
+  const int64_t by_cap = (len + max_split_tokens(cfg) - 1) / max_split_tokens(cfg);
+  return (int)std::min<int64_t>(kMaxPlanSplits, std::max<int64_t>(1, std::min(by_len, std::max(by_grid, by_cap))));
 }
 
 // Workspace: one partial result per (session, query head, partition).
@@ -208,6 +226,7 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache,
     if (cache->seq_len_host[b] < 0 || cache->seq_len_host[b] > cap) return KVQ_ERR_INVALID;
     max_len = std::max(max_len, cache->seq_len_host[b]);
   }
+  if (!plan_supported(cfg, max_len)) return KVQ_ERR_UNSUPPORTED;
   const Plan plan = plan_decode(cfg, max_len);
   if (!workspace || workspace_bytes < workspace_floats(cfg, plan) * sizeof(float)) return KVQ_ERR_WORKSPACE;
   const double c0 = params->codebook[0], c3 = params->codebook[3];

@@ -43,6 +43,8 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTabCopies = 32;     // byte-table copies: lane l reads copy l % 32
+constexpr float kLazyMax = 8.f;    // headroom (base-2 units) of the softmax reference max
+constexpr int kPageRun = kPartitionPages;   // page-table entries of one partition kept in LDS
 constexpr int kMaxSplits = 4096;
 
 __device__ __forceinline__ floatx4 mfma(const half8& a, const half8& b, const floatx4& c) {
@@ -101,20 +103,14 @@ struct GroupLoad {
   uint32_t md0, md1;     // modality bytes of the same positions
 };
 
-// Issues the loads of the group at position t0 without branching (so the
-// compiler can count outstanding loads exactly): a group outside [0, te) or on
-// an unmapped page reads page 0 instead and is flagged invalid.
+// Issues the loads of the group at position t0 (on physical page phys0)
+// without branching, so the compiler can count outstanding loads exactly: a
+// group outside [0, te) or on an unmapped page reads page 0 instead and is
+// flagged invalid.
 template <int D>
-__device__ __forceinline__ void load_group(const DecodeArgs& a, int b, int h, int t0, int te, int lane, int kg,
-                                           GroupLoad<D>& g, bool& ok) {
+__device__ __forceinline__ void load_group(const DecodeArgs& a, int h, int t0, int te, int lane, int kg,
+                                           int phys0, GroupLoad<D>& g, bool& ok) {
   const int page = t0 / a.page_tokens;
-  const int pg = min(page, a.max_pages - 1);
-  // The page table is read-only here: reading it through the constant address
-  // space makes this a scalar load, which does not wait on the vector loads
-  // already in flight.
-  const __attribute__((address_space(4))) int32_t* ptab =
-      (const __attribute__((address_space(4))) int32_t*)(a.page_table);
-  const int phys0 = ptab[static_cast<size_t>(b) * a.max_pages + pg];
   ok = t0 < te && page < a.max_pages && phys0 >= 0 && phys0 < a.num_pages;
   const int phys = ok ? phys0 : 0;
   const int gp = a.page_tokens / kGroupTokens;
@@ -169,66 +165,125 @@ __device__ __forceinline__ float f16_diff_hi(uint32_t a2, uint32_t b2) {
   return d;
 }
 
+// q * d (fp32 operands) split into fp16 hi + lo for two channels at once:
+// hi = fp16(q d), lo = fp16(q d - hi), so that hi + lo equals q d to about
+// 2^-22 relative.  Returns {hi pair, lo pair}.
+__device__ __forceinline__ uint2 split_product(float q0, float d0, float q1, float d1) {
+  uint32_t hi, lo;
+  asm("v_fma_mixlo_f16 %0, %1, %2, 0\n\t"
+      "v_fma_mixhi_f16 %0, %3, %4, 0"
+      : "=&v"(hi) : "v"(q0), "v"(d0), "v"(q1), "v"(d1));
+  asm("v_fma_mixlo_f16 %0, %1, %2, -%5 op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %0, %3, %4, -%5 op_sel:[0,0,1] op_sel_hi:[0,0,1]"
+      : "=&v"(lo) : "v"(q0), "v"(d0), "v"(q1), "v"(d1), "v"(hi));
+  return uint2{hi, lo};
+}
+
+// fp16 pair {p0 * n.lo, p1 * n.hi} from fp32 p and a register holding two fp16 norms.
+__device__ __forceinline__ uint32_t weight_pair(float p0, float p1, uint32_t n2) {
+  uint32_t w;
+  asm("v_fma_mixlo_f16 %0, %1, %3, 0 op_sel_hi:[0,1,0]\n\t"
+      "v_fma_mixhi_f16 %0, %2, %3, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]"
+      : "=&v"(w) : "v"(p0), "v"(p1), "v"(n2));
+  return w;
+}
+
+// Max / sum over the four rows (kg) of a wavefront for each of the 16
+// columns, with the permlane swaps (no LDS).  Every lane gets the result.
+__device__ __forceinline__ float rows_max(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float rows_sum(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+// Query operands of a lane (score column col, row group kg), constant over
+// the partition: q * scale * log2(e) / 2 on the lane's channels
+// 32 kt + 8 kg + i in fp32, and the operand of the group-bias product.  With
+// G <= 8 (BHL) the bias operand holds q's fp16 hi part in columns 0..7 and its
+// lo part in columns 8..15, so one product per statistics row covers both;
+// otherwise hi and lo are separate operands.
+template <int D, bool BHL>
+struct QueryOps {
+  float hq[D / 32][8];
+  half8 bq[D / 32];                 // BHL: hi (col < 8) or lo (col >= 8); else hi
+  half8 bq_lo[BHL ? 1 : D / 32];    // !BHL: lo
+};
+
 // FULL: all 32 positions of the group are inside the partition.
-template <int D, int SLOTS, bool ASYM, bool FULL>
+template <int D, int SLOTS, bool ASYM, bool BHL, bool FULL>
 __device__ __forceinline__ void process_group(const GroupLoad<D>& cur, int t0, int te, int kg, int col,
-                                              int lane, const uint2* tab, uint16_t* st_lds, uint32_t lane_off,
-                                              const float (&hq)[D / 32][8], const half8 (&bq_hi)[D / 32],
-                                              const half8 (&bq_lo)[D / 32], WaveState<D, SLOTS, ASYM>& ws) {
+                                              const uint2* tab, uint16_t* st_lds, uint32_t lane_off,
+                                              const QueryOps<D, BHL>& qo, WaveState<D, SLOTS, ASYM>& ws,
+                                              int lane) {
   constexpr int KT = D / 32;
   constexpr int CT = D / 16;
   constexpr int GP = Slots<SLOTS>::GP;
   constexpr int NSETS = Slots<SLOTS>::NSETS;
 
-  // Stage LO / HI rows; each lane then reads the 8-channel runs it needs.
+  // Stage the group's LO / HI rows; each lane then reads the 8-channel runs
+  // of its row group.
   if constexpr (D == 128) {
     reinterpret_cast<uint2*>(st_lds)[lane] = uint2{cur.st[0], cur.st[1]};
   } else {
     reinterpret_cast<uint32_t*>(st_lds)[lane] = cur.st[0];
   }
   wave_sync();
-  // Group bias sum_c q_c (LO_c + HI_c) / 2 (identical in every row) and
-  // q~ = q (HI - LO) / 2 split into fp16 hi + lo, one K-tile at a time.
-  floatx4 b0 = {0.f, 0.f, 0.f, 0.f}, b1 = {0.f, 0.f, 0.f, 0.f};
-  half8 qt_hi[KT], qt_lo[KT];
+
+  floatx4 bias4 = {0.f, 0.f, 0.f, 0.f}, bias4_lo = {0.f, 0.f, 0.f, 0.f};
+  floatx4 sc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
   for (int kt = 0; kt < KT; ++kt) {
     const uint4 lo4 = *reinterpret_cast<const uint4*>(st_lds + 32 * kt + 8 * kg);
     const uint4 hi4 = *reinterpret_cast<const uint4*>(st_lds + D + 32 * kt + 8 * kg);
-    const half8 lo8 = __builtin_bit_cast(half8, lo4);
-    const half8 hi8 = __builtin_bit_cast(half8, hi4);
-    b0 = mfma(lo8, bq_hi[kt], b0);
-    b1 = mfma(lo8, bq_lo[kt], b1);
-    b0 = mfma(hi8, bq_hi[kt], b0);
-    b1 = mfma(hi8, bq_lo[kt], b1);
+    // Group bias sum_c q_c (LO_c + HI_c) (q carries the 1/2): every row of
+    // the product holds it.
+    bias4 = mfma(__builtin_bit_cast(half8, lo4), qo.bq[kt], bias4);
+    bias4 = mfma(__builtin_bit_cast(half8, hi4), qo.bq[kt], bias4);
+    if constexpr (!BHL) {
+      bias4_lo = mfma(__builtin_bit_cast(half8, lo4), qo.bq_lo[kt], bias4_lo);
+      bias4_lo = mfma(__builtin_bit_cast(half8, hi4), qo.bq_lo[kt], bias4_lo);
+    }
+    // q~ = q (HI - LO) / 2 as fp16 hi + lo on this K-tile's 8 channels.
     const uint32_t lw[4] = {lo4.x, lo4.y, lo4.z, lo4.w};
     const uint32_t hw[4] = {hi4.x, hi4.y, hi4.z, hi4.w};
+    uint32_t th[4], tl[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float diff = (i & 1) ? f16_diff_hi(hw[i >> 1], lw[i >> 1]) : f16_diff_lo(hw[i >> 1], lw[i >> 1]);
-      const float qt = hq[kt][i] * diff;
-      const _Float16 h16 = static_cast<_Float16>(qt);
-      qt_hi[kt][i] = h16;
-      qt_lo[kt][i] = static_cast<_Float16>(qt - static_cast<float>(h16));
+    for (int p = 0; p < 4; ++p) {
+      const float d0 = f16_diff_lo(hw[p], lw[p]);
+      const float d1 = f16_diff_hi(hw[p], lw[p]);
+      const uint2 s = split_product(qo.hq[kt][2 * p], d0, qo.hq[kt][2 * p + 1], d1);
+      th[p] = s.x;
+      tl[p] = s.y;
     }
-  }
-  wave_sync();   // the LDS staging may be overwritten by the next group
-
-  // Scores for positions 16 mt + 4 kg + j of head `col`.
-  floatx4 sc[2];
+    const half8 qt_hi = __builtin_bit_cast(half8, uint4{th[0], th[1], th[2], th[3]});
+    const half8 qt_lo = __builtin_bit_cast(half8, uint4{tl[0], tl[1], tl[2], tl[3]});
+    // Scores for positions 16 mt + 4 kg + j of head `col`, this K-tile.
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    floatx4 s_hi = b0, s_lo = b1;
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
+    for (int mt = 0; mt < 2; ++mt) {
       const int j0 = mt * (D / 16) + kt * 2;   // code bytes j0, j0 + 1 of this (mt, kt)
       const uint2 x0 = lookup(tab, cur.kc[j0 >> 2], byte_sel(j0 & 3), lane_off);
       const uint2 x1 = lookup(tab, cur.kc[(j0 + 1) >> 2], byte_sel((j0 + 1) & 3), lane_off);
       const half8 ak = as_half8(x0, x1);
-      s_hi = mfma(ak, qt_hi[kt], s_hi);
-      s_lo = mfma(ak, qt_lo[kt], s_lo);
+      sc[mt] = mfma(ak, qt_hi, sc[mt]);
+      sc[mt] = mfma(ak, qt_lo, sc[mt]);
     }
-    sc[mt] = s_hi + s_lo;
+  }
+  wave_sync();   // the LDS staging may be overwritten by the next group
+
+  // Column bias: hi + lo parts (columns col and col +- 8 when BHL).
+  float bias = bias4[0];
+  if constexpr (BHL) {
+    bias += __uint_as_float(static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(__float_as_uint(bias)), 0x128, 0xF, 0xF, false)));
+  } else {
+    bias += bias4_lo[0];
   }
 
   // Online softmax (base 2) for head `col` over this group's positions.
@@ -238,10 +293,12 @@ __device__ __forceinline__ void process_group(const GroupLoad<D>& cur, int t0, i
   float mx = -__builtin_inff();
 #pragma unroll
   for (int i = 0; i < 8; ++i) mx = valid[i] ? fmaxf(mx, sc[i >> 2][i & 3]) : mx;
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m_new = fmaxf(ws.m_run, mx);
-  if (__any(m_new > ws.m_run)) {
+  mx = rows_max(mx) + bias;
+  // The reference max m_run only moves when a score passes it, and then to
+  // kLazyMax above the new max: weights 2^(s - m_run) stay <= 1, and the
+  // rescale of the accumulators (exact either way) is rarely needed.
+  if (__any(mx > ws.m_run)) {
+    const float m_new = fmaxf(ws.m_run, mx + kLazyMax);
     const float alpha = exp2f(ws.m_run - m_new);   // 0 on the first group
     ws.l_run *= alpha;
     const float alpha_v = __uint_as_float(to_value_column<SLOTS>(__float_as_uint(alpha)));
@@ -253,27 +310,21 @@ __device__ __forceinline__ void process_group(const GroupLoad<D>& cur, int t0, i
     }
     ws.m_run = m_new;
   }
+  const float off = ws.m_run - bias;
   const uint32_t n4[4] = {cur.nrm0.x, cur.nrm0.y, cur.nrm1.x, cur.nrm1.y};
   uint32_t wp[4];   // fp16 weights p * N of the lane's 8 positions, two per register
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    float w2[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int i = 2 * r + u;
-      // arguments are <= 0: the raw base-2 exponential flushes only results below 2^-126
-      const float p = __builtin_amdgcn_exp2f(sc[i >> 2][i & 3] - ws.m_run);
-      const float nrm = f16_bits_to_f32(static_cast<uint16_t>(n4[r] >> (16 * u)));
-      if constexpr (FULL) {
-        ws.l_run += p;
-        w2[u] = p * nrm;
-      } else {
-        ws.l_run += valid[i] ? p : 0.f;
-        w2[u] = valid[i] ? p * nrm : 0.f;
-      }
+    const int i0 = 2 * r, i1 = 2 * r + 1;
+    // arguments are <= 0: the raw base-2 exponential flushes only results below 2^-126
+    float p0 = __builtin_amdgcn_exp2f(sc[i0 >> 2][i0 & 3] - off);
+    float p1 = __builtin_amdgcn_exp2f(sc[i1 >> 2][i1 & 3] - off);
+    if constexpr (!FULL) {
+      p0 = valid[i0] ? p0 : 0.f;
+      p1 = valid[i1] ? p1 : 0.f;
     }
-    const half2v hw2 = {static_cast<_Float16>(w2[0]), static_cast<_Float16>(w2[1])};
-    wp[r] = to_value_column<SLOTS>(__builtin_bit_cast(uint32_t, hw2));
+    ws.l_run += p0 + p1;
+    wp[r] = to_value_column<SLOTS>(weight_pair(p0, p1, n4[r]));
   }
 
   // Value operands: rows = channels 16 ct + col, k = the positions of the scores.
@@ -333,29 +384,28 @@ __device__ __forceinline__ void process_group(const GroupLoad<D>& cur, int t0, i
   }
 }
 
-template <int D, int SLOTS, int NW, bool ASYM>
-__global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeArgs a) {
+template <int D, int SLOTS, int NW, bool ASYM, bool BHL>
+__global__ __launch_bounds__(NW * 64, 1) void decode_partition_kernel(DecodeArgs a) {
   constexpr int KT = D / 32;
   constexpr int CT = D / 16;
   constexpr int GP = Slots<SLOTS>::GP;
   constexpr int NSETS = Slots<SLOTS>::NSETS;
   constexpr int PS = kPartialHeader + kModalities * D;
   constexpr int kPrefetch = 2;     // groups in flight per wavefront
-  struct Merge {
-    float4 tree[NW / 2][NSETS][CT][64];   // wavefront accumulators handed down the reduction tree
-    float m[NW][kMaxGroupHeads];
-    float l[NW][kMaxGroupHeads];
-    float s[NW][kModalities][kMaxGroupHeads];
-    int mask;
-  };
+  constexpr int NPOS = NSETS * CT * 64;   // float4 accumulator slots of one wavefront
   union Smem {
     struct {
       uint2 tab[256 * kTabCopies];       // 64 KB: entry e, copy c at byte e*256 + c*8
       uint16_t stats[NW][2][D];          // per-wave staging of one group's LO / HI rows
     } s;
-    Merge merge;
+    float4 red[NW][NPOS];                // the wavefronts' rescaled accumulators
   };
   __shared__ Smem sm;
+  __shared__ float s_m[NW][kMaxGroupHeads];
+  __shared__ float s_l[NW][kMaxGroupHeads];
+  __shared__ float s_s[NW][kModalities][kMaxGroupHeads];
+  __shared__ int s_mask;
+  __shared__ int s_pt[kPageRun];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar) index
@@ -363,31 +413,85 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeArgs a)
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int G = a.group;
   const int L = a.seq_len[b];
+  const int tb = split * a.split_tokens;
+  const int te = (split == a.splits - 1) ? L : min(tb + a.split_tokens, L);
+  const int te_full = te & ~(kGroupTokens - 1);   // tb is a multiple of 32
+  const int stride = NW * kGroupTokens;
+  const int first = tb + wave * kGroupTokens;
 
-  // Byte table: one copy per lane of a 32-lane half wave.
-  for (int i = tid; i < 256 * kTabCopies; i += NW * 64) sm.s.tab[i] = a.byte_levels[i / kTabCopies];
-
-  // This lane's score head (padding columns reuse the last head; ignored):
-  // q * scale * log2(e) / 2 on channels 32kt + 8kg + i, in fp32 and as an
-  // fp16 pair hi + lo (the bias operand).
-  const int qh = h * G + min(col, G - 1);
-  const float* qp = a.q_rot + (static_cast<size_t>(b) * a.hq + qh) * D;
-  float hq[KT][8];
-  half8 bq_hi[KT], bq_lo[KT];
+  // Loads first (the query, the page-table run of the partition, the first
+  // groups), so that their latency overlaps the table set-up.  This lane's
+  // score head (padding columns reuse the last head; ignored): q on channels
+  // 32 kt + 8 kg + i, two float4 per K-tile.
+  const int qcol = BHL ? (col & 7) : col;
+  const int qh = h * G + min(qcol, G - 1);
+  const float4* qp = reinterpret_cast<const float4*>(a.q_rot + (static_cast<size_t>(b) * a.hq + qh) * D);
+  float4 qraw[KT][2];
 #pragma unroll
   for (int kt = 0; kt < KT; ++kt) {
+    qraw[kt][0] = qp[(32 * kt + 8 * kg) / 4];
+    qraw[kt][1] = qp[(32 * kt + 8 * kg) / 4 + 1];
+  }
+  // Page-table entries of the partition's pages (the plan keeps a partition
+  // within kPageRun pages), read by the main loop from LDS.
+  const int page0 = tb / a.page_tokens;
+  for (int i = tid; i < kPageRun; i += NW * 64) {
+    const int pg = page0 + i;
+    s_pt[i] = pg < a.max_pages ? a.page_table[static_cast<size_t>(b) * a.max_pages + pg] : -1;
+  }
+  // The first groups take their pages through the constant address space
+  // (scalar loads).
+  const __attribute__((address_space(4))) int32_t* ptab =
+      (const __attribute__((address_space(4))) int32_t*)(a.page_table + static_cast<size_t>(b) * a.max_pages);
+  GroupLoad<D> buf[kPrefetch];
+  bool ok[kPrefetch];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float v = qp[32 * kt + 8 * kg + i] * a.scale_log2e * 0.5f;
-      hq[kt][i] = v;
-      const _Float16 hi = static_cast<_Float16>(v);
-      bq_hi[kt][i] = hi;
-      bq_lo[kt][i] = static_cast<_Float16>(v - static_cast<float>(hi));
+  for (int k = 0; k < kPrefetch; ++k) {
+    const int t = first + k * stride;
+    const int phys = ptab[min(t / a.page_tokens, a.max_pages - 1)];
+    load_group<D>(a, h, t, te_full, lane, kg, phys, buf[k], ok[k]);
+  }
+
+  // Byte table: entry e = four fp16 levels of the codes in bits 2i..2i+1 of
+  // e; thread tid fills 16 of entry (tid / 2)'s 32 copies.
+  {
+    const int e = tid >> 1;
+    uint32_t lvl[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) lvl[k] = (a.level_f16[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
+    const uint2 v = {lvl[e & 3] | (lvl[(e >> 2) & 3] << 16), lvl[(e >> 4) & 3] | (lvl[e >> 6] << 16)};
+    for (int c = (tid & 1) * 16; c < (tid & 1) * 16 + 16; ++c) sm.s.tab[e * kTabCopies + c] = v;
+    if constexpr (NW * 64 < 512) {
+      // fewer threads than 2 per entry: the first pass covered entries < NW * 32
+      for (int e2 = e + NW * 32; e2 < 256; e2 += NW * 32) {
+        const uint2 v2 = {lvl[e2 & 3] | (lvl[(e2 >> 2) & 3] << 16), lvl[(e2 >> 4) & 3] | (lvl[e2 >> 6] << 16)};
+        for (int c = (tid & 1) * 16; c < (tid & 1) * 16 + 16; ++c) sm.s.tab[e2 * kTabCopies + c] = v2;
+      }
     }
   }
 
-  const int tb = split * a.split_tokens;
-  const int te = (split == a.splits - 1) ? L : min(tb + a.split_tokens, L);
+  QueryOps<D, BHL> qo;
+  {
+    const float sc = a.scale_log2e * 0.5f;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      const float qv[8] = {qraw[kt][0].x, qraw[kt][0].y, qraw[kt][0].z, qraw[kt][0].w,
+                           qraw[kt][1].x, qraw[kt][1].y, qraw[kt][1].z, qraw[kt][1].w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float v = qv[i] * sc;
+        qo.hq[kt][i] = v;
+        const _Float16 hi = static_cast<_Float16>(v);
+        const _Float16 lo = static_cast<_Float16>(v - static_cast<float>(hi));
+        if constexpr (BHL) {
+          qo.bq[kt][i] = col < 8 ? hi : lo;
+        } else {
+          qo.bq[kt][i] = hi;
+          qo.bq_lo[kt][i] = lo;
+        }
+      }
+    }
+  }
   const uint32_t lane_off = static_cast<uint32_t>(lane & (kTabCopies - 1)) << 3;
 
   WaveState<D, SLOTS, ASYM> ws;
@@ -401,6 +505,7 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeArgs a)
   }
 #pragma unroll
   for (int k = 0; k < (ASYM ? NSETS : 1); ++k) ws.accs[k] = floatx4{0.f, 0.f, 0.f, 0.f};
+  if (tid == 0) s_mask = 0;
   __syncthreads();
 
   const uint2* tab = sm.s.tab;
@@ -409,109 +514,91 @@ __global__ __launch_bounds__(NW * 64) void decode_partition_kernel(DecodeArgs a)
   // Prefetch ring over the partition's full groups: each wavefront keeps
   // kPrefetch groups in flight.  The one partial group a partition can end
   // with (the session's last) is handled after the loop.
-  const int te_full = te & ~(kGroupTokens - 1);   // tb is a multiple of 32
-  GroupLoad<D> buf[kPrefetch];
-  bool ok[kPrefetch];
-  const int stride = NW * kGroupTokens;
-  const int first = tb + wave * kGroupTokens;
-#pragma unroll
-  for (int k = 0; k < kPrefetch; ++k) load_group<D>(a, b, h, first + k * stride, te_full, lane, kg, buf[k], ok[k]);
   for (int base = first; base < te_full; base += kPrefetch * stride) {
 #pragma unroll
     for (int k = 0; k < kPrefetch; ++k) {
+      const int nxt = base + (k + kPrefetch) * stride;
+      const int pn = __builtin_amdgcn_readfirstlane(s_pt[min(nxt / a.page_tokens - page0, kPageRun - 1)]);
       if (ok[k])
-        process_group<D, SLOTS, ASYM, true>(buf[k], base + k * stride, te, kg, col, lane, tab, st_lds, lane_off,
-                                            hq, bq_hi, bq_lo, ws);
-      load_group<D>(a, b, h, base + (k + kPrefetch) * stride, te_full, lane, kg, buf[k], ok[k]);
+        process_group<D, SLOTS, ASYM, BHL, true>(buf[k], base + k * stride, te, kg, col, tab, st_lds, lane_off, qo,
+                                                 ws, lane);
+      load_group<D>(a, h, nxt, te_full, lane, kg, pn, buf[k], ok[k]);
     }
   }
   if (te_full >= tb && te_full < te && ((te_full - tb) / kGroupTokens) % NW == wave) {
-    load_group<D>(a, b, h, te_full, te, lane, kg, buf[0], ok[0]);
+    load_group<D>(a, h, te_full, te, lane, kg, s_pt[min(te_full / a.page_tokens - page0, kPageRun - 1)], buf[0], ok[0]);
     if (ok[0])
-      process_group<D, SLOTS, ASYM, false>(buf[0], te_full, te, kg, col, lane, tab, st_lds, lane_off, hq, bq_hi,
-                                           bq_lo, ws);
+      process_group<D, SLOTS, ASYM, BHL, false>(buf[0], te_full, te, kg, col, tab, st_lds, lane_off, qo, ws, lane);
   }
 
   // ---- merge the wavefronts of the workgroup, write one partial per query head
-  ws.l_run += __shfl_xor(ws.l_run, 16);
-  ws.l_run += __shfl_xor(ws.l_run, 32);
-  __syncthreads();   // the byte table is dead from here on
-  Merge& ms = sm.merge;
-  if (tid == 0) ms.mask = 0;
+  const float l_col = rows_sum(ws.l_run);
   const int slot = col / GP, hp = col % GP;
   if (kg == 0) {
-    ms.m[wave][col] = ws.m_run;
-    ms.l[wave][col] = ws.l_run;
+    s_m[wave][col] = ws.m_run;
+    s_l[wave][col] = l_col;
     if (slot < SLOTS) {
 #pragma unroll
       for (int k = 0; k < NSETS; ++k) {
         const int m = k * SLOTS + slot;
-        if (m < kModalities) ms.s[wave][m][hp] = ASYM ? ws.accs[ASYM ? k : 0][0] : 0.f;
+        if (m < kModalities) s_s[wave][m][hp] = ASYM ? ws.accs[ASYM ? k : 0][0] : 0.f;
       }
     }
+  }
+  if (ws.mask) atomicOr(&s_mask, ws.mask);
+  __syncthreads();   // every wavefront is past its main loop: the byte table is dead
+  // Bring the value columns (head hp) to the workgroup max of that head and
+  // hand them to LDS; then every thread sums a share over the wavefronts in
+  // a fixed order (bitwise reproducible) and writes it out.
+  {
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][hp]);
+    const float mw = s_m[wave][hp];
+    // (arguments <= 0: the raw base-2 exponential only flushes results below 2^-126)
+    const float e = (mw == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+#pragma unroll
+    for (int k = 0; k < NSETS; ++k)
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const floatx4 v = ws.acc[k][ct] * e;
+        sm.red[wave][(k * CT + ct) * 64 + lane] = float4{v[0], v[1], v[2], v[3]};
+      }
   }
   __syncthreads();
-  if (ws.mask) atomicOr(&ms.mask, ws.mask);
-  // Bring the value columns (head hp) to the workgroup max of that head, then
-  // sum the wavefronts pairwise down a fixed tree (bitwise reproducible).
-  float M = -__builtin_inff();
-  for (int w = 0; w < NW; ++w) M = fmaxf(M, ms.m[w][hp]);
-  const float mw = ms.m[wave][hp];
-  const float e = (mw == -__builtin_inff()) ? 0.f : exp2f(mw - M);
+  const int wmask = s_mask;
+  for (int pos = tid; pos < NPOS; pos += NW * 64) {
+    const int ln = pos & 63, kct = pos >> 6;
+    const int k = kct / CT, ct = kct % CT;
+    const int c2 = ln & 15, kg2 = ln >> 4;
+    const int sl2 = c2 / GP, hp2 = c2 % GP;
+    const int m = k * SLOTS + sl2;
+    if (sl2 < SLOTS && m < kModalities && hp2 < G && (wmask & (1 << m))) {
+      float4 s = sm.red[0][pos];
 #pragma unroll
-  for (int k = 0; k < NSETS; ++k)
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) ws.acc[k][ct] *= e;
-#pragma unroll
-  for (int half = NW / 2; half >= 1; half >>= 1) {
-    if (wave >= half && wave < 2 * half) {
-#pragma unroll
-      for (int k = 0; k < NSETS; ++k)
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-          const floatx4 v = ws.acc[k][ct];
-          ms.tree[wave - half][k][ct][lane] = float4{v[0], v[1], v[2], v[3]};
-        }
-    }
-    __syncthreads();
-    if (wave < half) {
-#pragma unroll
-      for (int k = 0; k < NSETS; ++k)
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-          const float4 v = ms.tree[wave][k][ct][lane];
-          ws.acc[k][ct] += floatx4{v.x, v.y, v.z, v.w};
-        }
-    }
-    __syncthreads();
-  }
-  const int wmask = ms.mask;
-  if (wave == 0 && slot < SLOTS && hp < G) {
-    float* part = a.partials + ((static_cast<size_t>(b) * a.hq + h * G + hp) * a.splits + split) * PS;
-#pragma unroll
-    for (int k = 0; k < NSETS; ++k) {
-      const int m = k * SLOTS + slot;
-      if (m < kModalities && (wmask & (1 << m))) {
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-          const floatx4 v = ws.acc[k][ct];
-          *reinterpret_cast<float4*>(part + kPartialHeader + m * D + 16 * ct + 4 * kg) = float4{v[0], v[1], v[2], v[3]};
-        }
+      for (int w = 1; w < NW; ++w) {
+        const float4 v = sm.red[w][pos];
+        s.x += v.x;
+        s.y += v.y;
+        s.z += v.z;
+        s.w += v.w;
       }
+      float* part = a.partials + ((static_cast<size_t>(b) * a.hq + h * G + hp2) * a.splits + split) * PS;
+      *reinterpret_cast<float4*>(part + kPartialHeader + m * D + 16 * ct + 4 * kg2) = s;
     }
   }
   if (tid < G * kPartialHeader) {
     const int hh = tid / kPartialHeader, f = tid % kPartialHeader;
     float* part = a.partials + ((static_cast<size_t>(b) * a.hq + h * G + hh) * a.splits + split) * PS;
     float Mh = -__builtin_inff();
-    for (int w = 0; w < NW; ++w) Mh = fmaxf(Mh, ms.m[w][hh]);
+    for (int w = 0; w < NW; ++w) Mh = fmaxf(Mh, s_m[w][hh]);
     float v = 0.f;
     if (f == 0) {
       v = Mh;
     } else if (f == 1 || (f >= 4 && f < 4 + kModalities)) {
       for (int w = 0; w < NW; ++w) {
-        const float mww = ms.m[w][hh];
-        if (mww != -__builtin_inff()) v += exp2f(mww - Mh) * (f == 1 ? ms.l[w][hh] : ms.s[w][f - 4][hh]);
+        const float mww = s_m[w][hh];
+        if (mww != -__builtin_inff()) v += __builtin_amdgcn_exp2f(mww - Mh) * (f == 1 ? s_l[w][hh] : s_s[w][f - 4][hh]);
       }
     } else if (f == 2) {
       v = __int_as_float(wmask);
@@ -720,11 +807,12 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
 
 template <int D, int SLOTS, int NW>
 void launch_partition(int batch, const DecodeArgs& a, hipStream_t s) {
+  constexpr bool BHL = SLOTS >= 2;   // G <= 8
   const dim3 grid(a.splits, a.hkv, batch);
   if (a.cmid != 0.f)
-    hipLaunchKernelGGL((decode_partition_kernel<D, SLOTS, NW, true>), grid, dim3(NW * 64), 0, s, a);
+    hipLaunchKernelGGL((decode_partition_kernel<D, SLOTS, NW, true, BHL>), grid, dim3(NW * 64), 0, s, a);
   else
-    hipLaunchKernelGGL((decode_partition_kernel<D, SLOTS, NW, false>), grid, dim3(NW * 64), 0, s, a);
+    hipLaunchKernelGGL((decode_partition_kernel<D, SLOTS, NW, false, BHL>), grid, dim3(NW * 64), 0, s, a);
 }
 
 template <int D>

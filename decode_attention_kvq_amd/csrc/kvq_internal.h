@@ -52,6 +52,7 @@ struct RotateArgs {
 //   [7] unused, then [3][d] per-modality value accumulators.
 constexpr int kDecodeWaves = 8;
 constexpr int kPartialHeader = 8;
+constexpr int kPartitionPages = 512;   // pages one partition may span (the kernel keeps their entries in LDS)
 
 struct DecodeArgs {
   const uint8_t* k_codes;

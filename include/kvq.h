@@ -159,8 +159,10 @@ size_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t max_len);
  * [batch][Hq][d] fp32; an empty session gives zeros.  The partition plan
  * comes from max(seq_len_host).  workspace: device, at least
  * kvq_decode_workspace_bytes(cfg, max(seq_len_host)) bytes.
- * Errors: KVQ_ERR_INVALID, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE,
- * KVQ_ERR_LAUNCH.
+ * Errors: KVQ_ERR_INVALID, KVQ_ERR_WORKSPACE, KVQ_ERR_LAUNCH,
+ * KVQ_ERR_UNSUPPORTED (also for a session longer than 4096 partitions of at
+ * most 510 pages each, i.e. 4096 * floor(510 * page_tokens / 256) * 256
+ * positions).
  */
 kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache,
                                 const kvq_params* params, const float* q_rot, float scale,
