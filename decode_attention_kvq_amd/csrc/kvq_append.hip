@@ -6,10 +6,13 @@
 // Method: OmniKVQuant page, Sec. 2 Method (TurboQuant bullet, and the two
 // OmniKVQuant bullets for keys and values).
 //
-// Every decision (statistics, codes) is taken in fp64, with the same
-// operation order as the definition, so that the stored codes and fp16
-// statistics are exactly those of an fp64 reference.  This file is compiled
-// with -ffp-contract=off for that reason.
+// Every decision is taken in fp64.  The statistics follow the definition's
+// operation order, so the stored fp16 LO / HI are exactly those of an fp64
+// reference; the key codes take the division once per channel and the value
+// rotation sums in a fixed order, which can only change a code whose
+// normalised value lies within a few ulps of a decision threshold.  This
+// file is compiled with -ffp-contract=off so that no operation is fused
+// behind the code's back.
 //
 // One launch.  Workgroup (j, h, b) re-quantizes the j-th 32-position group
 // touched by the append of session b, KV head h: all the group's keys (the
@@ -32,14 +35,35 @@ namespace {
 
 constexpr int kAppendThreads = 256;
 
+// Value of lane ^ M (M = 1, 2, 4) for a double: quad permutations through DPP
+// for M = 1, 2, a swizzle for M = 4 (no LDS memory traffic).
+template <int M>
+__device__ __forceinline__ int xor_lane(int v) {
+  if constexpr (M == 1) return __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  if constexpr (M == 2) return __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  return __builtin_amdgcn_ds_swizzle(v, (M << 10) | 0x1F);                                  // bit mode: xor M
+}
+template <int M>
+__device__ __forceinline__ double xor_lane(double v) {
+  const long long u = __double_as_longlong(v);
+  const int lo = xor_lane<M>(static_cast<int>(u & 0xFFFFFFFF));
+  const int hi = xor_lane<M>(static_cast<int>(u >> 32));
+  return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned int>(lo));
+}
+
+// Channel-major staging with rows padded to 33 positions: the writes of the
+// 8-threads-per-position layout and the per-channel reads both spread over
+// the LDS banks.
+constexpr int kPadTok = kGroupTokens + 1;
+
 template <int D>
 struct AppendSmem {
   static constexpr int TQ = kAppendThreads / D;   // parts of the value rotation's i range
   union {
-    double y[kGroupTokens][D];                    // rotated keys (statistics pass)
+    double y[D][kPadTok];                         // rotated keys (statistics pass)
     double r[TQ][kGroupTokens][D];                // value rotation partial sums
   } u;
-  double v[kGroupTokens][D];                      // new values
+  double v[D][kPadTok];                           // new values
   double lohi[2][D];                              // fp16 statistics as fp64
   double n[kGroupTokens];                         // value norms
   __align__(16) uint8_t kblk[8 * D];              // key codes of the group (lane-major)
@@ -161,36 +185,43 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
       }
     }
 #pragma unroll
-    for (int hh = CH; hh < D; hh <<= 1) {
-      const int m = hh / CH;
+    for (int i = 0; i < CH; ++i) {
+      const double p = xor_lane<1>(x[i]);
+      x[i] = (part & 1) ? (p - x[i]) : (x[i] + p);
+    }
 #pragma unroll
-      for (int i = 0; i < CH; ++i) {
-        const double p = __shfl_xor(x[i], m);
-        x[i] = (part & m) ? (p - x[i]) : (x[i] + p);
-      }
+    for (int i = 0; i < CH; ++i) {
+      const double p = xor_lane<2>(x[i]);
+      x[i] = (part & 2) ? (p - x[i]) : (x[i] + p);
+    }
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const double p = xor_lane<4>(x[i]);
+      x[i] = (part & 4) ? (p - x[i]) : (x[i] + p);
     }
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       x[i] = x[i] * a.inv_sqrt_d;
-      sm.u.y[tok][cb + i] = x[i];
-      sm.v[tok][cb + i] = vv[i];
+      sm.u.y[cb + i][tok] = x[i];
+      sm.v[cb + i][tok] = vv[i];
     }
     // Value norms: sum of squares over the thread's channels, then over the
     // 8 threads of the position.
     double ss = 0.0;
 #pragma unroll
     for (int i = 0; i < CH; ++i) ss = ss + vv[i] * vv[i];
-#pragma unroll
-    for (int m = 1; m < 8; m <<= 1) ss = ss + __shfl_xor(ss, m);
+    ss = ss + xor_lane<1>(ss);
+    ss = ss + xor_lane<2>(ss);
+    ss = ss + xor_lane<4>(ss);
     if (part == 0) sm.n[tok] = sqrt(ss);
     __syncthreads();
 
     // ---- key statistics: per channel min / max over the present positions
     if (tid < D) {
-      double lo = sm.u.y[0][tid], hi = lo;
+      double lo = sm.u.y[tid][0], hi = lo;
 #pragma unroll
       for (int t = 1; t < kGroupTokens; ++t) {
-        const double yv = sm.u.y[t][tid];
+        const double yv = sm.u.y[tid][t];
         lo = t < s_end ? fmin(lo, yv) : lo;
         hi = t < s_end ? fmax(hi, yv) : hi;
       }
@@ -198,13 +229,18 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
       uint16_t* st = a.k_stats + static_cast<size_t>(blk) * 2 * D;
       st[tid] = lo16;
       st[D + tid] = hi16;
-      sm.lohi[0][tid] = static_cast<double>(f16_bits_to_f32(lo16));
-      sm.lohi[1][tid] = static_cast<double>(f16_bits_to_f32(hi16));
+      // LO and the per-channel factor (c3 - c0) / (HI - LO) (HI - LO is exact
+      // in fp64); 0 marks HI == LO (every code 0).
+      const double LO = static_cast<double>(f16_bits_to_f32(lo16)), HI = static_cast<double>(f16_bits_to_f32(hi16));
+      sm.lohi[0][tid] = LO;
+      sm.lohi[1][tid] = HI > LO ? (a.c3 - a.c0) / (HI - LO) : 0.0;
     }
     __syncthreads();
 
-    // ---- key codes: z = c0 + ((y - LO) * (c3 - c0)) / (HI - LO); code = thresholds reached
-    const double span_c = a.c3 - a.c0;
+    // ---- key codes: z = c0 + (y - LO) (c3 - c0) / (HI - LO); code = thresholds
+    // reached.  The division is taken once per channel; z may differ from the
+    // definition's rounding order in its last bits, which can only move a
+    // value lying within a few ulps of a threshold.
 #pragma unroll
     for (int q4 = 0; q4 < CH / 4; ++q4) {
       uint32_t byte = 0;
@@ -212,9 +248,9 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
       for (int i = 0; i < 4; ++i) {
         const int c = cb + 4 * q4 + i;
         uint32_t code = 0;
-        const double LO = sm.lohi[0][c], HI = sm.lohi[1][c];
-        if (present && HI > LO) {
-          const double z = a.c0 + ((x[4 * q4 + i] - LO) * span_c) / (HI - LO);
+        const double LO = sm.lohi[0][c], f = sm.lohi[1][c];
+        if (present && f > 0.0) {
+          const double z = a.c0 + (x[4 * q4 + i] - LO) * f;
           code = (z >= a.thr0 ? 1u : 0u) + (z >= a.thr1 ? 1u : 0u) + (z >= a.thr2 ? 1u : 0u);
         }
         byte |= code << (2 * i);
@@ -237,7 +273,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
         // four interleaved partial sums, added in a fixed order
         double acc4[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-        for (int i = 0; i < IQ; ++i) acc4[i & 3] = fma(static_cast<double>(rr[i]), sm.v[s][i0 + i], acc4[i & 3]);
+        for (int i = 0; i < IQ; ++i) acc4[i & 3] = fma(static_cast<double>(rr[i]), sm.v[i0 + i][s], acc4[i & 3]);
         sm.u.r[pq][s][jc] = (acc4[0] + acc4[1]) + (acc4[2] + acc4[3]);
       }
     }

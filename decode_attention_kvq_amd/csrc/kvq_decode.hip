@@ -613,9 +613,9 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_partition_kernel(DecodeArgs
 // out = sum_m R_m A_m / l.  Every global load (headers, accumulator blocks,
 // rotation rows) is issued before the first reduction, so the kernel costs
 // one memory round trip; all sums run in a fixed order (bitwise
-// reproducible).  The RB row blocks of one head are numbered so that they
+// reproducible).  All workgroups of one KV head are numbered so that they
 // land on the same XCD (workgroups are dealt to the 8 XCDs round robin) and
-// share the head's partials through that XCD's L2.
+// share the head's rotations and partials through that XCD's L2.
 constexpr int kMergeThreads = 512;
 constexpr int kMergeChunk = 16;    // partial blocks in flight per thread
 constexpr int kXcds = 8;
@@ -645,12 +645,17 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
   __shared__ float s_red[NW][2 + kModalities];
   __shared__ float s_M;
 
+  // Workgroup -> (session b, KV head h, query head of the group gq, row
+  // block rb), with every workgroup of one (b, h) on the XCD (b Hkv + h) mod 8:
+  // they share that KV head's rotations and partials through one L2.
   const int x = blockIdx.x % kXcds, y = blockIdx.x / kXcds;
-  const int rb = y % RB;
-  const int hi = (y / RB) * kXcds + x;             // b * Hq + i
-  if (hi >= a.batch * a.hq) return;
-  const int i = hi % a.hq;
-  const int h = i / a.group;
+  const int per_key = a.group * RB;
+  const int key = (y / per_key) * kXcds + x;       // b * Hkv + h
+  if (key >= a.batch * a.hkv) return;
+  const int gq = (y % per_key) / RB, rb = y % RB;
+  const int h = key % a.hkv;
+  const int i = h * a.group + gq;
+  const int hi = (key / a.hkv) * a.hq + i;         // b * Hq + i
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = a.splits;
   const size_t head = static_cast<size_t>(hi);
@@ -820,8 +825,8 @@ hipError_t launch_decode_t(int batch, const DecodeArgs& a, hipStream_t s) {
   if (a.group <= 5) launch_partition<D, 3, kDecodeWaves>(batch, a, s);
   else if (a.group <= 8) launch_partition<D, 2, kDecodeWaves>(batch, a, s);
   else launch_partition<D, 1, kDecodeWaves / 2>(batch, a, s);
-  const int heads = a.hq * batch;
-  const dim3 mgrid(kXcds * MergeShape<D>::RB * ((heads + kXcds - 1) / kXcds));
+  const int keys = a.hkv * batch;
+  const dim3 mgrid(kXcds * ((keys + kXcds - 1) / kXcds) * a.group * MergeShape<D>::RB);
   if (a.cmid != 0.f)
     hipLaunchKernelGGL((decode_merge_kernel<D, true>), mgrid, dim3(kMergeThreads), 0, s, a);
   else
