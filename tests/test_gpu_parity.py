@@ -227,3 +227,84 @@ def test_graph_replayed_single_token_appends():
     a, b = cache.host_arrays(), ref.host_arrays()
     for key in ("k_codes", "k_stats", "v_codes", "v_norms", "modality", "seq_len"):
         np.testing.assert_array_equal(a[key], b[key], err_msg=key)
+
+
+# ------------------------------------------------------- full-size workloads
+
+def _decode_parity(w, cfg, params, cache, sessions, out=None):
+    import decode_attention_kvq_amd as K
+    h = H()
+    scale = h.default_scale(w)
+    if out is None:
+        q_rot = K.kvq_rotate_query(cfg, params, h.query_tensor(w))
+        out = K.kvq_decode_attention(cfg, cache, params, q_rot, scale).cpu().numpy()
+    ref = h.oracle_decode_over_gpu_codes(w, cfg, cache, O.as_f64(w.q, w.dtype), sessions, scale)
+    worst = max(float(h.normwise_rel_err(out[b].astype(np.float64), ref[b]).max()) for b in sessions)
+    return worst
+
+
+def test_full_80k_context():
+    """The benchmark's workload at full size (81,920 positions, 28/4 heads):
+    every code and statistic, and every head's output."""
+    h = H()
+    w = generate(2)
+    _say(f"full 80K: {int(w.lengths[0])} positions")
+    cfg, params, cache = h.build(w, chunks=[8192])
+    total, mism = h.check_codes(w, cfg, cache, [0])
+    _say(f"codes: {total} elements, {mism} boundary mismatches")
+    worst = _decode_parity(w, cfg, params, cache, [0])
+    _say(f"decode worst normwise rel err {worst:.3e}")
+    assert worst <= h.ATTN_TOL
+
+
+def test_full_batched_paged_sessions():
+    """32 sessions of 8K..64K positions under a random page table, decoded in
+    one launch; codes and outputs of a sample of sessions against the oracle."""
+    import decode_attention_kvq_amd as K
+    h = H()
+    w = generate(3)
+    _say(f"full batched: {w.cfg.batch} sessions, {int(w.lengths.sum())} positions")
+    cfg, params, cache = h.build(w, chunks=[16384])
+    q_rot = K.kvq_rotate_query(cfg, params, h.query_tensor(w))
+    out = K.kvq_decode_attention(cfg, cache, params, q_rot, h.default_scale(w)).cpu().numpy()
+    sample = [0, int(np.argmax(w.lengths)), int(np.argmin(w.lengths)), 31]
+    total, mism = h.check_codes(w, cfg, cache, sample)
+    _say(f"codes of sessions {sample}: {total} elements, {mism} boundary mismatches")
+    worst = _decode_parity(w, cfg, params, cache, sample, out)
+    _say(f"decode worst normwise rel err {worst:.3e}")
+    assert worst <= h.ATTN_TOL
+    assert np.all(np.isfinite(out))
+
+
+def test_full_stream_loop_append():
+    """A 131,072-position cache (32/8 heads), then one 1,024-position chunk
+    (640 video + 25 audio + 359 text) appended in one call, then the decode."""
+    h = H()
+    w = generate(4)
+    n0 = int(w.prefix_lengths[0])
+    _say(f"stream loop: prefill {n0}, append {int(w.lengths[0]) - n0}")
+    cfg, params, cache = h.build(w, upto=[n0 + 5], chunks=[16384])   # an open group before the chunk
+    h.append_range(cfg, cache, params, w, 0, n0 + 5, int(w.lengths[0]))
+    total, mism = h.check_codes(w, cfg, cache, [0])
+    _say(f"codes: {total} elements, {mism} boundary mismatches")
+    worst = _decode_parity(w, cfg, params, cache, [0])
+    _say(f"decode worst normwise rel err {worst:.3e}")
+    assert worst <= h.ATTN_TOL
+
+
+def test_degenerate_inputs():
+    """Zero value vectors (norm 0: codes 0), key channels constant over a
+    whole group (HI == LO: codes 0), and a group that is all one value."""
+    h = H()
+    w = generate(1, length=700)
+    k, v = w.k[0], w.v[0]
+    v[100] = 0                                   # bf16 +0
+    v[101:133] = 0
+    k[64:96, 0, 5] = k[64, 0, 5]                 # channel 5 of KV head 0 constant in group 2
+    k[160:192, 1, :] = k[160, 1, :]              # a whole group of identical keys (after rotation too)
+    _say("degenerate inputs cfg1 700")
+    cfg, params, cache = h.build(w, chunks=[97, 3, 600])
+    total, mism = h.check_codes(w, cfg, cache, [0])
+    worst = _decode_parity(w, cfg, params, cache, [0])
+    _say(f"codes {total} ({mism} at thresholds), decode worst {worst:.3e}")
+    assert worst <= h.ATTN_TOL
