@@ -153,6 +153,15 @@ struct WaveState {
 
 __device__ __forceinline__ int group_pos(int kg, int i) { return (i < 4) ? (4 * kg + i) : (16 + 4 * kg + i - 4); }
 
+// OR of a small per-lane bit set over the wavefront, one ballot per bit
+// (an LDS atomic with a per-lane operand would be serialised lane by lane).
+__device__ __forceinline__ int wave_or_bits(int bits) {
+  int r = 0;
+#pragma unroll
+  for (int m = 0; m < kModalities; ++m) r |= (__ballot((bits >> m) & 1) != 0ull) ? (1 << m) : 0;
+  return r;
+}
+
 // Exact fp32 difference of fp16 fields (low or high half) of two registers.
 __device__ __forceinline__ float f16_diff_lo(uint32_t a2, uint32_t b2) {
   float d;
@@ -545,7 +554,10 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_partition_kernel(DecodeArgs
       }
     }
   }
-  if (ws.mask) atomicOr(&s_mask, ws.mask);
+  {
+    const int wm = wave_or_bits(ws.mask);
+    if (lane == 0 && wm) atomicOr(&s_mask, wm);
+  }
   __syncthreads();   // every wavefront is past its main loop: the byte table is dead
   // Bring the value columns (head hp) to the workgroup max of that head and
   // hand them to LDS; then every thread sums a share over the wavefronts in
@@ -599,6 +611,515 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_partition_kernel(DecodeArgs
       for (int w = 0; w < NW; ++w) {
         const float mww = s_m[w][hh];
         if (mww != -__builtin_inff()) v += __builtin_amdgcn_exp2f(mww - Mh) * (f == 1 ? s_l[w][hh] : s_s[w][f - 4][hh]);
+      }
+    } else if (f == 2) {
+      v = __int_as_float(wmask);
+    }
+    part[f] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Producer / consumer partition kernel (G <= 8).
+//
+// kConsumers consumer wavefronts each take one 32-position group per step:
+// codes -> operands, scores, online softmax, value sums.  kProducers =
+// kConsumers / 2 producer wavefronts prepare, one step ahead, everything that
+// depends on the group statistics and the query: q~ = q (HI - LO) / 2 as an
+// fp16 hi + lo pair in the consumers' operand layout, and the group bias
+// sum_c q_c (LO_c + HI_c) / 2.  A producer serves two consumers at once: its
+// 16 matrix-core columns hold the 8 query heads of each of the two groups.
+// One workgroup barrier per step; every wavefront runs the same number of
+// steps.
+constexpr int kConsumers = 8;
+constexpr int kProducers = kConsumers / 2;
+constexpr int kPcWaves = kConsumers + kProducers;
+
+template <int D>
+struct __align__(16) QtSlot {
+  static constexpr int ROW = D + 8;     // fp16 per row (padding spreads the rows over the LDS banks)
+  _Float16 qt[2][8][ROW];               // [hi / lo][query head of the group][channel]
+  float bias[8];
+};
+
+// Loads of one group for a consumer: codes, norms and modality bytes.
+template <int D>
+struct ConsumerLoad {
+  uint32_t kc[D / 32];
+  uint32_t vc[D / 32];
+  uint2 nrm0, nrm1;
+  uint32_t md0, md1;
+};
+
+template <int D>
+__device__ __forceinline__ size_t block_index(const DecodeArgs& a, int h, int t0, int phys) {
+  return (static_cast<size_t>(phys) * a.hkv + h) * (a.page_tokens / kGroupTokens) + (t0 % a.page_tokens) / kGroupTokens;
+}
+
+// Buffer resource over `bytes` bytes at `base` (raw, untyped).  A load whose
+// offset is outside [0, bytes) returns zero without a memory access, so a
+// wavefront can issue the loads of a group it will not use (bytes = 0) and
+// keep the count of its loads in flight fixed.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// Loads of one group for a consumer; a group outside [0, te) or on an
+// unmapped page reads nothing (zeros) and is flagged invalid.
+template <int D>
+__device__ __forceinline__ void consumer_load(const DecodeArgs& a, int h, int t0, int te, int lane, int kg, int phys0,
+                                              ConsumerLoad<D>& g, bool& ok) {
+  ok = t0 < te && t0 / a.page_tokens < a.max_pages && phys0 >= 0 && phys0 < a.num_pages;
+  const int phys = ok ? phys0 : 0;
+  const int tin = ok ? t0 % a.page_tokens : 0;
+  const size_t blk = block_index<D>(a, h, ok ? t0 : 0, phys);
+  const int n_codes = ok ? 8 * D : 0;
+  const auto rk = span_rsrc(a.k_codes + blk * 8 * D, n_codes);
+  const auto rv = span_rsrc(a.v_codes + blk * 8 * D, n_codes);
+  const auto rn = span_rsrc(a.v_norms + (static_cast<size_t>(phys) * a.hkv + h) * a.page_tokens + tin,
+                            ok ? 2 * kGroupTokens : 0);
+  const auto rm = span_rsrc(a.modality + static_cast<size_t>(phys) * a.page_tokens + tin, ok ? kGroupTokens : 0);
+  if constexpr (D == 128) {
+    const uint4 k4 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, lane * 16, 0, 0));
+    const uint4 v4 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, lane * 16, 0, 0));
+    g.kc[0] = k4.x; g.kc[1] = k4.y; g.kc[2] = k4.z; g.kc[3] = k4.w;
+    g.vc[0] = v4.x; g.vc[1] = v4.y; g.vc[2] = v4.z; g.vc[3] = v4.w;
+  } else {
+    const uint2 k2 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rk, lane * 8, 0, 0));
+    const uint2 v2 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rv, lane * 8, 0, 0));
+    g.kc[0] = k2.x; g.kc[1] = k2.y;
+    g.vc[0] = v2.x; g.vc[1] = v2.y;
+  }
+  g.nrm0 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rn, 8 * kg, 0, 0));
+  g.nrm1 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rn, 32 + 8 * kg, 0, 0));
+  g.md0 = __builtin_amdgcn_raw_buffer_load_b32(rm, 4 * kg, 0, 0);
+  g.md1 = __builtin_amdgcn_raw_buffer_load_b32(rm, 16 + 4 * kg, 0, 0);
+}
+
+// This lane's share (D / 64 words) of a group's LO / HI rows.
+template <int D>
+__device__ __forceinline__ void stats_load(const DecodeArgs& a, int h, int t0, int te, int lane, int phys0,
+                                           uint32_t (&st)[D / 64]) {
+  const bool ok = t0 < te && t0 / a.page_tokens < a.max_pages && phys0 >= 0 && phys0 < a.num_pages;
+  const size_t blk = block_index<D>(a, h, ok ? t0 : 0, ok ? phys0 : 0);
+  const auto rs = span_rsrc(a.k_stats + blk * 2 * D, ok ? 2 * D * 2 : 0);
+  if constexpr (D == 128) {
+    const uint2 s2 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, lane * 8, 0, 0));
+    st[0] = s2.x; st[1] = s2.y;
+  } else {
+    st[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, lane * 4, 0, 0);
+  }
+}
+
+// Producer: q~ hi / lo and the bias of two groups (A for the lanes of columns
+// 0..7, B for columns 8..15) into the consumers' slots.
+template <int D>
+__device__ __forceinline__ void produce(const uint32_t (&stA)[D / 64], const uint32_t (&stB)[D / 64],
+                                        uint16_t* stage, QtSlot<D>* slotA, QtSlot<D>* slotB, int lane, int kg,
+                                        int col, const float (&hq)[D / 32][8], const half8 (&bq)[D / 32]) {
+  constexpr int KT = D / 32;
+  constexpr int ROW = QtSlot<D>::ROW;
+  // Stage both groups' LO / HI rows (group A at stage, B at stage + 2D).
+  if constexpr (D == 128) {
+    reinterpret_cast<uint2*>(stage)[lane] = uint2{stA[0], stA[1]};
+    reinterpret_cast<uint2*>(stage + 2 * D)[lane] = uint2{stB[0], stB[1]};
+  } else {
+    reinterpret_cast<uint32_t*>(stage)[lane] = stA[0];
+    reinterpret_cast<uint32_t*>(stage + 2 * D)[lane] = stB[0];
+  }
+  wave_sync();
+  const int grp = col >> 3;                       // 0: group A, 1: group B
+  const uint16_t* st = stage + grp * 2 * D;
+  QtSlot<D>* slot = grp ? slotB : slotA;
+  const int head = col & 7;
+  floatx4 bias4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) {
+    const uint4 lo4 = *reinterpret_cast<const uint4*>(st + 32 * kt + 8 * kg);
+    const uint4 hi4 = *reinterpret_cast<const uint4*>(st + D + 32 * kt + 8 * kg);
+    // Rows 0..7 of the product carry group A's statistics, rows 8..15 group
+    // B's; columns are q's fp16 hi (0..7) and lo (8..15) parts per head.
+    bias4 = mfma(__builtin_bit_cast(half8, lo4), bq[kt], bias4);
+    bias4 = mfma(__builtin_bit_cast(half8, hi4), bq[kt], bias4);
+    const uint32_t lw[4] = {lo4.x, lo4.y, lo4.z, lo4.w};
+    const uint32_t hw[4] = {hi4.x, hi4.y, hi4.z, hi4.w};
+    uint32_t th[4], tl[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const float d0 = f16_diff_lo(hw[p], lw[p]);
+      const float d1 = f16_diff_hi(hw[p], lw[p]);
+      const uint2 s = split_product(hq[kt][2 * p], d0, hq[kt][2 * p + 1], d1);
+      th[p] = s.x;
+      tl[p] = s.y;
+    }
+    *reinterpret_cast<uint4*>(&slot->qt[0][head][32 * kt + 8 * kg]) = uint4{th[0], th[1], th[2], th[3]};
+    *reinterpret_cast<uint4*>(&slot->qt[1][head][32 * kt + 8 * kg]) = uint4{tl[0], tl[1], tl[2], tl[3]};
+  }
+  // Lane (h, kg): rows 4 kg..4 kg + 3 (group kg < 2 ? A : B), column h's part.
+  float bias = bias4[0];
+  bias += __uint_as_float(static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(__float_as_uint(bias)), 0x128, 0xF, 0xF, false)));
+  if (col < 8 && (kg & 1) == 0) (kg ? slotB : slotA)->bias[col] = bias;
+  (void)ROW;
+  wave_sync();   // the staging may be overwritten by the next step
+}
+
+// Consumer: one group, given its q~ slot.  `partial`: the group extends past
+// te (the session's last, partially filled group).
+template <int D, int SLOTS, bool ASYM>
+__device__ __forceinline__ void consume(const ConsumerLoad<D>& cur, const QtSlot<D>* slot, int t0, int te,
+                                        bool partial, int kg, int col, const uint2* tab, uint32_t lane_off,
+                                        WaveState<D, SLOTS, ASYM>& ws) {
+  constexpr int KT = D / 32;
+  constexpr int CT = D / 16;
+  constexpr int GP = Slots<SLOTS>::GP;
+  constexpr int NSETS = Slots<SLOTS>::NSETS;
+  const int head = col & 7;
+  const float bias = slot->bias[head];
+  floatx4 sc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) {
+    const half8 qt_hi = *reinterpret_cast<const half8*>(&slot->qt[0][head][32 * kt + 8 * kg]);
+    const half8 qt_lo = *reinterpret_cast<const half8*>(&slot->qt[1][head][32 * kt + 8 * kg]);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int j0 = mt * (D / 16) + kt * 2;   // code bytes j0, j0 + 1 of this (mt, kt)
+      const uint2 x0 = lookup(tab, cur.kc[j0 >> 2], byte_sel(j0 & 3), lane_off);
+      const uint2 x1 = lookup(tab, cur.kc[(j0 + 1) >> 2], byte_sel((j0 + 1) & 3), lane_off);
+      const half8 ak = as_half8(x0, x1);
+      sc[mt] = mfma(ak, qt_hi, sc[mt]);
+      sc[mt] = mfma(ak, qt_lo, sc[mt]);
+    }
+  }
+  uint32_t vmask[4] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+  if (partial) {
+    // positions at or past te: score -inf (weight 0), weight bits cleared.
+    // (The empty asm keeps these compares out of the full-group path.)
+    int rem = te - t0;
+    asm volatile("" : "+s"(rem));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bool v = group_pos(kg, i) < rem;
+      sc[i >> 2][i & 3] = v ? sc[i >> 2][i & 3] : -__builtin_inff();
+      if (!v) vmask[i >> 1] &= (i & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+    }
+  }
+  float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                   fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+  mx = rows_max(mx) + bias;
+  // Lazy reference max (see kLazyMax): weights 2^(s - m_run) stay <= 1.
+  if (__any(mx > ws.m_run)) {
+    const float m_new = fmaxf(ws.m_run, mx + kLazyMax);
+    const float alpha = exp2f(ws.m_run - m_new);   // 0 on the first group
+    ws.l_run *= alpha;
+    const float alpha_v = __uint_as_float(to_value_column<SLOTS>(__float_as_uint(alpha)));
+#pragma unroll
+    for (int k = 0; k < NSETS; ++k) {
+      if constexpr (ASYM) ws.accs[k] *= alpha_v;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) ws.acc[k][ct] *= alpha_v;
+    }
+    ws.m_run = m_new;
+  }
+  const float off = ws.m_run - bias;
+  const uint32_t n4[4] = {cur.nrm0.x, cur.nrm0.y, cur.nrm1.x, cur.nrm1.y};
+  uint32_t wp[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int i0 = 2 * r, i1 = 2 * r + 1;
+    // arguments are <= 0 (or -inf): the raw base-2 exponential flushes only results below 2^-126
+    const float p0 = __builtin_amdgcn_exp2f(sc[i0 >> 2][i0 & 3] - off);
+    const float p1 = __builtin_amdgcn_exp2f(sc[i1 >> 2][i1 & 3] - off);
+    ws.l_run += p0 + p1;
+    wp[r] = to_value_column<SLOTS>(weight_pair(p0, p1, n4[r]) & vmask[r]);
+  }
+  half8 av[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    const int j0 = 2 * ct;
+    const uint2 x0 = lookup(tab, cur.vc[j0 >> 2], byte_sel(j0 & 3), lane_off);
+    const uint2 x1 = lookup(tab, cur.vc[(j0 + 1) >> 2], byte_sel((j0 + 1) & 3), lane_off);
+    av[ct] = as_half8(x0, x1);
+  }
+  const int slot_c = col / GP;
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(cur.md0 & 0xFFu);
+  const bool uniform = !partial && __all(cur.md0 == m0 * 0x01010101u && cur.md1 == m0 * 0x01010101u);
+  const uint32_t md[2] = {cur.md0, cur.md1};
+#pragma unroll
+  for (int k = 0; k < NSETS; ++k) {
+    const uint32_t lo_mod = static_cast<uint32_t>(k * SLOTS);
+    const uint32_t my_mod = lo_mod + static_cast<uint32_t>(slot_c);
+    const bool col_ok = slot_c < SLOTS && my_mod < kModalities;
+    bool present;
+    uint32_t bm[4];
+    int got = 0;
+    if (uniform) {
+      present = m0 >= lo_mod && m0 < lo_mod + SLOTS && m0 < kModalities;
+      got = present ? (1 << m0) : 0;
+      const bool take = col_ok && my_mod == m0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) bm[r] = take ? wp[r] : 0u;
+    } else {
+      int rem = partial ? te - t0 : kGroupTokens;
+      uint32_t mdo[2] = {md[0], md[1]};
+      asm volatile("" : "+s"(rem), "+v"(mdo[0]), "+v"(mdo[1]));   // keeps this path's work inside it
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        uint32_t keep = 0;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int i = 2 * r + u;
+          const uint32_t tm = (mdo[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+          const bool valid = group_pos(kg, i) < rem;
+          if (valid && tm >= lo_mod && tm < lo_mod + SLOTS && tm < kModalities) got |= 1 << tm;
+          keep |= (col_ok && tm == my_mod) ? (0xFFFFu << (16 * u)) : 0u;
+        }
+        bm[r] = wp[r] & keep;
+      }
+      present = __any(got != 0);
+    }
+    if (present) {
+      const half8 bw = __builtin_bit_cast(half8, uint4{bm[0], bm[1], bm[2], bm[3]});
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) ws.acc[k][ct] = mfma(av[ct], bw, ws.acc[k][ct]);
+      if constexpr (ASYM) {
+        const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
+        ws.accs[k] = mfma(ones, bw, ws.accs[k]);
+      }
+      ws.mask |= got;
+    }
+  }
+}
+
+template <int D, int SLOTS, bool ASYM>
+__global__ __launch_bounds__(kPcWaves * 64, 1) void decode_partition_pc_kernel(DecodeArgs a) {
+  constexpr int KT = D / 32;
+  constexpr int CT = D / 16;
+  constexpr int GP = Slots<SLOTS>::GP;
+  constexpr int NSETS = Slots<SLOTS>::NSETS;
+  constexpr int PS = kPartialHeader + kModalities * D;
+  constexpr int NT = kPcWaves * 64;
+  constexpr int NPOS = NSETS * CT * 64;   // float4 accumulator slots of one consumer
+  union Smem {
+    struct {
+      uint2 tab[256 * kTabCopies];              // 64 KB byte table
+      QtSlot<D> slots[kConsumers][2];           // q~ and bias per consumer, double-buffered by step
+      uint16_t stage[kProducers][2][2][D];      // producers' staging of two groups' LO / HI rows
+    } s;
+    float4 red[kConsumers][NPOS];               // the consumers' rescaled accumulators
+  };
+  __shared__ Smem sm;
+  __shared__ float s_m[kConsumers][kMaxGroupHeads];
+  __shared__ float s_l[kConsumers][kMaxGroupHeads];
+  __shared__ float s_s[kConsumers][kModalities][kMaxGroupHeads];
+  __shared__ int s_mask;
+  __shared__ int s_pt[kPageRun];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool producer = wave >= kConsumers;
+  const int c = wave;                              // consumer index (wave < kConsumers)
+  const int p = wave - kConsumers;                 // producer index (wave >= kConsumers)
+  const int kg = lane >> 4, col = lane & 15;
+  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int G = a.group;
+  const int L = a.seq_len[b];
+  const int tb = split * a.split_tokens;
+  const int te = (split == a.splits - 1) ? L : min(tb + a.split_tokens, L);
+  const int ng = te > tb ? (te - tb + kGroupTokens - 1) / kGroupTokens : 0;   // groups of the partition
+  const int steps = (ng + kConsumers - 1) / kConsumers;
+  const int page0 = tb / a.page_tokens;
+  const __attribute__((address_space(4))) int32_t* ptab =
+      (const __attribute__((address_space(4))) int32_t*)(a.page_table + static_cast<size_t>(b) * a.max_pages);
+  auto gpos = [&](int step, int cons) { return tb + (step * kConsumers + cons) * kGroupTokens; };
+
+  // Common set-up of both roles: page run of the partition and byte table.
+  auto setup = [&]() {
+    for (int i = tid; i < kPageRun; i += NT) {
+      const int pg = page0 + i;
+      s_pt[i] = pg < a.max_pages ? ptab[pg] : -1;
+    }
+    uint32_t lvl[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) lvl[k] = (a.level_f16[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
+    for (int i = tid; i < 256 * kTabCopies; i += NT) {
+      const int e = i / kTabCopies;
+      sm.s.tab[i] = uint2{lvl[e & 3] | (lvl[(e >> 2) & 3] << 16), lvl[(e >> 4) & 3] | (lvl[e >> 6] << 16)};
+    }
+    if (tid == 0) s_mask = 0;
+  };
+
+  auto pt_at = [&](int t) { return s_pt[min(t / a.page_tokens - page0, kPageRun - 1)]; };
+  auto pt_direct = [&](int t) { return ptab[min(t / a.page_tokens, a.max_pages - 1)]; };
+
+  // The two roles run separate loops over the same barriers, so neither holds
+  // the other's registers.  Each loop body covers two steps (even, then odd)
+  // with fixed buffers and unconditional loads, which keeps the compiler's
+  // count of loads in flight exact; steps past the end compute nothing and
+  // read the fallback group.  Barriers per role: 1 + 2 ceil((steps + 1) / 2).
+  if (producer) {
+    // ---- producer: step u's statistics in pst[u & 1] (two groups each)
+    uint32_t pst0[2][D / 64], pst1[2][D / 64];
+#pragma unroll
+    for (int gg = 0; gg < 2; ++gg) {
+      const int t0 = gpos(0, 2 * p + gg), t1 = gpos(1, 2 * p + gg);
+      stats_load<D>(a, h, t0, te, lane, pt_direct(t0), pst0[gg]);
+      stats_load<D>(a, h, t1, te, lane, pt_direct(t1), pst1[gg]);
+    }
+    float hq[KT][8];
+    half8 bq[KT];
+    const int qh = h * G + min(col & 7, G - 1);
+    const float4* qp = reinterpret_cast<const float4*>(a.q_rot + (static_cast<size_t>(b) * a.hq + qh) * D);
+    const float qs = a.scale_log2e * 0.5f;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      const float4 q0 = qp[(32 * kt + 8 * kg) / 4], q1 = qp[(32 * kt + 8 * kg) / 4 + 1];
+      const float qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float v = qv[i] * qs;
+        hq[kt][i] = v;
+        const _Float16 hi = static_cast<_Float16>(v);
+        bq[kt][i] = col < 8 ? hi : static_cast<_Float16>(v - static_cast<float>(hi));
+      }
+    }
+    setup();
+    __syncthreads();
+    uint16_t* stage = &sm.s.stage[p][0][0][0];
+    for (int s = -1; s < steps; s += 2) {
+      // step s + 1 (even) into slot 0, then fetch step s + 3
+      if (s + 1 < steps)
+        produce<D>(pst0[0], pst0[1], stage, &sm.s.slots[2 * p][0], &sm.s.slots[2 * p + 1][0], lane, kg, col, hq, bq);
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg) {
+        const int t = gpos(s + 3, 2 * p + gg);
+        stats_load<D>(a, h, t, te, lane, pt_at(t), pst0[gg]);
+      }
+      __syncthreads();
+      // step s + 2 (odd) into slot 1, then fetch step s + 4
+      if (s + 2 < steps)
+        produce<D>(pst1[0], pst1[1], stage, &sm.s.slots[2 * p][1], &sm.s.slots[2 * p + 1][1], lane, kg, col, hq, bq);
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg) {
+        const int t = gpos(s + 4, 2 * p + gg);
+        stats_load<D>(a, h, t, te, lane, pt_at(t), pst1[gg]);
+      }
+      __syncthreads();
+    }
+    __syncthreads();   // merge: consumers hand over their accumulators
+  } else {
+    // ---- consumer: step u's group in buf[u & 1]
+    ConsumerLoad<D> buf0, buf1;
+    bool ok0, ok1 = false;
+    {
+      const int t = gpos(0, c);
+      consumer_load<D>(a, h, t, te, lane, kg, pt_direct(t), buf0, ok0);
+    }
+    const uint32_t lane_off = static_cast<uint32_t>(lane & (kTabCopies - 1)) << 3;
+    WaveState<D, SLOTS, ASYM> ws;
+    ws.m_run = -__builtin_inff();
+    ws.l_run = 0.f;
+    ws.mask = 0;
+#pragma unroll
+    for (int k = 0; k < NSETS; ++k)
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) ws.acc[k][ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < (ASYM ? NSETS : 1); ++k) ws.accs[k] = floatx4{0.f, 0.f, 0.f, 0.f};
+    setup();
+    __syncthreads();
+    const uint2* tab = sm.s.tab;
+    for (int s = -1; s < steps; s += 2) {
+      // step s (odd; none before the first pass), then fetch step s + 2
+      if (s >= 0 && ok1) {
+        const int t0 = gpos(s, c);
+        consume<D, SLOTS, ASYM>(buf1, &sm.s.slots[c][1], t0, te, t0 + kGroupTokens > te, kg, col, tab, lane_off, ws);
+      }
+      {
+        const int t = gpos(s + 2, c);
+        consumer_load<D>(a, h, t, te, lane, kg, pt_at(t), buf1, ok1);
+      }
+      __syncthreads();
+      // step s + 1 (even), then fetch step s + 3
+      if (ok0) {
+        const int t0 = gpos(s + 1, c);
+        consume<D, SLOTS, ASYM>(buf0, &sm.s.slots[c][0], t0, te, t0 + kGroupTokens > te, kg, col, tab, lane_off, ws);
+      }
+      {
+        const int t = gpos(s + 3, c);
+        consumer_load<D>(a, h, t, te, lane, kg, pt_at(t), buf0, ok0);
+      }
+      __syncthreads();
+    }
+
+    // ---- merge the consumers of the workgroup
+    const int slot_c = col / GP, hp = col % GP;
+    const float l_col = rows_sum(ws.l_run);
+    if (kg == 0) {
+      s_m[c][col] = ws.m_run;
+      s_l[c][col] = l_col;
+      if (slot_c < SLOTS) {
+#pragma unroll
+        for (int k = 0; k < NSETS; ++k) {
+          const int m = k * SLOTS + slot_c;
+          if (m < kModalities) s_s[c][m][hp] = ASYM ? ws.accs[ASYM ? k : 0][0] : 0.f;
+        }
+      }
+    }
+    {
+      const int wm = wave_or_bits(ws.mask);
+      if (lane == 0 && wm) atomicOr(&s_mask, wm);
+    }
+    __syncthreads();   // the table and slots are dead from here on
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int w = 0; w < kConsumers; ++w) M = fmaxf(M, s_m[w][hp]);
+    const float mw = s_m[c][hp];
+    // (arguments <= 0: the raw base-2 exponential only flushes results below 2^-126)
+    const float e = (mw == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+#pragma unroll
+    for (int k = 0; k < NSETS; ++k)
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const floatx4 v = ws.acc[k][ct] * e;
+        sm.red[c][(k * CT + ct) * 64 + lane] = float4{v[0], v[1], v[2], v[3]};
+      }
+  }
+  __syncthreads();
+  const int wmask = s_mask;
+  for (int pos = tid; pos < NPOS; pos += NT) {
+    const int ln = pos & 63, kct = pos >> 6;
+    const int k = kct / CT, ct = kct % CT;
+    const int c2 = ln & 15, kg2 = ln >> 4;
+    const int sl2 = c2 / GP, hp2 = c2 % GP;
+    const int m = k * SLOTS + sl2;
+    if (sl2 < SLOTS && m < kModalities && hp2 < G && (wmask & (1 << m))) {
+      float4 sum = sm.red[0][pos];
+#pragma unroll
+      for (int w = 1; w < kConsumers; ++w) {
+        const float4 v = sm.red[w][pos];
+        sum.x += v.x;
+        sum.y += v.y;
+        sum.z += v.z;
+        sum.w += v.w;
+      }
+      float* part = a.partials + ((static_cast<size_t>(b) * a.hq + h * G + hp2) * a.splits + split) * PS;
+      *reinterpret_cast<float4*>(part + kPartialHeader + m * D + 16 * ct + 4 * kg2) = sum;
+    }
+  }
+  if (tid < G * kPartialHeader) {
+    const int hh = tid / kPartialHeader, f = tid % kPartialHeader;
+    float* part = a.partials + ((static_cast<size_t>(b) * a.hq + h * G + hh) * a.splits + split) * PS;
+    float Mh = -__builtin_inff();
+    for (int w = 0; w < kConsumers; ++w) Mh = fmaxf(Mh, s_m[w][hh]);
+    float v = 0.f;
+    if (f == 0) {
+      v = Mh;
+    } else if (f == 1 || (f >= 4 && f < 4 + kModalities)) {
+      for (int w = 0; w < kConsumers; ++w) {
+        const float mww = s_m[w][hh];
+        if (mww != -__builtin_inff())
+          v += __builtin_amdgcn_exp2f(mww - Mh) * (f == 1 ? s_l[w][hh] : s_s[w][f - 4][hh]);
       }
     } else if (f == 2) {
       v = __int_as_float(wmask);
@@ -820,10 +1341,19 @@ void launch_partition(int batch, const DecodeArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((decode_partition_kernel<D, SLOTS, NW, false, BHL>), grid, dim3(NW * 64), 0, s, a);
 }
 
+template <int D, int SLOTS>
+void launch_partition_pc(int batch, const DecodeArgs& a, hipStream_t s) {
+  const dim3 grid(a.splits, a.hkv, batch);
+  if (a.cmid != 0.f)
+    hipLaunchKernelGGL((decode_partition_pc_kernel<D, SLOTS, true>), grid, dim3(kPcWaves * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_partition_pc_kernel<D, SLOTS, false>), grid, dim3(kPcWaves * 64), 0, s, a);
+}
+
 template <int D>
 hipError_t launch_decode_t(int batch, const DecodeArgs& a, hipStream_t s) {
-  if (a.group <= 5) launch_partition<D, 3, kDecodeWaves>(batch, a, s);
-  else if (a.group <= 8) launch_partition<D, 2, kDecodeWaves>(batch, a, s);
+  if (a.group <= 5) launch_partition_pc<D, 3>(batch, a, s);
+  else if (a.group <= 8) launch_partition_pc<D, 2>(batch, a, s);
   else launch_partition<D, 1, kDecodeWaves / 2>(batch, a, s);
   const int keys = a.hkv * batch;
   const dim3 mgrid(kXcds * ((keys + kXcds - 1) / kXcds) * a.group * MergeShape<D>::RB);
