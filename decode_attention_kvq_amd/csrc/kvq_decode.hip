@@ -153,6 +153,15 @@ struct WaveState {
 
 __device__ __forceinline__ int group_pos(int kg, int i) { return (i < 4) ? (4 * kg + i) : (16 + 4 * kg + i - 4); }
 
+// Byte-table entry e: the fp16 levels of the four 2-bit codes in e (code i
+// in bits 2i..2i+1), level k read from bytes 2k, 2k + 1 of {t1 : t0} by
+// byte permutes.
+__device__ __forceinline__ uint2 tab_entry(uint32_t e, uint32_t t0, uint32_t t1) {
+  const uint32_t s0 = (e & 3u) * 0x0202u + ((e >> 2) & 3u) * 0x02020000u + 0x01000100u;
+  const uint32_t s1 = ((e >> 4) & 3u) * 0x0202u + (e >> 6) * 0x02020000u + 0x01000100u;
+  return uint2{__builtin_amdgcn_perm(t1, t0, s0), __builtin_amdgcn_perm(t1, t0, s1)};
+}
+
 // OR of a small per-lane bit set over the wavefront, one ballot per bit
 // (an LDS atomic with a per-lane operand would be serialised lane by lane).
 __device__ __forceinline__ int wave_or_bits(int bits) {
@@ -465,15 +474,13 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_partition_kernel(DecodeArgs
   // e; thread tid fills 16 of entry (tid / 2)'s 32 copies.
   {
     const int e = tid >> 1;
-    uint32_t lvl[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) lvl[k] = (a.level_f16[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
-    const uint2 v = {lvl[e & 3] | (lvl[(e >> 2) & 3] << 16), lvl[(e >> 4) & 3] | (lvl[e >> 6] << 16)};
+    const uint32_t t0 = a.level_f16[0], t1 = a.level_f16[1];
+    const uint2 v = tab_entry(e, t0, t1);
     for (int c = (tid & 1) * 16; c < (tid & 1) * 16 + 16; ++c) sm.s.tab[e * kTabCopies + c] = v;
     if constexpr (NW * 64 < 512) {
       // fewer threads than 2 per entry: the first pass covered entries < NW * 32
       for (int e2 = e + NW * 32; e2 < 256; e2 += NW * 32) {
-        const uint2 v2 = {lvl[e2 & 3] | (lvl[(e2 >> 2) & 3] << 16), lvl[(e2 >> 4) & 3] | (lvl[e2 >> 6] << 16)};
+        const uint2 v2 = tab_entry(e2, t0, t1);
         for (int c = (tid & 1) * 16; c < (tid & 1) * 16 + 16; ++c) sm.s.tab[e2 * kTabCopies + c] = v2;
       }
     }
@@ -712,14 +719,16 @@ __device__ __forceinline__ void stats_load(const DecodeArgs& a, int h, int t0, i
 }
 
 // Producer: q~ hi / lo and the bias of two groups (A for the lanes of columns
-// 0..7, B for columns 8..15) into the consumers' slots.
+// 0..7, B for columns 8..15) into the consumers' slots.  `stage` holds both
+// groups' LO / HI rows (fp16, for the bias products), `dstage` their channel
+// widths HI - LO (fp32, exact), each computed once per channel.
+// First part: stage the statistics (after which their registers are free).
 template <int D>
-__device__ __forceinline__ void produce(const uint32_t (&stA)[D / 64], const uint32_t (&stB)[D / 64],
-                                        uint16_t* stage, QtSlot<D>* slotA, QtSlot<D>* slotB, int lane, int kg,
-                                        int col, const float (&hq)[D / 32][8], const half8 (&bq)[D / 32]) {
-  constexpr int KT = D / 32;
-  constexpr int ROW = QtSlot<D>::ROW;
-  // Stage both groups' LO / HI rows (group A at stage, B at stage + 2D).
+__device__ __forceinline__ void produce_stage(const uint32_t (&stA)[D / 64], const uint32_t (&stB)[D / 64],
+                                              uint16_t* stage, float* dstage, int lane) {
+  constexpr int NW = D / 64;                      // statistics words per lane
+  // A lane's words are LO (lanes 0..31) or HI (lanes 32..63) fp16 pairs of
+  // channels (D / 32) (lane & 31) + [0, D / 32).
   if constexpr (D == 128) {
     reinterpret_cast<uint2*>(stage)[lane] = uint2{stA[0], stA[1]};
     reinterpret_cast<uint2*>(stage + 2 * D)[lane] = uint2{stB[0], stB[1]};
@@ -727,30 +736,59 @@ __device__ __forceinline__ void produce(const uint32_t (&stA)[D / 64], const uin
     reinterpret_cast<uint32_t*>(stage)[lane] = stA[0];
     reinterpret_cast<uint32_t*>(stage + 2 * D)[lane] = stB[0];
   }
+  // After the swap lanes 0..31 hold group A's LO (first) and HI (second)
+  // words, lanes 32..63 group B's.
+  float dv[2 * NW];
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(stA[w], stB[w], false, false);
+    dv[2 * w] = f16_diff_lo(sw[1], sw[0]);
+    dv[2 * w + 1] = f16_diff_hi(sw[1], sw[0]);
+  }
+  float* drow = dstage + (lane >> 5) * D + (D / 32) * (lane & 31);
+  if constexpr (D == 128) {
+    *reinterpret_cast<float4*>(drow) = float4{dv[0], dv[1], dv[2], dv[3]};
+  } else {
+    *reinterpret_cast<float2*>(drow) = float2{dv[0], dv[1]};
+  }
+}
+
+// Second part: operands and bias from the staging.
+template <int D>
+__device__ __forceinline__ void produce_compute(const uint16_t* stage, const float* dstage, QtSlot<D>* slotA,
+                                                QtSlot<D>* slotB, int kg, int col, const float (&hq)[D / 32][8],
+                                                const half8 (&bq)[D / 32]) {
+  constexpr int KT = D / 32;
   wave_sync();
   const int grp = col >> 3;                       // 0: group A, 1: group B
   const uint16_t* st = stage + grp * 2 * D;
+  const float* dg = dstage + grp * D;
   QtSlot<D>* slot = grp ? slotB : slotA;
   const int head = col & 7;
+  uint4 lo4[KT], hi4[KT];
+  float4 d4[KT][2];
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) {
+    lo4[kt] = *reinterpret_cast<const uint4*>(st + 32 * kt + 8 * kg);
+    hi4[kt] = *reinterpret_cast<const uint4*>(st + D + 32 * kt + 8 * kg);
+    d4[kt][0] = *reinterpret_cast<const float4*>(dg + 32 * kt + 8 * kg);
+    d4[kt][1] = *reinterpret_cast<const float4*>(dg + 32 * kt + 8 * kg + 4);
+  }
   floatx4 bias4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kt = 0; kt < KT; ++kt) {
-    const uint4 lo4 = *reinterpret_cast<const uint4*>(st + 32 * kt + 8 * kg);
-    const uint4 hi4 = *reinterpret_cast<const uint4*>(st + D + 32 * kt + 8 * kg);
     // Rows 0..7 of the product carry group A's statistics, rows 8..15 group
     // B's; columns are q's fp16 hi (0..7) and lo (8..15) parts per head.
-    bias4 = mfma(__builtin_bit_cast(half8, lo4), bq[kt], bias4);
-    bias4 = mfma(__builtin_bit_cast(half8, hi4), bq[kt], bias4);
-    const uint32_t lw[4] = {lo4.x, lo4.y, lo4.z, lo4.w};
-    const uint32_t hw[4] = {hi4.x, hi4.y, hi4.z, hi4.w};
+    bias4 = mfma(__builtin_bit_cast(half8, lo4[kt]), bq[kt], bias4);
+    bias4 = mfma(__builtin_bit_cast(half8, hi4[kt]), bq[kt], bias4);
+    const float d[8] = {d4[kt][0].x, d4[kt][0].y, d4[kt][0].z, d4[kt][0].w,
+                        d4[kt][1].x, d4[kt][1].y, d4[kt][1].z, d4[kt][1].w};
     uint32_t th[4], tl[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const float d0 = f16_diff_lo(hw[p], lw[p]);
-      const float d1 = f16_diff_hi(hw[p], lw[p]);
-      const uint2 s = split_product(hq[kt][2 * p], d0, hq[kt][2 * p + 1], d1);
-      th[p] = s.x;
-      tl[p] = s.y;
+      const uint2 sp = split_product(hq[kt][2 * p], d[2 * p], hq[kt][2 * p + 1], d[2 * p + 1]);
+      th[p] = sp.x;
+      tl[p] = sp.y;
     }
     *reinterpret_cast<uint4*>(&slot->qt[0][head][32 * kt + 8 * kg]) = uint4{th[0], th[1], th[2], th[3]};
     *reinterpret_cast<uint4*>(&slot->qt[1][head][32 * kt + 8 * kg]) = uint4{tl[0], tl[1], tl[2], tl[3]};
@@ -760,8 +798,6 @@ __device__ __forceinline__ void produce(const uint32_t (&stA)[D / 64], const uin
   bias += __uint_as_float(static_cast<uint32_t>(
       __builtin_amdgcn_update_dpp(0, static_cast<int>(__float_as_uint(bias)), 0x128, 0xF, 0xF, false)));
   if (col < 8 && (kg & 1) == 0) (kg ? slotB : slotA)->bias[col] = bias;
-  (void)ROW;
-  wave_sync();   // the staging may be overwritten by the next step
 }
 
 // Consumer: one group, given its q~ slot.  `partial`: the group extends past
@@ -905,6 +941,7 @@ __global__ __launch_bounds__(kPcWaves * 64, 1) void decode_partition_pc_kernel(D
       uint2 tab[256 * kTabCopies];              // 64 KB byte table
       QtSlot<D> slots[kConsumers][2];           // q~ and bias per consumer, double-buffered by step
       uint16_t stage[kProducers][2][2][D];      // producers' staging of two groups' LO / HI rows
+      float dstage[kProducers][2][D];           // and of their channel widths HI - LO
     } s;
     float4 red[kConsumers][NPOS];               // the consumers' rescaled accumulators
   };
@@ -939,12 +976,10 @@ __global__ __launch_bounds__(kPcWaves * 64, 1) void decode_partition_pc_kernel(D
       const int pg = page0 + i;
       s_pt[i] = pg < a.max_pages ? ptab[pg] : -1;
     }
-    uint32_t lvl[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) lvl[k] = (a.level_f16[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
-    for (int i = tid; i < 256 * kTabCopies; i += NT) {
-      const int e = i / kTabCopies;
-      sm.s.tab[i] = uint2{lvl[e & 3] | (lvl[(e >> 2) & 3] << 16), lvl[(e >> 4) & 3] | (lvl[e >> 6] << 16)};
+    // two copies of an entry per 16-byte store
+    for (int i = tid; i < 256 * kTabCopies / 2; i += NT) {
+      const uint2 v = tab_entry(static_cast<uint32_t>(i) / (kTabCopies / 2), a.level_f16[0], a.level_f16[1]);
+      reinterpret_cast<uint4*>(sm.s.tab)[i] = uint4{v.x, v.y, v.x, v.y};
     }
     if (tid == 0) s_mask = 0;
   };
@@ -986,24 +1021,31 @@ __global__ __launch_bounds__(kPcWaves * 64, 1) void decode_partition_pc_kernel(D
     setup();
     __syncthreads();
     uint16_t* stage = &sm.s.stage[p][0][0][0];
+    float* dstage = &sm.s.dstage[p][0][0];
+    // Per step: stage its statistics, fetch those of two steps later into the
+    // freed registers, then build the operands (the fetch overlaps the work).
     for (int s = -1; s < steps; s += 2) {
-      // step s + 1 (even) into slot 0, then fetch step s + 3
-      if (s + 1 < steps)
-        produce<D>(pst0[0], pst0[1], stage, &sm.s.slots[2 * p][0], &sm.s.slots[2 * p + 1][0], lane, kg, col, hq, bq);
+      // step s + 1 (even) into slot 0; fetch step s + 3
+      produce_stage<D>(pst0[0], pst0[1], stage, dstage, lane);
 #pragma unroll
       for (int gg = 0; gg < 2; ++gg) {
         const int t = gpos(s + 3, 2 * p + gg);
         stats_load<D>(a, h, t, te, lane, pt_at(t), pst0[gg]);
       }
+      if (s + 1 < steps)
+        produce_compute<D>(stage, dstage, &sm.s.slots[2 * p][0], &sm.s.slots[2 * p + 1][0], kg, col, hq, bq);
+      wave_sync();   // the staging may be overwritten by the next step
       __syncthreads();
-      // step s + 2 (odd) into slot 1, then fetch step s + 4
-      if (s + 2 < steps)
-        produce<D>(pst1[0], pst1[1], stage, &sm.s.slots[2 * p][1], &sm.s.slots[2 * p + 1][1], lane, kg, col, hq, bq);
+      // step s + 2 (odd) into slot 1; fetch step s + 4
+      produce_stage<D>(pst1[0], pst1[1], stage, dstage, lane);
 #pragma unroll
       for (int gg = 0; gg < 2; ++gg) {
         const int t = gpos(s + 4, 2 * p + gg);
         stats_load<D>(a, h, t, te, lane, pt_at(t), pst1[gg]);
       }
+      if (s + 2 < steps)
+        produce_compute<D>(stage, dstage, &sm.s.slots[2 * p][1], &sm.s.slots[2 * p + 1][1], kg, col, hq, bq);
+      wave_sync();
       __syncthreads();
     }
     __syncthreads();   // merge: consumers hand over their accumulators
