@@ -103,9 +103,11 @@ def main():
     scale = 1.0 / math.sqrt(d)
 
     def one_step(r, j):
+        # append the step's key / value and rotate its query (one launch:
+        # kvq_append_and_rotate = kvq_quantize_append + kvq_rotate_query), then decode
         cache = caches[r]
-        K.kvq_quantize_append(cfg, cache, params, k_steps[:, j:j + 1], v_steps[:, j:j + 1], m_steps[:, j:j + 1])
-        K.kvq_rotate_query(cfg, params, q, q_rot)
+        K.kvq_append_and_rotate(cfg, cache, params, k_steps[:, j:j + 1], v_steps[:, j:j + 1], m_steps[:, j:j + 1],
+                                q, q_rot)
         K.kvq_decode_attention(cfg, cache, params, q_rot, scale, out, ws)
 
     # Eager warm-up (also loads every kernel), then rewind the lengths.

@@ -17,7 +17,7 @@ import torch
 from . import _lib
 from ._lib import KVQ_BF16, KVQ_F32, KvqCache, KvqConfig, KvqError, KvqParams  # noqa: F401
 
-__all__ = ["Config", "Params", "Cache", "kvq_quantize_append", "kvq_rotate_query",
+__all__ = ["Config", "Params", "Cache", "kvq_quantize_append", "kvq_rotate_query", "kvq_append_and_rotate",
            "kvq_decode_workspace_bytes", "kvq_decode_attention", "KvqError"]
 
 _DTYPES = {torch.float32: KVQ_F32, torch.bfloat16: KVQ_BF16}
@@ -120,6 +120,32 @@ def kvq_quantize_append(cfg: Config, cache: Cache, params: Params, k_new: torch.
         _dev(k_new, "k_new", cfg.kv_dtype), _dev(v_new, "v_new", cfg.kv_dtype),
         _dev(modality_new, "modality_new", torch.uint8), _stream(stream))
     _lib.check("kvq_quantize_append", st)
+
+
+def kvq_append_and_rotate(cfg: Config, cache: Cache, params: Params, k_new: torch.Tensor,
+                          v_new: torch.Tensor, modality_new: torch.Tensor, q: torch.Tensor,
+                          q_rot: Optional[torch.Tensor] = None, b0: int = 0, stream=None) -> torch.Tensor:
+    """kvq_quantize_append(k_new, v_new, modality_new) and kvq_rotate_query(q) in
+    one launch, with identical results; returns q_rot [B, Hq, d] fp32."""
+    nb, n_new = int(k_new.shape[0]), int(k_new.shape[1])
+    if tuple(k_new.shape) != (nb, n_new, cfg.n_kv_heads, cfg.head_dim) or v_new.shape != k_new.shape:
+        raise ValueError("k_new / v_new must be [nb, n_new, Hkv, d]")
+    if tuple(modality_new.shape) != (nb, n_new):
+        raise ValueError("modality_new must be [nb, n_new]")
+    B = int(q.shape[0])
+    if tuple(q.shape) != (B, cfg.n_q_heads, cfg.head_dim):
+        raise ValueError("q must be [B, Hq, d]")
+    if q.dtype not in _DTYPES:
+        raise TypeError("q must be float32 or bfloat16")
+    if q_rot is None:
+        q_rot = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    st = _lib.load().kvq_append_and_rotate(
+        ctypes.byref(cfg.struct), ctypes.byref(cache.struct), ctypes.byref(params.struct), b0, nb, n_new,
+        _dev(k_new, "k_new", cfg.kv_dtype), _dev(v_new, "v_new", cfg.kv_dtype),
+        _dev(modality_new, "modality_new", torch.uint8), B, _dev(q, "q"), _DTYPES[q.dtype],
+        _dev(q_rot, "q_rot", torch.float32), _stream(stream))
+    _lib.check("kvq_append_and_rotate", st)
+    return q_rot
 
 
 def kvq_rotate_query(cfg: Config, params: Params, q: torch.Tensor, q_rot: Optional[torch.Tensor] = None,

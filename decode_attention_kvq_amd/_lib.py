@@ -12,7 +12,7 @@ LIB_PATH = os.path.join(_PKG, "libkvq.so")
 KVQ_OK, KVQ_ERR_INVALID, KVQ_ERR_UNSUPPORTED, KVQ_ERR_CAPACITY, KVQ_ERR_WORKSPACE, KVQ_ERR_LAUNCH = range(6)
 KVQ_F32, KVQ_BF16 = 0, 1
 
-EXPORTED = ("kvq_cache_buffer_bytes", "kvq_quantize_append", "kvq_rotate_query",
+EXPORTED = ("kvq_cache_buffer_bytes", "kvq_quantize_append", "kvq_rotate_query", "kvq_append_and_rotate",
             "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_status_string")
 
 
@@ -63,6 +63,11 @@ def load() -> ctypes.CDLL:
     lib.kvq_rotate_query.argtypes = [P(KvqConfig), P(KvqParams), ctypes.c_int32, ctypes.c_void_p,
                                      ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     lib.kvq_rotate_query.restype = ctypes.c_int
+    lib.kvq_append_and_rotate.argtypes = [P(KvqConfig), P(KvqCache), P(KvqParams), ctypes.c_int32,
+                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+                                          ctypes.c_void_p, ctypes.c_void_p]
+    lib.kvq_append_and_rotate.restype = ctypes.c_int
     lib.kvq_decode_workspace_bytes.argtypes = [P(KvqConfig), ctypes.c_int32]
     lib.kvq_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.kvq_decode_attention.argtypes = [P(KvqConfig), P(KvqCache), P(KvqParams), ctypes.c_void_p,

@@ -137,9 +137,10 @@ kvq_status kvq_cache_buffer_bytes(const kvq_config* cfg, size_t out[6]) {
   return KVQ_OK;
 }
 
-kvq_status kvq_quantize_append(const kvq_config* cfg, kvq_cache* cache, const kvq_params* params,
-                               int32_t b0, int32_t nb, int32_t n_new, const void* k_new,
-                               const void* v_new, const uint8_t* modality_new, hipStream_t stream) {
+// Validation and kernel arguments of an append (nothing is launched).
+static kvq_status prepare_append(const kvq_config* cfg, const kvq_cache* cache, const kvq_params* params,
+                                 int32_t b0, int32_t nb, int32_t n_new, const void* k_new, const void* v_new,
+                                 const uint8_t* modality_new, kvq::AppendArgs& a) {
   kvq_status st = check_config(cfg);
   if (st != KVQ_OK) return st;
   if ((st = check_params(params)) != KVQ_OK) return st;
@@ -153,7 +154,7 @@ kvq_status kvq_quantize_append(const kvq_config* cfg, kvq_cache* cache, const kv
     if ((int64_t)cache->seq_len_host[b] + n_new > cap) return KVQ_ERR_CAPACITY;
   }
   const double sd = sqrt((double)cfg->head_dim);
-  kvq::AppendArgs a;
+  a = kvq::AppendArgs{};
   a.k_codes = cache->k_codes;
   a.k_stats = cache->k_stats;
   a.v_codes = cache->v_codes;
@@ -182,7 +183,57 @@ kvq_status kvq_quantize_append(const kvq_config* cfg, kvq_cache* cache, const kv
   a.thr0 = (c[0] + c[1]) / 2.0;
   a.thr1 = (c[1] + c[2]) / 2.0;
   a.thr2 = (c[2] + c[3]) / 2.0;
+  a.rot_heads = 0;
+  return KVQ_OK;
+}
+
+// Validation and kernel arguments of a query rotation.
+static kvq_status prepare_rotate(const kvq_config* cfg, const kvq_params* params, int32_t batch, const void* q,
+                                 int32_t q_dtype, float* q_rot, kvq::RotateArgs& a) {
+  kvq_status st = check_config(cfg);
+  if (st != KVQ_OK) return st;
+  if (!params || !params->signs) return KVQ_ERR_INVALID;
+  if (batch <= 0 || !q || !q_rot) return KVQ_ERR_INVALID;
+  if (q_dtype != KVQ_F32 && q_dtype != KVQ_BF16) return KVQ_ERR_UNSUPPORTED;
+  a.q = q;
+  a.q_rot = q_rot;
+  a.signs = params->signs;
+  a.hq = cfg->n_q_heads;
+  a.group = cfg->n_q_heads / cfg->n_kv_heads;
+  a.inv_sqrt_d = 1.0 / sqrt((double)cfg->head_dim);
+  return KVQ_OK;
+}
+
+kvq_status kvq_quantize_append(const kvq_config* cfg, kvq_cache* cache, const kvq_params* params,
+                               int32_t b0, int32_t nb, int32_t n_new, const void* k_new,
+                               const void* v_new, const uint8_t* modality_new, hipStream_t stream) {
+  kvq::AppendArgs a;
+  const kvq_status st = prepare_append(cfg, cache, params, b0, nb, n_new, k_new, v_new, modality_new, a);
+  if (st != KVQ_OK || n_new == 0) return st;
   hipError_t e = kvq::launch_append(cfg->head_dim, cfg->kv_dtype == KVQ_BF16, nb, a, stream);
+  if (e != hipSuccess) return KVQ_ERR_LAUNCH;
+  for (int b = b0; b < b0 + nb; ++b) cache->seq_len_host[b] += n_new;
+  return KVQ_OK;
+}
+
+kvq_status kvq_append_and_rotate(const kvq_config* cfg, kvq_cache* cache, const kvq_params* params,
+                                 int32_t b0, int32_t nb, int32_t n_new, const void* k_new,
+                                 const void* v_new, const uint8_t* modality_new, int32_t batch,
+                                 const void* q, int32_t q_dtype, float* q_rot, hipStream_t stream) {
+  kvq::AppendArgs a;
+  kvq::RotateArgs r;
+  kvq_status st = prepare_append(cfg, cache, params, b0, nb, n_new, k_new, v_new, modality_new, a);
+  if (st != KVQ_OK) return st;
+  if ((st = prepare_rotate(cfg, params, batch, q, q_dtype, q_rot, r)) != KVQ_OK) return st;
+  hipError_t e;
+  if (n_new == 0) {
+    e = kvq::launch_rotate_query(cfg->head_dim, q_dtype == KVQ_BF16, batch, r, stream);
+  } else {
+    a.rq = r;
+    a.rot_heads = batch * cfg->n_q_heads;
+    a.rot_bf16 = q_dtype == KVQ_BF16;
+    e = kvq::launch_append(cfg->head_dim, cfg->kv_dtype == KVQ_BF16, nb, a, stream);
+  }
   if (e != hipSuccess) return KVQ_ERR_LAUNCH;
   for (int b = b0; b < b0 + nb; ++b) cache->seq_len_host[b] += n_new;
   return KVQ_OK;
@@ -190,18 +241,9 @@ kvq_status kvq_quantize_append(const kvq_config* cfg, kvq_cache* cache, const kv
 
 kvq_status kvq_rotate_query(const kvq_config* cfg, const kvq_params* params, int32_t batch,
                             const void* q, int32_t q_dtype, float* q_rot, hipStream_t stream) {
-  kvq_status st = check_config(cfg);
-  if (st != KVQ_OK) return st;
-  if (!params || !params->signs) return KVQ_ERR_INVALID;
-  if (batch <= 0 || !q || !q_rot) return KVQ_ERR_INVALID;
-  if (q_dtype != KVQ_F32 && q_dtype != KVQ_BF16) return KVQ_ERR_UNSUPPORTED;
   kvq::RotateArgs a;
-  a.q = q;
-  a.q_rot = q_rot;
-  a.signs = params->signs;
-  a.hq = cfg->n_q_heads;
-  a.group = cfg->n_q_heads / cfg->n_kv_heads;
-  a.inv_sqrt_d = 1.0 / sqrt((double)cfg->head_dim);
+  const kvq_status st = prepare_rotate(cfg, params, batch, q, q_dtype, q_rot, a);
+  if (st != KVQ_OK) return st;
   hipError_t e = kvq::launch_rotate_query(cfg->head_dim, q_dtype == KVQ_BF16, batch, a, stream);
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;
 }

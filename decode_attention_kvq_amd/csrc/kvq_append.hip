@@ -24,6 +24,9 @@
 // workgroup takes a ticket when done; the last one of a session advances its
 // length, so no workgroup can see the new length before it read the old one.
 //
+// kvq_append_and_rotate adds grid columns whose workgroups rotate the step's
+// query heads (kvq_rotate.h) while the append runs; they take no ticket.
+//
 // Latency matters more than throughput for the common one-position append:
 // each role issues its global loads in at most two dependent rounds, 16
 // threads share one position's channels (a short fp64 transform), and the
@@ -31,6 +34,7 @@
 // thread per channel.
 #include "kvq_common.h"
 #include "kvq_internal.h"
+#include "kvq_rotate.h"
 
 namespace kvq {
 
@@ -128,10 +132,23 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
   __shared__ AppendSmem<D> sm;
   __shared__ int s_last;
 
+  const int tid = threadIdx.x;
+  if (static_cast<int>(blockIdx.x) >= a.append_x) {
+    // ================= fused query rotation: 32 heads per workgroup
+    const int r = (static_cast<int>(blockIdx.x) - a.append_x) * static_cast<int>(gridDim.z * gridDim.y) +
+                  static_cast<int>(blockIdx.z * gridDim.y + blockIdx.y);
+    const int first = r * (kAppendThreads / rotq::kLanes);
+    if (first < a.rot_heads) {
+      const int bi = first + tid / rotq::kLanes, sub = tid % rotq::kLanes;
+      if (a.rot_bf16) rotq::rotate_head<D, true>(a.rq, a.rot_heads, bi, sub);
+      else rotq::rotate_head<D, false>(a.rq, a.rot_heads, bi, sub);
+    }
+    return;   // no ticket: only the append's workgroups count
+  }
   const int b = blockIdx.z, h = blockIdx.y, j = blockIdx.x >> 1;
   const bool vrole = blockIdx.x & 1;
   const int sb = a.b0 + b;
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int lane = tid & 63;
   const int tok = tid / kPosThreads, part = tid % kPosThreads, cb = part * CH;
 
   // Round trip 1: the session length; the value workgroup also reads the
@@ -406,7 +423,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
   // and rearms the ticket for the next append.
   __syncthreads();
   if (tid == 0) {
-    const int total = static_cast<int>(gridDim.x * gridDim.y);
+    const int total = a.append_x * static_cast<int>(gridDim.y);
     const int t = __hip_atomic_fetch_add(&a.tickets[sb], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     s_last = (t == total - 1);
   }
@@ -418,9 +435,13 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
 }
 
 template <int D, bool BF16>
-hipError_t launch_append_t(int nb, const AppendArgs& a, hipStream_t s) {
-  // two workgroups (keys, values) per touched group
-  const dim3 grid(2 * ((a.n_new + 30) / kGroupTokens + 1), a.hkv, nb);
+hipError_t launch_append_t(int nb, AppendArgs a, hipStream_t s) {
+  // two workgroups (keys, values) per touched group, then the columns of
+  // the fused query rotation (32 heads per workgroup)
+  a.append_x = 2 * ((a.n_new + 30) / kGroupTokens + 1);
+  const int rot_wgs = (a.rot_heads + kAppendThreads / rotq::kLanes - 1) / (kAppendThreads / rotq::kLanes);
+  const int rot_x = (rot_wgs + a.hkv * nb - 1) / (a.hkv * nb);
+  const dim3 grid(a.append_x + rot_x, a.hkv, nb);
   hipLaunchKernelGGL((append_kernel<D, BF16>), grid, dim3(kAppendThreads), 0, s, a);
   return hipGetLastError();
 }

@@ -13,6 +13,14 @@ constexpr int kModalities = 3;     // video, audio, text
 constexpr int kMaxGroupHeads = 16; // query heads per KV head supported by the kernels
 
 // Arguments of the append kernel (passed by value).
+struct RotateArgs {
+  const void* q;
+  float* q_rot;
+  const int8_t* signs;
+  int32_t hq, group;   // group = Hq / Hkv
+  double inv_sqrt_d;
+};
+
 struct AppendArgs {
   uint8_t* k_codes;
   uint16_t* k_stats;
@@ -33,14 +41,11 @@ struct AppendArgs {
   double sqrt_d;       // fl(sqrt(d))
   double c0, c3;       // outer levels (exact fp64 images of the fp32 levels)
   double thr0, thr1, thr2;  // decision thresholds (c_k + c_{k+1}) / 2
-};
-
-struct RotateArgs {
-  const void* q;
-  float* q_rot;
-  const int8_t* signs;
-  int32_t hq, group;   // group = Hq / Hkv
-  double inv_sqrt_d;
+  // Query rotation fused into the same launch (kvq_append_and_rotate):
+  // rot_heads query heads (0: none), q in bf16 if rot_bf16.  The launcher
+  // sets append_x, the grid columns of the append's own workgroups.
+  RotateArgs rq;
+  int32_t rot_heads, rot_bf16, append_x;
 };
 
 // Decode partitions: a workgroup of kDecodeWaves wavefronts streams one

@@ -142,6 +142,24 @@ kvq_status kvq_quantize_append(const kvq_config* cfg, kvq_cache* cache, const kv
 kvq_status kvq_rotate_query(const kvq_config* cfg, const kvq_params* params, int32_t batch,
                             const void* q, int32_t q_dtype, float* q_rot, hipStream_t stream);
 
+/*
+ * kvq_append_and_rotate - the two independent first steps of a decode step
+ * (Sec. 2 Method, key and value bullets; Sec. 1, Implementation bullet) in
+ * one launch: exactly kvq_quantize_append(cfg, cache, params, b0, nb, n_new,
+ * k_new, v_new, modality_new, stream) followed by kvq_rotate_query(cfg,
+ * params, batch, q, q_dtype, q_rot, stream), with identical results.  Extra
+ * workgroups of the append's launch rotate the query heads while the append
+ * runs, which saves one kernel launch per step.  With n_new == 0 only the
+ * rotation is launched.  Arguments, layouts and ownership are those of the
+ * two calls; q and q_rot must not overlap the append's inputs or the cache.
+ * Errors: those of either call, all checked before anything is launched.
+ */
+kvq_status kvq_append_and_rotate(const kvq_config* cfg, kvq_cache* cache, const kvq_params* params,
+                                 int32_t b0, int32_t nb, int32_t n_new,
+                                 const void* k_new, const void* v_new,
+                                 const uint8_t* modality_new, int32_t batch,
+                                 const void* q, int32_t q_dtype, float* q_rot, hipStream_t stream);
+
 /* Workspace bytes kvq_decode_attention needs when the longest session holds
  * max_len positions (split-K partial results). */
 size_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t max_len);

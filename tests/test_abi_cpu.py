@@ -126,6 +126,30 @@ def test_decode_and_rotate_reject_bad_arguments():
         assert lib.kvq_status_string(s)
 
 
+def test_append_and_rotate_rejects_bad_arguments_before_launch():
+    """The fused call checks both halves on the host; a failure in either
+    launches nothing and leaves the length mirror untouched."""
+    L, lib = _lib()
+    cfg = _cfg(L)
+    p = _fake_params(L)
+    c, lens = _fake_cache(L, [10, 20])
+    V = ctypes.c_void_p
+
+    def call(b0=0, nb=1, n_new=1, k=V(8), v=V(8), m=V(8), batch=2, q=V(8), qd=0, qr=V(8), params=p):
+        return lib.kvq_append_and_rotate(ctypes.byref(cfg), ctypes.byref(c), ctypes.byref(params) if params else None,
+                                         b0, nb, n_new, k, v, m, batch, q, qd, qr, None)
+    assert call(k=None) == L.KVQ_ERR_INVALID                 # append half
+    assert call(b0=1, nb=2) == L.KVQ_ERR_INVALID
+    assert call(n_new=-1) == L.KVQ_ERR_INVALID
+    assert call(n_new=4 * 256) == L.KVQ_ERR_CAPACITY
+    assert call(q=None) == L.KVQ_ERR_INVALID                 # rotation half
+    assert call(qr=None) == L.KVQ_ERR_INVALID
+    assert call(batch=0) == L.KVQ_ERR_INVALID
+    assert call(qd=7) == L.KVQ_ERR_UNSUPPORTED
+    assert call(params=None) == L.KVQ_ERR_INVALID
+    assert list(lens) == [10, 20]
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     import decode_attention_kvq_amd as K

@@ -84,6 +84,51 @@ def test_append_and_decode_parity(cfg_id, kw):
     assert worst <= h.ATTN_TOL
 
 
+FUSED_CASES = [
+    # (cfg_id, overrides, positions appended, first session, query dtype)
+    (0, dict(length=700), 1, 0, None),
+    (1, dict(length=1200), 45, 0, None),
+    (2, dict(length=900), 0, 0, None),
+    (2, dict(length=900), 1, 0, "f32"),
+    (3, dict(batch=3, len_range=(500, 1300)), 3, 1, None),
+]
+
+
+@pytest.mark.parametrize("cfg_id,kw,n_new,b0,qdt", FUSED_CASES,
+                         ids=[f"cfg{c}-n{n}-b{b}-{q or 'native'}" for c, _, n, b, q in FUSED_CASES])
+def test_append_and_rotate_equals_separate_calls(cfg_id, kw, n_new, b0, qdt):
+    """kvq_append_and_rotate gives the same cache bytes, lengths and rotated
+    queries as kvq_quantize_append followed by kvq_rotate_query."""
+    import decode_attention_kvq_amd as K
+    h = H()
+    w = generate(cfg_id, **kw)
+    nb = w.cfg.batch - b0
+    upto = [max(int(n) - n_new, 0) for n in w.lengths]
+    _say(f"fused append+rotate cfg{cfg_id} {kw} n_new={n_new} b0={b0} q={qdt or w.dtype} upto={upto}")
+    cfg, params, sep = h.build(w, upto=upto)
+    _, _, fus = h.build(w, upto=upto)
+    q = h.query_tensor(w)
+    if qdt == "f32":
+        q = q.float()
+    # every appended session gets the positions that follow its own prefix
+    ks = [h._kv_tensor(w.k[b][None, upto[b]:upto[b] + n_new], w.dtype) for b in range(b0, b0 + nb)]
+    vs = [h._kv_tensor(w.v[b][None, upto[b]:upto[b] + n_new], w.dtype) for b in range(b0, b0 + nb)]
+    ms = [torch.from_numpy(np.ascontiguousarray(w.modality[b][None, upto[b]:upto[b] + n_new])).cuda()
+          for b in range(b0, b0 + nb)]
+    k_new, v_new, m_new = torch.cat(ks), torch.cat(vs), torch.cat(ms)
+    K.kvq_quantize_append(cfg, sep, params, k_new, v_new, m_new, b0=b0)
+    q_sep = K.kvq_rotate_query(cfg, params, q)
+    q_fus = K.kvq_append_and_rotate(cfg, fus, params, k_new, v_new, m_new, q, b0=b0)
+    torch.cuda.synchronize()
+    a, b = sep.host_arrays(), fus.host_arrays()
+    for key in ("k_codes", "k_stats", "v_codes", "v_norms", "modality", "seq_len", "k_tail"):
+        np.testing.assert_array_equal(a[key], b[key], err_msg=key)
+    assert sep.lengths() == fus.lengths()
+    np.testing.assert_array_equal(q_sep.cpu().numpy(), q_fus.cpu().numpy())
+    if n_new:
+        h.check_codes(w, cfg, fus, range(b0, b0 + nb), lengths=[upto[b] + n_new for b in range(w.cfg.batch)])
+
+
 def test_chunked_append_equals_one_shot():
     """Appends of ragged sizes (re-quantizing the open group from the raw key
     tail each time) give the same cache bytes as one append of the stream."""
