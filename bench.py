@@ -28,6 +28,23 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 
+# HBM bytes of one decode launch (partition + merge kernels) at this workload,
+# from two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE), each scaled by
+# what the counter reads for a plain 256 MiB device copy (FETCH_SIZE x 1.9998,
+# WRITE_SIZE x 1.0); see profiles/decode_80k_hbm_bytes.md.  Valid only for
+# the decode source the counters were taken on (SHA-256 of kvq_decode.hip).
+DECODE_TRAFFIC = {"kvq_decode_sha256": None, "bytes": None}
+
+
+def decode_traffic_bytes():
+    import hashlib
+    path = os.path.join(ROOT, "decode_attention_kvq_amd", "csrc", "kvq_decode.hip")
+    try:
+        digest = hashlib.sha256(open(path, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    return DECODE_TRAFFIC["bytes"] if digest == DECODE_TRAFFIC["kvq_decode_sha256"] else None
+
 
 def algorithmic_decode_bytes(L: int, d: int, hq: int, hkv: int) -> int:
     """Bytes one decode must move: per (position, KV head) the key codes
@@ -208,7 +225,7 @@ def main():
                    "context": int(ctx_mean), "head_dim": d, "q_heads": hq, "kv_heads": hkv,
                    "batch": 1, "layer_replicas": args.replicas, "page_tokens": pt},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": decode_traffic_bytes(),
                      "kernel": "decode (partition + merge)", "bytes_per_launch": dec_bytes,
                      "avg_launch_us": dec_ms * 1e3},
         "cpu_baseline": cpu,
