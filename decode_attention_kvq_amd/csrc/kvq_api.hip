@@ -293,6 +293,11 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache,
   a.num_pages = cfg->num_pages;
   a.splits = plan.splits;
   a.split_tokens = plan.split_tokens;
+  a.page_shift = -1;
+  if ((cfg->page_tokens & (cfg->page_tokens - 1)) == 0) {
+    a.page_shift = 0;
+    while ((1 << a.page_shift) < cfg->page_tokens) ++a.page_shift;
+  }
   a.scale_log2e = (float)((double)scale * 1.4426950408889634);
   a.value_scale = (float)(1.0 / sqrt((double)cfg->head_dim));
   uint16_t lv[4];

@@ -103,6 +103,17 @@ struct GroupLoad {
   uint32_t md0, md1;     // modality bytes of the same positions
 };
 
+// Page of position t >= 0 and its index inside the page: a shift and a mask
+// when page_tokens is a power of two (the common case), else a division.
+__device__ __forceinline__ int page_of(const DecodeArgs& a, int t) {
+  if (a.page_shift >= 0) return t >> a.page_shift;
+  return static_cast<int>(static_cast<unsigned>(t) / static_cast<unsigned>(a.page_tokens));
+}
+__device__ __forceinline__ int in_page(const DecodeArgs& a, int t) {
+  if (a.page_shift >= 0) return t & (a.page_tokens - 1);
+  return static_cast<int>(static_cast<unsigned>(t) % static_cast<unsigned>(a.page_tokens));
+}
+
 // Issues the loads of the group at position t0 (on physical page phys0)
 // without branching, so the compiler can count outstanding loads exactly: a
 // group outside [0, te) or on an unmapped page reads page 0 instead and is
@@ -110,11 +121,11 @@ struct GroupLoad {
 template <int D>
 __device__ __forceinline__ void load_group(const DecodeArgs& a, int h, int t0, int te, int lane, int kg,
                                            int phys0, GroupLoad<D>& g, bool& ok) {
-  const int page = t0 / a.page_tokens;
+  const int page = page_of(a, t0);
   ok = t0 < te && page < a.max_pages && phys0 >= 0 && phys0 < a.num_pages;
   const int phys = ok ? phys0 : 0;
   const int gp = a.page_tokens / kGroupTokens;
-  const int tin = ok ? t0 % a.page_tokens : 0;
+  const int tin = ok ? in_page(a, t0) : 0;
   const size_t blk = (static_cast<size_t>(phys) * a.hkv + h) * gp + tin / kGroupTokens;
   const uint32_t* kp = reinterpret_cast<const uint32_t*>(a.k_codes + blk * 8 * D) + lane * (D / 32);
   const uint32_t* vp = reinterpret_cast<const uint32_t*>(a.v_codes + blk * 8 * D) + lane * (D / 32);
@@ -160,6 +171,12 @@ __device__ __forceinline__ uint2 tab_entry(uint32_t e, uint32_t t0, uint32_t t1)
   const uint32_t s0 = (e & 3u) * 0x0202u + ((e >> 2) & 3u) * 0x02020000u + 0x01000100u;
   const uint32_t s1 = ((e >> 4) & 3u) * 0x0202u + (e >> 6) * 0x02020000u + 0x01000100u;
   return uint2{__builtin_amdgcn_perm(t1, t0, s0), __builtin_amdgcn_perm(t1, t0, s1)};
+}
+
+// Modality bits of accumulator set k (modalities k SLOTS .. k SLOTS + SLOTS - 1).
+template <int SLOTS>
+__device__ __forceinline__ int set_bits(int k) {
+  return (((1 << SLOTS) - 1) << (k * SLOTS)) & ((1 << kModalities) - 1);
 }
 
 // OR of a small per-lane bit set over the wavefront, one ballot per bit
@@ -452,7 +469,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_partition_kernel(DecodeArgs
   }
   // Page-table entries of the partition's pages (the plan keeps a partition
   // within kPageRun pages), read by the main loop from LDS.
-  const int page0 = tb / a.page_tokens;
+  const int page0 = page_of(a, tb);
   for (int i = tid; i < kPageRun; i += NW * 64) {
     const int pg = page0 + i;
     s_pt[i] = pg < a.max_pages ? a.page_table[static_cast<size_t>(b) * a.max_pages + pg] : -1;
@@ -466,7 +483,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_partition_kernel(DecodeArgs
 #pragma unroll
   for (int k = 0; k < kPrefetch; ++k) {
     const int t = first + k * stride;
-    const int phys = ptab[min(t / a.page_tokens, a.max_pages - 1)];
+    const int phys = ptab[min(page_of(a, t), a.max_pages - 1)];
     load_group<D>(a, h, t, te_full, lane, kg, phys, buf[k], ok[k]);
   }
 
@@ -534,7 +551,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_partition_kernel(DecodeArgs
 #pragma unroll
     for (int k = 0; k < kPrefetch; ++k) {
       const int nxt = base + (k + kPrefetch) * stride;
-      const int pn = __builtin_amdgcn_readfirstlane(s_pt[min(nxt / a.page_tokens - page0, kPageRun - 1)]);
+      const int pn = __builtin_amdgcn_readfirstlane(s_pt[min(page_of(a, nxt) - page0, kPageRun - 1)]);
       if (ok[k])
         process_group<D, SLOTS, ASYM, BHL, true>(buf[k], base + k * stride, te, kg, col, tab, st_lds, lane_off, qo,
                                                  ws, lane);
@@ -542,7 +559,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_partition_kernel(DecodeArgs
     }
   }
   if (te_full >= tb && te_full < te && ((te_full - tb) / kGroupTokens) % NW == wave) {
-    load_group<D>(a, h, te_full, te, lane, kg, s_pt[min(te_full / a.page_tokens - page0, kPageRun - 1)], buf[0], ok[0]);
+    load_group<D>(a, h, te_full, te, lane, kg, s_pt[min(page_of(a, te_full) - page0, kPageRun - 1)], buf[0], ok[0]);
     if (ok[0])
       process_group<D, SLOTS, ASYM, BHL, false>(buf[0], te_full, te, kg, col, tab, st_lds, lane_off, qo, ws, lane);
   }
@@ -660,7 +677,7 @@ struct ConsumerLoad {
 
 template <int D>
 __device__ __forceinline__ size_t block_index(const DecodeArgs& a, int h, int t0, int phys) {
-  return (static_cast<size_t>(phys) * a.hkv + h) * (a.page_tokens / kGroupTokens) + (t0 % a.page_tokens) / kGroupTokens;
+  return (static_cast<size_t>(phys) * a.hkv + h) * (a.page_tokens / kGroupTokens) + in_page(a, t0) / kGroupTokens;
 }
 
 // Buffer resource over `bytes` bytes at `base` (raw, untyped).  A load whose
@@ -676,9 +693,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const void* base, in
 template <int D>
 __device__ __forceinline__ void consumer_load(const DecodeArgs& a, int h, int t0, int te, int lane, int kg, int phys0,
                                               ConsumerLoad<D>& g, bool& ok) {
-  ok = t0 < te && t0 / a.page_tokens < a.max_pages && phys0 >= 0 && phys0 < a.num_pages;
+  ok = t0 < te && page_of(a, t0) < a.max_pages && phys0 >= 0 && phys0 < a.num_pages;
   const int phys = ok ? phys0 : 0;
-  const int tin = ok ? t0 % a.page_tokens : 0;
+  const int tin = ok ? in_page(a, t0) : 0;
   const size_t blk = block_index<D>(a, h, ok ? t0 : 0, phys);
   const int n_codes = ok ? 8 * D : 0;
   const auto rk = span_rsrc(a.k_codes + blk * 8 * D, n_codes);
@@ -707,7 +724,7 @@ __device__ __forceinline__ void consumer_load(const DecodeArgs& a, int h, int t0
 template <int D>
 __device__ __forceinline__ void stats_load(const DecodeArgs& a, int h, int t0, int te, int lane, int phys0,
                                            uint32_t (&st)[D / 64]) {
-  const bool ok = t0 < te && t0 / a.page_tokens < a.max_pages && phys0 >= 0 && phys0 < a.num_pages;
+  const bool ok = t0 < te && page_of(a, t0) < a.max_pages && phys0 >= 0 && phys0 < a.num_pages;
   const size_t blk = block_index<D>(a, h, ok ? t0 : 0, ok ? phys0 : 0);
   const auto rs = span_rsrc(a.k_stats + blk * 2 * D, ok ? 2 * D * 2 : 0);
   if constexpr (D == 128) {
@@ -774,13 +791,13 @@ __device__ __forceinline__ void produce_compute(const uint16_t* stage, const flo
     d4[kt][0] = *reinterpret_cast<const float4*>(dg + 32 * kt + 8 * kg);
     d4[kt][1] = *reinterpret_cast<const float4*>(dg + 32 * kt + 8 * kg + 4);
   }
-  floatx4 bias4 = {0.f, 0.f, 0.f, 0.f};
+  floatx4 bias_lo = {0.f, 0.f, 0.f, 0.f}, bias_hi = {0.f, 0.f, 0.f, 0.f};   // two independent chains
 #pragma unroll
   for (int kt = 0; kt < KT; ++kt) {
     // Rows 0..7 of the product carry group A's statistics, rows 8..15 group
     // B's; columns are q's fp16 hi (0..7) and lo (8..15) parts per head.
-    bias4 = mfma(__builtin_bit_cast(half8, lo4[kt]), bq[kt], bias4);
-    bias4 = mfma(__builtin_bit_cast(half8, hi4[kt]), bq[kt], bias4);
+    bias_lo = mfma(__builtin_bit_cast(half8, lo4[kt]), bq[kt], bias_lo);
+    bias_hi = mfma(__builtin_bit_cast(half8, hi4[kt]), bq[kt], bias_hi);
     const float d[8] = {d4[kt][0].x, d4[kt][0].y, d4[kt][0].z, d4[kt][0].w,
                         d4[kt][1].x, d4[kt][1].y, d4[kt][1].z, d4[kt][1].w};
     uint32_t th[4], tl[4];
@@ -794,7 +811,7 @@ __device__ __forceinline__ void produce_compute(const uint16_t* stage, const flo
     *reinterpret_cast<uint4*>(&slot->qt[1][head][32 * kt + 8 * kg]) = uint4{tl[0], tl[1], tl[2], tl[3]};
   }
   // Lane (h, kg): rows 4 kg..4 kg + 3 (group kg < 2 ? A : B), column h's part.
-  float bias = bias4[0];
+  float bias = bias_lo[0] + bias_hi[0];
   bias += __uint_as_float(static_cast<uint32_t>(
       __builtin_amdgcn_update_dpp(0, static_cast<int>(__float_as_uint(bias)), 0x128, 0xF, 0xF, false)));
   if (col < 8 && (kg & 1) == 0) (kg ? slotB : slotA)->bias[col] = bias;
@@ -950,6 +967,7 @@ __global__ __launch_bounds__(kPcWaves * 64, 1) void decode_partition_pc_kernel(D
   __shared__ float s_l[kConsumers][kMaxGroupHeads];
   __shared__ float s_s[kConsumers][kModalities][kMaxGroupHeads];
   __shared__ int s_mask;
+  __shared__ int s_cmask[kConsumers];         // modalities each consumer saw
   __shared__ int s_pt[kPageRun];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -965,33 +983,36 @@ __global__ __launch_bounds__(kPcWaves * 64, 1) void decode_partition_pc_kernel(D
   const int te = (split == a.splits - 1) ? L : min(tb + a.split_tokens, L);
   const int ng = te > tb ? (te - tb + kGroupTokens - 1) / kGroupTokens : 0;   // groups of the partition
   const int steps = (ng + kConsumers - 1) / kConsumers;
-  const int page0 = tb / a.page_tokens;
+  const int page0 = page_of(a, tb);
   const __attribute__((address_space(4))) int32_t* ptab =
       (const __attribute__((address_space(4))) int32_t*)(a.page_table + static_cast<size_t>(b) * a.max_pages);
   auto gpos = [&](int step, int cons) { return tb + (step * kConsumers + cons) * kGroupTokens; };
 
-  // Common set-up of both roles: page run of the partition and byte table.
-  auto setup = [&]() {
-    for (int i = tid; i < kPageRun; i += NT) {
-      const int pg = page0 + i;
-      s_pt[i] = pg < a.max_pages ? ptab[pg] : -1;
-    }
+  // Set-up, done by the consumers while the producers build step 0's
+  // operands: page run of the partition (one entry per consumer thread,
+  // loaded before the first groups so its wait leaves them in flight), byte
+  // table, modality mask.
+  static_assert(kPageRun == kConsumers * 64, "one page-run entry per consumer thread");
+  auto setup = [&](int pt_entry) {
+    constexpr int NC = kConsumers * 64;
+    s_pt[tid] = pt_entry;
     // two copies of an entry per 16-byte store
-    for (int i = tid; i < 256 * kTabCopies / 2; i += NT) {
+    for (int i = tid; i < 256 * kTabCopies / 2; i += NC) {
       const uint2 v = tab_entry(static_cast<uint32_t>(i) / (kTabCopies / 2), a.level_f16[0], a.level_f16[1]);
       reinterpret_cast<uint4*>(sm.s.tab)[i] = uint4{v.x, v.y, v.x, v.y};
     }
     if (tid == 0) s_mask = 0;
   };
 
-  auto pt_at = [&](int t) { return s_pt[min(t / a.page_tokens - page0, kPageRun - 1)]; };
-  auto pt_direct = [&](int t) { return ptab[min(t / a.page_tokens, a.max_pages - 1)]; };
+  auto pt_at = [&](int t) { return s_pt[min(page_of(a, t) - page0, kPageRun - 1)]; };
+  auto pt_direct = [&](int t) { return ptab[min(page_of(a, t), a.max_pages - 1)]; };
 
   // The two roles run separate loops over the same barriers, so neither holds
-  // the other's registers.  Each loop body covers two steps (even, then odd)
-  // with fixed buffers and unconditional loads, which keeps the compiler's
-  // count of loads in flight exact; steps past the end compute nothing and
-  // read the fallback group.  Barriers per role: 1 + 2 ceil((steps + 1) / 2).
+  // the other's registers.  Step u uses slot u & 1, consumer buffer u & 1 and
+  // producer statistics u & 1.  Each loop pass covers two steps with fixed
+  // buffers and unconditional loads, which keeps the compiler's count of
+  // loads in flight exact; steps past the end compute nothing and read
+  // nothing (zero-span loads).  Barriers per role: 1 + 2 ceil(steps / 2).
   if (producer) {
     // ---- producer: step u's statistics in pst[u & 1] (two groups each)
     uint32_t pst0[2][D / 64], pst1[2][D / 64];
@@ -1018,44 +1039,56 @@ __global__ __launch_bounds__(kPcWaves * 64, 1) void decode_partition_pc_kernel(D
         bq[kt][i] = col < 8 ? hi : static_cast<_Float16>(v - static_cast<float>(hi));
       }
     }
-    setup();
-    __syncthreads();
     uint16_t* stage = &sm.s.stage[p][0][0][0];
     float* dstage = &sm.s.dstage[p][0][0];
     // Per step: stage its statistics, fetch those of two steps later into the
     // freed registers, then build the operands (the fetch overlaps the work).
-    for (int s = -1; s < steps; s += 2) {
-      // step s + 1 (even) into slot 0; fetch step s + 3
-      produce_stage<D>(pst0[0], pst0[1], stage, dstage, lane);
+    // Step 0 is built before the set-up barrier (its page-table reads for
+    // step 2 come after the products, off their path).
+    produce_stage<D>(pst0[0], pst0[1], stage, dstage, lane);
+    if (steps > 0)
+      produce_compute<D>(stage, dstage, &sm.s.slots[2 * p][0], &sm.s.slots[2 * p + 1][0], kg, col, hq, bq);
 #pragma unroll
-      for (int gg = 0; gg < 2; ++gg) {
-        const int t = gpos(s + 3, 2 * p + gg);
-        stats_load<D>(a, h, t, te, lane, pt_at(t), pst0[gg]);
-      }
-      if (s + 1 < steps)
-        produce_compute<D>(stage, dstage, &sm.s.slots[2 * p][0], &sm.s.slots[2 * p + 1][0], kg, col, hq, bq);
-      wave_sync();   // the staging may be overwritten by the next step
-      __syncthreads();
-      // step s + 2 (odd) into slot 1; fetch step s + 4
+    for (int gg = 0; gg < 2; ++gg) {
+      const int t = gpos(2, 2 * p + gg);
+      stats_load<D>(a, h, t, te, lane, pt_direct(t), pst0[gg]);
+    }
+    wave_sync();
+    __syncthreads();
+    for (int u = 0; u < steps; u += 2) {
+      // step u + 1 (odd) into slot 1; fetch step u + 3
       produce_stage<D>(pst1[0], pst1[1], stage, dstage, lane);
 #pragma unroll
       for (int gg = 0; gg < 2; ++gg) {
-        const int t = gpos(s + 4, 2 * p + gg);
+        const int t = gpos(u + 3, 2 * p + gg);
         stats_load<D>(a, h, t, te, lane, pt_at(t), pst1[gg]);
       }
-      if (s + 2 < steps)
+      if (u + 1 < steps)
         produce_compute<D>(stage, dstage, &sm.s.slots[2 * p][1], &sm.s.slots[2 * p + 1][1], kg, col, hq, bq);
+      wave_sync();   // the staging may be overwritten by the next step
+      __syncthreads();
+      // step u + 2 (even) into slot 0; fetch step u + 4
+      produce_stage<D>(pst0[0], pst0[1], stage, dstage, lane);
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg) {
+        const int t = gpos(u + 4, 2 * p + gg);
+        stats_load<D>(a, h, t, te, lane, pt_at(t), pst0[gg]);
+      }
+      if (u + 2 < steps)
+        produce_compute<D>(stage, dstage, &sm.s.slots[2 * p][0], &sm.s.slots[2 * p + 1][0], kg, col, hq, bq);
       wave_sync();
       __syncthreads();
     }
     __syncthreads();   // merge: consumers hand over their accumulators
   } else {
     // ---- consumer: step u's group in buf[u & 1]
+    const int pt_entry = page0 + tid < a.max_pages ? ptab[page0 + tid] : -1;
     ConsumerLoad<D> buf0, buf1;
-    bool ok0, ok1 = false;
+    bool ok0, ok1;
     {
-      const int t = gpos(0, c);
-      consumer_load<D>(a, h, t, te, lane, kg, pt_direct(t), buf0, ok0);
+      const int t0 = gpos(0, c), t1 = gpos(1, c);
+      consumer_load<D>(a, h, t0, te, lane, kg, pt_direct(t0), buf0, ok0);
+      consumer_load<D>(a, h, t1, te, lane, kg, pt_direct(t1), buf1, ok1);
     }
     const uint32_t lane_off = static_cast<uint32_t>(lane & (kTabCopies - 1)) << 3;
     WaveState<D, SLOTS, ASYM> ws;
@@ -1068,28 +1101,28 @@ __global__ __launch_bounds__(kPcWaves * 64, 1) void decode_partition_pc_kernel(D
       for (int ct = 0; ct < CT; ++ct) ws.acc[k][ct] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < (ASYM ? NSETS : 1); ++k) ws.accs[k] = floatx4{0.f, 0.f, 0.f, 0.f};
-    setup();
+    setup(pt_entry);
     __syncthreads();
     const uint2* tab = sm.s.tab;
-    for (int s = -1; s < steps; s += 2) {
-      // step s (odd; none before the first pass), then fetch step s + 2
-      if (s >= 0 && ok1) {
-        const int t0 = gpos(s, c);
-        consume<D, SLOTS, ASYM>(buf1, &sm.s.slots[c][1], t0, te, t0 + kGroupTokens > te, kg, col, tab, lane_off, ws);
-      }
-      {
-        const int t = gpos(s + 2, c);
-        consumer_load<D>(a, h, t, te, lane, kg, pt_at(t), buf1, ok1);
-      }
-      __syncthreads();
-      // step s + 1 (even), then fetch step s + 3
+    for (int u = 0; u < steps; u += 2) {
+      // step u (even), then fetch step u + 2
       if (ok0) {
-        const int t0 = gpos(s + 1, c);
+        const int t0 = gpos(u, c);
         consume<D, SLOTS, ASYM>(buf0, &sm.s.slots[c][0], t0, te, t0 + kGroupTokens > te, kg, col, tab, lane_off, ws);
       }
       {
-        const int t = gpos(s + 3, c);
+        const int t = gpos(u + 2, c);
         consumer_load<D>(a, h, t, te, lane, kg, pt_at(t), buf0, ok0);
+      }
+      __syncthreads();
+      // step u + 1 (odd), then fetch step u + 3
+      if (ok1) {
+        const int t0 = gpos(u + 1, c);
+        consume<D, SLOTS, ASYM>(buf1, &sm.s.slots[c][1], t0, te, t0 + kGroupTokens > te, kg, col, tab, lane_off, ws);
+      }
+      {
+        const int t = gpos(u + 3, c);
+        consumer_load<D>(a, h, t, te, lane, kg, pt_at(t), buf1, ok1);
       }
       __syncthreads();
     }
@@ -1108,9 +1141,10 @@ __global__ __launch_bounds__(kPcWaves * 64, 1) void decode_partition_pc_kernel(D
         }
       }
     }
-    {
-      const int wm = wave_or_bits(ws.mask);
-      if (lane == 0 && wm) atomicOr(&s_mask, wm);
+    const int wm = wave_or_bits(ws.mask);
+    if (lane == 0) {
+      s_cmask[c] = wm;
+      if (wm) atomicOr(&s_mask, wm);
     }
     __syncthreads();   // the table and slots are dead from here on
     float M = -__builtin_inff();
@@ -1119,13 +1153,16 @@ __global__ __launch_bounds__(kPcWaves * 64, 1) void decode_partition_pc_kernel(D
     const float mw = s_m[c][hp];
     // (arguments <= 0: the raw base-2 exponential only flushes results below 2^-126)
     const float e = (mw == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+    // a set none of this wavefront's groups touched is zero: not written, not read
 #pragma unroll
-    for (int k = 0; k < NSETS; ++k)
+    for (int k = 0; k < NSETS; ++k) {
+      if (!(wm & set_bits<SLOTS>(k))) continue;
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
         const floatx4 v = ws.acc[k][ct] * e;
         sm.red[c][(k * CT + ct) * 64 + lane] = float4{v[0], v[1], v[2], v[3]};
       }
+    }
   }
   __syncthreads();
   const int wmask = s_mask;
@@ -1136,9 +1173,10 @@ __global__ __launch_bounds__(kPcWaves * 64, 1) void decode_partition_pc_kernel(D
     const int sl2 = c2 / GP, hp2 = c2 % GP;
     const int m = k * SLOTS + sl2;
     if (sl2 < SLOTS && m < kModalities && hp2 < G && (wmask & (1 << m))) {
-      float4 sum = sm.red[0][pos];
+      float4 sum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int w = 1; w < kConsumers; ++w) {
+      for (int w = 0; w < kConsumers; ++w) {
+        if (!(s_cmask[w] & set_bits<SLOTS>(k))) continue;   // uniform over the wavefront's positions
         const float4 v = sm.red[w][pos];
         sum.x += v.x;
         sum.y += v.y;
@@ -1168,6 +1206,40 @@ __global__ __launch_bounds__(kPcWaves * 64, 1) void decode_partition_pc_kernel(D
     }
     part[f] = v;
   }
+}
+
+// Reductions over lanes without LDS round trips: DPP inside rows of 16
+// lanes (quad swaps, half-row and row mirrors), then the permlane swaps
+// across rows.  Every lane of the group gets the same result (each step adds
+// or maxes a pair in both orders, which are equal).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __uint_as_float(static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(__float_as_uint(v)), CTRL, 0xF, 0xF, false)));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<0xB1>(v);    // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);    // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v);   // row_half_mirror
+  v += dpp_f<0x140>(v);   // row_mirror
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
 }
 
 // Merge: workgroup (session, query head, row block) rescales every
@@ -1209,13 +1281,24 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
   __shared__ float s_M;
 
   // Workgroup -> (session b, KV head h, query head of the group gq, row
-  // block rb), with every workgroup of one (b, h) on the XCD (b Hkv + h) mod 8:
-  // they share that KV head's rotations and partials through one L2.
+  // block rb).  With at least 8 (session, KV head) keys, every workgroup of
+  // one key sits on the XCD key mod 8, sharing its rotations and partials
+  // through one L2; with fewer keys, key k takes the XCDs k, k + keys, ...
+  // so that every XCD works.
   const int x = blockIdx.x % kXcds, y = blockIdx.x / kXcds;
   const int per_key = a.group * RB;
-  const int key = (y / per_key) * kXcds + x;       // b * Hkv + h
-  if (key >= a.batch * a.hkv) return;
-  const int gq = (y % per_key) / RB, rb = y % RB;
+  const int keys = a.batch * a.hkv;
+  int key, item;
+  if (keys >= kXcds) {
+    key = (y / per_key) * kXcds + x;               // b * Hkv + h
+    item = y % per_key;
+  } else {
+    key = x % keys;
+    const int nx = (kXcds - 1 - key) / keys + 1;   // XCDs serving this key
+    item = y * nx + x / keys;
+  }
+  if (key >= keys || item >= per_key) return;
+  const int gq = item / RB, rb = item % RB;
   const int h = key % a.hkv;
   const int i = h * a.group + gq;
   const int hi = (key / a.hkv) * a.hq + i;         // b * Hq + i
@@ -1242,24 +1325,26 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
   const int col = tid % NCOL, g = tid / NCOL;
   const bool loader = g < SG;
   const int cm = col / F4, cf = col % F4;
+  // (every thread loads, the clamped indices stay inside the head's partials;
+  // only the loaders' values are used)
   float4 blk[kMergeChunk];
 #pragma unroll
   for (int k = 0; k < kMergeChunk; ++k) {
     const int s = min(g + k * SG, S - 1);
-    if (loader) blk[k] = reinterpret_cast<const float4*>(P + static_cast<size_t>(s) * PS + kPartialHeader + cm * D)[cf];
+    blk[k] = reinterpret_cast<const float4*>(P + static_cast<size_t>(s) * PS + kPartialHeader + cm * D)[cf];
   }
   // Headers: [m, l, mask, -, S0, S1, S2, -] of splits tid, tid + 512, ...
   // (the first one stays in registers).
   const float4 ninf4 = {-__builtin_inff(), 0.f, 0.f, 0.f};
-  const float4 hd0 = tid < S ? reinterpret_cast<const float4*>(P + static_cast<size_t>(tid) * PS)[0] : ninf4;
+  const float4 hd0r = reinterpret_cast<const float4*>(P + static_cast<size_t>(min(tid, S - 1)) * PS)[0];
+  const float4 hd0 = tid < S ? hd0r : ninf4;
   float4 hd1 = {0.f, 0.f, 0.f, 0.f};
   if constexpr (ASYM) {
     if (tid < S) hd1 = reinterpret_cast<const float4*>(P + static_cast<size_t>(tid) * PS)[1];
   }
   float mx = hd0.x;
   for (int s = tid + kMergeThreads; s < S; s += kMergeThreads) mx = fmaxf(mx, P[static_cast<size_t>(s) * PS]);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  mx = wave_max(mx);
   if (lane == 0) s_red[wave][0] = mx;
   __syncthreads();
   if (tid == 0) {
@@ -1284,13 +1369,10 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
       ss[2] += (pm & 4) ? e * h1.z : 0.f;
     }
   }
+  ls = wave_sum(ls);
+  if constexpr (ASYM)
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    ls += __shfl_xor(ls, off);
-    if constexpr (ASYM)
-#pragma unroll
-      for (int m = 0; m < kModalities; ++m) ss[m] += __shfl_xor(ss[m], off);
-  }
+    for (int m = 0; m < kModalities; ++m) ss[m] = wave_sum(ss[m]);
   if (lane == 0) {
     s_red[wave][1] = ls;
 #pragma unroll
@@ -1311,16 +1393,23 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
           blk[k] = reinterpret_cast<const float4*>(P + static_cast<size_t>(s) * PS + kPartialHeader + cm * D)[cf];
         }
       }
+      // weights and masks of the chunk first (no branch between the LDS
+      // reads), then the sums in split order
+      float ek[kMergeChunk];
+      bool pk[kMergeChunk];
 #pragma unroll
       for (int k = 0; k < kMergeChunk; ++k) {
         const int s = base + g + k * SG;
-        if (s < S && (s_mk[s] & bit)) {
-          const float e = s_e[s];
-          acc.x += e * blk[k].x;
-          acc.y += e * blk[k].y;
-          acc.z += e * blk[k].z;
-          acc.w += e * blk[k].w;
-        }
+        const int sc = min(s, S - 1);
+        ek[k] = s_e[sc];
+        pk[k] = (s < S) & ((s_mk[sc] & bit) != 0);   // both sides read: no branch
+      }
+#pragma unroll
+      for (int k = 0; k < kMergeChunk; ++k) {
+        acc.x += pk[k] ? ek[k] * blk[k].x : 0.f;
+        acc.y += pk[k] ? ek[k] * blk[k].y : 0.f;
+        acc.z += pk[k] ? ek[k] * blk[k].z : 0.f;
+        acc.w += pk[k] ? ek[k] * blk[k].w : 0.f;
       }
     }
     s_part[g][col] = acc;
@@ -1365,11 +1454,9 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
     acc += am;
     if constexpr (ASYM) rs += Sm[m] * rm;
   }
-#pragma unroll
-  for (int off = 1; off < QT; off <<= 1) {
-    acc += __shfl_xor(acc, off);
-    if constexpr (ASYM) rs += __shfl_xor(rs, off);
-  }
+  static_assert(QT == 16, "one output row per 16-lane row");
+  acc = row16_sum(acc);
+  if constexpr (ASYM) rs = row16_sum(rs);
   if (q == 0) a.out[head * D + row] = (l > 0.f) ? (a.chalf * acc + a.cmid * rs) * (a.value_scale / l) : 0.f;
 }
 
@@ -1398,7 +1485,9 @@ hipError_t launch_decode_t(int batch, const DecodeArgs& a, hipStream_t s) {
   else if (a.group <= 8) launch_partition_pc<D, 2>(batch, a, s);
   else launch_partition<D, 1, kDecodeWaves / 2>(batch, a, s);
   const int keys = a.hkv * batch;
-  const dim3 mgrid(kXcds * ((keys + kXcds - 1) / kXcds) * a.group * MergeShape<D>::RB);
+  const int per_key = a.group * MergeShape<D>::RB;
+  const int rows = keys >= kXcds ? ((keys + kXcds - 1) / kXcds) * per_key : (per_key + kXcds / keys - 1) / (kXcds / keys);
+  const dim3 mgrid(kXcds * rows);
   if (a.cmid != 0.f)
     hipLaunchKernelGGL((decode_merge_kernel<D, true>), mgrid, dim3(kMergeThreads), 0, s, a);
   else

@@ -75,6 +75,7 @@ struct DecodeArgs {
   int32_t hq, hkv, group, page_tokens, max_pages, num_pages;
   int32_t splits;         // partitions per (session, KV head)
   int32_t split_tokens;   // positions per partition (multiple of 32 * kDecodeWaves)
+  int32_t page_shift;     // log2(page_tokens) when it is a power of two, else -1
   float scale_log2e;      // softmax scale * log2(e)
   float value_scale;      // 1 / sqrt(d)
   float cmid, chalf;      // codebook centre (c0 + c3) / 2 and half range (c3 - c0) / 2
