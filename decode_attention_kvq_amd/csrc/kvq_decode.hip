@@ -643,6 +643,40 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_partition_kernel(DecodeArgs
   }
 }
 
+// Reductions over lanes without LDS round trips: DPP inside rows of 16
+// lanes (quad swaps, half-row and row mirrors), then the permlane swaps
+// across rows.  Every lane of the group gets the same result (each step adds
+// or maxes a pair in both orders, which are equal).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __uint_as_float(static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(__float_as_uint(v)), CTRL, 0xF, 0xF, false)));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<0xB1>(v);    // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);    // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v);   // row_half_mirror
+  v += dpp_f<0x140>(v);   // row_mirror
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+
 // ---------------------------------------------------------------------------
 // Producer / consumer partition kernel (G <= 8).
 //
@@ -829,21 +863,25 @@ __device__ __forceinline__ void consume(const ConsumerLoad<D>& cur, const QtSlot
   constexpr int NSETS = Slots<SLOTS>::NSETS;
   const int head = col & 7;
   const float bias = slot->bias[head];
+  // Columns 0..7 take q~'s fp16 hi parts of the heads, columns 8..15 the lo
+  // parts; the two halves of each score are joined across the row below.
   floatx4 sc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
   for (int kt = 0; kt < KT; ++kt) {
-    const half8 qt_hi = *reinterpret_cast<const half8*>(&slot->qt[0][head][32 * kt + 8 * kg]);
-    const half8 qt_lo = *reinterpret_cast<const half8*>(&slot->qt[1][head][32 * kt + 8 * kg]);
+    const half8 qt = *reinterpret_cast<const half8*>(&slot->qt[col >> 3][head][32 * kt + 8 * kg]);
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       const int j0 = mt * (D / 16) + kt * 2;   // code bytes j0, j0 + 1 of this (mt, kt)
       const uint2 x0 = lookup(tab, cur.kc[j0 >> 2], byte_sel(j0 & 3), lane_off);
       const uint2 x1 = lookup(tab, cur.kc[(j0 + 1) >> 2], byte_sel((j0 + 1) & 3), lane_off);
-      const half8 ak = as_half8(x0, x1);
-      sc[mt] = mfma(ak, qt_hi, sc[mt]);
-      sc[mt] = mfma(ak, qt_lo, sc[mt]);
+      sc[mt] = mfma(as_half8(x0, x1), qt, sc[mt]);
     }
   }
+  // score = hi part + lo part: add the partner column (col ^ 8, DPP row_ror:8)
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sc[mt][r] += dpp_f<0x128>(sc[mt][r]);
   uint32_t vmask[4] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
   if (partial) {
     // positions at or past te: score -inf (weight 0), weight bits cleared.
@@ -1206,40 +1244,6 @@ __global__ __launch_bounds__(kPcWaves * 64, 1) void decode_partition_pc_kernel(D
     }
     part[f] = v;
   }
-}
-
-// Reductions over lanes without LDS round trips: DPP inside rows of 16
-// lanes (quad swaps, half-row and row mirrors), then the permlane swaps
-// across rows.  Every lane of the group gets the same result (each step adds
-// or maxes a pair in both orders, which are equal).
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __uint_as_float(static_cast<uint32_t>(
-      __builtin_amdgcn_update_dpp(0, static_cast<int>(__float_as_uint(v)), CTRL, 0xF, 0xF, false)));
-}
-__device__ __forceinline__ float row16_sum(float v) {
-  v += dpp_f<0xB1>(v);    // quad_perm [1,0,3,2]
-  v += dpp_f<0x4E>(v);    // quad_perm [2,3,0,1]
-  v += dpp_f<0x141>(v);   // row_half_mirror
-  v += dpp_f<0x140>(v);   // row_mirror
-  return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-  v = row16_sum(v);
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
-}
-__device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, dpp_f<0xB1>(v));
-  v = fmaxf(v, dpp_f<0x4E>(v));
-  v = fmaxf(v, dpp_f<0x141>(v));
-  v = fmaxf(v, dpp_f<0x140>(v));
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
 }
 
 // Merge: workgroup (session, query head, row block) rescales every
