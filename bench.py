@@ -33,7 +33,8 @@ HBM_PEAK_GBS = 8000.0
 # what the counter reads for a plain 256 MiB device copy (FETCH_SIZE x 1.9998,
 # WRITE_SIZE x 1.0); see profiles/decode_80k_hbm_bytes.md.  Valid only for
 # the decode source the counters were taken on (SHA-256 of kvq_decode.hip).
-DECODE_TRAFFIC = {"kvq_decode_sha256": None, "bytes": None}
+DECODE_TRAFFIC = {"kvq_decode_sha256": "eebfa52c03253731fb6834c548ea2972622318740ae460a17e8c04614322a37a",
+                  "bytes": 35025910}
 
 
 def decode_traffic_bytes():
