@@ -209,6 +209,23 @@ def main():
     torch.cuda.synchronize()
     warm_ms = ew0.elapsed_time(ew1) / (10 * args.replicas)
 
+    # Context: a plain device copy (read + write) of the same byte count, one
+    # buffer per replica so it runs from HBM, HIP events.
+    sbufs = [torch.ones(dec_bytes // 4, dtype=torch.float32, device=dev) for _ in range(args.replicas)]
+    cdst = torch.empty_like(sbufs[0])
+    for sb in sbufs:
+        cdst.copy_(sb)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(5):
+        for sb in sbufs:
+            cdst.copy_(sb)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_ms = c0.elapsed_time(c1) / (5 * len(sbufs))
+    copy_bytes = 2 * cdst.numel() * 4
+    del sbufs, cdst
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, cfg, caches[0], args.cpu_seconds)
@@ -232,6 +249,7 @@ def main():
         "cpu_baseline": cpu,
         "extra": {"decode_us_hbm": dec_ms * 1e3, "decode_us_warm": warm_ms * 1e3,
                   "decode_kv_tokens_per_s": Ld / (dec_ms * 1e-3),
+                  "copy_read_write_GBps": copy_bytes / (copy_ms * 1e-3) / 1e9,
                   "step_wall_us": wall / steps * 1e6},
     }
     print(json.dumps(rec), flush=True)

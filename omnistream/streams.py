@@ -188,16 +188,17 @@ def _draw_values(rng, modality, basis, lam):
 
 def generate(cfg_id: int, length: Optional[int] = None, batch: Optional[int] = None,
              len_range: Optional[tuple] = None, append_tokens: Optional[int] = None,
-             page_tokens: Optional[int] = None) -> Workload:
+             page_tokens: Optional[int] = None, n_q_heads: Optional[int] = None) -> Workload:
     """Build the seeded workload of one configuration.
 
     Overrides shrink a configuration for fast tests while keeping its recipe,
-    head shapes and dtypes.  Seeds: SeedSequence(cfg_id) spawned in the fixed
+    KV heads and dtypes (n_q_heads changes only the number of queries, i.e.
+    the GQA group size).  Seeds: SeedSequence(cfg_id) spawned in the fixed
     order signs, bases, keys, values, chunking, queries, lengths/pages.
     """
     base = CONFIGS[cfg_id]
     cfg = StreamConfig(
-        base.cfg_id, base.name, base.head_dim, base.n_q_heads, base.n_kv_heads,
+        base.cfg_id, base.name, base.head_dim, base.n_q_heads if n_q_heads is None else n_q_heads, base.n_kv_heads,
         base.batch if batch is None else batch, base.dtype, base.recipe,
         length=base.length if length is None else length,
         len_range=base.len_range if len_range is None else len_range,

@@ -60,10 +60,15 @@ CASES = [
     (2, dict(length=5000)),
     (3, dict(batch=3, len_range=(700, 2600))),
     (4, dict(length=1500)),
+    # GQA groups above 8 (the one-role partition kernel): 16, 12 and 10 heads
+    (1, dict(length=3001, n_q_heads=32)),
+    (0, dict(length=1000, n_q_heads=12)),
+    (3, dict(batch=2, len_range=(700, 1900), n_q_heads=20)),
 ]
 
 
-@pytest.mark.parametrize("cfg_id,kw", CASES, ids=[f"cfg{c}" for c, _ in CASES])
+@pytest.mark.parametrize("cfg_id,kw", CASES, ids=[f"cfg{c}" + (f"-G{kw['n_q_heads']}" if "n_q_heads" in kw else "")
+                                                   for c, kw in CASES])
 def test_append_and_decode_parity(cfg_id, kw):
     import decode_attention_kvq_amd as K
     h = H()
