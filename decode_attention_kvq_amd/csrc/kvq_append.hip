@@ -420,17 +420,21 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
   }
 
   // Completion ticket of the session: the last workgroup advances seq_len
-  // and rearms the ticket for the next append.
+  // and rearms the ticket for the next append.  The only order needed is
+  // that every workgroup's read of seq_len precedes the last workgroup's
+  // store: each workgroup used that value (waited for it) before this
+  // barrier and its ticket, so relaxed atomics suffice.  The cache writes
+  // need no release here: the next kernel starts after this one completes.
   __syncthreads();
   if (tid == 0) {
     const int total = a.append_x * static_cast<int>(gridDim.y);
-    const int t = __hip_atomic_fetch_add(&a.tickets[sb], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const int t = __hip_atomic_fetch_add(&a.tickets[sb], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = (t == total - 1);
   }
   __syncthreads();
   if (s_last && tid == 0) {
     __hip_atomic_store(&a.tickets[sb], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&a.seq_len[sb], L_new, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&a.seq_len[sb], L_new, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
