@@ -57,11 +57,15 @@ def pack_key_codes(codes: np.ndarray, d: int) -> np.ndarray:
 
 
 def session_view(host: dict, cfg, b: int, length: int, h: int) -> dict:
-    """Logical arrays of session b, KV head h, from Cache.host_arrays()."""
+    """Logical arrays of session b, KV head h, from Cache.host_arrays().
+
+    A logical page whose page-table entry is negative is not retained: its
+    positions read as physical page 0 here and are False in `retained`."""
     d, hkv, pt = cfg.head_dim, cfg.n_kv_heads, cfg.page_tokens
     gp = pt // GROUP
     npg = -(-length // pt)
-    pages = host["page_table"][b, :npg].astype(np.int64)
+    mapped = host["page_table"][b, :npg].astype(np.int64)
+    pages = np.maximum(mapped, 0)
     kb = host["k_codes"].reshape(-1, hkv, gp, 8 * d)[pages, h]          # [npg, gp, 8d]
     vb = host["v_codes"].reshape(-1, hkv, gp, 8 * d)[pages, h]
     st = host["k_stats"].reshape(-1, hkv, gp, 2, d)[pages, h]           # [npg, gp, 2, d]
@@ -74,4 +78,5 @@ def session_view(host: dict, cfg, b: int, length: int, h: int) -> dict:
     return dict(k_codes=kc, v_codes=vc,
                 lo=st[:, 0].copy().view(np.float16), hi=st[:, 1].copy().view(np.float16),
                 norms=nr.reshape(-1)[:length].copy().view(np.float16),
-                modality=md.reshape(-1)[:length].copy())
+                modality=md.reshape(-1)[:length].copy(),
+                retained=np.repeat(mapped >= 0, pt)[:length])

@@ -45,6 +45,16 @@
  * Slots past the session length hold unspecified codes and are never read
  * as data.  The raw key tail keeps the keys of the open (partial) group:
  *   k_tail   [batch][Hkv][32][d] in kv_dtype, slot = position % 32
+ *
+ * Sparse page sets (the page-granular tile skipping of the OmniTide paging
+ * page, block-sparse paged attention).  A page-table entry outside
+ * [0, num_pages), -1 by convention, marks a logical page that is not
+ * retained: the decode reads nothing from it and its positions take no part
+ * in the softmax, and an append writes no codes, statistics, norms or
+ * modality bytes for positions on it (they are dropped; the session length
+ * still advances and the raw key tail is still kept).  Mapping a page again
+ * later exposes whatever its physical page holds.  A session with no
+ * retained position decodes to zeros.
  */
 #ifndef KVQ_H
 #define KVQ_H
@@ -86,7 +96,8 @@ typedef struct kvq_cache {
   uint8_t*       v_codes;     /* device */
   uint16_t*      v_norms;     /* device, fp16 bits */
   uint8_t*       modality;    /* device */
-  const int32_t* page_table;  /* device [batch][max_pages]: physical page of each logical page */
+  const int32_t* page_table;  /* device [batch][max_pages]: physical page of each logical page,
+                                  -1 for a page that is not retained */
   int32_t*       seq_len;     /* device [batch]: cached positions per session */
   void*          k_tail;      /* device [batch][Hkv][32][d] kv_dtype */
   int32_t*       append_tickets; /* device [batch], zero when the cache is created; the
@@ -167,14 +178,17 @@ size_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t max_len);
 /*
  * kvq_decode_attention - one decode step of every query head against the
  * packed cache (Sec. 1, Implementation bullet; Abstract: no dense FP16 cache).
- * For query head i of session b, over positions t < seq_len[b]:
+ * For query head i of session b, over positions t < seq_len[b] whose
+ * logical page is mapped (see sparse page sets above):
  *   s_t = scale * <q_rot[b][i], k_hat_t>,  k_hat_t = LO + (c[code]-c0)(HI-LO)/(c3-c0)
  *   p = softmax(s);  A_m = sum_{t: modality m} p_t (N_t / sqrt(d)) c[vcode_t]
  *   out[b][i] = sum_m R_{h,m} A_m
  * The context is split into partitions processed in parallel (online
  * softmax per partition); a second kernel merges them and applies R_{h,m}.
  * q_rot: device [batch][Hq][d] fp32 (from kvq_rotate_query); out: device
- * [batch][Hq][d] fp32; an empty session gives zeros.  The partition plan
+ * [batch][Hq][d] fp32; a session with no such position gives zeros.  Pages
+ * that are not retained still count towards the plan (their steps are
+ * skipped, not compacted away).  The partition plan
  * comes from max(seq_len_host).  workspace: device, at least
  * kvq_decode_workspace_bytes(cfg, max(seq_len_host)) bytes.
  * Errors: KVQ_ERR_INVALID, KVQ_ERR_WORKSPACE, KVQ_ERR_LAUNCH,

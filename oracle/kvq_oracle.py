@@ -36,6 +36,9 @@ Readings where the pages are silent (each repeated in the design notes):
     stored norm is fp16(n); reconstruction is R_m (N / sqrt(d)) c[code].
   * Query head i uses KV head floor(i / G); scores use scale 1/sqrt(d) unless
     given; an empty context attends to nothing and yields zeros.
+  * Sparse page sets (a retained-page list or mask, as in the survey's paging
+    follow-on): positions outside the retained set are left out before the
+    softmax, exactly as if they had never been cached.
 """
 from __future__ import annotations
 
@@ -239,35 +242,43 @@ def rotate_query(q: np.ndarray, signs: np.ndarray, n_kv_heads: int) -> np.ndarra
 
 
 def decode_attention_head(q_rot: np.ndarray, k_codes, lo16, hi16, v_codes, norms16,
-                          modality, rot, codebook, scale: float) -> np.ndarray:
+                          modality, rot, codebook, scale: float, retained=None) -> np.ndarray:
     """One query head over one KV head's packed cache, in the rotated domain.
 
-    scores s_t = scale * <q_rot, k_hat_t>; p = softmax(s) over all cached
+    scores s_t = scale * <q_rot, k_hat_t>; p = softmax(s) over the cached
     positions; A_m = sum over modality-m positions of p_t v_tilde_t; output
     o = sum_m R_m A_m (the inverse value rotation applied once per modality,
-    after aggregation)."""
+    after aggregation).
+
+    retained: optional boolean mask over positions (a sparse page set: the
+    positions kept, e.g. on the pages a retention policy kept).  Positions
+    outside it take no part: the softmax runs over the retained positions
+    only, and no retained position yields zeros."""
     L = k_codes.shape[0]
     d = q_rot.shape[-1]
-    if L == 0:
+    keep = np.ones(L, bool) if retained is None else np.asarray(retained, bool)[:L]
+    if L == 0 or not keep.any():
         return np.zeros(d)
     k_hat = dequantize_keys(k_codes, lo16, hi16, codebook)
     s = scale * (k_hat @ q_rot)
-    p = np.exp(s - s.max())
+    p = np.zeros(L)
+    p[keep] = np.exp(s[keep] - s[keep].max())
     p = p / p.sum()
     v_t = dequantize_values_rotated(v_codes, norms16, codebook)
     R = np.asarray(rot, np.float32).astype(np.float64)
     o = np.zeros(d)
     for m in range(N_MODALITIES):
-        idx = modality == m
+        idx = (modality == m) & keep
         if idx.any():
             o += R[m] @ (p[idx] @ v_t[idx])
     return o
 
 
 def decode_attention(q_rot: np.ndarray, caches: list, rot: np.ndarray, codebook,
-                     scale: float) -> np.ndarray:
+                     scale: float, retained=None) -> np.ndarray:
     """q_rot: [Hq, d]; caches: per KV head dicts with k_codes, lo, hi, v_codes,
-    norms and the shared modality; rot: [Hkv, 3, d, d].  Returns [Hq, d]."""
+    norms and the shared modality; rot: [Hkv, 3, d, d]; retained: optional
+    position mask (see decode_attention_head).  Returns [Hq, d]."""
     hq, d = q_rot.shape
     hkv = len(caches)
     g = hq // hkv
@@ -276,7 +287,7 @@ def decode_attention(q_rot: np.ndarray, caches: list, rot: np.ndarray, codebook,
         c = caches[i // g]
         out[i] = decode_attention_head(q_rot[i], c["k_codes"], c["lo"], c["hi"],
                                        c["v_codes"], c["norms"], c["modality"],
-                                       rot[i // g], codebook, scale)
+                                       rot[i // g], codebook, scale, retained)
     return out
 
 

@@ -24,14 +24,15 @@ def _kv_tensor(x: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
 
 
 def build(w: Workload, page_table: Optional[np.ndarray] = None, chunks: Optional[Sequence[int]] = None,
-          upto: Optional[Sequence[int]] = None, device="cuda"):
+          upto: Optional[Sequence[int]] = None, num_pages: Optional[int] = None, device="cuda"):
     """Create cfg/params/cache for workload w and append every session's stream
-    (split into `chunks` sized appends if given) up to `upto[b]` positions."""
+    (split into `chunks` sized appends if given) up to `upto[b]` positions.
+    The pool holds `num_pages` physical pages (default: the largest mapped one + 1)."""
     import decode_attention_kvq_amd as K
     c = w.cfg
     kv_dtype = torch.bfloat16 if c.dtype == "bf16" else torch.float32
     pt = w.page_table if page_table is None else page_table
-    num_pages = int(pt.max()) + 1
+    num_pages = int(pt.max()) + 1 if num_pages is None else int(num_pages)
     cfg = K.Config(c.head_dim, c.n_q_heads, c.n_kv_heads, c.batch, w.page_tokens, pt.shape[1],
                    num_pages, kv_dtype)
     params = K.Params(torch.from_numpy(w.signs).to(device), torch.from_numpy(w.rot).to(device),
@@ -125,15 +126,19 @@ def check_codes(w: Workload, cfg, cache, sessions: Sequence[int], lengths: Optio
 
 def oracle_decode_over_gpu_codes(w: Workload, cfg, cache, q: np.ndarray, sessions: Sequence[int],
                                  scale: float) -> dict:
-    """The oracle attending over the GPU's own packed cache (codes read back)."""
+    """The oracle attending over the GPU's own packed cache (codes read back),
+    over the positions of the pages the page table maps (a negative entry
+    marks a page that is not retained)."""
     from decode_attention_kvq_amd.layout import session_view
     host = cache.host_arrays()
     out = {}
     for b in sessions:
         n = int(host["seq_len"][b])
         caches = [session_view(host, cfg, b, n, h) for h in range(w.cfg.n_kv_heads)]
+        keep = caches[0]["retained"] if caches else None
         q_rot = O.rotate_query(q[b], w.signs, w.cfg.n_kv_heads)
-        out[b] = O.decode_attention(q_rot, caches, w.rot, w.codebook, scale)
+        out[b] = O.decode_attention(q_rot, caches, w.rot, w.codebook, scale,
+                                    retained=None if keep is None or keep.all() else keep)
     return out
 
 

@@ -64,11 +64,23 @@ CASES = [
     (1, dict(length=3001, n_q_heads=32)),
     (0, dict(length=1000, n_q_heads=12)),
     (3, dict(batch=2, len_range=(700, 1900), n_q_heads=20)),
+    # page sizes: one group per page, a size that is not a power of two, large pages
+    (1, dict(length=3001, page_tokens=32)),
+    (3, dict(batch=3, len_range=(700, 2600), page_tokens=96)),
+    (0, dict(length=2100, page_tokens=512)),
 ]
 
 
-@pytest.mark.parametrize("cfg_id,kw", CASES, ids=[f"cfg{c}" + (f"-G{kw['n_q_heads']}" if "n_q_heads" in kw else "")
-                                                   for c, kw in CASES])
+def _case_id(c, kw):
+    s = f"cfg{c}"
+    if "n_q_heads" in kw:
+        s += f"-G{kw['n_q_heads']}"
+    if "page_tokens" in kw:
+        s += f"-P{kw['page_tokens']}"
+    return s
+
+
+@pytest.mark.parametrize("cfg_id,kw", CASES, ids=[_case_id(c, kw) for c, kw in CASES])
 def test_append_and_decode_parity(cfg_id, kw):
     import decode_attention_kvq_amd as K
     h = H()
@@ -166,6 +178,94 @@ def test_paged_equals_contiguous():
     out_p = K.kvq_decode_attention(cfg_p, cache_p, params, q_rot).cpu().numpy()
     out_c = K.kvq_decode_attention(cfg_c, cache_c, params, q_rot).cpu().numpy()
     np.testing.assert_array_equal(out_p, out_c)
+
+
+# ------------------------------------------------ sparse page sets
+
+RETAINED_CASES = [
+    # (cfg_id, overrides, which logical pages lose their mapping)
+    (3, dict(batch=3, len_range=(700, 2600)), "random"),
+    (2, dict(length=5000), "alternate"),
+    (1, dict(length=3001, page_tokens=32), "random"),
+    (3, dict(batch=3, len_range=(700, 2600), page_tokens=96), "random"),
+    (3, dict(batch=3, len_range=(400, 1200)), "session"),
+]
+
+
+def _evicted(pattern: str, b: int, npg: int, rng) -> np.ndarray:
+    if pattern == "random":
+        return rng.random(npg) < 0.4
+    if pattern == "alternate":
+        return np.arange(npg) % 2 == 1
+    return np.full(npg, b == 1)          # "session": every page of session 1
+
+
+@pytest.mark.parametrize("cfg_id,kw,pattern", RETAINED_CASES,
+                         ids=[_case_id(c, kw) + f"-{p}" for c, kw, p in RETAINED_CASES])
+def test_decode_over_retained_pages(cfg_id, kw, pattern):
+    """A page-table entry of -1 drops that logical page from the decode: the
+    softmax runs over the positions of the mapped pages only (the oracle with
+    the same position mask), and a session with no mapped page gives zeros."""
+    import decode_attention_kvq_amd as K
+    h = H()
+    w = generate(cfg_id, **kw)
+    rng = np.random.default_rng(17)
+    cfg, params, cache = h.build(w)
+    pt = cache.page_table.cpu().numpy()
+    dropped = []
+    for b in range(w.cfg.batch):
+        npg = -(-int(w.lengths[b]) // w.page_tokens)
+        ev = _evicted(pattern, b, npg, rng)
+        pt[b, :npg][ev] = -1
+        dropped.append(int(ev.sum()))
+    cache.page_table.copy_(torch.from_numpy(pt))
+    _say(f"retained pages cfg{cfg_id} {kw} {pattern}: lengths={w.lengths.tolist()} pages dropped={dropped}")
+    scale = h.default_scale(w)
+    q_rot = K.kvq_rotate_query(cfg, params, h.query_tensor(w))
+    out = K.kvq_decode_attention(cfg, cache, params, q_rot, scale).cpu().numpy()
+    ref = h.oracle_decode_over_gpu_codes(w, cfg, cache, O.as_f64(w.q, w.dtype), range(w.cfg.batch), scale)
+    worst = 0.0
+    for b in range(w.cfg.batch):
+        if (pt[b] >= 0).sum() == 0:
+            np.testing.assert_array_equal(out[b], 0.0)
+            continue
+        worst = max(worst, float(h.normwise_rel_err(out[b].astype(np.float64), ref[b]).max()))
+    _say(f"decode worst normwise rel err {worst:.3e}")
+    assert worst <= h.ATTN_TOL
+
+
+def test_append_skips_unmapped_pages():
+    """Positions appended while their logical page has no physical page are not
+    stored: every mapped page holds the same bytes as in a build with all pages
+    mapped, the pages nobody maps stay untouched, lengths still advance, and
+    the decode equals the fully mapped cache's decode under the same sparse
+    page table."""
+    import decode_attention_kvq_amd as K
+    h = H()
+    w = generate(3, batch=3, len_range=(900, 2600))
+    rng = np.random.default_rng(23)
+    sparse = w.page_table.copy()
+    for b in range(w.cfg.batch):
+        npg = -(-int(w.lengths[b]) // w.page_tokens)
+        sparse[b, :npg][rng.random(npg) < 0.5] = -1
+    num_pages = int(w.page_table.max()) + 1
+    chunks = [45, 300, 7, 256]
+    _say(f"append onto unmapped pages: lengths={w.lengths.tolist()} "
+         f"unmapped={int((sparse < 0).sum() - (w.page_table < 0).sum())} chunks={chunks}")
+    cfg, params, full = h.build(w, chunks=chunks)
+    _, _, part = h.build(w, page_table=sparse, chunks=chunks, num_pages=num_pages)
+    a, b = full.host_arrays(), part.host_arrays()
+    np.testing.assert_array_equal(a["seq_len"], b["seq_len"])
+    kept = np.unique(sparse[sparse >= 0])
+    free = np.setdiff1d(np.arange(num_pages), kept)
+    for key in ("k_codes", "k_stats", "v_codes", "v_norms", "modality"):
+        pa, pb = a[key].reshape(num_pages, -1), b[key].reshape(num_pages, -1)
+        np.testing.assert_array_equal(pa[kept], pb[kept], err_msg=key)
+        assert not pb[free].any(), f"{key}: an unmapped page was written"
+    full.page_table.copy_(torch.from_numpy(sparse))
+    q_rot = K.kvq_rotate_query(cfg, params, h.query_tensor(w))
+    np.testing.assert_array_equal(K.kvq_decode_attention(cfg, part, params, q_rot).cpu().numpy(),
+                                  K.kvq_decode_attention(cfg, full, params, q_rot).cpu().numpy())
 
 
 def test_empty_and_tiny_sessions():

@@ -48,13 +48,22 @@ def _keys_map_to_unit(k, signs, codebook, group=32):
     return bad, lo, hi
 
 
-def _decode_rotates_with_transpose(q_rot, k_codes, lo16, hi16, v_codes, norms16, modality, rot, codebook, scale):
+def _decode_rotates_with_transpose(q_rot, k_codes, lo16, hi16, v_codes, norms16, modality, rot, codebook, scale,
+                                   retained=None):
     return _orig_dh(q_rot, k_codes, lo16, hi16, v_codes, norms16, modality,
-                    np.swapaxes(np.asarray(rot), -1, -2), codebook, scale)
+                    np.swapaxes(np.asarray(rot), -1, -2), codebook, scale, retained)
 
 
-def _decode_drops_scale(q_rot, k_codes, lo16, hi16, v_codes, norms16, modality, rot, codebook, scale):
-    return _orig_dh(q_rot, k_codes, lo16, hi16, v_codes, norms16, modality, rot, codebook, 1.0)
+def _decode_drops_scale(q_rot, k_codes, lo16, hi16, v_codes, norms16, modality, rot, codebook, scale,
+                        retained=None):
+    return _orig_dh(q_rot, k_codes, lo16, hi16, v_codes, norms16, modality, rot, codebook, 1.0, retained)
+
+
+def _decode_ignores_retained_set(q_rot, k_codes, lo16, hi16, v_codes, norms16, modality, rot, codebook, scale,
+                                 retained=None):
+    if retained is not None and not np.any(retained):
+        return np.zeros(q_rot.shape[-1])
+    return _orig_dh(q_rot, k_codes, lo16, hi16, v_codes, norms16, modality, rot, codebook, scale)
 
 
 def _rotate_query_wrong_head(q, signs, n_kv_heads):
@@ -83,6 +92,8 @@ MUTANTS = [
      [(P.test_decode_equals_dense_attention_over_dequantized_cache, 37)]),
     ("decode_attention_head", _decode_drops_scale,
      [(P.test_decode_equals_dense_attention_over_dequantized_cache, 37)]),
+    ("decode_attention_head", _decode_ignores_retained_set,
+     [(P.test_decode_over_a_retained_position_set, "random")]),
     ("rotate_query", _rotate_query_wrong_head,
      [(P.test_decode_equals_dense_attention_over_dequantized_cache, 37)]),
     ("dequantize_keys", _dequant_keys_off_by_one_level, [(P.test_key_group_range_is_restored, 0, 300)]),

@@ -248,9 +248,10 @@ def _tiny_case(seed, L, d=64, hq=4, hkv=2):
     return s, R, mod, q, caches
 
 
-def _dense_bruteforce(q, s, R, mod, caches, scale):
+def _dense_bruteforce(q, s, R, mod, caches, scale, keep=None):
     """Undo every rotation explicitly (scipy Hadamard matrix, R_m matrices),
-    then run textbook softmax attention on the dequantized dense cache."""
+    then run textbook softmax attention on the dequantized dense cache (over
+    the positions in `keep` only, when given)."""
     hq, d = q.shape
     hkv = len(caches)
     g = hq // hkv
@@ -268,8 +269,11 @@ def _dense_bruteforce(q, s, R, mod, caches, scale):
         K = krot @ M                                                   # k = M^T y, row form
         V = np.stack([R[h, mod[t]].astype(np.float64) @ (C["norms"][t].astype(np.float64)
                       / math.sqrt(d) * c[C["v_codes"][t]]) for t in range(L)])
-        p = scipy.special.softmax(scale * (K @ q[i]))
-        out[i] = p @ V
+        sel = np.arange(L) if keep is None else np.flatnonzero(keep[:L])
+        if sel.size == 0:
+            continue
+        p = scipy.special.softmax(scale * (K[sel] @ q[i]))
+        out[i] = p @ V[sel]
     return out
 
 
@@ -314,3 +318,26 @@ def test_decode_single_modality_uses_only_that_basis():
     a = O.decode_attention(O.rotate_query(q, s, 2), caches, R, CB, 0.125)
     b = O.decode_attention(O.rotate_query(q, s, 2), caches, R2, CB, 0.125)
     np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("pattern", ["pages", "random"])
+def test_decode_over_a_retained_position_set(pattern):
+    """A sparse page set: the masked decode equals textbook attention over the
+    retained positions alone; keeping everything changes nothing; keeping
+    nothing gives zeros."""
+    L = 160
+    s, R, mod, q, caches = _tiny_case(7, L)
+    scale = 1 / math.sqrt(64)
+    rng = np.random.default_rng(11)
+    if pattern == "pages":       # whole 32-position blocks kept or dropped
+        keep = np.repeat(rng.random(L // 32) < 0.5, 32)
+        keep[:32] = True
+    else:
+        keep = rng.random(L) < 0.3
+    qr = O.rotate_query(q, s, 2)
+    got = O.decode_attention(qr, caches, R, CB, scale, retained=keep)
+    ref = _dense_bruteforce(q, s, R, mod, caches, scale, keep)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12 * max(1.0, np.abs(ref).max()))
+    np.testing.assert_array_equal(O.decode_attention(qr, caches, R, CB, scale, retained=np.ones(L, bool)),
+                                  O.decode_attention(qr, caches, R, CB, scale))
+    np.testing.assert_array_equal(O.decode_attention(qr, caches, R, CB, scale, retained=np.zeros(L, bool)), 0)
