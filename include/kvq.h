@@ -46,8 +46,9 @@
  * as data.  The raw key tail keeps the keys of the open (partial) group:
  *   k_tail   [batch][Hkv][32][d] in kv_dtype, slot = position % 32
  *
- * Sparse page sets (the page-granular tile skipping of the OmniTide paging
- * page, block-sparse paged attention).  A page-table entry outside
+ * Sparse page sets (OmniTide page, Sec. 6 OmniPage and Sec. 6.1: pages sized
+ * to the attention tile, so that a page emptied by eviction can be skipped
+ * whole).  A page-table entry outside
  * [0, num_pages), -1 by convention, marks a logical page that is not
  * retained: the decode reads nothing from it and its positions take no part
  * in the softmax, and an append writes no codes, statistics, norms or
