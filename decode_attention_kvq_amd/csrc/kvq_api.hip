@@ -298,6 +298,10 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache,
     a.page_shift = 0;
     while ((1 << a.page_shift) < cfg->page_tokens) ++a.page_shift;
   }
+  a.blocks_per_page = cfg->n_kv_heads * (cfg->page_tokens / kGroupTokens);
+  // The streaming partition kernel addresses every cache array with 31-bit
+  // byte offsets; larger pools take the pointer-addressed kernel.
+  a.offsets31 = (size_t)cfg->num_pages * cfg->n_kv_heads * cfg->page_tokens * (cfg->head_dim / 4) < ((size_t)1 << 31);
   a.scale_log2e = (float)((double)scale * 1.4426950408889634);
   a.value_scale = (float)(1.0 / sqrt((double)cfg->head_dim));
   uint16_t lv[4];

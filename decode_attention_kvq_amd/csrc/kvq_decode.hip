@@ -31,6 +31,8 @@
 // Merge kernel: workgroups of (session, query head, block of output rows)
 // rescale and sum the partitions and apply the three R_m in a fixed order
 // (bitwise reproducible).
+#include <type_traits>
+
 #include "kvq_common.h"
 #include "kvq_internal.h"
 
@@ -1246,6 +1248,834 @@ __global__ __launch_bounds__(kPcWaves * 64, 1) void decode_partition_pc_kernel(D
   }
 }
 
+// ---------------------------------------------------------------------------
+// Streaming partition kernel (G <= 8).
+//
+// Every wavefront streams its own groups of the partition (g = wave,
+// wave + NW, ...) with kSwDepth groups of loads in flight and never waits for
+// another wavefront until the epilogue.  For each group it first builds the
+// statistics-dependent operands itself (one group ahead of the scores):
+//   - the group bias sum_c q_c (LO_c + HI_c) / 2 on the matrix cores, with
+//     the staged LO / HI rows as the A operand (rows 4kg, 4kg+2: LO; rows
+//     4kg+1, 4kg+3: HI) and q's fp16 hi / lo parts as the columns, so every
+//     lane of column col ends up with the bias of head col & 7;
+//   - q~ = q (HI - LO) / 2 as fp16 hi + lo, computed channel-major (a lane
+//     takes 8 channels of 1 or 2 heads, so every product is formed once) and
+//     handed to the score operand layout through a wave-private LDS slot of
+//     16-byte cells.
+// The scores, online softmax and value sums are those of the consumer above.
+constexpr int kSwWaves = 8;       // wavefronts per workgroup (the plan's unit is 32 * 8 positions)
+constexpr int kSwDepth = 4;       // groups of loads in flight per wavefront
+constexpr int kQtStride = 17;     // cells per channel block in a q~ slot (16 columns + 1, spreads the banks)
+
+template <int D>
+struct SwSlot {
+  uint4 qt[D / 8][kQtStride];     // [channel block cb][column]: channels 8cb..8cb+7 (hi: cols 0..7, lo: 8..15)
+};
+
+template <int D>
+struct SwLoad {
+  ConsumerLoad<D> c;
+  uint32_t st[D / 64];
+  bool ok;
+};
+
+// Buffer resources over the cache arrays, built once per kernel (every array
+// is below 2^31 bytes, checked on the host), plus a null resource whose loads
+// return zero without touching memory.  A group's loads take its block
+// offset as the scalar offset and a fixed per-lane vector offset.
+struct SwRsrc {
+  __amdgpu_buffer_rsrc_t k, v, st, nrm, md, null;
+};
+
+__device__ __forceinline__ SwRsrc sw_rsrc(const DecodeArgs& a) {
+  SwRsrc r;
+  r.k = span_rsrc(a.k_codes, 0x7FFFFFFF);
+  r.v = span_rsrc(a.v_codes, 0x7FFFFFFF);
+  r.st = span_rsrc(a.k_stats, 0x7FFFFFFF);
+  r.nrm = span_rsrc(a.v_norms, 0x7FFFFFFF);
+  r.md = span_rsrc(a.modality, 0x7FFFFFFF);
+  r.null = span_rsrc(a.k_codes, 0);
+  return r;
+}
+
+// Loads of one group: codes, statistics, norms and modality bytes of the
+// 32-position block blk (modality offset moff).  An invalid group (past the
+// partition, or on an unmapped page) passes blk = moff = 0: it reads block 0,
+// which stays in the L2, and is never consumed.
+template <int D>
+__device__ __forceinline__ void sw_load(const SwRsrc& r, int blk, int moff, int lane, int kg, SwLoad<D>& g) {
+  if constexpr (D == 128) {
+    const uint4 k4 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r.k, lane * 16, blk * (8 * D), 0));
+    const uint4 v4 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r.v, lane * 16, blk * (8 * D), 0));
+    g.c.kc[0] = k4.x; g.c.kc[1] = k4.y; g.c.kc[2] = k4.z; g.c.kc[3] = k4.w;
+    g.c.vc[0] = v4.x; g.c.vc[1] = v4.y; g.c.vc[2] = v4.z; g.c.vc[3] = v4.w;
+    const uint2 s2 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r.st, lane * 8, blk * (4 * D), 0));
+    g.st[0] = s2.x; g.st[1] = s2.y;
+  } else {
+    const uint2 k2 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r.k, lane * 8, blk * (8 * D), 0));
+    const uint2 v2 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r.v, lane * 8, blk * (8 * D), 0));
+    g.c.kc[0] = k2.x; g.c.kc[1] = k2.y;
+    g.c.vc[0] = v2.x; g.c.vc[1] = v2.y;
+    g.st[0] = __builtin_amdgcn_raw_buffer_load_b32(r.st, lane * 4, blk * (4 * D), 0);
+  }
+  g.c.nrm0 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r.nrm, 8 * kg, blk * 64, 0));
+  g.c.nrm1 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r.nrm, 32 + 8 * kg, blk * 64, 0));
+  g.c.md0 = __builtin_amdgcn_raw_buffer_load_b32(r.md, 4 * kg, moff, 0);
+  g.c.md1 = __builtin_amdgcn_raw_buffer_load_b32(r.md, 16 + 4 * kg, moff, 0);
+}
+
+// Heads per producer lane: D / 8 channel blocks x 8 heads over 64 lanes.
+template <int D>
+struct SwShape {
+  static constexpr int CB = D / 8;
+  static constexpr int HPL = 8 * CB / 64;
+};
+
+// Bias and q~ of one group from its statistics registers; `stage` is the
+// wavefront's 4D-byte staging of the LO / HI rows.
+template <int D>
+__device__ __forceinline__ float sw_produce(const uint32_t (&st)[D / 64], uint16_t* stage, SwSlot<D>* slot,
+                                            const float (&qs)[SwShape<D>::HPL][8], const uint4* bq_lds, int lane,
+                                            int kg) {
+  constexpr int KT = D / 32;
+  constexpr int CB = SwShape<D>::CB;
+  constexpr int HPL = SwShape<D>::HPL;
+  if constexpr (D == 128) {
+    reinterpret_cast<uint2*>(stage)[lane] = uint2{st[0], st[1]};
+  } else {
+    reinterpret_cast<uint32_t*>(stage)[lane] = st[0];
+  }
+  wave_sync();
+  const uint16_t* arow = stage + ((lane & 1) ? D : 0);   // A-operand row = lane & 15
+  floatx4 bacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt)
+    bacc = mfma(__builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(arow + 32 * kt + 8 * kg)),
+                __builtin_bit_cast(half8, bq_lds[kt * 64 + lane]), bacc);
+  const int cb = lane % CB, hs = lane / CB;
+  const uint4 lo4 = *reinterpret_cast<const uint4*>(stage + 8 * cb);
+  const uint4 hi4 = *reinterpret_cast<const uint4*>(stage + D + 8 * cb);
+  const uint32_t lw[4] = {lo4.x, lo4.y, lo4.z, lo4.w};
+  const uint32_t hw[4] = {hi4.x, hi4.y, hi4.z, hi4.w};
+  // The products below are hand-written instructions: make the LDS operands
+  // (query, statistics) complete first rather than rely on the compiler's
+  // wait insertion for inline assembly.
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  float d[8];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    d[2 * p] = f16_diff_lo(hw[p], lw[p]);
+    d[2 * p + 1] = f16_diff_hi(hw[p], lw[p]);
+  }
+#pragma unroll
+  for (int u = 0; u < HPL; ++u) {
+    const int head = hs * HPL + u;
+    uint32_t th[4], tl[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint2 sp = split_product(qs[u][2 * p], d[2 * p], qs[u][2 * p + 1], d[2 * p + 1]);
+      th[p] = sp.x;
+      tl[p] = sp.y;
+    }
+    slot->qt[cb][head] = uint4{th[0], th[1], th[2], th[3]};
+    slot->qt[cb][8 + head] = uint4{tl[0], tl[1], tl[2], tl[3]};
+  }
+  // rows 4kg (LO) and 4kg + 1 (HI); the partner column (col ^ 8) holds the
+  // other part of q
+  float bias = bacc[0] + bacc[1];
+  bias += dpp_f<0x128>(bias);
+  wave_sync();
+  return bias;
+}
+
+// Consumer step of the streaming kernel, in two parts so that the caller can
+// place independent work (the next group's operands) between the loads of
+// the codes and the softmax: sw_front looks up the key and value operands
+// and forms the scores (q~ from the wavefront's slot); sw_back runs the
+// online softmax and the value sums.
+template <int D>
+struct SwFront {
+  floatx4 sc[2];
+};
+
+// Value operands of a group: rows = channels 16 ct + col, k = positions.
+template <int D>
+__device__ __forceinline__ void sw_values(const ConsumerLoad<D>& cur, const uint2* tab, uint32_t lane_off,
+                                          half8 (&av)[D / 16]) {
+#pragma unroll
+  for (int ct = 0; ct < D / 16; ++ct) {
+    const int j0 = 2 * ct;
+    const uint2 x0 = lookup(tab, cur.vc[j0 >> 2], byte_sel(j0 & 3), lane_off);
+    const uint2 x1 = lookup(tab, cur.vc[(j0 + 1) >> 2], byte_sel((j0 + 1) & 3), lane_off);
+    av[ct] = as_half8(x0, x1);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void sw_front(const ConsumerLoad<D>& cur, const SwSlot<D>* slot, int kg, int col,
+                                         const uint2* tab, uint32_t lane_off, SwFront<D>& f) {
+  constexpr int KT = D / 32;
+  constexpr int CT = D / 16;
+  f.sc[0] = floatx4{0.f, 0.f, 0.f, 0.f};
+  f.sc[1] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) {
+    const half8 qt = __builtin_bit_cast(half8, slot->qt[4 * kt + kg][col]);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int j0 = mt * (D / 16) + kt * 2;   // code bytes j0, j0 + 1 of this (mt, kt)
+      const uint2 x0 = lookup(tab, cur.kc[j0 >> 2], byte_sel(j0 & 3), lane_off);
+      const uint2 x1 = lookup(tab, cur.kc[(j0 + 1) >> 2], byte_sel((j0 + 1) & 3), lane_off);
+      f.sc[mt] = mfma(as_half8(x0, x1), qt, f.sc[mt]);
+    }
+  }
+}
+
+template <int D, int SLOTS, bool ASYM>
+__device__ __forceinline__ void sw_back(const ConsumerLoad<D>& cur, SwFront<D>& f, float bias, int t0, int te,
+                                        bool partial, int kg, int col, const uint2* tab, uint32_t lane_off,
+                                        WaveState<D, SLOTS, ASYM>& ws) {
+  constexpr int CT = D / 16;
+  constexpr int GP = Slots<SLOTS>::GP;
+  constexpr int NSETS = Slots<SLOTS>::NSETS;
+  floatx4 (&sc)[2] = f.sc;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sc[mt][r] += dpp_f<0x128>(sc[mt][r]);
+  uint32_t vmask[4] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+  if (partial) {
+    int rem = te - t0;
+    asm volatile("" : "+s"(rem));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bool v = group_pos(kg, i) < rem;
+      sc[i >> 2][i & 3] = v ? sc[i >> 2][i & 3] : -__builtin_inff();
+      if (!v) vmask[i >> 1] &= (i & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+    }
+  }
+  // The weights are formed against the current reference max right away;
+  // the group's own max only decides (off the critical path) whether the
+  // reference must move first, which is rare (the reference sits kLazyMax
+  // above every score seen so far).
+  const uint32_t n4[4] = {cur.nrm0.x, cur.nrm0.y, cur.nrm1.x, cur.nrm1.y};
+  float pe[8];
+  uint32_t wp[4];
+  auto weights = [&](float off) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pe[i] = __builtin_amdgcn_exp2f(sc[i >> 2][i & 3] - off);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) wp[r] = to_value_column<SLOTS>(weight_pair(pe[2 * r], pe[2 * r + 1], n4[r]) & vmask[r]);
+  };
+  weights(ws.m_run - bias);
+  float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                   fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+  mx = rows_max(mx) + bias;
+  if (__any(mx > ws.m_run)) {
+    const float m_new = fmaxf(ws.m_run, mx + kLazyMax);
+    const float alpha = exp2f(ws.m_run - m_new);   // 0 on the first group
+    ws.l_run *= alpha;
+    const float alpha_v = __uint_as_float(to_value_column<SLOTS>(__float_as_uint(alpha)));
+#pragma unroll
+    for (int k = 0; k < NSETS; ++k) {
+      if constexpr (ASYM) ws.accs[k] *= alpha_v;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) ws.acc[k][ct] *= alpha_v;
+    }
+    ws.m_run = m_new;
+    // arguments are now <= 0 (or -inf): the raw base-2 exponential flushes only results below 2^-126
+    weights(ws.m_run - bias);
+  }
+  ws.l_run += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
+  half8 av[CT];
+  sw_values<D>(cur, tab, lane_off, av);
+  const int slot_c = col / GP;
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(cur.md0 & 0xFFu);
+  const bool uniform = !partial && __all(cur.md0 == m0 * 0x01010101u && cur.md1 == m0 * 0x01010101u);
+  const uint32_t md[2] = {cur.md0, cur.md1};
+#pragma unroll
+  for (int k = 0; k < NSETS; ++k) {
+    const uint32_t lo_mod = static_cast<uint32_t>(k * SLOTS);
+    const uint32_t my_mod = lo_mod + static_cast<uint32_t>(slot_c);
+    const bool col_ok = slot_c < SLOTS && my_mod < kModalities;
+    bool present;
+    uint32_t bm[4];
+    int got = 0;
+    if (uniform) {
+      present = m0 >= lo_mod && m0 < lo_mod + SLOTS && m0 < kModalities;
+      got = present ? (1 << m0) : 0;
+      const bool take = col_ok && my_mod == m0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) bm[r] = take ? wp[r] : 0u;
+    } else {
+      int rem = partial ? te - t0 : kGroupTokens;
+      uint32_t mdo[2] = {md[0], md[1]};
+      asm volatile("" : "+s"(rem), "+v"(mdo[0]), "+v"(mdo[1]));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        uint32_t keep = 0;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int i = 2 * r + u;
+          const uint32_t tm = (mdo[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+          const bool valid = group_pos(kg, i) < rem;
+          if (valid && tm >= lo_mod && tm < lo_mod + SLOTS && tm < kModalities) got |= 1 << tm;
+          keep |= (col_ok && tm == my_mod) ? (0xFFFFu << (16 * u)) : 0u;
+        }
+        bm[r] = wp[r] & keep;
+      }
+      present = __any(got != 0);
+    }
+    if (present) {
+      const half8 bw = __builtin_bit_cast(half8, uint4{bm[0], bm[1], bm[2], bm[3]});
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) ws.acc[k][ct] = mfma(av[ct], bw, ws.acc[k][ct]);
+      if constexpr (ASYM) {
+        const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
+        ws.accs[k] = mfma(ones, bw, ws.accs[k]);
+      }
+      ws.mask |= got;
+    }
+  }
+}
+
+// Softmax and value sums of a pair of groups (A, B) of one wavefront, with
+// rem_a / rem_b valid positions each (32 for a full group, fewer for the
+// session's last group, 0 for a group past the partition or on an unmapped
+// page; at least one of them is positive).  Positions past rem get the score
+// -inf, hence the weight 0.  The weights are formed against the current
+// reference max right away; the pair's own max only decides (off the
+// critical path) whether the reference must move first, which is rare: the
+// reference sits kLazyMax above every score seen so far.  Pairs of one
+// single modality (the common case inside a video, audio or text run) take
+// one branch to their accumulator set; others go through per-position
+// modality masks.
+template <int D, int SLOTS, bool ASYM>
+__device__ __forceinline__ void sw_back2(const ConsumerLoad<D>& ca, const ConsumerLoad<D>& cb, const SwFront<D>& fa,
+                                         const SwFront<D>& fb, float bias_a, float bias_b, int rem_a, int rem_b,
+                                         int kg, int col, const uint2* tab, uint32_t lane_off,
+                                         WaveState<D, SLOTS, ASYM>& ws) {
+  constexpr int CT = D / 16;
+  constexpr int GP = Slots<SLOTS>::GP;
+  constexpr int NSETS = Slots<SLOTS>::NSETS;
+  float s[2][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    s[0][i] = fa.sc[i >> 2][i & 3] + dpp_f<0x128>(fa.sc[i >> 2][i & 3]);
+    s[1][i] = fb.sc[i >> 2][i & 3] + dpp_f<0x128>(fb.sc[i >> 2][i & 3]);
+  }
+  if (rem_a < kGroupTokens || rem_b < kGroupTokens) {
+    int ra = rem_a, rb = rem_b;
+    asm volatile("" : "+s"(ra), "+s"(rb));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      s[0][i] = group_pos(kg, i) < ra ? s[0][i] : -__builtin_inff();
+      s[1][i] = group_pos(kg, i) < rb ? s[1][i] : -__builtin_inff();
+    }
+  }
+  const uint32_t na[4] = {ca.nrm0.x, ca.nrm0.y, ca.nrm1.x, ca.nrm1.y};
+  const uint32_t nb[4] = {cb.nrm0.x, cb.nrm0.y, cb.nrm1.x, cb.nrm1.y};
+  float pe[2][8];
+  uint32_t wa[4], wb[4];
+  auto weights = [&](float m_ref) {
+    const float oa = m_ref - bias_a, ob = m_ref - bias_b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      pe[0][i] = __builtin_amdgcn_exp2f(s[0][i] - oa);
+      pe[1][i] = __builtin_amdgcn_exp2f(s[1][i] - ob);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      wa[r] = to_value_column<SLOTS>(weight_pair(pe[0][2 * r], pe[0][2 * r + 1], na[r]));
+      wb[r] = to_value_column<SLOTS>(weight_pair(pe[1][2 * r], pe[1][2 * r + 1], nb[r]));
+    }
+  };
+  weights(ws.m_run);
+  float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                   fmaxf(fmaxf(s[0][4], s[0][5]), fmaxf(s[0][6], s[0][7]))) + bias_a;
+  mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])),
+                       fmaxf(fmaxf(s[1][4], s[1][5]), fmaxf(s[1][6], s[1][7]))) + bias_b);
+  mx = rows_max(mx);
+  if (__any(mx > ws.m_run)) {
+    const float m_new = fmaxf(ws.m_run, mx + kLazyMax);
+    const float alpha = exp2f(ws.m_run - m_new);   // 0 on the first group
+    ws.l_run *= alpha;
+    const float alpha_v = __uint_as_float(to_value_column<SLOTS>(__float_as_uint(alpha)));
+#pragma unroll
+    for (int k = 0; k < NSETS; ++k) {
+      if constexpr (ASYM) ws.accs[k] *= alpha_v;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) ws.acc[k][ct] *= alpha_v;
+    }
+    ws.m_run = m_new;
+    // arguments are now <= 0 (or -inf): the raw base-2 exponential flushes only results below 2^-126
+    weights(ws.m_run);
+  }
+  ws.l_run += (((pe[0][0] + pe[0][1]) + (pe[0][2] + pe[0][3])) + ((pe[0][4] + pe[0][5]) + (pe[0][6] + pe[0][7]))) +
+              (((pe[1][0] + pe[1][1]) + (pe[1][2] + pe[1][3])) + ((pe[1][4] + pe[1][5]) + (pe[1][6] + pe[1][7])));
+  const int slot_c = col / GP;
+  // value products of set k with the weight columns ba (group A) / bb (group B)
+  auto accumulate = [&](int k, const uint32_t (&ba)[4], const uint32_t (&bb)[4]) {
+    const half8 bwa = __builtin_bit_cast(half8, uint4{ba[0], ba[1], ba[2], ba[3]});
+    const half8 bwb = __builtin_bit_cast(half8, uint4{bb[0], bb[1], bb[2], bb[3]});
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const int j0 = 2 * ct;
+      const half8 va = as_half8(lookup(tab, ca.vc[j0 >> 2], byte_sel(j0 & 3), lane_off),
+                                lookup(tab, ca.vc[(j0 + 1) >> 2], byte_sel((j0 + 1) & 3), lane_off));
+      const half8 vb = as_half8(lookup(tab, cb.vc[j0 >> 2], byte_sel(j0 & 3), lane_off),
+                                lookup(tab, cb.vc[(j0 + 1) >> 2], byte_sel((j0 + 1) & 3), lane_off));
+      ws.acc[k][ct] = mfma(va, bwa, ws.acc[k][ct]);
+      ws.acc[k][ct] = mfma(vb, bwb, ws.acc[k][ct]);
+    }
+    if constexpr (ASYM) {
+      const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
+      ws.accs[k] = mfma(ones, bwa, ws.accs[k]);
+      ws.accs[k] = mfma(ones, bwb, ws.accs[k]);
+    }
+  };
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((rem_a > 0 ? ca.md0 : cb.md0) & 0xFFu);
+  const uint32_t mm = m0 * 0x01010101u;
+  const bool uniform = rem_a == kGroupTokens && rem_b == kGroupTokens && m0 < kModalities &&
+                       __all(ca.md0 == mm && ca.md1 == mm && cb.md0 == mm && cb.md1 == mm);
+  if (uniform) {
+    const int k0 = static_cast<int>(m0) / SLOTS;                    // the set holding m0
+    const bool take = slot_c == static_cast<int>(m0) - k0 * SLOTS;   // this column is m0's slot
+    uint32_t ba[4], bb[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      ba[r] = take ? wa[r] : 0u;
+      bb[r] = take ? wb[r] : 0u;
+    }
+#pragma unroll
+    for (int k = 0; k < NSETS; ++k)
+      if (k == k0) accumulate(k, ba, bb);
+    ws.mask |= 1 << m0;
+  } else {
+    int ra = rem_a, rb = rem_b;
+    uint32_t mda[2] = {ca.md0, ca.md1}, mdb[2] = {cb.md0, cb.md1};
+    asm volatile("" : "+s"(ra), "+s"(rb), "+v"(mda[0]), "+v"(mda[1]), "+v"(mdb[0]), "+v"(mdb[1]));
+#pragma unroll
+    for (int k = 0; k < NSETS; ++k) {
+      const uint32_t lo_mod = static_cast<uint32_t>(k * SLOTS);
+      const uint32_t my_mod = lo_mod + static_cast<uint32_t>(slot_c);
+      const bool col_ok = slot_c < SLOTS && my_mod < kModalities;
+      uint32_t ba[4], bb[4];
+      int got = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        uint32_t keep_a = 0, keep_b = 0;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int i = 2 * r + u;
+          const uint32_t ta = (mda[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+          const uint32_t tb2 = (mdb[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+          const bool va = group_pos(kg, i) < ra, vb = group_pos(kg, i) < rb;
+          if (va && ta >= lo_mod && ta < lo_mod + SLOTS && ta < kModalities) got |= 1 << ta;
+          if (vb && tb2 >= lo_mod && tb2 < lo_mod + SLOTS && tb2 < kModalities) got |= 1 << tb2;
+          keep_a |= (col_ok && ta == my_mod) ? (0xFFFFu << (16 * u)) : 0u;
+          keep_b |= (col_ok && tb2 == my_mod) ? (0xFFFFu << (16 * u)) : 0u;
+        }
+        ba[r] = wa[r] & keep_a;
+        bb[r] = wb[r] & keep_b;
+      }
+      if (__any(got != 0)) {
+        accumulate(k, ba, bb);
+        ws.mask |= wave_or_bits(got);
+      }
+    }
+  }
+}
+
+// Softmax and value sums of one group with rem valid positions (1..32): as
+// sw_back2 for a single group.
+template <int D, int SLOTS, bool ASYM>
+__device__ __forceinline__ void sw_back1(const ConsumerLoad<D>& ca, const SwFront<D>& fa, float bias_a, int rem_a,
+                                         int kg, int col, const uint2* tab, uint32_t lane_off,
+                                         WaveState<D, SLOTS, ASYM>& ws) {
+  constexpr int CT = D / 16;
+  constexpr int GP = Slots<SLOTS>::GP;
+  constexpr int NSETS = Slots<SLOTS>::NSETS;
+  float s[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s[i] = fa.sc[i >> 2][i & 3] + dpp_f<0x128>(fa.sc[i >> 2][i & 3]);
+  if (rem_a < kGroupTokens) {
+    int ra = rem_a;
+    asm volatile("" : "+s"(ra));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s[i] = group_pos(kg, i) < ra ? s[i] : -__builtin_inff();
+  }
+  const uint32_t na[4] = {ca.nrm0.x, ca.nrm0.y, ca.nrm1.x, ca.nrm1.y};
+  float pe[8];
+  uint32_t wa[4];
+  auto weights = [&](float m_ref) {
+    const float oa = m_ref - bias_a;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pe[i] = __builtin_amdgcn_exp2f(s[i] - oa);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) wa[r] = to_value_column<SLOTS>(weight_pair(pe[2 * r], pe[2 * r + 1], na[r]));
+  };
+  weights(ws.m_run);
+  float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+  mx = rows_max(mx) + bias_a;
+  if (__any(mx > ws.m_run)) {
+    const float m_new = fmaxf(ws.m_run, mx + kLazyMax);
+    const float alpha = exp2f(ws.m_run - m_new);   // 0 on the first group
+    ws.l_run *= alpha;
+    const float alpha_v = __uint_as_float(to_value_column<SLOTS>(__float_as_uint(alpha)));
+#pragma unroll
+    for (int k = 0; k < NSETS; ++k) {
+      if constexpr (ASYM) ws.accs[k] *= alpha_v;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) ws.acc[k][ct] *= alpha_v;
+    }
+    ws.m_run = m_new;
+    // arguments are now <= 0 (or -inf): the raw base-2 exponential flushes only results below 2^-126
+    weights(ws.m_run);
+  }
+  ws.l_run += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
+  const int slot_c = col / GP;
+  auto accumulate = [&](int k, const uint32_t (&ba)[4]) {
+    const half8 bwa = __builtin_bit_cast(half8, uint4{ba[0], ba[1], ba[2], ba[3]});
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const int j0 = 2 * ct;
+      const half8 va = as_half8(lookup(tab, ca.vc[j0 >> 2], byte_sel(j0 & 3), lane_off),
+                                lookup(tab, ca.vc[(j0 + 1) >> 2], byte_sel((j0 + 1) & 3), lane_off));
+      ws.acc[k][ct] = mfma(va, bwa, ws.acc[k][ct]);
+    }
+    if constexpr (ASYM) {
+      const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
+      ws.accs[k] = mfma(ones, bwa, ws.accs[k]);
+    }
+  };
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(ca.md0 & 0xFFu);
+  const uint32_t mm = m0 * 0x01010101u;
+  const bool uniform = rem_a == kGroupTokens && m0 < kModalities && __all(ca.md0 == mm && ca.md1 == mm);
+  if (uniform) {
+    const int k0 = static_cast<int>(m0) / SLOTS;
+    const bool take = slot_c == static_cast<int>(m0) - k0 * SLOTS;
+    uint32_t ba[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ba[r] = take ? wa[r] : 0u;
+#pragma unroll
+    for (int k = 0; k < NSETS; ++k)
+      if (k == k0) accumulate(k, ba);
+    ws.mask |= 1 << m0;
+  } else {
+    int ra = rem_a;
+    uint32_t mda[2] = {ca.md0, ca.md1};
+    asm volatile("" : "+s"(ra), "+v"(mda[0]), "+v"(mda[1]));
+#pragma unroll
+    for (int k = 0; k < NSETS; ++k) {
+      const uint32_t lo_mod = static_cast<uint32_t>(k * SLOTS);
+      const uint32_t my_mod = lo_mod + static_cast<uint32_t>(slot_c);
+      const bool col_ok = slot_c < SLOTS && my_mod < kModalities;
+      uint32_t ba[4];
+      int got = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        uint32_t keep_a = 0;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int i = 2 * r + u;
+          const uint32_t ta = (mda[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+          if (group_pos(kg, i) < ra && ta >= lo_mod && ta < lo_mod + SLOTS && ta < kModalities) got |= 1 << ta;
+          keep_a |= (col_ok && ta == my_mod) ? (0xFFFFu << (16 * u)) : 0u;
+        }
+        ba[r] = wa[r] & keep_a;
+      }
+      if (__any(got != 0)) {
+        accumulate(k, ba);
+        ws.mask |= wave_or_bits(got);
+      }
+    }
+  }
+}
+
+template <int D, int SLOTS, bool ASYM>
+__global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(DecodeArgs a) {
+  constexpr int KT = D / 32;
+  constexpr int CT = D / 16;
+  constexpr int GP = Slots<SLOTS>::GP;
+  constexpr int NSETS = Slots<SLOTS>::NSETS;
+  constexpr int PS = kPartialHeader + kModalities * D;
+  constexpr int NW = kSwWaves;
+  constexpr int NT = NW * 64;
+  constexpr int NPOS = NSETS * CT * 64;
+  constexpr int CB = SwShape<D>::CB;
+  constexpr int HPL = SwShape<D>::HPL;
+  union Smem {
+    struct {
+      uint2 tab[256 * kTabCopies];          // 64 KB byte table
+      SwSlot<D> slots[NW][2];               // q~ of the wavefront's current pair of groups
+      uint16_t stage[NW][2][2 * D];         // LO / HI rows of the pair being prepared
+    } s;
+    float4 red[NW][NPOS];                   // the wavefronts' rescaled accumulators
+  };
+  __shared__ Smem sm;
+  __shared__ float s_m[NW][kMaxGroupHeads];
+  __shared__ float s_l[NW][kMaxGroupHeads];
+  __shared__ float s_s[NW][kModalities][kMaxGroupHeads];
+  __shared__ int s_mask;
+  __shared__ int s_cmask[NW];
+  __shared__ int s_pt[kPageRun];
+  __shared__ float4 s_qs[2 * HPL * 64];   // producer lanes' q (scaled), [2u + half][lane]
+  __shared__ uint4 s_bq[KT * 64];         // bias operand of every lane, [kt][lane]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = lane >> 4, col = lane & 15;
+  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int G = a.group;
+  const int L = a.seq_len[b];
+  const int tb = split * a.split_tokens;
+  const int te = (split == a.splits - 1) ? L : min(tb + a.split_tokens, L);
+  const int ng = te > tb ? (te - tb + kGroupTokens - 1) / kGroupTokens : 0;   // groups of the partition
+  // Each wavefront takes a contiguous run of `steps` groups, starting at gw0,
+  // two at a time.
+  const int steps = (ng + NW - 1) / NW;
+  const int gw0 = wave * steps;
+  const int ps = a.page_shift;                     // page_tokens is a power of two here
+  const int pmask = a.page_tokens - 1;
+  const int page0 = tb >> ps;
+  const int npg = ng > 0 ? ((te - 1) >> ps) - page0 + 1 : 0;
+  int pt_entry = -1;
+  if (tid < npg) pt_entry = a.page_table[static_cast<size_t>(b) * a.max_pages + page0 + tid];
+  const SwRsrc rs = sw_rsrc(a);
+  const int hoff = h * (a.page_tokens / kGroupTokens);
+  static_assert(kPageRun <= NT, "one page-run entry per thread");
+
+  // Query constants: the producer lanes' q on channels 8cb..8cb+7 of their
+  // heads, and the bias operand (q's fp16 hi part in columns 0..7, lo part
+  // in columns 8..15, channels 32kt + 8kg + i).  Both carry scale * log2(e) / 2.
+  const float qsc = a.scale_log2e * 0.5f;
+  if (wave == 0) {
+    const int cb = lane % CB, hs = lane / CB;
+#pragma unroll
+    for (int u = 0; u < HPL; ++u) {
+      const int qh = h * G + min(hs * HPL + u, G - 1);
+      const float4* qp = reinterpret_cast<const float4*>(a.q_rot + (static_cast<size_t>(b) * a.hq + qh) * D + 8 * cb);
+      const float4 q0 = qp[0], q1 = qp[1];
+      s_qs[(2 * u) * 64 + lane] = float4{q0.x * qsc, q0.y * qsc, q0.z * qsc, q0.w * qsc};
+      s_qs[(2 * u + 1) * 64 + lane] = float4{q1.x * qsc, q1.y * qsc, q1.z * qsc, q1.w * qsc};
+    }
+  }
+  if (wave == 1) {
+    const int qh = h * G + min(col & 7, G - 1);
+    const float4* qp = reinterpret_cast<const float4*>(a.q_rot + (static_cast<size_t>(b) * a.hq + qh) * D);
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      const float4 q0 = qp[(32 * kt + 8 * kg) / 4], q1 = qp[(32 * kt + 8 * kg) / 4 + 1];
+      const float qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+      half8 bq;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float v = qv[i] * qsc;
+        const _Float16 hi = static_cast<_Float16>(v);
+        bq[i] = col < 8 ? hi : static_cast<_Float16>(v - static_cast<float>(hi));
+      }
+      s_bq[kt * 64 + lane] = __builtin_bit_cast(uint4, bq);
+    }
+  }
+
+  // Byte table (two copies of an entry per 16-byte store).
+  for (int i = tid; i < 256 * kTabCopies / 2; i += NT) {
+    const uint2 v = tab_entry(static_cast<uint32_t>(i) / (kTabCopies / 2), a.level_f16[0], a.level_f16[1]);
+    reinterpret_cast<uint4*>(sm.s.tab)[i] = uint4{v.x, v.y, v.x, v.y};
+  }
+  if (tid == 0) s_mask = 0;
+  const uint32_t lane_off = static_cast<uint32_t>(lane & (kTabCopies - 1)) << 3;
+  WaveState<D, SLOTS, ASYM> ws;
+  ws.m_run = -__builtin_inff();
+  ws.l_run = 0.f;
+  ws.mask = 0;
+#pragma unroll
+  for (int k = 0; k < NSETS; ++k)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) ws.acc[k][ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < (ASYM ? NSETS : 1); ++k) ws.accs[k] = floatx4{0.f, 0.f, 0.f, 0.f};
+  uint16_t* stage_a = &sm.s.stage[wave][0][0];
+  uint16_t* stage_b = &sm.s.stage[wave][1][0];
+  SwSlot<D>* slot_a = &sm.s.slots[wave][0];
+  SwSlot<D>* slot_b = &sm.s.slots[wave][1];
+  if (tid < kPageRun) s_pt[tid] = pt_entry;
+  __syncthreads();   // the byte table and the page run are complete
+  const uint2* tab = sm.s.tab;
+
+  // Group j of the wavefront's run: block and modality offsets (block 0 for
+  // an invalid group, see sw_load); returns whether the group is valid.
+  auto locate = [&](int j, int& blk, int& moff) {
+    const int gi = gw0 + j;
+    const int t0 = tb + gi * kGroupTokens;
+    const int phys = __builtin_amdgcn_readfirstlane(s_pt[min((t0 >> ps) - page0, kPageRun - 1)]);
+    const bool ok = j < steps && gi < ng && phys >= 0 && phys < a.num_pages;
+    const int tin = t0 & pmask;
+    blk = ok ? phys * a.blocks_per_page + hoff + (tin >> 5) : 0;
+    moff = ok ? phys * a.page_tokens + tin : 0;
+    return ok;
+  };
+  auto load_stats = [&](int j, uint32_t (&st)[D / 64]) {
+    int blk, moff;
+    locate(j, blk, moff);
+    if constexpr (D == 128) {
+      const uint2 s2 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs.st, lane * 8, blk * (4 * D), 0));
+      st[0] = s2.x;
+      st[1] = s2.y;
+    } else {
+      st[0] = __builtin_amdgcn_raw_buffer_load_b32(rs.st, lane * 4, blk * (4 * D), 0);
+    }
+  };
+  auto load_codes = [&](int j, ConsumerLoad<D>& c) {
+    int blk, moff;
+    const bool ok = locate(j, blk, moff);
+    if constexpr (D == 128) {
+      const uint4 k4 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs.k, lane * 16, blk * (8 * D), 0));
+      const uint4 v4 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs.v, lane * 16, blk * (8 * D), 0));
+      c.kc[0] = k4.x; c.kc[1] = k4.y; c.kc[2] = k4.z; c.kc[3] = k4.w;
+      c.vc[0] = v4.x; c.vc[1] = v4.y; c.vc[2] = v4.z; c.vc[3] = v4.w;
+    } else {
+      const uint2 k2 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs.k, lane * 8, blk * (8 * D), 0));
+      const uint2 v2 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs.v, lane * 8, blk * (8 * D), 0));
+      c.kc[0] = k2.x; c.kc[1] = k2.y;
+      c.vc[0] = v2.x; c.vc[1] = v2.y;
+    }
+    c.nrm0 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs.nrm, 8 * kg, blk * 64, 0));
+    c.nrm1 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs.nrm, 32 + 8 * kg, blk * 64, 0));
+    c.md0 = __builtin_amdgcn_raw_buffer_load_b32(rs.md, 4 * kg, moff, 0);
+    c.md1 = __builtin_amdgcn_raw_buffer_load_b32(rs.md, 16 + 4 * kg, moff, 0);
+    return ok;
+  };
+
+  // The producer lanes' q, read from LDS.
+  auto read_qs = [&](float (&q)[HPL][8]) {
+#pragma unroll
+    for (int u = 0; u < HPL; ++u) {
+      const float4 q0 = s_qs[(2 * u) * 64 + lane], q1 = s_qs[(2 * u + 1) * 64 + lane];
+      q[u][0] = q0.x; q[u][1] = q0.y; q[u][2] = q0.z; q[u][3] = q0.w;
+      q[u][4] = q1.x; q[u][5] = q1.y; q[u][6] = q1.z; q[u][7] = q1.w;
+    }
+  };
+  // Rings with fixed registers (group j uses ring j & 1): a group's
+  // statistics are fetched two groups ahead, its codes one group ahead, and
+  // its operands (q~, bias) are prepared during the previous group.
+  ConsumerLoad<D> cr[2];
+  bool okr[2];
+  uint32_t sr[2][D / 64];
+  load_stats(0, sr[0]);
+  load_stats(1, sr[1]);
+  okr[0] = load_codes(0, cr[0]);
+  float qs[HPL][8];
+  float bias = 0.f;
+  if (steps > 0) {
+    read_qs(qs);
+    bias = sw_produce<D>(sr[0], stage_a, slot_a, qs, s_bq, lane, kg);
+  }
+  auto step = [&](int j, auto ring) {
+    constexpr int r = decltype(ring)::value;
+    constexpr int r2 = r ^ 1;
+    SwSlot<D>* slot_cur = r ? slot_b : slot_a;
+    SwSlot<D>* slot_nxt = r ? slot_a : slot_b;
+    uint16_t* stage_nxt = r ? stage_a : stage_b;
+    okr[r2] = load_codes(j + 1, cr[r2]);
+    SwFront<D> f;
+    sw_front<D>(cr[r], slot_cur, kg, col, tab, lane_off, f);
+    float bias_next = 0.f;
+    if (j + 1 < steps) bias_next = sw_produce<D>(sr[r2], stage_nxt, slot_nxt, qs, s_bq, lane, kg);
+    load_stats(j + 2, sr[r]);
+    const int t0 = tb + (gw0 + j) * kGroupTokens;
+    if (okr[r])
+      sw_back1<D, SLOTS, ASYM>(cr[r], f, bias, min(te - t0, kGroupTokens), kg, col, tab, lane_off, ws);
+    bias = bias_next;
+  };
+  for (int j = 0; j < steps; j += 2) {
+    step(j, std::integral_constant<int, 0>{});
+    if (j + 1 < steps) step(j + 1, std::integral_constant<int, 1>{});
+  }
+
+  // ---- merge the wavefronts of the workgroup
+  const int c = wave;
+  const int slot_c = col / GP, hp = col % GP;
+  const float l_col = rows_sum(ws.l_run);
+  if (kg == 0) {
+    s_m[c][col] = ws.m_run;
+    s_l[c][col] = l_col;
+    if (slot_c < SLOTS) {
+#pragma unroll
+      for (int k = 0; k < NSETS; ++k) {
+        const int m = k * SLOTS + slot_c;
+        if (m < kModalities) s_s[c][m][hp] = ASYM ? ws.accs[ASYM ? k : 0][0] : 0.f;
+      }
+    }
+  }
+  const int wm = wave_or_bits(ws.mask);
+  if (lane == 0) {
+    s_cmask[c] = wm;
+    if (wm) atomicOr(&s_mask, wm);
+  }
+  __syncthreads();   // the table and slots are dead from here on
+  {
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][hp]);
+    const float mw = s_m[c][hp];
+    const float e = (mw == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+#pragma unroll
+    for (int k = 0; k < NSETS; ++k) {
+      if (!(wm & set_bits<SLOTS>(k))) continue;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const floatx4 v = ws.acc[k][ct] * e;
+        sm.red[c][(k * CT + ct) * 64 + lane] = float4{v[0], v[1], v[2], v[3]};
+      }
+    }
+  }
+  __syncthreads();
+  const int wmask = s_mask;
+  for (int pos = tid; pos < NPOS; pos += NT) {
+    const int ln = pos & 63, kct = pos >> 6;
+    const int k = kct / CT, ct = kct % CT;
+    const int c2 = ln & 15, kg2 = ln >> 4;
+    const int sl2 = c2 / GP, hp2 = c2 % GP;
+    const int m = k * SLOTS + sl2;
+    if (sl2 < SLOTS && m < kModalities && hp2 < G && (wmask & (1 << m))) {
+      float4 sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        if (!(s_cmask[w] & set_bits<SLOTS>(k))) continue;
+        const float4 v = sm.red[w][pos];
+        sum.x += v.x;
+        sum.y += v.y;
+        sum.z += v.z;
+        sum.w += v.w;
+      }
+      float* part = a.partials + ((static_cast<size_t>(b) * a.hq + h * G + hp2) * a.splits + split) * PS;
+      *reinterpret_cast<float4*>(part + kPartialHeader + m * D + 16 * ct + 4 * kg2) = sum;
+    }
+  }
+  if (tid < G * kPartialHeader) {
+    const int hh = tid / kPartialHeader, f = tid % kPartialHeader;
+    float* part = a.partials + ((static_cast<size_t>(b) * a.hq + h * G + hh) * a.splits + split) * PS;
+    float Mh = -__builtin_inff();
+    for (int w = 0; w < NW; ++w) Mh = fmaxf(Mh, s_m[w][hh]);
+    float v = 0.f;
+    if (f == 0) {
+      v = Mh;
+    } else if (f == 1 || (f >= 4 && f < 4 + kModalities)) {
+      for (int w = 0; w < NW; ++w) {
+        const float mww = s_m[w][hh];
+        if (mww != -__builtin_inff())
+          v += __builtin_amdgcn_exp2f(mww - Mh) * (f == 1 ? s_l[w][hh] : s_s[w][f - 4][hh]);
+      }
+    } else if (f == 2) {
+      v = __int_as_float(wmask);
+    }
+    part[f] = v;
+  }
+}
+
 // Merge: workgroup (session, query head, row block) rescales every
 // partition's partial to the global max, sums them per modality, and applies
 // the rows [rb D/RB, (rb+1) D/RB) of the inverse value rotations,
@@ -1483,10 +2313,20 @@ void launch_partition_pc(int batch, const DecodeArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((decode_partition_pc_kernel<D, SLOTS, false>), grid, dim3(kPcWaves * 64), 0, s, a);
 }
 
+template <int D, int SLOTS>
+void launch_partition_sw(int batch, const DecodeArgs& a, hipStream_t s) {
+  const dim3 grid(a.splits, a.hkv, batch);
+  if (a.cmid != 0.f)
+    hipLaunchKernelGGL((decode_partition_sw_kernel<D, SLOTS, true>), grid, dim3(kSwWaves * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_partition_sw_kernel<D, SLOTS, false>), grid, dim3(kSwWaves * 64), 0, s, a);
+}
+
 template <int D>
 hipError_t launch_decode_t(int batch, const DecodeArgs& a, hipStream_t s) {
-  if (a.group <= 5) launch_partition_pc<D, 3>(batch, a, s);
-  else if (a.group <= 8) launch_partition_pc<D, 2>(batch, a, s);
+  if (!a.offsets31 || a.page_shift < 0) launch_partition<D, 1, kDecodeWaves / 2>(batch, a, s);
+  else if (a.group <= 5) launch_partition_sw<D, 3>(batch, a, s);
+  else if (a.group <= 8) launch_partition_sw<D, 2>(batch, a, s);
   else launch_partition<D, 1, kDecodeWaves / 2>(batch, a, s);
   const int keys = a.hkv * batch;
   const int per_key = a.group * MergeShape<D>::RB;

@@ -76,6 +76,8 @@ struct DecodeArgs {
   int32_t splits;         // partitions per (session, KV head)
   int32_t split_tokens;   // positions per partition (multiple of 32 * kDecodeWaves)
   int32_t page_shift;     // log2(page_tokens) when it is a power of two, else -1
+  int32_t blocks_per_page; // hkv * page_tokens / 32: 32-position blocks of one physical page
+  int32_t offsets31;       // every cache array is below 2^31 bytes
   float scale_log2e;      // softmax scale * log2(e)
   float value_scale;      // 1 / sqrt(d)
   float cmid, chalf;      // codebook centre (c0 + c3) / 2 and half range (c3 - c0) / 2
