@@ -680,29 +680,7 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 // ---------------------------------------------------------------------------
-// Producer / consumer partition kernel (G <= 8).
-//
-// kConsumers consumer wavefronts each take one 32-position group per step:
-// codes -> operands, scores, online softmax, value sums.  kProducers =
-// kConsumers / 2 producer wavefronts prepare, one step ahead, everything that
-// depends on the group statistics and the query: q~ = q (HI - LO) / 2 as an
-// fp16 hi + lo pair in the consumers' operand layout, and the group bias
-// sum_c q_c (LO_c + HI_c) / 2.  A producer serves two consumers at once: its
-// 16 matrix-core columns hold the 8 query heads of each of the two groups.
-// One workgroup barrier per step; every wavefront runs the same number of
-// steps.
-constexpr int kConsumers = 8;
-constexpr int kProducers = kConsumers / 2;
-constexpr int kPcWaves = kConsumers + kProducers;
-
-template <int D>
-struct __align__(16) QtSlot {
-  static constexpr int ROW = D + 8;     // fp16 per row (padding spreads the rows over the LDS banks)
-  _Float16 qt[2][8][ROW];               // [hi / lo][query head of the group][channel]
-  float bias[8];
-};
-
-// Loads of one group for a consumer: codes, norms and modality bytes.
+// Operand registers of one group for the streaming kernel below.
 template <int D>
 struct ConsumerLoad {
   uint32_t kc[D / 32];
@@ -710,11 +688,6 @@ struct ConsumerLoad {
   uint2 nrm0, nrm1;
   uint32_t md0, md1;
 };
-
-template <int D>
-__device__ __forceinline__ size_t block_index(const DecodeArgs& a, int h, int t0, int phys) {
-  return (static_cast<size_t>(phys) * a.hkv + h) * (a.page_tokens / kGroupTokens) + in_page(a, t0) / kGroupTokens;
-}
 
 // Buffer resource over `bytes` bytes at `base` (raw, untyped).  A load whose
 // offset is outside [0, bytes) returns zero without a memory access, so a
@@ -724,560 +697,32 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }
 
-// Loads of one group for a consumer; a group outside [0, te) or on an
-// unmapped page reads nothing (zeros) and is flagged invalid.
-template <int D>
-__device__ __forceinline__ void consumer_load(const DecodeArgs& a, int h, int t0, int te, int lane, int kg, int phys0,
-                                              ConsumerLoad<D>& g, bool& ok) {
-  ok = t0 < te && page_of(a, t0) < a.max_pages && phys0 >= 0 && phys0 < a.num_pages;
-  const int phys = ok ? phys0 : 0;
-  const int tin = ok ? in_page(a, t0) : 0;
-  const size_t blk = block_index<D>(a, h, ok ? t0 : 0, phys);
-  const int n_codes = ok ? 8 * D : 0;
-  const auto rk = span_rsrc(a.k_codes + blk * 8 * D, n_codes);
-  const auto rv = span_rsrc(a.v_codes + blk * 8 * D, n_codes);
-  const auto rn = span_rsrc(a.v_norms + (static_cast<size_t>(phys) * a.hkv + h) * a.page_tokens + tin,
-                            ok ? 2 * kGroupTokens : 0);
-  const auto rm = span_rsrc(a.modality + static_cast<size_t>(phys) * a.page_tokens + tin, ok ? kGroupTokens : 0);
-  if constexpr (D == 128) {
-    const uint4 k4 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, lane * 16, 0, 0));
-    const uint4 v4 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, lane * 16, 0, 0));
-    g.kc[0] = k4.x; g.kc[1] = k4.y; g.kc[2] = k4.z; g.kc[3] = k4.w;
-    g.vc[0] = v4.x; g.vc[1] = v4.y; g.vc[2] = v4.z; g.vc[3] = v4.w;
-  } else {
-    const uint2 k2 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rk, lane * 8, 0, 0));
-    const uint2 v2 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rv, lane * 8, 0, 0));
-    g.kc[0] = k2.x; g.kc[1] = k2.y;
-    g.vc[0] = v2.x; g.vc[1] = v2.y;
-  }
-  g.nrm0 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rn, 8 * kg, 0, 0));
-  g.nrm1 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rn, 32 + 8 * kg, 0, 0));
-  g.md0 = __builtin_amdgcn_raw_buffer_load_b32(rm, 4 * kg, 0, 0);
-  g.md1 = __builtin_amdgcn_raw_buffer_load_b32(rm, 16 + 4 * kg, 0, 0);
-}
-
-// This lane's share (D / 64 words) of a group's LO / HI rows.
-template <int D>
-__device__ __forceinline__ void stats_load(const DecodeArgs& a, int h, int t0, int te, int lane, int phys0,
-                                           uint32_t (&st)[D / 64]) {
-  const bool ok = t0 < te && page_of(a, t0) < a.max_pages && phys0 >= 0 && phys0 < a.num_pages;
-  const size_t blk = block_index<D>(a, h, ok ? t0 : 0, ok ? phys0 : 0);
-  const auto rs = span_rsrc(a.k_stats + blk * 2 * D, ok ? 2 * D * 2 : 0);
-  if constexpr (D == 128) {
-    const uint2 s2 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, lane * 8, 0, 0));
-    st[0] = s2.x; st[1] = s2.y;
-  } else {
-    st[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, lane * 4, 0, 0);
-  }
-}
-
-// Producer: q~ hi / lo and the bias of two groups (A for the lanes of columns
-// 0..7, B for columns 8..15) into the consumers' slots.  `stage` holds both
-// groups' LO / HI rows (fp16, for the bias products), `dstage` their channel
-// widths HI - LO (fp32, exact), each computed once per channel.
-// First part: stage the statistics (after which their registers are free).
-template <int D>
-__device__ __forceinline__ void produce_stage(const uint32_t (&stA)[D / 64], const uint32_t (&stB)[D / 64],
-                                              uint16_t* stage, float* dstage, int lane) {
-  constexpr int NW = D / 64;                      // statistics words per lane
-  // A lane's words are LO (lanes 0..31) or HI (lanes 32..63) fp16 pairs of
-  // channels (D / 32) (lane & 31) + [0, D / 32).
-  if constexpr (D == 128) {
-    reinterpret_cast<uint2*>(stage)[lane] = uint2{stA[0], stA[1]};
-    reinterpret_cast<uint2*>(stage + 2 * D)[lane] = uint2{stB[0], stB[1]};
-  } else {
-    reinterpret_cast<uint32_t*>(stage)[lane] = stA[0];
-    reinterpret_cast<uint32_t*>(stage + 2 * D)[lane] = stB[0];
-  }
-  // After the swap lanes 0..31 hold group A's LO (first) and HI (second)
-  // words, lanes 32..63 group B's.
-  float dv[2 * NW];
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const auto sw = __builtin_amdgcn_permlane32_swap(stA[w], stB[w], false, false);
-    dv[2 * w] = f16_diff_lo(sw[1], sw[0]);
-    dv[2 * w + 1] = f16_diff_hi(sw[1], sw[0]);
-  }
-  float* drow = dstage + (lane >> 5) * D + (D / 32) * (lane & 31);
-  if constexpr (D == 128) {
-    *reinterpret_cast<float4*>(drow) = float4{dv[0], dv[1], dv[2], dv[3]};
-  } else {
-    *reinterpret_cast<float2*>(drow) = float2{dv[0], dv[1]};
-  }
-}
-
-// Second part: operands and bias from the staging.
-template <int D>
-__device__ __forceinline__ void produce_compute(const uint16_t* stage, const float* dstage, QtSlot<D>* slotA,
-                                                QtSlot<D>* slotB, int kg, int col, const float (&hq)[D / 32][8],
-                                                const half8 (&bq)[D / 32]) {
-  constexpr int KT = D / 32;
-  wave_sync();
-  const int grp = col >> 3;                       // 0: group A, 1: group B
-  const uint16_t* st = stage + grp * 2 * D;
-  const float* dg = dstage + grp * D;
-  QtSlot<D>* slot = grp ? slotB : slotA;
-  const int head = col & 7;
-  uint4 lo4[KT], hi4[KT];
-  float4 d4[KT][2];
-#pragma unroll
-  for (int kt = 0; kt < KT; ++kt) {
-    lo4[kt] = *reinterpret_cast<const uint4*>(st + 32 * kt + 8 * kg);
-    hi4[kt] = *reinterpret_cast<const uint4*>(st + D + 32 * kt + 8 * kg);
-    d4[kt][0] = *reinterpret_cast<const float4*>(dg + 32 * kt + 8 * kg);
-    d4[kt][1] = *reinterpret_cast<const float4*>(dg + 32 * kt + 8 * kg + 4);
-  }
-  floatx4 bias_lo = {0.f, 0.f, 0.f, 0.f}, bias_hi = {0.f, 0.f, 0.f, 0.f};   // two independent chains
-#pragma unroll
-  for (int kt = 0; kt < KT; ++kt) {
-    // Rows 0..7 of the product carry group A's statistics, rows 8..15 group
-    // B's; columns are q's fp16 hi (0..7) and lo (8..15) parts per head.
-    bias_lo = mfma(__builtin_bit_cast(half8, lo4[kt]), bq[kt], bias_lo);
-    bias_hi = mfma(__builtin_bit_cast(half8, hi4[kt]), bq[kt], bias_hi);
-    const float d[8] = {d4[kt][0].x, d4[kt][0].y, d4[kt][0].z, d4[kt][0].w,
-                        d4[kt][1].x, d4[kt][1].y, d4[kt][1].z, d4[kt][1].w};
-    uint32_t th[4], tl[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint2 sp = split_product(hq[kt][2 * p], d[2 * p], hq[kt][2 * p + 1], d[2 * p + 1]);
-      th[p] = sp.x;
-      tl[p] = sp.y;
-    }
-    *reinterpret_cast<uint4*>(&slot->qt[0][head][32 * kt + 8 * kg]) = uint4{th[0], th[1], th[2], th[3]};
-    *reinterpret_cast<uint4*>(&slot->qt[1][head][32 * kt + 8 * kg]) = uint4{tl[0], tl[1], tl[2], tl[3]};
-  }
-  // Lane (h, kg): rows 4 kg..4 kg + 3 (group kg < 2 ? A : B), column h's part.
-  float bias = bias_lo[0] + bias_hi[0];
-  bias += __uint_as_float(static_cast<uint32_t>(
-      __builtin_amdgcn_update_dpp(0, static_cast<int>(__float_as_uint(bias)), 0x128, 0xF, 0xF, false)));
-  if (col < 8 && (kg & 1) == 0) (kg ? slotB : slotA)->bias[col] = bias;
-}
-
-// Consumer: one group, given its q~ slot.  `partial`: the group extends past
-// te (the session's last, partially filled group).
-template <int D, int SLOTS, bool ASYM>
-__device__ __forceinline__ void consume(const ConsumerLoad<D>& cur, const QtSlot<D>* slot, int t0, int te,
-                                        bool partial, int kg, int col, const uint2* tab, uint32_t lane_off,
-                                        WaveState<D, SLOTS, ASYM>& ws) {
-  constexpr int KT = D / 32;
-  constexpr int CT = D / 16;
-  constexpr int GP = Slots<SLOTS>::GP;
-  constexpr int NSETS = Slots<SLOTS>::NSETS;
-  const int head = col & 7;
-  const float bias = slot->bias[head];
-  // Columns 0..7 take q~'s fp16 hi parts of the heads, columns 8..15 the lo
-  // parts; the two halves of each score are joined across the row below.
-  floatx4 sc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-  for (int kt = 0; kt < KT; ++kt) {
-    const half8 qt = *reinterpret_cast<const half8*>(&slot->qt[col >> 3][head][32 * kt + 8 * kg]);
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const int j0 = mt * (D / 16) + kt * 2;   // code bytes j0, j0 + 1 of this (mt, kt)
-      const uint2 x0 = lookup(tab, cur.kc[j0 >> 2], byte_sel(j0 & 3), lane_off);
-      const uint2 x1 = lookup(tab, cur.kc[(j0 + 1) >> 2], byte_sel((j0 + 1) & 3), lane_off);
-      sc[mt] = mfma(as_half8(x0, x1), qt, sc[mt]);
-    }
-  }
-  // score = hi part + lo part: add the partner column (col ^ 8, DPP row_ror:8)
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sc[mt][r] += dpp_f<0x128>(sc[mt][r]);
-  uint32_t vmask[4] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
-  if (partial) {
-    // positions at or past te: score -inf (weight 0), weight bits cleared.
-    // (The empty asm keeps these compares out of the full-group path.)
-    int rem = te - t0;
-    asm volatile("" : "+s"(rem));
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const bool v = group_pos(kg, i) < rem;
-      sc[i >> 2][i & 3] = v ? sc[i >> 2][i & 3] : -__builtin_inff();
-      if (!v) vmask[i >> 1] &= (i & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-    }
-  }
-  float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                   fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-  mx = rows_max(mx) + bias;
-  // Lazy reference max (see kLazyMax): weights 2^(s - m_run) stay <= 1.
-  if (__any(mx > ws.m_run)) {
-    const float m_new = fmaxf(ws.m_run, mx + kLazyMax);
-    const float alpha = exp2f(ws.m_run - m_new);   // 0 on the first group
-    ws.l_run *= alpha;
-    const float alpha_v = __uint_as_float(to_value_column<SLOTS>(__float_as_uint(alpha)));
-#pragma unroll
-    for (int k = 0; k < NSETS; ++k) {
-      if constexpr (ASYM) ws.accs[k] *= alpha_v;
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) ws.acc[k][ct] *= alpha_v;
-    }
-    ws.m_run = m_new;
-  }
-  const float off = ws.m_run - bias;
-  const uint32_t n4[4] = {cur.nrm0.x, cur.nrm0.y, cur.nrm1.x, cur.nrm1.y};
-  uint32_t wp[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int i0 = 2 * r, i1 = 2 * r + 1;
-    // arguments are <= 0 (or -inf): the raw base-2 exponential flushes only results below 2^-126
-    const float p0 = __builtin_amdgcn_exp2f(sc[i0 >> 2][i0 & 3] - off);
-    const float p1 = __builtin_amdgcn_exp2f(sc[i1 >> 2][i1 & 3] - off);
-    ws.l_run += p0 + p1;
-    wp[r] = to_value_column<SLOTS>(weight_pair(p0, p1, n4[r]) & vmask[r]);
-  }
-  half8 av[CT];
-#pragma unroll
-  for (int ct = 0; ct < CT; ++ct) {
-    const int j0 = 2 * ct;
-    const uint2 x0 = lookup(tab, cur.vc[j0 >> 2], byte_sel(j0 & 3), lane_off);
-    const uint2 x1 = lookup(tab, cur.vc[(j0 + 1) >> 2], byte_sel((j0 + 1) & 3), lane_off);
-    av[ct] = as_half8(x0, x1);
-  }
-  const int slot_c = col / GP;
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(cur.md0 & 0xFFu);
-  const bool uniform = !partial && __all(cur.md0 == m0 * 0x01010101u && cur.md1 == m0 * 0x01010101u);
-  const uint32_t md[2] = {cur.md0, cur.md1};
-#pragma unroll
-  for (int k = 0; k < NSETS; ++k) {
-    const uint32_t lo_mod = static_cast<uint32_t>(k * SLOTS);
-    const uint32_t my_mod = lo_mod + static_cast<uint32_t>(slot_c);
-    const bool col_ok = slot_c < SLOTS && my_mod < kModalities;
-    bool present;
-    uint32_t bm[4];
-    int got = 0;
-    if (uniform) {
-      present = m0 >= lo_mod && m0 < lo_mod + SLOTS && m0 < kModalities;
-      got = present ? (1 << m0) : 0;
-      const bool take = col_ok && my_mod == m0;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) bm[r] = take ? wp[r] : 0u;
-    } else {
-      int rem = partial ? te - t0 : kGroupTokens;
-      uint32_t mdo[2] = {md[0], md[1]};
-      asm volatile("" : "+s"(rem), "+v"(mdo[0]), "+v"(mdo[1]));   // keeps this path's work inside it
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        uint32_t keep = 0;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int i = 2 * r + u;
-          const uint32_t tm = (mdo[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-          const bool valid = group_pos(kg, i) < rem;
-          if (valid && tm >= lo_mod && tm < lo_mod + SLOTS && tm < kModalities) got |= 1 << tm;
-          keep |= (col_ok && tm == my_mod) ? (0xFFFFu << (16 * u)) : 0u;
-        }
-        bm[r] = wp[r] & keep;
-      }
-      present = __any(got != 0);
-    }
-    if (present) {
-      const half8 bw = __builtin_bit_cast(half8, uint4{bm[0], bm[1], bm[2], bm[3]});
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) ws.acc[k][ct] = mfma(av[ct], bw, ws.acc[k][ct]);
-      if constexpr (ASYM) {
-        const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
-        ws.accs[k] = mfma(ones, bw, ws.accs[k]);
-      }
-      ws.mask |= got;
-    }
-  }
-}
-
-template <int D, int SLOTS, bool ASYM>
-__global__ __launch_bounds__(kPcWaves * 64, 1) void decode_partition_pc_kernel(DecodeArgs a) {
-  constexpr int KT = D / 32;
-  constexpr int CT = D / 16;
-  constexpr int GP = Slots<SLOTS>::GP;
-  constexpr int NSETS = Slots<SLOTS>::NSETS;
-  constexpr int PS = kPartialHeader + kModalities * D;
-  constexpr int NT = kPcWaves * 64;
-  constexpr int NPOS = NSETS * CT * 64;   // float4 accumulator slots of one consumer
-  union Smem {
-    struct {
-      uint2 tab[256 * kTabCopies];              // 64 KB byte table
-      QtSlot<D> slots[kConsumers][2];           // q~ and bias per consumer, double-buffered by step
-      uint16_t stage[kProducers][2][2][D];      // producers' staging of two groups' LO / HI rows
-      float dstage[kProducers][2][D];           // and of their channel widths HI - LO
-    } s;
-    float4 red[kConsumers][NPOS];               // the consumers' rescaled accumulators
-  };
-  __shared__ Smem sm;
-  __shared__ float s_m[kConsumers][kMaxGroupHeads];
-  __shared__ float s_l[kConsumers][kMaxGroupHeads];
-  __shared__ float s_s[kConsumers][kModalities][kMaxGroupHeads];
-  __shared__ int s_mask;
-  __shared__ int s_cmask[kConsumers];         // modalities each consumer saw
-  __shared__ int s_pt[kPageRun];
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool producer = wave >= kConsumers;
-  const int c = wave;                              // consumer index (wave < kConsumers)
-  const int p = wave - kConsumers;                 // producer index (wave >= kConsumers)
-  const int kg = lane >> 4, col = lane & 15;
-  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int G = a.group;
-  const int L = a.seq_len[b];
-  const int tb = split * a.split_tokens;
-  const int te = (split == a.splits - 1) ? L : min(tb + a.split_tokens, L);
-  const int ng = te > tb ? (te - tb + kGroupTokens - 1) / kGroupTokens : 0;   // groups of the partition
-  const int steps = (ng + kConsumers - 1) / kConsumers;
-  const int page0 = page_of(a, tb);
-  const __attribute__((address_space(4))) int32_t* ptab =
-      (const __attribute__((address_space(4))) int32_t*)(a.page_table + static_cast<size_t>(b) * a.max_pages);
-  auto gpos = [&](int step, int cons) { return tb + (step * kConsumers + cons) * kGroupTokens; };
-
-  // Set-up, done by the consumers while the producers build step 0's
-  // operands: page run of the partition (one entry per consumer thread,
-  // loaded before the first groups so its wait leaves them in flight), byte
-  // table, modality mask.
-  static_assert(kPageRun == kConsumers * 64, "one page-run entry per consumer thread");
-  auto setup = [&](int pt_entry) {
-    constexpr int NC = kConsumers * 64;
-    s_pt[tid] = pt_entry;
-    // two copies of an entry per 16-byte store
-    for (int i = tid; i < 256 * kTabCopies / 2; i += NC) {
-      const uint2 v = tab_entry(static_cast<uint32_t>(i) / (kTabCopies / 2), a.level_f16[0], a.level_f16[1]);
-      reinterpret_cast<uint4*>(sm.s.tab)[i] = uint4{v.x, v.y, v.x, v.y};
-    }
-    if (tid == 0) s_mask = 0;
-  };
-
-  auto pt_at = [&](int t) { return s_pt[min(page_of(a, t) - page0, kPageRun - 1)]; };
-  auto pt_direct = [&](int t) { return ptab[min(page_of(a, t), a.max_pages - 1)]; };
-
-  // The two roles run separate loops over the same barriers, so neither holds
-  // the other's registers.  Step u uses slot u & 1, consumer buffer u & 1 and
-  // producer statistics u & 1.  Each loop pass covers two steps with fixed
-  // buffers and unconditional loads, which keeps the compiler's count of
-  // loads in flight exact; steps past the end compute nothing and read
-  // nothing (zero-span loads).  Barriers per role: 1 + 2 ceil(steps / 2).
-  if (producer) {
-    // ---- producer: step u's statistics in pst[u & 1] (two groups each)
-    uint32_t pst0[2][D / 64], pst1[2][D / 64];
-#pragma unroll
-    for (int gg = 0; gg < 2; ++gg) {
-      const int t0 = gpos(0, 2 * p + gg), t1 = gpos(1, 2 * p + gg);
-      stats_load<D>(a, h, t0, te, lane, pt_direct(t0), pst0[gg]);
-      stats_load<D>(a, h, t1, te, lane, pt_direct(t1), pst1[gg]);
-    }
-    float hq[KT][8];
-    half8 bq[KT];
-    const int qh = h * G + min(col & 7, G - 1);
-    const float4* qp = reinterpret_cast<const float4*>(a.q_rot + (static_cast<size_t>(b) * a.hq + qh) * D);
-    const float qs = a.scale_log2e * 0.5f;
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-      const float4 q0 = qp[(32 * kt + 8 * kg) / 4], q1 = qp[(32 * kt + 8 * kg) / 4 + 1];
-      const float qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float v = qv[i] * qs;
-        hq[kt][i] = v;
-        const _Float16 hi = static_cast<_Float16>(v);
-        bq[kt][i] = col < 8 ? hi : static_cast<_Float16>(v - static_cast<float>(hi));
-      }
-    }
-    uint16_t* stage = &sm.s.stage[p][0][0][0];
-    float* dstage = &sm.s.dstage[p][0][0];
-    // Per step: stage its statistics, fetch those of two steps later into the
-    // freed registers, then build the operands (the fetch overlaps the work).
-    // Step 0 is built before the set-up barrier (its page-table reads for
-    // step 2 come after the products, off their path).
-    produce_stage<D>(pst0[0], pst0[1], stage, dstage, lane);
-    if (steps > 0)
-      produce_compute<D>(stage, dstage, &sm.s.slots[2 * p][0], &sm.s.slots[2 * p + 1][0], kg, col, hq, bq);
-#pragma unroll
-    for (int gg = 0; gg < 2; ++gg) {
-      const int t = gpos(2, 2 * p + gg);
-      stats_load<D>(a, h, t, te, lane, pt_direct(t), pst0[gg]);
-    }
-    wave_sync();
-    __syncthreads();
-    for (int u = 0; u < steps; u += 2) {
-      // step u + 1 (odd) into slot 1; fetch step u + 3
-      produce_stage<D>(pst1[0], pst1[1], stage, dstage, lane);
-#pragma unroll
-      for (int gg = 0; gg < 2; ++gg) {
-        const int t = gpos(u + 3, 2 * p + gg);
-        stats_load<D>(a, h, t, te, lane, pt_at(t), pst1[gg]);
-      }
-      if (u + 1 < steps)
-        produce_compute<D>(stage, dstage, &sm.s.slots[2 * p][1], &sm.s.slots[2 * p + 1][1], kg, col, hq, bq);
-      wave_sync();   // the staging may be overwritten by the next step
-      __syncthreads();
-      // step u + 2 (even) into slot 0; fetch step u + 4
-      produce_stage<D>(pst0[0], pst0[1], stage, dstage, lane);
-#pragma unroll
-      for (int gg = 0; gg < 2; ++gg) {
-        const int t = gpos(u + 4, 2 * p + gg);
-        stats_load<D>(a, h, t, te, lane, pt_at(t), pst0[gg]);
-      }
-      if (u + 2 < steps)
-        produce_compute<D>(stage, dstage, &sm.s.slots[2 * p][0], &sm.s.slots[2 * p + 1][0], kg, col, hq, bq);
-      wave_sync();
-      __syncthreads();
-    }
-    __syncthreads();   // merge: consumers hand over their accumulators
-  } else {
-    // ---- consumer: step u's group in buf[u & 1]
-    const int pt_entry = page0 + tid < a.max_pages ? ptab[page0 + tid] : -1;
-    ConsumerLoad<D> buf0, buf1;
-    bool ok0, ok1;
-    {
-      const int t0 = gpos(0, c), t1 = gpos(1, c);
-      consumer_load<D>(a, h, t0, te, lane, kg, pt_direct(t0), buf0, ok0);
-      consumer_load<D>(a, h, t1, te, lane, kg, pt_direct(t1), buf1, ok1);
-    }
-    const uint32_t lane_off = static_cast<uint32_t>(lane & (kTabCopies - 1)) << 3;
-    WaveState<D, SLOTS, ASYM> ws;
-    ws.m_run = -__builtin_inff();
-    ws.l_run = 0.f;
-    ws.mask = 0;
-#pragma unroll
-    for (int k = 0; k < NSETS; ++k)
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) ws.acc[k][ct] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < (ASYM ? NSETS : 1); ++k) ws.accs[k] = floatx4{0.f, 0.f, 0.f, 0.f};
-    setup(pt_entry);
-    __syncthreads();
-    const uint2* tab = sm.s.tab;
-    for (int u = 0; u < steps; u += 2) {
-      // step u (even), then fetch step u + 2
-      if (ok0) {
-        const int t0 = gpos(u, c);
-        consume<D, SLOTS, ASYM>(buf0, &sm.s.slots[c][0], t0, te, t0 + kGroupTokens > te, kg, col, tab, lane_off, ws);
-      }
-      {
-        const int t = gpos(u + 2, c);
-        consumer_load<D>(a, h, t, te, lane, kg, pt_at(t), buf0, ok0);
-      }
-      __syncthreads();
-      // step u + 1 (odd), then fetch step u + 3
-      if (ok1) {
-        const int t0 = gpos(u + 1, c);
-        consume<D, SLOTS, ASYM>(buf1, &sm.s.slots[c][1], t0, te, t0 + kGroupTokens > te, kg, col, tab, lane_off, ws);
-      }
-      {
-        const int t = gpos(u + 3, c);
-        consumer_load<D>(a, h, t, te, lane, kg, pt_at(t), buf1, ok1);
-      }
-      __syncthreads();
-    }
-
-    // ---- merge the consumers of the workgroup
-    const int slot_c = col / GP, hp = col % GP;
-    const float l_col = rows_sum(ws.l_run);
-    if (kg == 0) {
-      s_m[c][col] = ws.m_run;
-      s_l[c][col] = l_col;
-      if (slot_c < SLOTS) {
-#pragma unroll
-        for (int k = 0; k < NSETS; ++k) {
-          const int m = k * SLOTS + slot_c;
-          if (m < kModalities) s_s[c][m][hp] = ASYM ? ws.accs[ASYM ? k : 0][0] : 0.f;
-        }
-      }
-    }
-    const int wm = wave_or_bits(ws.mask);
-    if (lane == 0) {
-      s_cmask[c] = wm;
-      if (wm) atomicOr(&s_mask, wm);
-    }
-    __syncthreads();   // the table and slots are dead from here on
-    float M = -__builtin_inff();
-#pragma unroll
-    for (int w = 0; w < kConsumers; ++w) M = fmaxf(M, s_m[w][hp]);
-    const float mw = s_m[c][hp];
-    // (arguments <= 0: the raw base-2 exponential only flushes results below 2^-126)
-    const float e = (mw == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-    // a set none of this wavefront's groups touched is zero: not written, not read
-#pragma unroll
-    for (int k = 0; k < NSETS; ++k) {
-      if (!(wm & set_bits<SLOTS>(k))) continue;
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        const floatx4 v = ws.acc[k][ct] * e;
-        sm.red[c][(k * CT + ct) * 64 + lane] = float4{v[0], v[1], v[2], v[3]};
-      }
-    }
-  }
-  __syncthreads();
-  const int wmask = s_mask;
-  for (int pos = tid; pos < NPOS; pos += NT) {
-    const int ln = pos & 63, kct = pos >> 6;
-    const int k = kct / CT, ct = kct % CT;
-    const int c2 = ln & 15, kg2 = ln >> 4;
-    const int sl2 = c2 / GP, hp2 = c2 % GP;
-    const int m = k * SLOTS + sl2;
-    if (sl2 < SLOTS && m < kModalities && hp2 < G && (wmask & (1 << m))) {
-      float4 sum = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int w = 0; w < kConsumers; ++w) {
-        if (!(s_cmask[w] & set_bits<SLOTS>(k))) continue;   // uniform over the wavefront's positions
-        const float4 v = sm.red[w][pos];
-        sum.x += v.x;
-        sum.y += v.y;
-        sum.z += v.z;
-        sum.w += v.w;
-      }
-      float* part = a.partials + ((static_cast<size_t>(b) * a.hq + h * G + hp2) * a.splits + split) * PS;
-      *reinterpret_cast<float4*>(part + kPartialHeader + m * D + 16 * ct + 4 * kg2) = sum;
-    }
-  }
-  if (tid < G * kPartialHeader) {
-    const int hh = tid / kPartialHeader, f = tid % kPartialHeader;
-    float* part = a.partials + ((static_cast<size_t>(b) * a.hq + h * G + hh) * a.splits + split) * PS;
-    float Mh = -__builtin_inff();
-    for (int w = 0; w < kConsumers; ++w) Mh = fmaxf(Mh, s_m[w][hh]);
-    float v = 0.f;
-    if (f == 0) {
-      v = Mh;
-    } else if (f == 1 || (f >= 4 && f < 4 + kModalities)) {
-      for (int w = 0; w < kConsumers; ++w) {
-        const float mww = s_m[w][hh];
-        if (mww != -__builtin_inff())
-          v += __builtin_amdgcn_exp2f(mww - Mh) * (f == 1 ? s_l[w][hh] : s_s[w][f - 4][hh]);
-      }
-    } else if (f == 2) {
-      v = __int_as_float(wmask);
-    }
-    part[f] = v;
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Streaming partition kernel (G <= 8).
 //
-// Every wavefront streams its own groups of the partition (g = wave,
-// wave + NW, ...) with kSwDepth groups of loads in flight and never waits for
-// another wavefront until the epilogue.  For each group it first builds the
-// statistics-dependent operands itself (one group ahead of the scores):
+// Every wavefront of the workgroup streams its own contiguous run of the
+// partition's 32-position groups and never waits for another wavefront until
+// the epilogue: a group's statistics are fetched two groups ahead and its
+// codes, norms and modality bytes one group ahead (buffer loads from
+// resources built once per kernel), and while a group's scores run the
+// wavefront prepares the next group's statistics-dependent operands itself:
 //   - the group bias sum_c q_c (LO_c + HI_c) / 2 on the matrix cores, with
 //     the staged LO / HI rows as the A operand (rows 4kg, 4kg+2: LO; rows
 //     4kg+1, 4kg+3: HI) and q's fp16 hi / lo parts as the columns, so every
 //     lane of column col ends up with the bias of head col & 7;
 //   - q~ = q (HI - LO) / 2 as fp16 hi + lo, computed channel-major (a lane
 //     takes 8 channels of 1 or 2 heads, so every product is formed once) and
-//     handed to the score operand layout through a wave-private LDS slot of
-//     16-byte cells.
-// The scores, online softmax and value sums are those of the consumer above.
+//     handed to the score operand layout through a wavefront-private LDS slot
+//     of 16-byte cells.
+// The scores, online softmax and value sums follow the partition kernel
+// above; the epilogue merges the wavefronts in LDS in a fixed order and
+// writes one partial per query head.
 constexpr int kSwWaves = 8;       // wavefronts per workgroup (the plan's unit is 32 * 8 positions)
-constexpr int kSwDepth = 4;       // groups of loads in flight per wavefront
 constexpr int kQtStride = 17;     // cells per channel block in a q~ slot (16 columns + 1, spreads the banks)
 
 template <int D>
 struct SwSlot {
   uint4 qt[D / 8][kQtStride];     // [channel block cb][column]: channels 8cb..8cb+7 (hi: cols 0..7, lo: 8..15)
-};
-
-template <int D>
-struct SwLoad {
-  ConsumerLoad<D> c;
-  uint32_t st[D / 64];
-  bool ok;
 };
 
 // Buffer resources over the cache arrays, built once per kernel (every array
@@ -1297,32 +742,6 @@ __device__ __forceinline__ SwRsrc sw_rsrc(const DecodeArgs& a) {
   r.md = span_rsrc(a.modality, 0x7FFFFFFF);
   r.null = span_rsrc(a.k_codes, 0);
   return r;
-}
-
-// Loads of one group: codes, statistics, norms and modality bytes of the
-// 32-position block blk (modality offset moff).  An invalid group (past the
-// partition, or on an unmapped page) passes blk = moff = 0: it reads block 0,
-// which stays in the L2, and is never consumed.
-template <int D>
-__device__ __forceinline__ void sw_load(const SwRsrc& r, int blk, int moff, int lane, int kg, SwLoad<D>& g) {
-  if constexpr (D == 128) {
-    const uint4 k4 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r.k, lane * 16, blk * (8 * D), 0));
-    const uint4 v4 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r.v, lane * 16, blk * (8 * D), 0));
-    g.c.kc[0] = k4.x; g.c.kc[1] = k4.y; g.c.kc[2] = k4.z; g.c.kc[3] = k4.w;
-    g.c.vc[0] = v4.x; g.c.vc[1] = v4.y; g.c.vc[2] = v4.z; g.c.vc[3] = v4.w;
-    const uint2 s2 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r.st, lane * 8, blk * (4 * D), 0));
-    g.st[0] = s2.x; g.st[1] = s2.y;
-  } else {
-    const uint2 k2 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r.k, lane * 8, blk * (8 * D), 0));
-    const uint2 v2 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r.v, lane * 8, blk * (8 * D), 0));
-    g.c.kc[0] = k2.x; g.c.kc[1] = k2.y;
-    g.c.vc[0] = v2.x; g.c.vc[1] = v2.y;
-    g.st[0] = __builtin_amdgcn_raw_buffer_load_b32(r.st, lane * 4, blk * (4 * D), 0);
-  }
-  g.c.nrm0 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r.nrm, 8 * kg, blk * 64, 0));
-  g.c.nrm1 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r.nrm, 32 + 8 * kg, blk * 64, 0));
-  g.c.md0 = __builtin_amdgcn_raw_buffer_load_b32(r.md, 4 * kg, moff, 0);
-  g.c.md1 = __builtin_amdgcn_raw_buffer_load_b32(r.md, 16 + 4 * kg, moff, 0);
 }
 
 // Heads per producer lane: D / 8 channel blocks x 8 heads over 64 lanes.
@@ -1399,19 +818,6 @@ struct SwFront {
   floatx4 sc[2];
 };
 
-// Value operands of a group: rows = channels 16 ct + col, k = positions.
-template <int D>
-__device__ __forceinline__ void sw_values(const ConsumerLoad<D>& cur, const uint2* tab, uint32_t lane_off,
-                                          half8 (&av)[D / 16]) {
-#pragma unroll
-  for (int ct = 0; ct < D / 16; ++ct) {
-    const int j0 = 2 * ct;
-    const uint2 x0 = lookup(tab, cur.vc[j0 >> 2], byte_sel(j0 & 3), lane_off);
-    const uint2 x1 = lookup(tab, cur.vc[(j0 + 1) >> 2], byte_sel((j0 + 1) & 3), lane_off);
-    av[ct] = as_half8(x0, x1);
-  }
-}
-
 template <int D>
 __device__ __forceinline__ void sw_front(const ConsumerLoad<D>& cur, const SwSlot<D>* slot, int kg, int col,
                                          const uint2* tab, uint32_t lane_off, SwFront<D>& f) {
@@ -1432,264 +838,15 @@ __device__ __forceinline__ void sw_front(const ConsumerLoad<D>& cur, const SwSlo
   }
 }
 
-template <int D, int SLOTS, bool ASYM>
-__device__ __forceinline__ void sw_back(const ConsumerLoad<D>& cur, SwFront<D>& f, float bias, int t0, int te,
-                                        bool partial, int kg, int col, const uint2* tab, uint32_t lane_off,
-                                        WaveState<D, SLOTS, ASYM>& ws) {
-  constexpr int CT = D / 16;
-  constexpr int GP = Slots<SLOTS>::GP;
-  constexpr int NSETS = Slots<SLOTS>::NSETS;
-  floatx4 (&sc)[2] = f.sc;
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sc[mt][r] += dpp_f<0x128>(sc[mt][r]);
-  uint32_t vmask[4] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
-  if (partial) {
-    int rem = te - t0;
-    asm volatile("" : "+s"(rem));
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const bool v = group_pos(kg, i) < rem;
-      sc[i >> 2][i & 3] = v ? sc[i >> 2][i & 3] : -__builtin_inff();
-      if (!v) vmask[i >> 1] &= (i & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-    }
-  }
-  // The weights are formed against the current reference max right away;
-  // the group's own max only decides (off the critical path) whether the
-  // reference must move first, which is rare (the reference sits kLazyMax
-  // above every score seen so far).
-  const uint32_t n4[4] = {cur.nrm0.x, cur.nrm0.y, cur.nrm1.x, cur.nrm1.y};
-  float pe[8];
-  uint32_t wp[4];
-  auto weights = [&](float off) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) pe[i] = __builtin_amdgcn_exp2f(sc[i >> 2][i & 3] - off);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) wp[r] = to_value_column<SLOTS>(weight_pair(pe[2 * r], pe[2 * r + 1], n4[r]) & vmask[r]);
-  };
-  weights(ws.m_run - bias);
-  float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                   fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-  mx = rows_max(mx) + bias;
-  if (__any(mx > ws.m_run)) {
-    const float m_new = fmaxf(ws.m_run, mx + kLazyMax);
-    const float alpha = exp2f(ws.m_run - m_new);   // 0 on the first group
-    ws.l_run *= alpha;
-    const float alpha_v = __uint_as_float(to_value_column<SLOTS>(__float_as_uint(alpha)));
-#pragma unroll
-    for (int k = 0; k < NSETS; ++k) {
-      if constexpr (ASYM) ws.accs[k] *= alpha_v;
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) ws.acc[k][ct] *= alpha_v;
-    }
-    ws.m_run = m_new;
-    // arguments are now <= 0 (or -inf): the raw base-2 exponential flushes only results below 2^-126
-    weights(ws.m_run - bias);
-  }
-  ws.l_run += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
-  half8 av[CT];
-  sw_values<D>(cur, tab, lane_off, av);
-  const int slot_c = col / GP;
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(cur.md0 & 0xFFu);
-  const bool uniform = !partial && __all(cur.md0 == m0 * 0x01010101u && cur.md1 == m0 * 0x01010101u);
-  const uint32_t md[2] = {cur.md0, cur.md1};
-#pragma unroll
-  for (int k = 0; k < NSETS; ++k) {
-    const uint32_t lo_mod = static_cast<uint32_t>(k * SLOTS);
-    const uint32_t my_mod = lo_mod + static_cast<uint32_t>(slot_c);
-    const bool col_ok = slot_c < SLOTS && my_mod < kModalities;
-    bool present;
-    uint32_t bm[4];
-    int got = 0;
-    if (uniform) {
-      present = m0 >= lo_mod && m0 < lo_mod + SLOTS && m0 < kModalities;
-      got = present ? (1 << m0) : 0;
-      const bool take = col_ok && my_mod == m0;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) bm[r] = take ? wp[r] : 0u;
-    } else {
-      int rem = partial ? te - t0 : kGroupTokens;
-      uint32_t mdo[2] = {md[0], md[1]};
-      asm volatile("" : "+s"(rem), "+v"(mdo[0]), "+v"(mdo[1]));
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        uint32_t keep = 0;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int i = 2 * r + u;
-          const uint32_t tm = (mdo[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-          const bool valid = group_pos(kg, i) < rem;
-          if (valid && tm >= lo_mod && tm < lo_mod + SLOTS && tm < kModalities) got |= 1 << tm;
-          keep |= (col_ok && tm == my_mod) ? (0xFFFFu << (16 * u)) : 0u;
-        }
-        bm[r] = wp[r] & keep;
-      }
-      present = __any(got != 0);
-    }
-    if (present) {
-      const half8 bw = __builtin_bit_cast(half8, uint4{bm[0], bm[1], bm[2], bm[3]});
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) ws.acc[k][ct] = mfma(av[ct], bw, ws.acc[k][ct]);
-      if constexpr (ASYM) {
-        const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
-        ws.accs[k] = mfma(ones, bw, ws.accs[k]);
-      }
-      ws.mask |= got;
-    }
-  }
-}
-
-// Softmax and value sums of a pair of groups (A, B) of one wavefront, with
-// rem_a / rem_b valid positions each (32 for a full group, fewer for the
-// session's last group, 0 for a group past the partition or on an unmapped
-// page; at least one of them is positive).  Positions past rem get the score
-// -inf, hence the weight 0.  The weights are formed against the current
-// reference max right away; the pair's own max only decides (off the
+// Softmax and value sums of one group with rem valid positions (1..32: 32
+// for a full group, fewer for the session's last group).  Positions past rem
+// get the score -inf, hence the weight 0.  The weights are formed against the
+// current reference max right away; the group's own max only decides (off the
 // critical path) whether the reference must move first, which is rare: the
-// reference sits kLazyMax above every score seen so far.  Pairs of one
-// single modality (the common case inside a video, audio or text run) take
-// one branch to their accumulator set; others go through per-position
-// modality masks.
-template <int D, int SLOTS, bool ASYM>
-__device__ __forceinline__ void sw_back2(const ConsumerLoad<D>& ca, const ConsumerLoad<D>& cb, const SwFront<D>& fa,
-                                         const SwFront<D>& fb, float bias_a, float bias_b, int rem_a, int rem_b,
-                                         int kg, int col, const uint2* tab, uint32_t lane_off,
-                                         WaveState<D, SLOTS, ASYM>& ws) {
-  constexpr int CT = D / 16;
-  constexpr int GP = Slots<SLOTS>::GP;
-  constexpr int NSETS = Slots<SLOTS>::NSETS;
-  float s[2][8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    s[0][i] = fa.sc[i >> 2][i & 3] + dpp_f<0x128>(fa.sc[i >> 2][i & 3]);
-    s[1][i] = fb.sc[i >> 2][i & 3] + dpp_f<0x128>(fb.sc[i >> 2][i & 3]);
-  }
-  if (rem_a < kGroupTokens || rem_b < kGroupTokens) {
-    int ra = rem_a, rb = rem_b;
-    asm volatile("" : "+s"(ra), "+s"(rb));
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      s[0][i] = group_pos(kg, i) < ra ? s[0][i] : -__builtin_inff();
-      s[1][i] = group_pos(kg, i) < rb ? s[1][i] : -__builtin_inff();
-    }
-  }
-  const uint32_t na[4] = {ca.nrm0.x, ca.nrm0.y, ca.nrm1.x, ca.nrm1.y};
-  const uint32_t nb[4] = {cb.nrm0.x, cb.nrm0.y, cb.nrm1.x, cb.nrm1.y};
-  float pe[2][8];
-  uint32_t wa[4], wb[4];
-  auto weights = [&](float m_ref) {
-    const float oa = m_ref - bias_a, ob = m_ref - bias_b;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      pe[0][i] = __builtin_amdgcn_exp2f(s[0][i] - oa);
-      pe[1][i] = __builtin_amdgcn_exp2f(s[1][i] - ob);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      wa[r] = to_value_column<SLOTS>(weight_pair(pe[0][2 * r], pe[0][2 * r + 1], na[r]));
-      wb[r] = to_value_column<SLOTS>(weight_pair(pe[1][2 * r], pe[1][2 * r + 1], nb[r]));
-    }
-  };
-  weights(ws.m_run);
-  float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                   fmaxf(fmaxf(s[0][4], s[0][5]), fmaxf(s[0][6], s[0][7]))) + bias_a;
-  mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])),
-                       fmaxf(fmaxf(s[1][4], s[1][5]), fmaxf(s[1][6], s[1][7]))) + bias_b);
-  mx = rows_max(mx);
-  if (__any(mx > ws.m_run)) {
-    const float m_new = fmaxf(ws.m_run, mx + kLazyMax);
-    const float alpha = exp2f(ws.m_run - m_new);   // 0 on the first group
-    ws.l_run *= alpha;
-    const float alpha_v = __uint_as_float(to_value_column<SLOTS>(__float_as_uint(alpha)));
-#pragma unroll
-    for (int k = 0; k < NSETS; ++k) {
-      if constexpr (ASYM) ws.accs[k] *= alpha_v;
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) ws.acc[k][ct] *= alpha_v;
-    }
-    ws.m_run = m_new;
-    // arguments are now <= 0 (or -inf): the raw base-2 exponential flushes only results below 2^-126
-    weights(ws.m_run);
-  }
-  ws.l_run += (((pe[0][0] + pe[0][1]) + (pe[0][2] + pe[0][3])) + ((pe[0][4] + pe[0][5]) + (pe[0][6] + pe[0][7]))) +
-              (((pe[1][0] + pe[1][1]) + (pe[1][2] + pe[1][3])) + ((pe[1][4] + pe[1][5]) + (pe[1][6] + pe[1][7])));
-  const int slot_c = col / GP;
-  // value products of set k with the weight columns ba (group A) / bb (group B)
-  auto accumulate = [&](int k, const uint32_t (&ba)[4], const uint32_t (&bb)[4]) {
-    const half8 bwa = __builtin_bit_cast(half8, uint4{ba[0], ba[1], ba[2], ba[3]});
-    const half8 bwb = __builtin_bit_cast(half8, uint4{bb[0], bb[1], bb[2], bb[3]});
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      const int j0 = 2 * ct;
-      const half8 va = as_half8(lookup(tab, ca.vc[j0 >> 2], byte_sel(j0 & 3), lane_off),
-                                lookup(tab, ca.vc[(j0 + 1) >> 2], byte_sel((j0 + 1) & 3), lane_off));
-      const half8 vb = as_half8(lookup(tab, cb.vc[j0 >> 2], byte_sel(j0 & 3), lane_off),
-                                lookup(tab, cb.vc[(j0 + 1) >> 2], byte_sel((j0 + 1) & 3), lane_off));
-      ws.acc[k][ct] = mfma(va, bwa, ws.acc[k][ct]);
-      ws.acc[k][ct] = mfma(vb, bwb, ws.acc[k][ct]);
-    }
-    if constexpr (ASYM) {
-      const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
-      ws.accs[k] = mfma(ones, bwa, ws.accs[k]);
-      ws.accs[k] = mfma(ones, bwb, ws.accs[k]);
-    }
-  };
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((rem_a > 0 ? ca.md0 : cb.md0) & 0xFFu);
-  const uint32_t mm = m0 * 0x01010101u;
-  const bool uniform = rem_a == kGroupTokens && rem_b == kGroupTokens && m0 < kModalities &&
-                       __all(ca.md0 == mm && ca.md1 == mm && cb.md0 == mm && cb.md1 == mm);
-  if (uniform) {
-    const int k0 = static_cast<int>(m0) / SLOTS;                    // the set holding m0
-    const bool take = slot_c == static_cast<int>(m0) - k0 * SLOTS;   // this column is m0's slot
-    uint32_t ba[4], bb[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      ba[r] = take ? wa[r] : 0u;
-      bb[r] = take ? wb[r] : 0u;
-    }
-#pragma unroll
-    for (int k = 0; k < NSETS; ++k)
-      if (k == k0) accumulate(k, ba, bb);
-    ws.mask |= 1 << m0;
-  } else {
-    int ra = rem_a, rb = rem_b;
-    uint32_t mda[2] = {ca.md0, ca.md1}, mdb[2] = {cb.md0, cb.md1};
-    asm volatile("" : "+s"(ra), "+s"(rb), "+v"(mda[0]), "+v"(mda[1]), "+v"(mdb[0]), "+v"(mdb[1]));
-#pragma unroll
-    for (int k = 0; k < NSETS; ++k) {
-      const uint32_t lo_mod = static_cast<uint32_t>(k * SLOTS);
-      const uint32_t my_mod = lo_mod + static_cast<uint32_t>(slot_c);
-      const bool col_ok = slot_c < SLOTS && my_mod < kModalities;
-      uint32_t ba[4], bb[4];
-      int got = 0;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        uint32_t keep_a = 0, keep_b = 0;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int i = 2 * r + u;
-          const uint32_t ta = (mda[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-          const uint32_t tb2 = (mdb[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-          const bool va = group_pos(kg, i) < ra, vb = group_pos(kg, i) < rb;
-          if (va && ta >= lo_mod && ta < lo_mod + SLOTS && ta < kModalities) got |= 1 << ta;
-          if (vb && tb2 >= lo_mod && tb2 < lo_mod + SLOTS && tb2 < kModalities) got |= 1 << tb2;
-          keep_a |= (col_ok && ta == my_mod) ? (0xFFFFu << (16 * u)) : 0u;
-          keep_b |= (col_ok && tb2 == my_mod) ? (0xFFFFu << (16 * u)) : 0u;
-        }
-        ba[r] = wa[r] & keep_a;
-        bb[r] = wb[r] & keep_b;
-      }
-      if (__any(got != 0)) {
-        accumulate(k, ba, bb);
-        ws.mask |= wave_or_bits(got);
-      }
-    }
-  }
-}
-
-// Softmax and value sums of one group with rem valid positions (1..32): as
-// sw_back2 for a single group.
+// reference sits kLazyMax above every score seen so far.  Groups of one single
+// modality (the common case inside a video, audio or text run) take one
+// branch to their accumulator set; others go through per-position modality
+// masks.
 template <int D, int SLOTS, bool ASYM>
 __device__ __forceinline__ void sw_back1(const ConsumerLoad<D>& ca, const SwFront<D>& fa, float bias_a, int rem_a,
                                          int kg, int col, const uint2* tab, uint32_t lane_off,
@@ -2022,13 +1179,17 @@ __global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(D
     for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][hp]);
     const float mw = s_m[c][hp];
     const float e = (mw == -__builtin_inff()) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+    // only columns of a real head whose modality received weight are handed over
 #pragma unroll
     for (int k = 0; k < NSETS; ++k) {
       if (!(wm & set_bits<SLOTS>(k))) continue;
+      const int m = k * SLOTS + slot_c;
+      if (slot_c < SLOTS && m < kModalities && hp < G && ((wm >> m) & 1)) {
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        const floatx4 v = ws.acc[k][ct] * e;
-        sm.red[c][(k * CT + ct) * 64 + lane] = float4{v[0], v[1], v[2], v[3]};
+        for (int ct = 0; ct < CT; ++ct) {
+          const floatx4 v = ws.acc[k][ct] * e;
+          sm.red[c][(k * CT + ct) * 64 + lane] = float4{v[0], v[1], v[2], v[3]};
+        }
       }
     }
   }
@@ -2041,15 +1202,19 @@ __global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(D
     const int sl2 = c2 / GP, hp2 = c2 % GP;
     const int m = k * SLOTS + sl2;
     if (sl2 < SLOTS && m < kModalities && hp2 < G && (wmask & (1 << m))) {
+      // all reads first (a wavefront that did not touch modality m left its
+      // slot unwritten: selected away, in a fixed order)
+      float4 v[NW];
+#pragma unroll
+      for (int w = 0; w < NW; ++w) v[w] = sm.red[w][pos];
       float4 sum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        if (!(s_cmask[w] & set_bits<SLOTS>(k))) continue;
-        const float4 v = sm.red[w][pos];
-        sum.x += v.x;
-        sum.y += v.y;
-        sum.z += v.z;
-        sum.w += v.w;
+        const bool t = (s_cmask[w] >> m) & 1;
+        sum.x += t ? v[w].x : 0.f;
+        sum.y += t ? v[w].y : 0.f;
+        sum.z += t ? v[w].z : 0.f;
+        sum.w += t ? v[w].w : 0.f;
       }
       float* part = a.partials + ((static_cast<size_t>(b) * a.hq + h * G + hp2) * a.splits + split) * PS;
       *reinterpret_cast<float4*>(part + kPartialHeader + m * D + 16 * ct + 4 * kg2) = sum;
@@ -2302,15 +1467,6 @@ void launch_partition(int batch, const DecodeArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((decode_partition_kernel<D, SLOTS, NW, true, BHL>), grid, dim3(NW * 64), 0, s, a);
   else
     hipLaunchKernelGGL((decode_partition_kernel<D, SLOTS, NW, false, BHL>), grid, dim3(NW * 64), 0, s, a);
-}
-
-template <int D, int SLOTS>
-void launch_partition_pc(int batch, const DecodeArgs& a, hipStream_t s) {
-  const dim3 grid(a.splits, a.hkv, batch);
-  if (a.cmid != 0.f)
-    hipLaunchKernelGGL((decode_partition_pc_kernel<D, SLOTS, true>), grid, dim3(kPcWaves * 64), 0, s, a);
-  else
-    hipLaunchKernelGGL((decode_partition_pc_kernel<D, SLOTS, false>), grid, dim3(kPcWaves * 64), 0, s, a);
 }
 
 template <int D, int SLOTS>
