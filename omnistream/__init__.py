@@ -11,6 +11,7 @@ from .streams import (  # noqa: F401
     StreamConfig,
     Workload,
     bf16_bits_to_f64,
+    calibration_queries,
     f64_to_bf16_bits,
     generate,
     lloyd_max_codebook_2bit,

@@ -266,7 +266,16 @@ def generate(cfg_id: int, length: Optional[int] = None, batch: Optional[int] = N
                     k=k_list, v=v_list, modality=m_list, q=q, lengths=total,
                     prefix_lengths=prefix, page_tokens=pt, max_pages=max_pages,
                     num_pages=num_pages, page_table=table,
-                    meta={"outlier_channels": [o.tolist() for o in outliers]})
+                    meta={"outlier_channels": [o.tolist() for o in outliers],
+                          "value_spectrum": lam})
+
+
+def calibration_queries(w: Workload, n_queries: int) -> np.ndarray:
+    """n_queries seeded N(0, 1) query vectors per query head, [n_queries, Hq, d]
+    in the workload's dtype: the queries a value-basis calibration attends
+    with.  Seeded apart from the workload's own draws (entropy (cfg_id, 7))."""
+    rng = np.random.default_rng(np.random.SeedSequence([w.cfg.cfg_id, 7]))
+    return _to_dtype(rng.standard_normal((n_queries, w.cfg.n_q_heads, w.cfg.head_dim)), w.cfg.dtype)
 
 
 def workload_digest(w: Workload) -> str:

@@ -105,3 +105,109 @@ def test_planted_mistake_is_caught(monkeypatch, name, mutant, pins):
     monkeypatch.setattr(O, name, mutant)
     for pin, *args in pins:
         assert _fails(pin, *args), f"{pin.__name__} did not notice {mutant.__name__}"
+
+
+# ------------------------------------------------ value-basis calibration
+
+from oracle import kvq_calib_oracle as CO  # noqa: E402
+import tests.test_calib_pins as CP  # noqa: E402
+
+_orig_ac = CO.attention_contribution
+_orig_wc = CO.weighted_covariance
+_orig_eb = CO.eigenbasis
+_orig_qe = CO.value_quantization_error
+
+
+def _contribution_over_queries(k, q_rows, scale):
+    """Normalises each token's scores over the queries instead of the tokens."""
+    s = scale * (np.asarray(q_rows, np.float64) @ np.asarray(k, np.float64).T)
+    p = np.exp(s - s.max(axis=0, keepdims=True))
+    p = p / p.sum(axis=0, keepdims=True)
+    return p.mean(axis=0) / k.shape[0]
+
+
+def _contribution_wrong_head(k, q, scale):
+    n, hkv, d = k.shape
+    nq, hq, _ = q.shape
+    out = np.zeros((hkv, n))
+    for h in range(hkv):
+        rows = q[:, h::hkv, :].reshape(-1, d)       # heads h, h + Hkv, ... instead of a contiguous group
+        out[h] = CO.attention_contribution(k[:, h, :], rows, scale)
+    return out
+
+
+def _covariance_uncentred(v, modality, w):
+    Cm, W, mu = _orig_wc(v, modality, w)
+    for m in range(3):
+        if W[m] > 0:
+            Cm[m] = Cm[m] + np.outer(mu[m], mu[m])
+    return Cm, W, mu
+
+
+def _covariance_squared_weights(v, modality, w):
+    return _orig_wc(v, modality, np.asarray(w, np.float64) ** 2)
+
+
+def _covariance_divides_by_count(v, modality, w):
+    Cm, W, mu = _orig_wc(v, modality, w)
+    for m in range(3):
+        cnt = int((np.asarray(modality) == m).sum())
+        if W[m] > 0:
+            Cm[m] = Cm[m] * W[m] / cnt
+    return Cm, W, mu
+
+
+def _eigenbasis_ascending(C):
+    R, lam = _orig_eb(C)
+    return R[:, ::-1].copy(), lam[::-1].copy()
+
+
+def _eigenbasis_rows(C):
+    R, lam = _orig_eb(C)
+    return R.T.copy(), lam
+
+
+def _eigenbasis_no_sign_rule(C):
+    R, lam = _orig_eb(C)
+    return -R, lam
+
+
+def _error_reconstructs_with_transpose(v, modality, rot, codebook):
+    """Quantizes with R_m^T v but reconstructs with R_m^T instead of R_m."""
+    codes, norms = O.quantize_values(v, modality, rot, codebook)
+    vt = O.dequantize_values_rotated(codes, norms, codebook)
+    R = np.asarray(rot, np.float32).astype(np.float64)
+    err = np.full(3, np.nan)
+    for m in range(3):
+        idx = np.asarray(modality) == m
+        if idx.any():
+            vh = vt[idx] @ R[m]
+            err[m] = ((v[idx] - vh) ** 2).sum() / (v[idx] ** 2).sum()
+    return err
+
+
+CALIB_MUTANTS = [
+    ("attention_contribution", _contribution_over_queries,
+     [(CP.test_weights_of_each_head_sum_to_one_and_follow_permutation,), (CP.test_two_tokens_follow_the_logistic_function,)]),
+    ("contribution_weights", _contribution_wrong_head, [(CP.test_query_heads_map_to_kv_head_floor_i_over_g,)]),
+    ("weighted_covariance", _covariance_uncentred,
+     [(CP.test_uniform_weights_give_population_covariance,), (CP.test_covariance_is_shift_invariant_and_per_modality,)]),
+    ("weighted_covariance", _covariance_squared_weights,
+     [(CP.test_doubled_weight_equals_duplicated_token_and_scale_invariance,)]),
+    ("weighted_covariance", _covariance_divides_by_count,
+     [(CP.test_covariance_recovers_constructed_matrix,)]),
+    ("eigenbasis", _eigenbasis_ascending, [(CP.test_eigenbasis_of_diagonal_is_sorted_permutation,)]),
+    ("eigenbasis", _eigenbasis_rows, [(CP.test_eigenbasis_recovers_known_basis_with_sign_rule,)]),
+    ("eigenbasis", _eigenbasis_no_sign_rule, [(CP.test_eigenbasis_two_by_two_closed_form,),
+                                              (CP.test_calibration_recovers_each_modality_basis_exactly,)]),
+    ("value_quantization_error", _error_reconstructs_with_transpose,
+     [(CP.test_error_harness_matches_the_quantizer_distortion,),
+      (CP.test_error_harness_is_invariant_under_a_common_rotation,)]),
+]
+
+
+@pytest.mark.parametrize("name,mutant,pins", CALIB_MUTANTS, ids=[m[1].__name__ for m in CALIB_MUTANTS])
+def test_planted_calibration_mistake_is_caught(monkeypatch, name, mutant, pins):
+    monkeypatch.setattr(CO, name, mutant)
+    for pin, *args in pins:
+        assert _fails(pin, *args), f"{pin.__name__} did not notice {mutant.__name__}"
