@@ -15,10 +15,12 @@ from typing import Optional, Sequence
 import torch
 
 from . import _lib
-from ._lib import KVQ_BF16, KVQ_F32, KvqCache, KvqConfig, KvqError, KvqParams  # noqa: F401
+from ._lib import KVQ_BF16, KVQ_F32, KvqCache, KvqCalibShape, KvqConfig, KvqError, KvqParams  # noqa: F401
 
 __all__ = ["Config", "Params", "Cache", "kvq_quantize_append", "kvq_rotate_query", "kvq_append_and_rotate",
-           "kvq_decode_workspace_bytes", "kvq_decode_attention", "KvqError"]
+           "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_calib_workspace_bytes",
+           "kvq_calib_eigenbasis_workspace_bytes", "kvq_calib_contribution", "kvq_calib_covariance",
+           "kvq_calib_eigenbasis", "KvqError"]
 
 _DTYPES = {torch.float32: KVQ_F32, torch.bfloat16: KVQ_BF16}
 
@@ -188,3 +190,96 @@ def kvq_decode_attention(cfg: Config, cache: Cache, params: Params, q_rot: torch
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
     _lib.check("kvq_decode_attention", st)
     return out
+
+
+# ------------------------------------------------------ value-basis calibration
+
+def _calib_shape(head_dim: int, n_q_heads: int, n_kv_heads: int, n_tokens: int, n_queries: int) -> KvqCalibShape:
+    return KvqCalibShape(int(head_dim), int(n_q_heads), int(n_kv_heads), int(n_tokens), int(n_queries))
+
+
+def kvq_calib_workspace_bytes(head_dim: int, n_q_heads: int, n_kv_heads: int, n_tokens: int,
+                              n_queries: int) -> int:
+    shape = _calib_shape(head_dim, n_q_heads, n_kv_heads, n_tokens, n_queries)
+    return int(_lib.load().kvq_calib_workspace_bytes(ctypes.byref(shape)))
+
+
+def kvq_calib_eigenbasis_workspace_bytes(count: int, head_dim: int) -> int:
+    return int(_lib.load().kvq_calib_eigenbasis_workspace_bytes(int(count), int(head_dim)))
+
+
+def _workspace(need: int, workspace, device) -> torch.Tensor:
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    return workspace
+
+
+def kvq_calib_contribution(k: torch.Tensor, q: torch.Tensor, scale: Optional[float] = None,
+                           weights: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                           stream=None) -> torch.Tensor:
+    """k: [n, Hkv, d], q: [nq, Hq, d] (fp32 or bf16) -> weights [Hkv, n] fp64."""
+    if k.dim() != 3 or q.dim() != 3 or k.shape[2] != q.shape[2]:
+        raise ValueError("k must be [n, Hkv, d] and q [nq, Hq, d]")
+    if k.dtype not in _DTYPES or q.dtype not in _DTYPES:
+        raise TypeError("k and q must be float32 or bfloat16")
+    n, hkv, d = (int(x) for x in k.shape)
+    nq, hq = int(q.shape[0]), int(q.shape[1])
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    shape = _calib_shape(d, hq, hkv, n, nq)
+    if weights is None:
+        weights = torch.empty((hkv, n), dtype=torch.float64, device=k.device)
+    workspace = _workspace(kvq_calib_workspace_bytes(d, hq, hkv, n, nq), workspace, k.device)
+    st = _lib.load().kvq_calib_contribution(
+        ctypes.byref(shape), _dev(k, "k"), _DTYPES[k.dtype], _dev(q, "q"), _DTYPES[q.dtype], float(scale),
+        _dev(weights, "weights", torch.float64), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _lib.check("kvq_calib_contribution", st)
+    return weights
+
+
+def kvq_calib_covariance(v: torch.Tensor, modality: torch.Tensor, weights: torch.Tensor,
+                         cov: Optional[torch.Tensor] = None, weight_sum: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None, stream=None):
+    """v: [n, Hkv, d] (fp32 or bf16), modality: [n] uint8, weights: [Hkv, n] fp64
+    -> (cov [Hkv, 3, d, d] fp64, weight_sum [Hkv, 3] fp64)."""
+    if v.dim() != 3 or v.dtype not in _DTYPES:
+        raise ValueError("v must be [n, Hkv, d] float32 or bfloat16")
+    n, hkv, d = (int(x) for x in v.shape)
+    if tuple(modality.shape) != (n,) or tuple(weights.shape) != (hkv, n):
+        raise ValueError("modality must be [n] and weights [Hkv, n]")
+    shape = _calib_shape(d, hkv, hkv, n, 1)
+    if cov is None:
+        cov = torch.empty((hkv, 3, d, d), dtype=torch.float64, device=v.device)
+    if weight_sum is None:
+        weight_sum = torch.empty((hkv, 3), dtype=torch.float64, device=v.device)
+    workspace = _workspace(kvq_calib_workspace_bytes(d, hkv, hkv, n, 1), workspace, v.device)
+    st = _lib.load().kvq_calib_covariance(
+        ctypes.byref(shape), _dev(v, "v"), _DTYPES[v.dtype], _dev(modality, "modality", torch.uint8),
+        _dev(weights, "weights", torch.float64), _dev(cov, "cov", torch.float64),
+        _dev(weight_sum, "weight_sum", torch.float64), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _lib.check("kvq_calib_covariance", st)
+    return cov, weight_sum
+
+
+def kvq_calib_eigenbasis(cov: torch.Tensor, rot: Optional[torch.Tensor] = None,
+                         eigenvalues: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                         stream=None):
+    """cov: [..., d, d] fp64 symmetric -> (rot [..., d, d] fp32 with eigenvector
+    columns in decreasing eigenvalue order, eigenvalues [..., d] fp64)."""
+    if cov.dim() < 2 or cov.shape[-1] != cov.shape[-2]:
+        raise ValueError("cov must be [..., d, d]")
+    d = int(cov.shape[-1])
+    count = int(cov.numel() // (d * d))
+    if rot is None:
+        rot = torch.empty(cov.shape, dtype=torch.float32, device=cov.device)
+    if eigenvalues is None:
+        eigenvalues = torch.empty(cov.shape[:-1], dtype=torch.float64, device=cov.device)
+    workspace = _workspace(kvq_calib_eigenbasis_workspace_bytes(count, d), workspace, cov.device)
+    st = _lib.load().kvq_calib_eigenbasis(
+        count, d, _dev(cov, "cov", torch.float64), _dev(rot, "rot", torch.float32),
+        _dev(eigenvalues, "eigenvalues", torch.float64), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _lib.check("kvq_calib_eigenbasis", st)
+    return rot, eigenvalues

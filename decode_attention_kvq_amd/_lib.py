@@ -1,4 +1,4 @@
-"""ctypes view of libkvq.so (the C ABI declared in include/kvq.h)."""
+"""ctypes view of libkvq.so (the C ABI declared in include/kvq.h and include/kvq_calib.h)."""
 from __future__ import annotations
 
 import ctypes
@@ -13,7 +13,9 @@ KVQ_OK, KVQ_ERR_INVALID, KVQ_ERR_UNSUPPORTED, KVQ_ERR_CAPACITY, KVQ_ERR_WORKSPAC
 KVQ_F32, KVQ_BF16 = 0, 1
 
 EXPORTED = ("kvq_cache_buffer_bytes", "kvq_quantize_append", "kvq_rotate_query", "kvq_append_and_rotate",
-            "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_status_string")
+            "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_status_string",
+            "kvq_calib_workspace_bytes", "kvq_calib_eigenbasis_workspace_bytes", "kvq_calib_contribution",
+            "kvq_calib_covariance", "kvq_calib_eigenbasis")
 
 
 class KvqConfig(ctypes.Structure):
@@ -34,6 +36,12 @@ class KvqCache(ctypes.Structure):
 class KvqParams(ctypes.Structure):
     _fields_ = [("signs", ctypes.c_void_p), ("rot", ctypes.c_void_p),
                 ("codebook", ctypes.c_float * 4)]
+
+
+class KvqCalibShape(ctypes.Structure):
+    _fields_ = [("head_dim", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("n_tokens", ctypes.c_int32),
+                ("n_queries", ctypes.c_int32)]
 
 
 class KvqError(RuntimeError):
@@ -74,6 +82,18 @@ def load() -> ctypes.CDLL:
                                          ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_size_t, ctypes.c_void_p]
     lib.kvq_decode_attention.restype = ctypes.c_int
+    V = ctypes.c_void_p
+    lib.kvq_calib_workspace_bytes.argtypes = [P(KvqCalibShape)]
+    lib.kvq_calib_workspace_bytes.restype = ctypes.c_size_t
+    lib.kvq_calib_eigenbasis_workspace_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    lib.kvq_calib_eigenbasis_workspace_bytes.restype = ctypes.c_size_t
+    lib.kvq_calib_contribution.argtypes = [P(KvqCalibShape), V, ctypes.c_int32, V, ctypes.c_int32, ctypes.c_double,
+                                           V, V, ctypes.c_size_t, V]
+    lib.kvq_calib_contribution.restype = ctypes.c_int
+    lib.kvq_calib_covariance.argtypes = [P(KvqCalibShape), V, ctypes.c_int32, V, V, V, V, V, ctypes.c_size_t, V]
+    lib.kvq_calib_covariance.restype = ctypes.c_int
+    lib.kvq_calib_eigenbasis.argtypes = [ctypes.c_int32, ctypes.c_int32, V, V, V, V, ctypes.c_size_t, V]
+    lib.kvq_calib_eigenbasis.restype = ctypes.c_int
     lib.kvq_status_string.argtypes = [ctypes.c_int]
     lib.kvq_status_string.restype = ctypes.c_char_p
     _lib = lib

@@ -26,6 +26,8 @@ SOURCES = {
     # the decode takes no decision on NaNs: max / min need no quieting
     "kvq_decode.hip": ["-fno-honor-nans"],
     "kvq_api.hip": [],
+    # calibration: scores formed identically in two kernels, symmetric products
+    "kvq_calib.hip": ["-ffp-contract=off"],
 }
 
 COMMON = [

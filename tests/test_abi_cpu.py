@@ -19,7 +19,8 @@ def _lib():
 
 
 def _declared():
-    src = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    inc = os.path.join(ROOT, "include")
+    src = "".join(open(os.path.join(inc, f)).read() for f in sorted(os.listdir(inc)) if f.endswith(".h"))
     return sorted(set(re.findall(r"^\s*(?:kvq_status|size_t|const char\*)\s+(kvq_\w+)\s*\(", src, re.M)))
 
 
@@ -157,3 +158,46 @@ def test_binding_refuses_cpu_tensors():
     cfg = K.Config(64, 2, 1, 1, 256, 8, 8, torch.float32)
     with pytest.raises(TypeError):
         K.Params(torch.ones(1, 64, dtype=torch.int8), torch.zeros(1, 3, 64, 64), [-1.5, -0.5, 0.5, 1.5])
+
+
+def test_calibration_rejects_bad_arguments_without_launching():
+    L, lib = _lib()
+    V = ctypes.c_void_p
+
+    def shape(**kw):
+        f = dict(head_dim=128, n_q_heads=16, n_kv_heads=2, n_tokens=1000, n_queries=4)
+        f.update(kw)
+        return L.KvqCalibShape(*[f[name] for name, _ in L.KvqCalibShape._fields_])
+    good = shape()
+    need = lib.kvq_calib_workspace_bytes(ctypes.byref(good))
+    assert need >= lib.kvq_calib_eigenbasis_workspace_bytes(6, 128) == 6 * 128 * 128 * 8
+    assert lib.kvq_calib_workspace_bytes(ctypes.byref(shape(head_dim=96))) == 0
+    assert lib.kvq_calib_eigenbasis_workspace_bytes(-1, 128) == 0
+    for kw, status in [(dict(head_dim=96), 2), (dict(n_q_heads=15), 1), (dict(n_tokens=-1), 1),
+                       (dict(n_queries=0), 1), (dict(n_kv_heads=0), 1)]:
+        s_ = shape(**kw)
+        assert lib.kvq_calib_contribution(ctypes.byref(s_), V(8), 1, V(8), 1, 0.1, V(8), V(8), need, None) == status
+        assert lib.kvq_calib_covariance(ctypes.byref(s_), V(8), 1, V(8), V(8), V(8), V(8), V(8), need, None) == status
+    con = lambda **kw: lib.kvq_calib_contribution(
+        ctypes.byref(kw.pop("shape", good)), kw.pop("k", V(8)), kw.pop("kd", 1), kw.pop("q", V(8)), kw.pop("qd", 1),
+        kw.pop("scale", 0.1), kw.pop("w", V(8)), kw.pop("ws", V(8)), kw.pop("nbytes", need), None)
+    assert con(kd=5) == L.KVQ_ERR_UNSUPPORTED
+    assert con(scale=0.0) == L.KVQ_ERR_INVALID
+    assert con(scale=float("inf")) == L.KVQ_ERR_INVALID
+    assert con(q=None) == L.KVQ_ERR_INVALID
+    assert con(ws=None) == L.KVQ_ERR_WORKSPACE
+    assert con(nbytes=16) == L.KVQ_ERR_WORKSPACE
+    assert con(shape=shape(n_tokens=0), k=None, q=None, w=None) == L.KVQ_OK      # nothing to do
+    cov = lambda **kw: lib.kvq_calib_covariance(
+        ctypes.byref(good), kw.pop("v", V(8)), kw.pop("vd", 0), kw.pop("m", V(8)), kw.pop("w", V(8)),
+        kw.pop("c", V(8)), kw.pop("s", V(8)), kw.pop("ws", V(8)), kw.pop("nbytes", need), None)
+    assert cov(vd=3) == L.KVQ_ERR_UNSUPPORTED
+    assert cov(m=None) == L.KVQ_ERR_INVALID and cov(c=None) == L.KVQ_ERR_INVALID and cov(s=None) == L.KVQ_ERR_INVALID
+    assert cov(nbytes=1) == L.KVQ_ERR_WORKSPACE
+    eig = lambda count=6, d=128, c=V(8), r=V(8), e=V(8), ws=V(8), nbytes=need: lib.kvq_calib_eigenbasis(
+        count, d, c, r, e, ws, nbytes, None)
+    assert eig(count=-1) == L.KVQ_ERR_INVALID
+    assert eig(d=32) == L.KVQ_ERR_UNSUPPORTED
+    assert eig(r=None) == L.KVQ_ERR_INVALID
+    assert eig(nbytes=6 * 128 * 128 * 8 - 1) == L.KVQ_ERR_WORKSPACE
+    assert eig(count=0, c=None, r=None, e=None) == L.KVQ_OK                       # nothing to do
