@@ -64,6 +64,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calibration-only", action="store_true",
+                    help="only time the value-basis calibration on the 80K stream and print its JSON line")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB ten times (reference "
                          "for the HBM byte counters) and exit")
@@ -91,6 +93,9 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     L0 = 81920
+    if args.calibration_only:
+        print(json.dumps({"value_calibration": time_calibration(L0)}), flush=True)
+        return
     extra = args.steps // args.replicas + args.warmup // args.replicas + 4
     w = generate(2, length=L0 + extra)
     c = w.cfg
@@ -242,6 +247,8 @@ def main():
     copy_bytes = 2 * cdst.numel() * 4
     del sbufs, cdst
 
+    calib = time_calibration(L0)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, cfg, caches[0], args.cpu_seconds)
@@ -267,9 +274,73 @@ def main():
                   "decode_kv_tokens_per_s": Ld / (dec_ms * 1e-3),
                   "decode_us_half_pages_retained": half_ms * 1e3,
                   "copy_read_write_GBps": copy_bytes / (copy_ms * 1e-3) / 1e9,
-                  "step_wall_us": wall / steps * 1e6},
+                  "step_wall_us": wall / steps * 1e6,
+                  "value_calibration": calib},
     }
     print(json.dumps(rec), flush=True)
+
+
+def time_calibration(n_tokens: int, n_queries: int = 8, repeats: int = 5) -> dict:
+    """Value-basis calibration (contribution weights -> per-modality weighted
+    covariances -> eigenbases) over the first n_tokens of the 80K omni stream
+    (28 query / 4 KV heads, d = 128, bf16), n_queries calibration queries per
+    query head.  Inputs resident on the GPU; HIP events per step on the
+    launch stream; the median of `repeats` runs after one warm-up."""
+    import torch
+    import decode_attention_kvq_amd as K
+    from omnistream import calibration_queries, generate
+    from tests import kvq_harness as H
+
+    w = generate(2, length=n_tokens)
+    dev = torch.device("cuda", 0)
+    k = H._kv_tensor(w.k[0], w.dtype, dev)
+    v = H._kv_tensor(w.v[0], w.dtype, dev)
+    mod = torch.from_numpy(np.ascontiguousarray(w.modality[0])).to(dev)
+    q = H._kv_tensor(calibration_queries(w, n_queries), w.dtype, dev)
+    c = w.cfg
+    ws = torch.empty(K.kvq_calib_workspace_bytes(c.head_dim, c.n_q_heads, c.n_kv_heads, n_tokens, n_queries),
+                     dtype=torch.uint8, device=dev)
+    wt = torch.empty((c.n_kv_heads, n_tokens), dtype=torch.float64, device=dev)
+    cov = torch.empty((c.n_kv_heads, 3, c.head_dim, c.head_dim), dtype=torch.float64, device=dev)
+    wsum = torch.empty((c.n_kv_heads, 3), dtype=torch.float64, device=dev)
+    rot = torch.empty(cov.shape, dtype=torch.float32, device=dev)
+    lam = torch.empty(cov.shape[:-1], dtype=torch.float64, device=dev)
+    stream = torch.cuda.current_stream()
+    times = []
+    for rep in range(repeats + 1):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        ev[0].record(stream)
+        K.kvq_calib_contribution(k, q, weights=wt, workspace=ws)
+        ev[1].record(stream)
+        K.kvq_calib_covariance(v, mod, wt, cov=cov, weight_sum=wsum, workspace=ws)
+        ev[2].record(stream)
+        K.kvq_calib_eigenbasis(cov, rot=rot, eigenvalues=lam, workspace=ws)
+        ev[3].record(stream)
+        torch.cuda.synchronize()
+        if rep:
+            times.append([ev[i].elapsed_time(ev[i + 1]) for i in range(3)])
+    t = np.median(np.array(times), axis=0)
+    # the fp64 oracle's whole calibration on one host thread, for context
+    from threadpoolctl import threadpool_limits
+    from oracle import kvq_calib_oracle as CO
+    from oracle import kvq_oracle as O
+    with threadpool_limits(limits=1):
+        t_cpu = time.perf_counter()
+        CO.calibrate_value_bases(O.as_f64(w.k[0], w.dtype), O.as_f64(w.v[0], w.dtype), w.modality[0],
+                                 O.as_f64(calibration_queries(w, n_queries), w.dtype), 1.0 / math.sqrt(c.head_dim))
+        t_cpu = time.perf_counter() - t_cpu
+    rows = n_queries * c.n_q_heads
+    d = c.head_dim
+    # fp64 flops: scores twice (max / sum pass, then weights) at 2 per FMA;
+    # covariance: one product and one FMA per (token, KV head, entry i <= j)
+    contrib_flop = 2.0 * n_tokens * rows * d * 2
+    cov_flop = 2.0 * n_tokens * c.n_kv_heads * d * (d + 1) / 2
+    return {"workload": f"{n_tokens} tokens, {c.n_q_heads}/{c.n_kv_heads} heads, d={d}, {n_queries} queries/head",
+            "ms_total": float(t.sum()), "ms_contribution": float(t[0]), "ms_covariance": float(t[1]),
+            "ms_eigenbasis": float(t[2]), "matrices": 3 * c.n_kv_heads,
+            "contribution_fp64_TFLOPs": contrib_flop / (t[0] * 1e-3) / 1e12,
+            "covariance_fp64_TFLOPs": cov_flop / (t[1] * 1e-3) / 1e12,
+            "fp64_peak_TFLOPs": 78.6, "oracle_ms_1thread": t_cpu * 1e3}
 
 
 def cpu_baseline(w, cfg, cache, budget_s: float) -> dict:

@@ -131,18 +131,25 @@ __global__ __launch_bounds__(kTokBlock) void calib_block_stats_kernel(ContribArg
   }
 }
 
-// Final (max, sum) per (KV head, row): the blocks merged in block order.
-__global__ __launch_bounds__(256) void calib_stats_merge_kernel(ContribArgs a) {
-  const int h = blockIdx.y;
-  const int r = blockIdx.x * 256 + threadIdx.x;
-  if (r >= a.rows) return;
+// Final (max, sum) per (KV head, row).  One wavefront per row: lane l merges
+// blocks l, l + 64, ... in order, then a fixed butterfly merges the lanes.
+__global__ __launch_bounds__(64) void calib_stats_merge_kernel(ContribArgs a) {
+  const int r = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
   double m = -INFINITY, l = 0.0;
-  for (int b = 0; b < a.nblk; ++b) {
+  for (int b = lane; b < a.nblk; b += 64) {
     const double* p = a.part + ((static_cast<size_t>(h) * a.nblk + b) * a.rows + r) * 2;
     merge_ms(m, l, p[0], p[1]);
   }
-  a.stats[(static_cast<size_t>(h) * a.rows + r) * 2] = m;
-  a.stats[(static_cast<size_t>(h) * a.rows + r) * 2 + 1] = l;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const double m2 = __shfl_xor(m, off, 64);
+    const double l2 = __shfl_xor(l, off, 64);
+    merge_ms(m, l, m2, l2);
+  }
+  if (lane == 0) {
+    a.stats[(static_cast<size_t>(h) * a.rows + r) * 2] = m;
+    a.stats[(static_cast<size_t>(h) * a.rows + r) * 2 + 1] = l;
+  }
 }
 
 // w[h][t] = (1 / rows) sum_r exp(s_rt - m_r) / l_r, rows in order.
@@ -183,10 +190,11 @@ struct CovArgs {
   const double* weights;    // [hkv][n]
   double* cov;              // [hkv][3][D][D]
   double* wsum;             // [hkv][3]
-  double* part_mean;        // [S][hkv][3][D + 1]: sum w v (D entries), then sum w
+  double* part_mean;        // [mean_splits][hkv][3][D + 1]: sum w v (D entries), then sum w
   double* mean;             // [hkv][3][D]
   double* part_cov;         // [S][hkv][3][D][D]
-  int32_t n, hkv, splits, split_tokens;
+  int32_t n, hkv, splits, split_tokens;   // covariance tiles' token splits
+  int32_t mean_splits, mean_split_tokens;  // weighted-mean pass's token splits
 };
 
 // Partial weighted sums of one (split, KV head): thread = (phase, channel);
@@ -196,17 +204,28 @@ __global__ __launch_bounds__(256) void calib_mean_part_kernel(CovArgs a) {
   constexpr int P = 256 / D;
   __shared__ double s_wv[P][kCalibModalities][D];
   __shared__ double s_w[P][kCalibModalities];
+  constexpr int U = 4;   // tokens whose loads are issued together
   const int s = blockIdx.x, h = blockIdx.y;
   const int ph = threadIdx.x / D, c = threadIdx.x % D;
-  const int t0 = s * a.split_tokens, t1 = min(a.n, t0 + a.split_tokens);
+  const int t0 = s * a.mean_split_tokens, t1 = min(a.n, t0 + a.mean_split_tokens);
   double wv[kCalibModalities] = {0.0, 0.0, 0.0}, ws[kCalibModalities] = {0.0, 0.0, 0.0};
-  for (int t = t0 + ph; t < t1; t += P) {
-    const int m = a.modality[t];
-    const double w = a.weights[static_cast<size_t>(h) * a.n + t];
-    const double x = load_input<VB>(a.v, (static_cast<size_t>(t) * a.hkv + h) * D + c);
-    if (m == 0) { wv[0] = __builtin_fma(w, x, wv[0]); ws[0] += w; }
-    else if (m == 1) { wv[1] = __builtin_fma(w, x, wv[1]); ws[1] += w; }
-    else if (m == 2) { wv[2] = __builtin_fma(w, x, wv[2]); ws[2] += w; }
+  for (int tb = t0 + ph; tb < t1; tb += U * P) {
+    int md[U];
+    double wt[U], x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = tb + u * P;
+      const bool in = t < t1;
+      md[u] = in ? a.modality[t] : 3;
+      wt[u] = in ? a.weights[static_cast<size_t>(h) * a.n + t] : 0.0;
+      x[u] = in ? load_input<VB>(a.v, (static_cast<size_t>(t) * a.hkv + h) * D + c) : 0.0;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {   // tokens in increasing order
+      if (md[u] == 0) { wv[0] = __builtin_fma(wt[u], x[u], wv[0]); ws[0] += wt[u]; }
+      else if (md[u] == 1) { wv[1] = __builtin_fma(wt[u], x[u], wv[1]); ws[1] += wt[u]; }
+      else if (md[u] == 2) { wv[2] = __builtin_fma(wt[u], x[u], wv[2]); ws[2] += wt[u]; }
+    }
   }
 #pragma unroll
   for (int m = 0; m < kCalibModalities; ++m) s_wv[ph][m][c] = wv[m];
@@ -237,11 +256,23 @@ __global__ __launch_bounds__(256) void calib_mean_merge_kernel(CovArgs a) {
   if (e >= a.hkv * kCalibModalities * D) return;
   const int c = e % D, hm = e / D;
   const int h = hm / kCalibModalities, m = hm % kCalibModalities;
+  constexpr int U = 8;   // splits whose partial sums are loaded together
+  const size_t stride = static_cast<size_t>(a.hkv) * kCalibModalities * (D + 1);
+  const double* p0 = a.part_mean + (static_cast<size_t>(h) * kCalibModalities + m) * (D + 1);
   double sx = 0.0, sw = 0.0;
-  for (int s = 0; s < a.splits; ++s) {
-    const double* p = a.part_mean + ((static_cast<size_t>(s) * a.hkv + h) * kCalibModalities + m) * (D + 1);
-    sx += p[c];
-    sw += p[D];
+  for (int s0 = 0; s0 < a.mean_splits; s0 += U) {
+    double x[U], w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool in = s0 + u < a.mean_splits;
+      x[u] = in ? p0[(s0 + u) * stride + c] : 0.0;
+      w[u] = in ? p0[(s0 + u) * stride + D] : 0.0;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {   // splits in increasing order
+      sx += x[u];
+      sw += w[u];
+    }
   }
   a.mean[static_cast<size_t>(hm) * D + c] = sw > 0.0 ? sx / sw : 0.0;
   if (c == 0) a.wsum[hm] = sw;
@@ -361,14 +392,32 @@ __global__ __launch_bounds__(256) void calib_cov_merge_kernel(CovArgs a) {
 // "Matrix Computations", Sec. 8.5: the symmetric Schur 2 x 2 rotation and
 // the parallel ordering).  Each sweep visits every pair (p, q) once through
 // D - 1 rounds of D / 2 disjoint pairs (round-robin ordering: player 0
-// fixed, the others rotated).  A round forms its rotations from the current
-// matrix, then applies J^T A J one 2 x 2 block at a time (blocks (ki, kj) and
-// (kj, ki) from one task, so A stays exactly symmetric) and V <- V J (rows of
-// W = V^T, kept in the workspace).  A pair whose off-diagonal entry is
-// negligible against its diagonal is set to zero without a rotation; the
-// sweeps end when one rotates nothing (at most kJacobiSweeps).
+// fixed, the others rotated).
+//
+// Phase 1 rotates A alone, in LDS: a round forms its rotations from the
+// current matrix, then applies J^T A J one 2 x 2 block at a time (blocks
+// (ki, kj) and (kj, ki) from one task, so A stays exactly symmetric).  A pair
+// whose off-diagonal entry is negligible (against its diagonal, or below
+// the rounding noise of the whole matrix) is set to zero without a rotation;
+// the sweeps end when one rotates nothing (at most kJacobiSweeps).  Each
+// round's tangents t go to a log in the workspace.
+// Phase 2 replays the log on V = I (V^T kept in LDS where A was):
+// V <- V J round by round, c and s recomputed from t with the same
+// operations as in phase 1, so they are the same numbers.
 template <int D>
-constexpr int jacobi_threads() { return D == 128 ? 1024 : 256; }
+constexpr int jacobi_threads() { return D == 128 ? 512 : 256; }
+
+// Pair k of round r of the round-robin ordering, as (p, q) with p < q.
+template <int D>
+__device__ __forceinline__ void jacobi_pair(int r, int k, int& p, int& q) {
+  const int x = k == 0 ? 0 : 1 + (k - 1 + r) % (D - 1);
+  const int y = 1 + (D - 2 - k + r) % (D - 1);
+  p = min(x, y);
+  q = max(x, y);
+}
+
+// Barrier for LDS traffic only: the log's global stores stay in flight.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <int D>
 __global__ __launch_bounds__(jacobi_threads<D>()) void calib_jacobi_kernel(const double* cov, float* rot,
@@ -376,20 +425,38 @@ __global__ __launch_bounds__(jacobi_threads<D>()) void calib_jacobi_kernel(const
   constexpr int NP = D / 2;
   constexpr int LD = D + 1;
   constexpr int NT = jacobi_threads<D>();
+  constexpr int NAT = NP * NP / NT;   // 2 x 2 block tasks per thread (those with ki > kj idle)
+  constexpr int NWT = NP * D / NT;    // (pair, column) tasks of V^T per thread
+  static_assert(NWT * NT == NP * D && NAT * NT == NP * NP && NT >= D && D % NWT == 0, "tasks divide evenly");
   constexpr double kNegligible = 0x1p-53;   // |a_pq| <= 2^-53 sqrt(|a_pp a_qq|): already diagonal to rounding
-  __shared__ double A[D * LD];
-  __shared__ double s_c[NP], s_s[NP], s_t[NP];
-  __shared__ int s_p[NP], s_q[NP];
+  __shared__ double A[D * LD];             // phase 1: A; phase 2: V^T (row j = column j of V)
+  __shared__ double s_c[2][NP], s_s[2][NP], s_t[NP];
+  __shared__ int s_p[2][NP], s_q[2][NP];
   __shared__ int s_changed;
   __shared__ double s_lam[D];
+  __shared__ double s_sq[NT];
   const int mat = blockIdx.x, tid = threadIdx.x;
   const double* C = cov + static_cast<size_t>(mat) * D * D;
-  double* W = work + static_cast<size_t>(mat) * D * D;
+  double* log = work + static_cast<size_t>(mat) * kJacobiSweeps * (D - 1) * NP;
+  double sq = 0.0;
   for (int e = tid; e < D * D; e += NT) {
     const int i = e / D, j = e % D;
-    A[i * LD + j] = i <= j ? C[static_cast<size_t>(i) * D + j] : C[static_cast<size_t>(j) * D + i];
-    W[e] = i == j ? 1.0 : 0.0;
+    const double x = i <= j ? C[static_cast<size_t>(i) * D + j] : C[static_cast<size_t>(j) * D + i];
+    A[i * LD + j] = x;
+    sq = __builtin_fma(x, x, sq);
   }
+  // |A|_F^2 by a fixed tree: a rotation leaves rounding noise of order
+  // 2^-53 |A|_F off the diagonal, so entries below 2^-51 |A|_F are left alone
+  s_sq[tid] = sq;
+  __syncthreads();
+  for (int st = NT / 2; st > 0; st >>= 1) {
+    if (tid < st) s_sq[tid] += s_sq[tid + st];
+    __syncthreads();
+  }
+  const double floor_abs = 0x1p-51 * sqrt(s_sq[0]);
+
+  // ---- phase 1: A <- J^T A J until a sweep rotates nothing
+  int sweeps = 0;
   for (int sweep = 0; sweep < kJacobiSweeps; ++sweep) {
     __syncthreads();
     if (tid == 0) s_changed = 0;
@@ -397,45 +464,57 @@ __global__ __launch_bounds__(jacobi_threads<D>()) void calib_jacobi_kernel(const
     for (int r = 0; r < D - 1; ++r) {
       if (tid < NP) {
         const int k = tid;
-        const int x = k == 0 ? 0 : 1 + (k - 1 + r) % (D - 1);
-        const int y = 1 + (D - 2 - k + r) % (D - 1);
-        const int p = min(x, y), q = max(x, y);
+        int p, q;
+        jacobi_pair<D>(r, k, p, q);
         const double app = A[p * LD + p], aqq = A[q * LD + q], apq = A[p * LD + q];
-        double c = 1.0, s = 0.0, t = 0.0;
-        if (fabs(apq) > kNegligible * sqrt(fabs(app) * fabs(aqq))) {
+        double t = 0.0;
+        if (fabs(apq) > kNegligible * sqrt(fabs(app) * fabs(aqq)) && fabs(apq) > floor_abs) {
           const double theta = (aqq - app) / (2.0 * apq);
           if (fabs(theta) > 1e100) {
             t = 0.5 / theta;
           } else {
             t = (theta >= 0.0 ? 1.0 : -1.0) / (fabs(theta) + sqrt(1.0 + theta * theta));
           }
-          c = 1.0 / sqrt(1.0 + t * t);
-          s = t * c;
           s_changed = 1;
         }
-        s_p[k] = p;
-        s_q[k] = q;
-        s_c[k] = c;
-        s_s[k] = s;
+        const double c = 1.0 / sqrt(1.0 + t * t);
+        s_p[0][k] = p;
+        s_q[0][k] = q;
+        s_c[0][k] = c;
+        s_s[0][k] = t * c;
         s_t[k] = t;
+        log[(static_cast<size_t>(sweep) * (D - 1) + r) * NP + k] = t;
       }
-      __syncthreads();
-      for (int e = tid; e < NP * NP; e += NT) {
-        const int ki = e / NP, kj = e % NP;
+      lds_barrier();
+      // this round's tasks touch disjoint entries: all loads, then all stores
+      double blk[NAT][4];
+#pragma unroll
+      for (int u = 0; u < NAT; ++u) {
+        const int e = tid + u * NT, ki = e / NP, kj = e % NP;
+        const int pi = s_p[0][ki], qi = s_q[0][ki], pj = s_p[0][kj], qj = s_q[0][kj];
+        if (ki <= kj) {
+          blk[u][0] = A[pi * LD + pj];
+          blk[u][1] = A[pi * LD + qj];
+          blk[u][2] = A[qi * LD + pj];
+          blk[u][3] = A[qi * LD + qj];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < NAT; ++u) {
+        const int e = tid + u * NT, ki = e / NP, kj = e % NP;
         if (ki > kj) continue;
-        const int pi = s_p[ki], qi = s_q[ki], pj = s_p[kj], qj = s_q[kj];
+        const int pi = s_p[0][ki], qi = s_q[0][ki], pj = s_p[0][kj], qj = s_q[0][kj];
+        const double a_pp = blk[u][0], a_pq = blk[u][1], a_qp = blk[u][2], a_qq = blk[u][3];
         if (ki == kj) {
-          const double app = A[pi * LD + pi], aqq = A[qi * LD + qi], apq = A[pi * LD + qi];
+          // the rotated pair itself: exact zero off the diagonal
           const double t = s_t[ki];
-          A[pi * LD + pi] = app - t * apq;
-          A[qi * LD + qi] = aqq + t * apq;
+          A[pi * LD + pi] = a_pp - t * a_pq;
+          A[qi * LD + qi] = a_qq + t * a_pq;
           A[pi * LD + qi] = 0.0;
           A[qi * LD + pi] = 0.0;
           continue;
         }
-        const double ci = s_c[ki], si = s_s[ki], cj = s_c[kj], sj = s_s[kj];
-        const double a_pp = A[pi * LD + pj], a_pq = A[pi * LD + qj];
-        const double a_qp = A[qi * LD + pj], a_qq = A[qi * LD + qj];
+        const double ci = s_c[0][ki], si = s_s[0][ki], cj = s_c[0][kj], sj = s_s[0][kj];
         // rows (J_i^T from the left), then columns (J_j from the right)
         const double r_pp = ci * a_pp - si * a_qp, r_pq = ci * a_pq - si * a_qq;
         const double r_qp = si * a_pp + ci * a_qp, r_qq = si * a_pq + ci * a_qq;
@@ -450,20 +529,53 @@ __global__ __launch_bounds__(jacobi_threads<D>()) void calib_jacobi_kernel(const
         A[qi * LD + qj] = n_qq;
         A[qj * LD + qi] = n_qq;
       }
-      for (int e = tid; e < NP * D; e += NT) {
-        const int k = e / D, i = e % D;
-        const int p = s_p[k], q = s_q[k];
-        const double c = s_c[k], s = s_s[k];
-        const double x = W[static_cast<size_t>(p) * D + i], y = W[static_cast<size_t>(q) * D + i];
-        W[static_cast<size_t>(p) * D + i] = c * x - s * y;
-        W[static_cast<size_t>(q) * D + i] = s * x + c * y;
-      }
-      __syncthreads();
+      lds_barrier();
     }
+    sweeps = sweep + 1;
     if (!s_changed) break;
   }
-  __syncthreads();
+  __syncthreads();   // the log is complete and visible to the workgroup
   if (tid < D) s_lam[tid] = A[tid * LD + tid];
+  __syncthreads();
+
+  // ---- phase 2: V^T <- J^T V^T, replayed from the log, starting from I
+  for (int e = tid; e < D * D; e += NT) A[(e / D) * LD + e % D] = (e / D == e % D) ? 1.0 : 0.0;
+  for (int sweep = 0; sweep < sweeps; ++sweep) {
+    for (int r = 0; r < D - 1; ++r) {
+      // parameter buffers alternate with the round count (D - 1 rounds per
+      // sweep is odd, so not with r): one barrier per round suffices
+      const int b = (sweep * (D - 1) + r) & 1;
+      if (tid < NP) {
+        const int k = tid;
+        int p, q;
+        jacobi_pair<D>(r, k, p, q);
+        const double t = log[(static_cast<size_t>(sweep) * (D - 1) + r) * NP + k];
+        const double c = 1.0 / sqrt(1.0 + t * t);
+        s_p[b][k] = p;
+        s_q[b][k] = q;
+        s_c[b][k] = c;
+        s_s[b][k] = t * c;
+      }
+      __syncthreads();
+      // thread = one pair, columns i0, i0 + D / NWT, ...: the pair's
+      // parameters are read once per round
+      constexpr int CS = D / NWT;                 // column stride
+      const int k = tid / CS, i0 = tid % CS;
+      const int rp = s_p[b][k] * LD, rq = s_q[b][k] * LD;
+      const double c = s_c[b][k], sn = s_s[b][k];
+      double wx[NWT], wy[NWT];
+#pragma unroll
+      for (int u = 0; u < NWT; ++u) {
+        wx[u] = A[rp + i0 + u * CS];
+        wy[u] = A[rq + i0 + u * CS];
+      }
+#pragma unroll
+      for (int u = 0; u < NWT; ++u) {
+        A[rp + i0 + u * CS] = c * wx[u] - sn * wy[u];
+        A[rq + i0 + u * CS] = sn * wx[u] + c * wy[u];
+      }
+    }
+  }
   __syncthreads();
   if (tid < D) {
     const double lam = s_lam[tid];
@@ -472,7 +584,7 @@ __global__ __launch_bounds__(jacobi_threads<D>()) void calib_jacobi_kernel(const
       const double lk = s_lam[k];
       rank += (lk > lam || (lk == lam && k < tid)) ? 1 : 0;
     }
-    const double* wr = W + static_cast<size_t>(tid) * D;
+    const double* wr = &A[tid * LD];
     int best = 0;
     double bv = fabs(wr[0]);
     for (int i = 1; i < D; ++i) {
@@ -493,7 +605,8 @@ __global__ __launch_bounds__(jacobi_threads<D>()) void calib_jacobi_kernel(const
 
 struct CalibPlan {
   int rows, nblk;          // contribution
-  int splits, split_tokens;  // covariance
+  int splits, split_tokens;  // covariance tiles
+  int mean_splits, mean_split_tokens;  // weighted means: 1024 tokens per split
   size_t contrib_bytes, cov_bytes, eig_bytes;
 };
 
@@ -528,20 +641,22 @@ CalibPlan plan_calib(const kvq_calib_shape* s) {
   splits = std::max(1, (n + per - 1) / per);
   p.splits = splits;
   p.split_tokens = per;
-  p.cov_bytes = align256(static_cast<size_t>(splits) * hkv * kCalibModalities * (d + 1) * sizeof(double)) +
+  p.mean_split_tokens = 1024;
+  p.mean_splits = std::max(1, (n + 1023) / 1024);
+  p.cov_bytes = align256(static_cast<size_t>(p.mean_splits) * hkv * kCalibModalities * (d + 1) * sizeof(double)) +
                 align256(static_cast<size_t>(hkv) * kCalibModalities * d * sizeof(double)) +
                 align256(static_cast<size_t>(splits) * hkv * kCalibModalities * d * d * sizeof(double));
-  p.eig_bytes = static_cast<size_t>(3) * hkv * d * d * sizeof(double);
+  p.eig_bytes = static_cast<size_t>(3) * hkv * kJacobiSweeps * (d - 1) * (d / 2) * sizeof(double);
   return p;
 }
 
 template <int D>
 void launch_contribution(const ContribArgs& a, bool kb, bool qb, hipStream_t st) {
-  const dim3 gb(a.nblk, a.hkv), gm((a.rows + 255) / 256, a.hkv);
+  const dim3 gb(a.nblk, a.hkv), gm(a.rows, a.hkv);
 #define KVQ_CONTRIB(KB, QB)                                                                    \
   do {                                                                                         \
     hipLaunchKernelGGL((calib_block_stats_kernel<D, KB, QB>), gb, dim3(kTokBlock), 0, st, a); \
-    hipLaunchKernelGGL(calib_stats_merge_kernel, gm, dim3(256), 0, st, a);                     \
+    hipLaunchKernelGGL(calib_stats_merge_kernel, gm, dim3(64), 0, st, a);                      \
     hipLaunchKernelGGL((calib_weights_kernel<D, KB, QB>), gb, dim3(kTokBlock), 0, st, a);     \
   } while (0)
   if (kb && qb) KVQ_CONTRIB(true, true);
@@ -554,7 +669,7 @@ void launch_contribution(const ContribArgs& a, bool kb, bool qb, hipStream_t st)
 template <int D>
 void launch_covariance(const CovArgs& a, bool vb, hipStream_t st) {
   constexpr int NB = D / kTile;
-  const dim3 gpart(a.splits, a.hkv);
+  const dim3 gpart(a.mean_splits, a.hkv);
   const dim3 gmm((a.hkv * kCalibModalities * D + 255) / 256);
   const dim3 gtile(NB * (NB + 1) / 2, a.splits, a.hkv);
   const size_t ncov = static_cast<size_t>(a.hkv) * kCalibModalities * D * D;
@@ -586,7 +701,8 @@ size_t kvq_calib_workspace_bytes(const kvq_calib_shape* shape) {
 
 size_t kvq_calib_eigenbasis_workspace_bytes(int32_t count, int32_t head_dim) {
   if (count < 0 || (head_dim != 64 && head_dim != 128)) return 0;
-  return static_cast<size_t>(count) * head_dim * head_dim * sizeof(double);
+  // the rotation log: one tangent per (sweep, round, pair)
+  return static_cast<size_t>(count) * kJacobiSweeps * (head_dim - 1) * (head_dim / 2) * sizeof(double);
 }
 
 kvq_status kvq_calib_contribution(const kvq_calib_shape* shape, const void* k, int32_t k_dtype, const void* q,
@@ -640,7 +756,7 @@ kvq_status kvq_calib_covariance(const kvq_calib_shape* shape, const void* v, int
   a.wsum = weight_sum;
   char* w = static_cast<char*>(workspace);
   a.part_mean = reinterpret_cast<double*>(w);
-  w += align256(static_cast<size_t>(p.splits) * hkv * kCalibModalities * (d + 1) * sizeof(double));
+  w += align256(static_cast<size_t>(p.mean_splits) * hkv * kCalibModalities * (d + 1) * sizeof(double));
   a.mean = reinterpret_cast<double*>(w);
   w += align256(static_cast<size_t>(hkv) * kCalibModalities * d * sizeof(double));
   a.part_cov = reinterpret_cast<double*>(w);
@@ -648,6 +764,8 @@ kvq_status kvq_calib_covariance(const kvq_calib_shape* shape, const void* v, int
   a.hkv = hkv;
   a.splits = p.splits;
   a.split_tokens = p.split_tokens;
+  a.mean_splits = p.mean_splits;
+  a.mean_split_tokens = p.mean_split_tokens;
   (void)hipGetLastError();
   if (d == 128) launch_covariance<128>(a, v_dtype == KVQ_BF16, stream);
   else launch_covariance<64>(a, v_dtype == KVQ_BF16, stream);

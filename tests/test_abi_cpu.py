@@ -170,7 +170,8 @@ def test_calibration_rejects_bad_arguments_without_launching():
         return L.KvqCalibShape(*[f[name] for name, _ in L.KvqCalibShape._fields_])
     good = shape()
     need = lib.kvq_calib_workspace_bytes(ctypes.byref(good))
-    assert need >= lib.kvq_calib_eigenbasis_workspace_bytes(6, 128) == 6 * 128 * 128 * 8
+    eig_need = 6 * 50 * 127 * 64 * 8          # the Jacobi rotation log: (sweep, round, pair) tangents
+    assert need >= lib.kvq_calib_eigenbasis_workspace_bytes(6, 128) == eig_need
     assert lib.kvq_calib_workspace_bytes(ctypes.byref(shape(head_dim=96))) == 0
     assert lib.kvq_calib_eigenbasis_workspace_bytes(-1, 128) == 0
     for kw, status in [(dict(head_dim=96), 2), (dict(n_q_heads=15), 1), (dict(n_tokens=-1), 1),
@@ -199,5 +200,5 @@ def test_calibration_rejects_bad_arguments_without_launching():
     assert eig(count=-1) == L.KVQ_ERR_INVALID
     assert eig(d=32) == L.KVQ_ERR_UNSUPPORTED
     assert eig(r=None) == L.KVQ_ERR_INVALID
-    assert eig(nbytes=6 * 128 * 128 * 8 - 1) == L.KVQ_ERR_WORKSPACE
+    assert eig(nbytes=eig_need - 1) == L.KVQ_ERR_WORKSPACE
     assert eig(count=0, c=None, r=None, e=None) == L.KVQ_OK                       # nothing to do
