@@ -39,6 +39,16 @@ Readings where the pages are silent (each repeated in the design notes):
   * Sparse page sets (a retained-page list or mask, as in the survey's paging
     follow-on): positions outside the retained set are left out before the
     softmax, exactly as if they had never been cached.
+  * TurboQuant baseline (Sec. 2 Method, TurboQuant bullet; Sec. 1 Problem
+    bullet: one fixed scale per token rather than local ranges): a key is
+    coded like a value, with the randomized Hadamard as its rotation:
+    n = ||k||, z = sqrt(d) H_d (s * k) / sqrt(d) / n, nearest level, fp16(n);
+    values use the same randomized Hadamard for every modality.
+  * Key-grouping harness (Sec. 3, "Key Adaptation" bullet): the 32-token
+    min-max groups are formed over the stream taken in a given order
+    (temporal; modality-only, i.e. sorted by modality keeping time order;
+    shuffled within each modality; shuffled globally), and the relative
+    squared error of the reconstructed rotated keys is reported.
 """
 from __future__ import annotations
 
@@ -303,3 +313,111 @@ def quantize_session(k: np.ndarray, v: np.ndarray, modality: np.ndarray,
         vc, nrm = quantize_values(v[:, h], modality, rot[h], codebook)
         out.append(dict(k_codes=kc, lo=lo, hi=hi, v_codes=vc, norms=nrm, modality=modality))
     return out
+
+
+# ------------------------------------------------------ TurboQuant baseline
+
+def quantize_keys_per_token(k: np.ndarray, signs: np.ndarray, codebook) -> tuple:
+    """TurboQuant key codec for one KV head (Sec. 2 Method, TurboQuant bullet):
+    magnitude n = ||k|| apart, direction rotated by the randomized Hadamard,
+    z = sqrt(d) y / n on the fixed codebook.  k: [L, d] float64.  Returns
+    codes [L, d] uint8 and norms [L] float16; n == 0 gives codes 0."""
+    L, d = k.shape
+    y = randomized_hadamard(k, signs)
+    n = np.sqrt(np.sum(np.asarray(k, np.float64) ** 2, axis=1))
+    codes = np.zeros((L, d), np.uint8)
+    ok = n > 0
+    codes[ok] = nearest_level(np.sqrt(d) * y[ok] / n[ok][:, None], codebook)
+    return codes, n.astype(np.float16)
+
+
+def key_per_token_normalized_values(k: np.ndarray, signs: np.ndarray) -> np.ndarray:
+    """The fp64 value z each per-token key code is decided on (NaN for n == 0)."""
+    d = k.shape[1]
+    y = randomized_hadamard(k, signs)
+    n = np.sqrt(np.sum(np.asarray(k, np.float64) ** 2, axis=1))
+    with np.errstate(divide="ignore", invalid="ignore"):
+        z = np.sqrt(d) * y / n[:, None]
+    z[n == 0] = np.nan
+    return z
+
+
+def dequantize_keys_per_token(codes: np.ndarray, norms16: np.ndarray, codebook) -> np.ndarray:
+    """Rotated-domain reconstruction y_hat = (N / sqrt(d)) c[code]."""
+    return dequantize_values_rotated(codes, norms16, codebook)
+
+
+def hadamard_value_basis(signs: np.ndarray) -> np.ndarray:
+    """R [d, d] with R^T v = H_d (s * v) / sqrt(d): the shared randomized
+    Hadamard of TurboQuant written as a value basis (columns = basis)."""
+    d = len(signs)
+    # row i of the transform of the identity is s_i H_d[:, i] / sqrt(d): the
+    # matrix D H_d / sqrt(d), whose columns give v @ R = H_d (s * v) / sqrt(d)
+    return randomized_hadamard(np.eye(d), signs)
+
+
+def decode_attention_head_per_token_keys(q_rot, k_codes, k_norms16, v_codes, norms16, modality, rot,
+                                         codebook, scale: float, retained=None) -> np.ndarray:
+    """decode_attention_head with TurboQuant keys: k_hat_t = (N_t / sqrt(d)) c[code]
+    in the rotated domain; values and the softmax as before."""
+    L = k_codes.shape[0]
+    d = q_rot.shape[-1]
+    keep = np.ones(L, bool) if retained is None else np.asarray(retained, bool)[:L]
+    if L == 0 or not keep.any():
+        return np.zeros(d)
+    k_hat = dequantize_keys_per_token(k_codes, k_norms16, codebook)
+    s = scale * (k_hat @ q_rot)
+    p = np.zeros(L)
+    p[keep] = np.exp(s[keep] - s[keep].max())
+    p = p / p.sum()
+    v_t = dequantize_values_rotated(v_codes, norms16, codebook)
+    R = np.asarray(rot, np.float32).astype(np.float64)
+    o = np.zeros(d)
+    for m in range(N_MODALITIES):
+        idx = (modality == m) & keep
+        if idx.any():
+            o += R[m] @ (p[idx] @ v_t[idx])
+    return o
+
+
+# ----------------------------------------------------- key-grouping harness
+
+GROUP_ORDERS = ("temporal", "modality", "modality_shuffled", "shuffled")
+
+
+def grouping_order(modality: np.ndarray, order: str, seed: int = 0) -> np.ndarray:
+    """Token order in which the 32-token key groups are formed.
+    temporal: stream order; modality: all tokens of modality 0, then 1, then
+    2, each in stream order; modality_shuffled: the same blocks, each in a
+    random order; shuffled: one random order over the whole stream."""
+    L = len(modality)
+    rng = np.random.default_rng(seed)
+    if order == "temporal":
+        return np.arange(L)
+    if order == "modality":
+        return np.argsort(modality, kind="stable")
+    if order == "modality_shuffled":
+        return np.concatenate([rng.permutation(np.flatnonzero(modality == m)) for m in range(N_MODALITIES)])
+    if order == "shuffled":
+        return rng.permutation(L)
+    raise ValueError(order)
+
+
+def key_grouping_error(k: np.ndarray, modality: np.ndarray, signs: np.ndarray, codebook,
+                       order: str, seed: int = 0) -> float:
+    """Relative squared error sum ||y - y_hat||^2 / sum ||y||^2 of one KV
+    head's rotated keys when the min-max groups are formed in `order`."""
+    perm = grouping_order(modality, order, seed)
+    kp = np.asarray(k, np.float64)[perm]
+    codes, lo, hi = quantize_keys(kp, signs, codebook)
+    y = randomized_hadamard(kp, signs)
+    y_hat = dequantize_keys(codes, lo, hi, codebook)
+    return float(((y - y_hat) ** 2).sum() / (y ** 2).sum())
+
+
+def per_token_key_error(k: np.ndarray, signs: np.ndarray, codebook) -> float:
+    """The same relative error for TurboQuant's per-token key codec."""
+    codes, norms = quantize_keys_per_token(k, signs, codebook)
+    y = randomized_hadamard(k, signs)
+    y_hat = dequantize_keys_per_token(codes, norms, codebook)
+    return float(((y - y_hat) ** 2).sum() / (y ** 2).sum())

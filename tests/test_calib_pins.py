@@ -269,7 +269,7 @@ def test_error_harness_matches_the_quantizer_distortion():
     for d, n in ((64, 4000), (128, 2000)):
         v = rng.standard_normal((n, d))
         signs = np.where(rng.random(d) < 0.5, -1.0, 1.0)
-        H = O.randomized_hadamard(np.eye(d), signs).T      # columns: r = v @ H = H_d (s * v) / sqrt(d)
+        H = O.hadamard_value_basis(signs)                  # r = v @ H = H_d (s * v) / sqrt(d)
         R = np.linalg.qr(rng.standard_normal((d, d)))[0]
         rot = np.stack([H, R, H]).astype(np.float32)
         mod = np.repeat(np.array([0, 1], np.uint8), [n // 2, n - n // 2])

@@ -211,3 +211,56 @@ def test_planted_calibration_mistake_is_caught(monkeypatch, name, mutant, pins):
     monkeypatch.setattr(CO, name, mutant)
     for pin, *args in pins:
         assert _fails(pin, *args), f"{pin.__name__} did not notice {mutant.__name__}"
+
+
+# ------------------------------------------- TurboQuant baseline and harness
+
+import tests.test_turbo_pins as TP  # noqa: E402
+
+_orig_qkt = O.quantize_keys_per_token
+_orig_hvb = O.hadamard_value_basis
+_orig_dkt = O.dequantize_keys_per_token
+_orig_go = O.grouping_order
+
+
+def _per_token_keys_without_sqrt_d(k, signs, codebook):
+    L, d = k.shape
+    y = O.randomized_hadamard(k, signs)
+    n = np.sqrt(np.sum(np.asarray(k, np.float64) ** 2, axis=1))
+    codes = np.zeros((L, d), np.uint8)
+    ok = n > 0
+    codes[ok] = O.nearest_level(y[ok] / n[ok][:, None], codebook)
+    return codes, n.astype(np.float16)
+
+
+def _hadamard_basis_transposed(signs):
+    return _orig_hvb(signs).T
+
+
+def _per_token_dequant_drops_norm(codes, norms16, codebook):
+    return _orig_dkt(codes, np.ones_like(norms16), codebook)
+
+
+def _modality_order_loses_time(modality, order, seed=0):
+    """Modality blocks, but each in reverse stream order."""
+    if order == "modality":
+        return np.lexsort((-np.arange(len(modality)), modality))
+    return _orig_go(modality, order, seed)
+
+
+TURBO_MUTANTS = [
+    ("quantize_keys_per_token", _per_token_keys_without_sqrt_d,
+     [(TP.test_per_token_key_codes_and_norms,), (TP.test_per_token_keys_reach_the_quantizer_distortion, 64)]),
+    ("hadamard_value_basis", _hadamard_basis_transposed, [(TP.test_hadamard_value_basis_is_the_randomized_hadamard,)]),
+    ("dequantize_keys_per_token", _per_token_dequant_drops_norm,
+     [(TP.test_per_token_keys_reach_the_quantizer_distortion, 128)]),
+    ("grouping_order", _modality_order_loses_time,
+     [(TP.test_grouping_orders_are_permutations_with_the_stated_structure,)]),
+]
+
+
+@pytest.mark.parametrize("name,mutant,pins", TURBO_MUTANTS, ids=[m[1].__name__ for m in TURBO_MUTANTS])
+def test_planted_baseline_mistake_is_caught(monkeypatch, name, mutant, pins):
+    monkeypatch.setattr(O, name, mutant)
+    for pin, *args in pins:
+        assert _fails(pin, *args), f"{pin.__name__} did not notice {mutant.__name__}"
