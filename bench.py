@@ -248,6 +248,8 @@ def main():
     del sbufs, cdst
 
     calib = time_calibration(L0)
+    del g_step, g_dec, g_warm
+    turbo = time_turboquant_decode(w, table, L0, args.replicas, n_dec, scale)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -275,9 +277,61 @@ def main():
                   "decode_us_half_pages_retained": half_ms * 1e3,
                   "copy_read_write_GBps": copy_bytes / (copy_ms * 1e-3) / 1e9,
                   "step_wall_us": wall / steps * 1e6,
-                  "value_calibration": calib},
+                  "value_calibration": calib,
+                  "turboquant_baseline": turbo},
     }
     print(json.dumps(rec), flush=True)
+
+
+def time_turboquant_decode(w, table, L0: int, replicas: int, n_dec: int, scale: float) -> dict:
+    """The TurboQuant baseline through the same kernels: per-token key norms
+    instead of group statistics, the shared randomized Hadamard as every
+    value basis; the same 80K context on `replicas` HBM-resident caches,
+    decode launches only, HIP events on the launch stream."""
+    import torch
+    import decode_attention_kvq_amd as K
+    from tests import kvq_harness as H
+
+    dev = torch.device("cuda", 0)
+    cfg, params, c0 = H.build(w, page_table=table, upto=[L0], key_mode=K.KVQ_KEYS_PER_TOKEN,
+                              rot=H.hadamard_rot(w))
+    caches = [c0]
+    for _ in range(replicas - 1):
+        cc = K.Cache(cfg, torch.from_numpy(table), device=dev)
+        for name in ("k_codes", "k_stats", "v_codes", "v_norms", "modality", "k_tail", "seq_len"):
+            getattr(cc, name).copy_(getattr(c0, name))
+        cc.set_lengths(c0.lengths())
+        caches.append(cc)
+    q_rot = K.kvq_rotate_query(cfg, params, H.query_tensor(w, dev))
+    out = torch.empty(q_rot.shape, dtype=torch.float32, device=dev)
+    ws = torch.empty(K.kvq_decode_workspace_bytes(cfg, L0), dtype=torch.uint8, device=dev)
+    for cc in caches:
+        K.kvq_decode_attention(cfg, cc, params, q_rot, scale, out, ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s_cap = torch.cuda.Stream()
+    s_cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s_cap):
+        with torch.cuda.graph(g, stream=s_cap):
+            for cc in caches:
+                K.kvq_decode_attention(cfg, cc, params, q_rot, scale, out, ws)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    g.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n_dec):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (n_dec * replicas)
+    d, hq, hkv = w.cfg.head_dim, w.cfg.n_q_heads, w.cfg.n_kv_heads
+    # per (position, KV head): key and value codes (d / 4 bytes each), two fp16 norms
+    nbytes = L0 * hkv * (d // 4 + d // 4 + 4) + L0 + hkv * 3 * d * d * 4 + 2 * hq * d * 4
+    del g, caches
+    return {"workload": "same 80K decode, per-token keys + shared Hadamard values",
+            "decode_us_hbm": ms * 1e3, "bytes_per_launch": nbytes,
+            "achieved_GBps": nbytes / (ms * 1e-3) / 1e9}
 
 
 def time_calibration(n_tokens: int, n_queries: int = 8, repeats: int = 5) -> dict:

@@ -15,7 +15,8 @@ from typing import Optional, Sequence
 import torch
 
 from . import _lib
-from ._lib import KVQ_BF16, KVQ_F32, KvqCache, KvqCalibShape, KvqConfig, KvqError, KvqParams  # noqa: F401
+from ._lib import (KVQ_BF16, KVQ_F32, KVQ_KEYS_GROUP_MINMAX, KVQ_KEYS_PER_TOKEN, KvqCache,  # noqa: F401
+                   KvqCalibShape, KvqConfig, KvqError, KvqParams)
 
 __all__ = ["Config", "Params", "Cache", "kvq_quantize_append", "kvq_rotate_query", "kvq_append_and_rotate",
            "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_calib_workspace_bytes",
@@ -41,15 +42,18 @@ def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
 
 
 class Config:
-    """Shapes of one packed cache (mirrors kvq_config)."""
+    """Shapes of one packed cache (mirrors kvq_config).  key_mode selects the
+    key codec: KVQ_KEYS_GROUP_MINMAX (OmniKVQuant) or KVQ_KEYS_PER_TOKEN (the
+    TurboQuant baseline)."""
 
     def __init__(self, head_dim: int, n_q_heads: int, n_kv_heads: int, batch: int,
-                 page_tokens: int, max_pages: int, num_pages: int, kv_dtype: torch.dtype):
+                 page_tokens: int, max_pages: int, num_pages: int, kv_dtype: torch.dtype,
+                 key_mode: int = KVQ_KEYS_GROUP_MINMAX):
         self.head_dim, self.n_q_heads, self.n_kv_heads = head_dim, n_q_heads, n_kv_heads
         self.batch, self.page_tokens, self.max_pages, self.num_pages = batch, page_tokens, max_pages, num_pages
-        self.kv_dtype = kv_dtype
+        self.kv_dtype, self.key_mode = kv_dtype, int(key_mode)
         self.struct = KvqConfig(head_dim, n_q_heads, n_kv_heads, batch, page_tokens, max_pages,
-                                num_pages, _DTYPES[kv_dtype])
+                                num_pages, _DTYPES[kv_dtype], self.key_mode)
 
     def buffer_bytes(self) -> list:
         out = (ctypes.c_size_t * 6)()

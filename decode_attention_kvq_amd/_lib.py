@@ -11,6 +11,7 @@ LIB_PATH = os.path.join(_PKG, "libkvq.so")
 
 KVQ_OK, KVQ_ERR_INVALID, KVQ_ERR_UNSUPPORTED, KVQ_ERR_CAPACITY, KVQ_ERR_WORKSPACE, KVQ_ERR_LAUNCH = range(6)
 KVQ_F32, KVQ_BF16 = 0, 1
+KVQ_KEYS_GROUP_MINMAX, KVQ_KEYS_PER_TOKEN = 0, 1
 
 EXPORTED = ("kvq_cache_buffer_bytes", "kvq_quantize_append", "kvq_rotate_query", "kvq_append_and_rotate",
             "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_status_string",
@@ -22,7 +23,8 @@ class KvqConfig(ctypes.Structure):
     _fields_ = [("head_dim", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
                 ("n_kv_heads", ctypes.c_int32), ("batch", ctypes.c_int32),
                 ("page_tokens", ctypes.c_int32), ("max_pages", ctypes.c_int32),
-                ("num_pages", ctypes.c_int32), ("kv_dtype", ctypes.c_int32)]
+                ("num_pages", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+                ("key_mode", ctypes.c_int32)]
 
 
 class KvqCache(ctypes.Structure):

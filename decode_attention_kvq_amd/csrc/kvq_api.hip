@@ -28,6 +28,7 @@ kvq_status check_config(const kvq_config* cfg) {
   if (cfg->max_pages <= 0 || cfg->num_pages <= 0) return KVQ_ERR_INVALID;
   if ((int64_t)cfg->max_pages * cfg->page_tokens > INT32_MAX) return KVQ_ERR_INVALID;
   if (cfg->kv_dtype != KVQ_F32 && cfg->kv_dtype != KVQ_BF16) return KVQ_ERR_UNSUPPORTED;
+  if (cfg->key_mode != KVQ_KEYS_GROUP_MINMAX && cfg->key_mode != KVQ_KEYS_PER_TOKEN) return KVQ_ERR_INVALID;
   return KVQ_OK;
 }
 
@@ -183,6 +184,7 @@ static kvq_status prepare_append(const kvq_config* cfg, const kvq_cache* cache, 
   a.thr0 = (c[0] + c[1]) / 2.0;
   a.thr1 = (c[1] + c[2]) / 2.0;
   a.thr2 = (c[2] + c[3]) / 2.0;
+  a.key_mode = cfg->key_mode;
   a.rot_heads = 0;
   return KVQ_OK;
 }
@@ -317,6 +319,10 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache,
   }
   a.cmid = (float)((c0 + c3) / 2.0);
   a.chalf = (float)((c3 - c0) / 2.0);
+  a.key_mode = cfg->key_mode;
+  // per-token keys run on the streaming partition kernel only
+  if (a.key_mode == KVQ_KEYS_PER_TOKEN && (a.group > 8 || !a.offsets31 || a.page_shift < 0))
+    return KVQ_ERR_UNSUPPORTED;
   hipError_t e = kvq::launch_decode(cfg->head_dim, cfg->batch, a, stream);
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;
 }

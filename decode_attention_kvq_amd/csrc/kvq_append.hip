@@ -1,7 +1,8 @@
 // Quantize-append: keys (randomized Hadamard rotation + per-group min-max
-// scaling onto the fixed codebook) and values (per-modality rotation + norm
-// scaling onto the fixed codebook), written into the lane-major 2-bit group
-// blocks of the paged cache.
+// scaling onto the fixed codebook; or, for the TurboQuant baseline, per-token
+// norm scaling) and values (per-modality rotation + norm scaling onto the
+// fixed codebook), written into the lane-major 2-bit group blocks of the
+// paged cache.
 //
 // Method: OmniKVQuant page, Sec. 2 Method (TurboQuant bullet, and the two
 // OmniKVQuant bullets for keys and values).
@@ -233,6 +234,41 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
       }
       __syncthreads();
 
+      if (a.key_mode == KVQ_KEYS_PER_TOKEN) {
+        // ---- per-token keys (TurboQuant): n = ||k|| (squares over the
+        // thread's channels, then across the 16 lanes of the position, as for
+        // the values), z = sqrt(d) y / n, nearest level; the norms go to the
+        // first 32 entries of the group's statistics block.
+        double ss = 0.0;
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+          const double f = static_cast<double>(__uint_as_float(element_bits<BF16>(kw, i)));
+          ss = ss + f * f;
+        }
+        ss = lanes_sum<kPosThreads>(ss);
+        const double n = sqrt(ss);
+#pragma unroll
+        for (int q4 = 0; q4 < CH / 4; ++q4) {
+          uint32_t byte = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            uint32_t code = 0;
+            if (present && n > 0.0) {
+              const double z = (a.sqrt_d * x[4 * q4 + i]) / n;
+              code = (z >= a.thr0 ? 1u : 0u) + (z >= a.thr1 ? 1u : 0u) + (z >= a.thr2 ? 1u : 0u);
+            }
+            byte |= code << (2 * i);
+          }
+          sm.k.kblk[key_code_byte<D>(tok, cb + 4 * q4)] = static_cast<uint8_t>(byte);
+        }
+        if (part == 0) a.k_stats[static_cast<size_t>(blk) * 2 * D + tok] = present ? f64_to_f16_rne(n) : uint16_t(0);
+        __syncthreads();
+        if (tid < D / 2) {
+          uint4* dst = reinterpret_cast<uint4*>(a.k_codes + static_cast<size_t>(blk) * 8 * D);
+          dst[tid] = reinterpret_cast<const uint4*>(sm.k.kblk)[tid];
+        }
+      } else {
+
       // ---- statistics: per channel min / max over the present positions;
       // QR threads per channel each take TPQ positions, then combine across
       // lanes (min / max are exact in any order).
@@ -293,6 +329,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
         uint4* dst = reinterpret_cast<uint4*>(a.k_codes + static_cast<size_t>(blk) * 8 * D);
         dst[tid] = reinterpret_cast<const uint4*>(sm.k.kblk)[tid];
       }
+      }   // group min-max keys
     }
 
     // Raw keys of the new open group go to the tail; the key workgroup of

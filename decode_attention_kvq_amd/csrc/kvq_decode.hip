@@ -686,6 +686,7 @@ struct ConsumerLoad {
   uint32_t kc[D / 32];
   uint32_t vc[D / 32];
   uint2 nrm0, nrm1;
+  uint2 knrm0, knrm1;     // per-token key norms (per-token key mode only)
   uint32_t md0, md1;
 };
 
@@ -753,10 +754,15 @@ struct SwShape {
 
 // Bias and q~ of one group from its statistics registers; `stage` is the
 // wavefront's 4D-byte staging of the LO / HI rows.
-template <int D>
+//
+// Per-token key mode: the keys carry no group statistics; the rows staged
+// for the bias hold c0 + c3 as an fp16 hi + lo pair (so the bias is
+// sum_c q_c (c0 + c3) / 2), and the channel range HI - LO is the constant
+// c3 - c0 (`range`): q~ is the same for every group.
+template <int D, bool TQ = false>
 __device__ __forceinline__ float sw_produce(const uint32_t (&st)[D / 64], uint16_t* stage, SwSlot<D>* slot,
                                             const float (&qs)[SwShape<D>::HPL][8], const uint4* bq_lds, int lane,
-                                            int kg) {
+                                            int kg, float range = 0.f) {
   constexpr int KT = D / 32;
   constexpr int CB = SwShape<D>::CB;
   constexpr int HPL = SwShape<D>::HPL;
@@ -784,8 +790,13 @@ __device__ __forceinline__ float sw_produce(const uint32_t (&st)[D / 64], uint16
   float d[8];
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    d[2 * p] = f16_diff_lo(hw[p], lw[p]);
-    d[2 * p + 1] = f16_diff_hi(hw[p], lw[p]);
+    if constexpr (TQ) {
+      d[2 * p] = range;
+      d[2 * p + 1] = range;
+    } else {
+      d[2 * p] = f16_diff_lo(hw[p], lw[p]);
+      d[2 * p + 1] = f16_diff_hi(hw[p], lw[p]);
+    }
   }
 #pragma unroll
   for (int u = 0; u < HPL; ++u) {
@@ -847,16 +858,32 @@ __device__ __forceinline__ void sw_front(const ConsumerLoad<D>& cur, const SwSlo
 // modality (the common case inside a video, audio or text run) take one
 // branch to their accumulator set; others go through per-position modality
 // masks.
-template <int D, int SLOTS, bool ASYM>
-__device__ __forceinline__ void sw_back1(const ConsumerLoad<D>& ca, const SwFront<D>& fa, float bias_a, int rem_a,
+//
+// Per-token key mode (TQ): score i is (bias + dot_i) N_i / sqrt(d), with the
+// key norm N_i of the lane's position i (fp16 pairs in knrm0 / knrm1, in the
+// value norms' order); the bias is then folded in and not added again.
+template <int D, int SLOTS, bool ASYM, bool TQ = false>
+__device__ __forceinline__ void sw_back1(const ConsumerLoad<D>& ca, const SwFront<D>& fa, float bias_in, int rem_a,
                                          int kg, int col, const uint2* tab, uint32_t lane_off,
-                                         WaveState<D, SLOTS, ASYM>& ws) {
+                                         WaveState<D, SLOTS, ASYM>& ws, float key_scale = 0.f) {
   constexpr int CT = D / 16;
   constexpr int GP = Slots<SLOTS>::GP;
   constexpr int NSETS = Slots<SLOTS>::NSETS;
   float s[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) s[i] = fa.sc[i >> 2][i & 3] + dpp_f<0x128>(fa.sc[i >> 2][i & 3]);
+  float bias_a = bias_in;
+  if constexpr (TQ) {
+    const uint32_t kn[4] = {ca.knrm0.x, ca.knrm0.y, ca.knrm1.x, ca.knrm1.y};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float n0 = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(kn[r] & 0xFFFFu)));
+      const float n1 = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(kn[r] >> 16)));
+      s[2 * r] = (s[2 * r] + bias_in) * (n0 * key_scale);
+      s[2 * r + 1] = (s[2 * r + 1] + bias_in) * (n1 * key_scale);
+    }
+    bias_a = 0.f;
+  }
   if (rem_a < kGroupTokens) {
     int ra = rem_a;
     asm volatile("" : "+s"(ra));
@@ -951,7 +978,7 @@ __device__ __forceinline__ void sw_back1(const ConsumerLoad<D>& ca, const SwFron
   }
 }
 
-template <int D, int SLOTS, bool ASYM>
+template <int D, int SLOTS, bool ASYM, bool TQ>
 __global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(DecodeArgs a) {
   constexpr int KT = D / 32;
   constexpr int CT = D / 16;
@@ -1103,6 +1130,11 @@ __global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(D
     c.nrm1 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs.nrm, 32 + 8 * kg, blk * 64, 0));
     c.md0 = __builtin_amdgcn_raw_buffer_load_b32(rs.md, 4 * kg, moff, 0);
     c.md1 = __builtin_amdgcn_raw_buffer_load_b32(rs.md, 16 + 4 * kg, moff, 0);
+    if constexpr (TQ) {
+      // per-token key norms: the first 64 bytes of the group's statistics block
+      c.knrm0 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs.st, 8 * kg, blk * (4 * D), 0));
+      c.knrm1 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs.st, 32 + 8 * kg, blk * (4 * D), 0));
+    }
     return ok;
   };
 
@@ -1121,30 +1153,46 @@ __global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(D
   ConsumerLoad<D> cr[2];
   bool okr[2];
   uint32_t sr[2][D / 64];
-  load_stats(0, sr[0]);
-  load_stats(1, sr[1]);
+  if constexpr (!TQ) {
+    load_stats(0, sr[0]);
+    load_stats(1, sr[1]);
+  } else {
+    // constant rows: c0 + c3 (= 2 cmid) as an fp16 hi part (the LO row,
+    // staged by lanes 0..31) and lo part (the HI row, lanes 32..63)
+    const float csum = 2.f * a.cmid;
+    const _Float16 shi = static_cast<_Float16>(csum);
+    const _Float16 slo = static_cast<_Float16>(csum - static_cast<float>(shi));
+    const uint32_t h2 = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, shi)) * 0x10001u;
+    const uint32_t l2 = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, slo)) * 0x10001u;
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) sr[0][i] = lane < 32 ? h2 : l2;
+  }
   okr[0] = load_codes(0, cr[0]);
   float qs[HPL][8];
   float bias = 0.f;
   if (steps > 0) {
     read_qs(qs);
-    bias = sw_produce<D>(sr[0], stage_a, slot_a, qs, s_bq, lane, kg);
+    if constexpr (TQ) bias = sw_produce<D, true>(sr[0], stage_a, slot_a, qs, s_bq, lane, kg, 2.f * a.chalf);
+    else bias = sw_produce<D>(sr[0], stage_a, slot_a, qs, s_bq, lane, kg);
   }
   auto step = [&](int j, auto ring) {
     constexpr int r = decltype(ring)::value;
     constexpr int r2 = r ^ 1;
-    SwSlot<D>* slot_cur = r ? slot_b : slot_a;
+    SwSlot<D>* slot_cur = (r && !TQ) ? slot_b : slot_a;
     SwSlot<D>* slot_nxt = r ? slot_a : slot_b;
     uint16_t* stage_nxt = r ? stage_a : stage_b;
     okr[r2] = load_codes(j + 1, cr[r2]);
     SwFront<D> f;
     sw_front<D>(cr[r], slot_cur, kg, col, tab, lane_off, f);
-    float bias_next = 0.f;
-    if (j + 1 < steps) bias_next = sw_produce<D>(sr[r2], stage_nxt, slot_nxt, qs, s_bq, lane, kg);
-    load_stats(j + 2, sr[r]);
+    float bias_next = bias;
+    if constexpr (!TQ) {
+      if (j + 1 < steps) bias_next = sw_produce<D>(sr[r2], stage_nxt, slot_nxt, qs, s_bq, lane, kg);
+      load_stats(j + 2, sr[r]);
+    }
     const int t0 = tb + (gw0 + j) * kGroupTokens;
     if (okr[r])
-      sw_back1<D, SLOTS, ASYM>(cr[r], f, bias, min(te - t0, kGroupTokens), kg, col, tab, lane_off, ws);
+      sw_back1<D, SLOTS, ASYM, TQ>(cr[r], f, bias, min(te - t0, kGroupTokens), kg, col, tab, lane_off, ws,
+                                   a.value_scale);
     bias = bias_next;
   };
   for (int j = 0; j < steps; j += 2) {
@@ -1472,10 +1520,14 @@ void launch_partition(int batch, const DecodeArgs& a, hipStream_t s) {
 template <int D, int SLOTS>
 void launch_partition_sw(int batch, const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(a.splits, a.hkv, batch);
-  if (a.cmid != 0.f)
-    hipLaunchKernelGGL((decode_partition_sw_kernel<D, SLOTS, true>), grid, dim3(kSwWaves * 64), 0, s, a);
-  else
-    hipLaunchKernelGGL((decode_partition_sw_kernel<D, SLOTS, false>), grid, dim3(kSwWaves * 64), 0, s, a);
+  const dim3 block(kSwWaves * 64);
+  if (a.key_mode == KVQ_KEYS_PER_TOKEN) {
+    if (a.cmid != 0.f) hipLaunchKernelGGL((decode_partition_sw_kernel<D, SLOTS, true, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((decode_partition_sw_kernel<D, SLOTS, false, true>), grid, block, 0, s, a);
+  } else {
+    if (a.cmid != 0.f) hipLaunchKernelGGL((decode_partition_sw_kernel<D, SLOTS, true, false>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((decode_partition_sw_kernel<D, SLOTS, false, false>), grid, block, 0, s, a);
+  }
 }
 
 template <int D>

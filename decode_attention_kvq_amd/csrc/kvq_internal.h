@@ -41,6 +41,7 @@ struct AppendArgs {
   double sqrt_d;       // fl(sqrt(d))
   double c0, c3;       // outer levels (exact fp64 images of the fp32 levels)
   double thr0, thr1, thr2;  // decision thresholds (c_k + c_{k+1}) / 2
+  int32_t key_mode;         // KVQ_KEYS_GROUP_MINMAX or KVQ_KEYS_PER_TOKEN
   // Query rotation fused into the same launch (kvq_append_and_rotate):
   // rot_heads query heads (0: none), q in bf16 if rot_bf16.  The launcher
   // sets append_x, the grid columns of the append's own workgroups.
@@ -81,6 +82,7 @@ struct DecodeArgs {
   float scale_log2e;      // softmax scale * log2(e)
   float value_scale;      // 1 / sqrt(d)
   float cmid, chalf;      // codebook centre (c0 + c3) / 2 and half range (c3 - c0) / 2
+  int32_t key_mode;       // KVQ_KEYS_GROUP_MINMAX or KVQ_KEYS_PER_TOKEN
   uint32_t level_f16[2];  // normalized levels (2 c_k - c0 - c3) / (c3 - c0) as fp16 bits, k = 0..3
   uint2 byte_levels[256]; // byte e of four 2-bit codes -> its four fp16 levels (code of bits 2i..2i+1 first)
 };

@@ -75,7 +75,9 @@ def session_view(host: dict, cfg, b: int, length: int, h: int) -> dict:
     kc = unpack_key_blocks(kb, d).reshape(-1, d)[:length]
     vc = unpack_value_blocks(vb, d).reshape(-1, d)[:length]
     st = st.reshape(-1, 2, d)[:ng]
-    return dict(k_codes=kc, v_codes=vc,
+    # per-token key mode: the group's key norms are the first 32 entries of row 0
+    k_norms = st[:, 0, :GROUP].reshape(-1)[:length].copy().view(np.float16)
+    return dict(k_codes=kc, v_codes=vc, k_norms=k_norms,
                 lo=st[:, 0].copy().view(np.float16), hi=st[:, 1].copy().view(np.float16),
                 norms=nr.reshape(-1)[:length].copy().view(np.float16),
                 modality=md.reshape(-1)[:length].copy(),

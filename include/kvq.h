@@ -80,6 +80,23 @@ typedef enum {
 
 typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype;
 
+/* Key codec of a cache (kvq_config.key_mode).
+ *   KVQ_KEYS_GROUP_MINMAX (0): OmniKVQuant's keys (Sec. 2 Method, key
+ *     bullet): min-max statistics per 32-token group and channel.
+ *   KVQ_KEYS_PER_TOKEN (1): the TurboQuant baseline (Sec. 2 Method,
+ *     TurboQuant bullet: magnitude apart, randomized Hadamard, fixed codebook
+ *     on the rotated direction): n = ||k||, y = H_d (s_h * k) / sqrt(d),
+ *     code = nearest level of sqrt(d) y / n, norm stored as fp16.  The norms
+ *     of a group's 32 positions occupy the first 32 fp16 entries of the
+ *     group's k_stats block (row 0); the rest of the block is unused.  The
+ *     decode reconstructs k_hat = (N / sqrt(d)) c[code].  Supported by the
+ *     decode for G <= 8, page_tokens a power of two and a pool whose arrays
+ *     stay below 2^31 bytes (KVQ_ERR_UNSUPPORTED otherwise).  With
+ *     kvq_params.rot set to the randomized Hadamard for every modality
+ *     (R_{h,m} = diag(s_h) H_d / sqrt(d)), the cache is the TurboQuant
+ *     baseline run through the same kernels. */
+typedef enum { KVQ_KEYS_GROUP_MINMAX = 0, KVQ_KEYS_PER_TOKEN = 1 } kvq_key_mode;
+
 typedef struct kvq_config {
   int32_t head_dim;     /* d: 64 or 128 */
   int32_t n_q_heads;    /* Hq */
@@ -89,6 +106,7 @@ typedef struct kvq_config {
   int32_t max_pages;    /* page-table row length: capacity = max_pages * page_tokens */
   int32_t num_pages;    /* physical pages in the pool */
   int32_t kv_dtype;     /* kvq_dtype of appended K/V (and of the raw key tail) */
+  int32_t key_mode;     /* kvq_key_mode: the key codec of the whole cache */
 } kvq_config;
 
 typedef struct kvq_cache {

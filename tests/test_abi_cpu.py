@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 def _cfg(L, **kw):
     base = dict(head_dim=128, n_q_heads=16, n_kv_heads=2, batch=2, page_tokens=256, max_pages=4,
-                num_pages=8, kv_dtype=L.KVQ_BF16)
+                num_pages=8, kv_dtype=L.KVQ_BF16, key_mode=L.KVQ_KEYS_GROUP_MINMAX)
     base.update(kw)
     return L.KvqConfig(*[base[f] for f, _ in L.KvqConfig._fields_])
 
@@ -60,7 +60,7 @@ def _fake_cache(L, lengths):
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=96), 2), (dict(head_dim=256), 2), (dict(n_q_heads=15), 1),
     (dict(n_q_heads=34, n_kv_heads=2), 2), (dict(page_tokens=100), 1), (dict(batch=0), 1),
-    (dict(kv_dtype=7), 2), (dict(max_pages=0), 1),
+    (dict(kv_dtype=7), 2), (dict(max_pages=0), 1), (dict(key_mode=2), 1), (dict(key_mode=-1), 1),
 ])
 def test_config_validation(kw, status):
     L, lib = _lib()
