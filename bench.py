@@ -30,11 +30,11 @@ HBM_PEAK_GBS = 8000.0
 
 # HBM bytes of one decode launch (partition + merge kernels) at this workload,
 # from two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE), each scaled by
-# what the counter reads for a plain 256 MiB device copy (FETCH_SIZE x 1.9998,
+# what the counter reads for a plain 256 MiB device copy (FETCH_SIZE x 1.9997,
 # WRITE_SIZE x 1.0); see profiles/decode_80k_hbm_bytes.md.  Valid only for
 # the decode source the counters were taken on (SHA-256 of kvq_decode.hip).
-DECODE_TRAFFIC = {"kvq_decode_sha256": "d2439facc73684ed2ab3bff7c0290e5b7a324338ec7cd71f0c20d5dda4ad8a2d",
-                  "bytes": 34952726}
+DECODE_TRAFFIC = {"kvq_decode_sha256": "ca14639d6a848d6018b93f921261129a0d66038ce65871e2d9d193da8bd3ea78",
+                  "bytes": 34955290}
 
 
 def decode_traffic_bytes():
