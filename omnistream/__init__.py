@@ -14,6 +14,7 @@ from .streams import (  # noqa: F401
     calibration_queries,
     f64_to_bf16_bits,
     generate,
+    lloyd_max_codebook,
     lloyd_max_codebook_2bit,
     workload_digest,
 )

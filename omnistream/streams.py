@@ -18,6 +18,7 @@ bullet) would ideally recover.
 from __future__ import annotations
 
 import hashlib
+import math
 from dataclasses import dataclass, field
 from typing import List, Optional
 
@@ -32,6 +33,42 @@ _CODEBOOK_2BIT = (-1.5104, -0.4528, 0.4528, 1.5104)
 
 def lloyd_max_codebook_2bit() -> np.ndarray:
     return np.array(_CODEBOOK_2BIT, dtype=np.float32)
+
+
+def _normal_pdf(x: float) -> float:
+    return math.exp(-0.5 * x * x) / math.sqrt(2.0 * math.pi)
+
+
+def _normal_cdf(x: float) -> float:
+    return 0.5 * (1.0 + math.erf(x / math.sqrt(2.0)))
+
+
+def lloyd_max_codebook(bits: int) -> np.ndarray:
+    """The fixed codebook for `bits`-bit codes: the 2^bits reconstruction
+    levels of the Lloyd-Max quantizer for a standard normal source, as fp32
+    (2 bits: the four levels above; 3 and 4 bits: Lloyd's iteration, each
+    level the conditional mean of its cell, (pdf(a) - pdf(b)) / (cdf(b) -
+    cdf(a)), cells split at the midpoints, run to convergence in fp64)."""
+    if bits == 2:
+        return lloyd_max_codebook_2bit()
+    if bits not in (3, 4):
+        raise ValueError("bits must be 2, 3 or 4")
+    n = 1 << bits
+    c = [-3.0 + 6.0 * (k + 0.5) / n for k in range(n)]
+    for _ in range(100000):
+        b = [(c[k] + c[k + 1]) / 2.0 for k in range(n - 1)]
+        new = []
+        for k in range(n):
+            pa = _normal_pdf(b[k - 1]) if k > 0 else 0.0
+            pb = _normal_pdf(b[k]) if k < n - 1 else 0.0
+            fa = _normal_cdf(b[k - 1]) if k > 0 else 0.0
+            fb = _normal_cdf(b[k]) if k < n - 1 else 1.0
+            new.append((pa - pb) / (fb - fa))
+        done = max(abs(x - y) for x, y in zip(new, c)) < 1e-15
+        c = new
+        if done:
+            break
+    return np.array(c, dtype=np.float32)
 
 
 @dataclass(frozen=True)
@@ -188,12 +225,13 @@ def _draw_values(rng, modality, basis, lam):
 
 def generate(cfg_id: int, length: Optional[int] = None, batch: Optional[int] = None,
              len_range: Optional[tuple] = None, append_tokens: Optional[int] = None,
-             page_tokens: Optional[int] = None, n_q_heads: Optional[int] = None) -> Workload:
+             page_tokens: Optional[int] = None, n_q_heads: Optional[int] = None,
+             bits: int = 2) -> Workload:
     """Build the seeded workload of one configuration.
 
     Overrides shrink a configuration for fast tests while keeping its recipe,
     KV heads and dtypes (n_q_heads changes only the number of queries, i.e.
-    the GQA group size).  Seeds: SeedSequence(cfg_id) spawned in the fixed
+    the GQA group size; bits picks the fixed codebook, 2, 3 or 4 bits).  Seeds: SeedSequence(cfg_id) spawned in the fixed
     order signs, bases, keys, values, chunking, queries, lengths/pages.
     """
     base = CONFIGS[cfg_id]
@@ -262,7 +300,7 @@ def generate(cfg_id: int, length: Optional[int] = None, batch: Optional[int] = N
         table[b, :npages[b]] = pool[off:off + npages[b]]
         off += npages[b]
 
-    return Workload(cfg=cfg, signs=signs, codebook=lloyd_max_codebook_2bit(), rot=rot,
+    return Workload(cfg=cfg, signs=signs, codebook=lloyd_max_codebook(bits), rot=rot,
                     k=k_list, v=v_list, modality=m_list, q=q, lengths=total,
                     prefix_lengths=prefix, page_tokens=pt, max_pages=max_pages,
                     num_pages=num_pages, page_table=table,
