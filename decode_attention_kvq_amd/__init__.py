@@ -48,12 +48,12 @@ class Config:
 
     def __init__(self, head_dim: int, n_q_heads: int, n_kv_heads: int, batch: int,
                  page_tokens: int, max_pages: int, num_pages: int, kv_dtype: torch.dtype,
-                 key_mode: int = KVQ_KEYS_GROUP_MINMAX):
+                 key_mode: int = KVQ_KEYS_GROUP_MINMAX, bits: int = 2):
         self.head_dim, self.n_q_heads, self.n_kv_heads = head_dim, n_q_heads, n_kv_heads
         self.batch, self.page_tokens, self.max_pages, self.num_pages = batch, page_tokens, max_pages, num_pages
-        self.kv_dtype, self.key_mode = kv_dtype, int(key_mode)
+        self.kv_dtype, self.key_mode, self.bits = kv_dtype, int(key_mode), int(bits)
         self.struct = KvqConfig(head_dim, n_q_heads, n_kv_heads, batch, page_tokens, max_pages,
-                                num_pages, _DTYPES[kv_dtype], self.key_mode)
+                                num_pages, _DTYPES[kv_dtype], self.key_mode, self.bits)
 
     def buffer_bytes(self) -> list:
         out = (ctypes.c_size_t * 6)()
@@ -62,13 +62,17 @@ class Config:
 
 
 class Params:
-    """Hadamard signs [Hkv, d] int8, value bases [Hkv, 3, d, d] fp32, 4 levels."""
+    """Hadamard signs [Hkv, d] int8, value bases [Hkv, 3, d, d] fp32, and the
+    2^bits codebook levels (at most 16)."""
 
     def __init__(self, signs: torch.Tensor, rot: torch.Tensor, codebook: Sequence[float]):
         self.signs, self.rot = signs, rot
         self.codebook = [float(c) for c in codebook]
+        if not 1 <= len(self.codebook) <= 16:
+            raise ValueError("the codebook holds 4, 8 or 16 levels")
+        padded = self.codebook + [0.0] * (16 - len(self.codebook))
         self.struct = KvqParams(_dev(signs, "signs", torch.int8), _dev(rot, "rot", torch.float32),
-                                (ctypes.c_float * 4)(*self.codebook))
+                                (ctypes.c_float * 16)(*padded))
 
 
 class Cache:

@@ -24,7 +24,7 @@ class KvqConfig(ctypes.Structure):
                 ("n_kv_heads", ctypes.c_int32), ("batch", ctypes.c_int32),
                 ("page_tokens", ctypes.c_int32), ("max_pages", ctypes.c_int32),
                 ("num_pages", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
-                ("key_mode", ctypes.c_int32)]
+                ("key_mode", ctypes.c_int32), ("bits", ctypes.c_int32)]
 
 
 class KvqCache(ctypes.Structure):
@@ -37,7 +37,7 @@ class KvqCache(ctypes.Structure):
 
 class KvqParams(ctypes.Structure):
     _fields_ = [("signs", ctypes.c_void_p), ("rot", ctypes.c_void_p),
-                ("codebook", ctypes.c_float * 4)]
+                ("codebook", ctypes.c_float * 16)]
 
 
 class KvqCalibShape(ctypes.Structure):

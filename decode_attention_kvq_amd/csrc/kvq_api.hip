@@ -12,10 +12,10 @@ namespace {
 using kvq::kGroupTokens;
 using kvq::kMaxGroupHeads;
 
-bool codebook_ok(const float c[4]) {
-  for (int k = 0; k < 4; ++k)
-    if (!isfinite(c[k])) return false;
-  return c[0] < c[1] && c[1] < c[2] && c[2] < c[3];
+bool codebook_ok(const float* c, int n) {
+  for (int k = 0; k < n; ++k)
+    if (!isfinite(c[k]) || (k > 0 && !(c[k - 1] < c[k]))) return false;
+  return true;
 }
 
 kvq_status check_config(const kvq_config* cfg) {
@@ -29,12 +29,13 @@ kvq_status check_config(const kvq_config* cfg) {
   if ((int64_t)cfg->max_pages * cfg->page_tokens > INT32_MAX) return KVQ_ERR_INVALID;
   if (cfg->kv_dtype != KVQ_F32 && cfg->kv_dtype != KVQ_BF16) return KVQ_ERR_UNSUPPORTED;
   if (cfg->key_mode != KVQ_KEYS_GROUP_MINMAX && cfg->key_mode != KVQ_KEYS_PER_TOKEN) return KVQ_ERR_INVALID;
+  if (cfg->bits < 2 || cfg->bits > 4) return KVQ_ERR_UNSUPPORTED;
   return KVQ_OK;
 }
 
-kvq_status check_params(const kvq_params* p) {
+kvq_status check_params(const kvq_config* cfg, const kvq_params* p) {
   if (!p || !p->signs || !p->rot) return KVQ_ERR_INVALID;
-  if (!codebook_ok(p->codebook)) return KVQ_ERR_INVALID;
+  if (!codebook_ok(p->codebook, 1 << cfg->bits)) return KVQ_ERR_INVALID;
   return KVQ_OK;
 }
 
@@ -129,9 +130,9 @@ kvq_status kvq_cache_buffer_bytes(const kvq_config* cfg, size_t out[6]) {
   if (!out) return KVQ_ERR_INVALID;
   const size_t d = cfg->head_dim, hkv = cfg->n_kv_heads, pt = cfg->page_tokens, np = cfg->num_pages;
   const size_t groups = np * hkv * (pt / kGroupTokens);
-  out[0] = groups * 8 * d;                 // k_codes
+  out[0] = groups * 4 * cfg->bits * d;     // k_codes
   out[1] = groups * 2 * d * 2;             // k_stats (fp16)
-  out[2] = groups * 8 * d;                 // v_codes
+  out[2] = groups * 4 * cfg->bits * d;     // v_codes
   out[3] = np * hkv * pt * 2;              // v_norms (fp16)
   out[4] = np * pt;                        // modality
   out[5] = (size_t)cfg->batch * hkv * kGroupTokens * d * (cfg->kv_dtype == KVQ_BF16 ? 2 : 4);
@@ -144,7 +145,7 @@ static kvq_status prepare_append(const kvq_config* cfg, const kvq_cache* cache, 
                                  const uint8_t* modality_new, kvq::AppendArgs& a) {
   kvq_status st = check_config(cfg);
   if (st != KVQ_OK) return st;
-  if ((st = check_params(params)) != KVQ_OK) return st;
+  if ((st = check_params(cfg, params)) != KVQ_OK) return st;
   if ((st = check_cache(cache)) != KVQ_OK) return st;
   if (b0 < 0 || nb <= 0 || b0 + nb > cfg->batch || n_new < 0) return KVQ_ERR_INVALID;
   if (n_new == 0) return KVQ_OK;
@@ -178,12 +179,13 @@ static kvq_status prepare_append(const kvq_config* cfg, const kvq_cache* cache, 
   a.num_pages = cfg->num_pages;
   a.inv_sqrt_d = 1.0 / sd;
   a.sqrt_d = sd;
-  const double c[4] = {params->codebook[0], params->codebook[1], params->codebook[2], params->codebook[3]};
-  a.c0 = c[0];
-  a.c3 = c[3];
-  a.thr0 = (c[0] + c[1]) / 2.0;
-  a.thr1 = (c[1] + c[2]) / 2.0;
-  a.thr2 = (c[2] + c[3]) / 2.0;
+  const int n = 1 << cfg->bits;
+  a.c0 = params->codebook[0];
+  a.cmax = params->codebook[n - 1];
+  a.nthr = n - 1;
+  for (int k = 0; k < 15; ++k)
+    a.thr[k] = k < n - 1 ? ((double)params->codebook[k] + (double)params->codebook[k + 1]) / 2.0 : INFINITY;
+  a.bits = cfg->bits;
   a.key_mode = cfg->key_mode;
   a.rot_heads = 0;
   return KVQ_OK;
@@ -261,7 +263,7 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache,
                                 hipStream_t stream) {
   kvq_status st = check_config(cfg);
   if (st != KVQ_OK) return st;
-  if ((st = check_params(params)) != KVQ_OK) return st;
+  if ((st = check_params(cfg, params)) != KVQ_OK) return st;
   if ((st = check_cache(cache)) != KVQ_OK) return st;
   if (!q_rot || !out || !isfinite(scale)) return KVQ_ERR_INVALID;
   int32_t max_len = 0;
@@ -273,7 +275,8 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache,
   if (!plan_supported(cfg, max_len)) return KVQ_ERR_UNSUPPORTED;
   const Plan plan = plan_decode(cfg, max_len);
   if (!workspace || workspace_bytes < workspace_floats(cfg, plan) * sizeof(float)) return KVQ_ERR_WORKSPACE;
-  const double c0 = params->codebook[0], c3 = params->codebook[3];
+  const int nlev = 1 << cfg->bits;
+  const double c0 = params->codebook[0], c3 = params->codebook[nlev - 1];   // outer levels
   kvq::DecodeArgs a;
   a.k_codes = cache->k_codes;
   a.k_stats = cache->k_stats;
@@ -303,16 +306,23 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache,
   a.blocks_per_page = cfg->n_kv_heads * (cfg->page_tokens / kGroupTokens);
   // The streaming partition kernel addresses every cache array with 31-bit
   // byte offsets; larger pools take the pointer-addressed kernel.
-  a.offsets31 = (size_t)cfg->num_pages * cfg->n_kv_heads * cfg->page_tokens * (cfg->head_dim / 4) < ((size_t)1 << 31);
+  a.offsets31 = (size_t)cfg->num_pages * cfg->n_kv_heads * cfg->page_tokens * cfg->head_dim * cfg->bits / 8 <
+                ((size_t)1 << 31);
   a.scale_log2e = (float)((double)scale * 1.4426950408889634);
   a.value_scale = (float)(1.0 / sqrt((double)cfg->head_dim));
-  uint16_t lv[4];
-  for (int k = 0; k < 4; ++k) {
-    const _Float16 v = (_Float16)((2.0 * params->codebook[k] - c0 - c3) / (c3 - c0));
+  // normalized levels l_k = (2 c_k - c0 - c_{n-1}) / (c_{n-1} - c0) as fp16
+  // and, for the scores at 3 / 4 bits, 2^12 times the part fp16 missed
+  uint16_t lv[16] = {0}, lr[16] = {0};
+  for (int k = 0; k < nlev; ++k) {
+    const double l = (2.0 * params->codebook[k] - c0 - c3) / (c3 - c0);
+    const _Float16 v = (_Float16)l;
     lv[k] = __builtin_bit_cast(uint16_t, v);
+    lr[k] = __builtin_bit_cast(uint16_t, (_Float16)((l - (double)v) * 4096.0));
   }
-  a.level_f16[0] = lv[0] | ((uint32_t)lv[1] << 16);
-  a.level_f16[1] = lv[2] | ((uint32_t)lv[3] << 16);
+  for (int w = 0; w < 8; ++w) {
+    a.level_f16[w] = lv[2 * w] | ((uint32_t)lv[2 * w + 1] << 16);
+    a.level_lo_f16[w] = lr[2 * w] | ((uint32_t)lr[2 * w + 1] << 16);
+  }
   for (int e = 0; e < 256; ++e) {
     a.byte_levels[e].x = lv[e & 3] | ((uint32_t)lv[(e >> 2) & 3] << 16);
     a.byte_levels[e].y = lv[(e >> 4) & 3] | ((uint32_t)lv[(e >> 6) & 3] << 16);
@@ -320,8 +330,9 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache,
   a.cmid = (float)((c0 + c3) / 2.0);
   a.chalf = (float)((c3 - c0) / 2.0);
   a.key_mode = cfg->key_mode;
-  // per-token keys run on the streaming partition kernel only
-  if (a.key_mode == KVQ_KEYS_PER_TOKEN && (a.group > 8 || !a.offsets31 || a.page_shift < 0))
+  a.bits = cfg->bits;
+  // per-token keys and 3- / 4-bit codes run on the streaming partition kernel only
+  if ((a.key_mode == KVQ_KEYS_PER_TOKEN || a.bits != 2) && (a.group > 8 || !a.offsets31 || a.page_shift < 0))
     return KVQ_ERR_UNSUPPORTED;
   hipError_t e = kvq::launch_decode(cfg->head_dim, cfg->batch, a, stream);
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;

@@ -103,16 +103,72 @@ template <int D>
 struct KeySmem {
   double y[kGroupTokens][D];                      // rotated keys, one row per position
   double lohi[2][D];                              // LO and the per-channel factor
-  __align__(16) uint8_t kblk[8 * D];              // the group's key codes (lane-major)
+  __align__(16) uint8_t kblk[8 * D];              // the group's 2-bit key codes (lane-major)
+  uint8_t code[kGroupTokens][D];                  // 3- / 4-bit key codes, one byte each
 };
 
 template <int D>
 struct ValSmem {
   float v[kGroupTokens][D];                       // new values (the inputs are exact in fp32)
   double n[kGroupTokens];                         // value norms
-  uint8_t code[kGroupTokens][D];                  // value codes of the new positions
+  uint8_t code[kGroupTokens][D];                  // value codes (3- / 4-bit: also the earlier positions)
   uint8_t mod[kGroupTokens];
+  uint32_t oldw[4 * D];                           // 3- / 4-bit: the group's stored value block
 };
+
+// Level index of a normalised value: the number of decision thresholds it
+// reaches (the thresholds ascend; ties go up).
+__device__ __forceinline__ uint32_t level_index(const AppendArgs& a, double z) {
+  uint32_t c = 0;
+  for (int i = 0; i < a.nthr; ++i) c += z >= a.thr[i] ? 1u : 0u;
+  return c;
+}
+
+// b-bit lane-major blocks (include/kvq.h): lane L owns b D / 64 words, a bit
+// stream of operand units of 8 codes, code k of unit u at bit 8 b u + b k.
+// Position and channel of code g (unit g / 8, k = g % 8) of lane L:
+//   keys   t = 16 (u / (D/32)) + L % 16,  c = 32 (u % (D/32)) + 8 (L / 16) + k
+//   values t = 16 (k / 4) + 4 (L / 16) + k % 4,  c = 16 u + L % 16
+template <int D, bool VALUE>
+__device__ __forceinline__ void code_slot(int lane, int g, int& t, int& c) {
+  const int u = g >> 3, k = g & 7;
+  if constexpr (VALUE) {
+    t = 16 * (k >> 2) + 4 * (lane >> 4) + (k & 3);
+    c = 16 * u + (lane & 15);
+  } else {
+    t = 16 * (u / (D / 32)) + (lane & 15);
+    c = 32 * (u % (D / 32)) + 8 * (lane >> 4) + k;
+  }
+}
+
+// Word w (of the block's b D words) of a b-bit block, from one code byte per
+// (position, channel); code(t, c) gives the code of a slot.
+template <int D, bool VALUE, typename F>
+__device__ __forceinline__ uint32_t pack_word(int bits, int w, F code) {
+  const int wpl = bits * D / 64;                 // words per lane
+  const int lane = w / wpl, b0 = 32 * (w % wpl);
+  uint32_t out = 0;
+  for (int g = b0 / bits; g * bits < b0 + 32; ++g) {
+    int t, c;
+    code_slot<D, VALUE>(lane, g, t, c);
+    const int sh = g * bits - b0;
+    const uint32_t v = code(t, c);
+    out |= sh >= 0 ? (v << sh) : (v >> -sh);
+  }
+  return out;
+}
+
+// Code of value slot (t, c) in a stored b-bit block (words in LDS).
+template <int D>
+__device__ __forceinline__ uint32_t unpack_value_code(int bits, const uint32_t* words, int t, int c) {
+  const int L = 16 * ((t & 15) >> 2) + (c & 15), u = c >> 4, k = 4 * (t >> 4) + (t & 3);
+  const int p = 8 * bits * u + bits * k;          // bit in the lane's stream
+  const int wpl = bits * D / 64;
+  const int wi = L * wpl + (p >> 5), sh = p & 31;
+  uint32_t v = words[wi] >> sh;
+  if (sh + bits > 32) v |= words[wi + 1] << (32 - sh);
+  return v & ((1u << bits) - 1u);
+}
 
 template <int D>
 union AppendSmem {
@@ -186,6 +242,21 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
       ? (static_cast<long long>(phys) * a.hkv + h) * (a.page_tokens / kGroupTokens) + (t0 % a.page_tokens) / kGroupTokens
       : -1;
 
+  // The key block of the group: 2 bits as built in LDS, wider codes packed
+  // from one byte per code.
+  auto store_key_block = [&](long long blk_) {
+    if (a.bits == 2) {
+      if (tid < D / 2) {
+        uint4* dst = reinterpret_cast<uint4*>(a.k_codes + static_cast<size_t>(blk_) * 8 * D);
+        dst[tid] = reinterpret_cast<const uint4*>(sm.k.kblk)[tid];
+      }
+    } else {
+      uint32_t* dst = reinterpret_cast<uint32_t*>(a.k_codes + static_cast<size_t>(blk_) * 4 * a.bits * D);
+      for (int w = tid; w < a.bits * D; w += kAppendThreads)
+        dst[w] = pack_word<D, false>(a.bits, w, [&](int t, int c) { return static_cast<uint32_t>(sm.k.code[t][c]); });
+    }
+  };
+
   if (!vrole) {
     // ================= keys =================
     const char* krow = (t0 + tok < L_old)
@@ -255,18 +326,16 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
             uint32_t code = 0;
             if (present && n > 0.0) {
               const double z = (a.sqrt_d * x[4 * q4 + i]) / n;
-              code = (z >= a.thr0 ? 1u : 0u) + (z >= a.thr1 ? 1u : 0u) + (z >= a.thr2 ? 1u : 0u);
+              code = level_index(a, z);
             }
             byte |= code << (2 * i);
+            sm.k.code[tok][cb + 4 * q4 + i] = static_cast<uint8_t>(code);
           }
-          sm.k.kblk[key_code_byte<D>(tok, cb + 4 * q4)] = static_cast<uint8_t>(byte);
+          if (a.bits == 2) sm.k.kblk[key_code_byte<D>(tok, cb + 4 * q4)] = static_cast<uint8_t>(byte);
         }
         if (part == 0) a.k_stats[static_cast<size_t>(blk) * 2 * D + tok] = present ? f64_to_f16_rne(n) : uint16_t(0);
         __syncthreads();
-        if (tid < D / 2) {
-          uint4* dst = reinterpret_cast<uint4*>(a.k_codes + static_cast<size_t>(blk) * 8 * D);
-          dst[tid] = reinterpret_cast<const uint4*>(sm.k.kblk)[tid];
-        }
+        store_key_block(blk);
       } else {
 
       // ---- statistics: per channel min / max over the present positions;
@@ -299,7 +368,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
           // exact in fp64); 0 marks HI == LO (every code 0).
           const double LO = static_cast<double>(f16_bits_to_f32(lo16)), HI = static_cast<double>(f16_bits_to_f32(hi16));
           sm.k.lohi[0][c] = LO;
-          sm.k.lohi[1][c] = HI > LO ? (a.c3 - a.c0) / (HI - LO) : 0.0;
+          sm.k.lohi[1][c] = HI > LO ? (a.cmax - a.c0) / (HI - LO) : 0.0;
         }
       }
       __syncthreads();
@@ -318,17 +387,15 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
           const double LO = sm.k.lohi[0][c], f = sm.k.lohi[1][c];
           if (present && f > 0.0) {
             const double z = a.c0 + (x[4 * q4 + i] - LO) * f;
-            code = (z >= a.thr0 ? 1u : 0u) + (z >= a.thr1 ? 1u : 0u) + (z >= a.thr2 ? 1u : 0u);
+            code = level_index(a, z);
           }
           byte |= code << (2 * i);
+          sm.k.code[tok][c] = static_cast<uint8_t>(code);
         }
-        sm.k.kblk[key_code_byte<D>(tok, cb + 4 * q4)] = static_cast<uint8_t>(byte);
+        if (a.bits == 2) sm.k.kblk[key_code_byte<D>(tok, cb + 4 * q4)] = static_cast<uint8_t>(byte);
       }
       __syncthreads();
-      if (tid < D / 2) {
-        uint4* dst = reinterpret_cast<uint4*>(a.k_codes + static_cast<size_t>(blk) * 8 * D);
-        dst[tid] = reinterpret_cast<const uint4*>(sm.k.kblk)[tid];
-      }
+      store_key_block(blk);
       }   // group min-max keys
     }
 
@@ -370,9 +437,11 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
     // Round trip 3 (needed only at the end): the group's stored value codes,
     // for positions before s_first.  The 8D-byte block is 2D words: thread
     // tid < 2D owns word tid.
-    uint8_t* vb = a.v_codes + static_cast<size_t>(blk) * 8 * D;
-    const bool vword = tid < 2 * D;
+    uint8_t* vb = a.v_codes + static_cast<size_t>(blk) * 4 * a.bits * D;
+    const bool vword = a.bits == 2 && tid < 2 * D;
     const uint32_t old_v = (s_first > 0 && vword) ? reinterpret_cast<const uint32_t*>(vb)[tid] : 0u;
+    if (a.bits != 2 && s_first > 0)
+      for (int w = tid; w < a.bits * D; w += kAppendThreads) sm.v.oldw[w] = reinterpret_cast<const uint32_t*>(vb)[w];
 
     // Modalities among the new positions (every wave computes the same mask).
     uint32_t mods = 0;
@@ -393,6 +462,10 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
     ss = lanes_sum<kPosThreads>(ss);
     if (part == 0) sm.v.n[tok] = sqrt(ss);
     __syncthreads();
+    // 3- / 4-bit: the earlier positions' codes, out of the stored block
+    if (a.bits != 2)
+      for (int e = tid; e < s_first * D; e += kAppendThreads)
+        sm.v.code[e / D][e % D] = static_cast<uint8_t>(unpack_value_code<D>(a.bits, sm.v.oldw, e / D, e % D));
 
     // ---- r = R_m^T v, one modality at a time (the rows of modality mpre
     // were loaded above): four interleaved partial sums over the part's rows,
@@ -416,7 +489,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
           uint32_t code = 0;
           if (n > 0.0) {
             const double z = (a.sqrt_d * r) / n;
-            code = (z >= a.thr0 ? 1u : 0u) + (z >= a.thr1 ? 1u : 0u) + (z >= a.thr2 ? 1u : 0u);
+            code = level_index(a, z);
           }
           sm.v.code[s][jc] = static_cast<uint8_t>(code);
         }
@@ -448,6 +521,15 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
         outw |= out << (8 * k);
       }
       reinterpret_cast<uint32_t*>(vb)[tid] = outw;
+    }
+    if (a.bits != 2) {
+      auto vcode = [&](int t, int c) -> uint32_t {
+        if (t < s_first) return sm.v.code[t][c];
+        if (t < s_end) return sm.v.mod[t] < kModalities ? sm.v.code[t][c] : 0u;
+        return 0u;
+      };
+      for (int w = tid; w < a.bits * D; w += kAppendThreads)
+        reinterpret_cast<uint32_t*>(vb)[w] = pack_word<D, true>(a.bits, w, vcode);
     }
     if (tid < kGroupTokens && tid >= s_first && tid < s_end) {
       const int pos = (t0 + tid) % a.page_tokens;

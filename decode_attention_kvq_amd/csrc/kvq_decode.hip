@@ -681,10 +681,10 @@ __device__ __forceinline__ float wave_max(float v) {
 
 // ---------------------------------------------------------------------------
 // Operand registers of one group for the streaming kernel below.
-template <int D>
+template <int D, int BITS = 2>
 struct ConsumerLoad {
-  uint32_t kc[D / 32];
-  uint32_t vc[D / 32];
+  uint32_t kc[BITS * D / 64];   // the lane's key code words (b d / 16 bytes of the group block)
+  uint32_t vc[BITS * D / 64];
   uint2 nrm0, nrm1;
   uint2 knrm0, knrm1;     // per-token key norms (per-token key mode only)
   uint32_t md0, md1;
@@ -696,6 +696,83 @@ struct ConsumerLoad {
 // keep the count of its loads in flight fixed.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// NW consecutive 32-bit words at byte offset voff (per lane) + soff, in as
+// few buffer loads as the width allows.
+template <int NW>
+__device__ __forceinline__ void load_lane_words(__amdgpu_buffer_rsrc_t r, int voff, int soff, uint32_t (&w)[NW]) {
+#pragma unroll
+  for (int i = 0; i + 4 <= NW; i += 4) {
+    const uint4 x = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 4 * i, soff, 0));
+    w[i] = x.x; w[i + 1] = x.y; w[i + 2] = x.z; w[i + 3] = x.w;
+  }
+  constexpr int R = NW & 3;
+  if constexpr (R >= 2) {
+    const uint2 x = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff + 4 * (NW - R), soff, 0));
+    w[NW - R] = x.x; w[NW - R + 1] = x.y;
+  }
+  if constexpr (R & 1) w[NW - 1] = __builtin_amdgcn_raw_buffer_load_b32(r, voff + 4 * (NW - 1), soff, 0);
+}
+
+// The pair-table entries behind operand unit u (8 codes, 8 BITS bits from bit
+// 8 BITS u of the lane's code words) for BITS = 3, 4: four lookups, each
+// giving two codes' levels.  4 bits: a byte holds 2 codes; 3 bits: a 6-bit
+// field does.  An entry is {hi: the two levels in fp16, lo: 2^12 times what
+// fp16 missed of them}, one 8-byte copy per lane pair of banks (32 copies,
+// 256 bytes per entry), so lane_off = 8 (lane % 32) as for the byte table.
+template <int BITS, int NW>
+__device__ __forceinline__ void unit_pairs(const uint32_t (&w)[NW], int u, const uint2* tab, uint32_t lane_off,
+                                           uint2 (&e)[4]) {
+  const char* base = reinterpret_cast<const char*>(tab);
+  if constexpr (BITS == 4) {
+    const uint32_t x = w[u];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      e[i] = *reinterpret_cast<const uint2*>(base + __builtin_amdgcn_perm(x, lane_off, byte_sel(i)));
+  } else {
+    const int b0 = 24 * u, wi = b0 >> 5, sh = b0 & 31;
+    uint32_t x = w[wi] >> sh;
+    if (sh > 8) x |= w[wi + 1] << (32 - sh);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      e[i] = *reinterpret_cast<const uint2*>(base + ((((x >> (6 * i)) & 63u) << 8) | lane_off));
+  }
+}
+
+// The 8 fp16 levels of operand unit u in code order.  2 bits: two lookups in
+// the byte table (a byte holds 4 codes); 3 and 4 bits: the hi parts of the
+// unit's pair entries.
+template <int BITS, int NW>
+__device__ __forceinline__ half8 unit_operand(const uint32_t (&w)[NW], int u, const uint2* tab, uint32_t lane_off) {
+  if constexpr (BITS == 2) {
+    const int j0 = 2 * u;
+    return as_half8(lookup(tab, w[j0 >> 2], byte_sel(j0 & 3), lane_off),
+                    lookup(tab, w[(j0 + 1) >> 2], byte_sel((j0 + 1) & 3), lane_off));
+  } else {
+    uint2 e[4];
+    unit_pairs<BITS>(w, u, tab, lane_off, e);
+    return __builtin_bit_cast(half8, uint4{e[0].x, e[1].x, e[2].x, e[3].x});
+  }
+}
+
+// 3 / 4 bits: the hi and the (2^12-scaled) lo levels of operand unit u.
+template <int BITS, int NW>
+__device__ __forceinline__ void unit_operand_hilo(const uint32_t (&w)[NW], int u, const uint2* tab,
+                                                  uint32_t lane_off, half8& hi, half8& lo) {
+  uint2 e[4];
+  unit_pairs<BITS>(w, u, tab, lane_off, e);
+  hi = __builtin_bit_cast(half8, uint4{e[0].x, e[1].x, e[2].x, e[3].x});
+  lo = __builtin_bit_cast(half8, uint4{e[0].y, e[1].y, e[2].y, e[3].y});
+}
+
+// Pair-table entry e: codes e % 2^BITS (low half) and e / 2^BITS (high half);
+// x from the fp16 levels, y from their 2^12-scaled remainders.
+template <int BITS>
+__device__ __forceinline__ uint2 pair_entry(uint32_t e, const uint32_t (&lv)[8], const uint32_t (&lr)[8]) {
+  const uint32_t k0 = e & ((1u << BITS) - 1u), k1 = e >> BITS;
+  auto half_of = [](const uint32_t (&t)[8], uint32_t k) { return (t[k >> 1] >> (16 * (k & 1))) & 0xFFFFu; };
+  return uint2{half_of(lv, k0) | (half_of(lv, k1) << 16), half_of(lr, k0) | (half_of(lr, k1) << 16)};
 }
 
 // ---------------------------------------------------------------------------
@@ -827,24 +904,33 @@ __device__ __forceinline__ float sw_produce(const uint32_t (&st)[D / 64], uint16
 template <int D>
 struct SwFront {
   floatx4 sc[2];
+  floatx4 sl[2];   // 3 / 4 bits: the scores' lo-level part (times 2^12)
 };
 
-template <int D>
-__device__ __forceinline__ void sw_front(const ConsumerLoad<D>& cur, const SwSlot<D>* slot, int kg, int col,
+template <int D, int BITS>
+__device__ __forceinline__ void sw_front(const ConsumerLoad<D, BITS>& cur, const SwSlot<D>* slot, int kg, int col,
                                          const uint2* tab, uint32_t lane_off, SwFront<D>& f) {
   constexpr int KT = D / 32;
   constexpr int CT = D / 16;
   f.sc[0] = floatx4{0.f, 0.f, 0.f, 0.f};
   f.sc[1] = floatx4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (BITS != 2) {
+    f.sl[0] = floatx4{0.f, 0.f, 0.f, 0.f};
+    f.sl[1] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
 #pragma unroll
   for (int kt = 0; kt < KT; ++kt) {
     const half8 qt = __builtin_bit_cast(half8, slot->qt[4 * kt + kg][col]);
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const int j0 = mt * (D / 16) + kt * 2;   // code bytes j0, j0 + 1 of this (mt, kt)
-      const uint2 x0 = lookup(tab, cur.kc[j0 >> 2], byte_sel(j0 & 3), lane_off);
-      const uint2 x1 = lookup(tab, cur.kc[(j0 + 1) >> 2], byte_sel((j0 + 1) & 3), lane_off);
-      f.sc[mt] = mfma(as_half8(x0, x1), qt, f.sc[mt]);
+    for (int mt = 0; mt < 2; ++mt) {   // operand unit (positions 16 mt.., channels 32 kt..)
+      if constexpr (BITS == 2) {
+        f.sc[mt] = mfma(unit_operand<BITS>(cur.kc, mt * (D / 32) + kt, tab, lane_off), qt, f.sc[mt]);
+      } else {
+        half8 hi, lo;
+        unit_operand_hilo<BITS>(cur.kc, mt * (D / 32) + kt, tab, lane_off, hi, lo);
+        f.sc[mt] = mfma(hi, qt, f.sc[mt]);
+        f.sl[mt] = mfma(lo, qt, f.sl[mt]);
+      }
     }
   }
 }
@@ -862,8 +948,8 @@ __device__ __forceinline__ void sw_front(const ConsumerLoad<D>& cur, const SwSlo
 // Per-token key mode (TQ): score i is (bias + dot_i) N_i / sqrt(d), with the
 // key norm N_i of the lane's position i (fp16 pairs in knrm0 / knrm1, in the
 // value norms' order); the bias is then folded in and not added again.
-template <int D, int SLOTS, bool ASYM, bool TQ = false>
-__device__ __forceinline__ void sw_back1(const ConsumerLoad<D>& ca, const SwFront<D>& fa, float bias_in, int rem_a,
+template <int D, int SLOTS, bool ASYM, bool TQ = false, int BITS = 2>
+__device__ __forceinline__ void sw_back1(const ConsumerLoad<D, BITS>& ca, const SwFront<D>& fa, float bias_in, int rem_a,
                                          int kg, int col, const uint2* tab, uint32_t lane_off,
                                          WaveState<D, SLOTS, ASYM>& ws, float key_scale = 0.f) {
   constexpr int CT = D / 16;
@@ -872,6 +958,10 @@ __device__ __forceinline__ void sw_back1(const ConsumerLoad<D>& ca, const SwFron
   float s[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) s[i] = fa.sc[i >> 2][i & 3] + dpp_f<0x128>(fa.sc[i >> 2][i & 3]);
+  if constexpr (BITS != 2) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s[i] += 0x1p-12f * (fa.sl[i >> 2][i & 3] + dpp_f<0x128>(fa.sl[i >> 2][i & 3]));
+  }
   float bias_a = bias_in;
   if constexpr (TQ) {
     const uint32_t kn[4] = {ca.knrm0.x, ca.knrm0.y, ca.knrm1.x, ca.knrm1.y};
@@ -924,9 +1014,7 @@ __device__ __forceinline__ void sw_back1(const ConsumerLoad<D>& ca, const SwFron
     const half8 bwa = __builtin_bit_cast(half8, uint4{ba[0], ba[1], ba[2], ba[3]});
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
-      const int j0 = 2 * ct;
-      const half8 va = as_half8(lookup(tab, ca.vc[j0 >> 2], byte_sel(j0 & 3), lane_off),
-                                lookup(tab, ca.vc[(j0 + 1) >> 2], byte_sel((j0 + 1) & 3), lane_off));
+      const half8 va = unit_operand<BITS>(ca.vc, ct, tab, lane_off);   // channels 16 ct + lane % 16
       ws.acc[k][ct] = mfma(va, bwa, ws.acc[k][ct]);
     }
     if constexpr (ASYM) {
@@ -978,7 +1066,7 @@ __device__ __forceinline__ void sw_back1(const ConsumerLoad<D>& ca, const SwFron
   }
 }
 
-template <int D, int SLOTS, bool ASYM, bool TQ>
+template <int D, int SLOTS, bool ASYM, bool TQ, int BITS>
 __global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(DecodeArgs a) {
   constexpr int KT = D / 32;
   constexpr int CT = D / 16;
@@ -1064,10 +1152,18 @@ __global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(D
     }
   }
 
-  // Byte table (two copies of an entry per 16-byte store).
-  for (int i = tid; i < 256 * kTabCopies / 2; i += NT) {
-    const uint2 v = tab_entry(static_cast<uint32_t>(i) / (kTabCopies / 2), a.level_f16[0], a.level_f16[1]);
-    reinterpret_cast<uint4*>(sm.s.tab)[i] = uint4{v.x, v.y, v.x, v.y};
+  if constexpr (BITS == 2) {
+    // Byte table (two copies of an entry per 16-byte store).
+    for (int i = tid; i < 256 * kTabCopies / 2; i += NT) {
+      const uint2 v = tab_entry(static_cast<uint32_t>(i) / (kTabCopies / 2), a.level_f16[0], a.level_f16[1]);
+      reinterpret_cast<uint4*>(sm.s.tab)[i] = uint4{v.x, v.y, v.x, v.y};
+    }
+  } else {
+    // Pair table: 2^(2 BITS) entries of 32 8-byte copies (two per 16-byte store).
+    for (int i = tid; i < (1 << (2 * BITS)) * 16; i += NT) {
+      const uint2 v = pair_entry<BITS>(static_cast<uint32_t>(i) >> 4, a.level_f16, a.level_lo_f16);
+      reinterpret_cast<uint4*>(sm.s.tab)[i] = uint4{v.x, v.y, v.x, v.y};
+    }
   }
   if (tid == 0) s_mask = 0;
   const uint32_t lane_off = static_cast<uint32_t>(lane & (kTabCopies - 1)) << 3;
@@ -1112,20 +1208,12 @@ __global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(D
       st[0] = __builtin_amdgcn_raw_buffer_load_b32(rs.st, lane * 4, blk * (4 * D), 0);
     }
   };
-  auto load_codes = [&](int j, ConsumerLoad<D>& c) {
+  auto load_codes = [&](int j, ConsumerLoad<D, BITS>& c) {
     int blk, moff;
     const bool ok = locate(j, blk, moff);
-    if constexpr (D == 128) {
-      const uint4 k4 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs.k, lane * 16, blk * (8 * D), 0));
-      const uint4 v4 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs.v, lane * 16, blk * (8 * D), 0));
-      c.kc[0] = k4.x; c.kc[1] = k4.y; c.kc[2] = k4.z; c.kc[3] = k4.w;
-      c.vc[0] = v4.x; c.vc[1] = v4.y; c.vc[2] = v4.z; c.vc[3] = v4.w;
-    } else {
-      const uint2 k2 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs.k, lane * 8, blk * (8 * D), 0));
-      const uint2 v2 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs.v, lane * 8, blk * (8 * D), 0));
-      c.kc[0] = k2.x; c.kc[1] = k2.y;
-      c.vc[0] = v2.x; c.vc[1] = v2.y;
-    }
+    constexpr int LW = BITS * D / 64;   // code words per lane
+    load_lane_words<LW>(rs.k, lane * 4 * LW, blk * (4 * BITS * D), c.kc);
+    load_lane_words<LW>(rs.v, lane * 4 * LW, blk * (4 * BITS * D), c.vc);
     c.nrm0 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs.nrm, 8 * kg, blk * 64, 0));
     c.nrm1 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs.nrm, 32 + 8 * kg, blk * 64, 0));
     c.md0 = __builtin_amdgcn_raw_buffer_load_b32(rs.md, 4 * kg, moff, 0);
@@ -1150,7 +1238,7 @@ __global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(D
   // Rings with fixed registers (group j uses ring j & 1): a group's
   // statistics are fetched two groups ahead, its codes one group ahead, and
   // its operands (q~, bias) are prepared during the previous group.
-  ConsumerLoad<D> cr[2];
+  ConsumerLoad<D, BITS> cr[2];
   bool okr[2];
   uint32_t sr[2][D / 64];
   if constexpr (!TQ) {
@@ -1183,7 +1271,7 @@ __global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(D
     uint16_t* stage_nxt = r ? stage_a : stage_b;
     okr[r2] = load_codes(j + 1, cr[r2]);
     SwFront<D> f;
-    sw_front<D>(cr[r], slot_cur, kg, col, tab, lane_off, f);
+    sw_front<D, BITS>(cr[r], slot_cur, kg, col, tab, lane_off, f);
     float bias_next = bias;
     if constexpr (!TQ) {
       if (j + 1 < steps) bias_next = sw_produce<D>(sr[r2], stage_nxt, slot_nxt, qs, s_bq, lane, kg);
@@ -1191,8 +1279,8 @@ __global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(D
     }
     const int t0 = tb + (gw0 + j) * kGroupTokens;
     if (okr[r])
-      sw_back1<D, SLOTS, ASYM, TQ>(cr[r], f, bias, min(te - t0, kGroupTokens), kg, col, tab, lane_off, ws,
-                                   a.value_scale);
+      sw_back1<D, SLOTS, ASYM, TQ, BITS>(cr[r], f, bias, min(te - t0, kGroupTokens), kg, col, tab, lane_off, ws,
+                                         a.value_scale);
     bias = bias_next;
   };
   for (int j = 0; j < steps; j += 2) {
@@ -1517,17 +1605,28 @@ void launch_partition(int batch, const DecodeArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((decode_partition_kernel<D, SLOTS, NW, false, BHL>), grid, dim3(NW * 64), 0, s, a);
 }
 
-template <int D, int SLOTS>
-void launch_partition_sw(int batch, const DecodeArgs& a, hipStream_t s) {
+template <int D, int SLOTS, int BITS>
+void launch_partition_sw_bits(int batch, const DecodeArgs& a, hipStream_t s) {
   const dim3 grid(a.splits, a.hkv, batch);
   const dim3 block(kSwWaves * 64);
   if (a.key_mode == KVQ_KEYS_PER_TOKEN) {
-    if (a.cmid != 0.f) hipLaunchKernelGGL((decode_partition_sw_kernel<D, SLOTS, true, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((decode_partition_sw_kernel<D, SLOTS, false, true>), grid, block, 0, s, a);
+    if (a.cmid != 0.f)
+      hipLaunchKernelGGL((decode_partition_sw_kernel<D, SLOTS, true, true, BITS>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_partition_sw_kernel<D, SLOTS, false, true, BITS>), grid, block, 0, s, a);
   } else {
-    if (a.cmid != 0.f) hipLaunchKernelGGL((decode_partition_sw_kernel<D, SLOTS, true, false>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((decode_partition_sw_kernel<D, SLOTS, false, false>), grid, block, 0, s, a);
+    if (a.cmid != 0.f)
+      hipLaunchKernelGGL((decode_partition_sw_kernel<D, SLOTS, true, false, BITS>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_partition_sw_kernel<D, SLOTS, false, false, BITS>), grid, block, 0, s, a);
   }
+}
+
+template <int D, int SLOTS>
+void launch_partition_sw(int batch, const DecodeArgs& a, hipStream_t s) {
+  if (a.bits == 4) launch_partition_sw_bits<D, SLOTS, 4>(batch, a, s);
+  else if (a.bits == 3) launch_partition_sw_bits<D, SLOTS, 3>(batch, a, s);
+  else launch_partition_sw_bits<D, SLOTS, 2>(batch, a, s);
 }
 
 template <int D>

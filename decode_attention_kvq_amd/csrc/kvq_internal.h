@@ -39,8 +39,10 @@ struct AppendArgs {
   int32_t b0, n_new, hkv, page_tokens, max_pages, num_pages;
   double inv_sqrt_d;   // fl(1 / fl(sqrt(d))), computed on the host
   double sqrt_d;       // fl(sqrt(d))
-  double c0, c3;       // outer levels (exact fp64 images of the fp32 levels)
-  double thr0, thr1, thr2;  // decision thresholds (c_k + c_{k+1}) / 2
+  double c0, cmax;     // outer levels c0, c_{n-1} (exact fp64 images of the fp32 levels)
+  double thr[15];      // decision thresholds (c_k + c_{k+1}) / 2, k < n - 1 (then +inf)
+  int32_t nthr;        // n - 1 thresholds, n = 2^bits levels
+  int32_t bits;        // code width (2, 3, 4)
   int32_t key_mode;         // KVQ_KEYS_GROUP_MINMAX or KVQ_KEYS_PER_TOKEN
   // Query rotation fused into the same launch (kvq_append_and_rotate):
   // rot_heads query heads (0: none), q in bf16 if rot_bf16.  The launcher
@@ -83,7 +85,9 @@ struct DecodeArgs {
   float value_scale;      // 1 / sqrt(d)
   float cmid, chalf;      // codebook centre (c0 + c3) / 2 and half range (c3 - c0) / 2
   int32_t key_mode;       // KVQ_KEYS_GROUP_MINMAX or KVQ_KEYS_PER_TOKEN
-  uint32_t level_f16[2];  // normalized levels (2 c_k - c0 - c3) / (c3 - c0) as fp16 bits, k = 0..3
+  int32_t bits;           // code width (2, 3, 4)
+  uint32_t level_f16[8];  // normalized levels (2 c_k - c0 - c_{n-1}) / (c_{n-1} - c0) as fp16 bits, k < n
+  uint32_t level_lo_f16[8]; // 2^12 (level - fp16 level) as fp16 bits (3 / 4 bits: the scores' lo part)
   uint2 byte_levels[256]; // byte e of four 2-bit codes -> its four fp16 levels (code of bits 2i..2i+1 first)
 };
 

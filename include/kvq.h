@@ -28,20 +28,28 @@
  *     groups aligned to absolute positions 32g.
  *
  * Packed cache (paged; a contiguous cache is an identity page table).
- * page_tokens is a multiple of 32; GP = page_tokens / 32 groups per page.
- * Physical page p, KV head h, group-in-page j, position-in-page s:
- *   k_codes  [num_pages][Hkv][GP][8d] bytes   2-bit key codes of one group
- *   v_codes  [num_pages][Hkv][GP][8d] bytes   2-bit value codes of one group
+ * page_tokens is a multiple of 32; GP = page_tokens / 32 groups per page;
+ * b = kvq_config.bits.  Physical page p, KV head h, group-in-page j,
+ * position-in-page s:
+ *   k_codes  [num_pages][Hkv][GP][4bd] bytes  b-bit key codes of one group
+ *   v_codes  [num_pages][Hkv][GP][4bd] bytes  b-bit value codes of one group
  *   k_stats  [num_pages][Hkv][GP][2][d] fp16  rotated-key group min (row 0) and max (row 1)
  *   v_norms  [num_pages][Hkv][page_tokens] fp16  value norms
  *   modality [num_pages][page_tokens] uint8
- * Inside one 8d-byte group block the codes are laid out for the decode
- * kernel's matrix-core operands ("lane-major").  With W = d/8 bytes per lane
- * and lane L in [0, 64):
+ * Inside one 4bd-byte group block the codes are laid out for the decode
+ * kernel's matrix-core operands ("lane-major"): lane L in [0, 64) owns the
+ * W = bd/16 bytes at L*W, read as a little-endian bit stream of operand
+ * units of 8 codes (8b bits); code k of unit u starts at bit 8b*u + b*k:
  *   key   (token t in 0..31, channel c): L = ((c % 32) / 8) * 16 + t % 16,
- *         byte = L*W + (t / 16)*(d/16) + (c / 32)*2 + (c % 8) / 4, bits 2*(c % 4)
+ *         u = (t / 16)*(d/32) + c / 32, k = c % 8
  *   value (token t, channel c):          L = ((t % 16) / 4) * 16 + c % 16,
- *         byte = L*W + (c / 16)*2 + t / 16, bits 2*(t % 4)
+ *         u = c / 16, k = (t / 16)*4 + t % 4
+ * With b = 2 this is byte L*W + (t/16)*(d/16) + (c/32)*2 + (c%8)/4, bits
+ * 2*(c%4) for keys and byte L*W + (c/16)*2 + t/16, bits 2*(t%4) for values.
+ * 3- and 4-bit codes (Sec. 3 Experiments, ablation over 2 to 4 bits) are
+ * decoded by the streaming partition kernel only: G <= 8, page_tokens a
+ * power of two and every cache array below 2^31 bytes (KVQ_ERR_UNSUPPORTED
+ * otherwise).
  * Slots past the session length hold unspecified codes and are never read
  * as data.  The raw key tail keeps the keys of the open (partial) group:
  *   k_tail   [batch][Hkv][32][d] in kv_dtype, slot = position % 32
@@ -107,6 +115,7 @@ typedef struct kvq_config {
   int32_t num_pages;    /* physical pages in the pool */
   int32_t kv_dtype;     /* kvq_dtype of appended K/V (and of the raw key tail) */
   int32_t key_mode;     /* kvq_key_mode: the key codec of the whole cache */
+  int32_t bits;         /* code width b: 2, 3 or 4 bits per element, 2^b codebook levels */
 } kvq_config;
 
 typedef struct kvq_cache {
@@ -128,7 +137,8 @@ typedef struct kvq_cache {
 typedef struct kvq_params {
   const int8_t* signs;        /* device [Hkv][d], each +1 or -1: Hadamard signs per KV head */
   const float*  rot;          /* device [Hkv][3][d][d] row-major R_{h,m}; columns are the basis */
-  float         codebook[4];  /* strictly increasing reconstruction levels c0 < c1 < c2 < c3 */
+  float         codebook[16]; /* the first n = 2^bits entries: strictly increasing reconstruction
+                                 levels c0 < ... < c_{n-1}; the rest is ignored */
 } kvq_params;
 
 /* Bytes of each cache buffer for a configuration, in the order k_codes,

@@ -36,8 +36,9 @@ def build(w: Workload, page_table: Optional[np.ndarray] = None, chunks: Optional
     kv_dtype = torch.bfloat16 if c.dtype == "bf16" else torch.float32
     pt = w.page_table if page_table is None else page_table
     num_pages = int(pt.max()) + 1 if num_pages is None else int(num_pages)
+    bits = int(len(w.codebook)).bit_length() - 1          # 4, 8 or 16 levels
     cfg = K.Config(c.head_dim, c.n_q_heads, c.n_kv_heads, c.batch, w.page_tokens, pt.shape[1],
-                   num_pages, kv_dtype, key_mode)
+                   num_pages, kv_dtype, key_mode, bits)
     rot = w.rot if rot is None else np.ascontiguousarray(rot, dtype=np.float32)
     params = K.Params(torch.from_numpy(w.signs).to(device), torch.from_numpy(rot).to(device),
                       w.codebook.tolist())

@@ -42,13 +42,13 @@ def test_library_exports_every_declared_symbol():
 
 def _cfg(L, **kw):
     base = dict(head_dim=128, n_q_heads=16, n_kv_heads=2, batch=2, page_tokens=256, max_pages=4,
-                num_pages=8, kv_dtype=L.KVQ_BF16, key_mode=L.KVQ_KEYS_GROUP_MINMAX)
+                num_pages=8, kv_dtype=L.KVQ_BF16, key_mode=L.KVQ_KEYS_GROUP_MINMAX, bits=2)
     base.update(kw)
     return L.KvqConfig(*[base[f] for f, _ in L.KvqConfig._fields_])
 
 
 def _fake_params(L, codebook=(-1.5104, -0.4528, 0.4528, 1.5104)):
-    return L.KvqParams(0x1000, 0x2000, (ctypes.c_float * 4)(*codebook))
+    return L.KvqParams(0x1000, 0x2000, (ctypes.c_float * 16)(*codebook, *([0.0] * (16 - len(codebook)))))
 
 
 def _fake_cache(L, lengths):
@@ -61,6 +61,7 @@ def _fake_cache(L, lengths):
     (dict(head_dim=96), 2), (dict(head_dim=256), 2), (dict(n_q_heads=15), 1),
     (dict(n_q_heads=34, n_kv_heads=2), 2), (dict(page_tokens=100), 1), (dict(batch=0), 1),
     (dict(kv_dtype=7), 2), (dict(max_pages=0), 1), (dict(key_mode=2), 1), (dict(key_mode=-1), 1),
+    (dict(bits=1), 2), (dict(bits=5), 2), (dict(bits=8), 2),
 ])
 def test_config_validation(kw, status):
     L, lib = _lib()
@@ -68,12 +69,27 @@ def test_config_validation(kw, status):
     assert lib.kvq_cache_buffer_bytes(ctypes.byref(_cfg(L, **kw)), out) == status
 
 
-def test_buffer_sizes():
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_buffer_sizes(bits):
     L, lib = _lib()
     out = (ctypes.c_size_t * 6)()
-    assert lib.kvq_cache_buffer_bytes(ctypes.byref(_cfg(L)), out) == 0
+    assert lib.kvq_cache_buffer_bytes(ctypes.byref(_cfg(L, bits=bits)), out) == 0
     groups = 8 * 2 * 8
-    assert list(out) == [groups * 1024, groups * 512, groups * 1024, 8 * 2 * 256 * 2, 8 * 256, 2 * 2 * 32 * 128 * 2]
+    code = groups * 4 * bits * 128                       # 4 b d bytes per group block
+    assert list(out) == [code, groups * 512, code, 8 * 2 * 256 * 2, 8 * 256, 2 * 2 * 32 * 128 * 2]
+
+
+def test_codebook_must_increase_over_its_2_to_the_bits_levels():
+    L, lib = _lib()
+    c, lens = _fake_cache(L, [0, 0])
+    ok8 = _fake_params(L, tuple(float(x) for x in range(-4, 4)))
+    bad8 = _fake_params(L, (-3.0, -2.0, -1.0, 0.0, 0.5, 0.4, 2.0, 3.0))
+    short = _fake_params(L)                                         # 4 levels, then zeros
+    for p, st in [(ok8, 0), (bad8, 1), (short, 1)]:
+        cfg = _cfg(L, bits=3)
+        # an empty append validates every argument and launches nothing
+        assert lib.kvq_quantize_append(ctypes.byref(cfg), ctypes.byref(c), ctypes.byref(p), 0, 2, 0,
+                                       ctypes.c_void_p(8), ctypes.c_void_p(8), ctypes.c_void_p(8), None) == st
 
 
 def test_append_rejects_bad_arguments_without_launching():
