@@ -249,7 +249,12 @@ def main():
 
     calib = time_calibration(L0)
     del g_step, g_dec, g_warm
-    turbo = time_turboquant_decode(w, table, L0, args.replicas, n_dec, scale)
+    import decode_attention_kvq_amd as K_
+    from tests import kvq_harness as H_
+    turbo = time_variant_decode(w, table, L0, args.replicas, n_dec, scale, key_mode=K_.KVQ_KEYS_PER_TOKEN,
+                                rot=H_.hadamard_rot(w))
+    turbo["workload"] = "same 80K decode, per-token keys + shared Hadamard values"
+    wide = {f"{b}bit": time_variant_decode(w, table, L0, args.replicas, n_dec, scale, bits=b) for b in (3, 4)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -278,23 +283,29 @@ def main():
                   "copy_read_write_GBps": copy_bytes / (copy_ms * 1e-3) / 1e9,
                   "step_wall_us": wall / steps * 1e6,
                   "value_calibration": calib,
-                  "turboquant_baseline": turbo},
+                  "turboquant_baseline": turbo,
+                  "wider_codes": wide},
     }
     print(json.dumps(rec), flush=True)
 
 
-def time_turboquant_decode(w, table, L0: int, replicas: int, n_dec: int, scale: float) -> dict:
-    """The TurboQuant baseline through the same kernels: per-token key norms
-    instead of group statistics, the shared randomized Hadamard as every
-    value basis; the same 80K context on `replicas` HBM-resident caches,
-    decode launches only, HIP events on the launch stream."""
+def time_variant_decode(w, table, L0: int, replicas: int, n_dec: int, scale: float, key_mode: int = 0,
+                        rot=None, bits: int = 2) -> dict:
+    """The same 80K decode for another cache variant through the same
+    kernels: per-token keys (key_mode 1) and / or other value bases, or 3- /
+    4-bit codes (the stream's own tokens with the wider codebook); `replicas`
+    HBM-resident caches, decode launches only, HIP events on the launch
+    stream."""
+    import dataclasses
+
     import torch
     import decode_attention_kvq_amd as K
+    from omnistream import lloyd_max_codebook
     from tests import kvq_harness as H
 
     dev = torch.device("cuda", 0)
-    cfg, params, c0 = H.build(w, page_table=table, upto=[L0], key_mode=K.KVQ_KEYS_PER_TOKEN,
-                              rot=H.hadamard_rot(w))
+    wv = dataclasses.replace(w, codebook=lloyd_max_codebook(bits)) if bits != 2 else w
+    cfg, params, c0 = H.build(wv, page_table=table, upto=[L0], key_mode=key_mode, rot=rot)
     caches = [c0]
     for _ in range(replicas - 1):
         cc = K.Cache(cfg, torch.from_numpy(table), device=dev)
@@ -302,7 +313,7 @@ def time_turboquant_decode(w, table, L0: int, replicas: int, n_dec: int, scale: 
             getattr(cc, name).copy_(getattr(c0, name))
         cc.set_lengths(c0.lengths())
         caches.append(cc)
-    q_rot = K.kvq_rotate_query(cfg, params, H.query_tensor(w, dev))
+    q_rot = K.kvq_rotate_query(cfg, params, H.query_tensor(wv, dev))
     out = torch.empty(q_rot.shape, dtype=torch.float32, device=dev)
     ws = torch.empty(K.kvq_decode_workspace_bytes(cfg, L0), dtype=torch.uint8, device=dev)
     for cc in caches:
@@ -326,12 +337,13 @@ def time_turboquant_decode(w, table, L0: int, replicas: int, n_dec: int, scale: 
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / (n_dec * replicas)
     d, hq, hkv = w.cfg.head_dim, w.cfg.n_q_heads, w.cfg.n_kv_heads
-    # per (position, KV head): key and value codes (d / 4 bytes each), two fp16 norms
-    nbytes = L0 * hkv * (d // 4 + d // 4 + 4) + L0 + hkv * 3 * d * d * 4 + 2 * hq * d * 4
+    # per (position, KV head): key and value codes (b d / 8 bytes each), the
+    # key statistics (2 d fp16 per 32 positions) or a key norm, a value norm
+    per = 2 * bits * d // 8 + (4 if key_mode else (2 * d * 2) // 32 + 2)
+    nbytes = L0 * hkv * per + L0 + hkv * 3 * d * d * 4 + 2 * hq * d * 4
     del g, caches
-    return {"workload": "same 80K decode, per-token keys + shared Hadamard values",
-            "decode_us_hbm": ms * 1e3, "bytes_per_launch": nbytes,
-            "achieved_GBps": nbytes / (ms * 1e-3) / 1e9}
+    return {"decode_us_hbm": ms * 1e3, "bytes_per_launch": nbytes, "achieved_GBps": nbytes / (ms * 1e-3) / 1e9,
+            "frac_of_8TBps": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
 def time_calibration(n_tokens: int, n_queries: int = 8, repeats: int = 5) -> dict:
