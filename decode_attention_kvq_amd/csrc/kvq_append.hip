@@ -118,9 +118,11 @@ struct ValSmem {
 
 // Level index of a normalised value: the number of decision thresholds it
 // reaches (the thresholds ascend; ties go up).
+template <int BITS>
 __device__ __forceinline__ uint32_t level_index(const AppendArgs& a, double z) {
   uint32_t c = 0;
-  for (int i = 0; i < a.nthr; ++i) c += z >= a.thr[i] ? 1u : 0u;
+#pragma unroll
+  for (int i = 0; i < (1 << BITS) - 1; ++i) c += z >= a.thr[i] ? 1u : 0u;
   return c;
 }
 
@@ -176,7 +178,7 @@ union AppendSmem {
   ValSmem<D> v;
 };
 
-template <int D, bool BF16>
+template <int D, bool BF16, int BITS>
 __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
   constexpr int CH = D / kPosThreads;             // channels per thread (inputs, transform, key codes)
   constexpr int ESZ = BF16 ? 2 : 4;
@@ -245,15 +247,15 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
   // The key block of the group: 2 bits as built in LDS, wider codes packed
   // from one byte per code.
   auto store_key_block = [&](long long blk_) {
-    if (a.bits == 2) {
+    if (BITS == 2) {
       if (tid < D / 2) {
         uint4* dst = reinterpret_cast<uint4*>(a.k_codes + static_cast<size_t>(blk_) * 8 * D);
         dst[tid] = reinterpret_cast<const uint4*>(sm.k.kblk)[tid];
       }
     } else {
-      uint32_t* dst = reinterpret_cast<uint32_t*>(a.k_codes + static_cast<size_t>(blk_) * 4 * a.bits * D);
-      for (int w = tid; w < a.bits * D; w += kAppendThreads)
-        dst[w] = pack_word<D, false>(a.bits, w, [&](int t, int c) { return static_cast<uint32_t>(sm.k.code[t][c]); });
+      uint32_t* dst = reinterpret_cast<uint32_t*>(a.k_codes + static_cast<size_t>(blk_) * 4 * BITS * D);
+      for (int w = tid; w < BITS * D; w += kAppendThreads)
+        dst[w] = pack_word<D, false>(BITS, w, [&](int t, int c) { return static_cast<uint32_t>(sm.k.code[t][c]); });
     }
   };
 
@@ -326,12 +328,12 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
             uint32_t code = 0;
             if (present && n > 0.0) {
               const double z = (a.sqrt_d * x[4 * q4 + i]) / n;
-              code = level_index(a, z);
+              code = level_index<BITS>(a, z);
             }
             byte |= code << (2 * i);
-            sm.k.code[tok][cb + 4 * q4 + i] = static_cast<uint8_t>(code);
+            if (BITS != 2) sm.k.code[tok][cb + 4 * q4 + i] = static_cast<uint8_t>(code);
           }
-          if (a.bits == 2) sm.k.kblk[key_code_byte<D>(tok, cb + 4 * q4)] = static_cast<uint8_t>(byte);
+          if (BITS == 2) sm.k.kblk[key_code_byte<D>(tok, cb + 4 * q4)] = static_cast<uint8_t>(byte);
         }
         if (part == 0) a.k_stats[static_cast<size_t>(blk) * 2 * D + tok] = present ? f64_to_f16_rne(n) : uint16_t(0);
         __syncthreads();
@@ -387,12 +389,12 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
           const double LO = sm.k.lohi[0][c], f = sm.k.lohi[1][c];
           if (present && f > 0.0) {
             const double z = a.c0 + (x[4 * q4 + i] - LO) * f;
-            code = level_index(a, z);
+            code = level_index<BITS>(a, z);
           }
           byte |= code << (2 * i);
-          sm.k.code[tok][c] = static_cast<uint8_t>(code);
+          if (BITS != 2) sm.k.code[tok][c] = static_cast<uint8_t>(code);
         }
-        if (a.bits == 2) sm.k.kblk[key_code_byte<D>(tok, cb + 4 * q4)] = static_cast<uint8_t>(byte);
+        if (BITS == 2) sm.k.kblk[key_code_byte<D>(tok, cb + 4 * q4)] = static_cast<uint8_t>(byte);
       }
       __syncthreads();
       store_key_block(blk);
@@ -437,11 +439,11 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
     // Round trip 3 (needed only at the end): the group's stored value codes,
     // for positions before s_first.  The 8D-byte block is 2D words: thread
     // tid < 2D owns word tid.
-    uint8_t* vb = a.v_codes + static_cast<size_t>(blk) * 4 * a.bits * D;
-    const bool vword = a.bits == 2 && tid < 2 * D;
+    uint8_t* vb = a.v_codes + static_cast<size_t>(blk) * 4 * BITS * D;
+    const bool vword = BITS == 2 && tid < 2 * D;
     const uint32_t old_v = (s_first > 0 && vword) ? reinterpret_cast<const uint32_t*>(vb)[tid] : 0u;
-    if (a.bits != 2 && s_first > 0)
-      for (int w = tid; w < a.bits * D; w += kAppendThreads) sm.v.oldw[w] = reinterpret_cast<const uint32_t*>(vb)[w];
+    if (BITS != 2 && s_first > 0)
+      for (int w = tid; w < BITS * D; w += kAppendThreads) sm.v.oldw[w] = reinterpret_cast<const uint32_t*>(vb)[w];
 
     // Modalities among the new positions (every wave computes the same mask).
     uint32_t mods = 0;
@@ -463,9 +465,9 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
     if (part == 0) sm.v.n[tok] = sqrt(ss);
     __syncthreads();
     // 3- / 4-bit: the earlier positions' codes, out of the stored block
-    if (a.bits != 2)
+    if (BITS != 2)
       for (int e = tid; e < s_first * D; e += kAppendThreads)
-        sm.v.code[e / D][e % D] = static_cast<uint8_t>(unpack_value_code<D>(a.bits, sm.v.oldw, e / D, e % D));
+        sm.v.code[e / D][e % D] = static_cast<uint8_t>(unpack_value_code<D>(BITS, sm.v.oldw, e / D, e % D));
 
     // ---- r = R_m^T v, one modality at a time (the rows of modality mpre
     // were loaded above): four interleaved partial sums over the part's rows,
@@ -489,7 +491,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
           uint32_t code = 0;
           if (n > 0.0) {
             const double z = (a.sqrt_d * r) / n;
-            code = level_index(a, z);
+            code = level_index<BITS>(a, z);
           }
           sm.v.code[s][jc] = static_cast<uint8_t>(code);
         }
@@ -522,14 +524,14 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
       }
       reinterpret_cast<uint32_t*>(vb)[tid] = outw;
     }
-    if (a.bits != 2) {
+    if (BITS != 2) {
       auto vcode = [&](int t, int c) -> uint32_t {
         if (t < s_first) return sm.v.code[t][c];
         if (t < s_end) return sm.v.mod[t] < kModalities ? sm.v.code[t][c] : 0u;
         return 0u;
       };
-      for (int w = tid; w < a.bits * D; w += kAppendThreads)
-        reinterpret_cast<uint32_t*>(vb)[w] = pack_word<D, true>(a.bits, w, vcode);
+      for (int w = tid; w < BITS * D; w += kAppendThreads)
+        reinterpret_cast<uint32_t*>(vb)[w] = pack_word<D, true>(BITS, w, vcode);
     }
     if (tid < kGroupTokens && tid >= s_first && tid < s_end) {
       const int pos = (t0 + tid) % a.page_tokens;
@@ -565,7 +567,9 @@ hipError_t launch_append_t(int nb, AppendArgs a, hipStream_t s) {
   const int rot_wgs = (a.rot_heads + kAppendThreads / rotq::kLanes - 1) / (kAppendThreads / rotq::kLanes);
   const int rot_x = (rot_wgs + a.hkv * nb - 1) / (a.hkv * nb);
   const dim3 grid(a.append_x + rot_x, a.hkv, nb);
-  hipLaunchKernelGGL((append_kernel<D, BF16>), grid, dim3(kAppendThreads), 0, s, a);
+  if (a.bits == 4) hipLaunchKernelGGL((append_kernel<D, BF16, 4>), grid, dim3(kAppendThreads), 0, s, a);
+  else if (a.bits == 3) hipLaunchKernelGGL((append_kernel<D, BF16, 3>), grid, dim3(kAppendThreads), 0, s, a);
+  else hipLaunchKernelGGL((append_kernel<D, BF16, 2>), grid, dim3(kAppendThreads), 0, s, a);
   return hipGetLastError();
 }
 
