@@ -941,9 +941,9 @@ __device__ __forceinline__ void sw_front(const ConsumerLoad<D, BITS>& cur, const
 // current reference max right away; the group's own max only decides (off the
 // critical path) whether the reference must move first, which is rare: the
 // reference sits kLazyMax above every score seen so far.  Groups of one single
-// modality (the common case inside a video, audio or text run) take one
-// branch to their accumulator set; others go through per-position modality
-// masks.
+// modality (the common case inside a video, audio or text run) form their
+// weight operands with one select per set; others go through per-position
+// modality masks.
 //
 // Per-token key mode (TQ): score i is (bias + dot_i) N_i / sqrt(d), with the
 // key norm N_i of the lane's position i (fp16 pairs in knrm0 / knrm1, in the
@@ -1009,43 +1009,35 @@ __device__ __forceinline__ void sw_back1(const ConsumerLoad<D, BITS>& ca, const 
     weights(ws.m_run);
   }
   ws.l_run += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
+  // Weight operands of the accumulator sets: set k's column (slot_c, hp)
+  // keeps the positions whose modality is k SLOTS + slot_c.  Only these
+  // operands depend on the branch; every set then takes its matrix-core
+  // products unconditionally (a set without its modalities adds exact
+  // zeros), so the accumulators are updated in place, never copied.  The
+  // lane's modality bits go into ws.mask, OR-ed over the wavefront at the end.
   const int slot_c = col / GP;
-  auto accumulate = [&](int k, const uint32_t (&ba)[4]) {
-    const half8 bwa = __builtin_bit_cast(half8, uint4{ba[0], ba[1], ba[2], ba[3]});
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      const half8 va = unit_operand<BITS>(ca.vc, ct, tab, lane_off);   // channels 16 ct + lane % 16
-      ws.acc[k][ct] = mfma(va, bwa, ws.acc[k][ct]);
-    }
-    if constexpr (ASYM) {
-      const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
-      ws.accs[k] = mfma(ones, bwa, ws.accs[k]);
-    }
-  };
+  uint32_t bs[NSETS][4];
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(ca.md0 & 0xFFu);
   const uint32_t mm = m0 * 0x01010101u;
   const bool uniform = rem_a == kGroupTokens && m0 < kModalities && __all(ca.md0 == mm && ca.md1 == mm);
   if (uniform) {
     const int k0 = static_cast<int>(m0) / SLOTS;
     const bool take = slot_c == static_cast<int>(m0) - k0 * SLOTS;
-    uint32_t ba[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) ba[r] = take ? wa[r] : 0u;
 #pragma unroll
     for (int k = 0; k < NSETS; ++k)
-      if (k == k0) accumulate(k, ba);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) bs[k][r] = (take && k == k0) ? wa[r] : 0u;
     ws.mask |= 1 << m0;
   } else {
     int ra = rem_a;
     uint32_t mda[2] = {ca.md0, ca.md1};
     asm volatile("" : "+s"(ra), "+v"(mda[0]), "+v"(mda[1]));
+    int got = 0;
 #pragma unroll
     for (int k = 0; k < NSETS; ++k) {
       const uint32_t lo_mod = static_cast<uint32_t>(k * SLOTS);
       const uint32_t my_mod = lo_mod + static_cast<uint32_t>(slot_c);
       const bool col_ok = slot_c < SLOTS && my_mod < kModalities;
-      uint32_t ba[4];
-      int got = 0;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         uint32_t keep_a = 0;
@@ -1056,13 +1048,24 @@ __device__ __forceinline__ void sw_back1(const ConsumerLoad<D, BITS>& ca, const 
           if (group_pos(kg, i) < ra && ta >= lo_mod && ta < lo_mod + SLOTS && ta < kModalities) got |= 1 << ta;
           keep_a |= (col_ok && ta == my_mod) ? (0xFFFFu << (16 * u)) : 0u;
         }
-        ba[r] = wa[r] & keep_a;
-      }
-      if (__any(got != 0)) {
-        accumulate(k, ba);
-        ws.mask |= wave_or_bits(got);
+        bs[k][r] = wa[r] & keep_a;
       }
     }
+    ws.mask |= got;
+  }
+  half8 bw[NSETS];
+#pragma unroll
+  for (int k = 0; k < NSETS; ++k) bw[k] = __builtin_bit_cast(half8, uint4{bs[k][0], bs[k][1], bs[k][2], bs[k][3]});
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    const half8 va = unit_operand<BITS>(ca.vc, ct, tab, lane_off);   // channels 16 ct + lane % 16
+#pragma unroll
+    for (int k = 0; k < NSETS; ++k) ws.acc[k][ct] = mfma(va, bw[k], ws.acc[k][ct]);
+  }
+  if constexpr (ASYM) {
+    const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
+#pragma unroll
+    for (int k = 0; k < NSETS; ++k) ws.accs[k] = mfma(ones, bw[k], ws.accs[k]);
   }
 }
 
