@@ -838,8 +838,8 @@ struct SwShape {
 // c3 - c0 (`range`): q~ is the same for every group.
 template <int D, bool TQ = false>
 __device__ __forceinline__ float sw_produce(const uint32_t (&st)[D / 64], uint16_t* stage, SwSlot<D>* slot,
-                                            const float (&qs)[SwShape<D>::HPL][8], const uint4* bq_lds, int lane,
-                                            int kg, float range = 0.f) {
+                                            const float (&qs)[SwShape<D>::HPL][8], const uint4 (&bq)[D / 32],
+                                            int lane, int kg, float range = 0.f) {
   constexpr int KT = D / 32;
   constexpr int CB = SwShape<D>::CB;
   constexpr int HPL = SwShape<D>::HPL;
@@ -854,7 +854,7 @@ __device__ __forceinline__ float sw_produce(const uint32_t (&st)[D / 64], uint16
 #pragma unroll
   for (int kt = 0; kt < KT; ++kt)
     bacc = mfma(__builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(arow + 32 * kt + 8 * kg)),
-                __builtin_bit_cast(half8, bq_lds[kt * 64 + lane]), bacc);
+                __builtin_bit_cast(half8, bq[kt]), bacc);
   const int cb = lane % CB, hs = lane / CB;
   const uint4 lo4 = *reinterpret_cast<const uint4*>(stage + 8 * cb);
   const uint4 hi4 = *reinterpret_cast<const uint4*>(stage + D + 8 * cb);
@@ -1259,12 +1259,15 @@ __global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(D
     for (int i = 0; i < D / 64; ++i) sr[0][i] = lane < 32 ? h2 : l2;
   }
   okr[0] = load_codes(0, cr[0]);
+  uint4 bqr[KT];   // the bias operand, the same for every group: kept in registers
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) bqr[kt] = s_bq[kt * 64 + lane];
   float qs[HPL][8];
   float bias = 0.f;
   if (steps > 0) {
     read_qs(qs);
-    if constexpr (TQ) bias = sw_produce<D, true>(sr[0], stage_a, slot_a, qs, s_bq, lane, kg, 2.f * a.chalf);
-    else bias = sw_produce<D>(sr[0], stage_a, slot_a, qs, s_bq, lane, kg);
+    if constexpr (TQ) bias = sw_produce<D, true>(sr[0], stage_a, slot_a, qs, bqr, lane, kg, 2.f * a.chalf);
+    else bias = sw_produce<D>(sr[0], stage_a, slot_a, qs, bqr, lane, kg);
   }
   auto step = [&](int j, auto ring) {
     constexpr int r = decltype(ring)::value;
@@ -1277,7 +1280,7 @@ __global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(D
     sw_front<D, BITS>(cr[r], slot_cur, kg, col, tab, lane_off, f);
     float bias_next = bias;
     if constexpr (!TQ) {
-      if (j + 1 < steps) bias_next = sw_produce<D>(sr[r2], stage_nxt, slot_nxt, qs, s_bq, lane, kg);
+      if (j + 1 < steps) bias_next = sw_produce<D>(sr[r2], stage_nxt, slot_nxt, qs, bqr, lane, kg);
       load_stats(j + 2, sr[r]);
     }
     const int t0 = tb + (gw0 + j) * kGroupTokens;
