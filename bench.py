@@ -33,8 +33,8 @@ HBM_PEAK_GBS = 8000.0
 # what the counter reads for a plain 256 MiB device copy (FETCH_SIZE x 1.9997,
 # WRITE_SIZE x 1.0); see profiles/decode_80k_hbm_bytes.md.  Valid only for
 # the decode source the counters were taken on (SHA-256 of kvq_decode.hip).
-DECODE_TRAFFIC = {"kvq_decode_sha256": "d44196174b0f345c83899e61c8b6e35a3708a4153227b42c232d4c1f2a5aff5b",
-                  "bytes": 34950218}
+DECODE_TRAFFIC = {"kvq_decode_sha256": "d653c69b43dd53d2b8656456fb67011f6f25f85b7f51df840714c208efbf20d9",
+                  "bytes": 34897435}
 
 
 def decode_traffic_bytes():
