@@ -1108,10 +1108,11 @@ __global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(D
   const int tb = split * a.split_tokens;
   const int te = (split == a.splits - 1) ? L : min(tb + a.split_tokens, L);
   const int ng = te > tb ? (te - tb + kGroupTokens - 1) / kGroupTokens : 0;   // groups of the partition
-  // Each wavefront takes a contiguous run of `steps` groups, starting at gw0,
-  // two at a time.
+  // The groups are dealt to the wavefronts round robin: step j of wavefront
+  // w is group w + NW j, so the NW wavefronts read NW adjacent blocks at a
+  // time, and the mapped pages of a sparse page set (a 256-position page
+  // holds 8 groups) fall to every wavefront alike.
   const int steps = (ng + NW - 1) / NW;
-  const int gw0 = wave * steps;
   const int ps = a.page_shift;                     // page_tokens is a power of two here
   const int pmask = a.page_tokens - 1;
   const int page0 = tb >> ps;
@@ -1191,7 +1192,7 @@ __global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(D
   // Group j of the wavefront's run: block and modality offsets (block 0 for
   // an invalid group, see sw_load); returns whether the group is valid.
   auto locate = [&](int j, int& blk, int& moff) {
-    const int gi = gw0 + j;
+    const int gi = wave + NW * j;
     const int t0 = tb + gi * kGroupTokens;
     const int phys = __builtin_amdgcn_readfirstlane(s_pt[min((t0 >> ps) - page0, kPageRun - 1)]);
     const bool ok = j < steps && gi < ng && phys >= 0 && phys < a.num_pages;
@@ -1276,14 +1277,17 @@ __global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(D
     SwSlot<D>* slot_nxt = r ? slot_a : slot_b;
     uint16_t* stage_nxt = r ? stage_a : stage_b;
     okr[r2] = load_codes(j + 1, cr[r2]);
+    // A group on an unmapped page (or past the run) costs only its loop
+    // step: no scores, no operands for it, no softmax (the branches are
+    // uniform; a skipped group leaves its q~ slot untouched).
     SwFront<D> f;
-    sw_front<D, BITS>(cr[r], slot_cur, kg, col, tab, lane_off, f);
+    if (okr[r]) sw_front<D, BITS>(cr[r], slot_cur, kg, col, tab, lane_off, f);
     float bias_next = bias;
     if constexpr (!TQ) {
-      if (j + 1 < steps) bias_next = sw_produce<D>(sr[r2], stage_nxt, slot_nxt, qs, bqr, lane, kg);
+      if (j + 1 < steps && okr[r2]) bias_next = sw_produce<D>(sr[r2], stage_nxt, slot_nxt, qs, bqr, lane, kg);
       load_stats(j + 2, sr[r]);
     }
-    const int t0 = tb + (gw0 + j) * kGroupTokens;
+    const int t0 = tb + (wave + NW * j) * kGroupTokens;
     if (okr[r])
       sw_back1<D, SLOTS, ASYM, TQ, BITS>(cr[r], f, bias, min(te - t0, kGroupTokens), kg, col, tab, lane_off, ws,
                                          a.value_scale);
