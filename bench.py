@@ -33,8 +33,8 @@ HBM_PEAK_GBS = 8000.0
 # what the counter reads for a plain 256 MiB device copy (FETCH_SIZE x 1.9997,
 # WRITE_SIZE x 1.0); see profiles/decode_80k_hbm_bytes.md.  Valid only for
 # the decode source the counters were taken on (SHA-256 of kvq_decode.hip).
-DECODE_TRAFFIC = {"kvq_decode_sha256": "d653c69b43dd53d2b8656456fb67011f6f25f85b7f51df840714c208efbf20d9",
-                  "bytes": 34897435}
+DECODE_TRAFFIC = {"kvq_decode_sha256": "fb0af28a8adb44a0e86a5f4c2ab31b6e1b4d06614c0c3e0999a7add4728270a1",
+                  "bytes": 34910618}
 
 
 def decode_traffic_bytes():
