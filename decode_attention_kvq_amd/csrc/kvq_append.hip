@@ -210,16 +210,36 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
   const int lane = tid & 63;
   const int tok = tid / kPosThreads, part = tid % kPosThreads, cb = part * CH;
 
-  // Round trip 1: the session length; the value workgroup also reads the
-  // modalities of every new position its group could hold (rows
-  // [32 j - 32, 32 j + 32) of the append, whatever the old length), which
-  // pick the rotation rows it prefetches.
+  // Round trip 1: every load that needs only the kernel arguments, issued
+  // together and without branching on the role (a branch would make the
+  // compiler wait for one role's loads before the next ones): the signs of
+  // channels cb.. (the key transform), the modalities of every new position
+  // the group could hold (rows [32 j - 32, 32 j + 32) of the append,
+  // whatever the old length: they pick the rotation rows the value
+  // workgroup prefetches), and the session length.  A one-position append
+  // (the decode step) also reads its input rows here: row tok of the raw
+  // tail and the new row (key workgroup: position tok of the open group is
+  // one of the two), or the new row (value workgroup).  Longer appends read
+  // theirs once the length has placed the group.
+  const bool one = a.n_new == 1;
+  uint32_t sgw[CH / 4];
+#pragma unroll
+  for (int k = 0; k < CH / 4; ++k) sgw[k] = reinterpret_cast<const uint32_t*>(a.signs + h * D + cb)[k];
+  const int widx = 32 * j - 32 + lane;
+  const bool wok = widx >= 0 && widx < a.n_new;
+  const uint32_t wmod = a.modality_new[static_cast<size_t>(b) * a.n_new + min(max(widx, 0), a.n_new - 1)];
+  uint32_t w_tail[NWORDS], w_one[NWORDS];
+  if (one) {
+    const char* tail_row = static_cast<const char*>(a.k_tail) +
+                           (((static_cast<size_t>(sb) * a.hkv + h) * kGroupTokens + tok) * D + cb) * ESZ;
+    const char* new_row = static_cast<const char*>(vrole ? a.v_new : a.k_new) +
+                          ((static_cast<size_t>(b) * a.hkv + h) * D + cb) * ESZ;
+    load_words(tail_row, w_tail);
+    load_words(new_row, w_one);
+  }
   const int L_old = a.seq_len[sb];
   int mpre = 0;
   if (vrole) {
-    const int widx = 32 * j - 32 + lane;
-    const bool wok = widx >= 0 && widx < a.n_new;
-    const uint32_t wmod = a.modality_new[static_cast<size_t>(b) * a.n_new + min(max(widx, 0), a.n_new - 1)];
     uint32_t wmods = 0;
 #pragma unroll
     for (int m = 0; m < kModalities; ++m)
@@ -227,22 +247,39 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
     mpre = wmods ? __builtin_ctz(wmods) : 0;
   }
 
-  // Round trip 2: page table, inputs, and (values) the prefetched rotation rows.
+  // Round trip 2: the page table, the inputs of a longer append, and (values)
+  // the prefetched rotation rows.  The arithmetic does not wait for the
+  // page: only the stores (and the read of the group's earlier value codes)
+  // need it, so a group on an unmapped page is computed and dropped.
   const int L_new = L_old + a.n_new;
   const int t0 = (L_old / kGroupTokens + j) * kGroupTokens;
   const bool active = t0 < L_new;
-  int phys = -1;
-  if (active) {
-    const int page = t0 / a.page_tokens;
-    phys = page < a.max_pages ? a.page_table[static_cast<size_t>(sb) * a.max_pages + page] : -1;
-  }
   const int s_first = max(L_old - t0, 0);        // first new position of the group
   const int s_end = min(kGroupTokens, L_new - t0);
   const bool present = tok < s_end;
   const int inew = min(max(t0 + tok - L_old, 0), a.n_new - 1);   // clamped row of k_new / v_new
-  const long long blk = (active && phys >= 0 && phys < a.num_pages)
-      ? (static_cast<long long>(phys) * a.hkv + h) * (a.page_tokens / kGroupTokens) + (t0 % a.page_tokens) / kGroupTokens
-      : -1;
+  // A longer append's input row (position tok of the group: the raw tail's
+  // row or row inew of the new keys; row inew of the new values), issued
+  // before the page entry so that waiting for it never waits for the page.
+  uint32_t w_in[NWORDS];
+  if (!one) {
+    const char* row = vrole
+        ? static_cast<const char*>(a.v_new) + (((static_cast<size_t>(b) * a.n_new + inew) * a.hkv + h) * D + cb) * ESZ
+        : (t0 + tok < L_old)
+            ? static_cast<const char*>(a.k_tail) + (((static_cast<size_t>(sb) * a.hkv + h) * kGroupTokens + tok) * D + cb) * ESZ
+            : static_cast<const char*>(a.k_new) + (((static_cast<size_t>(b) * a.n_new + inew) * a.hkv + h) * D + cb) * ESZ;
+    load_words<NWORDS>(row, w_in);
+  }
+  const int page = t0 / a.page_tokens;
+  const int pt_raw = a.page_table[static_cast<size_t>(sb) * a.max_pages + min(page, a.max_pages - 1)];
+  // The group's block (-1: not stored), formed where it is first needed so
+  // that the wait for the page entry comes as late as possible.
+  auto phys_of = [&]() { return (active && page < a.max_pages) ? __builtin_amdgcn_readfirstlane(pt_raw) : -1; };
+  auto block_of = [&](int phys) -> long long {
+    return (active && phys >= 0 && phys < a.num_pages)
+        ? (static_cast<long long>(phys) * a.hkv + h) * (a.page_tokens / kGroupTokens) + (t0 % a.page_tokens) / kGroupTokens
+        : -1;
+  };
 
   // The key block of the group: 2 bits as built in LDS, wider codes packed
   // from one byte per code.
@@ -261,16 +298,12 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
 
   if (!vrole) {
     // ================= keys =================
-    const char* krow = (t0 + tok < L_old)
-        ? static_cast<const char*>(a.k_tail) + (((static_cast<size_t>(sb) * a.hkv + h) * kGroupTokens + tok) * D + cb) * ESZ
-        : static_cast<const char*>(a.k_new) + (((static_cast<size_t>(b) * a.n_new + inew) * a.hkv + h) * D + cb) * ESZ;
     uint32_t kw[NWORDS];
-    load_words<NWORDS>(krow, kw);
-    uint32_t sgw[CH / 4];
+    const bool from_tail = t0 + tok < L_old;
 #pragma unroll
-    for (int k = 0; k < CH / 4; ++k) sgw[k] = reinterpret_cast<const uint32_t*>(a.signs + h * D + cb)[k];
+    for (int i = 0; i < NWORDS; ++i) kw[i] = !one ? w_in[i] : from_tail ? w_tail[i] : w_one[i];
 
-    if (blk >= 0) {
+    {
       // ---- y = H (s * k) / sqrt(d) in fp64 (exact up to the one scaling).
       // Channel c = part * CH + i: the transform over i runs inside the
       // thread, the one over part across the 16 lanes of the position.
@@ -306,6 +339,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
         sm.k.y[tok][cb + i] = x[i];
       }
       __syncthreads();
+      const long long blk = block_of(phys_of());
 
       if (a.key_mode == KVQ_KEYS_PER_TOKEN) {
         // ---- per-token keys (TurboQuant): n = ||k|| (squares over the
@@ -335,9 +369,9 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
           }
           if (BITS == 2) sm.k.kblk[key_code_byte<D>(tok, cb + 4 * q4)] = static_cast<uint8_t>(byte);
         }
-        if (part == 0) a.k_stats[static_cast<size_t>(blk) * 2 * D + tok] = present ? f64_to_f16_rne(n) : uint16_t(0);
+        if (part == 0 && blk >= 0) a.k_stats[static_cast<size_t>(blk) * 2 * D + tok] = present ? f64_to_f16_rne(n) : uint16_t(0);
         __syncthreads();
-        store_key_block(blk);
+        if (blk >= 0) store_key_block(blk);
       } else {
 
       // ---- statistics: per channel min / max over the present positions;
@@ -363,9 +397,11 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
         }
         if (q == 0) {
           const uint16_t lo16 = f64_to_f16_rne(lo), hi16 = f64_to_f16_rne(hi);
-          uint16_t* st = a.k_stats + static_cast<size_t>(blk) * 2 * D;
-          st[c] = lo16;
-          st[D + c] = hi16;
+          if (blk >= 0) {
+            uint16_t* st = a.k_stats + static_cast<size_t>(blk) * 2 * D;
+            st[c] = lo16;
+            st[D + c] = hi16;
+          }
           // LO and the per-channel factor (c3 - c0) / (HI - LO) (HI - LO is
           // exact in fp64); 0 marks HI == LO (every code 0).
           const double LO = static_cast<double>(f16_bits_to_f32(lo16)), HI = static_cast<double>(f16_bits_to_f32(hi16));
@@ -397,7 +433,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
         if (BITS == 2) sm.k.kblk[key_code_byte<D>(tok, cb + 4 * q4)] = static_cast<uint8_t>(byte);
       }
       __syncthreads();
-      store_key_block(blk);
+      if (blk >= 0) store_key_block(blk);
       }   // group min-max keys
     }
 
@@ -419,11 +455,11 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
         }
       }
     }
-  } else if (blk >= 0) {
+  } else {
     // ================= values =================
-    const char* vrow = static_cast<const char*>(a.v_new) + (((static_cast<size_t>(b) * a.n_new + inew) * a.hkv + h) * D + cb) * ESZ;
     uint32_t vw[NWORDS];
-    load_words<NWORDS>(vrow, vw);
+#pragma unroll
+    for (int i = 0; i < NWORDS; ++i) vw[i] = one ? w_one[i] : w_in[i];
     const int ms = lane & 31;                      // this lane's modality slot
     const bool ms_fresh = ms >= s_first && ms < s_end;
     const uint32_t mod_l = a.modality_new[static_cast<size_t>(b) * a.n_new + min(max(t0 + ms - L_old, 0), a.n_new - 1)];
@@ -436,13 +472,16 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
 #pragma unroll
       for (int i = 0; i < IQ; ++i) rr[i] = Rm[static_cast<size_t>(i) * D];
     }
+    const int phys = phys_of();
+    const long long blk = block_of(phys);
     // Round trip 3 (needed only at the end): the group's stored value codes,
     // for positions before s_first.  The 8D-byte block is 2D words: thread
     // tid < 2D owns word tid.
-    uint8_t* vb = a.v_codes + static_cast<size_t>(blk) * 4 * BITS * D;
+    const bool stored = blk >= 0;
+    uint8_t* vb = a.v_codes + static_cast<size_t>(stored ? blk : 0) * 4 * BITS * D;
     const bool vword = BITS == 2 && tid < 2 * D;
-    const uint32_t old_v = (s_first > 0 && vword) ? reinterpret_cast<const uint32_t*>(vb)[tid] : 0u;
-    if (BITS != 2 && s_first > 0)
+    const uint32_t old_v = (stored && s_first > 0 && vword) ? reinterpret_cast<const uint32_t*>(vb)[tid] : 0u;
+    if (BITS != 2 && stored && s_first > 0)
       for (int w = tid; w < BITS * D; w += kAppendThreads) sm.v.oldw[w] = reinterpret_cast<const uint32_t*>(vb)[w];
 
     // Modalities among the new positions (every wave computes the same mask).
@@ -502,7 +541,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
     // ---- stores: value block (earlier positions keep their stored codes;
     // a position with a modality outside the known ones gets code 0), norms,
     // modality
-    if (vword) {
+    if (stored && vword) {
       uint32_t outw = 0;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -524,7 +563,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
       }
       reinterpret_cast<uint32_t*>(vb)[tid] = outw;
     }
-    if (BITS != 2) {
+    if (BITS != 2 && stored) {
       auto vcode = [&](int t, int c) -> uint32_t {
         if (t < s_first) return sm.v.code[t][c];
         if (t < s_end) return sm.v.mod[t] < kModalities ? sm.v.code[t][c] : 0u;
@@ -533,7 +572,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
       for (int w = tid; w < BITS * D; w += kAppendThreads)
         reinterpret_cast<uint32_t*>(vb)[w] = pack_word<D, true>(BITS, w, vcode);
     }
-    if (tid < kGroupTokens && tid >= s_first && tid < s_end) {
+    if (stored && tid < kGroupTokens && tid >= s_first && tid < s_end) {
       const int pos = (t0 + tid) % a.page_tokens;
       a.v_norms[(static_cast<size_t>(phys) * a.hkv + h) * a.page_tokens + pos] = f64_to_f16_rne(sm.v.n[tid]);
       if (h == 0) a.modality[static_cast<size_t>(phys) * a.page_tokens + pos] = sm.v.mod[tid];
