@@ -234,12 +234,15 @@ def test_decode_over_retained_pages(cfg_id, kw, pattern):
     assert worst <= h.ATTN_TOL
 
 
-def test_append_skips_unmapped_pages():
+@pytest.mark.parametrize("chunks", [[45, 300, 7, 256], [1, 1, 1, 61]], ids=["chunked", "one-position"])
+def test_append_skips_unmapped_pages(chunks):
     """Positions appended while their logical page has no physical page are not
     stored: every mapped page holds the same bytes as in a build with all pages
     mapped, the pages nobody maps stay untouched, lengths still advance, and
     the decode equals the fully mapped cache's decode under the same sparse
-    page table."""
+    page table.  Both append paths: longer appends, and one-position appends
+    (the decode step's, which read their inputs before the length is known)
+    at every offset inside a group."""
     import decode_attention_kvq_amd as K
     h = H()
     w = generate(3, batch=3, len_range=(900, 2600))
@@ -249,7 +252,6 @@ def test_append_skips_unmapped_pages():
         npg = -(-int(w.lengths[b]) // w.page_tokens)
         sparse[b, :npg][rng.random(npg) < 0.5] = -1
     num_pages = int(w.page_table.max()) + 1
-    chunks = [45, 300, 7, 256]
     _say(f"append onto unmapped pages: lengths={w.lengths.tolist()} "
          f"unmapped={int((sparse < 0).sum() - (w.page_table < 0).sum())} chunks={chunks}")
     cfg, params, full = h.build(w, chunks=chunks)
