@@ -14,7 +14,9 @@ from .streams import (  # noqa: F401
     calibration_queries,
     f64_to_bf16_bits,
     generate,
+    hadamard_value_bases,
     lloyd_max_codebook,
     lloyd_max_codebook_2bit,
+    sylvester_hadamard,
     workload_digest,
 )

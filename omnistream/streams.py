@@ -308,6 +308,32 @@ def generate(cfg_id: int, length: Optional[int] = None, batch: Optional[int] = N
                           "value_spectrum": lam})
 
 
+def sylvester_hadamard(d: int) -> np.ndarray:
+    """The d x d Sylvester Hadamard matrix (entries +-1, natural order), by the
+    doubling construction H_1 = [1], H_2n = [[H, H], [H, -H]] (np.kron)."""
+    if d < 1 or d & (d - 1):
+        raise ValueError("d must be a power of two")
+    H = np.ones((1, 1), np.int64)
+    while H.shape[0] < d:
+        H = np.kron(np.array([[1, 1], [1, -1]], np.int64), H)
+    return H
+
+
+def hadamard_value_bases(w: Workload) -> np.ndarray:
+    """Value bases of the shared-rotation (TurboQuant) baseline as an input
+    array [Hkv, 3, d, d] float32: every modality of KV head h gets
+    R = diag(s_h) H_d / sqrt(d), so that the forward map R^T v is the
+    randomized Hadamard H_d (s_h * v) / sqrt(d) of the keys.  Entries are
+    +-1/sqrt(d), exact in fp32 for d = 64 and rounded once for d = 128."""
+    d = w.cfg.head_dim
+    H = sylvester_hadamard(d).astype(np.float64)
+    out = np.empty((w.cfg.n_kv_heads, 3, d, d), np.float32)
+    for h in range(w.cfg.n_kv_heads):
+        R = (w.signs[h].astype(np.float64)[:, None] * H) / np.sqrt(d)
+        out[h] = R.astype(np.float32)[None]
+    return out
+
+
 def calibration_queries(w: Workload, n_queries: int) -> np.ndarray:
     """n_queries seeded N(0, 1) query vectors per query head, [n_queries, Hq, d]
     in the workload's dtype: the queries a value-basis calibration attends

@@ -9,7 +9,18 @@ import numpy as np
 import torch
 
 from omnistream import Workload
-from oracle import kvq_oracle as O
+
+
+class _LazyOracle:
+    """The fp64 oracle, imported on first use: the cache-building helpers
+    here (used by the benchmark's GPU legs too) never load it."""
+
+    def __getattr__(self, name):
+        from oracle import kvq_oracle
+        return getattr(kvq_oracle, name)
+
+
+O = _LazyOracle()
 
 ATTN_TOL = 2e-3          # max normwise relative error per (session, query head)
 BOUNDARY_EPS = 1e-6      # |z - threshold| below which a code may differ
@@ -70,9 +81,10 @@ def query_tensor(w: Workload, device="cuda") -> torch.Tensor:
 
 def hadamard_rot(w: Workload) -> np.ndarray:
     """The TurboQuant value basis: every modality of KV head h uses the
-    randomized Hadamard of h, [Hkv, 3, d, d] fp32."""
-    return np.stack([np.stack([O.hadamard_value_basis(w.signs[h])] * 3)
-                     for h in range(w.cfg.n_kv_heads)]).astype(np.float32)
+    randomized Hadamard of h, [Hkv, 3, d, d] fp32 (an input, built by the
+    stream generator)."""
+    from omnistream import hadamard_value_bases
+    return hadamard_value_bases(w)
 
 
 def oracle_session(w: Workload, b: int, length: Optional[int] = None, key_mode: int = 0,
@@ -144,34 +156,53 @@ def compare_session_codes(w: Workload, b: int, gpu: dict, ora: list, h: int, len
     return stats
 
 
+def _map_sessions(fn, sessions, threads: int):
+    """fn over the sessions, on a pool of host threads when threads > 1 (the
+    oracle's heavy steps are NumPy calls that release the interpreter lock;
+    no thread touches the GPU)."""
+    sessions = list(sessions)
+    if threads <= 1 or len(sessions) <= 1:
+        return [fn(b) for b in sessions]
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        return list(ex.map(fn, sessions))
+
+
 def check_codes(w: Workload, cfg, cache, sessions: Sequence[int], lengths: Optional[Sequence[int]] = None,
-                rot: Optional[np.ndarray] = None):
+                rot: Optional[np.ndarray] = None, threads: int = 1):
     from decode_attention_kvq_amd.layout import session_view
     host = cache.host_arrays()
-    total = mism = 0
     key_mode = getattr(cfg, "key_mode", 0)
-    for b in sessions:
+
+    def one(b):
         n = int(w.lengths[b] if lengths is None else lengths[b])
         assert int(host["seq_len"][b]) == n
         ora = oracle_session(w, b, n, key_mode, rot)
+        tot = mis = 0
         for h in range(w.cfg.n_kv_heads):
             gpu = session_view(host, cfg, b, n, h)
             s = compare_session_codes(w, b, gpu, ora, h, n, key_mode, rot)
-            total += s["elements"]
-            mism += s["boundary_mismatches"]
+            tot += s["elements"]
+            mis += s["boundary_mismatches"]
+        return tot, mis
+
+    res = _map_sessions(one, sessions, threads)
+    total = sum(r[0] for r in res)
+    mism = sum(r[1] for r in res)
     assert mism <= BOUNDARY_FRAC * max(total, 1), f"{mism} boundary mismatches of {total}"
     return total, mism
 
 
 def oracle_decode_over_gpu_codes(w: Workload, cfg, cache, q: np.ndarray, sessions: Sequence[int],
-                                 scale: float, rot: Optional[np.ndarray] = None) -> dict:
+                                 scale: float, rot: Optional[np.ndarray] = None, threads: int = 1) -> dict:
     """The oracle attending over the GPU's own packed cache (codes read back),
     over the positions of the pages the page table maps (a negative entry
     marks a page that is not retained)."""
     from decode_attention_kvq_amd.layout import session_view
     host = cache.host_arrays()
     out = {}
-    for b in sessions:
+
+    def one(b):
         n = int(host["seq_len"][b])
         caches = [session_view(host, cfg, b, n, h) for h in range(w.cfg.n_kv_heads)]
         keep = caches[0]["retained"] if caches else None
@@ -179,13 +210,16 @@ def oracle_decode_over_gpu_codes(w: Workload, cfg, cache, q: np.ndarray, session
         r = w.rot if rot is None else rot
         ret = None if keep is None or keep.all() else keep
         if getattr(cfg, "key_mode", 0) == 0:
-            out[b] = O.decode_attention(q_rot, caches, r, w.codebook, scale, retained=ret)
-        else:
-            g = w.cfg.n_q_heads // w.cfg.n_kv_heads
-            out[b] = np.stack([O.decode_attention_head_per_token_keys(
-                q_rot[i], caches[i // g]["k_codes"], caches[i // g]["k_norms"], caches[i // g]["v_codes"],
-                caches[i // g]["norms"], caches[i // g]["modality"], r[i // g], w.codebook, scale, ret)
-                for i in range(w.cfg.n_q_heads)])
+            return O.decode_attention(q_rot, caches, r, w.codebook, scale, retained=ret)
+        g = w.cfg.n_q_heads // w.cfg.n_kv_heads
+        return np.stack([O.decode_attention_head_per_token_keys(
+            q_rot[i], caches[i // g]["k_codes"], caches[i // g]["k_norms"], caches[i // g]["v_codes"],
+            caches[i // g]["norms"], caches[i // g]["modality"], r[i // g], w.codebook, scale, ret)
+            for i in range(w.cfg.n_q_heads)])
+
+    sessions = list(sessions)
+    for b, o in zip(sessions, _map_sessions(one, sessions, threads)):
+        out[b] = o
     return out
 
 

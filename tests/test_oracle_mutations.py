@@ -78,10 +78,63 @@ def _dequant_keys_off_by_one_level(codes, lo16, hi16, codebook, group=32):
     return _orig_dk(np.minimum(codes + 1, 3).astype(np.uint8), lo16, hi16, codebook, group)
 
 
+def _ties_go_down(z, codebook):
+    """Wrong threshold side: a value exactly on a threshold takes the lower level."""
+    b = O.decision_thresholds(codebook)
+    return (np.asarray(z)[..., None] > b).sum(axis=-1).astype(np.uint8)
+
+
+def _keys_per_group_scalar_stats(k, signs, codebook, group=32):
+    """One min / max per group over every channel instead of per channel."""
+    y = O.randomized_hadamard(k, signs)
+    L, d = y.shape
+    ng = -(-L // group)
+    c = np.asarray(codebook, np.float32).astype(np.float64)
+    codes = np.zeros((L, d), np.uint8)
+    lo16 = np.zeros((ng, d), np.float16)
+    hi16 = np.zeros((ng, d), np.float16)
+    for g in range(ng):
+        yg = y[g * group:(g + 1) * group]
+        lo16[g] = np.float16(yg.min())
+        hi16[g] = np.float16(yg.max())
+        LO, HI = lo16[g].astype(np.float64), hi16[g].astype(np.float64)
+        z = c[0] + (yg - LO) * (c[-1] - c[0]) / np.where(HI > LO, HI - LO, 1.0)
+        codes[g * group:(g + 1) * group] = np.where(HI > LO, O.nearest_level(z, codebook), 0)
+    return codes, lo16, hi16
+
+
+def _key_z_from_unrounded_range(k, signs, lo16, hi16, codebook, group=32):
+    """z taken against the exact group min / max instead of the stored fp16 LO / HI."""
+    y = O.randomized_hadamard(k, signs)
+    ng = -(-y.shape[0] // group)
+    lo = np.stack([y[g * group:(g + 1) * group].min(0) for g in range(ng)])
+    hi = np.stack([y[g * group:(g + 1) * group].max(0) for g in range(ng)])
+    return _orig_knv(k, signs, lo, hi, codebook, group)
+
+
+def _key_z_on_unit_range(k, signs, lo16, hi16, codebook, group=32):
+    """z mapped onto [-1, 1] instead of [c0, c3]."""
+    z = _orig_knv(k, signs, lo16, hi16, codebook, group)
+    c = np.asarray(codebook, np.float32).astype(np.float64)
+    return -1.0 + (z - c[0]) * 2.0 / (c[-1] - c[0])
+
+
+def _bf16_as_upper_fp16(bits):
+    """Reads the raw 16 bits as IEEE half precision instead of bfloat16."""
+    return np.asarray(bits, np.uint16).view(np.float16).astype(np.float64)
+
+
+def _bf16_truncated_fraction(bits):
+    """Drops the lowest fraction bit of every bfloat16 value."""
+    u = (np.asarray(bits, dtype=np.uint16) & np.uint16(0xFFFE)).astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
+
+
 _orig_qv = O.quantize_values
 _orig_qk = O.quantize_keys
 _orig_dh = O.decode_attention_head
 _orig_dk = O.dequantize_keys
+_orig_knv = O.key_normalized_values
 
 MUTANTS = [
     ("randomized_hadamard", _signs_after_h, [(P.test_randomized_hadamard_is_H_times_D, 64)]),
@@ -97,6 +150,13 @@ MUTANTS = [
     ("rotate_query", _rotate_query_wrong_head,
      [(P.test_decode_equals_dense_attention_over_dequantized_cache, 37)]),
     ("dequantize_keys", _dequant_keys_off_by_one_level, [(P.test_key_group_range_is_restored, 0, 300)]),
+    ("nearest_level", _ties_go_down, [(P.test_nearest_level_ties_go_up,)]),
+    ("quantize_keys", _keys_per_group_scalar_stats, [(P.test_key_group_range_is_restored, 0, 300)]),
+    ("key_normalized_values", _key_z_from_unrounded_range, [(P.test_key_normalized_values_decide_the_codes, 0, 289)]),
+    ("key_normalized_values", _key_z_on_unit_range, [(P.test_key_normalized_values_decide_the_codes, 0, 289),
+                                                     (P.test_key_normalized_values_on_a_hand_worked_group,)]),
+    ("bf16_to_f64", _bf16_as_upper_fp16, [(P.test_bf16_to_f64_on_every_bit_pattern,)]),
+    ("bf16_to_f64", _bf16_truncated_fraction, [(P.test_bf16_to_f64_on_every_bit_pattern,)]),
 ]
 
 

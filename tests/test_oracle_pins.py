@@ -341,3 +341,103 @@ def test_decode_over_a_retained_position_set(pattern):
     np.testing.assert_array_equal(O.decode_attention(qr, caches, R, CB, scale, retained=np.ones(L, bool)),
                                   O.decode_attention(qr, caches, R, CB, scale))
     np.testing.assert_array_equal(O.decode_attention(qr, caches, R, CB, scale, retained=np.zeros(L, bool)), 0)
+
+
+# ------------------------------------------- input conversion, value bases
+
+def test_bf16_to_f64_on_every_bit_pattern():
+    """All 65,536 bfloat16 bit patterns: the oracle's fp64 image equals torch's
+    bfloat16 -> float32 conversion (NaNs compared by class, zeros by sign),
+    and a few patterns worked by hand from the format (sign, 8-bit exponent
+    with bias 127, 7-bit fraction) come out exactly."""
+    import torch
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = O.bf16_to_f64(bits)
+    with np.errstate(invalid="ignore"):
+        ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float32).numpy().astype(np.float64)
+    nan = np.isnan(ref)
+    np.testing.assert_array_equal(np.isnan(got), nan)
+    assert nan.sum() == 2 * 127                       # exponent all ones, fraction nonzero, both signs
+    np.testing.assert_array_equal(got[~nan], ref[~nan])
+    np.testing.assert_array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+    hand = {0x3F80: 1.0, 0xC000: -2.0, 0x3FC0: 1.5, 0x0001: 2.0 ** -133, 0x0080: 2.0 ** -126,
+            0x7F7F: (2 - 2.0 ** -7) * 2.0 ** 127, 0x7F80: np.inf, 0xFF80: -np.inf, 0x8000: -0.0,
+            0x3E80: 0.25, 0x4049: 3.140625}
+    for b, v in hand.items():
+        g = O.bf16_to_f64(np.array([b], np.uint16))[0]
+        assert g == v and np.signbit(g) == np.signbit(v), (hex(b), g, v)
+
+
+@pytest.mark.parametrize("cfg_id", [0, 1, 2, 3, 4])
+def test_generated_value_bases_are_orthogonal(cfg_id):
+    """Every generated fp32 value basis R_{h,m} is orthogonal to 1e-6: the
+    oracle inverts the forward map R_m^T with R_m (Sec. 2, values bullet: the
+    reconstructed values use the modality's rotation), which needs
+    R_m^T R_m = R_m R_m^T = I.  The bases depend only on the configuration's
+    seed, so a short stream gives the full configuration's bases."""
+    w = generate(cfg_id, length=64, batch=1, len_range=(64, 64) if cfg_id == 3 else None)
+    hkv, d = w.cfg.n_kv_heads, w.cfg.head_dim
+    assert w.rot.shape == (hkv, 3, d, d) and w.rot.dtype == np.float32
+    I = np.eye(d)
+    for h in range(hkv):
+        for m in range(3):
+            R = w.rot[h, m].astype(np.float64)
+            assert np.abs(R.T @ R - I).max() < 1e-6, (h, m)
+            assert np.abs(R @ R.T - I).max() < 1e-6, (h, m)
+    # the three modalities of a head have different bases (per-modality rotation)
+    for h in range(hkv):
+        assert np.abs(w.rot[h, 0] - w.rot[h, 1]).max() > 0.1 and np.abs(w.rot[h, 1] - w.rot[h, 2]).max() > 0.1
+
+
+# ------------------------------------- the z each key code is decided on
+
+@pytest.mark.parametrize("cfg_id,L", [(0, 289), (1, 333), (2, 97)])
+def test_key_normalized_values_decide_the_codes(cfg_id, L):
+    """key_normalized_values reports the z each key code is decided on:
+    nearest_level(z) reproduces quantize_keys' codes wherever z is defined,
+    z is NaN exactly where the stored range is empty (HI == LO: here the
+    single-position last group), and z stays inside [c0, c3] up to the fp16
+    rounding of LO / HI (Sec. 2 Method, key bullet)."""
+    w, k = _keys(cfg_id, L)
+    c = CB.astype(np.float64)
+    gi = np.arange(L) // 32
+    for h in range(w.cfg.n_kv_heads):
+        codes, lo, hi = O.quantize_keys(k[:, h], w.signs[h], CB)
+        z = O.key_normalized_values(k[:, h], w.signs[h], lo, hi, CB)
+        empty = (lo.astype(np.float64) == hi.astype(np.float64))[gi]
+        if L % 32 == 1:
+            assert empty[-1].all()
+        np.testing.assert_array_equal(np.isnan(z), empty)
+        np.testing.assert_array_equal(O.nearest_level(z[~empty], CB), codes[~empty])
+        # y lies in [true min, true max]; LO / HI are those within half an fp16 ulp
+        LO, HI = lo.astype(np.float64)[gi], hi.astype(np.float64)[gi]
+        ulp = np.spacing(np.maximum(np.abs(LO), np.abs(HI)).astype(np.float16)).astype(np.float64)
+        slack = (c[-1] - c[0]) * ulp / np.where(empty, 1.0, HI - LO)
+        ok = ~empty
+        assert np.all(z[ok] >= c[0] - slack[ok] - 1e-12) and np.all(z[ok] <= c[-1] + slack[ok] + 1e-12)
+
+
+def test_key_normalized_values_on_a_hand_worked_group():
+    """Rotated keys placed at known fractions f of an fp16-exact group range:
+    the position at the group minimum has z = c0, the maximum z = c3, and
+    fraction f gives z = c0 + f (c3 - c0), so the quarter points of the range
+    fall on the levels' affine images (the range maps onto [c0, c3])."""
+    d = 64
+    rng = np.random.default_rng(21)
+    s = np.where(rng.random(d) < 0.5, -1, 1).astype(np.int8)
+    LO = np.round(rng.uniform(-4, 0, d) * 8) / 8                 # fp16-exact
+    HI = LO + np.round(rng.uniform(0.5, 6, d) * 8) / 8
+    fr = np.array([0.0, 0.25, 0.5, 0.75, 1.0, 0.125, 0.375, 0.625])
+    f = fr[np.arange(32)[:, None] % 8 + 0 * np.arange(d)[None, :]]
+    f[0], f[1] = 0.0, 1.0                                         # both extremes present in every channel
+    y = LO + f * (HI - LO)                                        # exact in fp64
+    M = scipy.linalg.hadamard(d) @ np.diag(s.astype(np.float64)) / math.sqrt(d)
+    k = y @ M                                                     # M^T y: the key whose rotation is y
+    codes, lo, hi = O.quantize_keys(k, s, CB)
+    np.testing.assert_array_equal(lo[0].astype(np.float64), LO)
+    np.testing.assert_array_equal(hi[0].astype(np.float64), HI)
+    z = O.key_normalized_values(k, s, lo, hi, CB)
+    c = CB.astype(np.float64)
+    np.testing.assert_allclose(z, c[0] + f * (c[-1] - c[0]), rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(codes[f == 0.0], 0)
+    np.testing.assert_array_equal(codes[f == 1.0], 3)

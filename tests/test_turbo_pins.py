@@ -132,3 +132,22 @@ def test_stationary_keys_give_the_same_error_in_every_order():
     mod = rng.integers(0, 3, L).astype(np.uint8)
     errs = [O.key_grouping_error(k, mod, s, CB, o, seed=2) for o in O.GROUP_ORDERS]
     assert max(errs) - min(errs) < 0.02 * min(errs)
+
+
+@pytest.mark.parametrize("cfg_id", [0, 2])
+def test_generated_hadamard_bases_equal_the_oracle_basis(cfg_id):
+    """The shared-rotation baseline's value bases are an input built by the
+    stream generator (Sylvester doubling); they equal the oracle's pinned
+    randomized-Hadamard basis rounded once to fp32, for every KV head and
+    modality, and the generator's matrix is scipy's Hadamard."""
+    import scipy.linalg
+    from omnistream import generate, hadamard_value_bases, sylvester_hadamard
+    w = generate(cfg_id, length=64)
+    d = w.cfg.head_dim
+    np.testing.assert_array_equal(sylvester_hadamard(d), scipy.linalg.hadamard(d))
+    R = hadamard_value_bases(w)
+    assert R.shape == (w.cfg.n_kv_heads, 3, d, d) and R.dtype == np.float32
+    for h in range(w.cfg.n_kv_heads):
+        ref = O.hadamard_value_basis(w.signs[h]).astype(np.float32)
+        for m in range(3):
+            np.testing.assert_array_equal(R[h, m], ref)
