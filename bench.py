@@ -66,6 +66,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibration-only", action="store_true",
                     help="only time the value-basis calibration on the 80K stream and print its JSON line")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only replay the 80K decode graph (partition + merge over the layer replicas) "
+                         "--steps times and print its timing (for profiler runs)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB ten times (reference "
                          "for the HBM byte counters) and exit")
@@ -166,6 +169,22 @@ def main():
     n_rep = max(1, args.steps // args.replicas)
     n_warm = max(1, args.warmup // args.replicas)
     stream = torch.cuda.current_stream()
+    if args.decode_only:
+        for _ in range(n_warm):
+            g_dec.replay()
+        torch.cuda.synchronize()
+        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        d0.record(stream)
+        for _ in range(n_rep):
+            g_dec.replay()
+        d1.record(stream)
+        torch.cuda.synchronize()
+        us = d0.elapsed_time(d1) * 1e3 / (n_rep * args.replicas)
+        nb = algorithmic_decode_bytes(L0, d, hq, hkv)
+        print(json.dumps({"decode_only": {"context": L0, "launches": n_rep * args.replicas,
+                                          "warmup_launches": n_warm * args.replicas, "avg_launch_us": us,
+                                          "bytes_per_launch": nb, "GBps": nb / us / 1e3}}), flush=True)
+        return
     for _ in range(n_warm):
         g_step.replay()
     torch.cuda.synchronize()
@@ -250,9 +269,9 @@ def main():
     calib = time_calibration(L0)
     del g_step, g_dec, g_warm
     import decode_attention_kvq_amd as K_
-    from tests import kvq_harness as H_
+    from omnistream import hadamard_value_bases
     turbo = time_variant_decode(w, table, L0, args.replicas, n_dec, scale, key_mode=K_.KVQ_KEYS_PER_TOKEN,
-                                rot=H_.hadamard_rot(w))
+                                rot=hadamard_value_bases(w))
     turbo["workload"] = "same 80K decode, per-token keys + shared Hadamard values"
     wide = {f"{b}bit": time_variant_decode(w, table, L0, args.replicas, n_dec, scale, bits=b) for b in (3, 4)}
 

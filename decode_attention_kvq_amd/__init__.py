@@ -181,20 +181,24 @@ def kvq_decode_workspace_bytes(cfg: Config, max_len: int) -> int:
 
 def kvq_decode_attention(cfg: Config, cache: Cache, params: Params, q_rot: torch.Tensor,
                          scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-                         workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """q_rot: [batch, Hq, d] fp32 -> out [batch, Hq, d] fp32."""
+                         workspace: Optional[torch.Tensor] = None, stream=None,
+                         out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """q_rot: [batch, Hq, d] fp32 -> out [batch, Hq, d] in out_dtype (fp32 or
+    bf16; an `out` tensor given sets the dtype)."""
     if tuple(q_rot.shape) != (cfg.batch, cfg.n_q_heads, cfg.head_dim):
         raise ValueError("q_rot must be [batch, Hq, d]")
     if scale is None:
         scale = 1.0 / math.sqrt(cfg.head_dim)
     if out is None:
-        out = torch.empty(q_rot.shape, dtype=torch.float32, device=q_rot.device)
+        out = torch.empty(q_rot.shape, dtype=out_dtype, device=q_rot.device)
+    if out.dtype not in _DTYPES or tuple(out.shape) != tuple(q_rot.shape):
+        raise ValueError("out must be [batch, Hq, d] float32 or bfloat16")
     need = kvq_decode_workspace_bytes(cfg, max(cache.lengths()))
     if workspace is None:
         workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=q_rot.device)
     st = _lib.load().kvq_decode_attention(
         ctypes.byref(cfg.struct), ctypes.byref(cache.struct), ctypes.byref(params.struct),
-        _dev(q_rot, "q_rot", torch.float32), float(scale), _dev(out, "out", torch.float32),
+        _dev(q_rot, "q_rot", torch.float32), float(scale), _dev(out, "out"), _DTYPES[out.dtype],
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
     _lib.check("kvq_decode_attention", st)
     return out

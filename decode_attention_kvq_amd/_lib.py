@@ -81,7 +81,7 @@ def load() -> ctypes.CDLL:
     lib.kvq_decode_workspace_bytes.argtypes = [P(KvqConfig), ctypes.c_int32]
     lib.kvq_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.kvq_decode_attention.argtypes = [P(KvqConfig), P(KvqCache), P(KvqParams), ctypes.c_void_p,
-                                         ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_float, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                          ctypes.c_size_t, ctypes.c_void_p]
     lib.kvq_decode_attention.restype = ctypes.c_int
     V = ctypes.c_void_p

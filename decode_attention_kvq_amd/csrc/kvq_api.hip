@@ -259,13 +259,14 @@ size_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t max_len) {
 
 kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache,
                                 const kvq_params* params, const float* q_rot, float scale,
-                                float* out, void* workspace, size_t workspace_bytes,
+                                void* out, int32_t out_dtype, void* workspace, size_t workspace_bytes,
                                 hipStream_t stream) {
   kvq_status st = check_config(cfg);
   if (st != KVQ_OK) return st;
   if ((st = check_params(cfg, params)) != KVQ_OK) return st;
   if ((st = check_cache(cache)) != KVQ_OK) return st;
   if (!q_rot || !out || !isfinite(scale)) return KVQ_ERR_INVALID;
+  if (out_dtype != KVQ_F32 && out_dtype != KVQ_BF16) return KVQ_ERR_UNSUPPORTED;
   int32_t max_len = 0;
   const int64_t cap = (int64_t)cfg->max_pages * cfg->page_tokens;
   for (int b = 0; b < cfg->batch; ++b) {
@@ -288,6 +289,7 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache,
   a.q_rot = q_rot;
   a.rot = params->rot;
   a.out = out;
+  a.out_bf16 = out_dtype == KVQ_BF16;
   a.partials = static_cast<float*>(workspace);
   a.batch = cfg->batch;
   a.hq = cfg->n_q_heads;

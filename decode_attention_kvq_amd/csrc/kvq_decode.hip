@@ -46,6 +46,14 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTabCopies = 32;     // byte-table copies: lane l reads copy l % 32
 constexpr float kLazyMax = 8.f;    // headroom (base-2 units) of the softmax reference max
+// Value weights p * N are fp16 matrix-core operands.  They are formed as
+// 2^(s - m_run + wshift) * N with wshift = kWeightExp + 14 - nE, where every
+// norm N seen so far is below 2^(nE - 14): the weights stay below
+// 2^kWeightExp (fp16 overflows at 2^16) and the largest ones far above the
+// fp16 subnormal range, whatever the scale of the values.  The factor is a
+// shift of the softmax reference (the partial stores m_run - wshift), so it
+// cancels in the output.
+constexpr int kWeightExp = 15;
 constexpr int kPageRun = kPartitionPages;   // page-table entries of one partition kept in LDS
 constexpr int kMaxSplits = 4096;
 
@@ -116,6 +124,28 @@ __device__ __forceinline__ int in_page(const DecodeArgs& a, int t) {
   return static_cast<int>(static_cast<unsigned>(t) % static_cast<unsigned>(a.page_tokens));
 }
 
+// Physical page of logical page pg (>= page0) of session b: from the
+// partition's page run in LDS (its first `run` entries were loaded) when it
+// lies inside it, else from the page
+// table in global memory through scalar loads.  The second case only arises
+// for the last partition of a session that grew on the device after the plan
+// was made (a captured decode replayed while appends advance the length); it
+// is slower, never wrong.  -1 past the end of the table.
+__device__ __forceinline__ int phys_page(const DecodeArgs& a, const int* s_pt, int run, int b, int page0, int pg) {
+  const int i = pg - page0;
+  if (i < run) return __builtin_amdgcn_readfirstlane(s_pt[i]);
+  if (pg >= a.max_pages) return -1;
+  const __attribute__((address_space(4))) int32_t* ptab =
+      (const __attribute__((address_space(4))) int32_t*)(a.page_table);
+  return ptab[static_cast<size_t>(b) * a.max_pages + pg];
+}
+
+// Positions of session b the decode may attend: its device length, bounded
+// by the capacity of its page-table row.
+__device__ __forceinline__ int session_length(const DecodeArgs& a, int b) {
+  return min(a.seq_len[b], a.max_pages * a.page_tokens);
+}
+
 // Issues the loads of the group at position t0 (on physical page phys0)
 // without branching, so the compiler can count outstanding loads exactly: a
 // group outside [0, te) or on an unmapped page reads page 0 instead and is
@@ -158,7 +188,9 @@ template <int D, int SLOTS, bool ASYM>
 struct WaveState {
   static constexpr int NSETS = Slots<SLOTS>::NSETS;
   float m_run;                      // running max (base 2) of this lane's score head
-  float l_run;                      // this lane's share of the softmax denominator
+  float l_run;                      // this lane's share of the softmax denominator (scaled like the weights)
+  int nE;                           // norm reference: every value norm seen is below 2^(nE - 14) (wave-uniform)
+  float wshift;                     // kWeightExp + 14 - nE: the weights carry the factor 2^wshift
   floatx4 acc[NSETS][D / 16];       // value accumulators (columns = slot/head pairs)
   floatx4 accs[ASYM ? NSETS : 1];   // sum of weights per column (non-symmetric codebook)
   int mask;                         // modalities that received weight
@@ -173,6 +205,27 @@ __device__ __forceinline__ uint2 tab_entry(uint32_t e, uint32_t t0, uint32_t t1)
   const uint32_t s0 = (e & 3u) * 0x0202u + ((e >> 2) & 3u) * 0x02020000u + 0x01000100u;
   const uint32_t s1 = ((e >> 4) & 3u) * 0x0202u + (e >> 6) * 0x02020000u + 0x01000100u;
   return uint2{__builtin_amdgcn_perm(t1, t0, s0), __builtin_amdgcn_perm(t1, t0, s1)};
+}
+
+// max(E, 1) over the fp16 exponent fields E of a group's 32 value norms
+// (norms are >= 0, so their bit patterns order like their values); lanes of
+// a row hold the same 8 norms, the four rows hold the group's 32.  keep = the
+// number of leading positions of the group that hold data (later slots may
+// hold anything and are left out).  Wave-uniform result.
+__device__ __forceinline__ int group_norm_exponent(uint2 n0, uint2 n1, int kg, int keep) {
+  const uint32_t w[4] = {n0.x, n0.y, n1.x, n1.y};
+  uint32_t m = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int p0 = (r < 2 ? 4 * kg : 16 + 4 * kg) + 2 * (r & 1);   // positions of the two halves
+    const uint32_t lo = p0 < keep ? (w[r] & 0x7FFFu) : 0u;
+    const uint32_t hi = p0 + 1 < keep ? ((w[r] >> 16) & 0x7FFFu) : 0u;
+    m = max(m, max(lo, hi));
+  }
+  const int e = static_cast<int>(m >> 10);
+  const int e01 = max(__builtin_amdgcn_readlane(e, 0), __builtin_amdgcn_readlane(e, 16));
+  const int e23 = max(__builtin_amdgcn_readlane(e, 32), __builtin_amdgcn_readlane(e, 48));
+  return max(max(e01, e23), 1);
 }
 
 // Modality bits of accumulator set k (modalities k SLOTS .. k SLOTS + SLOTS - 1).
@@ -333,10 +386,13 @@ __device__ __forceinline__ void process_group(const GroupLoad<D>& cur, int t0, i
   mx = rows_max(mx) + bias;
   // The reference max m_run only moves when a score passes it, and then to
   // kLazyMax above the new max: weights 2^(s - m_run) stay <= 1, and the
-  // rescale of the accumulators (exact either way) is rarely needed.
-  if (__any(mx > ws.m_run)) {
+  // rescale of the accumulators (exact either way) is rarely needed.  The
+  // norm reference moves when a norm reaches it (see kWeightExp).
+  const int gE = group_norm_exponent(cur.nrm0, cur.nrm1, kg, FULL ? kGroupTokens : te - t0);
+  if (__any(mx > ws.m_run) || gE > ws.nE) {
     const float m_new = fmaxf(ws.m_run, mx + kLazyMax);
-    const float alpha = exp2f(ws.m_run - m_new);   // 0 on the first group
+    const int nE_new = max(ws.nE, gE);
+    const float alpha = exp2f((ws.m_run - m_new) - static_cast<float>(nE_new - ws.nE));   // 0 on the first group
     ws.l_run *= alpha;
     const float alpha_v = __uint_as_float(to_value_column<SLOTS>(__float_as_uint(alpha)));
 #pragma unroll
@@ -346,14 +402,16 @@ __device__ __forceinline__ void process_group(const GroupLoad<D>& cur, int t0, i
       for (int ct = 0; ct < CT; ++ct) ws.acc[k][ct] *= alpha_v;
     }
     ws.m_run = m_new;
+    ws.nE = nE_new;
+    ws.wshift = static_cast<float>(kWeightExp + 14 - nE_new);
   }
-  const float off = ws.m_run - bias;
+  const float off = ws.m_run - bias - ws.wshift;
   const uint32_t n4[4] = {cur.nrm0.x, cur.nrm0.y, cur.nrm1.x, cur.nrm1.y};
   uint32_t wp[4];   // fp16 weights p * N of the lane's 8 positions, two per register
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int i0 = 2 * r, i1 = 2 * r + 1;
-    // arguments are <= 0: the raw base-2 exponential flushes only results below 2^-126
+    // arguments are <= wshift <= 28: the raw base-2 exponential flushes only results below 2^-126
     float p0 = __builtin_amdgcn_exp2f(sc[i0 >> 2][i0 & 3] - off);
     float p1 = __builtin_amdgcn_exp2f(sc[i1 >> 2][i1 & 3] - off);
     if constexpr (!FULL) {
@@ -449,7 +507,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_partition_kernel(DecodeArgs
   const int kg = lane >> 4, col = lane & 15;
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int G = a.group;
-  const int L = a.seq_len[b];
+  const int L = session_length(a, b);
   const int tb = split * a.split_tokens;
   const int te = (split == a.splits - 1) ? L : min(tb + a.split_tokens, L);
   const int te_full = te & ~(kGroupTokens - 1);   // tb is a multiple of 32
@@ -532,6 +590,8 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_partition_kernel(DecodeArgs
   WaveState<D, SLOTS, ASYM> ws;
   ws.m_run = -__builtin_inff();
   ws.l_run = 0.f;
+  ws.nE = 1;
+  ws.wshift = static_cast<float>(kWeightExp + 13);
   ws.mask = 0;
 #pragma unroll
   for (int k = 0; k < NSETS; ++k) {
@@ -553,7 +613,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_partition_kernel(DecodeArgs
 #pragma unroll
     for (int k = 0; k < kPrefetch; ++k) {
       const int nxt = base + (k + kPrefetch) * stride;
-      const int pn = __builtin_amdgcn_readfirstlane(s_pt[min(page_of(a, nxt) - page0, kPageRun - 1)]);
+      const int pn = nxt < te_full ? phys_page(a, s_pt, kPageRun, b, page0, page_of(a, nxt)) : -1;
       if (ok[k])
         process_group<D, SLOTS, ASYM, BHL, true>(buf[k], base + k * stride, te, kg, col, tab, st_lds, lane_off, qo,
                                                  ws, lane);
@@ -561,7 +621,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_partition_kernel(DecodeArgs
     }
   }
   if (te_full >= tb && te_full < te && ((te_full - tb) / kGroupTokens) % NW == wave) {
-    load_group<D>(a, h, te_full, te, lane, kg, s_pt[min(page_of(a, te_full) - page0, kPageRun - 1)], buf[0], ok[0]);
+    load_group<D>(a, h, te_full, te, lane, kg, phys_page(a, s_pt, kPageRun, b, page0, page_of(a, te_full)), buf[0], ok[0]);
     if (ok[0])
       process_group<D, SLOTS, ASYM, BHL, false>(buf[0], te_full, te, kg, col, tab, st_lds, lane_off, qo, ws, lane);
   }
@@ -570,7 +630,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_partition_kernel(DecodeArgs
   const float l_col = rows_sum(ws.l_run);
   const int slot = col / GP, hp = col % GP;
   if (kg == 0) {
-    s_m[wave][col] = ws.m_run;
+    s_m[wave][col] = ws.m_run - ws.wshift;   // the reference of the scaled sums
     s_l[wave][col] = l_col;
     if (slot < SLOTS) {
 #pragma unroll
@@ -643,6 +703,13 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_partition_kernel(DecodeArgs
     }
     part[f] = v;
   }
+}
+
+// fp32 -> bf16 bits, round to nearest, ties to even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  return static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
 // Reductions over lanes without LDS round trips: DPP inside rows of 16
@@ -984,7 +1051,7 @@ __device__ __forceinline__ void sw_back1(const ConsumerLoad<D, BITS>& ca, const 
   float pe[8];
   uint32_t wa[4];
   auto weights = [&](float m_ref) {
-    const float oa = m_ref - bias_a;
+    const float oa = m_ref - bias_a - ws.wshift;
 #pragma unroll
     for (int i = 0; i < 8; ++i) pe[i] = __builtin_amdgcn_exp2f(s[i] - oa);
 #pragma unroll
@@ -993,9 +1060,11 @@ __device__ __forceinline__ void sw_back1(const ConsumerLoad<D, BITS>& ca, const 
   weights(ws.m_run);
   float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
   mx = rows_max(mx) + bias_a;
-  if (__any(mx > ws.m_run)) {
+  const int gE = group_norm_exponent(ca.nrm0, ca.nrm1, kg, rem_a);
+  if (__any(mx > ws.m_run) || gE > ws.nE) {
     const float m_new = fmaxf(ws.m_run, mx + kLazyMax);
-    const float alpha = exp2f(ws.m_run - m_new);   // 0 on the first group
+    const int nE_new = max(ws.nE, gE);
+    const float alpha = exp2f((ws.m_run - m_new) - static_cast<float>(nE_new - ws.nE));   // 0 on the first group
     ws.l_run *= alpha;
     const float alpha_v = __uint_as_float(to_value_column<SLOTS>(__float_as_uint(alpha)));
 #pragma unroll
@@ -1005,7 +1074,9 @@ __device__ __forceinline__ void sw_back1(const ConsumerLoad<D, BITS>& ca, const 
       for (int ct = 0; ct < CT; ++ct) ws.acc[k][ct] *= alpha_v;
     }
     ws.m_run = m_new;
-    // arguments are now <= 0 (or -inf): the raw base-2 exponential flushes only results below 2^-126
+    ws.nE = nE_new;
+    ws.wshift = static_cast<float>(kWeightExp + 14 - nE_new);
+    // arguments are now <= wshift (or -inf): the raw base-2 exponential flushes only results below 2^-126
     weights(ws.m_run);
   }
   ws.l_run += ((pe[0] + pe[1]) + (pe[2] + pe[3])) + ((pe[4] + pe[5]) + (pe[6] + pe[7]));
@@ -1104,7 +1175,7 @@ __global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(D
   const int kg = lane >> 4, col = lane & 15;
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int G = a.group;
-  const int L = a.seq_len[b];
+  const int L = session_length(a, b);
   const int tb = split * a.split_tokens;
   const int te = (split == a.splits - 1) ? L : min(tb + a.split_tokens, L);
   const int ng = te > tb ? (te - tb + kGroupTokens - 1) / kGroupTokens : 0;   // groups of the partition
@@ -1116,9 +1187,13 @@ __global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(D
   const int ps = a.page_shift;                     // page_tokens is a power of two here
   const int pmask = a.page_tokens - 1;
   const int page0 = tb >> ps;
-  const int npg = ng > 0 ? ((te - 1) >> ps) - page0 + 1 : 0;
+  // The page run covers the partition's planned span [tb, tb + split_tokens)
+  // (at most kPageRun pages by the plan), or for the last partition, which
+  // takes every position past the plan, kPageRun pages; its load does not
+  // wait for the session length.
+  const int npl = split == a.splits - 1 ? kPageRun : min(((tb + a.split_tokens - 1) >> ps) - page0 + 1, kPageRun);
   int pt_entry = -1;
-  if (tid < npg) pt_entry = a.page_table[static_cast<size_t>(b) * a.max_pages + page0 + tid];
+  if (tid < npl && page0 + tid < a.max_pages) pt_entry = a.page_table[static_cast<size_t>(b) * a.max_pages + page0 + tid];
   const SwRsrc rs = sw_rsrc(a);
   const int hoff = h * (a.page_tokens / kGroupTokens);
   static_assert(kPageRun <= NT, "one page-run entry per thread");
@@ -1174,6 +1249,8 @@ __global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(D
   WaveState<D, SLOTS, ASYM> ws;
   ws.m_run = -__builtin_inff();
   ws.l_run = 0.f;
+  ws.nE = 1;
+  ws.wshift = static_cast<float>(kWeightExp + 13);
   ws.mask = 0;
 #pragma unroll
   for (int k = 0; k < NSETS; ++k)
@@ -1194,8 +1271,9 @@ __global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(D
   auto locate = [&](int j, int& blk, int& moff) {
     const int gi = wave + NW * j;
     const int t0 = tb + gi * kGroupTokens;
-    const int phys = __builtin_amdgcn_readfirstlane(s_pt[min((t0 >> ps) - page0, kPageRun - 1)]);
-    const bool ok = j < steps && gi < ng && phys >= 0 && phys < a.num_pages;
+    const bool inside = j < steps && gi < ng;
+    const int phys = inside ? phys_page(a, s_pt, npl, b, page0, t0 >> ps) : -1;
+    const bool ok = inside && phys >= 0 && phys < a.num_pages;
     const int tin = t0 & pmask;
     blk = ok ? phys * a.blocks_per_page + hoff + (tin >> 5) : 0;
     moff = ok ? phys * a.page_tokens + tin : 0;
@@ -1303,7 +1381,7 @@ __global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(D
   const int slot_c = col / GP, hp = col % GP;
   const float l_col = rows_sum(ws.l_run);
   if (kg == 0) {
-    s_m[c][col] = ws.m_run;
+    s_m[c][col] = ws.m_run - ws.wshift;   // the reference of the scaled sums
     s_l[c][col] = l_col;
     if (slot_c < SLOTS) {
 #pragma unroll
@@ -1602,7 +1680,13 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
   static_assert(QT == 16, "one output row per 16-lane row");
   acc = row16_sum(acc);
   if constexpr (ASYM) rs = row16_sum(rs);
-  if (q == 0) a.out[head * D + row] = (l > 0.f) ? (a.chalf * acc + a.cmid * rs) * (a.value_scale / l) : 0.f;
+  if (q == 0) {
+    const float o = (l > 0.f) ? (a.chalf * acc + a.cmid * rs) * (a.value_scale / l) : 0.f;
+    if (a.out_bf16)
+      static_cast<uint16_t*>(a.out)[head * D + row] = f32_to_bf16_rne(o);
+    else
+      static_cast<float*>(a.out)[head * D + row] = o;
+  }
 }
 
 template <int D, int SLOTS, int NW>

@@ -72,7 +72,7 @@ struct DecodeArgs {
   const int32_t* seq_len;
   const float* q_rot;
   const float* rot;
-  float* out;
+  void* out;              // [B][Hq][d] fp32, or bf16 when out_bf16
   float* partials;        // workspace: [B][Hq][splits][kPartialHeader + 3d] partials
   int32_t batch;
   int32_t hq, hkv, group, page_tokens, max_pages, num_pages;
@@ -86,6 +86,7 @@ struct DecodeArgs {
   float cmid, chalf;      // codebook centre (c0 + c3) / 2 and half range (c3 - c0) / 2
   int32_t key_mode;       // KVQ_KEYS_GROUP_MINMAX or KVQ_KEYS_PER_TOKEN
   int32_t bits;           // code width (2, 3, 4)
+  int32_t out_bf16;       // write the output as bf16 (round to nearest even) instead of fp32
   uint32_t level_f16[8];  // normalized levels (2 c_k - c0 - c_{n-1}) / (c_{n-1} - c0) as fp16 bits, k < n
   uint32_t level_lo_f16[8]; // 2^12 (level - fp16 level) as fp16 bits (3 / 4 bits: the scores' lo part)
   uint2 byte_levels[256]; // byte e of four 2-bit codes -> its four fp16 levels (code of bits 2i..2i+1 first)

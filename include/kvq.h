@@ -214,20 +214,31 @@ size_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t max_len);
  *   out[b][i] = sum_m R_{h,m} A_m
  * The context is split into partitions processed in parallel (online
  * softmax per partition); a second kernel merges them and applies R_{h,m}.
- * q_rot: device [batch][Hq][d] fp32 (from kvq_rotate_query); out: device
- * [batch][Hq][d] fp32; a session with no such position gives zeros.  Pages
- * that are not retained still count towards the plan (their steps are
- * skipped, not compacted away).  The partition plan
- * comes from max(seq_len_host).  workspace: device, at least
- * kvq_decode_workspace_bytes(cfg, max(seq_len_host)) bytes.
- * Errors: KVQ_ERR_INVALID, KVQ_ERR_WORKSPACE, KVQ_ERR_LAUNCH,
- * KVQ_ERR_UNSUPPORTED (also for a session longer than 4096 partitions of at
- * most 510 pages each, i.e. 4096 * floor(510 * page_tokens / 256) * 256
- * positions).
+ * q_rot: device [batch][Hq][d] fp32 (from kvq_rotate_query).
+ * out: device [batch][Hq][d] in out_dtype: KVQ_F32, or KVQ_BF16 (the fp32
+ * result rounded to nearest even); a session with no attended position
+ * gives zeros.  Pages that are not retained still count towards the plan
+ * (their steps are skipped, not compacted away).
+ * Plan and replay: the partition plan comes from max(seq_len_host) at the
+ * call.  The kernels read the lengths from the device seq_len, so a decode
+ * captured in a HIP graph and replayed after appends have advanced seq_len
+ * on the device stays correct: the last partition of each session takes
+ * every position past the plan, up to max_pages * page_tokens (the kernels
+ * bound the length there), reading its page-table entries beyond the
+ * planned span from global memory.  It only gets slower as the sessions
+ * outgrow the captured plan.
+ * workspace: device, at least kvq_decode_workspace_bytes(cfg,
+ * max(seq_len_host)) bytes, owned by the caller; calls that share a
+ * workspace must not overlap in time.
+ * Errors: KVQ_ERR_INVALID (null pointers, lengths outside [0, capacity],
+ * non-finite scale), KVQ_ERR_WORKSPACE, KVQ_ERR_LAUNCH, KVQ_ERR_UNSUPPORTED
+ * (out_dtype not KVQ_F32 / KVQ_BF16; a session longer than 4096 partitions
+ * of at most 510 pages each, i.e. 4096 * floor(510 * page_tokens / 256) *
+ * 256 positions).
  */
 kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache,
                                 const kvq_params* params, const float* q_rot, float scale,
-                                float* out, void* workspace, size_t workspace_bytes,
+                                void* out, int32_t out_dtype, void* workspace, size_t workspace_bytes,
                                 hipStream_t stream);
 
 /* Static description of a status code. */

@@ -125,10 +125,11 @@ def test_decode_and_rotate_reject_bad_arguments():
     c, lens = _fake_cache(L, [10, 1000])
     need = lib.kvq_decode_workspace_bytes(ctypes.byref(cfg), 1000)
     assert need > 0
-    dec = lambda ws, nbytes, scale=0.1: lib.kvq_decode_attention(
+    dec = lambda ws, nbytes, scale=0.1, od=L.KVQ_F32: lib.kvq_decode_attention(
         ctypes.byref(cfg), ctypes.byref(c), ctypes.byref(p), ctypes.c_void_p(8), ctypes.c_float(scale),
-        ctypes.c_void_p(8), ws, nbytes, None)
+        ctypes.c_void_p(8), od, ws, nbytes, None)
     assert dec(None, need) == L.KVQ_ERR_WORKSPACE
+    assert dec(ctypes.c_void_p(8), need, od=7) == L.KVQ_ERR_UNSUPPORTED          # output dtype
     assert dec(ctypes.c_void_p(8), need - 1) == L.KVQ_ERR_WORKSPACE
     assert dec(ctypes.c_void_p(8), need, float("nan")) == L.KVQ_ERR_INVALID
     lens[1] = 5000                                                                # beyond capacity

@@ -383,6 +383,9 @@ def test_graph_replayed_single_token_appends():
 
 # ------------------------------------------------------- full-size workloads
 
+ORACLE_THREADS = 16    # host threads for the oracle side of the full-size checks
+
+
 def _decode_parity(w, cfg, params, cache, sessions, out=None):
     import decode_attention_kvq_amd as K
     h = H()
@@ -390,7 +393,8 @@ def _decode_parity(w, cfg, params, cache, sessions, out=None):
     if out is None:
         q_rot = K.kvq_rotate_query(cfg, params, h.query_tensor(w))
         out = K.kvq_decode_attention(cfg, cache, params, q_rot, scale).cpu().numpy()
-    ref = h.oracle_decode_over_gpu_codes(w, cfg, cache, O.as_f64(w.q, w.dtype), sessions, scale)
+    ref = h.oracle_decode_over_gpu_codes(w, cfg, cache, O.as_f64(w.q, w.dtype), sessions, scale,
+                                         threads=ORACLE_THREADS)
     worst = max(float(h.normwise_rel_err(out[b].astype(np.float64), ref[b]).max()) for b in sessions)
     return worst
 
@@ -409,9 +413,25 @@ def test_full_80k_context():
     assert worst <= h.ATTN_TOL
 
 
+def test_full_16k_context():
+    """The 16K workload at its full size (16,384 positions, 16/2 heads):
+    every code and statistic, and every head's output."""
+    h = H()
+    w = generate(1)
+    assert int(w.lengths[0]) == 16384
+    _say(f"full 16K: {int(w.lengths[0])} positions")
+    cfg, params, cache = h.build(w, chunks=[5000])
+    total, mism = h.check_codes(w, cfg, cache, [0])
+    _say(f"codes: {total} elements, {mism} boundary mismatches")
+    worst = _decode_parity(w, cfg, params, cache, [0])
+    _say(f"decode worst normwise rel err {worst:.3e}")
+    assert worst <= h.ATTN_TOL
+
+
 def test_full_batched_paged_sessions():
     """32 sessions of 8K..64K positions under a random page table, decoded in
-    one launch; codes and outputs of a sample of sessions against the oracle."""
+    one launch: the codes and statistics of every session and every head's
+    output against the oracle."""
     import decode_attention_kvq_amd as K
     h = H()
     w = generate(3)
@@ -419,13 +439,13 @@ def test_full_batched_paged_sessions():
     cfg, params, cache = h.build(w, chunks=[16384])
     q_rot = K.kvq_rotate_query(cfg, params, h.query_tensor(w))
     out = K.kvq_decode_attention(cfg, cache, params, q_rot, h.default_scale(w)).cpu().numpy()
-    sample = [0, int(np.argmax(w.lengths)), int(np.argmin(w.lengths)), 31]
-    total, mism = h.check_codes(w, cfg, cache, sample)
-    _say(f"codes of sessions {sample}: {total} elements, {mism} boundary mismatches")
-    worst = _decode_parity(w, cfg, params, cache, sample, out)
-    _say(f"decode worst normwise rel err {worst:.3e}")
-    assert worst <= h.ATTN_TOL
     assert np.all(np.isfinite(out))
+    sessions = list(range(w.cfg.batch))
+    total, mism = h.check_codes(w, cfg, cache, sessions, threads=ORACLE_THREADS)
+    _say(f"codes of all {len(sessions)} sessions: {total} elements, {mism} boundary mismatches")
+    worst = _decode_parity(w, cfg, params, cache, sessions, out)
+    _say(f"decode worst normwise rel err over all sessions {worst:.3e}")
+    assert worst <= h.ATTN_TOL
 
 
 def test_full_stream_loop_append():

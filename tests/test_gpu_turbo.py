@@ -101,3 +101,42 @@ def test_per_token_keys_need_the_streaming_kernel():
     with pytest.raises(K.KvqError) as e:
         K.kvq_decode_attention(cfg, cache, params, q_rot)
     assert e.value.status == 2
+
+
+def test_key_grouping_harness_on_gpu_codes():
+    """The key-grouping comparison (Sec. 3, "Key Adaptation" bullet) run
+    through the kernels: for each grouping order the permuted stream is
+    appended with kvq_quantize_append, and the relative error of the rotated
+    keys rebuilt from the GPU's codes and statistics equals the oracle's
+    harness number; the per-token (TurboQuant) key codec likewise."""
+    import dataclasses
+
+    import decode_attention_kvq_amd as K
+    from decode_attention_kvq_amd.layout import session_view
+    h = H()
+    w = generate(2, length=16384)
+    n = int(w.lengths[0])
+    k64 = O.as_f64(w.k[0], w.dtype)
+    for order in O.GROUP_ORDERS:
+        perm = O.grouping_order(w.modality[0], order)
+        wp = dataclasses.replace(w, k=[w.k[0][perm]], v=[w.v[0][perm]], modality=[w.modality[0][perm]])
+        cfg, params, cache = h.build(wp)
+        host = cache.host_arrays()
+        for hh in range(w.cfg.n_kv_heads):
+            g = session_view(host, cfg, 0, n, hh)
+            y = O.randomized_hadamard(k64[perm, hh], w.signs[hh])
+            y_hat = O.dequantize_keys(g["k_codes"], g["lo"], g["hi"], w.codebook)
+            got = float(((y - y_hat) ** 2).sum() / (y ** 2).sum())
+            ref = O.key_grouping_error(k64[:, hh], w.modality[0], w.signs[hh], w.codebook, order)
+            _say(f"{order:18s} head {hh}: GPU codes {got:.6f}, oracle {ref:.6f}")
+            assert abs(got - ref) <= 1e-6 * ref
+    cfg, params, cache = h.build(w, key_mode=K.KVQ_KEYS_PER_TOKEN, rot=h.hadamard_rot(w))
+    host = cache.host_arrays()
+    for hh in range(w.cfg.n_kv_heads):
+        g = session_view(host, cfg, 0, n, hh)
+        y = O.randomized_hadamard(k64[:, hh], w.signs[hh])
+        y_hat = O.dequantize_keys_per_token(g["k_codes"], g["k_norms"], w.codebook)
+        got = float(((y - y_hat) ** 2).sum() / (y ** 2).sum())
+        ref = O.per_token_key_error(k64[:, hh], w.signs[hh], w.codebook)
+        _say(f"per-token keys     head {hh}: GPU codes {got:.6f}, oracle {ref:.6f}")
+        assert abs(got - ref) <= 1e-6 * ref
