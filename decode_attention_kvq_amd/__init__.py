@@ -19,7 +19,8 @@ from ._lib import (KVQ_BF16, KVQ_F32, KVQ_KEYS_GROUP_MINMAX, KVQ_KEYS_PER_TOKEN,
                    KvqCalibShape, KvqConfig, KvqError, KvqParams)
 
 __all__ = ["Config", "Params", "Cache", "kvq_quantize_append", "kvq_rotate_query", "kvq_append_and_rotate",
-           "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_calib_workspace_bytes",
+           "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_decode_attention_noalloc",
+           "kvq_calib_workspace_bytes",
            "kvq_calib_eigenbasis_workspace_bytes", "kvq_calib_contribution", "kvq_calib_covariance",
            "kvq_calib_eigenbasis", "KvqError"]
 
@@ -201,6 +202,24 @@ def kvq_decode_attention(cfg: Config, cache: Cache, params: Params, q_rot: torch
         _dev(q_rot, "q_rot", torch.float32), float(scale), _dev(out, "out"), _DTYPES[out.dtype],
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
     _lib.check("kvq_decode_attention", st)
+    return out
+
+
+def kvq_decode_attention_noalloc(cfg: Config, cache: Cache, params: Params, q_rot: torch.Tensor,
+                                 out: torch.Tensor, scale: Optional[float] = None, stream=None) -> torch.Tensor:
+    """kvq_decode_attention with the partials in the library's static device
+    scratch: nothing is allocated, by the library or here (the caller passes
+    `out`, [batch, Hq, d] fp32 or bf16)."""
+    if tuple(q_rot.shape) != (cfg.batch, cfg.n_q_heads, cfg.head_dim):
+        raise ValueError("q_rot must be [batch, Hq, d]")
+    if out.dtype not in _DTYPES or tuple(out.shape) != tuple(q_rot.shape):
+        raise ValueError("out must be [batch, Hq, d] float32 or bfloat16")
+    if scale is None:
+        scale = 1.0 / math.sqrt(cfg.head_dim)
+    st = _lib.load().kvq_decode_attention_noalloc(
+        ctypes.byref(cfg.struct), ctypes.byref(cache.struct), ctypes.byref(params.struct),
+        _dev(q_rot, "q_rot", torch.float32), float(scale), _dev(out, "out"), _DTYPES[out.dtype], _stream(stream))
+    _lib.check("kvq_decode_attention_noalloc", st)
     return out
 
 

@@ -9,12 +9,15 @@ import torch  # noqa: F401  (loads the HIP runtime the library binds to)
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkvq.so")
 
-KVQ_OK, KVQ_ERR_INVALID, KVQ_ERR_UNSUPPORTED, KVQ_ERR_CAPACITY, KVQ_ERR_WORKSPACE, KVQ_ERR_LAUNCH = range(6)
+(KVQ_OK, KVQ_ERR_INVALID, KVQ_ERR_UNSUPPORTED, KVQ_ERR_CAPACITY, KVQ_ERR_WORKSPACE, KVQ_ERR_LAUNCH,
+ KVQ_ERR_SCRATCH) = range(7)
+KVQ_NOALLOC_SCRATCH_BYTES = 16 << 20      # include/kvq.h
 KVQ_F32, KVQ_BF16 = 0, 1
 KVQ_KEYS_GROUP_MINMAX, KVQ_KEYS_PER_TOKEN = 0, 1
 
 EXPORTED = ("kvq_cache_buffer_bytes", "kvq_quantize_append", "kvq_rotate_query", "kvq_append_and_rotate",
-            "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_status_string",
+            "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_decode_attention_noalloc",
+            "kvq_status_string",
             "kvq_calib_workspace_bytes", "kvq_calib_eigenbasis_workspace_bytes", "kvq_calib_contribution",
             "kvq_calib_covariance", "kvq_calib_eigenbasis")
 
@@ -84,6 +87,9 @@ def load() -> ctypes.CDLL:
                                          ctypes.c_float, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                          ctypes.c_size_t, ctypes.c_void_p]
     lib.kvq_decode_attention.restype = ctypes.c_int
+    lib.kvq_decode_attention_noalloc.argtypes = [P(KvqConfig), P(KvqCache), P(KvqParams), ctypes.c_void_p,
+                                                 ctypes.c_float, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+    lib.kvq_decode_attention_noalloc.restype = ctypes.c_int
     V = ctypes.c_void_p
     lib.kvq_calib_workspace_bytes.argtypes = [P(KvqCalibShape)]
     lib.kvq_calib_workspace_bytes.restype = ctypes.c_size_t

@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "kvq_internal.h"
 
@@ -120,6 +121,7 @@ const char* kvq_status_string(kvq_status s) {
     case KVQ_ERR_CAPACITY: return "cache capacity exceeded";
     case KVQ_ERR_WORKSPACE: return "workspace missing or too small";
     case KVQ_ERR_LAUNCH: return "kernel launch failed";
+    case KVQ_ERR_SCRATCH: return "decode partials exceed the no-allocation scratch (KVQ_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }
@@ -257,10 +259,42 @@ size_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t max_len) {
   return workspace_floats(cfg, Plan{splits_bound(cfg, max_len), 0}) * sizeof(float);
 }
 
-kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache,
-                                const kvq_params* params, const float* q_rot, float scale,
-                                void* out, int32_t out_dtype, void* workspace, size_t workspace_bytes,
-                                hipStream_t stream) {
+}  // extern "C"
+
+// ------------------------------------------------ decode without allocation
+//
+// The partial results of kvq_decode_attention_noalloc live in `scratch`, a
+// device array of this file that each GPU the library runs on holds until the
+// process ends.  Host code never passes the array's name to a kernel (on the
+// host it is only a stand-in for the symbol): its device address is looked up
+// once per device with hipGetSymbolAddress, with that device current, and
+// kept in g_scratch_ptr.
+static __device__ __align__(256) float scratch[KVQ_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+static constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch array, or null on error.
+static void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+// The decode behind both entry points: the partial results go to the
+// caller's `workspace` (workspace_bytes long) or, with scratch = true, to the
+// current device's scratch array; every argument is checked before either is
+// touched.
+static kvq_status decode_impl(const kvq_config* cfg, const kvq_cache* cache, const kvq_params* params,
+                              const float* q_rot, float scale, void* out, int32_t out_dtype, void* workspace,
+                              size_t workspace_bytes, bool scratch, hipStream_t stream) {
   kvq_status st = check_config(cfg);
   if (st != KVQ_OK) return st;
   if ((st = check_params(cfg, params)) != KVQ_OK) return st;
@@ -275,7 +309,14 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache,
   }
   if (!plan_supported(cfg, max_len)) return KVQ_ERR_UNSUPPORTED;
   const Plan plan = plan_decode(cfg, max_len);
-  if (!workspace || workspace_bytes < workspace_floats(cfg, plan) * sizeof(float)) return KVQ_ERR_WORKSPACE;
+  const size_t need = workspace_floats(cfg, plan) * sizeof(float);
+  if (scratch) {
+    if (need > KVQ_NOALLOC_SCRATCH_BYTES) return KVQ_ERR_SCRATCH;
+    workspace = scratch_address();
+    if (!workspace) return KVQ_ERR_LAUNCH;
+  } else if (!workspace || workspace_bytes < need) {
+    return KVQ_ERR_WORKSPACE;
+  }
   const int nlev = 1 << cfg->bits;
   const double c0 = params->codebook[0], c3 = params->codebook[nlev - 1];   // outer levels
   kvq::DecodeArgs a;
@@ -338,6 +379,23 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache,
     return KVQ_ERR_UNSUPPORTED;
   hipError_t e = kvq::launch_decode(cfg->head_dim, cfg->batch, a, stream);
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;
+}
+
+
+extern "C" {
+
+kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache,
+                                const kvq_params* params, const float* q_rot, float scale,
+                                void* out, int32_t out_dtype, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  return decode_impl(cfg, cache, params, q_rot, scale, out, out_dtype, workspace, workspace_bytes, false, stream);
+}
+
+kvq_status kvq_decode_attention_noalloc(const kvq_config* cfg, const kvq_cache* cache,
+                                        const kvq_params* params, const float* q_rot, float scale,
+                                        void* out, int32_t out_dtype, hipStream_t stream) {
+  return decode_impl(cfg, cache, params, q_rot, scale, out, out_dtype, nullptr, KVQ_NOALLOC_SCRATCH_BYTES, true,
+                     stream);
 }
 
 }  // extern "C"

@@ -83,7 +83,8 @@ typedef enum {
   KVQ_ERR_UNSUPPORTED = 2,  /* d not in {64,128}, G > 16, dtype not supported */
   KVQ_ERR_CAPACITY = 3,     /* append would exceed max_pages * page_tokens */
   KVQ_ERR_WORKSPACE = 4,    /* decode workspace null or too small */
-  KVQ_ERR_LAUNCH = 5        /* a HIP launch failed */
+  KVQ_ERR_LAUNCH = 5,       /* a HIP launch failed */
+  KVQ_ERR_SCRATCH = 6       /* kvq_decode_attention_noalloc: partials beyond the static scratch */
 } kvq_status;
 
 typedef enum { KVQ_F32 = 0, KVQ_BF16 = 1 } kvq_dtype;
@@ -240,6 +241,29 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache,
                                 const kvq_params* params, const float* q_rot, float scale,
                                 void* out, int32_t out_dtype, void* workspace, size_t workspace_bytes,
                                 hipStream_t stream);
+
+/*
+ * kvq_decode_attention_noalloc - kvq_decode_attention for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments (minus the workspace),
+ * same kernels and plan, bitwise the same output.  The split-K partial
+ * results go to a device array inside the library,
+ * KVQ_NOALLOC_SCRATCH_BYTES (16 MiB) per GPU, held by each GPU the library
+ * runs on until the process ends; the call itself allocates and frees
+ * nothing.  Nothing in the array needs to start at zero (every partial a
+ * decode reads, it writes first).  Every call on one GPU shares that GPU's
+ * array: calls that overlap in time on one GPU (two streams, two host
+ * threads) race and give wrong results; serialise them.  The partials of a
+ * decode take batch * Hq * splits * (8 + 3 d) * 4 bytes (splits from the
+ * partition plan of max(seq_len_host)); larger requests return
+ * KVQ_ERR_SCRATCH before anything is launched.  Errors: those of
+ * kvq_decode_attention except KVQ_ERR_WORKSPACE, plus KVQ_ERR_SCRATCH;
+ * KVQ_ERR_LAUNCH also when the scratch address cannot be obtained.
+ */
+#define KVQ_NOALLOC_SCRATCH_BYTES (16u << 20)
+kvq_status kvq_decode_attention_noalloc(const kvq_config* cfg, const kvq_cache* cache,
+                                        const kvq_params* params, const float* q_rot, float scale,
+                                        void* out, int32_t out_dtype, hipStream_t stream);
 
 /* Static description of a status code. */
 const char* kvq_status_string(kvq_status status);

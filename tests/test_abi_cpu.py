@@ -144,6 +144,26 @@ def test_decode_and_rotate_reject_bad_arguments():
         assert lib.kvq_status_string(s)
 
 
+def test_noalloc_decode_rejects_before_launch():
+    """The no-allocation decode checks its arguments, then the size of the
+    partials against the static scratch, on the host: a plan needing more
+    than KVQ_NOALLOC_SCRATCH_BYTES returns KVQ_ERR_SCRATCH with no launch and
+    no device call (this host has no GPU)."""
+    L, lib = _lib()
+    p = _fake_params(L)
+    V = ctypes.c_void_p
+    call = lambda cfg, c, od=L.KVQ_F32: lib.kvq_decode_attention_noalloc(
+        ctypes.byref(cfg), ctypes.byref(c), ctypes.byref(p), V(8), ctypes.c_float(0.1), V(8), od, None)
+    big = _cfg(L, batch=64, n_q_heads=128, n_kv_heads=8, max_pages=256, num_pages=64 * 256)
+    c, lens = _fake_cache(L, [65536] * 64)
+    # 64 sessions x 128 query heads x 2 partitions x (8 + 3 * 128) floats = 25.7 MB > 16 MiB
+    assert call(big, c) == L.KVQ_ERR_SCRATCH
+    assert call(big, c, od=9) == L.KVQ_ERR_UNSUPPORTED
+    lens[3] = -1
+    assert call(big, c) == L.KVQ_ERR_INVALID
+    assert lib.kvq_status_string(L.KVQ_ERR_SCRATCH)
+
+
 def test_append_and_rotate_rejects_bad_arguments_before_launch():
     """The fused call checks both halves on the host; a failure in either
     launches nothing and leaves the length mirror untouched."""
