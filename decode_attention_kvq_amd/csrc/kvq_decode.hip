@@ -1504,23 +1504,16 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
   __shared__ float s_M;
 
   // Workgroup -> (session b, KV head h, query head of the group gq, row
-  // block rb).  With at least 8 (session, KV head) keys, every workgroup of
-  // one key sits on the XCD key mod 8, sharing its rotations and partials
-  // through one L2; with fewer keys, key k takes the XCDs k, k + keys, ...
-  // so that every XCD works.
+  // block rb): every workgroup of one (session, KV head) key sits on the XCD
+  // key mod 8 (workgroups are dealt to the XCDs round robin), so the key's
+  // rotations and partials are fetched from HBM once and shared through that
+  // XCD's L2; with fewer than 8 keys the other XCDs stay idle.
   const int x = blockIdx.x % kXcds, y = blockIdx.x / kXcds;
   const int per_key = a.group * RB;
   const int keys = a.batch * a.hkv;
-  int key, item;
-  if (keys >= kXcds) {
-    key = (y / per_key) * kXcds + x;               // b * Hkv + h
-    item = y % per_key;
-  } else {
-    key = x % keys;
-    const int nx = (kXcds - 1 - key) / keys + 1;   // XCDs serving this key
-    item = y * nx + x / keys;
-  }
-  if (key >= keys || item >= per_key) return;
+  const int key = (y / per_key) * kXcds + x;       // b * Hkv + h
+  const int item = y % per_key;
+  if (key >= keys) return;
   const int gq = item / RB, rb = item % RB;
   const int h = key % a.hkv;
   const int i = h * a.group + gq;
@@ -1731,7 +1724,7 @@ hipError_t launch_decode_t(int batch, const DecodeArgs& a, hipStream_t s) {
   else launch_partition<D, 1, kDecodeWaves / 2>(batch, a, s);
   const int keys = a.hkv * batch;
   const int per_key = a.group * MergeShape<D>::RB;
-  const int rows = keys >= kXcds ? ((keys + kXcds - 1) / kXcds) * per_key : (per_key + kXcds / keys - 1) / (kXcds / keys);
+  const int rows = ((keys + kXcds - 1) / kXcds) * per_key;
   const dim3 mgrid(kXcds * rows);
   if (a.cmid != 0.f)
     hipLaunchKernelGGL((decode_merge_kernel<D, true>), mgrid, dim3(kMergeThreads), 0, s, a);

@@ -313,7 +313,7 @@ def test_graph_replays_match_eager():
     q_rot = K.kvq_rotate_query(cfg, params, h.query_tensor(w))
     eager = K.kvq_decode_attention(cfg, cache, params, q_rot).clone()
     out = torch.empty_like(eager)
-    ws = torch.empty(K.kvq_decode_workspace_bytes(cfg, 3000), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(K.kvq_decode_workspace_bytes(cfg, 3000), dtype=torch.uint8, device="cuda")
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())

@@ -113,7 +113,7 @@ def test_captured_decode_replayed_after_the_sessions_outgrow_its_plan():
     scale = h.default_scale(w)
     q_rot = K.kvq_rotate_query(cfg, params, h.query_tensor(w))
     out = torch.empty(q_rot.shape, dtype=torch.float32, device=q_rot.device)
-    ws = torch.empty(K.kvq_decode_workspace_bytes(cfg, 1000), dtype=torch.uint8, device=q_rot.device)
+    ws = torch.zeros(K.kvq_decode_workspace_bytes(cfg, 1000), dtype=torch.uint8, device=q_rot.device)
     K.kvq_decode_attention(cfg, cache, params, q_rot, scale, out, ws)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
@@ -134,3 +134,27 @@ def test_captured_decode_replayed_after_the_sessions_outgrow_its_plan():
         err = float(h.normwise_rel_err(got[0], ref[0]).max())
         _say(f"replay at {n} positions: worst normwise rel err {err:.3e}")
         assert err <= h.ATTN_TOL
+
+
+def test_one_workspace_serves_successive_decodes_of_different_shapes():
+    """One workspace reused by decodes of three different configurations
+    (twice each) gives bitwise the outputs of fresh workspaces: nothing a
+    decode reads from it is left over from an earlier decode."""
+    import decode_attention_kvq_amd as K
+    h = H()
+    shapes = [(2, dict(length=9000)), (3, dict(batch=3, len_range=(700, 2600))), (1, dict(length=2100, n_q_heads=32))]
+    built = []
+    need = 0
+    for cfg_id, kw in shapes:
+        w = generate(cfg_id, **kw)
+        cfg, params, cache = h.build(w)
+        q_rot = K.kvq_rotate_query(cfg, params, h.query_tensor(w))
+        built.append((cfg, params, cache, q_rot))
+        need = max(need, K.kvq_decode_workspace_bytes(cfg, max(cache.lengths())))
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")      # stale bytes: a large float pattern
+    for rep in range(2):
+        for cfg, params, cache, q_rot in built:
+            ref = K.kvq_decode_attention(cfg, cache, params, q_rot)
+            got = K.kvq_decode_attention(cfg, cache, params, q_rot, workspace=ws)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(got.cpu().numpy().view(np.uint32), ref.cpu().numpy().view(np.uint32))
