@@ -375,27 +375,35 @@ def extra_80k(K, cfg, params, caches, table, q_rot, out, ws, scale, n_dec, dec_b
 
 
 def time_stream_read(nbytes: int, replicas: int, launches: int) -> dict:
-    """A plain streaming read of nbytes (the decode's algorithmic bytes): one
-    torch sum-reduction over int32 words of a replica buffer per launch, the
-    replicas cycled so the reads come from HBM; HIP events over `launches`
-    launches.  The time of one launch of a read-only kernel of this size."""
+    """The floor for one read-only kernel of nbytes (the decode's algorithmic
+    bytes): kvq_probe_stream_read, a plain 16-byte streaming read, over
+    `replicas` buffers cycled so the reads come from HBM, HIP events over
+    `launches` launches, for several grid sizes; the fastest is reported."""
     import torch
-    bufs = [torch.ones(nbytes // 4, dtype=torch.int32, device="cuda") for _ in range(replicas)]
-    sink = torch.empty((), dtype=torch.int64, device="cuda")
-    for b in bufs:
-        torch.sum(b, dim=0, dtype=torch.int64, out=sink)
-    torch.cuda.synchronize()
+    import decode_attention_kvq_amd as K
+    nb = (nbytes // 16) * 16
+    bufs = [torch.ones(nb // 4, dtype=torch.int32, device="cuda") for _ in range(replicas)]
+    sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
-    e0, e1 = _events()
-    e0.record(stream)
-    for i in range(launches):
-        torch.sum(bufs[i % replicas], dim=0, dtype=torch.int64, out=sink)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / launches
-    nb = (nbytes // 4) * 4
+    shapes = {}
+    for wgs in (256, 512, 1024, 2048, 4096):
+        for b in bufs:
+            K.kvq_probe_stream_read(b, sink, wgs)
+        torch.cuda.synchronize()
+        e0, e1 = _events()
+        e0.record(stream)
+        for i in range(launches):
+            K.kvq_probe_stream_read(bufs[i % replicas], sink, wgs)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        shapes[wgs] = e0.elapsed_time(e1) * 1e3 / launches
+    best = min(shapes, key=shapes.get)
+    us = shapes[best]
+    del bufs
     return {"bytes_per_launch": nb, "avg_launch_us": us, "GBps": nb / us / 1e3,
-            "frac_of_8TBps": nb / us / 1e3 / HBM_PEAK_GBS, "kernel": "torch.sum over int32 (reduction)"}
+            "frac_of_8TBps": nb / us / 1e3 / HBM_PEAK_GBS, "workgroups": best,
+            "us_by_workgroups": {str(k): round(v, 3) for k, v in shapes.items()},
+            "kernel": "kvq_probe_stream_read (256 threads per workgroup)"}
 
 
 def time_batched_paged(replicas: int, n_rep: int = 10) -> dict:

@@ -20,7 +20,7 @@ from ._lib import (KVQ_BF16, KVQ_F32, KVQ_KEYS_GROUP_MINMAX, KVQ_KEYS_PER_TOKEN,
 
 __all__ = ["Config", "Params", "Cache", "kvq_quantize_append", "kvq_rotate_query", "kvq_append_and_rotate",
            "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_decode_attention_noalloc",
-           "kvq_calib_workspace_bytes",
+           "kvq_calib_workspace_bytes", "kvq_probe_stream_read",
            "kvq_calib_eigenbasis_workspace_bytes", "kvq_calib_contribution", "kvq_calib_covariance",
            "kvq_calib_eigenbasis", "KvqError"]
 
@@ -221,6 +221,16 @@ def kvq_decode_attention_noalloc(cfg: Config, cache: Cache, params: Params, q_ro
         _dev(q_rot, "q_rot", torch.float32), float(scale), _dev(out, "out"), _DTYPES[out.dtype], _stream(stream))
     _lib.check("kvq_decode_attention_noalloc", st)
     return out
+
+
+def kvq_probe_stream_read(buf: torch.Tensor, sink: torch.Tensor, workgroups: int, stream=None) -> None:
+    """Measurement aid: one launch reading every byte of `buf` once (see
+    include/kvq.h); sink: int32 tensor of at least `workgroups` words."""
+    if sink.numel() < workgroups:
+        raise ValueError("sink needs one word per workgroup")
+    st = _lib.load().kvq_probe_stream_read(_dev(buf, "buf"), buf.numel() * buf.element_size(),
+                                           _dev(sink, "sink", torch.int32), int(workgroups), _stream(stream))
+    _lib.check("kvq_probe_stream_read", st)
 
 
 # ------------------------------------------------------ value-basis calibration

@@ -17,7 +17,7 @@ KVQ_KEYS_GROUP_MINMAX, KVQ_KEYS_PER_TOKEN = 0, 1
 
 EXPORTED = ("kvq_cache_buffer_bytes", "kvq_quantize_append", "kvq_rotate_query", "kvq_append_and_rotate",
             "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_decode_attention_noalloc",
-            "kvq_status_string",
+            "kvq_status_string", "kvq_probe_stream_read",
             "kvq_calib_workspace_bytes", "kvq_calib_eigenbasis_workspace_bytes", "kvq_calib_contribution",
             "kvq_calib_covariance", "kvq_calib_eigenbasis")
 
@@ -102,6 +102,9 @@ def load() -> ctypes.CDLL:
     lib.kvq_calib_covariance.restype = ctypes.c_int
     lib.kvq_calib_eigenbasis.argtypes = [ctypes.c_int32, ctypes.c_int32, V, V, V, V, ctypes.c_size_t, V]
     lib.kvq_calib_eigenbasis.restype = ctypes.c_int
+    lib.kvq_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int32,
+                                          ctypes.c_void_p]
+    lib.kvq_probe_stream_read.restype = ctypes.c_int
     lib.kvq_status_string.argtypes = [ctypes.c_int]
     lib.kvq_status_string.restype = ctypes.c_char_p
     _lib = lib

@@ -26,6 +26,7 @@ SOURCES = {
     # the decode takes no decision on NaNs: max / min need no quieting
     "kvq_decode.hip": ["-fno-honor-nans"],
     "kvq_api.hip": [],
+    "kvq_probe.hip": [],
     # calibration: scores formed identically in two kernels, symmetric products
     "kvq_calib.hip": ["-ffp-contract=off"],
 }

@@ -398,4 +398,11 @@ kvq_status kvq_decode_attention_noalloc(const kvq_config* cfg, const kvq_cache* 
                      stream);
 }
 
+kvq_status kvq_probe_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_t workgroups,
+                                 hipStream_t stream) {
+  if (!buf || !sink || workgroups <= 0 || bytes < 16 || (bytes & 15) || ((uintptr_t)buf & 15))
+    return KVQ_ERR_INVALID;
+  return kvq::launch_stream_read(buf, bytes, sink, workgroups, stream) == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;
+}
+
 }  // extern "C"

@@ -95,5 +95,6 @@ struct DecodeArgs {
 hipError_t launch_append(int d, bool bf16, int nb, const AppendArgs& a, hipStream_t s);
 hipError_t launch_rotate_query(int d, bool bf16, int batch, const RotateArgs& a, hipStream_t s);
 hipError_t launch_decode(int d, int batch, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int workgroups, hipStream_t s);
 
 }  // namespace kvq

@@ -265,6 +265,19 @@ kvq_status kvq_decode_attention_noalloc(const kvq_config* cfg, const kvq_cache* 
                                         const kvq_params* params, const float* q_rot, float scale,
                                         void* out, int32_t out_dtype, hipStream_t stream);
 
+/*
+ * kvq_probe_stream_read - measurement aid, not part of the method: one
+ * launch that reads `bytes` of device memory at `buf` once (16-byte loads,
+ * `workgroups` workgroups of 256 threads, grid-stride) and XORs one word per
+ * workgroup into sink[0 .. workgroups).  Timing it over buffers the size of
+ * a decode's algorithmic bytes gives the floor for one read-only kernel of
+ * that size on this GPU.  buf: device, 16-byte aligned, bytes a positive
+ * multiple of 16; sink: device, workgroups words.  Errors: KVQ_ERR_INVALID,
+ * KVQ_ERR_LAUNCH.
+ */
+kvq_status kvq_probe_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_t workgroups,
+                                 hipStream_t stream);
+
 /* Static description of a status code. */
 const char* kvq_status_string(kvq_status status);
 

@@ -158,3 +158,21 @@ def test_one_workspace_serves_successive_decodes_of_different_shapes():
             got = K.kvq_decode_attention(cfg, cache, params, q_rot, workspace=ws)
             torch.cuda.synchronize()
             np.testing.assert_array_equal(got.cpu().numpy().view(np.uint32), ref.cpu().numpy().view(np.uint32))
+
+
+def test_stream_read_probe_reads_every_word():
+    """The measurement probe reads every 16-byte chunk exactly once: the XOR
+    of its per-workgroup words equals the XOR of the whole buffer, for several
+    grid sizes and a length that is not a multiple of the grid."""
+    import decode_attention_kvq_amd as K
+    rng = np.random.default_rng(5)
+    n = 4 * (3 * 1024 * 1024 + 37)                  # int32 words, 16-byte multiple
+    host = rng.integers(-2**31, 2**31 - 1, size=n, dtype=np.int64).astype(np.int32)
+    buf = torch.from_numpy(host).cuda()
+    ref = int(np.bitwise_xor.reduce(host.view(np.uint32)))
+    for wgs in (1, 7, 256, 2048):
+        sink = torch.zeros(wgs, dtype=torch.int32, device="cuda")
+        K.kvq_probe_stream_read(buf, sink, wgs)
+        torch.cuda.synchronize()
+        got = int(np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)))
+        assert got == ref, wgs
