@@ -126,6 +126,10 @@ def main():
     ap.add_argument("--decode-only", action="store_true",
                     help="only replay the 80K decode graph (partition + merge over the layer replicas) "
                          "--steps times and print its timing (for profiler runs)")
+    ap.add_argument("--batched-only", action="store_true",
+                    help="only time the 32-session paged decode and print its JSON line")
+    ap.add_argument("--stream-loop-only", action="store_true",
+                    help="only time the 131K stream loop (append, decode, loop) and print its JSON line")
     ap.add_argument("--stream-read", action="store_true",
                     help="only time a plain streaming read of the 80K decode's byte count (one reduction "
                          "kernel per read, layer replicas) --steps times and print its timing")
@@ -157,6 +161,12 @@ def main():
         return
     if args.calibration_only:
         print(json.dumps({"value_calibration": time_calibration(L80K)}), flush=True)
+        return
+    if args.batched_only:
+        print(json.dumps({"batched_paged_decode": time_batched_paged(max(3, args.replicas // 6))}), flush=True)
+        return
+    if args.stream_loop_only:
+        print(json.dumps({"stream_loop": time_stream_loop(max(4, args.replicas // 5))}), flush=True)
         return
 
     import decode_attention_kvq_amd as K

@@ -1166,7 +1166,6 @@ __global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(D
   __shared__ float s_s[NW][kModalities][kMaxGroupHeads];
   __shared__ int s_mask;
   __shared__ int s_cmask[NW];
-  __shared__ int s_pt[kPageRun];
   __shared__ float4 s_qs[2 * HPL * 64];   // producer lanes' q (scaled), [2u + half][lane]
   __shared__ uint4 s_bq[KT * 64];         // bias operand of every lane, [kt][lane]
 
@@ -1186,17 +1185,24 @@ __global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(D
   const int steps = (ng + NW - 1) / NW;
   const int ps = a.page_shift;                     // page_tokens is a power of two here
   const int pmask = a.page_tokens - 1;
-  const int page0 = tb >> ps;
-  // The page run covers the partition's planned span [tb, tb + split_tokens)
-  // (at most kPageRun pages by the plan), or for the last partition, which
-  // takes every position past the plan, kPageRun pages; its load does not
-  // wait for the session length.
-  const int npl = split == a.splits - 1 ? kPageRun : min(((tb + a.split_tokens - 1) >> ps) - page0 + 1, kPageRun);
-  int pt_entry = -1;
-  if (tid < npl && page0 + tid < a.max_pages) pt_entry = a.page_table[static_cast<size_t>(b) * a.max_pages + page0 + tid];
+  // Page-table entries of the wavefront's own groups, one per lane: lane j
+  // holds the physical page of the group of step j (-1 past the table).  A
+  // step reads its entry with v_readlane, so finding a group's block needs
+  // no LDS access (an LDS or scalar-memory read would make the wavefront
+  // wait for every LDS operation it has in flight).  The load does not wait
+  // for the session length.
+  int v_page = -1;
+  {
+    const int pgl = (tb + (wave + NW * lane) * kGroupTokens) >> ps;
+    if (pgl < a.max_pages) v_page = a.page_table[static_cast<size_t>(b) * a.max_pages + pgl];
+  }
+  // The session's page-table row for steps from 64 on (a partition that grew
+  // past its plan): read with vector loads, which leave the LDS and
+  // scalar-memory counter alone.
+  const __amdgpu_buffer_rsrc_t rpt = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int32_t*>(a.page_table + static_cast<size_t>(b) * a.max_pages), 0, a.max_pages * 4, 0x00020000);
   const SwRsrc rs = sw_rsrc(a);
   const int hoff = h * (a.page_tokens / kGroupTokens);
-  static_assert(kPageRun <= NT, "one page-run entry per thread");
 
   // Query constants: the producer lanes' q on channels 8cb..8cb+7 of their
   // heads, and the bias operand (q's fp16 hi part in columns 0..7, lo part
@@ -1262,8 +1268,7 @@ __global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(D
   uint16_t* stage_b = &sm.s.stage[wave][1][0];
   SwSlot<D>* slot_a = &sm.s.slots[wave][0];
   SwSlot<D>* slot_b = &sm.s.slots[wave][1];
-  if (tid < kPageRun) s_pt[tid] = pt_entry;
-  __syncthreads();   // the byte table and the page run are complete
+  __syncthreads();   // the byte table is complete
   const uint2* tab = sm.s.tab;
 
   // Group j of the wavefront's run: block and modality offsets (block 0 for
@@ -1272,7 +1277,16 @@ __global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(D
     const int gi = wave + NW * j;
     const int t0 = tb + gi * kGroupTokens;
     const bool inside = j < steps && gi < ng;
-    const int phys = inside ? phys_page(a, s_pt, npl, b, page0, t0 >> ps) : -1;
+    int phys = -1;
+    if (inside) {
+      if (j < 64) {
+        phys = __builtin_amdgcn_readlane(v_page, j);
+      } else {
+        const int pg = t0 >> ps;
+        phys = pg < a.max_pages ? __builtin_amdgcn_readfirstlane(__builtin_amdgcn_raw_buffer_load_b32(rpt, 0, 4 * pg, 0))
+                                : -1;
+      }
+    }
     const bool ok = inside && phys >= 0 && phys < a.num_pages;
     const int tin = t0 & pmask;
     blk = ok ? phys * a.blocks_per_page + hoff + (tin >> 5) : 0;
@@ -1338,6 +1352,7 @@ __global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(D
     for (int i = 0; i < D / 64; ++i) sr[0][i] = lane < 32 ? h2 : l2;
   }
   okr[0] = load_codes(0, cr[0]);
+
   uint4 bqr[KT];   // the bias operand, the same for every group: kept in registers
 #pragma unroll
   for (int kt = 0; kt < KT; ++kt) bqr[kt] = s_bq[kt * 64 + lane];
