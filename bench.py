@@ -118,6 +118,9 @@ def main():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--replicas", type=int, default=20)
+    ap.add_argument("--context", type=int, default=L80K,
+                    help="cached positions before the first step (the workload's is 81,920; other values "
+                         "for partition-plan studies with --decode-only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="the 80K step and its decode only")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU budget of each oracle timing")
@@ -176,7 +179,7 @@ def main():
     R = args.replicas
     W, S = max(args.warmup, 0), max(args.steps, 1)
     extra_pos = (W + S) // R + 8
-    L0 = L80K
+    L0 = args.context
     w = generate(2, length=L0 + extra_pos)
     c = w.cfg
     d, hq, hkv = c.head_dim, c.n_q_heads, c.n_kv_heads

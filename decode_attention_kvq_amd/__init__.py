@@ -20,6 +20,7 @@ from ._lib import (KVQ_BF16, KVQ_F32, KVQ_KEYS_GROUP_MINMAX, KVQ_KEYS_PER_TOKEN,
 
 __all__ = ["Config", "Params", "Cache", "kvq_quantize_append", "kvq_rotate_query", "kvq_append_and_rotate",
            "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_decode_attention_noalloc",
+           "kvq_decode_step_workspace_bytes", "kvq_decode_step",
            "kvq_calib_workspace_bytes", "kvq_probe_stream_read",
            "kvq_calib_eigenbasis_workspace_bytes", "kvq_calib_contribution", "kvq_calib_covariance",
            "kvq_calib_eigenbasis", "KvqError"]
@@ -220,6 +221,50 @@ def kvq_decode_attention_noalloc(cfg: Config, cache: Cache, params: Params, q_ro
         ctypes.byref(cfg.struct), ctypes.byref(cache.struct), ctypes.byref(params.struct),
         _dev(q_rot, "q_rot", torch.float32), float(scale), _dev(out, "out"), _DTYPES[out.dtype], _stream(stream))
     _lib.check("kvq_decode_attention_noalloc", st)
+    return out
+
+
+def kvq_decode_step_workspace_bytes(cfg: Config, max_len: int) -> int:
+    return int(_lib.load().kvq_decode_step_workspace_bytes(ctypes.byref(cfg.struct), int(max_len)))
+
+
+def kvq_decode_step(cfg: Config, cache: Cache, params: Params, k_new: torch.Tensor, v_new: torch.Tensor,
+                    modality_new: torch.Tensor, q: torch.Tensor, q_rot: Optional[torch.Tensor] = None,
+                    scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None, stream=None,
+                    out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """One decode step of every session: append k_new / v_new / modality_new
+    ([batch, 1, Hkv, d] in cfg.kv_dtype; [batch, 1] uint8), rotate q ([batch,
+    Hq, d] fp32 or bf16) into q_rot, and attend every position including the
+    new one; returns out [batch, Hq, d] in out_dtype (an `out` tensor given
+    sets the dtype)."""
+    B = cfg.batch
+    if tuple(k_new.shape) != (B, 1, cfg.n_kv_heads, cfg.head_dim) or v_new.shape != k_new.shape:
+        raise ValueError("k_new / v_new must be [batch, 1, Hkv, d]")
+    if tuple(modality_new.shape) != (B, 1):
+        raise ValueError("modality_new must be [batch, 1]")
+    if tuple(q.shape) != (B, cfg.n_q_heads, cfg.head_dim):
+        raise ValueError("q must be [batch, Hq, d]")
+    if q.dtype not in _DTYPES:
+        raise TypeError("q must be float32 or bfloat16")
+    if q_rot is None:
+        q_rot = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(cfg.head_dim)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    if out.dtype not in _DTYPES or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must be [batch, Hq, d] float32 or bfloat16")
+    if workspace is None:
+        need = kvq_decode_step_workspace_bytes(cfg, max(cache.lengths()) + 1)
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
+    st = _lib.load().kvq_decode_step(
+        ctypes.byref(cfg.struct), ctypes.byref(cache.struct), ctypes.byref(params.struct),
+        _dev(k_new, "k_new", cfg.kv_dtype), _dev(v_new, "v_new", cfg.kv_dtype),
+        _dev(modality_new, "modality_new", torch.uint8), _dev(q, "q"), _DTYPES[q.dtype],
+        _dev(q_rot, "q_rot", torch.float32), float(scale), _dev(out, "out"), _DTYPES[out.dtype],
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream))
+    _lib.check("kvq_decode_step", st)
     return out
 
 

@@ -17,6 +17,7 @@ KVQ_KEYS_GROUP_MINMAX, KVQ_KEYS_PER_TOKEN = 0, 1
 
 EXPORTED = ("kvq_cache_buffer_bytes", "kvq_quantize_append", "kvq_rotate_query", "kvq_append_and_rotate",
             "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_decode_attention_noalloc",
+            "kvq_decode_step_workspace_bytes", "kvq_decode_step",
             "kvq_status_string", "kvq_probe_stream_read",
             "kvq_calib_workspace_bytes", "kvq_calib_eigenbasis_workspace_bytes", "kvq_calib_contribution",
             "kvq_calib_covariance", "kvq_calib_eigenbasis")
@@ -90,6 +91,13 @@ def load() -> ctypes.CDLL:
     lib.kvq_decode_attention_noalloc.argtypes = [P(KvqConfig), P(KvqCache), P(KvqParams), ctypes.c_void_p,
                                                  ctypes.c_float, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
     lib.kvq_decode_attention_noalloc.restype = ctypes.c_int
+    lib.kvq_decode_step_workspace_bytes.argtypes = [P(KvqConfig), ctypes.c_int32]
+    lib.kvq_decode_step_workspace_bytes.restype = ctypes.c_size_t
+    lib.kvq_decode_step.argtypes = [P(KvqConfig), P(KvqCache), P(KvqParams), ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                    ctypes.c_float, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                    ctypes.c_size_t, ctypes.c_void_p]
+    lib.kvq_decode_step.restype = ctypes.c_int
     V = ctypes.c_void_p
     lib.kvq_calib_workspace_bytes.argtypes = [P(KvqCalibShape)]
     lib.kvq_calib_workspace_bytes.restype = ctypes.c_size_t

@@ -67,12 +67,15 @@ int64_t max_split_tokens(const kvq_config* cfg) {
   return ((int64_t)(kvq::kPartitionPages - 2) * cfg->page_tokens / kUnit) * kUnit;
 }
 
-Plan plan_decode(const kvq_config* cfg, int32_t max_len) {
-  constexpr int64_t kCUs = 256;
+// `reserve` workgroups (at most 32) of the same launch run something else
+// (the fused step's append): the partitions then spread over the remaining
+// compute units, so that the launch still fits one round.
+Plan plan_decode(const kvq_config* cfg, int32_t max_len, int reserve = 0) {
+  const int64_t cus = 256 - ((reserve > 0 && reserve <= 32) ? reserve : 0);
   const int64_t len = std::max<int32_t>(max_len, 1);
   const int64_t total = len * cfg->batch * cfg->n_kv_heads;
-  int64_t per = (total + kCUs - 1) / kCUs;
-  if (per > 4096) per = (total + 4 * kCUs - 1) / (4 * kCUs);
+  int64_t per = (total + cus - 1) / cus;
+  if (per > 4096) per = (total + 4 * cus - 1) / (4 * cus);
   per = std::max(kUnit, ((per + kUnit - 1) / kUnit) * kUnit);
   int64_t splits = (len + per - 1) / per;
   while (splits > kMaxPlanSplits) {
@@ -92,8 +95,9 @@ bool plan_supported(const kvq_config* cfg, int32_t max_len) {
   return (int64_t)max_len <= kMaxPlanSplits * max_split_tokens(cfg);
 }
 
-// Upper bound of plan_decode(cfg, len).splits over every len <= max_len, so a
-// workspace sized for max_len serves every shorter context too.
+// Upper bound of plan_decode(cfg, len, reserve).splits over every len <=
+// max_len and reserve, so a workspace sized for max_len serves every shorter
+// context too.
 int splits_bound(const kvq_config* cfg, int32_t max_len) {
   const int64_t heads = (int64_t)cfg->batch * cfg->n_kv_heads;
   const int64_t len = std::max<int32_t>(max_len, 1);
@@ -107,6 +111,15 @@ int splits_bound(const kvq_config* cfg, int32_t max_len) {
 size_t workspace_floats(const kvq_config* cfg, const Plan& p) {
   const size_t heads = (size_t)cfg->batch * cfg->n_q_heads;
   return heads * p.splits * (kvq::kPartialHeader + 3 * cfg->head_dim);
+}
+
+// Fused decode step: the partials, then (from a 256-byte boundary) one
+// open-group staging record per (session, KV head).
+size_t step_stage_offset(const kvq_config* cfg, const Plan& p) {
+  return (workspace_floats(cfg, p) * sizeof(float) + 255) / 256 * 256;
+}
+size_t step_workspace_bytes(const kvq_config* cfg, const Plan& p) {
+  return step_stage_offset(cfg, p) + (size_t)cfg->batch * cfg->n_kv_heads * kvq::stage_record_bytes(cfg->head_dim);
 }
 
 }  // namespace
@@ -259,6 +272,11 @@ size_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t max_len) {
   return workspace_floats(cfg, Plan{splits_bound(cfg, max_len), 0}) * sizeof(float);
 }
 
+size_t kvq_decode_step_workspace_bytes(const kvq_config* cfg, int32_t max_len) {
+  if (check_config(cfg) != KVQ_OK || max_len < 0) return 0;
+  return step_workspace_bytes(cfg, Plan{splits_bound(cfg, max_len), 0});
+}
+
 }  // extern "C"
 
 // ------------------------------------------------ decode without allocation
@@ -288,38 +306,36 @@ static void* scratch_address() {
   return g_scratch_ptr[dev];
 }
 
-// The decode behind both entry points: the partial results go to the
-// caller's `workspace` (workspace_bytes long) or, with scratch = true, to the
-// current device's scratch array; every argument is checked before either is
-// touched.
-static kvq_status decode_impl(const kvq_config* cfg, const kvq_cache* cache, const kvq_params* params,
-                              const float* q_rot, float scale, void* out, int32_t out_dtype, void* workspace,
-                              size_t workspace_bytes, bool scratch, hipStream_t stream) {
+// Checks of a decode's own arguments (those of the cache, parameters and
+// configuration included) and its plan for the host-side lengths (+ extra
+// positions, the fused step's append), with the longest length.
+static kvq_status check_decode(const kvq_config* cfg, const kvq_cache* cache, const kvq_params* params,
+                               const void* q, float scale, const void* out, int32_t out_dtype, int32_t extra,
+                               int32_t& max_len) {
   kvq_status st = check_config(cfg);
   if (st != KVQ_OK) return st;
   if ((st = check_params(cfg, params)) != KVQ_OK) return st;
   if ((st = check_cache(cache)) != KVQ_OK) return st;
-  if (!q_rot || !out || !isfinite(scale)) return KVQ_ERR_INVALID;
+  if (!q || !out || !isfinite(scale)) return KVQ_ERR_INVALID;
   if (out_dtype != KVQ_F32 && out_dtype != KVQ_BF16) return KVQ_ERR_UNSUPPORTED;
-  int32_t max_len = 0;
+  max_len = 0;
   const int64_t cap = (int64_t)cfg->max_pages * cfg->page_tokens;
   for (int b = 0; b < cfg->batch; ++b) {
     if (cache->seq_len_host[b] < 0 || cache->seq_len_host[b] > cap) return KVQ_ERR_INVALID;
-    max_len = std::max(max_len, cache->seq_len_host[b]);
+    if ((int64_t)cache->seq_len_host[b] + extra > cap) return KVQ_ERR_CAPACITY;
+    max_len = std::max(max_len, cache->seq_len_host[b] + extra);
   }
   if (!plan_supported(cfg, max_len)) return KVQ_ERR_UNSUPPORTED;
-  const Plan plan = plan_decode(cfg, max_len);
-  const size_t need = workspace_floats(cfg, plan) * sizeof(float);
-  if (scratch) {
-    if (need > KVQ_NOALLOC_SCRATCH_BYTES) return KVQ_ERR_SCRATCH;
-    workspace = scratch_address();
-    if (!workspace) return KVQ_ERR_LAUNCH;
-  } else if (!workspace || workspace_bytes < need) {
-    return KVQ_ERR_WORKSPACE;
-  }
+  return KVQ_OK;
+}
+
+// Kernel arguments of a decode with the given plan and partials buffer.
+static kvq::DecodeArgs decode_args(const kvq_config* cfg, const kvq_cache* cache, const kvq_params* params,
+                                   const float* q_rot, float scale, void* out, int32_t out_dtype, const Plan& plan,
+                                   void* partials) {
   const int nlev = 1 << cfg->bits;
   const double c0 = params->codebook[0], c3 = params->codebook[nlev - 1];   // outer levels
-  kvq::DecodeArgs a;
+  kvq::DecodeArgs a{};
   a.k_codes = cache->k_codes;
   a.k_stats = cache->k_stats;
   a.v_codes = cache->v_codes;
@@ -331,7 +347,7 @@ static kvq_status decode_impl(const kvq_config* cfg, const kvq_cache* cache, con
   a.rot = params->rot;
   a.out = out;
   a.out_bf16 = out_dtype == KVQ_BF16;
-  a.partials = static_cast<float*>(workspace);
+  a.partials = static_cast<float*>(partials);
   a.batch = cfg->batch;
   a.hq = cfg->n_q_heads;
   a.hkv = cfg->n_kv_heads;
@@ -361,22 +377,48 @@ static kvq_status decode_impl(const kvq_config* cfg, const kvq_cache* cache, con
     const _Float16 v = (_Float16)l;
     lv[k] = __builtin_bit_cast(uint16_t, v);
     lr[k] = __builtin_bit_cast(uint16_t, (_Float16)((l - (double)v) * 4096.0));
+    if (k < 4) a.level_f32[k] = (float)l;
   }
   for (int w = 0; w < 8; ++w) {
     a.level_f16[w] = lv[2 * w] | ((uint32_t)lv[2 * w + 1] << 16);
     a.level_lo_f16[w] = lr[2 * w] | ((uint32_t)lr[2 * w + 1] << 16);
   }
-  for (int e = 0; e < 256; ++e) {
-    a.byte_levels[e].x = lv[e & 3] | ((uint32_t)lv[(e >> 2) & 3] << 16);
-    a.byte_levels[e].y = lv[(e >> 4) & 3] | ((uint32_t)lv[(e >> 6) & 3] << 16);
-  }
   a.cmid = (float)((c0 + c3) / 2.0);
   a.chalf = (float)((c3 - c0) / 2.0);
   a.key_mode = cfg->key_mode;
   a.bits = cfg->bits;
-  // per-token keys and 3- / 4-bit codes run on the streaming partition kernel only
-  if ((a.key_mode == KVQ_KEYS_PER_TOKEN || a.bits != 2) && (a.group > 8 || !a.offsets31 || a.page_shift < 0))
-    return KVQ_ERR_UNSUPPORTED;
+  return a;
+}
+
+// Per-token keys and 3- / 4-bit codes run on the streaming partition kernel
+// only.
+static bool decode_supported(const kvq::DecodeArgs& a) {
+  return !((a.key_mode == KVQ_KEYS_PER_TOKEN || a.bits != 2) && (a.group > 8 || !a.offsets31 || a.page_shift < 0));
+}
+
+// The decode behind both entry points: the partial results go to the
+// caller's `workspace` (workspace_bytes long) or, with scratch = true, to the
+// current device's scratch array; every argument is checked before either is
+// touched.
+static kvq_status decode_impl(const kvq_config* cfg, const kvq_cache* cache, const kvq_params* params,
+                              const float* q_rot, float scale, void* out, int32_t out_dtype, void* workspace,
+                              size_t workspace_bytes, bool scratch, hipStream_t stream) {
+  int32_t max_len = 0;
+  kvq_status st = check_decode(cfg, cache, params, q_rot, scale, out, out_dtype, 0, max_len);
+  if (st != KVQ_OK) return st;
+  const Plan plan = plan_decode(cfg, max_len);
+  const size_t need = workspace_floats(cfg, plan) * sizeof(float);
+  if (scratch) {
+    if (need > KVQ_NOALLOC_SCRATCH_BYTES) return KVQ_ERR_SCRATCH;
+  } else if (!workspace || workspace_bytes < need) {
+    return KVQ_ERR_WORKSPACE;
+  }
+  kvq::DecodeArgs a = decode_args(cfg, cache, params, q_rot, scale, out, out_dtype, plan, workspace);
+  if (!decode_supported(a)) return KVQ_ERR_UNSUPPORTED;
+  if (scratch) {
+    a.partials = static_cast<float*>(scratch_address());
+    if (!a.partials) return KVQ_ERR_LAUNCH;
+  }
   hipError_t e = kvq::launch_decode(cfg->head_dim, cfg->batch, a, stream);
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;
 }
@@ -396,6 +438,55 @@ kvq_status kvq_decode_attention_noalloc(const kvq_config* cfg, const kvq_cache* 
                                         void* out, int32_t out_dtype, hipStream_t stream) {
   return decode_impl(cfg, cache, params, q_rot, scale, out, out_dtype, nullptr, KVQ_NOALLOC_SCRATCH_BYTES, true,
                      stream);
+}
+
+kvq_status kvq_decode_step(const kvq_config* cfg, kvq_cache* cache, const kvq_params* params,
+                           const void* k_new, const void* v_new, const uint8_t* modality_new, const void* q,
+                           int32_t q_dtype, float* q_rot, float scale, void* out, int32_t out_dtype,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  // every check first: nothing is launched unless the whole step can run
+  kvq::AppendArgs ap;
+  kvq::RotateArgs r;
+  kvq_status st = prepare_append(cfg, cache, params, 0, cfg ? cfg->batch : 0, 1, k_new, v_new, modality_new, ap);
+  if (st != KVQ_OK) return st;
+  if ((st = prepare_rotate(cfg, params, cfg->batch, q, q_dtype, q_rot, r)) != KVQ_OK) return st;
+  int32_t max_len = 0;
+  if ((st = check_decode(cfg, cache, params, q_rot, scale, out, out_dtype, 1, max_len)) != KVQ_OK) return st;
+  const int group = cfg->n_q_heads / cfg->n_kv_heads;
+  const bool pow2 = (cfg->page_tokens & (cfg->page_tokens - 1)) == 0;
+  const bool offsets31 = (size_t)cfg->num_pages * cfg->n_kv_heads * cfg->page_tokens * cfg->head_dim * cfg->bits / 8 <
+                         ((size_t)1 << 31);
+  const bool fused = cfg->bits == 2 && cfg->key_mode == KVQ_KEYS_GROUP_MINMAX &&
+                     params->codebook[0] == -params->codebook[3] && group <= 8 && pow2 && offsets31 &&
+                     q_dtype == cfg->kv_dtype;
+  const int reserve = fused ? 2 * cfg->n_kv_heads * cfg->batch : 0;
+  const Plan plan = plan_decode(cfg, max_len, reserve);
+  const size_t need = fused ? step_workspace_bytes(cfg, plan) : workspace_floats(cfg, plan) * sizeof(float);
+  if (!workspace || workspace_bytes < need) return KVQ_ERR_WORKSPACE;
+  kvq::DecodeArgs a = decode_args(cfg, cache, params, q_rot, scale, out, out_dtype, plan, workspace);
+  if (!decode_supported(a)) return KVQ_ERR_UNSUPPORTED;
+  hipError_t e;
+  if (!fused) {
+    // the same work as kvq_append_and_rotate followed by kvq_decode_attention
+    ap.rq = r;
+    ap.rot_heads = cfg->batch * cfg->n_q_heads;
+    ap.rot_bf16 = q_dtype == KVQ_BF16;
+    e = kvq::launch_append(cfg->head_dim, cfg->kv_dtype == KVQ_BF16, cfg->batch, ap, stream);
+    if (e == hipSuccess) e = kvq::launch_decode(cfg->head_dim, cfg->batch, a, stream);
+  } else {
+    uint8_t* stage = static_cast<uint8_t*>(workspace) + step_stage_offset(cfg, plan);
+    ap.rq = r;
+    ap.rot_heads = 0;
+    ap.append_x = 2;
+    ap.defer_len = 1;
+    ap.stage = stage;
+    a.stage = stage;
+    a.step_len = cache->seq_len;
+    e = kvq::launch_decode_step(cfg->head_dim, cfg->kv_dtype == KVQ_BF16, cfg->batch, a, ap, stream);
+  }
+  if (e != hipSuccess) return KVQ_ERR_LAUNCH;
+  for (int b = 0; b < cfg->batch; ++b) cache->seq_len_host[b] += 1;
+  return KVQ_OK;
 }
 
 kvq_status kvq_probe_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_t workgroups,

@@ -33,8 +33,10 @@
 // (bitwise reproducible).
 #include <type_traits>
 
+#include "kvq_append.h"
 #include "kvq_common.h"
 #include "kvq_internal.h"
+#include "kvq_rotate.h"
 
 namespace kvq {
 
@@ -1140,8 +1142,15 @@ __device__ __forceinline__ void sw_back1(const ConsumerLoad<D, BITS>& ca, const 
   }
 }
 
-template <int D, int SLOTS, bool ASYM, bool TQ, int BITS>
-__global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(DecodeArgs a) {
+// STEP: the fused decode step's launch.  Grid columns from a.splits on run
+// the append (ap, one position per session: the key workgroup, then the
+// value workgroup of each (session, KV head); kvq_append.h) in this kernel's
+// shared memory; the partitions rotate their own query heads (ap.rq, inputs
+// in bf16 when BF16) and attend the closed groups only, positions below
+// 32 floor(L / 32) of the session's length L before the append.  Neither
+// side reads what the other writes; the merge attends the open group.
+template <int D, int SLOTS, bool ASYM, bool TQ, int BITS, bool STEP = false, bool BF16 = false>
+__global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(DecodeArgs a, AppendArgs ap) {
   constexpr int KT = D / 32;
   constexpr int CT = D / 16;
   constexpr int GP = Slots<SLOTS>::GP;
@@ -1159,6 +1168,7 @@ __global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(D
       uint16_t stage[NW][2][2 * D];         // LO / HI rows of the pair being prepared
     } s;
     float4 red[NW][NPOS];                   // the wavefronts' rescaled accumulators
+    app::AppendSmem<D> app;                 // STEP: the append's workgroups
   };
   __shared__ Smem sm;
   __shared__ float s_m[NW][kMaxGroupHeads];
@@ -1168,13 +1178,22 @@ __global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(D
   __shared__ int s_cmask[NW];
   __shared__ float4 s_qs[2 * HPL * 64];   // producer lanes' q (scaled), [2u + half][lane]
   __shared__ uint4 s_bq[KT * 64];         // bias operand of every lane, [kt][lane]
+  __shared__ float s_qrot[STEP ? 8 : 1][D];   // STEP: the rotated query heads of the group
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kg = lane >> 4, col = lane & 15;
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  if constexpr (STEP) {
+    if (split >= a.splits) {
+      static_assert(NT == app::kAppendThreads, "the append's workgroup size");
+      app::append_group<D, BF16, 2>(ap, sm.app, s_mask, split - a.splits, h, b, 0);
+      return;
+    }
+  }
   const int G = a.group;
-  const int L = session_length(a, b);
+  // STEP: the closed groups only (the append rewrites the open one)
+  const int L = STEP ? (session_length(a, b) & ~(kGroupTokens - 1)) : session_length(a, b);
   const int tb = split * a.split_tokens;
   const int te = (split == a.splits - 1) ? L : min(tb + a.split_tokens, L);
   const int ng = te > tb ? (te - tb + kGroupTokens - 1) / kGroupTokens : 0;   // groups of the partition
@@ -1204,6 +1223,32 @@ __global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(D
   const SwRsrc rs = sw_rsrc(a);
   const int hoff = h * (a.page_tokens / kGroupTokens);
 
+  // STEP: the group's query heads rotated here (16 lanes per head, heads
+  // 4 w .. 4 w + 3 on wavefront w < 2), into LDS for the query constants
+  // below; the partition of split 0 also stores them for the merge.
+  if constexpr (STEP) {
+    if (wave < 2) {
+      constexpr int RCH = D / rotq::kLanes;
+      const int hl = 4 * wave + lane / rotq::kLanes, sub = lane % rotq::kLanes;
+      const int bi = b * a.hq + h * G + min(hl, G - 1);
+      float o[RCH];
+      rotq::rotate_values<D, BF16>(ap.rq, bi, sub, o);
+#pragma unroll
+      for (int i = 0; i < RCH; ++i) s_qrot[hl][sub * RCH + i] = o[i];
+      if (split == 0 && hl < G) {
+        float4* dst = reinterpret_cast<float4*>(ap.rq.q_rot + static_cast<size_t>(bi) * D + sub * RCH);
+#pragma unroll
+        for (int k = 0; k < RCH / 4; ++k) dst[k] = float4{o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]};
+      }
+    }
+    __syncthreads();
+  }
+  // Row of query head qh (of this KV head) in the rotated frame.
+  auto q_row = [&](int qh) -> const float* {
+    if constexpr (STEP) return &s_qrot[qh - h * G][0];
+    else return a.q_rot + (static_cast<size_t>(b) * a.hq + qh) * D;
+  };
+
   // Query constants: the producer lanes' q on channels 8cb..8cb+7 of their
   // heads, and the bias operand (q's fp16 hi part in columns 0..7, lo part
   // in columns 8..15, channels 32kt + 8kg + i).  Both carry scale * log2(e) / 2.
@@ -1213,7 +1258,7 @@ __global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(D
 #pragma unroll
     for (int u = 0; u < HPL; ++u) {
       const int qh = h * G + min(hs * HPL + u, G - 1);
-      const float4* qp = reinterpret_cast<const float4*>(a.q_rot + (static_cast<size_t>(b) * a.hq + qh) * D + 8 * cb);
+      const float4* qp = reinterpret_cast<const float4*>(q_row(qh) + 8 * cb);
       const float4 q0 = qp[0], q1 = qp[1];
       s_qs[(2 * u) * 64 + lane] = float4{q0.x * qsc, q0.y * qsc, q0.z * qsc, q0.w * qsc};
       s_qs[(2 * u + 1) * 64 + lane] = float4{q1.x * qsc, q1.y * qsc, q1.z * qsc, q1.w * qsc};
@@ -1221,7 +1266,7 @@ __global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(D
   }
   if (wave == 1) {
     const int qh = h * G + min(col & 7, G - 1);
-    const float4* qp = reinterpret_cast<const float4*>(a.q_rot + (static_cast<size_t>(b) * a.hq + qh) * D);
+    const float4* qp = reinterpret_cast<const float4*>(q_row(qh));
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
       const float4 q0 = qp[(32 * kt + 8 * kg) / 4], q1 = qp[(32 * kt + 8 * kg) / 4 + 1];
@@ -1499,7 +1544,15 @@ struct MergeShape {
   static constexpr int RR = D / RB;                 // rows per block
 };
 
-template <int D, bool ASYM>
+// STEP (the fused decode step's merge): the open group of each session,
+// positions [32 floor(L / 32), L + 1) after the append of position L, staged
+// by the step's append workgroups (kStage*), is attended here as one more
+// partial, and one workgroup per session advances its length to L + 1.
+// Its partial follows the partitions' form: reference max M_o = the largest
+// score, weights 2^(s - M_o), value sums over the normalized levels per
+// modality; a position whose modality is not a known one counts in the
+// denominator only.
+template <int D, bool ASYM, bool STEP = false>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs a) {
   constexpr int PS = kPartialHeader + kModalities * D;
   constexpr int F4 = D / 4;                        // float4 per accumulator block
@@ -1517,6 +1570,16 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
   __shared__ float s_A[kModalities][D];
   __shared__ float s_red[NW][2 + kModalities];
   __shared__ float s_M;
+  static_assert(!(STEP && ASYM), "the fused step takes a symmetric codebook");
+  constexpr int OQ = D / 16;                       // open group: channels per score thread (16 per position)
+  constexpr int OP = kMergeThreads / D;            // value threads per channel
+  constexpr int OT = kGroupTokens / OP;            // positions per value thread
+  __shared__ float s_osc[STEP ? kGroupTokens : 1];     // scores (base 2), -inf past the group's end
+  __shared__ float s_onrm[STEP ? kGroupTokens : 1];
+  __shared__ int s_omod[STEP ? kGroupTokens : 1];
+  __shared__ float s_oA[STEP ? kModalities : 1][STEP ? D : 1];
+  __shared__ float s_oM, s_ol;
+  __shared__ int s_omask;
 
   // Workgroup -> (session b, KV head h, query head of the group gq, row
   // block rb): every workgroup of one (session, KV head) key sits on the XCD
@@ -1573,6 +1636,59 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
   if constexpr (ASYM) {
     if (tid < S) hd1 = reinterpret_cast<const float4*>(P + static_cast<size_t>(tid) * PS)[1];
   }
+  // STEP: the open group's loads (beside the partials'), then its scores:
+  // thread (t, part) takes channels part OQ .. of position t, the 16 parts
+  // of a position sit in one row of 16 lanes.  k_hat = mid + half * level,
+  // mid / half = (HI +- LO) / 2.
+  const uint8_t* rec = nullptr;
+  uint32_t ovc[OT / 4];
+  if constexpr (STEP) {
+    rec = a.stage + static_cast<size_t>(key) * stage_record_bytes(D);
+    const int2 meta = *reinterpret_cast<const int2*>(rec + kStageMeta);
+    const int t = tid / 16, part = tid % 16, c0 = part * OQ;
+    float qv[OQ];
+    {
+      const float4* qp = reinterpret_cast<const float4*>(a.q_rot + head * D + c0);
+#pragma unroll
+      for (int k = 0; k < OQ / 4; ++k) {
+        const float4 v = qp[k];
+        qv[4 * k] = v.x; qv[4 * k + 1] = v.y; qv[4 * k + 2] = v.z; qv[4 * k + 3] = v.w;
+      }
+    }
+    const uint16_t* lo_row = reinterpret_cast<const uint16_t*>(rec + kStageCodes + 16 * D);
+    uint16_t lo16[OQ], hi16[OQ];
+#pragma unroll
+    for (int i = 0; i < OQ; ++i) {
+      lo16[i] = lo_row[c0 + i];
+      hi16[i] = lo_row[D + c0 + i];
+    }
+    uint32_t kb[OQ / 4];
+#pragma unroll
+    for (int k = 0; k < OQ / 4; ++k) kb[k] = rec[kStageCodes + key_code_byte<D>(t, c0 + 4 * k)];
+    const uint16_t nrm = reinterpret_cast<const uint16_t*>(rec + kStageNorms)[t];
+    const int md = rec[kStageMods + t];
+    // value threads: channel tid / OP, positions (tid % OP) OT ..; a code
+    // byte holds four consecutive positions of one channel
+    {
+      const int vc = tid / OP, vt0 = (tid % OP) * OT;
+#pragma unroll
+      for (int k = 0; k < OT / 4; ++k) ovc[k] = rec[kStageCodes + 8 * D + value_code_byte<D>(vt0 + 4 * k, vc)];
+    }
+    float dot = 0.f;
+#pragma unroll
+    for (int i = 0; i < OQ; ++i) {
+      const float lo = f16_bits_to_f32(lo16[i]), hi = f16_bits_to_f32(hi16[i]);
+      const float lvl = a.level_f32[(kb[i >> 2] >> (2 * (i & 3))) & 3u];
+      dot += qv[i] * ((hi + lo) * 0.5f + (hi - lo) * 0.5f * lvl);
+    }
+    dot = row16_sum(dot);
+    if (part == 0) {
+      s_osc[t] = (meta.x != 0 && t < meta.y) ? dot * a.scale_log2e : -__builtin_inff();
+      s_onrm[t] = f16_bits_to_f32(nrm);
+      s_omod[t] = md;
+    }
+  }
+
   float mx = hd0.x;
   for (int s = tid + kMergeThreads; s < S; s += kMergeThreads) mx = fmaxf(mx, P[static_cast<size_t>(s) * PS]);
   mx = wave_max(mx);
@@ -1581,10 +1697,61 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
   if (tid == 0) {
     float M = s_red[0][0];
     for (int w = 1; w < NW; ++w) M = fmaxf(M, s_red[w][0]);
+    if constexpr (STEP) {
+      // the open group's reference max, denominator and modality mask
+      float mo = -__builtin_inff();
+      for (int t = 0; t < kGroupTokens; ++t) mo = fmaxf(mo, s_osc[t]);
+      float lo = 0.f;
+      int mk = 0;
+      if (mo != -__builtin_inff()) {
+        for (int t = 0; t < kGroupTokens; ++t) {
+          if (s_osc[t] == -__builtin_inff()) continue;
+          lo += exp2f(s_osc[t] - mo);
+          if (s_omod[t] < kModalities) mk |= 1 << s_omod[t];
+        }
+      }
+      s_oM = mo;
+      s_ol = lo;
+      s_omask = mk;
+      M = fmaxf(M, mo);
+    }
     s_M = M;
   }
   __syncthreads();
   const float M = s_M;
+  float e_o = 0.f;
+  int omask = 0;
+  if constexpr (STEP) {
+    // the open group's value sums per modality: thread (channel, part)
+    // takes OT positions, the OP parts of a channel sit in adjacent lanes
+    const float mo = s_oM;
+    omask = s_omask;
+    e_o = mo == -__builtin_inff() ? 0.f : exp2f(mo - M);
+    const int vc = tid / OP, vt0 = (tid % OP) * OT;
+    float av[kModalities] = {0.f, 0.f, 0.f};
+    if (mo != -__builtin_inff()) {
+#pragma unroll
+      for (int k = 0; k < OT; ++k) {
+        const int t = vt0 + k;
+        const float sc = s_osc[t];
+        const float w = sc == -__builtin_inff() ? 0.f : exp2f(sc - mo) * s_onrm[t];
+        const float lvl = a.level_f32[(ovc[k >> 2] >> (2 * (t & 3))) & 3u];
+        const int md = s_omod[t];
+#pragma unroll
+        for (int m = 0; m < kModalities; ++m) av[m] += md == m ? w * lvl : 0.f;
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < kModalities; ++m) {
+      av[m] += dpp_f<0xB1>(av[m]);      // quad_perm [1,0,3,2]
+      av[m] += dpp_f<0x4E>(av[m]);      // quad_perm [2,3,0,1]
+      if constexpr (OP == 8) av[m] += dpp_f<0x141>(av[m]);   // row_half_mirror
+    }
+    if (tid % OP == 0) {
+#pragma unroll
+      for (int m = 0; m < kModalities; ++m) s_oA[m][vc] = av[m];
+    }
+  }
   float ls = 0.f, ss[kModalities] = {0.f, 0.f, 0.f};
   for (int s = tid; s < S; s += kMergeThreads) {
     const float4 h0 = s == tid ? hd0 : reinterpret_cast<const float4*>(P + static_cast<size_t>(s) * PS)[0];
@@ -1599,6 +1766,9 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
       ss[1] += (pm & 2) ? e * h1.y : 0.f;
       ss[2] += (pm & 4) ? e * h1.z : 0.f;
     }
+  }
+  if constexpr (STEP) {
+    if (tid == 0) ls += e_o * s_ol;
   }
   ls = wave_sum(ls);
   if constexpr (ASYM)
@@ -1641,6 +1811,14 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
         acc.y += pk[k] ? ek[k] * blk[k].y : 0.f;
         acc.z += pk[k] ? ek[k] * blk[k].z : 0.f;
         acc.w += pk[k] ? ek[k] * blk[k].w : 0.f;
+      }
+    }
+    if constexpr (STEP) {
+      if (g == 0 && ((omask >> cm) & 1)) {
+        acc.x += e_o * s_oA[cm][4 * cf + 0];
+        acc.y += e_o * s_oA[cm][4 * cf + 1];
+        acc.z += e_o * s_oA[cm][4 * cf + 2];
+        acc.w += e_o * s_oA[cm][4 * cf + 3];
       }
     }
     s_part[g][col] = acc;
@@ -1688,6 +1866,11 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
   static_assert(QT == 16, "one output row per 16-lane row");
   acc = row16_sum(acc);
   if constexpr (ASYM) rs = row16_sum(rs);
+  if constexpr (STEP) {
+    // one workgroup per session advances its length (nothing else in this
+    // launch reads it)
+    if (tid == 0 && item == 0 && h == 0) a.step_len[key / a.hkv] += 1;
+  }
   if (q == 0) {
     const float o = (l > 0.f) ? (a.chalf * acc + a.cmid * rs) * (a.value_scale / l) : 0.f;
     if (a.out_bf16)
@@ -1713,14 +1896,18 @@ void launch_partition_sw_bits(int batch, const DecodeArgs& a, hipStream_t s) {
   const dim3 block(kSwWaves * 64);
   if (a.key_mode == KVQ_KEYS_PER_TOKEN) {
     if (a.cmid != 0.f)
-      hipLaunchKernelGGL((decode_partition_sw_kernel<D, SLOTS, true, true, BITS>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((decode_partition_sw_kernel<D, SLOTS, true, true, BITS>), grid, block, 0, s, a,
+                         AppendArgs{});
     else
-      hipLaunchKernelGGL((decode_partition_sw_kernel<D, SLOTS, false, true, BITS>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((decode_partition_sw_kernel<D, SLOTS, false, true, BITS>), grid, block, 0, s, a,
+                         AppendArgs{});
   } else {
     if (a.cmid != 0.f)
-      hipLaunchKernelGGL((decode_partition_sw_kernel<D, SLOTS, true, false, BITS>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((decode_partition_sw_kernel<D, SLOTS, true, false, BITS>), grid, block, 0, s, a,
+                         AppendArgs{});
     else
-      hipLaunchKernelGGL((decode_partition_sw_kernel<D, SLOTS, false, false, BITS>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((decode_partition_sw_kernel<D, SLOTS, false, false, BITS>), grid, block, 0, s, a,
+                         AppendArgs{});
   }
 }
 
@@ -1731,20 +1918,48 @@ void launch_partition_sw(int batch, const DecodeArgs& a, hipStream_t s) {
   else launch_partition_sw_bits<D, SLOTS, 2>(batch, a, s);
 }
 
+// Merge grid: per (session, KV head) key, group * RB workgroups, all on the
+// XCD key mod 8 (see decode_merge_kernel).
+template <int D, bool ASYM, bool STEP>
+void launch_merge(int batch, const DecodeArgs& a, hipStream_t s) {
+  const int keys = a.hkv * batch;
+  const int per_key = a.group * MergeShape<D>::RB;
+  const int rows = ((keys + kXcds - 1) / kXcds) * per_key;
+  hipLaunchKernelGGL((decode_merge_kernel<D, ASYM, STEP>), dim3(kXcds * rows), dim3(kMergeThreads), 0, s, a);
+}
+
 template <int D>
 hipError_t launch_decode_t(int batch, const DecodeArgs& a, hipStream_t s) {
   if (!a.offsets31 || a.page_shift < 0) launch_partition<D, 1, kDecodeWaves / 2>(batch, a, s);
   else if (a.group <= 5) launch_partition_sw<D, 3>(batch, a, s);
   else if (a.group <= 8) launch_partition_sw<D, 2>(batch, a, s);
   else launch_partition<D, 1, kDecodeWaves / 2>(batch, a, s);
-  const int keys = a.hkv * batch;
-  const int per_key = a.group * MergeShape<D>::RB;
-  const int rows = ((keys + kXcds - 1) / kXcds) * per_key;
-  const dim3 mgrid(kXcds * rows);
-  if (a.cmid != 0.f)
-    hipLaunchKernelGGL((decode_merge_kernel<D, true>), mgrid, dim3(kMergeThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((decode_merge_kernel<D, false>), mgrid, dim3(kMergeThreads), 0, s, a);
+  if (a.cmid != 0.f) launch_merge<D, true, false>(batch, a, s);
+  else launch_merge<D, false, false>(batch, a, s);
+  return hipGetLastError();
+}
+
+// Fused decode step: partitions + the append's two workgroups per (session,
+// KV head) in one grid (2-bit codes, group statistics, symmetric codebook,
+// G <= 8, power-of-two pages, 31-bit offsets: the caller checks), then the
+// merge with the open group.
+template <int D, int SLOTS, bool BF16>
+void launch_step_partition(int batch, const DecodeArgs& a, const AppendArgs& ap, hipStream_t s) {
+  const dim3 grid(a.splits + 2, a.hkv, batch);
+  hipLaunchKernelGGL((decode_partition_sw_kernel<D, SLOTS, false, false, 2, true, BF16>), grid,
+                     dim3(kSwWaves * 64), 0, s, a, ap);
+}
+
+template <int D>
+hipError_t launch_decode_step_t(bool bf16, int batch, const DecodeArgs& a, const AppendArgs& ap, hipStream_t s) {
+  if (a.group <= 5) {
+    if (bf16) launch_step_partition<D, 3, true>(batch, a, ap, s);
+    else launch_step_partition<D, 3, false>(batch, a, ap, s);
+  } else {
+    if (bf16) launch_step_partition<D, 2, true>(batch, a, ap, s);
+    else launch_step_partition<D, 2, false>(batch, a, ap, s);
+  }
+  launch_merge<D, false, true>(batch, a, s);
   return hipGetLastError();
 }
 
@@ -1752,6 +1967,11 @@ hipError_t launch_decode_t(int batch, const DecodeArgs& a, hipStream_t s) {
 
 hipError_t launch_decode(int d, int batch, const DecodeArgs& a, hipStream_t s) {
   return d == 64 ? launch_decode_t<64>(batch, a, s) : launch_decode_t<128>(batch, a, s);
+}
+
+hipError_t launch_decode_step(int d, bool bf16, int batch, const DecodeArgs& a, const AppendArgs& ap,
+                              hipStream_t s) {
+  return d == 64 ? launch_decode_step_t<64>(bf16, batch, a, ap, s) : launch_decode_step_t<128>(bf16, batch, a, ap, s);
 }
 
 }  // namespace kvq

@@ -49,7 +49,20 @@ struct AppendArgs {
   // sets append_x, the grid columns of the append's own workgroups.
   RotateArgs rq;
   int32_t rot_heads, rot_bf16, append_x;
+  // Fused decode step: the append leaves the session lengths to the step's
+  // merge (defer_len) and copies the open group to the staging records.
+  int32_t defer_len;
+  uint8_t* stage;
 };
+
+// Open-group staging record of the fused decode step, one per (session, KV
+// head) in the step's workspace after the partials: written by the step's
+// append workgroups, read by its merge.  Byte offsets:
+constexpr int kStageMeta = 0;      // int32 [0]: 1 if the group's page is mapped, [1]: positions in the group
+constexpr int kStageNorms = 64;    // 32 fp16 value norms
+constexpr int kStageMods = 128;    // 32 modality bytes
+constexpr int kStageCodes = 256;   // key block (8d bytes), value block (8d bytes), LO and HI rows (2d fp16 each)
+__host__ __device__ constexpr int stage_record_bytes(int d) { return kStageCodes + 20 * d; }
 
 // Decode partitions: a workgroup of kDecodeWaves wavefronts streams one
 // contiguous range of 32-position groups of one (session, KV head) and writes
@@ -89,12 +102,21 @@ struct DecodeArgs {
   int32_t out_bf16;       // write the output as bf16 (round to nearest even) instead of fp32
   uint32_t level_f16[8];  // normalized levels (2 c_k - c0 - c_{n-1}) / (c_{n-1} - c0) as fp16 bits, k < n
   uint32_t level_lo_f16[8]; // 2^12 (level - fp16 level) as fp16 bits (3 / 4 bits: the scores' lo part)
-  uint2 byte_levels[256]; // byte e of four 2-bit codes -> its four fp16 levels (code of bits 2i..2i+1 first)
+  // Fused decode step (null / unused otherwise): the open-group records, the
+  // lengths the merge advances, and the 2-bit normalized levels in fp32.
+  const uint8_t* stage;
+  int32_t* step_len;
+  float level_f32[4];
 };
 
 hipError_t launch_append(int d, bool bf16, int nb, const AppendArgs& a, hipStream_t s);
 hipError_t launch_rotate_query(int d, bool bf16, int batch, const RotateArgs& a, hipStream_t s);
 hipError_t launch_decode(int d, int batch, const DecodeArgs& a, hipStream_t s);
+// Fused decode step: the partitions over the closed groups and the append
+// workgroups (ap: one position per session, every session) in one launch,
+// then the merge with the open group.  bf16: query and cache inputs in bf16.
+hipError_t launch_decode_step(int d, bool bf16, int batch, const DecodeArgs& a, const AppendArgs& ap,
+                              hipStream_t s);
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int workgroups, hipStream_t s);
 
 }  // namespace kvq

@@ -6,9 +6,10 @@
 // d / 16 channels per lane; the transform runs in fp64 (exact for bf16 /
 // fp32 inputs) inside the lane and then across the head's 16 lanes (DPP quad
 // permutes and swizzles, no LDS memory), and is rounded once to fp32 after
-// the 1 / sqrt(d) scaling.  Files that include this compile with
-// -ffp-contract=off; the lane butterflies' fma has a +-1 factor, so it
-// rounds exactly like the addition it stands for.
+// the 1 / sqrt(d) scaling.  Every function here turns floating-point
+// contraction off for its own body (the including file's setting does not
+// matter); the lane butterflies' fma has a +-1 factor, so it rounds exactly
+// like the addition it stands for.
 #pragma once
 
 #include "kvq_common.h"
@@ -26,25 +27,29 @@ __device__ __forceinline__ int xor_lane(int v) {
   return __builtin_amdgcn_ds_swizzle(v, (M << 10) | 0x1F);                                  // bit mode: xor M
 }
 
-// x + x[lane ^ M] where the lane bit is clear, x[lane ^ M] - x where it is set.
 template <int M>
-__device__ __forceinline__ double butterfly(double x, double sgn) {
-  const long long u = __double_as_longlong(x);
+__device__ __forceinline__ double xor_lane(double v) {
+  const long long u = __double_as_longlong(v);
   const int lo = xor_lane<M>(static_cast<int>(u & 0xFFFFFFFF));
   const int hi = xor_lane<M>(static_cast<int>(u >> 32));
-  const double p = __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned int>(lo));
-  return __builtin_fma(sgn, x, p);
+  return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned int>(lo));
 }
 
-// Rotates head bi_raw (= b * Hq + i) with the 16 lanes whose lane-in-head
-// index is `sub`.  All 16 lanes of a head must call it together; a head
-// index past n_heads works on the last head and stores nothing.
+// x + x[lane ^ M] where the lane bit is clear, x[lane ^ M] - x where it is set
+// (sgn = +1 / -1; the product is exact, so the fma rounds once, like the sum).
+template <int M>
+__device__ __forceinline__ double butterfly(double x, double sgn) {
+  return __builtin_fma(sgn, x, xor_lane<M>(x));
+}
+
+// Channels sub * CH .. sub * CH + CH - 1 of the rotated head bi (= b * Hq +
+// i), computed by the 16 lanes whose lane-in-head index is `sub`; all 16
+// lanes of a head must call it together.
 template <int D, bool BF16>
-__device__ __forceinline__ void rotate_head(const RotateArgs& a, int n_heads, int bi_raw, int sub) {
+__device__ __forceinline__ void rotate_values(const RotateArgs& a, int bi, int sub, float (&o)[D / kLanes]) {
+#pragma clang fp contract(off)
   constexpr int CH = D / kLanes;                   // channels per lane: 8 (d = 128) or 4 (d = 64)
   constexpr int ESZ = BF16 ? 2 : 4;
-  const bool live = bi_raw < n_heads;
-  const int bi = live ? bi_raw : n_heads - 1;
   const int h = (bi % a.hq) / a.group;
   const int c0 = sub * CH;
 
@@ -98,11 +103,23 @@ __device__ __forceinline__ void rotate_head(const RotateArgs& a, int n_heads, in
 #pragma unroll
   for (int i = 0; i < CH; ++i) x[i] = butterfly<8>(x[i], (sub & 8) ? -1.0 : 1.0);
 
-  if (live) {
-    float o[CH];
 #pragma unroll
-    for (int i = 0; i < CH; ++i) o[i] = static_cast<float>(x[i] * a.inv_sqrt_d);
-    float4* dst = reinterpret_cast<float4*>(a.q_rot + static_cast<size_t>(bi) * D + c0);
+  for (int i = 0; i < CH; ++i) o[i] = static_cast<float>(x[i] * a.inv_sqrt_d);
+}
+
+// Rotates head bi_raw (= b * Hq + i) into q_rot with the 16 lanes whose
+// lane-in-head index is `sub`.  All 16 lanes of a head must call it
+// together; a head index past n_heads works on the last head and stores
+// nothing.
+template <int D, bool BF16>
+__device__ __forceinline__ void rotate_head(const RotateArgs& a, int n_heads, int bi_raw, int sub) {
+  constexpr int CH = D / kLanes;
+  const bool live = bi_raw < n_heads;
+  const int bi = live ? bi_raw : n_heads - 1;
+  float o[CH];
+  rotate_values<D, BF16>(a, bi, sub, o);
+  if (live) {
+    float4* dst = reinterpret_cast<float4*>(a.q_rot + static_cast<size_t>(bi) * D + sub * CH);
 #pragma unroll
     for (int k = 0; k < CH / 4; ++k) dst[k] = float4{o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]};
   }

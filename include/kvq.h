@@ -242,6 +242,50 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache,
                                 void* out, int32_t out_dtype, void* workspace, size_t workspace_bytes,
                                 hipStream_t stream);
 
+/* Workspace bytes kvq_decode_step needs when the longest session holds
+ * max_len positions after the step (split-K partial results and one
+ * open-group record per session and KV head). */
+size_t kvq_decode_step_workspace_bytes(const kvq_config* cfg, int32_t max_len);
+
+/*
+ * kvq_decode_step - one whole decode step of every session (Sec. 2 Method,
+ * key and value bullets; Sec. 1, Implementation bullet): append one position
+ * to each session of the batch, rotate the queries, and attend every
+ * position including the new one.  The result is that of
+ *   kvq_append_and_rotate(cfg, cache, params, 0, cfg->batch, 1, k_new, v_new,
+ *                         modality_new, cfg->batch, q, q_dtype, q_rot, stream)
+ *   kvq_decode_attention(cfg, cache, params, q_rot, scale, out, out_dtype,
+ *                        workspace, workspace_bytes, stream)
+ * with the same cache bytes, lengths and q_rot, bit for bit, and out equal up
+ * to fp32 rounding (the open group is summed in another order).
+ * With 2-bit codes, group-statistics keys, a symmetric codebook (c0 = -c3),
+ * G <= 8, a power-of-two page_tokens, cache arrays below 2^31 bytes and
+ * q_dtype == kv_dtype, the step runs in two launches instead of three: the
+ * first runs the decode partitions over each session's closed groups
+ * (positions below 32 floor(L / 32), L = the length before the step; the
+ * partitions rotate their own query heads) side by side with the append's
+ * workgroups, which also copy the open group to the workspace; the second
+ * merges the partitions, attends the open group [32 floor(L / 32), L + 1)
+ * and advances the lengths.  Other configurations launch the two calls
+ * above.
+ * k_new, v_new: device [batch][1][Hkv][d] in cfg->kv_dtype; modality_new:
+ * device [batch][1] uint8; q: device [batch][Hq][d] in q_dtype; q_rot:
+ * device [batch][Hq][d] fp32 (written); out: device [batch][Hq][d] in
+ * out_dtype.  workspace: device, at least
+ * kvq_decode_step_workspace_bytes(cfg, max(seq_len_host) + 1), owned by the
+ * caller; steps that share a workspace or a cache must not overlap in time.
+ * Plan and replay: as for kvq_decode_attention, from max(seq_len_host) + 1;
+ * a captured step replayed later appends at, and attends up to, the device
+ * lengths of the replay.
+ * Errors: those of the two calls (KVQ_ERR_CAPACITY when a session is full),
+ * all checked before anything is launched.
+ */
+kvq_status kvq_decode_step(const kvq_config* cfg, kvq_cache* cache, const kvq_params* params,
+                           const void* k_new, const void* v_new, const uint8_t* modality_new,
+                           const void* q, int32_t q_dtype, float* q_rot, float scale,
+                           void* out, int32_t out_dtype, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
 /*
  * kvq_decode_attention_noalloc - kvq_decode_attention for callers that cannot
  * allocate device memory: code under HIP graph capture, tight serving loops,

@@ -188,6 +188,43 @@ def test_append_and_rotate_rejects_bad_arguments_before_launch():
     assert list(lens) == [10, 20]
 
 
+def test_decode_step_rejects_bad_arguments_before_launch():
+    """The fused decode step checks the append, the rotation and the decode on
+    the host; a failure launches nothing and leaves the length mirror as it
+    was.  Its workspace covers the partials and the open-group records, and
+    a workspace sized for a length serves every shorter one."""
+    L, lib = _lib()
+    cfg = _cfg(L)                                   # G = 8, 256-position pages, bf16: the two-launch path
+    p = _fake_params(L)
+    c, lens = _fake_cache(L, [10, 700])
+    V = ctypes.c_void_p
+    need = lib.kvq_decode_step_workspace_bytes(ctypes.byref(cfg), 701)
+    # partials of at least one partition per (session, query head), then
+    # 2 x 2 records of 256 + 20 d bytes
+    assert need >= 2 * 16 * (8 + 3 * 128) * 4 + 4 * (256 + 20 * 128)
+    assert all(lib.kvq_decode_step_workspace_bytes(ctypes.byref(cfg), n) <= need for n in (0, 1, 33, 256, 700))
+
+    def call(k=V(8), v=V(8), m=V(8), q=V(8), qd=L.KVQ_BF16, qr=V(8), scale=0.1, out=V(8), od=L.KVQ_F32,
+             ws=V(8), nbytes=need, params=p):
+        return lib.kvq_decode_step(ctypes.byref(cfg), ctypes.byref(c), ctypes.byref(params) if params else None,
+                                   k, v, m, q, qd, qr, ctypes.c_float(scale), out, od, ws, nbytes, None)
+    assert call(ws=None) == L.KVQ_ERR_WORKSPACE
+    assert call(nbytes=need - 1) == L.KVQ_ERR_WORKSPACE
+    assert call(k=None) == L.KVQ_ERR_INVALID
+    assert call(m=None) == L.KVQ_ERR_INVALID
+    assert call(q=None) == L.KVQ_ERR_INVALID
+    assert call(qr=None) == L.KVQ_ERR_INVALID
+    assert call(out=None) == L.KVQ_ERR_INVALID
+    assert call(scale=float("inf")) == L.KVQ_ERR_INVALID
+    assert call(qd=7) == L.KVQ_ERR_UNSUPPORTED
+    assert call(od=7) == L.KVQ_ERR_UNSUPPORTED
+    assert call(params=None) == L.KVQ_ERR_INVALID
+    lens[1] = 4 * 256                               # a full session: no room for the step's position
+    assert call() == L.KVQ_ERR_CAPACITY
+    lens[1] = 700
+    assert list(lens) == [10, 700]
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     import decode_attention_kvq_amd as K
