@@ -3,7 +3,8 @@
 One step = one decode step of one attention layer on the seeded synthetic
 omni stream (81,920 cached positions, 28 query / 4 KV heads, d = 128, bf16
 input): quantize-append the step's new key/value, rotate the query, and run
-the fused decode over the packed cache.  Steps cycle over R layer replicas
+the fused decode over the packed cache, in one kvq_decode_step call (two
+launches; the same step as two calls is reported beside it).  Steps cycle over R layer replicas
 (R x 27.8 MB > the 256 MB Infinity Cache) so that the cache is read from HBM.
 Exactly --warmup untimed steps, then exactly --steps timed steps.
 
@@ -198,9 +199,18 @@ def main():
     ws = torch.zeros(K.kvq_decode_workspace_bytes(cfg, L0 + extra_pos), dtype=torch.uint8, device=dev)
     scale = 1.0 / math.sqrt(d)
 
+    ws_step = torch.zeros(K.kvq_decode_step_workspace_bytes(cfg, L0 + extra_pos), dtype=torch.uint8, device=dev)
+
     def one_step(r):
-        # append the step's key / value and rotate its query (one launch:
-        # kvq_append_and_rotate = kvq_quantize_append + kvq_rotate_query), then decode
+        # one decode step, kvq_decode_step: append the step's key / value,
+        # rotate its query and attend every position (two launches: the
+        # partitions over the closed groups beside the append, then the merge
+        # with the open group)
+        K.kvq_decode_step(cfg, caches[r], params, k_steps[:, :1], v_steps[:, :1], m_steps[:, :1], q, q_rot,
+                          scale, out, ws_step)
+
+    def one_step_two_calls(r):
+        # the same step as kvq_append_and_rotate (one launch), then kvq_decode_attention
         cache = caches[r]
         K.kvq_append_and_rotate(cfg, cache, params, k_steps[:, :1], v_steps[:, :1], m_steps[:, :1], q, q_rot)
         K.kvq_decode_attention(cfg, cache, params, q_rot, scale, out, ws)
@@ -208,6 +218,7 @@ def main():
     # Eager pass over every replica (loads every kernel), then rewind the lengths.
     for r in range(R):
         one_step(r)
+        one_step_two_calls(r)
     torch.cuda.synchronize()
     for cc in caches:
         cc.set_lengths([L0])
@@ -289,7 +300,28 @@ def main():
     dec_bytes = algorithmic_decode_bytes([Ld], d, hq, hkv)
     achieved = dec_bytes / (dec_ms * 1e-3) / 1e9
 
+    # The same steps as two calls (append + rotate, then decode: three launches).
+    g_two = _capture([lambda r=r: one_step_two_calls(r) for r in range(R)], s_cap)
+    for cc, n in zip(caches, len_after):
+        cc.set_lengths([int(n)])
+    torch.cuda.synchronize()
+    g_two.replay()
+    n_two = max(5, S // R)
+    t0e, t1e = _events()
+    t0e.record(stream)
+    for _ in range(n_two):
+        g_two.replay()
+    t1e.record(stream)
+    torch.cuda.synchronize()
+    two_us = t0e.elapsed_time(t1e) * 1e3 / (n_two * R)
+    for cc, n in zip(caches, len_after):
+        cc.set_lengths([int(n)])
+    torch.cuda.synchronize()
+    del g_two
+
     extra = {"decode_us_hbm": dec_ms * 1e3, "decode_kv_tokens_per_s": Ld / (dec_ms * 1e-3),
+             "step_us": ms_step * 1e3, "step_minus_decode_us": ms_step * 1e3 - dec_ms * 1e3,
+             "step_two_calls_us": two_us,
              "step_wall_us": wall / S * 1e6, "warmup_steps_run": W, "timed_steps_run": S}
     if not args.no_extra:
         extra.update(extra_80k(K, cfg, params, caches, table, q_rot, out, ws, scale, n_dec, dec_bytes, s_cap, R,
@@ -323,7 +355,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32 accumulate over 2-bit codes (bf16 input)",
         "data": "synthetic seeded omni stream (video/audio/text chunks), random bases",
-        "config": {"workload": "decode step at 81,920-position context: append 1 token + rotate q + fused decode",
+        "config": {"workload": "decode step at 81,920-position context (kvq_decode_step: append 1 token + rotate q "
+                               "+ fused decode, two launches)",
                    "context": round(ctx_mean, 1), "head_dim": d, "q_heads": hq, "kv_heads": hkv,
                    "batch": 1, "layer_replicas": R, "page_tokens": pt},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",

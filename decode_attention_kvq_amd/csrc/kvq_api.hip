@@ -113,10 +113,11 @@ size_t workspace_floats(const kvq_config* cfg, const Plan& p) {
   return heads * p.splits * (kvq::kPartialHeader + 3 * cfg->head_dim);
 }
 
-// Fused decode step: the partials, then (from a 256-byte boundary) one
-// open-group staging record per (session, KV head).
+// Fused decode step: the partials (one more per head: the open group's),
+// then (from a 256-byte boundary) one open-group staging record per
+// (session, KV head).
 size_t step_stage_offset(const kvq_config* cfg, const Plan& p) {
-  return (workspace_floats(cfg, p) * sizeof(float) + 255) / 256 * 256;
+  return (workspace_floats(cfg, Plan{p.splits + 1, p.split_tokens}) * sizeof(float) + 255) / 256 * 256;
 }
 size_t step_workspace_bytes(const kvq_config* cfg, const Plan& p) {
   return step_stage_offset(cfg, p) + (size_t)cfg->batch * cfg->n_kv_heads * kvq::stage_record_bytes(cfg->head_dim);
@@ -356,6 +357,7 @@ static kvq::DecodeArgs decode_args(const kvq_config* cfg, const kvq_cache* cache
   a.max_pages = cfg->max_pages;
   a.num_pages = cfg->num_pages;
   a.splits = plan.splits;
+  a.pstride = plan.splits;
   a.split_tokens = plan.split_tokens;
   a.page_shift = -1;
   if ((cfg->page_tokens & (cfg->page_tokens - 1)) == 0) {
@@ -459,7 +461,7 @@ kvq_status kvq_decode_step(const kvq_config* cfg, kvq_cache* cache, const kvq_pa
   const bool fused = cfg->bits == 2 && cfg->key_mode == KVQ_KEYS_GROUP_MINMAX &&
                      params->codebook[0] == -params->codebook[3] && group <= 8 && pow2 && offsets31 &&
                      q_dtype == cfg->kv_dtype;
-  const int reserve = fused ? 2 * cfg->n_kv_heads * cfg->batch : 0;
+  const int reserve = fused ? cfg->n_kv_heads * cfg->batch : 0;
   const Plan plan = plan_decode(cfg, max_len, reserve);
   const size_t need = fused ? step_workspace_bytes(cfg, plan) : workspace_floats(cfg, plan) * sizeof(float);
   if (!workspace || workspace_bytes < need) return KVQ_ERR_WORKSPACE;
@@ -482,6 +484,7 @@ kvq_status kvq_decode_step(const kvq_config* cfg, kvq_cache* cache, const kvq_pa
     ap.stage = stage;
     a.stage = stage;
     a.step_len = cache->seq_len;
+    a.pstride = plan.splits + 1;
     e = kvq::launch_decode_step(cfg->head_dim, cfg->kv_dtype == KVQ_BF16, cfg->batch, a, ap, stream);
   }
   if (e != hipSuccess) return KVQ_ERR_LAUNCH;

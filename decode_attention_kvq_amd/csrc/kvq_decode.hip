@@ -683,13 +683,13 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_partition_kernel(DecodeArgs
         s.z += v.z;
         s.w += v.w;
       }
-      float* part = a.partials + ((static_cast<size_t>(b) * a.hq + h * G + hp2) * a.splits + split) * PS;
+      float* part = a.partials + ((static_cast<size_t>(b) * a.hq + h * G + hp2) * a.pstride + split) * PS;
       *reinterpret_cast<float4*>(part + kPartialHeader + m * D + 16 * ct + 4 * kg2) = s;
     }
   }
   if (tid < G * kPartialHeader) {
     const int hh = tid / kPartialHeader, f = tid % kPartialHeader;
-    float* part = a.partials + ((static_cast<size_t>(b) * a.hq + h * G + hh) * a.splits + split) * PS;
+    float* part = a.partials + ((static_cast<size_t>(b) * a.hq + h * G + hh) * a.pstride + split) * PS;
     float Mh = -__builtin_inff();
     for (int w = 0; w < NW; ++w) Mh = fmaxf(Mh, s_m[w][hh]);
     float v = 0.f;
@@ -1142,13 +1142,126 @@ __device__ __forceinline__ void sw_back1(const ConsumerLoad<D, BITS>& ca, const 
   }
 }
 
-// STEP: the fused decode step's launch.  Grid columns from a.splits on run
-// the append (ap, one position per session: the key workgroup, then the
-// value workgroup of each (session, KV head); kvq_append.h) in this kernel's
-// shared memory; the partitions rotate their own query heads (ap.rq, inputs
-// in bf16 when BF16) and attend the closed groups only, positions below
-// 32 floor(L / 32) of the session's length L before the append.  Neither
-// side reads what the other writes; the merge attends the open group.
+// Shared memory of the fused step's append workgroup.
+template <int D>
+struct StepSmem {
+  app::AppendSmem<D> app;
+  float q[8][D];                        // the KV head's query heads, rotated
+  float sc[8][kGroupTokens];            // open group: scores (base 2), -inf where nothing is attended
+  float w[8][kGroupTokens];             // weights 2^(s - M) N
+  float nrm[kGroupTokens];
+  int mod[kGroupTokens];
+  int last;                             // the append's ticket flag (unused: the merge advances the lengths)
+};
+
+// The fused step's work for (session b, KV head h) beside the partitions:
+// the append of the step's position (the key role, then the value role of
+// kvq_append.h, which also copy the open group to its staging record), then
+// the open group's partial for every query head i of the KV head, as partial
+// a.splits of the head in the partitions' form: scores
+// s_t = scale log2(e) <q_rot_i, k_hat_t> with k_hat = (HI + LO) / 2 +
+// level (HI - LO) / 2, reference max M = max_t s_t, denominator
+// sum_t 2^(s_t - M), per modality m the sums of the weights 2^(s_t - M) N_t
+// times the normalized value levels (a position whose modality is not a
+// known one counts in the denominator only).  Runs in fp32.  All 512
+// threads call it.
+template <int D, bool BF16>
+__device__ __forceinline__ void step_append_open_group(const DecodeArgs& a, const AppendArgs& ap, StepSmem<D>& sm,
+                                                       int h, int b) {
+  constexpr int NT = kSwWaves * 64;
+  constexpr int OQ = D / 16;                      // scores: channels per thread, 16 threads per position
+  constexpr int VG = NT / D;                      // values: threads per channel (query heads dealt round robin)
+  constexpr int PS = kPartialHeader + kModalities * D;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = a.group;
+  if (wave < 2) {
+    // the KV head's query heads (16 lanes per head, head 4 w .. 4 w + 3 on wavefront w)
+    constexpr int RCH = D / rotq::kLanes;
+    const int hl = 4 * wave + lane / rotq::kLanes, sub = lane % rotq::kLanes;
+    float o[RCH];
+    rotq::rotate_values<D, BF16>(ap.rq, b * a.hq + h * G + min(hl, G - 1), sub, o);
+#pragma unroll
+    for (int i = 0; i < RCH; ++i) sm.q[hl][sub * RCH + i] = o[i];
+  }
+  app::append_group<D, BF16, 2>(ap, sm.app, sm.last, 0, h, b, 0);
+  __syncthreads();
+  app::append_group<D, BF16, 2>(ap, sm.app, sm.last, 1, h, b, 0);
+  __syncthreads();   // the staging record is complete (written by this workgroup)
+
+  const uint8_t* rec = a.stage + static_cast<size_t>(b * a.hkv + h) * stage_record_bytes(D);
+  {
+    // scores: thread (t, part) takes channels part OQ .. of position t
+    const int t = tid / 16, part = tid % 16, c0 = part * OQ;
+    const int2 meta = *reinterpret_cast<const int2*>(rec + kStageMeta);
+    const uint16_t* lohi = reinterpret_cast<const uint16_t*>(rec + kStageCodes + 16 * D);
+    float kh[OQ];
+#pragma unroll
+    for (int i = 0; i < OQ; ++i) {
+      const float lo = f16_bits_to_f32(lohi[c0 + i]), hi = f16_bits_to_f32(lohi[D + c0 + i]);
+      const uint32_t byte = rec[kStageCodes + key_code_byte<D>(t, c0 + (i & ~3))];
+      const float lvl = a.level_f32[(byte >> (2 * (i & 3))) & 3u];
+      kh[i] = (hi + lo) * 0.5f + (hi - lo) * 0.5f * lvl;
+    }
+    const bool live = meta.x != 0 && t < meta.y;
+    for (int i = 0; i < G; ++i) {
+      float dot = 0.f;
+#pragma unroll
+      for (int c = 0; c < OQ; ++c) dot += sm.q[i][c0 + c] * kh[c];
+      dot = row16_sum(dot);
+      if (part == 0) sm.sc[i][t] = live ? dot * a.scale_log2e : -__builtin_inff();
+    }
+    if (part == 0) {
+      sm.nrm[t] = f16_bits_to_f32(reinterpret_cast<const uint16_t*>(rec + kStageNorms)[t]);
+      sm.mod[t] = rec[kStageMods + t];
+    }
+  }
+  __syncthreads();
+  if (wave < G) {
+    // softmax of query head `wave`: lane t < 32 takes position t
+    const int t = lane & (kGroupTokens - 1);
+    const float sc = lane < kGroupTokens ? sm.sc[wave][t] : -__builtin_inff();
+    const float mo = wave_max(sc);
+    const float e = (mo == -__builtin_inff() || sc == -__builtin_inff()) ? 0.f : exp2f(sc - mo);
+    const float lsum = wave_sum(e);
+    const int md = sm.mod[t];
+    int mk = 0;
+#pragma unroll
+    for (int m = 0; m < kModalities; ++m)
+      if (__any(e > 0.f && md == m)) mk |= 1 << m;
+    if (lane < kGroupTokens) sm.w[wave][t] = e * sm.nrm[t];
+    float* part = a.partials + ((static_cast<size_t>(b) * a.hq + h * G + wave) * a.pstride + a.splits) * PS;
+    if (lane < kPartialHeader)
+      part[lane] = lane == 0 ? mo : lane == 1 ? lsum : lane == 2 ? __int_as_float(mk) : 0.f;
+  }
+  __syncthreads();
+  {
+    // value sums: channel c, query heads i = tid / D, + VG, ...
+    const int c = tid % D;
+    uint32_t vb[kGroupTokens / 4];
+#pragma unroll
+    for (int k = 0; k < kGroupTokens / 4; ++k) vb[k] = rec[kStageCodes + 8 * D + value_code_byte<D>(4 * k, c)];
+    for (int i = tid / D; i < G; i += VG) {
+      float av[kModalities] = {0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < kGroupTokens; ++t) {
+        const float x = sm.w[i][t] * a.level_f32[(vb[t >> 2] >> (2 * (t & 3))) & 3u];
+        const int md = sm.mod[t];
+#pragma unroll
+        for (int m = 0; m < kModalities; ++m) av[m] += md == m ? x : 0.f;
+      }
+      float* part = a.partials + ((static_cast<size_t>(b) * a.hq + h * G + i) * a.pstride + a.splits) * PS;
+#pragma unroll
+      for (int m = 0; m < kModalities; ++m) part[kPartialHeader + m * D + c] = av[m];
+    }
+  }
+}
+
+// STEP: the fused decode step's launch.  Grid column a.splits runs the
+// step's append and the open group's partial for each (session, KV head)
+// (step_append_open_group) in this kernel's shared memory; the partitions
+// rotate their own query heads (ap.rq, inputs in bf16 when BF16) and attend
+// the closed groups only, positions below 32 floor(L / 32) of the session's
+// length L before the append.  Neither side reads what the other writes.
 template <int D, int SLOTS, bool ASYM, bool TQ, int BITS, bool STEP = false, bool BF16 = false>
 __global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(DecodeArgs a, AppendArgs ap) {
   constexpr int KT = D / 32;
@@ -1168,7 +1281,7 @@ __global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(D
       uint16_t stage[NW][2][2 * D];         // LO / HI rows of the pair being prepared
     } s;
     float4 red[NW][NPOS];                   // the wavefronts' rescaled accumulators
-    app::AppendSmem<D> app;                 // STEP: the append's workgroups
+    StepSmem<D> step;                       // STEP: the append's workgroups
   };
   __shared__ Smem sm;
   __shared__ float s_m[NW][kMaxGroupHeads];
@@ -1178,7 +1291,6 @@ __global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(D
   __shared__ int s_cmask[NW];
   __shared__ float4 s_qs[2 * HPL * 64];   // producer lanes' q (scaled), [2u + half][lane]
   __shared__ uint4 s_bq[KT * 64];         // bias operand of every lane, [kt][lane]
-  __shared__ float s_qrot[STEP ? 8 : 1][D];   // STEP: the rotated query heads of the group
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1187,7 +1299,7 @@ __global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(D
   if constexpr (STEP) {
     if (split >= a.splits) {
       static_assert(NT == app::kAppendThreads, "the append's workgroup size");
-      app::append_group<D, BF16, 2>(ap, sm.app, s_mask, split - a.splits, h, b, 0);
+      step_append_open_group<D, BF16>(a, ap, sm.step, h, b);
       return;
     }
   }
@@ -1223,62 +1335,73 @@ __global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(D
   const SwRsrc rs = sw_rsrc(a);
   const int hoff = h * (a.page_tokens / kGroupTokens);
 
-  // STEP: the group's query heads rotated here (16 lanes per head, heads
-  // 4 w .. 4 w + 3 on wavefront w < 2), into LDS for the query constants
-  // below; the partition of split 0 also stores them for the merge.
+  // Query constants: the producer lanes' q on channels 8cb..8cb+7 of their
+  // heads, and the bias operand (q's fp16 hi part in columns 0..7, lo part
+  // in columns 8..15, channels 32kt + 8kg + i).  Both carry scale * log2(e) / 2.
+  const float qsc = a.scale_log2e * 0.5f;
   if constexpr (STEP) {
+    // The group's query heads rotated here, 16 lanes per head (head hl =
+    // 4 w .. 4 w + 3 on wavefront w < 2, channels RCH sub ..), and written
+    // straight into both layouts (the split-0 partition also stores q_rot).
     if (wave < 2) {
       constexpr int RCH = D / rotq::kLanes;
       const int hl = 4 * wave + lane / rotq::kLanes, sub = lane % rotq::kLanes;
       const int bi = b * a.hq + h * G + min(hl, G - 1);
       float o[RCH];
       rotq::rotate_values<D, BF16>(ap.rq, bi, sub, o);
-#pragma unroll
-      for (int i = 0; i < RCH; ++i) s_qrot[hl][sub * RCH + i] = o[i];
       if (split == 0 && hl < G) {
         float4* dst = reinterpret_cast<float4*>(ap.rq.q_rot + static_cast<size_t>(bi) * D + sub * RCH);
 #pragma unroll
         for (int k = 0; k < RCH / 4; ++k) dst[k] = float4{o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]};
       }
-    }
-    __syncthreads();
-  }
-  // Row of query head qh (of this KV head) in the rotated frame.
-  auto q_row = [&](int qh) -> const float* {
-    if constexpr (STEP) return &s_qrot[qh - h * G][0];
-    else return a.q_rot + (static_cast<size_t>(b) * a.hq + qh) * D;
-  };
-
-  // Query constants: the producer lanes' q on channels 8cb..8cb+7 of their
-  // heads, and the bias operand (q's fp16 hi part in columns 0..7, lo part
-  // in columns 8..15, channels 32kt + 8kg + i).  Both carry scale * log2(e) / 2.
-  const float qsc = a.scale_log2e * 0.5f;
-  if (wave == 0) {
-    const int cb = lane % CB, hs = lane / CB;
+      const int hs = hl / HPL, u = hl % HPL;
 #pragma unroll
-    for (int u = 0; u < HPL; ++u) {
-      const int qh = h * G + min(hs * HPL + u, G - 1);
-      const float4* qp = reinterpret_cast<const float4*>(q_row(qh) + 8 * cb);
-      const float4 q0 = qp[0], q1 = qp[1];
-      s_qs[(2 * u) * 64 + lane] = float4{q0.x * qsc, q0.y * qsc, q0.z * qsc, q0.w * qsc};
-      s_qs[(2 * u + 1) * 64 + lane] = float4{q1.x * qsc, q1.y * qsc, q1.z * qsc, q1.w * qsc};
-    }
-  }
-  if (wave == 1) {
-    const int qh = h * G + min(col & 7, G - 1);
-    const float4* qp = reinterpret_cast<const float4*>(q_row(qh));
+      for (int k = 0; k < RCH / 4; ++k) {
+        const int c4 = sub * RCH + 4 * k;            // channels c4 .. c4 + 3
+        float v[4];
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-      const float4 q0 = qp[(32 * kt + 8 * kg) / 4], q1 = qp[(32 * kt + 8 * kg) / 4 + 1];
-      const float qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-      half8 bq;
+        for (int i = 0; i < 4; ++i) v[i] = o[4 * k + i] * qsc;
+        s_qs[(2 * u + ((c4 >> 2) & 1)) * 64 + hs * CB + (c4 >> 3)] = float4{v[0], v[1], v[2], v[3]};
+        _Float16 hi[4], lo[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float v = qv[i] * qsc;
-        const _Float16 hi = static_cast<_Float16>(v);
-        bq[i] = col < 8 ? hi : static_cast<_Float16>(v - static_cast<float>(hi));
+        for (int i = 0; i < 4; ++i) {
+          hi[i] = static_cast<_Float16>(v[i]);
+          lo[i] = static_cast<_Float16>(v[i] - static_cast<float>(hi[i]));
+        }
+        uint2* bq2 = reinterpret_cast<uint2*>(s_bq);
+        const int l0 = (c4 >> 5) * 64 + ((c4 & 31) >> 3) * 16 + hl;   // [kt][kg * 16 + column]
+        bq2[2 * l0 + ((c4 & 7) >> 2)] = __builtin_bit_cast(uint2, hi);
+        bq2[2 * (l0 + 8) + ((c4 & 7) >> 2)] = __builtin_bit_cast(uint2, lo);
       }
-      s_bq[kt * 64 + lane] = __builtin_bit_cast(uint4, bq);
+    }
+  } else {
+    if (wave == 0) {
+      const int cb = lane % CB, hs = lane / CB;
+#pragma unroll
+      for (int u = 0; u < HPL; ++u) {
+        const int qh = h * G + min(hs * HPL + u, G - 1);
+        const float4* qp = reinterpret_cast<const float4*>(a.q_rot + (static_cast<size_t>(b) * a.hq + qh) * D + 8 * cb);
+        const float4 q0 = qp[0], q1 = qp[1];
+        s_qs[(2 * u) * 64 + lane] = float4{q0.x * qsc, q0.y * qsc, q0.z * qsc, q0.w * qsc};
+        s_qs[(2 * u + 1) * 64 + lane] = float4{q1.x * qsc, q1.y * qsc, q1.z * qsc, q1.w * qsc};
+      }
+    }
+    if (wave == 1) {
+      const int qh = h * G + min(col & 7, G - 1);
+      const float4* qp = reinterpret_cast<const float4*>(a.q_rot + (static_cast<size_t>(b) * a.hq + qh) * D);
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        const float4 q0 = qp[(32 * kt + 8 * kg) / 4], q1 = qp[(32 * kt + 8 * kg) / 4 + 1];
+        const float qv[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+        half8 bq;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float v = qv[i] * qsc;
+          const _Float16 hi = static_cast<_Float16>(v);
+          bq[i] = col < 8 ? hi : static_cast<_Float16>(v - static_cast<float>(hi));
+        }
+        s_bq[kt * 64 + lane] = __builtin_bit_cast(uint4, bq);
+      }
     }
   }
 
@@ -1500,13 +1623,13 @@ __global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(D
         sum.z += t ? v[w].z : 0.f;
         sum.w += t ? v[w].w : 0.f;
       }
-      float* part = a.partials + ((static_cast<size_t>(b) * a.hq + h * G + hp2) * a.splits + split) * PS;
+      float* part = a.partials + ((static_cast<size_t>(b) * a.hq + h * G + hp2) * a.pstride + split) * PS;
       *reinterpret_cast<float4*>(part + kPartialHeader + m * D + 16 * ct + 4 * kg2) = sum;
     }
   }
   if (tid < G * kPartialHeader) {
     const int hh = tid / kPartialHeader, f = tid % kPartialHeader;
-    float* part = a.partials + ((static_cast<size_t>(b) * a.hq + h * G + hh) * a.splits + split) * PS;
+    float* part = a.partials + ((static_cast<size_t>(b) * a.hq + h * G + hh) * a.pstride + split) * PS;
     float Mh = -__builtin_inff();
     for (int w = 0; w < NW; ++w) Mh = fmaxf(Mh, s_m[w][hh]);
     float v = 0.f;
@@ -1544,14 +1667,9 @@ struct MergeShape {
   static constexpr int RR = D / RB;                 // rows per block
 };
 
-// STEP (the fused decode step's merge): the open group of each session,
-// positions [32 floor(L / 32), L + 1) after the append of position L, staged
-// by the step's append workgroups (kStage*), is attended here as one more
-// partial, and one workgroup per session advances its length to L + 1.
-// Its partial follows the partitions' form: reference max M_o = the largest
-// score, weights 2^(s - M_o), value sums over the normalized levels per
-// modality; a position whose modality is not a known one counts in the
-// denominator only.
+// STEP (the fused decode step's merge): the partials include the open
+// group's (the last one of each head), and one workgroup per session
+// advances its length.
 template <int D, bool ASYM, bool STEP = false>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs a) {
   constexpr int PS = kPartialHeader + kModalities * D;
@@ -1571,15 +1689,6 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
   __shared__ float s_red[NW][2 + kModalities];
   __shared__ float s_M;
   static_assert(!(STEP && ASYM), "the fused step takes a symmetric codebook");
-  constexpr int OQ = D / 16;                       // open group: channels per score thread (16 per position)
-  constexpr int OP = kMergeThreads / D;            // value threads per channel
-  constexpr int OT = kGroupTokens / OP;            // positions per value thread
-  __shared__ float s_osc[STEP ? kGroupTokens : 1];     // scores (base 2), -inf past the group's end
-  __shared__ float s_onrm[STEP ? kGroupTokens : 1];
-  __shared__ int s_omod[STEP ? kGroupTokens : 1];
-  __shared__ float s_oA[STEP ? kModalities : 1][STEP ? D : 1];
-  __shared__ float s_oM, s_ol;
-  __shared__ int s_omask;
 
   // Workgroup -> (session b, KV head h, query head of the group gq, row
   // block rb): every workgroup of one (session, KV head) key sits on the XCD
@@ -1597,7 +1706,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
   const int i = h * a.group + gq;
   const int hi = (key / a.hkv) * a.hq + i;         // b * Hq + i
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int S = a.splits;
+  const int S = a.pstride;
   const size_t head = static_cast<size_t>(hi);
   const float* P = a.partials + head * static_cast<size_t>(S) * PS;
 
@@ -1636,59 +1745,6 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
   if constexpr (ASYM) {
     if (tid < S) hd1 = reinterpret_cast<const float4*>(P + static_cast<size_t>(tid) * PS)[1];
   }
-  // STEP: the open group's loads (beside the partials'), then its scores:
-  // thread (t, part) takes channels part OQ .. of position t, the 16 parts
-  // of a position sit in one row of 16 lanes.  k_hat = mid + half * level,
-  // mid / half = (HI +- LO) / 2.
-  const uint8_t* rec = nullptr;
-  uint32_t ovc[OT / 4];
-  if constexpr (STEP) {
-    rec = a.stage + static_cast<size_t>(key) * stage_record_bytes(D);
-    const int2 meta = *reinterpret_cast<const int2*>(rec + kStageMeta);
-    const int t = tid / 16, part = tid % 16, c0 = part * OQ;
-    float qv[OQ];
-    {
-      const float4* qp = reinterpret_cast<const float4*>(a.q_rot + head * D + c0);
-#pragma unroll
-      for (int k = 0; k < OQ / 4; ++k) {
-        const float4 v = qp[k];
-        qv[4 * k] = v.x; qv[4 * k + 1] = v.y; qv[4 * k + 2] = v.z; qv[4 * k + 3] = v.w;
-      }
-    }
-    const uint16_t* lo_row = reinterpret_cast<const uint16_t*>(rec + kStageCodes + 16 * D);
-    uint16_t lo16[OQ], hi16[OQ];
-#pragma unroll
-    for (int i = 0; i < OQ; ++i) {
-      lo16[i] = lo_row[c0 + i];
-      hi16[i] = lo_row[D + c0 + i];
-    }
-    uint32_t kb[OQ / 4];
-#pragma unroll
-    for (int k = 0; k < OQ / 4; ++k) kb[k] = rec[kStageCodes + key_code_byte<D>(t, c0 + 4 * k)];
-    const uint16_t nrm = reinterpret_cast<const uint16_t*>(rec + kStageNorms)[t];
-    const int md = rec[kStageMods + t];
-    // value threads: channel tid / OP, positions (tid % OP) OT ..; a code
-    // byte holds four consecutive positions of one channel
-    {
-      const int vc = tid / OP, vt0 = (tid % OP) * OT;
-#pragma unroll
-      for (int k = 0; k < OT / 4; ++k) ovc[k] = rec[kStageCodes + 8 * D + value_code_byte<D>(vt0 + 4 * k, vc)];
-    }
-    float dot = 0.f;
-#pragma unroll
-    for (int i = 0; i < OQ; ++i) {
-      const float lo = f16_bits_to_f32(lo16[i]), hi = f16_bits_to_f32(hi16[i]);
-      const float lvl = a.level_f32[(kb[i >> 2] >> (2 * (i & 3))) & 3u];
-      dot += qv[i] * ((hi + lo) * 0.5f + (hi - lo) * 0.5f * lvl);
-    }
-    dot = row16_sum(dot);
-    if (part == 0) {
-      s_osc[t] = (meta.x != 0 && t < meta.y) ? dot * a.scale_log2e : -__builtin_inff();
-      s_onrm[t] = f16_bits_to_f32(nrm);
-      s_omod[t] = md;
-    }
-  }
-
   float mx = hd0.x;
   for (int s = tid + kMergeThreads; s < S; s += kMergeThreads) mx = fmaxf(mx, P[static_cast<size_t>(s) * PS]);
   mx = wave_max(mx);
@@ -1697,61 +1753,10 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
   if (tid == 0) {
     float M = s_red[0][0];
     for (int w = 1; w < NW; ++w) M = fmaxf(M, s_red[w][0]);
-    if constexpr (STEP) {
-      // the open group's reference max, denominator and modality mask
-      float mo = -__builtin_inff();
-      for (int t = 0; t < kGroupTokens; ++t) mo = fmaxf(mo, s_osc[t]);
-      float lo = 0.f;
-      int mk = 0;
-      if (mo != -__builtin_inff()) {
-        for (int t = 0; t < kGroupTokens; ++t) {
-          if (s_osc[t] == -__builtin_inff()) continue;
-          lo += exp2f(s_osc[t] - mo);
-          if (s_omod[t] < kModalities) mk |= 1 << s_omod[t];
-        }
-      }
-      s_oM = mo;
-      s_ol = lo;
-      s_omask = mk;
-      M = fmaxf(M, mo);
-    }
     s_M = M;
   }
   __syncthreads();
   const float M = s_M;
-  float e_o = 0.f;
-  int omask = 0;
-  if constexpr (STEP) {
-    // the open group's value sums per modality: thread (channel, part)
-    // takes OT positions, the OP parts of a channel sit in adjacent lanes
-    const float mo = s_oM;
-    omask = s_omask;
-    e_o = mo == -__builtin_inff() ? 0.f : exp2f(mo - M);
-    const int vc = tid / OP, vt0 = (tid % OP) * OT;
-    float av[kModalities] = {0.f, 0.f, 0.f};
-    if (mo != -__builtin_inff()) {
-#pragma unroll
-      for (int k = 0; k < OT; ++k) {
-        const int t = vt0 + k;
-        const float sc = s_osc[t];
-        const float w = sc == -__builtin_inff() ? 0.f : exp2f(sc - mo) * s_onrm[t];
-        const float lvl = a.level_f32[(ovc[k >> 2] >> (2 * (t & 3))) & 3u];
-        const int md = s_omod[t];
-#pragma unroll
-        for (int m = 0; m < kModalities; ++m) av[m] += md == m ? w * lvl : 0.f;
-      }
-    }
-#pragma unroll
-    for (int m = 0; m < kModalities; ++m) {
-      av[m] += dpp_f<0xB1>(av[m]);      // quad_perm [1,0,3,2]
-      av[m] += dpp_f<0x4E>(av[m]);      // quad_perm [2,3,0,1]
-      if constexpr (OP == 8) av[m] += dpp_f<0x141>(av[m]);   // row_half_mirror
-    }
-    if (tid % OP == 0) {
-#pragma unroll
-      for (int m = 0; m < kModalities; ++m) s_oA[m][vc] = av[m];
-    }
-  }
   float ls = 0.f, ss[kModalities] = {0.f, 0.f, 0.f};
   for (int s = tid; s < S; s += kMergeThreads) {
     const float4 h0 = s == tid ? hd0 : reinterpret_cast<const float4*>(P + static_cast<size_t>(s) * PS)[0];
@@ -1766,9 +1771,6 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
       ss[1] += (pm & 2) ? e * h1.y : 0.f;
       ss[2] += (pm & 4) ? e * h1.z : 0.f;
     }
-  }
-  if constexpr (STEP) {
-    if (tid == 0) ls += e_o * s_ol;
   }
   ls = wave_sum(ls);
   if constexpr (ASYM)
@@ -1811,14 +1813,6 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
         acc.y += pk[k] ? ek[k] * blk[k].y : 0.f;
         acc.z += pk[k] ? ek[k] * blk[k].z : 0.f;
         acc.w += pk[k] ? ek[k] * blk[k].w : 0.f;
-      }
-    }
-    if constexpr (STEP) {
-      if (g == 0 && ((omask >> cm) & 1)) {
-        acc.x += e_o * s_oA[cm][4 * cf + 0];
-        acc.y += e_o * s_oA[cm][4 * cf + 1];
-        acc.z += e_o * s_oA[cm][4 * cf + 2];
-        acc.w += e_o * s_oA[cm][4 * cf + 3];
       }
     }
     s_part[g][col] = acc;
@@ -1945,7 +1939,7 @@ hipError_t launch_decode_t(int batch, const DecodeArgs& a, hipStream_t s) {
 // merge with the open group.
 template <int D, int SLOTS, bool BF16>
 void launch_step_partition(int batch, const DecodeArgs& a, const AppendArgs& ap, hipStream_t s) {
-  const dim3 grid(a.splits + 2, a.hkv, batch);
+  const dim3 grid(a.splits + 1, a.hkv, batch);
   hipLaunchKernelGGL((decode_partition_sw_kernel<D, SLOTS, false, false, 2, true, BF16>), grid,
                      dim3(kSwWaves * 64), 0, s, a, ap);
 }

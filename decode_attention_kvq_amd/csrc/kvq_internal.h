@@ -57,7 +57,8 @@ struct AppendArgs {
 
 // Open-group staging record of the fused decode step, one per (session, KV
 // head) in the step's workspace after the partials: written by the step's
-// append workgroups, read by its merge.  Byte offsets:
+// append (key and value roles), then read by the same workgroup for the open
+// group's partial.  Byte offsets:
 constexpr int kStageMeta = 0;      // int32 [0]: 1 if the group's page is mapped, [1]: positions in the group
 constexpr int kStageNorms = 64;    // 32 fp16 value norms
 constexpr int kStageMods = 128;    // 32 modality bytes
@@ -86,10 +87,11 @@ struct DecodeArgs {
   const float* q_rot;
   const float* rot;
   void* out;              // [B][Hq][d] fp32, or bf16 when out_bf16
-  float* partials;        // workspace: [B][Hq][splits][kPartialHeader + 3d] partials
+  float* partials;        // workspace: [B][Hq][pstride][kPartialHeader + 3d] partials
   int32_t batch;
   int32_t hq, hkv, group, page_tokens, max_pages, num_pages;
   int32_t splits;         // partitions per (session, KV head)
+  int32_t pstride;        // partials per (session, query head): splits, or splits + 1 (the fused step's open group)
   int32_t split_tokens;   // positions per partition (multiple of 32 * kDecodeWaves)
   int32_t page_shift;     // log2(page_tokens) when it is a power of two, else -1
   int32_t blocks_per_page; // hkv * page_tokens / 32: 32-position blocks of one physical page
@@ -112,9 +114,10 @@ struct DecodeArgs {
 hipError_t launch_append(int d, bool bf16, int nb, const AppendArgs& a, hipStream_t s);
 hipError_t launch_rotate_query(int d, bool bf16, int batch, const RotateArgs& a, hipStream_t s);
 hipError_t launch_decode(int d, int batch, const DecodeArgs& a, hipStream_t s);
-// Fused decode step: the partitions over the closed groups and the append
-// workgroups (ap: one position per session, every session) in one launch,
-// then the merge with the open group.  bf16: query and cache inputs in bf16.
+// Fused decode step: the partitions over the closed groups and, per
+// (session, KV head), one workgroup for the append (ap: one position per
+// session, every session) and the open group's partial, in one launch; then
+// the merge.  bf16: query and cache inputs in bf16.
 hipError_t launch_decode_step(int d, bool bf16, int batch, const DecodeArgs& a, const AppendArgs& ap,
                               hipStream_t s);
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int workgroups, hipStream_t s);
