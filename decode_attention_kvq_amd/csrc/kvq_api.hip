@@ -47,17 +47,21 @@ kvq_status check_cache(const kvq_cache* c) {
   return KVQ_OK;
 }
 
-// Context partitions for the decode.  A partition is a multiple of
-// 32 * kDecodeWaves positions (every wavefront of the workgroup takes whole
-// groups).  Partitions are sized from the longest session so that a batch of
-// such sessions spreads over about one workgroup per compute unit (256 CUs),
-// or four per CU when that would make partitions longer than 4096 positions,
-// and never span more than kPartitionPages - 2 pages (the kernel keeps a
-// partition's page-table entries in LDS).  The plan depends only on
-// (cfg, max_len), so the workspace size is known before the call.
+// Context partitions for the decode: `splits` partitions per (session, KV
+// head) of near-equal whole 32-position groups (split_tokens positions, the
+// first split_extra partitions one group more), sized from the longest
+// session.  They fill the compute units once (one workgroup per CU, 256
+// CUs), or four times when partitions would be longer than 4096 positions;
+// every wavefront gets a group at least; and a partition never spans more
+// than kPartitionPages - 2 pages (the older partition kernel keeps a
+// partition's page-table entries in LDS).  Near-equal partitions leave the
+// longest with one group more than the shortest: one wavefront with one
+// more step.  The plan depends only on (cfg, max_len, reserve), so the
+// workspace size is known before the call.
 struct Plan {
   int splits;
   int split_tokens;
+  int split_extra;
 };
 
 constexpr int64_t kUnit = kGroupTokens * kvq::kDecodeWaves;
@@ -72,22 +76,15 @@ int64_t max_split_tokens(const kvq_config* cfg) {
 // compute units, so that the launch still fits one round.
 Plan plan_decode(const kvq_config* cfg, int32_t max_len, int reserve = 0) {
   const int64_t cus = 256 - ((reserve > 0 && reserve <= 32) ? reserve : 0);
-  const int64_t len = std::max<int32_t>(max_len, 1);
-  const int64_t total = len * cfg->batch * cfg->n_kv_heads;
-  int64_t per = (total + cus - 1) / cus;
-  if (per > 4096) per = (total + 4 * cus - 1) / (4 * cus);
-  per = std::max(kUnit, ((per + kUnit - 1) / kUnit) * kUnit);
-  int64_t splits = (len + per - 1) / per;
-  while (splits > kMaxPlanSplits) {
-    per *= 2;
-    splits = (len + per - 1) / per;
-  }
-  const int64_t cap = max_split_tokens(cfg);
-  if (per > cap) {
-    per = cap;
-    splits = (len + per - 1) / per;
-  }
-  return {(int)splits, (int)per};
+  const int64_t heads = (int64_t)cfg->batch * cfg->n_kv_heads;
+  const int64_t groups = (std::max<int32_t>(max_len, 1) + kGroupTokens - 1) / kGroupTokens;
+  const int64_t cap = max_split_tokens(cfg) / kGroupTokens;
+  int64_t p = std::max<int64_t>(1, cus / heads);
+  if (groups > 128 * p) p = std::max<int64_t>(1, 4 * cus / heads);
+  p = std::min<int64_t>(p, (groups + kvq::kDecodeWaves - 1) / kvq::kDecodeWaves);
+  p = std::max<int64_t>(p, (groups + cap - 1) / cap);
+  p = std::max<int64_t>(1, std::min<int64_t>(p, kMaxPlanSplits));
+  return {(int)p, (int)(groups / p * kGroupTokens), (int)(groups % p)};
 }
 
 // Longest context the plan supports (splits stay within kMaxPlanSplits).
@@ -113,14 +110,9 @@ size_t workspace_floats(const kvq_config* cfg, const Plan& p) {
   return heads * p.splits * (kvq::kPartialHeader + 3 * cfg->head_dim);
 }
 
-// Fused decode step: the partials (one more per head: the open group's),
-// then (from a 256-byte boundary) one open-group staging record per
-// (session, KV head).
-size_t step_stage_offset(const kvq_config* cfg, const Plan& p) {
-  return (workspace_floats(cfg, Plan{p.splits + 1, p.split_tokens}) * sizeof(float) + 255) / 256 * 256;
-}
+// Fused decode step: one more partial per head, the open group's.
 size_t step_workspace_bytes(const kvq_config* cfg, const Plan& p) {
-  return step_stage_offset(cfg, p) + (size_t)cfg->batch * cfg->n_kv_heads * kvq::stage_record_bytes(cfg->head_dim);
+  return workspace_floats(cfg, Plan{p.splits + 1, p.split_tokens, p.split_extra}) * sizeof(float);
 }
 
 }  // namespace
@@ -270,12 +262,12 @@ kvq_status kvq_rotate_query(const kvq_config* cfg, const kvq_params* params, int
 
 size_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t max_len) {
   if (check_config(cfg) != KVQ_OK || max_len < 0) return 0;
-  return workspace_floats(cfg, Plan{splits_bound(cfg, max_len), 0}) * sizeof(float);
+  return workspace_floats(cfg, Plan{splits_bound(cfg, max_len), 0, 0}) * sizeof(float);
 }
 
 size_t kvq_decode_step_workspace_bytes(const kvq_config* cfg, int32_t max_len) {
   if (check_config(cfg) != KVQ_OK || max_len < 0) return 0;
-  return step_workspace_bytes(cfg, Plan{splits_bound(cfg, max_len), 0});
+  return step_workspace_bytes(cfg, Plan{splits_bound(cfg, max_len), 0, 0});
 }
 
 }  // extern "C"
@@ -359,6 +351,7 @@ static kvq::DecodeArgs decode_args(const kvq_config* cfg, const kvq_cache* cache
   a.splits = plan.splits;
   a.pstride = plan.splits;
   a.split_tokens = plan.split_tokens;
+  a.split_extra = plan.split_extra;
   a.page_shift = -1;
   if ((cfg->page_tokens & (cfg->page_tokens - 1)) == 0) {
     a.page_shift = 0;
@@ -476,13 +469,10 @@ kvq_status kvq_decode_step(const kvq_config* cfg, kvq_cache* cache, const kvq_pa
     e = kvq::launch_append(cfg->head_dim, cfg->kv_dtype == KVQ_BF16, cfg->batch, ap, stream);
     if (e == hipSuccess) e = kvq::launch_decode(cfg->head_dim, cfg->batch, a, stream);
   } else {
-    uint8_t* stage = static_cast<uint8_t*>(workspace) + step_stage_offset(cfg, plan);
     ap.rq = r;
     ap.rot_heads = 0;
     ap.append_x = 2;
     ap.defer_len = 1;
-    ap.stage = stage;
-    a.stage = stage;
     a.step_len = cache->seq_len;
     a.pstride = plan.splits + 1;
     e = kvq::launch_decode_step(cfg->head_dim, cfg->kv_dtype == KVQ_BF16, cfg->batch, a, ap, stream);

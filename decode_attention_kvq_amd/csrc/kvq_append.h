@@ -28,7 +28,7 @@
 // workgroup takes a ticket when done; the last one of a session advances its
 // length, so no workgroup can see the new length before it read the old one
 // (the fused step defers this to its merge, and also copies the open group's
-// blocks, statistics, norms and modality bytes to a staging record).
+// blocks, statistics, norms and modality bytes to a record in shared memory).
 //
 // Latency matters more than throughput for the common one-position append:
 // each role issues its global loads in at most two dependent rounds, 16
@@ -165,9 +165,12 @@ union AppendSmem {
 // bx is even, values when odd.  All kAppendThreads threads call it together.
 // sm and s_last live in the caller's shared memory; ticket_total is the
 // number of workgroups of one session that take a completion ticket.
+// stage: null, or (the fused decode step: one-position appends to a 2-bit
+// cache with group statistics) a record in the caller's shared memory that
+// receives a copy of the open group (kStage* layout).
 template <int D, bool BF16, int BITS>
 __device__ __forceinline__ void append_group(const AppendArgs& a, AppendSmem<D>& sm, int& s_last, int bx, int h,
-                                             int b, int ticket_total) {
+                                             int b, int ticket_total, uint8_t* stage = nullptr) {
 #pragma clang fp contract(off)
   constexpr int CH = D / kPosThreads;             // channels per thread (inputs, transform, key codes)
   constexpr int ESZ = BF16 ? 2 : 4;
@@ -181,9 +184,6 @@ __device__ __forceinline__ void append_group(const AppendArgs& a, AppendSmem<D>&
   const int j = bx >> 1;
   const bool vrole = bx & 1;
   const int sb = a.b0 + b;
-  // Staging record of the open group (fused decode step only: one-position
-  // appends to a 2-bit cache with group statistics), else null.
-  uint8_t* const stage = a.stage ? a.stage + static_cast<size_t>(sb * a.hkv + h) * stage_record_bytes(D) : nullptr;
   const int lane = tid & 63;
   const int tok = tid / kPosThreads, part = tid % kPosThreads, cb = part * CH;
 

@@ -142,6 +142,12 @@ __device__ __forceinline__ int phys_page(const DecodeArgs& a, const int* s_pt, i
   return ptab[static_cast<size_t>(b) * a.max_pages + pg];
 }
 
+// First position of partition s: partitions of split_tokens positions, the
+// first split_extra of them one 32-position group longer.
+__device__ __forceinline__ int split_begin(const DecodeArgs& a, int s) {
+  return s * a.split_tokens + kGroupTokens * min(s, a.split_extra);
+}
+
 // Positions of session b the decode may attend: its device length, bounded
 // by the capacity of its page-table row.
 __device__ __forceinline__ int session_length(const DecodeArgs& a, int b) {
@@ -510,8 +516,8 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_partition_kernel(DecodeArgs
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int G = a.group;
   const int L = session_length(a, b);
-  const int tb = split * a.split_tokens;
-  const int te = (split == a.splits - 1) ? L : min(tb + a.split_tokens, L);
+  const int tb = split_begin(a, split);
+  const int te = (split == a.splits - 1) ? L : min(split_begin(a, split + 1), L);
   const int te_full = te & ~(kGroupTokens - 1);   // tb is a multiple of 32
   const int stride = NW * kGroupTokens;
   const int first = tb + wave * kGroupTokens;
@@ -1152,11 +1158,13 @@ struct StepSmem {
   float nrm[kGroupTokens];
   int mod[kGroupTokens];
   int last;                             // the append's ticket flag (unused: the merge advances the lengths)
+  __align__(16) uint8_t rec[stage_record_bytes(D)];   // the open group (kStage* layout)
 };
 
 // The fused step's work for (session b, KV head h) beside the partitions:
 // the append of the step's position (the key role, then the value role of
-// kvq_append.h, which also copy the open group to its staging record), then
+// kvq_append.h, which also copy the open group to a record in this
+// workgroup's shared memory), then
 // the open group's partial for every query head i of the KV head, as partial
 // a.splits of the head in the partitions' form: scores
 // s_t = scale log2(e) <q_rot_i, k_hat_t> with k_hat = (HI + LO) / 2 +
@@ -1183,12 +1191,12 @@ __device__ __forceinline__ void step_append_open_group(const DecodeArgs& a, cons
 #pragma unroll
     for (int i = 0; i < RCH; ++i) sm.q[hl][sub * RCH + i] = o[i];
   }
-  app::append_group<D, BF16, 2>(ap, sm.app, sm.last, 0, h, b, 0);
+  app::append_group<D, BF16, 2>(ap, sm.app, sm.last, 0, h, b, 0, sm.rec);
   __syncthreads();
-  app::append_group<D, BF16, 2>(ap, sm.app, sm.last, 1, h, b, 0);
-  __syncthreads();   // the staging record is complete (written by this workgroup)
+  app::append_group<D, BF16, 2>(ap, sm.app, sm.last, 1, h, b, 0, sm.rec);
+  __syncthreads();   // the open group's record is complete
 
-  const uint8_t* rec = a.stage + static_cast<size_t>(b * a.hkv + h) * stage_record_bytes(D);
+  const uint8_t* rec = sm.rec;
   {
     // scores: thread (t, part) takes channels part OQ .. of position t
     const int t = tid / 16, part = tid % 16, c0 = part * OQ;
@@ -1306,8 +1314,8 @@ __global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(D
   const int G = a.group;
   // STEP: the closed groups only (the append rewrites the open one)
   const int L = STEP ? (session_length(a, b) & ~(kGroupTokens - 1)) : session_length(a, b);
-  const int tb = split * a.split_tokens;
-  const int te = (split == a.splits - 1) ? L : min(tb + a.split_tokens, L);
+  const int tb = split_begin(a, split);
+  const int te = (split == a.splits - 1) ? L : min(split_begin(a, split + 1), L);
   const int ng = te > tb ? (te - tb + kGroupTokens - 1) / kGroupTokens : 0;   // groups of the partition
   // The groups are dealt to the wavefronts round robin: step j of wavefront
   // w is group w + NW j, so the NW wavefronts read NW adjacent blocks at a

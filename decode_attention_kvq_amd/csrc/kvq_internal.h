@@ -50,15 +50,14 @@ struct AppendArgs {
   RotateArgs rq;
   int32_t rot_heads, rot_bf16, append_x;
   // Fused decode step: the append leaves the session lengths to the step's
-  // merge (defer_len) and copies the open group to the staging records.
+  // merge.
   int32_t defer_len;
-  uint8_t* stage;
 };
 
-// Open-group staging record of the fused decode step, one per (session, KV
-// head) in the step's workspace after the partials: written by the step's
-// append (key and value roles), then read by the same workgroup for the open
-// group's partial.  Byte offsets:
+// Open-group record of the fused decode step, in the shared memory of the
+// workgroup that runs the step's append for one (session, KV head): written
+// by the append's key and value roles, then read for the open group's
+// partial.  Byte offsets:
 constexpr int kStageMeta = 0;      // int32 [0]: 1 if the group's page is mapped, [1]: positions in the group
 constexpr int kStageNorms = 64;    // 32 fp16 value norms
 constexpr int kStageMods = 128;    // 32 modality bytes
@@ -92,7 +91,8 @@ struct DecodeArgs {
   int32_t hq, hkv, group, page_tokens, max_pages, num_pages;
   int32_t splits;         // partitions per (session, KV head)
   int32_t pstride;        // partials per (session, query head): splits, or splits + 1 (the fused step's open group)
-  int32_t split_tokens;   // positions per partition (multiple of 32 * kDecodeWaves)
+  int32_t split_tokens;   // positions of a partition, a multiple of 32 ...
+  int32_t split_extra;    // ... plus 32 for each of the first split_extra partitions
   int32_t page_shift;     // log2(page_tokens) when it is a power of two, else -1
   int32_t blocks_per_page; // hkv * page_tokens / 32: 32-position blocks of one physical page
   int32_t offsets31;       // every cache array is below 2^31 bytes
@@ -104,9 +104,8 @@ struct DecodeArgs {
   int32_t out_bf16;       // write the output as bf16 (round to nearest even) instead of fp32
   uint32_t level_f16[8];  // normalized levels (2 c_k - c0 - c_{n-1}) / (c_{n-1} - c0) as fp16 bits, k < n
   uint32_t level_lo_f16[8]; // 2^12 (level - fp16 level) as fp16 bits (3 / 4 bits: the scores' lo part)
-  // Fused decode step (null / unused otherwise): the open-group records, the
-  // lengths the merge advances, and the 2-bit normalized levels in fp32.
-  const uint8_t* stage;
+  // Fused decode step (null / unused otherwise): the lengths the merge
+  // advances, and the 2-bit normalized levels in fp32.
   int32_t* step_len;
   float level_f32[4];
 };

@@ -243,8 +243,8 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache,
                                 hipStream_t stream);
 
 /* Workspace bytes kvq_decode_step needs when the longest session holds
- * max_len positions after the step (split-K partial results and one
- * open-group record per session and KV head). */
+ * max_len positions after the step (split-K partial results, one more per
+ * query head for the open group). */
 size_t kvq_decode_step_workspace_bytes(const kvq_config* cfg, int32_t max_len);
 
 /*
@@ -263,11 +263,11 @@ size_t kvq_decode_step_workspace_bytes(const kvq_config* cfg, int32_t max_len);
  * q_dtype == kv_dtype, the step runs in two launches instead of three: the
  * first runs the decode partitions over each session's closed groups
  * (positions below 32 floor(L / 32), L = the length before the step; the
- * partitions rotate their own query heads) side by side with the append's
- * workgroups, which also copy the open group to the workspace; the second
- * merges the partitions, attends the open group [32 floor(L / 32), L + 1)
- * and advances the lengths.  Other configurations launch the two calls
- * above.
+ * partitions rotate their own query heads) side by side with one workgroup
+ * per session and KV head that runs the append and then attends the open
+ * group [32 floor(L / 32), L + 1) as one more partial; the second merges
+ * the partials and advances the lengths.  Other configurations launch the
+ * two calls above.
  * k_new, v_new: device [batch][1][Hkv][d] in cfg->kv_dtype; modality_new:
  * device [batch][1] uint8; q: device [batch][Hq][d] in q_dtype; q_rot:
  * device [batch][Hq][d] fp32 (written); out: device [batch][Hq][d] in

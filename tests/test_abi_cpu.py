@@ -191,7 +191,7 @@ def test_append_and_rotate_rejects_bad_arguments_before_launch():
 def test_decode_step_rejects_bad_arguments_before_launch():
     """The fused decode step checks the append, the rotation and the decode on
     the host; a failure launches nothing and leaves the length mirror as it
-    was.  Its workspace covers the partials and the open-group records, and
+    was.  Its workspace covers the partials, the open group's included, and
     a workspace sized for a length serves every shorter one."""
     L, lib = _lib()
     cfg = _cfg(L)                                   # G = 8, 256-position pages, bf16: the two-launch path
@@ -199,9 +199,9 @@ def test_decode_step_rejects_bad_arguments_before_launch():
     c, lens = _fake_cache(L, [10, 700])
     V = ctypes.c_void_p
     need = lib.kvq_decode_step_workspace_bytes(ctypes.byref(cfg), 701)
-    # partials of at least one partition per (session, query head), then
-    # 2 x 2 records of 256 + 20 d bytes
-    assert need >= 2 * 16 * (8 + 3 * 128) * 4 + 4 * (256 + 20 * 128)
+    # per (session, query head): the partials of at least one partition and
+    # the open group's
+    assert need >= 2 * 16 * 2 * (8 + 3 * 128) * 4
     assert all(lib.kvq_decode_step_workspace_bytes(ctypes.byref(cfg), n) <= need for n in (0, 1, 33, 256, 700))
 
     def call(k=V(8), v=V(8), m=V(8), q=V(8), qd=L.KVQ_BF16, qr=V(8), scale=0.1, out=V(8), od=L.KVQ_F32,
