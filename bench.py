@@ -41,8 +41,8 @@ L80K = 81920
 # (FETCH_SIZE x 1.9997, WRITE_SIZE x 1.0); see profiles/decode_80k_hbm_bytes.md.
 # Valid only for the decode source the counters were taken on (SHA-256 of
 # kvq_decode.hip); otherwise `traffic` is reported as null.
-DECODE_TRAFFIC = {"kvq_decode_sha256": "fb0af28a8adb44a0e86a5f4c2ab31b6e1b4d06614c0c3e0999a7add4728270a1",
-                  "bytes": 34910618}
+DECODE_TRAFFIC = {"kvq_decode_sha256": "7c014ea6399e0561e4e09b59d99fcf0bc4e42b0ba7c973fc767cfffa0f49cd3c",
+                  "bytes": 32870366}
 
 
 def decode_traffic_bytes():
@@ -423,26 +423,36 @@ def extra_80k(K, cfg, params, caches, table, q_rot, out, ws, scale, n_dec, dec_b
 def time_stream_read(nbytes: int, replicas: int, launches: int) -> dict:
     """The floor for one read-only kernel of nbytes (the decode's algorithmic
     bytes): kvq_probe_stream_read, a plain 16-byte streaming read, over
-    `replicas` buffers cycled so the reads come from HBM, HIP events over
-    `launches` launches, for several grid sizes; the fastest is reported."""
+    `replicas` buffers cycled so the reads come from HBM, launched from a HIP
+    graph like the decode, HIP events over about `launches` launches, for
+    several grid sizes; the fastest is reported."""
     import torch
     import decode_attention_kvq_amd as K
     nb = (nbytes // 16) * 16
     bufs = [torch.ones(nb // 4, dtype=torch.int32, device="cuda") for _ in range(replicas)]
     sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
+    s_cap = torch.cuda.Stream()
+    s_cap.wait_stream(stream)
+    n_rep = max(1, launches // replicas)
     shapes = {}
     for wgs in (256, 512, 1024, 2048, 4096):
+        # one graph of `replicas` launches (one per buffer), replayed: the
+        # launches run back to back like the decode's
         for b in bufs:
             K.kvq_probe_stream_read(b, sink, wgs)
         torch.cuda.synchronize()
+        g = _capture([lambda b=b: K.kvq_probe_stream_read(b, sink, wgs) for b in bufs], s_cap)
+        g.replay()
+        torch.cuda.synchronize()
         e0, e1 = _events()
         e0.record(stream)
-        for i in range(launches):
-            K.kvq_probe_stream_read(bufs[i % replicas], sink, wgs)
+        for _ in range(n_rep):
+            g.replay()
         e1.record(stream)
         torch.cuda.synchronize()
-        shapes[wgs] = e0.elapsed_time(e1) * 1e3 / launches
+        shapes[wgs] = e0.elapsed_time(e1) * 1e3 / (n_rep * replicas)
+        del g
     best = min(shapes, key=shapes.get)
     us = shapes[best]
     del bufs
