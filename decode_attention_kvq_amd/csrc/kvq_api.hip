@@ -51,8 +51,9 @@ kvq_status check_cache(const kvq_cache* c) {
 // head) of near-equal whole 32-position groups (split_tokens positions, the
 // first split_extra partitions one group more), sized from the longest
 // session.  They fill the compute units once (one workgroup per CU, 256
-// CUs), or four times when partitions would be longer than 4096 positions;
-// every wavefront gets a group at least; and a partition never spans more
+// CUs; long partitions beat several rounds of short ones, which each pay
+// the set-up and the epilogue again); every wavefront gets a group at
+// least; and a partition never spans more
 // than kPartitionPages - 2 pages (the older partition kernel keeps a
 // partition's page-table entries in LDS).  Near-equal partitions leave the
 // longest with one group more than the shortest: one wavefront with one
@@ -80,7 +81,6 @@ Plan plan_decode(const kvq_config* cfg, int32_t max_len, int reserve = 0) {
   const int64_t groups = (std::max<int32_t>(max_len, 1) + kGroupTokens - 1) / kGroupTokens;
   const int64_t cap = max_split_tokens(cfg) / kGroupTokens;
   int64_t p = std::max<int64_t>(1, cus / heads);
-  if (groups > 128 * p) p = std::max<int64_t>(1, 4 * cus / heads);
   p = std::min<int64_t>(p, (groups + kvq::kDecodeWaves - 1) / kvq::kDecodeWaves);
   p = std::max<int64_t>(p, (groups + cap - 1) / cap);
   p = std::max<int64_t>(1, std::min<int64_t>(p, kMaxPlanSplits));

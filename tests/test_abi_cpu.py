@@ -154,9 +154,9 @@ def test_noalloc_decode_rejects_before_launch():
     V = ctypes.c_void_p
     call = lambda cfg, c, od=L.KVQ_F32: lib.kvq_decode_attention_noalloc(
         ctypes.byref(cfg), ctypes.byref(c), ctypes.byref(p), V(8), ctypes.c_float(0.1), V(8), od, None)
-    big = _cfg(L, batch=64, n_q_heads=128, n_kv_heads=8, max_pages=256, num_pages=64 * 256)
-    c, lens = _fake_cache(L, [65536] * 64)
-    # 64 sessions x 128 query heads x 2 partitions x (8 + 3 * 128) floats = 25.7 MB > 16 MiB
+    big = _cfg(L, batch=128, n_q_heads=128, n_kv_heads=8, max_pages=256, num_pages=128 * 256)
+    c, lens = _fake_cache(L, [65536] * 128)
+    # 128 sessions x 128 query heads x 1 partition x (8 + 3 * 128) floats = 25.7 MB > 16 MiB
     assert call(big, c) == L.KVQ_ERR_SCRATCH
     assert call(big, c, od=9) == L.KVQ_ERR_UNSUPPORTED
     lens[3] = -1
