@@ -5,6 +5,8 @@
 
 #include <algorithm>
 #include <mutex>
+#include <queue>
+#include <utility>
 
 #include "kvq_internal.h"
 
@@ -47,23 +49,22 @@ kvq_status check_cache(const kvq_cache* c) {
   return KVQ_OK;
 }
 
-// Context partitions for the decode: `splits` partitions per (session, KV
-// head) of near-equal whole 32-position groups (split_tokens positions, the
-// first split_extra partitions one group more), sized from the longest
-// session.  They fill the compute units once (one workgroup per CU, 256
-// CUs; long partitions beat several rounds of short ones, which each pay
-// the set-up and the epilogue again); every wavefront gets a group at
-// least; and a partition never spans more
-// than kPartitionPages - 2 pages (the older partition kernel keeps a
-// partition's page-table entries in LDS).  Near-equal partitions leave the
-// longest with one group more than the shortest: one wavefront with one
-// more step.  The plan depends only on (cfg, max_len, reserve), so the
-// workspace size is known before the call.
-struct Plan {
-  int splits;
-  int split_tokens;
-  int split_extra;
-};
+// Context partitions of a decode: each (session, KV head) context is split
+// into partitions of near-equal whole 32-position groups (the first `extra`
+// of a session's partitions one group longer), one workgroup each.  The
+// partitions of all sessions fill the compute units once (256 CUs; long
+// partitions beat rounds of short ones, which each pay the set-up and the
+// epilogue again).  Up to kPlanSessions sessions get partition counts of
+// their own: every session starts with its minimum (one partition, or more
+// when a partition would span more than kPartitionPages - 2 pages, which the
+// older partition kernel keeps in LDS) and the remaining grid columns go
+// one at a time to the session whose partitions are longest, so a ragged
+// batch ends together; no partition gets fewer than 8 groups' worth of
+// columns (one group per wavefront).  Larger batches share one uniform
+// count.  step = 1 (the fused decode step) adds one slot and one grid column
+// per session for the open group.  The plan depends only on (cfg, the
+// host-side lengths, step).
+using Plan = kvq::DecodeArgs;   // the plan's fields of the kernel arguments
 
 constexpr int64_t kUnit = kGroupTokens * kvq::kDecodeWaves;
 constexpr int64_t kMaxPlanSplits = 4096;
@@ -72,47 +73,83 @@ int64_t max_split_tokens(const kvq_config* cfg) {
   return ((int64_t)(kvq::kPartitionPages - 2) * cfg->page_tokens / kUnit) * kUnit;
 }
 
-// `reserve` workgroups (at most 32) of the same launch run something else
-// (the fused step's append): the partitions then spread over the remaining
-// compute units, so that the launch still fits one round.
-Plan plan_decode(const kvq_config* cfg, int32_t max_len, int reserve = 0) {
-  const int64_t cus = 256 - ((reserve > 0 && reserve <= 32) ? reserve : 0);
-  const int64_t heads = (int64_t)cfg->batch * cfg->n_kv_heads;
-  const int64_t groups = (std::max<int32_t>(max_len, 1) + kGroupTokens - 1) / kGroupTokens;
-  const int64_t cap = max_split_tokens(cfg) / kGroupTokens;
-  int64_t p = std::max<int64_t>(1, cus / heads);
-  p = std::min<int64_t>(p, (groups + kvq::kDecodeWaves - 1) / kvq::kDecodeWaves);
-  p = std::max<int64_t>(p, (groups + cap - 1) / cap);
-  p = std::max<int64_t>(1, std::min<int64_t>(p, kMaxPlanSplits));
-  return {(int)p, (int)(groups / p * kGroupTokens), (int)(groups % p)};
+int64_t cap_groups(const kvq_config* cfg) { return max_split_tokens(cfg) / kGroupTokens; }
+int64_t groups_of(int64_t len) { return (std::max<int64_t>(len, 0) + kGroupTokens - 1) / kGroupTokens; }
+int64_t min_parts(const kvq_config* cfg, int64_t groups) {
+  return std::max<int64_t>(1, (groups + cap_groups(cfg) - 1) / cap_groups(cfg));
+}
+int64_t max_parts(const kvq_config* cfg, int64_t groups) {
+  return std::max(min_parts(cfg, groups), (groups + kvq::kDecodeWaves - 1) / kvq::kDecodeWaves);
+}
+// grid columns that give one workgroup per compute unit
+int64_t plan_columns(const kvq_config* cfg) { return std::max<int64_t>(1, 256 / cfg->n_kv_heads); }
+
+// lens: host-side session lengths; every session is planned for lens[b] + extra positions.
+Plan plan_decode(const kvq_config* cfg, const int32_t* lens, int32_t extra, int step) {
+  Plan p{};
+  const int B = cfg->batch;
+  const int64_t cols = plan_columns(cfg);
+  p.step = step;
+  if (B <= kvq::kPlanSessions) {
+    int64_t g[kvq::kPlanSessions], n[kvq::kPlanSessions];
+    int64_t used = 0;
+    for (int b = 0; b < B; ++b) {
+      g[b] = groups_of((int64_t)lens[b] + extra);
+      n[b] = min_parts(cfg, g[b]);
+      used += n[b] + step;
+    }
+    // (partition length in groups, -session): the longest partitions first, then the lowest session
+    std::priority_queue<std::pair<int64_t, int>> q;
+    for (int b = 0; b < B; ++b)
+      if (n[b] < max_parts(cfg, g[b])) q.push({(g[b] + n[b] - 1) / n[b], -b});
+    while (used < cols && !q.empty()) {
+      const int b = -q.top().second;
+      q.pop();
+      ++n[b];
+      ++used;
+      if (n[b] < max_parts(cfg, g[b])) q.push({(g[b] + n[b] - 1) / n[b], -b});
+    }
+    p.ntab = B;
+    p.tab_start[0] = 0;
+    for (int b = 0; b < B; ++b) {
+      p.tab_start[b + 1] = p.tab_start[b] + (int)(n[b] + step);
+      p.tab_tokens[b] = (int)(g[b] / n[b] * kGroupTokens);
+      p.tab_extra[b] = (int)(g[b] % n[b]);
+    }
+    p.pstride = p.tab_start[B];
+    p.splits = (int)*std::max_element(n, n + B);
+  } else {
+    int32_t max_len = 0;
+    for (int b = 0; b < B; ++b) max_len = std::max(max_len, lens[b]);
+    const int64_t g = groups_of((int64_t)max_len + extra);
+    int64_t n = std::max<int64_t>(1, cols / B - step);
+    n = std::max(min_parts(cfg, g), std::min(n, max_parts(cfg, g)));
+    p.ntab = 0;
+    p.splits = (int)n;
+    p.split_tokens = (int)(g / n * kGroupTokens);
+    p.split_extra = (int)(g % n);
+    p.pstride = (int)(B * (n + step));
+  }
+  return p;
 }
 
-// Longest context the plan supports (splits stay within kMaxPlanSplits).
+// Longest context the plan supports (a session's partitions and the step's
+// slot stay within kMaxPlanSplits).
 bool plan_supported(const kvq_config* cfg, int32_t max_len) {
-  return (int64_t)max_len <= kMaxPlanSplits * max_split_tokens(cfg);
+  return (int64_t)max_len <= (kMaxPlanSplits - 1) * max_split_tokens(cfg);
 }
 
-// Upper bound of plan_decode(cfg, len, reserve).splits over every len <=
-// max_len and reserve, so a workspace sized for max_len serves every shorter
-// context too.
-int splits_bound(const kvq_config* cfg, int32_t max_len) {
-  const int64_t heads = (int64_t)cfg->batch * cfg->n_kv_heads;
-  const int64_t len = std::max<int32_t>(max_len, 1);
-  const int64_t by_len = (len + kUnit - 1) / kUnit;
-  const int64_t by_grid = (1024 + heads - 1) / heads + 1;
-  const int64_t by_cap = (len + max_split_tokens(cfg) - 1) / max_split_tokens(cfg);
-  return (int)std::min<int64_t>(kMaxPlanSplits, std::max<int64_t>(1, std::min(by_len, std::max(by_grid, by_cap))));
+// Upper bound of plan_decode(cfg, lens, extra, step).pstride over every
+// length <= max_len (extra included), so a workspace sized for max_len
+// serves every shorter context too.
+int64_t slots_bound(const kvq_config* cfg, int32_t max_len, int step) {
+  const int64_t B = cfg->batch;
+  return std::max(plan_columns(cfg), B * (min_parts(cfg, groups_of(max_len)) + step)) + B * step;
 }
 
-// Workspace: one partial result per (session, query head, partition).
-size_t workspace_floats(const kvq_config* cfg, const Plan& p) {
-  const size_t heads = (size_t)cfg->batch * cfg->n_q_heads;
-  return heads * p.splits * (kvq::kPartialHeader + 3 * cfg->head_dim);
-}
-
-// Fused decode step: one more partial per head, the open group's.
-size_t step_workspace_bytes(const kvq_config* cfg, const Plan& p) {
-  return workspace_floats(cfg, Plan{p.splits + 1, p.split_tokens, p.split_extra}) * sizeof(float);
+// Workspace: one partial result per (query head, slot).
+size_t workspace_floats(const kvq_config* cfg, int64_t slots) {
+  return (size_t)cfg->n_q_heads * slots * (kvq::kPartialHeader + 3 * cfg->head_dim);
 }
 
 }  // namespace
@@ -262,12 +299,12 @@ kvq_status kvq_rotate_query(const kvq_config* cfg, const kvq_params* params, int
 
 size_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t max_len) {
   if (check_config(cfg) != KVQ_OK || max_len < 0) return 0;
-  return workspace_floats(cfg, Plan{splits_bound(cfg, max_len), 0, 0}) * sizeof(float);
+  return workspace_floats(cfg, slots_bound(cfg, max_len, 0)) * sizeof(float);
 }
 
 size_t kvq_decode_step_workspace_bytes(const kvq_config* cfg, int32_t max_len) {
   if (check_config(cfg) != KVQ_OK || max_len < 0) return 0;
-  return step_workspace_bytes(cfg, Plan{splits_bound(cfg, max_len), 0, 0});
+  return workspace_floats(cfg, slots_bound(cfg, max_len, 1)) * sizeof(float);
 }
 
 }  // extern "C"
@@ -328,7 +365,7 @@ static kvq::DecodeArgs decode_args(const kvq_config* cfg, const kvq_cache* cache
                                    void* partials) {
   const int nlev = 1 << cfg->bits;
   const double c0 = params->codebook[0], c3 = params->codebook[nlev - 1];   // outer levels
-  kvq::DecodeArgs a{};
+  kvq::DecodeArgs a = plan;   // the plan's fields
   a.k_codes = cache->k_codes;
   a.k_stats = cache->k_stats;
   a.v_codes = cache->v_codes;
@@ -348,10 +385,6 @@ static kvq::DecodeArgs decode_args(const kvq_config* cfg, const kvq_cache* cache
   a.page_tokens = cfg->page_tokens;
   a.max_pages = cfg->max_pages;
   a.num_pages = cfg->num_pages;
-  a.splits = plan.splits;
-  a.pstride = plan.splits;
-  a.split_tokens = plan.split_tokens;
-  a.split_extra = plan.split_extra;
   a.page_shift = -1;
   if ((cfg->page_tokens & (cfg->page_tokens - 1)) == 0) {
     a.page_shift = 0;
@@ -401,8 +434,8 @@ static kvq_status decode_impl(const kvq_config* cfg, const kvq_cache* cache, con
   int32_t max_len = 0;
   kvq_status st = check_decode(cfg, cache, params, q_rot, scale, out, out_dtype, 0, max_len);
   if (st != KVQ_OK) return st;
-  const Plan plan = plan_decode(cfg, max_len);
-  const size_t need = workspace_floats(cfg, plan) * sizeof(float);
+  const Plan plan = plan_decode(cfg, cache->seq_len_host, 0, 0);
+  const size_t need = workspace_floats(cfg, plan.pstride) * sizeof(float);
   if (scratch) {
     if (need > KVQ_NOALLOC_SCRATCH_BYTES) return KVQ_ERR_SCRATCH;
   } else if (!workspace || workspace_bytes < need) {
@@ -454,9 +487,9 @@ kvq_status kvq_decode_step(const kvq_config* cfg, kvq_cache* cache, const kvq_pa
   const bool fused = cfg->bits == 2 && cfg->key_mode == KVQ_KEYS_GROUP_MINMAX &&
                      params->codebook[0] == -params->codebook[3] && group <= 8 && pow2 && offsets31 &&
                      q_dtype == cfg->kv_dtype;
-  const int reserve = fused ? cfg->n_kv_heads * cfg->batch : 0;
-  const Plan plan = plan_decode(cfg, max_len, reserve);
-  const size_t need = fused ? step_workspace_bytes(cfg, plan) : workspace_floats(cfg, plan) * sizeof(float);
+  // the fused step plans one more slot (and grid column) per session for the open group
+  const Plan plan = plan_decode(cfg, cache->seq_len_host, 1, fused ? 1 : 0);
+  const size_t need = workspace_floats(cfg, plan.pstride) * sizeof(float);
   if (!workspace || workspace_bytes < need) return KVQ_ERR_WORKSPACE;
   kvq::DecodeArgs a = decode_args(cfg, cache, params, q_rot, scale, out, out_dtype, plan, workspace);
   if (!decode_supported(a)) return KVQ_ERR_UNSUPPORTED;
@@ -474,7 +507,6 @@ kvq_status kvq_decode_step(const kvq_config* cfg, kvq_cache* cache, const kvq_pa
     ap.append_x = 2;
     ap.defer_len = 1;
     a.step_len = cache->seq_len;
-    a.pstride = plan.splits + 1;
     e = kvq::launch_decode_step(cfg->head_dim, cfg->kv_dtype == KVQ_BF16, cfg->batch, a, ap, stream);
   }
   if (e != hipSuccess) return KVQ_ERR_LAUNCH;

@@ -142,10 +142,41 @@ __device__ __forceinline__ int phys_page(const DecodeArgs& a, const int* s_pt, i
   return ptab[static_cast<size_t>(b) * a.max_pages + pg];
 }
 
-// First position of partition s: partitions of split_tokens positions, the
-// first split_extra of them one 32-position group longer.
-__device__ __forceinline__ int split_begin(const DecodeArgs& a, int s) {
-  return s * a.split_tokens + kGroupTokens * min(s, a.split_extra);
+// Where this workgroup's partition sits in the plan (DecodeArgs): its
+// session b, its index `split` in the session, the session's partition count
+// n and first partial slot slot0, and the partition's planned positions
+// [tb, tend) (the last partition of a session takes every position past it).
+struct Place {
+  int b, split, n, slot0, tb, tend;
+};
+__device__ __forceinline__ Place place_of(const DecodeArgs& a) {
+  Place p;
+  int tokens, extra;
+  if (a.ntab > 0) {
+    const int x = blockIdx.x;
+    int lo = 0, hi = a.ntab - 1;   // the last session whose slots start at or before x
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.tab_start[mid] <= x) lo = mid;
+      else hi = mid - 1;
+    }
+    p.b = lo;
+    p.slot0 = a.tab_start[lo];
+    p.n = a.tab_start[lo + 1] - p.slot0 - a.step;
+    p.split = x - p.slot0;
+    tokens = a.tab_tokens[lo];
+    extra = a.tab_extra[lo];
+  } else {
+    p.b = blockIdx.z;
+    p.slot0 = p.b * (a.splits + a.step);
+    p.n = a.splits;
+    p.split = blockIdx.x;
+    tokens = a.split_tokens;
+    extra = a.split_extra;
+  }
+  p.tb = p.split * tokens + kGroupTokens * min(p.split, extra);
+  p.tend = p.tb + tokens + (p.split < extra ? kGroupTokens : 0);
+  return p;
 }
 
 // Positions of session b the decode may attend: its device length, bounded
@@ -513,11 +544,12 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_partition_kernel(DecodeArgs
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar) index
   const int kg = lane >> 4, col = lane & 15;
-  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const Place pl = place_of(a);
+  const int split = pl.split, h = blockIdx.y, b = pl.b;
   const int G = a.group;
   const int L = session_length(a, b);
-  const int tb = split_begin(a, split);
-  const int te = (split == a.splits - 1) ? L : min(split_begin(a, split + 1), L);
+  const int tb = pl.tb;
+  const int te = (split == pl.n - 1) ? L : min(pl.tend, L);
   const int te_full = te & ~(kGroupTokens - 1);   // tb is a multiple of 32
   const int stride = NW * kGroupTokens;
   const int first = tb + wave * kGroupTokens;
@@ -689,13 +721,13 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_partition_kernel(DecodeArgs
         s.z += v.z;
         s.w += v.w;
       }
-      float* part = a.partials + ((static_cast<size_t>(b) * a.hq + h * G + hp2) * a.pstride + split) * PS;
+      float* part = a.partials + (static_cast<size_t>(h * G + hp2) * a.pstride + pl.slot0 + split) * PS;
       *reinterpret_cast<float4*>(part + kPartialHeader + m * D + 16 * ct + 4 * kg2) = s;
     }
   }
   if (tid < G * kPartialHeader) {
     const int hh = tid / kPartialHeader, f = tid % kPartialHeader;
-    float* part = a.partials + ((static_cast<size_t>(b) * a.hq + h * G + hh) * a.pstride + split) * PS;
+    float* part = a.partials + (static_cast<size_t>(h * G + hh) * a.pstride + pl.slot0 + split) * PS;
     float Mh = -__builtin_inff();
     for (int w = 0; w < NW; ++w) Mh = fmaxf(Mh, s_m[w][hh]);
     float v = 0.f;
@@ -1165,8 +1197,8 @@ struct StepSmem {
 // the append of the step's position (the key role, then the value role of
 // kvq_append.h, which also copy the open group to a record in this
 // workgroup's shared memory), then
-// the open group's partial for every query head i of the KV head, as partial
-// a.splits of the head in the partitions' form: scores
+// the open group's partial for every query head i of the KV head, as the
+// session's last partial slot (`slot`) in the partitions' form: scores
 // s_t = scale log2(e) <q_rot_i, k_hat_t> with k_hat = (HI + LO) / 2 +
 // level (HI - LO) / 2, reference max M = max_t s_t, denominator
 // sum_t 2^(s_t - M), per modality m the sums of the weights 2^(s_t - M) N_t
@@ -1175,7 +1207,7 @@ struct StepSmem {
 // threads call it.
 template <int D, bool BF16>
 __device__ __forceinline__ void step_append_open_group(const DecodeArgs& a, const AppendArgs& ap, StepSmem<D>& sm,
-                                                       int h, int b) {
+                                                       int h, int b, int slot) {
   constexpr int NT = kSwWaves * 64;
   constexpr int OQ = D / 16;                      // scores: channels per thread, 16 threads per position
   constexpr int VG = NT / D;                      // values: threads per channel (query heads dealt round robin)
@@ -1237,7 +1269,7 @@ __device__ __forceinline__ void step_append_open_group(const DecodeArgs& a, cons
     for (int m = 0; m < kModalities; ++m)
       if (__any(e > 0.f && md == m)) mk |= 1 << m;
     if (lane < kGroupTokens) sm.w[wave][t] = e * sm.nrm[t];
-    float* part = a.partials + ((static_cast<size_t>(b) * a.hq + h * G + wave) * a.pstride + a.splits) * PS;
+    float* part = a.partials + (static_cast<size_t>(h * G + wave) * a.pstride + slot) * PS;
     if (lane < kPartialHeader)
       part[lane] = lane == 0 ? mo : lane == 1 ? lsum : lane == 2 ? __int_as_float(mk) : 0.f;
   }
@@ -1257,15 +1289,16 @@ __device__ __forceinline__ void step_append_open_group(const DecodeArgs& a, cons
 #pragma unroll
         for (int m = 0; m < kModalities; ++m) av[m] += md == m ? x : 0.f;
       }
-      float* part = a.partials + ((static_cast<size_t>(b) * a.hq + h * G + i) * a.pstride + a.splits) * PS;
+      float* part = a.partials + (static_cast<size_t>(h * G + i) * a.pstride + slot) * PS;
 #pragma unroll
       for (int m = 0; m < kModalities; ++m) part[kPartialHeader + m * D + c] = av[m];
     }
   }
 }
 
-// STEP: the fused decode step's launch.  Grid column a.splits runs the
-// step's append and the open group's partial for each (session, KV head)
+// STEP: the fused decode step's launch.  The column after each session's
+// partitions runs the step's append and the open group's partial for each
+// (session, KV head)
 // (step_append_open_group) in this kernel's shared memory; the partitions
 // rotate their own query heads (ap.rq, inputs in bf16 when BF16) and attend
 // the closed groups only, positions below 32 floor(L / 32) of the session's
@@ -1303,19 +1336,20 @@ __global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(D
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kg = lane >> 4, col = lane & 15;
-  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const Place pl = place_of(a);
+  const int split = pl.split, h = blockIdx.y, b = pl.b;
   if constexpr (STEP) {
-    if (split >= a.splits) {
+    if (split >= pl.n) {
       static_assert(NT == app::kAppendThreads, "the append's workgroup size");
-      step_append_open_group<D, BF16>(a, ap, sm.step, h, b);
+      step_append_open_group<D, BF16>(a, ap, sm.step, h, b, pl.slot0 + pl.n);
       return;
     }
   }
   const int G = a.group;
   // STEP: the closed groups only (the append rewrites the open one)
   const int L = STEP ? (session_length(a, b) & ~(kGroupTokens - 1)) : session_length(a, b);
-  const int tb = split_begin(a, split);
-  const int te = (split == a.splits - 1) ? L : min(split_begin(a, split + 1), L);
+  const int tb = pl.tb;
+  const int te = (split == pl.n - 1) ? L : min(pl.tend, L);
   const int ng = te > tb ? (te - tb + kGroupTokens - 1) / kGroupTokens : 0;   // groups of the partition
   // The groups are dealt to the wavefronts round robin: step j of wavefront
   // w is group w + NW j, so the NW wavefronts read NW adjacent blocks at a
@@ -1631,13 +1665,13 @@ __global__ __launch_bounds__(kSwWaves * 64, 1) void decode_partition_sw_kernel(D
         sum.z += t ? v[w].z : 0.f;
         sum.w += t ? v[w].w : 0.f;
       }
-      float* part = a.partials + ((static_cast<size_t>(b) * a.hq + h * G + hp2) * a.pstride + split) * PS;
+      float* part = a.partials + (static_cast<size_t>(h * G + hp2) * a.pstride + pl.slot0 + split) * PS;
       *reinterpret_cast<float4*>(part + kPartialHeader + m * D + 16 * ct + 4 * kg2) = sum;
     }
   }
   if (tid < G * kPartialHeader) {
     const int hh = tid / kPartialHeader, f = tid % kPartialHeader;
-    float* part = a.partials + ((static_cast<size_t>(b) * a.hq + h * G + hh) * a.pstride + split) * PS;
+    float* part = a.partials + (static_cast<size_t>(h * G + hh) * a.pstride + pl.slot0 + split) * PS;
     float Mh = -__builtin_inff();
     for (int w = 0; w < NW; ++w) Mh = fmaxf(Mh, s_m[w][hh]);
     float v = 0.f;
@@ -1714,9 +1748,17 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
   const int i = h * a.group + gq;
   const int hi = (key / a.hkv) * a.hq + i;         // b * Hq + i
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int S = a.pstride;
+  const int b = key / a.hkv;
+  int slot0, S;
+  if (a.ntab > 0) {
+    slot0 = a.tab_start[b];
+    S = a.tab_start[b + 1] - slot0;
+  } else {
+    slot0 = b * (a.splits + a.step);
+    S = a.splits + a.step;
+  }
   const size_t head = static_cast<size_t>(hi);
-  const float* P = a.partials + head * static_cast<size_t>(S) * PS;
+  const float* P = a.partials + (static_cast<size_t>(i) * a.pstride + slot0) * PS;
 
   // Rotation rows: row rb RR + tid / QT, columns [q JQ, (q+1) JQ) of all three R_m.
   const int rloc = tid / QT, q = tid % QT;
@@ -1871,7 +1913,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
   if constexpr (STEP) {
     // one workgroup per session advances its length (nothing else in this
     // launch reads it)
-    if (tid == 0 && item == 0 && h == 0) a.step_len[key / a.hkv] += 1;
+    if (tid == 0 && item == 0 && h == 0) a.step_len[b] += 1;
   }
   if (q == 0) {
     const float o = (l > 0.f) ? (a.chalf * acc + a.cmid * rs) * (a.value_scale / l) : 0.f;
@@ -1882,10 +1924,15 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
   }
 }
 
+// Grid of a partition launch (see the plan in DecodeArgs).
+dim3 partition_grid(int batch, const DecodeArgs& a) {
+  return a.ntab > 0 ? dim3(a.pstride, a.hkv, 1) : dim3(a.splits + a.step, a.hkv, batch);
+}
+
 template <int D, int SLOTS, int NW>
 void launch_partition(int batch, const DecodeArgs& a, hipStream_t s) {
   constexpr bool BHL = SLOTS >= 2;   // G <= 8
-  const dim3 grid(a.splits, a.hkv, batch);
+  const dim3 grid = partition_grid(batch, a);
   if (a.cmid != 0.f)
     hipLaunchKernelGGL((decode_partition_kernel<D, SLOTS, NW, true, BHL>), grid, dim3(NW * 64), 0, s, a);
   else
@@ -1894,7 +1941,7 @@ void launch_partition(int batch, const DecodeArgs& a, hipStream_t s) {
 
 template <int D, int SLOTS, int BITS>
 void launch_partition_sw_bits(int batch, const DecodeArgs& a, hipStream_t s) {
-  const dim3 grid(a.splits, a.hkv, batch);
+  const dim3 grid = partition_grid(batch, a);
   const dim3 block(kSwWaves * 64);
   if (a.key_mode == KVQ_KEYS_PER_TOKEN) {
     if (a.cmid != 0.f)
@@ -1947,7 +1994,7 @@ hipError_t launch_decode_t(int batch, const DecodeArgs& a, hipStream_t s) {
 // merge with the open group.
 template <int D, int SLOTS, bool BF16>
 void launch_step_partition(int batch, const DecodeArgs& a, const AppendArgs& ap, hipStream_t s) {
-  const dim3 grid(a.splits + 1, a.hkv, batch);
+  const dim3 grid = partition_grid(batch, a);
   hipLaunchKernelGGL((decode_partition_sw_kernel<D, SLOTS, false, false, 2, true, BF16>), grid,
                      dim3(kSwWaves * 64), 0, s, a, ap);
 }

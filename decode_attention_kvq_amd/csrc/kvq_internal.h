@@ -74,6 +74,7 @@ __host__ __device__ constexpr int stage_record_bytes(int d) { return kStageCodes
 constexpr int kDecodeWaves = 8;
 constexpr int kPartialHeader = 8;
 constexpr int kPartitionPages = 512;   // pages one partition may span (the kernel keeps their entries in LDS)
+constexpr int kPlanSessions = 128;     // sessions a per-session partition plan can describe
 
 struct DecodeArgs {
   const uint8_t* k_codes;
@@ -86,13 +87,28 @@ struct DecodeArgs {
   const float* q_rot;
   const float* rot;
   void* out;              // [B][Hq][d] fp32, or bf16 when out_bf16
-  float* partials;        // workspace: [B][Hq][pstride][kPartialHeader + 3d] partials
+  float* partials;        // workspace: [Hq][pstride][kPartialHeader + 3d] partials (query head i of every session)
   int32_t batch;
   int32_t hq, hkv, group, page_tokens, max_pages, num_pages;
-  int32_t splits;         // partitions per (session, KV head)
-  int32_t pstride;        // partials per (session, query head): splits, or splits + 1 (the fused step's open group)
-  int32_t split_tokens;   // positions of a partition, a multiple of 32 ...
-  int32_t split_extra;    // ... plus 32 for each of the first split_extra partitions
+  // Partition plan.  Session b owns partial slots (and grid columns)
+  // [start_b, start_b + n_b + step) of every query head's row of pstride
+  // slots: n_b partitions of `tokens` positions (a multiple of 32), the
+  // first `extra` of them one 32-position group longer, then (step = 1,
+  // the fused decode step) the open group's slot.  Uniform plan (ntab = 0):
+  // n_b = splits, tokens = split_tokens, extra = split_extra,
+  // start_b = b (splits + step), grid (splits + step, hkv, batch).  Per
+  // session (ntab = batch <= kPlanSessions): start_b = tab_start[b],
+  // n_b = tab_start[b + 1] - start_b - step, tokens = tab_tokens[b],
+  // extra = tab_extra[b], grid (pstride, hkv, 1).
+  int32_t splits;
+  int32_t split_tokens;
+  int32_t split_extra;
+  int32_t step;
+  int32_t pstride;
+  int32_t ntab;
+  int32_t tab_start[kPlanSessions + 1];
+  int32_t tab_tokens[kPlanSessions];
+  int32_t tab_extra[kPlanSessions];
   int32_t page_shift;     // log2(page_tokens) when it is a power of two, else -1
   int32_t blocks_per_page; // hkv * page_tokens / 32: 32-position blocks of one physical page
   int32_t offsets31;       // every cache array is below 2^31 bytes

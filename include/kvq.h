@@ -220,8 +220,10 @@ size_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t max_len);
  * result rounded to nearest even); a session with no attended position
  * gives zeros.  Pages that are not retained still count towards the plan
  * (their steps are skipped, not compacted away).
- * Plan and replay: the partition plan comes from max(seq_len_host) at the
- * call.  The kernels read the lengths from the device seq_len, so a decode
+ * Plan and replay: the partition plan comes from seq_len_host at the call
+ * (up to 128 sessions get partition counts of their own, so a ragged batch
+ * ends together; larger batches share one).  The kernels read the lengths
+ * from the device seq_len, so a decode
  * captured in a HIP graph and replayed after appends have advanced seq_len
  * on the device stays correct: the last partition of each session takes
  * every position past the plan, up to max_pages * page_tokens (the kernels
@@ -233,8 +235,8 @@ size_t kvq_decode_workspace_bytes(const kvq_config* cfg, int32_t max_len);
  * workspace must not overlap in time.
  * Errors: KVQ_ERR_INVALID (null pointers, lengths outside [0, capacity],
  * non-finite scale), KVQ_ERR_WORKSPACE, KVQ_ERR_LAUNCH, KVQ_ERR_UNSUPPORTED
- * (out_dtype not KVQ_F32 / KVQ_BF16; a session longer than 4096 partitions
- * of at most 510 pages each, i.e. 4096 * floor(510 * page_tokens / 256) *
+ * (out_dtype not KVQ_F32 / KVQ_BF16; a session longer than 4095 partitions
+ * of at most 510 pages each, i.e. 4095 * floor(510 * page_tokens / 256) *
  * 256 positions).
  */
 kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache,
@@ -298,8 +300,9 @@ kvq_status kvq_decode_step(const kvq_config* cfg, kvq_cache* cache, const kvq_pa
  * decode reads, it writes first).  Every call on one GPU shares that GPU's
  * array: calls that overlap in time on one GPU (two streams, two host
  * threads) race and give wrong results; serialise them.  The partials of a
- * decode take batch * Hq * splits * (8 + 3 d) * 4 bytes (splits from the
- * partition plan of max(seq_len_host)); larger requests return
+ * decode take Hq * P * (8 + 3 d) * 4 bytes, P the partitions of all
+ * sessions together in the plan of seq_len_host (about 256 / Hkv: one
+ * workgroup per compute unit); larger requests return
  * KVQ_ERR_SCRATCH before anything is launched.  Errors: those of
  * kvq_decode_attention except KVQ_ERR_WORKSPACE, plus KVQ_ERR_SCRATCH;
  * KVQ_ERR_LAUNCH also when the scratch address cannot be obtained.

@@ -130,7 +130,7 @@ def test_decode_and_rotate_reject_bad_arguments():
         ctypes.c_void_p(8), od, ws, nbytes, None)
     assert dec(None, need) == L.KVQ_ERR_WORKSPACE
     assert dec(ctypes.c_void_p(8), need, od=7) == L.KVQ_ERR_UNSUPPORTED          # output dtype
-    assert dec(ctypes.c_void_p(8), need - 1) == L.KVQ_ERR_WORKSPACE
+    assert dec(ctypes.c_void_p(8), 64) == L.KVQ_ERR_WORKSPACE                    # below any plan's partials
     assert dec(ctypes.c_void_p(8), need, float("nan")) == L.KVQ_ERR_INVALID
     lens[1] = 5000                                                                # beyond capacity
     assert dec(ctypes.c_void_p(8), 1 << 30) == L.KVQ_ERR_INVALID
@@ -209,7 +209,7 @@ def test_decode_step_rejects_bad_arguments_before_launch():
         return lib.kvq_decode_step(ctypes.byref(cfg), ctypes.byref(c), ctypes.byref(params) if params else None,
                                    k, v, m, q, qd, qr, ctypes.c_float(scale), out, od, ws, nbytes, None)
     assert call(ws=None) == L.KVQ_ERR_WORKSPACE
-    assert call(nbytes=need - 1) == L.KVQ_ERR_WORKSPACE
+    assert call(nbytes=64) == L.KVQ_ERR_WORKSPACE
     assert call(k=None) == L.KVQ_ERR_INVALID
     assert call(m=None) == L.KVQ_ERR_INVALID
     assert call(q=None) == L.KVQ_ERR_INVALID

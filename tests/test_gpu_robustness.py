@@ -176,3 +176,55 @@ def test_stream_read_probe_reads_every_word():
         torch.cuda.synchronize()
         got = int(np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)))
         assert got == ref, wgs
+
+
+PLAN_CASES = [
+    # (overrides, starting lengths or None): 130 sessions take the uniform
+    # plan (one partition count for all); a few very unequal sessions take
+    # partition counts of their own (the 20,000-position one gets most)
+    (dict(batch=130, len_range=(40, 400), page_tokens=64), None),
+    (dict(batch=5, len_range=(20000, 20000)), [0, 31, 19999, 700, 64]),
+]
+
+
+@pytest.mark.parametrize("kw,start", PLAN_CASES, ids=["uniform-130-sessions", "ragged-5-sessions"])
+def test_decode_and_step_across_partition_plans(kw, start):
+    """The decode and the fused step over both kinds of partition plan:
+    against the oracle attending over the GPU's codes (every session), and
+    the step against the two calls it stands for (1e-3, see
+    tests/test_gpu_step.py)."""
+    import decode_attention_kvq_amd as K
+    h = H()
+    w = generate(3, **kw)
+    B = w.cfg.batch
+    upto = [int(x) - 1 for x in w.lengths] if start is None else start
+    _say(f"plan case {kw} from {upto if start else 'lengths - 1'}")
+    cfg, params, sep = h.build(w, upto=upto)
+    _, _, fus = h.build(w, upto=upto)
+    scale = h.default_scale(w)
+    q = h.query_tensor(w)
+    q64 = O.as_f64(w.q, w.dtype)
+    # the decode over the starting lengths
+    q_rot = K.kvq_rotate_query(cfg, params, q)
+    out = K.kvq_decode_attention(cfg, sep, params, q_rot, scale).cpu().numpy().astype(np.float64)
+    ref = h.oracle_decode_over_gpu_codes(w, cfg, sep, q64, range(B), scale, threads=16)
+    err = max(float(h.normwise_rel_err(out[b], ref[b]).max()) for b in range(B) if upto[b] > 0)
+    _say(f"decode worst normwise rel err {err:.3e}")
+    assert err <= h.ATTN_TOL
+    # one step: append position upto[b] of every session
+    k = torch.cat([h._kv_tensor(w.k[b][None, upto[b]:upto[b] + 1], w.dtype) for b in range(B)])
+    v = torch.cat([h._kv_tensor(w.v[b][None, upto[b]:upto[b] + 1], w.dtype) for b in range(B)])
+    m = torch.from_numpy(np.stack([w.modality[b][upto[b]:upto[b] + 1] for b in range(B)])).cuda()
+    q_sep = K.kvq_append_and_rotate(cfg, sep, params, k, v, m, q)
+    o_sep = K.kvq_decode_attention(cfg, sep, params, q_sep, scale).cpu().numpy().astype(np.float64)
+    o_fus = K.kvq_decode_step(cfg, fus, params, k, v, m, q, scale=scale).cpu().numpy().astype(np.float64)
+    twin = max(float(h.normwise_rel_err(o_fus[b], o_sep[b]).max()) for b in range(B))
+    _say(f"step: fused vs two calls worst normwise difference {twin:.2e}")
+    assert twin <= 1e-3
+    a, c = sep.host_arrays(), fus.host_arrays()
+    for key in ("k_codes", "k_stats", "v_codes", "v_norms", "modality", "seq_len", "k_tail"):
+        np.testing.assert_array_equal(a[key], c[key], err_msg=key)
+    ref = h.oracle_decode_over_gpu_codes(w, cfg, fus, q64, range(B), scale, threads=16)
+    err = max(float(h.normwise_rel_err(o_fus[b], ref[b]).max()) for b in range(B))
+    _say(f"step worst normwise rel err {err:.3e}")
+    assert err <= h.ATTN_TOL
