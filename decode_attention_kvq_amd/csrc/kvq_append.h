@@ -10,7 +10,7 @@
 // Every decision is taken in fp64.  The statistics follow the definition's
 // operation order, so the stored fp16 LO / HI are exactly those of an fp64
 // reference; the key codes take the division once per channel and the value
-// rotation sums in a fixed order, which can only change a code whose
+// rotation sums in a fixed order (the matrix cores' own), which can only change a code whose
 // normalised value lies within a few ulps of a decision threshold.  The
 // body turns floating-point contraction off, so that no operation is fused
 // behind the code's back whatever the including file's setting (the
@@ -30,11 +30,12 @@
 // (the fused step defers this to its merge, and also copies the open group's
 // blocks, statistics, norms and modality bytes to a record in shared memory).
 //
-// Latency matters more than throughput for the common one-position append:
-// each role issues its global loads in at most two dependent rounds, 16
-// threads share one position's channels (a short fp64 transform), and the
-// statistics and the value rotation are reduced across lanes, not by one
-// thread per channel.
+// Latency matters for the common one-position append, throughput for a
+// chunk: each role issues its global loads in at most two dependent rounds,
+// 16 threads share one position's channels (a short fp64 transform), the
+// statistics are reduced across lanes, and the value rotation R_m^T v of all
+// the group's new positions runs on the fp64 matrix cores (16 x 16 tiles of
+// positions x output channels) instead of one position after another.
 #pragma once
 
 #include "kvq_common.h"
@@ -43,6 +44,8 @@
 
 namespace kvq {
 namespace app {
+
+typedef double doublex4 __attribute__((ext_vector_type(4)));
 
 constexpr int kAppendThreads = 512;
 constexpr int kPosThreads = 16;                   // threads sharing one position's channels
@@ -177,7 +180,6 @@ __device__ __forceinline__ void append_group(const AppendArgs& a, AppendSmem<D>&
   constexpr int NWORDS = CH * ESZ / 4;
   constexpr int QR = kAppendThreads / D;          // threads per channel (statistics), parts of R's rows (values)
   constexpr int TPQ = kGroupTokens / QR;          // positions per statistics thread
-  constexpr int IQ = D / QR;                      // rows of R per part
   constexpr int W = D / 8;
   static_assert(kPosThreads * kGroupTokens == kAppendThreads, "one thread per (position, slice)");
   const int tid = threadIdx.x;
@@ -451,15 +453,25 @@ __device__ __forceinline__ void append_group(const AppendArgs& a, AppendSmem<D>&
     const int ms = lane & 31;                      // this lane's modality slot
     const bool ms_fresh = ms >= s_first && ms < s_end;
     const uint32_t mod_l = a.modality_new[static_cast<size_t>(b) * a.n_new + min(max(t0 + ms - L_old, 0), a.n_new - 1)];
-    // Rotation: thread (jc, vp) sums rows [vp IQ, vp IQ + IQ) of R for output
-    // channel jc; the QR parts of a channel sit in adjacent lanes.
-    const int jc = tid / QR, vp = tid % QR, i0 = vp * IQ;
-    float rr[IQ];
-    {
-      const float* Rm = a.rot + ((static_cast<size_t>(h) * kModalities + mpre) * D + i0) * D + jc;
+    // Rotation on the fp64 matrix cores (v_mfma_f64_16x16x4f64): a tile of 16
+    // positions x 16 output channels, D[s][c] = sum_i v[s][i] R[i][c], sums
+    // over D / 4 steps of 4 rows.  Wavefront w takes channel tile w % NTC
+    // (and, with fewer channel tiles than wavefronts, position tile w / NTC);
+    // at step k lane l holds B = R[4k + l/16][16 nt + l%16] and
+    // A = v[16 mt + l%16][4k + l/16], and the tile's results
+    // D[16 mt + 4r + l/16][16 nt + l%16], r < 4.  The rows of modality mpre
+    // are loaded here, with the other round-trip-2 loads.
+    constexpr int NTC = D / 16;                    // channel tiles
+    constexpr int KS = D / 4;                      // steps of 4 rows
+    const int wv = tid >> 6;
+    const int c_out = 16 * (wv % NTC) + (lane & 15);
+    float rb[KS];
+    auto load_rot = [&](int m) {
+      const float* Rm = a.rot + (static_cast<size_t>(h) * kModalities + m) * D * D + c_out;
 #pragma unroll
-      for (int i = 0; i < IQ; ++i) rr[i] = Rm[static_cast<size_t>(i) * D];
-    }
+      for (int k = 0; k < KS; ++k) rb[k] = Rm[static_cast<size_t>(4 * k + (lane >> 4)) * D];
+    };
+    load_rot(mpre);
     const int phys = phys_of();
     const long long blk = block_of(phys);
     // Round trip 3 (needed only at the end): the group's stored value codes,
@@ -505,31 +517,36 @@ __device__ __forceinline__ void append_group(const AppendArgs& a, AppendSmem<D>&
       for (int e = tid; e < s_first * D; e += kAppendThreads)
         sm.v.code[e / D][e % D] = static_cast<uint8_t>(unpack_value_code<D>(BITS, sm.v.oldw, e / D, e % D));
 
-    // ---- r = R_m^T v, one modality at a time (the rows of modality mpre
-    // were loaded above): four interleaved partial sums over the part's rows,
-    // added in a fixed order, then the parts across lanes.
+    // ---- r = R_m^T v on the matrix cores, one modality at a time, over the
+    // position tiles that hold new positions.  Each output sums its D exact
+    // products (bf16 or fp32 times fp32) in fp64 in one fixed order whatever
+    // the tile's other rows hold (rows of positions that are not new are
+    // computed from stale data and dropped), so a position's code does not
+    // depend on how the stream was chunked.
+    const int mt_lo = s_first >> 4, mt_hi = (s_end - 1) >> 4;
+    constexpr int MT0 = NTC < 8 ? 8 / NTC : 1;     // wavefronts per channel tile
     for (int m = 0; m < kModalities; ++m) {
       if (!(mods & (1u << m))) continue;
-      if (m != mpre) {
-        const float* Rm = a.rot + ((static_cast<size_t>(h) * kModalities + m) * D + i0) * D + jc;
+      if (m != mpre) load_rot(m);
+      for (int mt = mt_lo + wv / NTC; mt <= mt_hi; mt += MT0) {
+        doublex4 acc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-        for (int i = 0; i < IQ; ++i) rr[i] = Rm[static_cast<size_t>(i) * D];
-      }
-      for (int s = s_first; s < s_end; ++s) {
-        if (sm.v.mod[s] != m) continue;
-        double acc4[4] = {0.0, 0.0, 0.0, 0.0};
+        for (int k = 0; k < KS; ++k) {
+          const double av = static_cast<double>(sm.v.v[16 * mt + (lane & 15)][4 * k + (lane >> 4)]);
+          acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av, static_cast<double>(rb[k]), acc, 0, 0, 0);
+        }
 #pragma unroll
-        for (int i = 0; i < IQ; ++i)
-          acc4[i & 3] = fma(static_cast<double>(rr[i]), static_cast<double>(sm.v.v[s][i0 + i]), acc4[i & 3]);
-        const double r = lanes_sum<QR>((acc4[0] + acc4[1]) + (acc4[2] + acc4[3]));
-        if (vp == 0) {
-          const double n = sm.v.n[s];
-          uint32_t code = 0;
-          if (n > 0.0) {
-            const double z = (a.sqrt_d * r) / n;
-            code = level_index<BITS>(a, z);
+        for (int r = 0; r < 4; ++r) {
+          const int s = 16 * mt + 4 * r + (lane >> 4);
+          if (s >= s_first && s < s_end && sm.v.mod[s] == m) {
+            const double n = sm.v.n[s];
+            uint32_t code = 0;
+            if (n > 0.0) {
+              const double z = (a.sqrt_d * acc[r]) / n;
+              code = level_index<BITS>(a, z);
+            }
+            sm.v.code[s][c_out] = static_cast<uint8_t>(code);
           }
-          sm.v.code[s][jc] = static_cast<uint8_t>(code);
         }
       }
     }
