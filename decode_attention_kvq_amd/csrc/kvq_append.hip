@@ -27,7 +27,12 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
     }
     return;   // no ticket: only the append's workgroups count
   }
-  app::append_group<D, BF16, BITS>(a, sm, s_last, blockIdx.x, blockIdx.y, blockIdx.z,
+  // The value workgroups (the longer ones: a group's rotation R_m^T v) take
+  // the first grid columns, the key workgroups the rest, so that a chunk's
+  // value work is dispatched first and the short key work fills in behind it.
+  const int half = a.append_x / 2, x = blockIdx.x;
+  const int bx = x < half ? 2 * x + 1 : 2 * (x - half);
+  app::append_group<D, BF16, BITS>(a, sm, s_last, bx, blockIdx.y, blockIdx.z,
                                    a.append_x * static_cast<int>(gridDim.y));
 }
 
