@@ -86,7 +86,8 @@ __device__ __forceinline__ uint32_t element_bits(const uint32_t (&w)[NWORDS], in
 
 template <int D>
 struct KeySmem {
-  double y[kGroupTokens][D];                      // rotated keys, one row per position
+  double y[kGroupTokens][D + 1];                  // rotated keys, one row per position (padded: the statistics
+                                                  // read one channel of 8 positions per 4 lanes)
   double lohi[2][D];                              // LO and the per-channel factor
   __align__(16) uint8_t kblk[8 * D];              // the group's 2-bit key codes (lane-major)
   uint8_t code[kGroupTokens][D];                  // 3- / 4-bit key codes, one byte each
@@ -94,7 +95,8 @@ struct KeySmem {
 
 template <int D>
 struct ValSmem {
-  float v[kGroupTokens][D];                       // new values (the inputs are exact in fp32)
+  float v[kGroupTokens][D + 1];                   // new values (the inputs are exact in fp32); rows padded so a
+                                                  // column of 16 positions spans 16 LDS banks
   double n[kGroupTokens];                         // value norms
   uint8_t code[kGroupTokens][D];                  // value codes (3- / 4-bit: also the earlier positions)
   uint8_t mod[kGroupTokens];
