@@ -38,11 +38,11 @@ L80K = 81920
 # HBM bytes of one decode launch (partition + merge kernels) at the 80K
 # workload, from two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE), each
 # scaled by what the counter reads for a plain 256 MiB device copy
-# (FETCH_SIZE x 1.9997, WRITE_SIZE x 1.0); see profiles/decode_80k_hbm_bytes.md.
+# (FETCH_SIZE x 1.9998, WRITE_SIZE x 1.0); see profiles/decode_80k_hbm_bytes.md.
 # Valid only for the decode source the counters were taken on (SHA-256 of
 # kvq_decode.hip); otherwise `traffic` is reported as null.
-DECODE_TRAFFIC = {"kvq_decode_sha256": "7c014ea6399e0561e4e09b59d99fcf0bc4e42b0ba7c973fc767cfffa0f49cd3c",
-                  "bytes": 32870366}
+DECODE_TRAFFIC = {"kvq_decode_sha256": "d429d307260c14a50838913430052a9b2bd6b89673ba8ffc7f9c18801c1dad35",
+                  "bytes": 32901595}
 
 
 def decode_traffic_bytes():
