@@ -416,6 +416,21 @@ __device__ __forceinline__ void jacobi_pair(int r, int k, int& p, int& q) {
   q = max(x, y);
 }
 
+// Block task e of the NP (NP + 1) / 2 pairs (ki, kj) with ki <= kj: rows
+// r and NP - 1 - r of that triangle (NP - r and r + 1 entries) share row r
+// of an (NP / 2) x (NP + 1) rectangle, e = (NP + 1) r + c.
+template <int NP>
+__device__ __forceinline__ void block_task(int e, int& ki, int& kj) {
+  const int r = e / (NP + 1), c = e % (NP + 1);
+  if (c < NP - r) {
+    ki = r;
+    kj = r + c;
+  } else {
+    ki = NP - 1 - r;
+    kj = ki + c - (NP - r);
+  }
+}
+
 // Barrier for LDS traffic only: the log's global stores stay in flight.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
@@ -425,9 +440,12 @@ __global__ __launch_bounds__(jacobi_threads<D>()) void calib_jacobi_kernel(const
   constexpr int NP = D / 2;
   constexpr int LD = D + 1;
   constexpr int NT = jacobi_threads<D>();
-  constexpr int NAT = NP * NP / NT;   // 2 x 2 block tasks per thread (those with ki > kj idle)
+  // 2 x 2 block tasks (ki, kj), ki <= kj: NP (NP + 1) / 2 of them, numbered
+  // densely (block_task) and dealt round robin, NAT per thread at most
+  constexpr int NTASK = NP * (NP + 1) / 2;
+  constexpr int NAT = (NTASK + NT - 1) / NT;
   constexpr int NWT = NP * D / NT;    // (pair, column) tasks of V^T per thread
-  static_assert(NWT * NT == NP * D && NAT * NT == NP * NP && NT >= D && D % NWT == 0, "tasks divide evenly");
+  static_assert(NWT * NT == NP * D && NT >= D && D % NWT == 0, "tasks divide evenly");
   constexpr double kNegligible = 0x1p-53;   // |a_pq| <= 2^-53 sqrt(|a_pp a_qq|): already diagonal to rounding
   __shared__ double A[D * LD];             // phase 1: A; phase 2: V^T (row j = column j of V)
   __shared__ double s_c[2][NP], s_s[2][NP], s_t[NP];
@@ -490,9 +508,11 @@ __global__ __launch_bounds__(jacobi_threads<D>()) void calib_jacobi_kernel(const
       double blk[NAT][4];
 #pragma unroll
       for (int u = 0; u < NAT; ++u) {
-        const int e = tid + u * NT, ki = e / NP, kj = e % NP;
-        const int pi = s_p[0][ki], qi = s_q[0][ki], pj = s_p[0][kj], qj = s_q[0][kj];
-        if (ki <= kj) {
+        const int e = tid + u * NT;
+        if (e < NTASK) {
+          int ki, kj;
+          block_task<NP>(e, ki, kj);
+          const int pi = s_p[0][ki], qi = s_q[0][ki], pj = s_p[0][kj], qj = s_q[0][kj];
           blk[u][0] = A[pi * LD + pj];
           blk[u][1] = A[pi * LD + qj];
           blk[u][2] = A[qi * LD + pj];
@@ -501,8 +521,10 @@ __global__ __launch_bounds__(jacobi_threads<D>()) void calib_jacobi_kernel(const
       }
 #pragma unroll
       for (int u = 0; u < NAT; ++u) {
-        const int e = tid + u * NT, ki = e / NP, kj = e % NP;
-        if (ki > kj) continue;
+        const int e = tid + u * NT;
+        if (e >= NTASK) continue;
+        int ki, kj;
+        block_task<NP>(e, ki, kj);
         const int pi = s_p[0][ki], qi = s_q[0][ki], pj = s_p[0][kj], qj = s_q[0][kj];
         const double a_pp = blk[u][0], a_pq = blk[u][1], a_qp = blk[u][2], a_qq = blk[u][3];
         if (ki == kj) {
@@ -540,23 +562,28 @@ __global__ __launch_bounds__(jacobi_threads<D>()) void calib_jacobi_kernel(const
 
   // ---- phase 2: V^T <- J^T V^T, replayed from the log, starting from I
   for (int e = tid; e < D * D; e += NT) A[(e / D) * LD + e % D] = (e / D == e % D) ? 1.0 : 0.0;
+  // the log is read one round ahead, so its load waits behind a round's work
+  const int rounds = sweeps * (D - 1);
+  double t_next = (tid < NP && rounds > 0) ? log[tid] : 0.0;
   for (int sweep = 0; sweep < sweeps; ++sweep) {
     for (int r = 0; r < D - 1; ++r) {
       // parameter buffers alternate with the round count (D - 1 rounds per
       // sweep is odd, so not with r): one barrier per round suffices
-      const int b = (sweep * (D - 1) + r) & 1;
+      const int round = sweep * (D - 1) + r;
+      const int b = round & 1;
       if (tid < NP) {
         const int k = tid;
         int p, q;
         jacobi_pair<D>(r, k, p, q);
-        const double t = log[(static_cast<size_t>(sweep) * (D - 1) + r) * NP + k];
+        const double t = t_next;
+        if (round + 1 < rounds) t_next = log[static_cast<size_t>(round + 1) * NP + k];
         const double c = 1.0 / sqrt(1.0 + t * t);
         s_p[b][k] = p;
         s_q[b][k] = q;
         s_c[b][k] = c;
         s_s[b][k] = t * c;
       }
-      __syncthreads();
+      lds_barrier();   // (the prefetched log load stays in flight)
       // thread = one pair, columns i0, i0 + D / NWT, ...: the pair's
       // parameters are read once per round
       constexpr int CS = D / NWT;                 // column stride
