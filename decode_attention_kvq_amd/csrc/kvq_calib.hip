@@ -7,8 +7,10 @@
 // rotation.  Calibration runs once, off the decode path; every sum below has
 // a fixed order, so results do not depend on timing.
 //
-// fp64 matrix and vector throughput are the same on this chip, so the
-// contractions (scores, covariance) run on the vector ALUs with fp64 FMAs.
+// fp64 matrix and vector peaks are the same on this chip: the scores run on
+// the vector ALUs with fp64 FMAs, the covariance (a product of staged tiles)
+// on the fp64 matrix cores, where one instruction takes 1,024 multiply-adds
+// from two operand registers per lane instead of reading them from LDS.
 #include <math.h>
 
 #include <algorithm>
@@ -22,8 +24,6 @@ namespace {
 constexpr int kCalibModalities = 3;
 constexpr int kRowChunk = 16;        // query rows whose scores a thread forms together
 constexpr int kTokBlock = 256;       // tokens per workgroup in the score kernels
-constexpr int kTile = 32;            // covariance tile (kTile x kTile entries)
-constexpr int kTileTokens = 64;      // tokens staged in LDS per covariance step
 constexpr int kJacobiSweeps = 50;    // hard cap on Jacobi sweeps
 
 // ------------------------------------------------------------ contribution
@@ -192,60 +192,96 @@ struct CovArgs {
   double* wsum;             // [hkv][3]
   double* part_mean;        // [mean_splits][hkv][3][D + 1]: sum w v (D entries), then sum w
   double* mean;             // [hkv][3][D]
-  double* part_cov;         // [S][hkv][3][D][D]
-  int32_t n, hkv, splits, split_tokens;   // covariance tiles' token splits
+  int32_t* order;           // [n]: the tokens grouped by modality (calib_group_*_kernel)
+  int32_t* counts;          // [3]: tokens per modality
+  int32_t* group_blk;       // [ceil(n / 1024)][3]: per-block counts, then starting positions
+  double* part_cov;         // [S][hkv][3][D][D], entries i <= j
+  int32_t n, hkv, splits;   // covariance: each modality's tokens in `splits` ranges
   int32_t mean_splits, mean_split_tokens;  // weighted-mean pass's token splits
 };
 
-// Partial weighted sums of one (split, KV head): thread = (phase, channel);
-// phases stride the split's tokens and are combined in phase order.
+// Eight consecutive inputs from element idx (a multiple of 8), exactly.
+template <bool VB>
+__device__ __forceinline__ void load8(const void* p, size_t idx, float (&x)[8]) {
+  if constexpr (VB) {
+    const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + idx);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  } else {
+    const float4* q = reinterpret_cast<const float4*>(static_cast<const float*>(p) + idx);
+    const float4 a = q[0], b = q[1];
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
+}
+
+// Partial weighted sums of one (split, KV head): thread = (token phase, 8
+// channels); each phase takes the split's tokens ph, ph + P, ... in
+// increasing order, and the phases are combined in phase order.
 template <int D, bool VB>
 __global__ __launch_bounds__(256) void calib_mean_part_kernel(CovArgs a) {
-  constexpr int P = 256 / D;
+  constexpr int TPR = D / 8;        // threads per token row
+  constexpr int P = 256 / TPR;      // token phases
+  constexpr int U = 4;              // tokens whose loads are issued together
   __shared__ double s_wv[P][kCalibModalities][D];
   __shared__ double s_w[P][kCalibModalities];
-  constexpr int U = 4;   // tokens whose loads are issued together
-  const int s = blockIdx.x, h = blockIdx.y;
-  const int ph = threadIdx.x / D, c = threadIdx.x % D;
+  const int s = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int ph = tid / TPR, c0 = (tid % TPR) * 8;
   const int t0 = s * a.mean_split_tokens, t1 = min(a.n, t0 + a.mean_split_tokens);
-  double wv[kCalibModalities] = {0.0, 0.0, 0.0}, ws[kCalibModalities] = {0.0, 0.0, 0.0};
+  double wv[kCalibModalities][8], ws[kCalibModalities];
+#pragma unroll
+  for (int m = 0; m < kCalibModalities; ++m) {
+    ws[m] = 0.0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) wv[m][i] = 0.0;
+  }
   for (int tb = t0 + ph; tb < t1; tb += U * P) {
     int md[U];
-    double wt[U], x[U];
+    double wt[U];
+    float x[U][8];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = tb + u * P;
       const bool in = t < t1;
-      md[u] = in ? a.modality[t] : 3;
-      wt[u] = in ? a.weights[static_cast<size_t>(h) * a.n + t] : 0.0;
-      x[u] = in ? load_input<VB>(a.v, (static_cast<size_t>(t) * a.hkv + h) * D + c) : 0.0;
+      const int tt = in ? t : t0;
+      md[u] = in ? a.modality[tt] : 3;
+      wt[u] = a.weights[static_cast<size_t>(h) * a.n + tt];
+      load8<VB>(a.v, (static_cast<size_t>(tt) * a.hkv + h) * D + c0, x[u]);
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {   // tokens in increasing order
-      if (md[u] == 0) { wv[0] = __builtin_fma(wt[u], x[u], wv[0]); ws[0] += wt[u]; }
-      else if (md[u] == 1) { wv[1] = __builtin_fma(wt[u], x[u], wv[1]); ws[1] += wt[u]; }
-      else if (md[u] == 2) { wv[2] = __builtin_fma(wt[u], x[u], wv[2]); ws[2] += wt[u]; }
-    }
+    for (int u = 0; u < U; ++u)   // tokens in increasing order
+#pragma unroll
+      for (int m = 0; m < kCalibModalities; ++m) {
+        const bool take = md[u] == m;
+        ws[m] = take ? ws[m] + wt[u] : ws[m];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          wv[m][i] = take ? __builtin_fma(wt[u], static_cast<double>(x[u][i]), wv[m][i]) : wv[m][i];
+      }
   }
 #pragma unroll
-  for (int m = 0; m < kCalibModalities; ++m) s_wv[ph][m][c] = wv[m];
-  if (c == 0)
+  for (int m = 0; m < kCalibModalities; ++m)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s_wv[ph][m][c0 + i] = wv[m][i];
+  if (c0 == 0)
 #pragma unroll
     for (int m = 0; m < kCalibModalities; ++m) s_w[ph][m] = ws[m];
   __syncthreads();
-  if (ph == 0) {
-    double* out = a.part_mean + (static_cast<size_t>(s) * a.hkv + h) * kCalibModalities * (D + 1);
-#pragma unroll
-    for (int m = 0; m < kCalibModalities; ++m) {
-      double x = s_wv[0][m][c];
-      for (int p = 1; p < P; ++p) x += s_wv[p][m][c];
-      out[m * (D + 1) + c] = x;
-      if (c == 0) {
-        double w = s_w[0][m];
-        for (int p = 1; p < P; ++p) w += s_w[p][m];
-        out[m * (D + 1) + D] = w;
-      }
-    }
+  double* out = a.part_mean + (static_cast<size_t>(s) * a.hkv + h) * kCalibModalities * (D + 1);
+  for (int e = tid; e < kCalibModalities * D; e += 256) {
+    const int m = e / D, c = e % D;
+    double x = s_wv[0][m][c];
+    for (int p = 1; p < P; ++p) x += s_wv[p][m][c];
+    out[m * (D + 1) + c] = x;
+  }
+  if (tid < kCalibModalities) {
+    double w = s_w[0][tid];
+    for (int p = 1; p < P; ++p) w += s_w[p][tid];
+    out[tid * (D + 1) + D] = w;
   }
 }
 
@@ -278,112 +314,304 @@ __global__ __launch_bounds__(256) void calib_mean_merge_kernel(CovArgs a) {
   if (c == 0) a.wsum[hm] = sw;
 }
 
-// Partial covariance tile of one (split, KV head): entries (i, j) of tile
-// (bi, bj), bi <= bj, for the three modalities.  Each term is w * (x_i x_j)
-// with the product of the centred values formed first, so entry (j, i) of a
-// diagonal tile, formed by another thread, is the same number; off-diagonal
-// tiles are written to both halves.  Thread = 2 x 2 entries.
-template <int D, bool VB>
-__global__ __launch_bounds__(256) void calib_cov_part_kernel(CovArgs a) {
-  constexpr int NB = D / kTile;
-  __shared__ double xi[kTileTokens][kTile + 1];
-  __shared__ double xj[kTileTokens][kTile + 1];
-  __shared__ double s_w[kTileTokens];
-  __shared__ int s_md[kTileTokens];
-  __shared__ double s_mean[kCalibModalities][2][kTile];
-  // tile index -> (bi, bj) with bi <= bj
-  int tile = blockIdx.x, bi = 0;
-  while (tile >= NB - bi) {
-    tile -= NB - bi;
+// The calibration tokens grouped by modality, for the covariance: `order`
+// lists the tokens of modality 0 in increasing order, then those of 1, then
+// those of 2 (tokens with another modality byte are left out), and counts[m]
+// is the number of tokens of modality m.  Three launches over blocks of
+// 1,024 tokens: each block counts its tokens per modality; one workgroup
+// turns the counts into each block's starting position per modality; each
+// block writes its tokens there, ranked within the block by wavefront
+// ballots (lanes in token order, wavefronts in order).
+constexpr int kGroupThreads = 1024;
+constexpr int kGroupWaves = kGroupThreads / 64;
+
+__device__ __forceinline__ int group_modality(const CovArgs& a, int t) {
+  return t < a.n ? a.modality[t] : kCalibModalities;
+}
+
+__global__ __launch_bounds__(kGroupThreads) void calib_group_count_kernel(CovArgs a) {
+  __shared__ int s_c[kGroupWaves][kCalibModalities];
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m = group_modality(a, b * kGroupThreads + tid);
+#pragma unroll
+  for (int k = 0; k < kCalibModalities; ++k) {
+    const int c = __popcll(__ballot(m == k));
+    if (lane == 0) s_c[wave][k] = c;
+  }
+  __syncthreads();
+  if (tid < kCalibModalities) {
+    int c = 0;
+    for (int w = 0; w < kGroupWaves; ++w) c += s_c[w][tid];
+    a.group_blk[static_cast<size_t>(b) * kCalibModalities + tid] = c;
+  }
+}
+
+// Block counts -> starting positions (in place), and counts[m].
+__global__ __launch_bounds__(kGroupThreads) void calib_group_scan_kernel(CovArgs a, int nblk) {
+  __shared__ int s_sc[kCalibModalities][kGroupThreads];
+  __shared__ int s_base[kCalibModalities];
+  const int tid = threadIdx.x;
+  int tot[kCalibModalities] = {0, 0, 0};
+  for (int b = tid; b < nblk; b += kGroupThreads)
+#pragma unroll
+    for (int k = 0; k < kCalibModalities; ++k) tot[k] += a.group_blk[static_cast<size_t>(b) * kCalibModalities + k];
+  // inclusive scans of s_sc[k][0 ..) over the threads (Hillis-Steele)
+  auto scan = [&](const int (&c)[kCalibModalities]) {
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kCalibModalities; ++k) s_sc[k][tid] = c[k];
+    __syncthreads();
+    for (int off = 1; off < kGroupThreads; off <<= 1) {
+      int v[kCalibModalities];
+#pragma unroll
+      for (int k = 0; k < kCalibModalities; ++k) v[k] = tid >= off ? s_sc[k][tid - off] : 0;
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < kCalibModalities; ++k) s_sc[k][tid] += v[k];
+      __syncthreads();
+    }
+  };
+  scan(tot);
+  if (tid < kCalibModalities) a.counts[tid] = s_sc[tid][kGroupThreads - 1];
+  if (tid == 0) {
+    s_base[0] = 0;
+    s_base[1] = s_sc[0][kGroupThreads - 1];
+    s_base[2] = s_sc[0][kGroupThreads - 1] + s_sc[1][kGroupThreads - 1];
+  }
+  __syncthreads();
+  int carry[kCalibModalities] = {s_base[0], s_base[1], s_base[2]};
+  for (int b0 = 0; b0 < nblk; b0 += kGroupThreads) {
+    const int b = b0 + tid;
+    int c[kCalibModalities];
+#pragma unroll
+    for (int k = 0; k < kCalibModalities; ++k) c[k] = b < nblk ? a.group_blk[static_cast<size_t>(b) * kCalibModalities + k] : 0;
+    scan(c);
+    if (b < nblk)
+#pragma unroll
+      for (int k = 0; k < kCalibModalities; ++k)
+        a.group_blk[static_cast<size_t>(b) * kCalibModalities + k] = carry[k] + s_sc[k][tid] - c[k];
+#pragma unroll
+    for (int k = 0; k < kCalibModalities; ++k) carry[k] += s_sc[k][kGroupThreads - 1];
+  }
+}
+
+__global__ __launch_bounds__(kGroupThreads) void calib_group_scatter_kernel(CovArgs a) {
+  __shared__ int s_c[kGroupWaves][kCalibModalities];
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t = b * kGroupThreads + tid;
+  const int m = group_modality(a, t);
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int rank = 0;
+#pragma unroll
+  for (int k = 0; k < kCalibModalities; ++k) {
+    const uint64_t mk = __ballot(m == k);
+    if (m == k) rank = __popcll(mk & below);
+    if (lane == 0) s_c[wave][k] = __popcll(mk);
+  }
+  __syncthreads();
+  if (m < kCalibModalities) {
+    int at = a.group_blk[static_cast<size_t>(b) * kCalibModalities + m] + rank;
+    for (int w = 0; w < wave; ++w) at += s_c[w][m];
+    a.order[at] = t;
+  }
+}
+
+// Partial covariances of one (split s, KV head h) on the fp64 matrix cores,
+// modality by modality: range s of modality m's tokens (`order`, each
+// modality's list cut into `splits` ranges of a multiple of 4 tokens, so
+// every workgroup gets the same share of every modality) goes through LDS
+// 64 tokens at a time, and every 4 tokens are one k-step of
+// v_mfma_f64_16x16x4f64 per 16 x 16 tile of the upper triangle:
+// C[i][j] += sum_t (w_t x_ti) x_tj with x = v - mu_m (A: lane l holds
+// token l / 16, channel i = l % 16 of the tile's rows; B the same token and
+// column channel; x staged in LDS as fp64, centred once; D element r of lane l is entry (4 r + l / 16, l % 16)).
+// The 36 (d = 128) or 10 (d = 64) tiles are dealt to 12 or 10 wavefronts,
+// three or one each.
+// Entries i <= j are stored; the merge mirrors them, so the result is
+// exactly symmetric.  Each k-step adds its products in the matrix core's
+// fixed order, k-steps in token order: the result depends only on the
+// inputs and the plan.
+typedef double calib_dx4 __attribute__((ext_vector_type(4)));
+constexpr int kCovChunk = 64;   // tokens staged per step
+
+template <int D>
+struct CovShape {
+  static constexpr int NB = D / 16;                 // 16-channel blocks
+  static constexpr int NTL = NB * (NB + 1) / 2;     // tiles (bi <= bj): 36 or 10
+  static constexpr int TPW = D == 128 ? 3 : 1;      // tiles per wavefront, the same for all
+  static constexpr int NWV = NTL / TPW;             // wavefronts: 12 or 10
+  static constexpr int NT = NWV * 64;
+  static constexpr int LDX = D + 16;                // staged row stride in doubles: rows 4k, 4k + 1
+                                                    // of a k-step (one half-wavefront) use disjoint banks
+  static constexpr int PPR = D / 8;                 // staging pieces (8 channels) per token row
+  static constexpr int NPC = (kCovChunk * PPR + NT - 1) / NT;   // pieces per thread at most
+};
+
+// Tile e of the NB (NB + 1) / 2 upper-triangle 16 x 16 tiles, row-major.
+template <int NB>
+__device__ __forceinline__ void cov_tile(int e, int& bi, int& bj) {
+  bi = 0;
+  while (e >= NB - bi) {
+    e -= NB - bi;
     ++bi;
   }
-  const int bj = bi + tile;
-  const int s = blockIdx.y, h = blockIdx.z;
-  const int tid = threadIdx.x;
-  const int ti = tid / 16, tj = tid % 16;
-  const int t0 = s * a.split_tokens, t1 = min(a.n, t0 + a.split_tokens);
-  if (tid < kCalibModalities * 2 * kTile) {
-    const int m = tid / (2 * kTile), side = (tid / kTile) & 1, cc = tid % kTile;
-    const int ch = (side ? bj : bi) * kTile + cc;
-    s_mean[m][side][cc] = a.mean[(static_cast<size_t>(h) * kCalibModalities + m) * D + ch];
-  }
-  double acc0[4] = {0.0, 0.0, 0.0, 0.0}, acc1[4] = {0.0, 0.0, 0.0, 0.0}, acc2[4] = {0.0, 0.0, 0.0, 0.0};
-  for (int base = t0; base < t1; base += kTileTokens) {
-    __syncthreads();
-    if (tid < kTileTokens) {
-      const int t = base + tid;
-      int m = 3;
-      double w = 0.0;
-      if (t < t1) {
-        m = a.modality[t];
-        w = a.weights[static_cast<size_t>(h) * a.n + t];
-      }
-      s_md[tid] = m < kCalibModalities ? m : 3;
-      s_w[tid] = w;
-    }
-    __syncthreads();
-    for (int e = tid; e < kTileTokens * kTile; e += 256) {
-      const int tt = e / kTile, cc = e % kTile;
-      const int t = base + tt;
-      const int m = s_md[tt];
-      double vi = 0.0, vj = 0.0;
-      if (m < kCalibModalities) {
-        const size_t row = (static_cast<size_t>(t) * a.hkv + h) * D;
-        vi = load_input<VB>(a.v, row + bi * kTile + cc) - s_mean[m][0][cc];
-        vj = load_input<VB>(a.v, row + bj * kTile + cc) - s_mean[m][1][cc];
-      }
-      xi[tt][cc] = vi;
-      xj[tt][cc] = vj;
-    }
-    __syncthreads();
-    const int nt = min(kTileTokens, t1 - base);
-    for (int tt = 0; tt < nt; ++tt) {
-      const int m = s_md[tt];
-      if (m >= kCalibModalities) continue;
-      const double w = s_w[tt];
-      const double a0 = xi[tt][2 * ti], a1 = xi[tt][2 * ti + 1];
-      const double b0 = xj[tt][2 * tj], b1 = xj[tt][2 * tj + 1];
-      const double p00 = a0 * b0, p01 = a0 * b1, p10 = a1 * b0, p11 = a1 * b1;
-      if (m == 0) {
-        acc0[0] = __builtin_fma(w, p00, acc0[0]); acc0[1] = __builtin_fma(w, p01, acc0[1]);
-        acc0[2] = __builtin_fma(w, p10, acc0[2]); acc0[3] = __builtin_fma(w, p11, acc0[3]);
-      } else if (m == 1) {
-        acc1[0] = __builtin_fma(w, p00, acc1[0]); acc1[1] = __builtin_fma(w, p01, acc1[1]);
-        acc1[2] = __builtin_fma(w, p10, acc1[2]); acc1[3] = __builtin_fma(w, p11, acc1[3]);
-      } else {
-        acc2[0] = __builtin_fma(w, p00, acc2[0]); acc2[1] = __builtin_fma(w, p01, acc2[1]);
-        acc2[2] = __builtin_fma(w, p10, acc2[2]); acc2[3] = __builtin_fma(w, p11, acc2[3]);
-      }
-    }
-  }
-  const int i0 = bi * kTile + 2 * ti, j0 = bj * kTile + 2 * tj;
-  auto store = [&](int m, double x00, double x01, double x10, double x11) {
-    double* out = a.part_cov + ((static_cast<size_t>(s) * a.hkv + h) * kCalibModalities + m) * D * D;
-    const double x[4] = {x00, x01, x10, x11};
+  bj = bi + e;
+}
+
+template <int D, bool VB>
+__global__ __launch_bounds__(CovShape<D>::NT) void calib_cov_part_kernel(CovArgs a) {
+  using S = CovShape<D>;
+  constexpr int TPW = S::TPW;
+  constexpr int NT = S::NT;
+  static_assert(S::NWV * TPW == S::NTL, "every wavefront takes TPW tiles");
+  __shared__ double xs[kCovChunk][S::LDX];   // centred values x = v - mu_m of the chunk's tokens
+  __shared__ double s_w[kCovChunk];
+  __shared__ double s_mu[D];
+  const int s = blockIdx.x, h = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // the wavefront's tiles TPW wave .. TPW wave + TPW - 1: LDS offsets of this
+  // lane's channel in the tile's row and column blocks (a diagonal tile reads
+  // the same channel twice: no branch in the loop)
+  int ci[TPW], cj[TPW], bi[TPW], bj[TPW];
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+  for (int u = 0; u < TPW; ++u) {
+    cov_tile<S::NB>(TPW * wave + u, bi[u], bj[u]);
+    ci[u] = 16 * bi[u] + (lane & 15);
+    cj[u] = 16 * bj[u] + (lane & 15);
+  }
+  // staging: piece p = (token row p / PPR, channels 8 (p % PPR) ..) for
+  // p = tid, tid + NT, ...; the raw 16-byte words of the next chunk are
+  // loaded while this one is used (and waited for only when staged), its
+  // token indices one chunk earlier still
+  constexpr int EB = VB ? 2 : 4;                 // bytes per input element
+  constexpr int WPP = 8 * EB / 16;               // 16-byte words per piece
+  uint4 xr[S::NPC][WPP];
+  double wr[S::NPC];
+  bool vr[S::NPC];
+  int tn[S::NPC];
+  auto piece_ok = [&](int k) { return tid + k * NT < kCovChunk * S::PPR; };
+  auto fetch = [&]() {
 #pragma unroll
-      for (int v = 0; v < 2; ++v) {
-        out[static_cast<size_t>(i0 + u) * D + j0 + v] = x[2 * u + v];
-        if (bi != bj) out[static_cast<size_t>(j0 + v) * D + i0 + u] = x[2 * u + v];
-      }
+    for (int k = 0; k < S::NPC; ++k) {
+      const int p = tid + k * NT;
+      const int t = piece_ok(k) ? tn[k] : -1;
+      const int tt = t >= 0 ? t : 0;
+      const uint4* src = reinterpret_cast<const uint4*>(
+          static_cast<const char*>(a.v) + ((static_cast<size_t>(tt) * a.hkv + h) * D + 8 * (p % S::PPR)) * EB);
+#pragma unroll
+      for (int q = 0; q < WPP; ++q) xr[k][q] = src[q];
+      wr[k] = a.weights[static_cast<size_t>(h) * a.n + tt];
+      vr[k] = t >= 0;
+    }
   };
-  store(0, acc0[0], acc0[1], acc0[2], acc0[3]);
-  store(1, acc1[0], acc1[1], acc1[2], acc1[3]);
-  store(2, acc2[0], acc2[1], acc2[2], acc2[3]);
+
+  int off = 0;
+  for (int m = 0; m < kCalibModalities; ++m) {
+    const int cnt = a.counts[m];
+    const int64_t per = ((static_cast<int64_t>(cnt) + a.splits - 1) / a.splits + 3) & ~static_cast<int64_t>(3);
+    const int r0 = static_cast<int>(min(static_cast<int64_t>(cnt), s * per));
+    const int r1 = static_cast<int>(min(static_cast<int64_t>(cnt), r0 + per));
+    auto tokens = [&](int base) {   // token of each of the thread's pieces in the chunk at base
+#pragma unroll
+      for (int k = 0; k < S::NPC; ++k) {
+        const int r = base + (tid + k * NT) / S::PPR;
+        tn[k] = r < r1 ? a.order[static_cast<size_t>(off) + r] : -1;
+      }
+    };
+    calib_dx4 acc[TPW];
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) acc[u] = calib_dx4{0.0, 0.0, 0.0, 0.0};
+    __syncthreads();   // the previous modality's staging has read s_mu
+    if (tid < D) s_mu[tid] = a.mean[(static_cast<size_t>(h) * kCalibModalities + m) * D + tid];
+    if (r0 < r1) {
+      tokens(r0);
+      fetch();
+      tokens(r0 + kCovChunk);
+    }
+    for (int base = r0; base < r1; base += kCovChunk) {
+      __syncthreads();   // s_mu is set; the previous chunk's reads are done
+#pragma unroll
+      for (int k = 0; k < S::NPC; ++k) {
+        if (!piece_ok(k)) continue;
+        const int p = tid + k * NT, row = p / S::PPR, c0 = 8 * (p % S::PPR);
+        const uint32_t* wd = reinterpret_cast<const uint32_t*>(xr[k]);
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {
+          float f0, f1;
+          if constexpr (VB) {
+            f0 = __uint_as_float(wd[i / 2] << 16);
+            f1 = __uint_as_float(wd[i / 2] & 0xFFFF0000u);
+          } else {
+            f0 = __uint_as_float(wd[i]);
+            f1 = __uint_as_float(wd[i + 1]);
+          }
+          const double x0 = vr[k] ? static_cast<double>(f0) - s_mu[c0 + i] : 0.0;
+          const double x1 = vr[k] ? static_cast<double>(f1) - s_mu[c0 + i + 1] : 0.0;
+          *reinterpret_cast<double2*>(&xs[row][c0 + i]) = double2{x0, x1};
+        }
+        if (p % S::PPR == 0) s_w[row] = vr[k] ? wr[k] : 0.0;
+      }
+      __syncthreads();
+      if (base + kCovChunk < r1) {
+        fetch();
+        tokens(base + 2 * kCovChunk);
+      }
+      const int nks = (min(kCovChunk, r1 - base) + 3) / 4;
+      for (int ks = 0; ks < nks; ++ks) {
+        const int tok = 4 * ks + (lane >> 4);
+        const double w = s_w[tok];
+        const double* row = xs[tok];
+        double xa[TPW], xb[TPW];
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+          xa[u] = row[ci[u]];
+          xb[u] = row[cj[u]];
+        }
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) acc[u] = __builtin_amdgcn_mfma_f64_16x16x4f64(w * xa[u], xb[u], acc[u], 0, 0, 0);
+      }
+    }
+    double* out = a.part_cov + ((static_cast<size_t>(s) * a.hkv + h) * kCalibModalities + m) * D * D;
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int ii = 4 * r + (lane >> 4), jj = lane & 15;
+        if (bi[u] != bj[u] || ii <= jj) out[static_cast<size_t>(16 * bi[u] + ii) * D + 16 * bj[u] + jj] = acc[u][r];
+      }
+    }
+    off += cnt;
+  }
 }
 
 // Covariances: the splits' partial sums in split order, divided by W.
+// Thread (i, j), i <= j, reads the stored entry (its row, so the reads of a
+// wavefront are contiguous) and writes entries (i, j) and (j, i).
 template <int D>
 __global__ __launch_bounds__(256) void calib_cov_merge_kernel(CovArgs a) {
   const size_t e = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
   const size_t per = static_cast<size_t>(D) * D;
   if (e >= static_cast<size_t>(a.hkv) * kCalibModalities * per) return;
   const size_t hm = e / per;
+  const int i = static_cast<int>(e % per) / D, j = static_cast<int>(e % per) % D;
+  if (i > j) return;
+  const double* p = a.part_cov + e;
+  const size_t stride = static_cast<size_t>(a.hkv) * kCalibModalities * per;
+  constexpr int U = 8;   // splits whose partial sums are loaded together
   double x = 0.0;
-  for (int s = 0; s < a.splits; ++s) x += a.part_cov[static_cast<size_t>(s) * a.hkv * kCalibModalities * per + e];
+  for (int s0 = 0; s0 < a.splits; s0 += U) {
+    double v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = s0 + u < a.splits ? p[(s0 + u) * stride] : 0.0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) x += v[u];   // splits in increasing order
+  }
   const double w = a.wsum[hm];
-  a.cov[e] = w > 0.0 ? x / w : 0.0;
+  const double c = w > 0.0 ? x / w : 0.0;
+  a.cov[e] = c;
+  a.cov[hm * per + static_cast<size_t>(j) * D + i] = c;
 }
 
 // -------------------------------------------------------------- eigenbasis
@@ -632,7 +860,7 @@ __global__ __launch_bounds__(jacobi_threads<D>()) void calib_jacobi_kernel(const
 
 struct CalibPlan {
   int rows, nblk;          // contribution
-  int splits, split_tokens;  // covariance tiles
+  int splits;               // covariance: token ranges per modality
   int mean_splits, mean_split_tokens;  // weighted means: 1024 tokens per split
   size_t contrib_bytes, cov_bytes, eig_bytes;
 };
@@ -657,21 +885,17 @@ CalibPlan plan_calib(const kvq_calib_shape* s) {
   p.nblk = std::max(1, (n + kTokBlock - 1) / kTokBlock);
   p.contrib_bytes = align256(static_cast<size_t>(hkv) * p.nblk * p.rows * 2 * sizeof(double)) +
                     align256(static_cast<size_t>(hkv) * p.rows * 2 * sizeof(double));
-  // covariance: about 512 workgroups, at least 256 tokens per split, at most 64 splits
-  const int nb = d / kTile;
-  const int tiles = nb * (nb + 1) / 2;
-  int splits = std::max(1, (512 + tiles * hkv - 1) / (tiles * hkv));
+  // covariance: each modality's tokens in `splits` ranges, one workgroup per
+  // (range, KV head) for all three modalities: at most 256 workgroups (one
+  // per CU), about 256 tokens per workgroup at least
+  int splits = std::max(1, 256 / hkv);
   splits = std::min(splits, std::max(1, (n + 255) / 256));
-  splits = std::min(splits, 64);
-  int per = (std::max(n, 1) + splits - 1) / splits;
-  per = ((per + kTileTokens - 1) / kTileTokens) * kTileTokens;
-  splits = std::max(1, (n + per - 1) / per);
   p.splits = splits;
-  p.split_tokens = per;
   p.mean_split_tokens = 1024;
   p.mean_splits = std::max(1, (n + 1023) / 1024);
   p.cov_bytes = align256(static_cast<size_t>(p.mean_splits) * hkv * kCalibModalities * (d + 1) * sizeof(double)) +
                 align256(static_cast<size_t>(hkv) * kCalibModalities * d * sizeof(double)) +
+                align256((static_cast<size_t>(n) + 4 + 3 * (static_cast<size_t>(n) / 1024 + 1)) * sizeof(int32_t)) +
                 align256(static_cast<size_t>(splits) * hkv * kCalibModalities * d * d * sizeof(double));
   p.eig_bytes = static_cast<size_t>(3) * hkv * kJacobiSweeps * (d - 1) * (d / 2) * sizeof(double);
   return p;
@@ -695,20 +919,24 @@ void launch_contribution(const ContribArgs& a, bool kb, bool qb, hipStream_t st)
 
 template <int D>
 void launch_covariance(const CovArgs& a, bool vb, hipStream_t st) {
-  constexpr int NB = D / kTile;
   const dim3 gpart(a.mean_splits, a.hkv);
   const dim3 gmm((a.hkv * kCalibModalities * D + 255) / 256);
-  const dim3 gtile(NB * (NB + 1) / 2, a.splits, a.hkv);
+  const dim3 gcov(a.splits, a.hkv);
+  constexpr int cov_threads = CovShape<D>::NT;
   const size_t ncov = static_cast<size_t>(a.hkv) * kCalibModalities * D * D;
   const dim3 gcm(static_cast<unsigned>((ncov + 255) / 256));
+  const int nblk = std::max(1, (a.n + kGroupThreads - 1) / kGroupThreads);
+  hipLaunchKernelGGL(calib_group_count_kernel, dim3(nblk), dim3(kGroupThreads), 0, st, a);
+  hipLaunchKernelGGL(calib_group_scan_kernel, dim3(1), dim3(kGroupThreads), 0, st, a, nblk);
+  hipLaunchKernelGGL(calib_group_scatter_kernel, dim3(nblk), dim3(kGroupThreads), 0, st, a);
   if (vb) {
     hipLaunchKernelGGL((calib_mean_part_kernel<D, true>), gpart, dim3(256), 0, st, a);
     hipLaunchKernelGGL((calib_mean_merge_kernel<D>), gmm, dim3(256), 0, st, a);
-    hipLaunchKernelGGL((calib_cov_part_kernel<D, true>), gtile, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((calib_cov_part_kernel<D, true>), gcov, dim3(cov_threads), 0, st, a);
   } else {
     hipLaunchKernelGGL((calib_mean_part_kernel<D, false>), gpart, dim3(256), 0, st, a);
     hipLaunchKernelGGL((calib_mean_merge_kernel<D>), gmm, dim3(256), 0, st, a);
-    hipLaunchKernelGGL((calib_cov_part_kernel<D, false>), gtile, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((calib_cov_part_kernel<D, false>), gcov, dim3(cov_threads), 0, st, a);
   }
   hipLaunchKernelGGL((calib_cov_merge_kernel<D>), gcm, dim3(256), 0, st, a);
 }
@@ -772,6 +1000,7 @@ kvq_status kvq_calib_covariance(const kvq_calib_shape* shape, const void* v, int
   if (!dtype_ok(v_dtype)) return KVQ_ERR_UNSUPPORTED;
   if (!cov || !weight_sum) return KVQ_ERR_INVALID;
   if (shape->n_tokens > 0 && (!v || !modality || !weights)) return KVQ_ERR_INVALID;
+  if (reinterpret_cast<uintptr_t>(v) % 16 != 0) return KVQ_ERR_INVALID;   // read in 16-byte pieces
   const CalibPlan p = plan_calib(shape);
   if (!workspace || workspace_bytes < p.cov_bytes) return KVQ_ERR_WORKSPACE;
   const int d = shape->head_dim, hkv = shape->n_kv_heads;
@@ -786,11 +1015,15 @@ kvq_status kvq_calib_covariance(const kvq_calib_shape* shape, const void* v, int
   w += align256(static_cast<size_t>(p.mean_splits) * hkv * kCalibModalities * (d + 1) * sizeof(double));
   a.mean = reinterpret_cast<double*>(w);
   w += align256(static_cast<size_t>(hkv) * kCalibModalities * d * sizeof(double));
+  a.counts = reinterpret_cast<int32_t*>(w);
+  a.order = a.counts + 4;
+  a.group_blk = a.order + shape->n_tokens;
+  w += align256((static_cast<size_t>(shape->n_tokens) + 4 + 3 * (static_cast<size_t>(shape->n_tokens) / 1024 + 1)) *
+                sizeof(int32_t));
   a.part_cov = reinterpret_cast<double*>(w);
   a.n = shape->n_tokens;
   a.hkv = hkv;
   a.splits = p.splits;
-  a.split_tokens = p.split_tokens;
   a.mean_splits = p.mean_splits;
   a.mean_split_tokens = p.mean_split_tokens;
   (void)hipGetLastError();

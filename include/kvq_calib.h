@@ -72,12 +72,12 @@ kvq_status kvq_calib_contribution(const kvq_calib_shape* shape, const void* k, i
  * kvq_calib_covariance - the weighted covariance of each (KV head,
  * modality) (Sec. 2 Method, value bullet: a covariance computed separately
  * per modality).
- * v: device [n][Hkv][d] in v_dtype; modality: device [n] uint8; weights:
+ * v: device [n][Hkv][d] in v_dtype, 16-byte aligned; modality: device [n] uint8; weights:
  * device [Hkv][n] fp64 (e.g. from kvq_calib_contribution); cov: device
  * [Hkv][3][d][d] fp64 output, exactly symmetric; weight_sum: device [Hkv][3]
  * fp64 output (W per modality).
- * Errors: KVQ_ERR_INVALID, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE,
- * KVQ_ERR_LAUNCH.
+ * Errors: KVQ_ERR_INVALID (null pointer, bad shape, v not 16-byte aligned),
+ * KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE, KVQ_ERR_LAUNCH.
  */
 kvq_status kvq_calib_covariance(const kvq_calib_shape* shape, const void* v, int32_t v_dtype,
                                 const uint8_t* modality, const double* weights, double* cov,

@@ -264,11 +264,12 @@ def test_calibration_rejects_bad_arguments_without_launching():
     assert con(nbytes=16) == L.KVQ_ERR_WORKSPACE
     assert con(shape=shape(n_tokens=0), k=None, q=None, w=None) == L.KVQ_OK      # nothing to do
     cov = lambda **kw: lib.kvq_calib_covariance(
-        ctypes.byref(good), kw.pop("v", V(8)), kw.pop("vd", 0), kw.pop("m", V(8)), kw.pop("w", V(8)),
+        ctypes.byref(good), kw.pop("v", V(16)), kw.pop("vd", 0), kw.pop("m", V(8)), kw.pop("w", V(8)),
         kw.pop("c", V(8)), kw.pop("s", V(8)), kw.pop("ws", V(8)), kw.pop("nbytes", need), None)
     assert cov(vd=3) == L.KVQ_ERR_UNSUPPORTED
     assert cov(m=None) == L.KVQ_ERR_INVALID and cov(c=None) == L.KVQ_ERR_INVALID and cov(s=None) == L.KVQ_ERR_INVALID
     assert cov(nbytes=1) == L.KVQ_ERR_WORKSPACE
+    assert cov(v=V(24)) == L.KVQ_ERR_INVALID                                      # v read in 16-byte pieces
     eig = lambda count=6, d=128, c=V(8), r=V(8), e=V(8), ws=V(8), nbytes=need: lib.kvq_calib_eigenbasis(
         count, d, c, r, e, ws, nbytes, None)
     assert eig(count=-1) == L.KVQ_ERR_INVALID
