@@ -628,10 +628,10 @@ __global__ __launch_bounds__(256) void calib_cov_merge_kernel(CovArgs a) {
 // whose off-diagonal entry is negligible (against its diagonal, or below
 // the rounding noise of the whole matrix) is set to zero without a rotation;
 // the sweeps end when one rotates nothing (at most kJacobiSweeps).  Each
-// round's tangents t go to a log in the workspace.
+// round's rotations (c, s) go to a log in the workspace; a round that
+// rotates no pair skips the update.
 // Phase 2 replays the log on V = I (V^T kept in LDS where A was):
-// V <- V J round by round, c and s recomputed from t with the same
-// operations as in phase 1, so they are the same numbers.
+// V <- V J round by round with phase 1's own (c, s).
 template <int D>
 constexpr int jacobi_threads() { return D == 128 ? 512 : 256; }
 
@@ -676,14 +676,16 @@ __global__ __launch_bounds__(jacobi_threads<D>()) void calib_jacobi_kernel(const
   static_assert(NWT * NT == NP * D && NT >= D && D % NWT == 0, "tasks divide evenly");
   constexpr double kNegligible = 0x1p-53;   // |a_pq| <= 2^-53 sqrt(|a_pp a_qq|): already diagonal to rounding
   __shared__ double A[D * LD];             // phase 1: A; phase 2: V^T (row j = column j of V)
-  __shared__ double s_c[2][NP], s_s[2][NP], s_t[NP];
-  __shared__ int s_p[2][NP], s_q[2][NP];
+  __shared__ double2 s_cs[NP];             // (c, s) of each pair
+  __shared__ double s_t[NP];
+  __shared__ int2 s_pq[NP];                // (p, q) of each pair
   __shared__ int s_changed;
+  __shared__ int s_rot[2];                 // phase 1: the round rotates some pair
   __shared__ double s_lam[D];
   __shared__ double s_sq[NT];
   const int mat = blockIdx.x, tid = threadIdx.x;
   const double* C = cov + static_cast<size_t>(mat) * D * D;
-  double* log = work + static_cast<size_t>(mat) * kJacobiSweeps * (D - 1) * NP;
+  double2* log = reinterpret_cast<double2*>(work) + static_cast<size_t>(mat) * kJacobiSweeps * (D - 1) * NP;
   double sq = 0.0;
   for (int e = tid; e < D * D; e += NT) {
     const int i = e / D, j = e % D;
@@ -703,6 +705,7 @@ __global__ __launch_bounds__(jacobi_threads<D>()) void calib_jacobi_kernel(const
 
   // ---- phase 1: A <- J^T A J until a sweep rotates nothing
   int sweeps = 0;
+  int rc = 0;   // rounds so far (the per-round flag alternates between two slots)
   for (int sweep = 0; sweep < kJacobiSweeps; ++sweep) {
     __syncthreads();
     if (tid == 0) s_changed = 0;
@@ -724,14 +727,22 @@ __global__ __launch_bounds__(jacobi_threads<D>()) void calib_jacobi_kernel(const
           s_changed = 1;
         }
         const double c = 1.0 / sqrt(1.0 + t * t);
-        s_p[0][k] = p;
-        s_q[0][k] = q;
-        s_c[0][k] = c;
-        s_s[0][k] = t * c;
+        s_pq[k] = int2{p, q};
+        s_cs[k] = double2{c, t * c};
         s_t[k] = t;
-        log[(static_cast<size_t>(sweep) * (D - 1) + r) * NP + k] = t;
+        log[(static_cast<size_t>(sweep) * (D - 1) + r) * NP + k] = double2{c, t * c};
+        // a pair left alone gets the exact zero its own task would write
+        // (the other tasks never touch entry (p, q))
+        if (t == 0.0) {
+          A[p * LD + q] = 0.0;
+          A[q * LD + p] = 0.0;
+        }
+        const bool any = __any(t != 0.0);   // (the pairs are all in wavefront 0)
+        if (k == 0) s_rot[rc & 1] = any;
       }
       lds_barrier();
+      // a round that rotates nothing leaves every other entry as it is
+      if (!s_rot[rc++ & 1]) continue;
       // this round's tasks touch disjoint entries: all loads, then all stores
       double blk[NAT][4];
 #pragma unroll
@@ -740,7 +751,8 @@ __global__ __launch_bounds__(jacobi_threads<D>()) void calib_jacobi_kernel(const
         if (e < NTASK) {
           int ki, kj;
           block_task<NP>(e, ki, kj);
-          const int pi = s_p[0][ki], qi = s_q[0][ki], pj = s_p[0][kj], qj = s_q[0][kj];
+          const int2 pqi = s_pq[ki], pqj = s_pq[kj];
+          const int pi = pqi.x, qi = pqi.y, pj = pqj.x, qj = pqj.y;
           blk[u][0] = A[pi * LD + pj];
           blk[u][1] = A[pi * LD + qj];
           blk[u][2] = A[qi * LD + pj];
@@ -753,7 +765,8 @@ __global__ __launch_bounds__(jacobi_threads<D>()) void calib_jacobi_kernel(const
         if (e >= NTASK) continue;
         int ki, kj;
         block_task<NP>(e, ki, kj);
-        const int pi = s_p[0][ki], qi = s_q[0][ki], pj = s_p[0][kj], qj = s_q[0][kj];
+        const int2 pqi = s_pq[ki], pqj = s_pq[kj];
+        const int pi = pqi.x, qi = pqi.y, pj = pqj.x, qj = pqj.y;
         const double a_pp = blk[u][0], a_pq = blk[u][1], a_qp = blk[u][2], a_qq = blk[u][3];
         if (ki == kj) {
           // the rotated pair itself: exact zero off the diagonal
@@ -764,7 +777,8 @@ __global__ __launch_bounds__(jacobi_threads<D>()) void calib_jacobi_kernel(const
           A[qi * LD + pi] = 0.0;
           continue;
         }
-        const double ci = s_c[0][ki], si = s_s[0][ki], cj = s_c[0][kj], sj = s_s[0][kj];
+        const double2 csi = s_cs[ki], csj = s_cs[kj];
+        const double ci = csi.x, si = csi.y, cj = csj.x, sj = csj.y;
         // rows (J_i^T from the left), then columns (J_j from the right)
         const double r_pp = ci * a_pp - si * a_qp, r_pq = ci * a_pq - si * a_qq;
         const double r_qp = si * a_pp + ci * a_qp, r_qq = si * a_pq + ci * a_qq;
@@ -788,36 +802,27 @@ __global__ __launch_bounds__(jacobi_threads<D>()) void calib_jacobi_kernel(const
   if (tid < D) s_lam[tid] = A[tid * LD + tid];
   __syncthreads();
 
-  // ---- phase 2: V^T <- J^T V^T, replayed from the log, starting from I
+  // ---- phase 2: V^T <- J^T V^T, replayed from the log, starting from I:
+  // thread = one pair k of every round and columns i0, i0 + D / NWT, ...;
+  // its (c, s) are read one round ahead, and a pair that was left alone
+  // (s = 0, c = 1) leaves its two rows as they are
   for (int e = tid; e < D * D; e += NT) A[(e / D) * LD + e % D] = (e / D == e % D) ? 1.0 : 0.0;
-  // the log is read one round ahead, so its load waits behind a round's work
-  const int rounds = sweeps * (D - 1);
-  double t_next = (tid < NP && rounds > 0) ? log[tid] : 0.0;
-  for (int sweep = 0; sweep < sweeps; ++sweep) {
-    for (int r = 0; r < D - 1; ++r) {
-      // parameter buffers alternate with the round count (D - 1 rounds per
-      // sweep is odd, so not with r): one barrier per round suffices
-      const int round = sweep * (D - 1) + r;
-      const int b = round & 1;
-      if (tid < NP) {
-        const int k = tid;
-        int p, q;
-        jacobi_pair<D>(r, k, p, q);
-        const double t = t_next;
-        if (round + 1 < rounds) t_next = log[static_cast<size_t>(round + 1) * NP + k];
-        const double c = 1.0 / sqrt(1.0 + t * t);
-        s_p[b][k] = p;
-        s_q[b][k] = q;
-        s_c[b][k] = c;
-        s_s[b][k] = t * c;
-      }
-      lds_barrier();   // (the prefetched log load stays in flight)
-      // thread = one pair, columns i0, i0 + D / NWT, ...: the pair's
-      // parameters are read once per round
-      constexpr int CS = D / NWT;                 // column stride
-      const int k = tid / CS, i0 = tid % CS;
-      const int rp = s_p[b][k] * LD, rq = s_q[b][k] * LD;
-      const double c = s_c[b][k], sn = s_s[b][k];
+  {
+    constexpr int CS = D / NWT;                 // threads per pair, column stride
+    const int k = tid / CS, i0 = tid % CS;
+    const int rounds = sweeps * (D - 1);
+    double2 cs_next = rounds > 0 ? log[k] : double2{1.0, 0.0};
+    int r = 0;
+    for (int round = 0; round < rounds; ++round) {
+      const double2 cs = cs_next;
+      if (round + 1 < rounds) cs_next = log[static_cast<size_t>(round + 1) * NP + k];
+      int p, q;
+      jacobi_pair<D>(r, k, p, q);
+      r = r == D - 2 ? 0 : r + 1;
+      lds_barrier();   // the previous round's rows are written (the log loads stay in flight)
+      if (cs.y == 0.0) continue;
+      const int rp = p * LD, rq = q * LD;
+      const double c = cs.x, sn = cs.y;
       double wx[NWT], wy[NWT];
 #pragma unroll
       for (int u = 0; u < NWT; ++u) {
@@ -897,7 +902,7 @@ CalibPlan plan_calib(const kvq_calib_shape* s) {
                 align256(static_cast<size_t>(hkv) * kCalibModalities * d * sizeof(double)) +
                 align256((static_cast<size_t>(n) + 4 + 3 * (static_cast<size_t>(n) / 1024 + 1)) * sizeof(int32_t)) +
                 align256(static_cast<size_t>(splits) * hkv * kCalibModalities * d * d * sizeof(double));
-  p.eig_bytes = static_cast<size_t>(3) * hkv * kJacobiSweeps * (d - 1) * (d / 2) * sizeof(double);
+  p.eig_bytes = static_cast<size_t>(3) * hkv * kJacobiSweeps * (d - 1) * (d / 2) * 2 * sizeof(double);
   return p;
 }
 
@@ -956,8 +961,8 @@ size_t kvq_calib_workspace_bytes(const kvq_calib_shape* shape) {
 
 size_t kvq_calib_eigenbasis_workspace_bytes(int32_t count, int32_t head_dim) {
   if (count < 0 || (head_dim != 64 && head_dim != 128)) return 0;
-  // the rotation log: one tangent per (sweep, round, pair)
-  return static_cast<size_t>(count) * kJacobiSweeps * (head_dim - 1) * (head_dim / 2) * sizeof(double);
+  // the rotation log: (c, s) per (sweep, round, pair)
+  return static_cast<size_t>(count) * kJacobiSweeps * (head_dim - 1) * (head_dim / 2) * 2 * sizeof(double);
 }
 
 kvq_status kvq_calib_contribution(const kvq_calib_shape* shape, const void* k, int32_t k_dtype, const void* q,

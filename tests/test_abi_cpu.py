@@ -244,7 +244,7 @@ def test_calibration_rejects_bad_arguments_without_launching():
         return L.KvqCalibShape(*[f[name] for name, _ in L.KvqCalibShape._fields_])
     good = shape()
     need = lib.kvq_calib_workspace_bytes(ctypes.byref(good))
-    eig_need = 6 * 50 * 127 * 64 * 8          # the Jacobi rotation log: (sweep, round, pair) tangents
+    eig_need = 6 * 50 * 127 * 64 * 16         # the Jacobi rotation log: (c, s) per (sweep, round, pair)
     assert need >= lib.kvq_calib_eigenbasis_workspace_bytes(6, 128) == eig_need
     assert lib.kvq_calib_workspace_bytes(ctypes.byref(shape(head_dim=96))) == 0
     assert lib.kvq_calib_eigenbasis_workspace_bytes(-1, 128) == 0
