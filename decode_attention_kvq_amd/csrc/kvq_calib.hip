@@ -87,11 +87,16 @@ __device__ __forceinline__ void merge_ms(double& m, double& l, double m2, double
 }
 
 // Per (KV head, block of kTokBlock tokens, query row): max and sum of
-// exp(score - max) over the block's tokens.  Thread = token.
+// exp(score - max) over the block's tokens.  Thread = token.  The block max
+// comes first (a max is exact in any order), then one exponential per
+// (token, row), summed by a fixed butterfly in each wavefront and over the
+// wavefronts in order.
 template <int D, bool KB, bool QB>
 __global__ __launch_bounds__(kTokBlock) void calib_block_stats_kernel(ContribArgs a) {
+  constexpr int NWB = kTokBlock / 64;
   __shared__ double sq[kRowChunk][D];
-  __shared__ double red_m[kTokBlock / 64][kRowChunk], red_l[kTokBlock / 64][kRowChunk];
+  __shared__ double red[NWB][kRowChunk];
+  __shared__ double s_bm[kRowChunk];
   const int h = blockIdx.y, blk = blockIdx.x;
   const int t = blk * kTokBlock + threadIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -103,29 +108,37 @@ __global__ __launch_bounds__(kTokBlock) void calib_block_stats_kernel(ContribArg
     __syncthreads();
     double dot[kRowChunk];
     chunk_dots<D, KB>(a.k, row_off, sq, dot);
+    double sc[kRowChunk];
 #pragma unroll
     for (int r = 0; r < kRowChunk; ++r) {
-      double m = ok ? a.scale * dot[r] : -INFINITY;
-      double l = ok ? 1.0 : 0.0;
-      // butterfly over the wavefront (fixed pattern; lane 0 keeps the result)
+      sc[r] = ok ? a.scale * dot[r] : -INFINITY;
+      double m = sc[r];
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-        const double m2 = __shfl_xor(m, off, 64);
-        const double l2 = __shfl_xor(l, off, 64);
-        merge_ms(m, l, m2, l2);
-      }
-      if (lane == 0) {
-        red_m[wave][r] = m;
-        red_l[wave][r] = l;
-      }
+      for (int off = 32; off > 0; off >>= 1) m = fmax(m, __shfl_xor(m, off, 64));
+      if (lane == 0) red[wave][r] = m;
+    }
+    __syncthreads();
+    if (threadIdx.x < kRowChunk) {
+      double m = red[0][threadIdx.x];
+      for (int w = 1; w < NWB; ++w) m = fmax(m, red[w][threadIdx.x]);
+      s_bm[threadIdx.x] = m;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kRowChunk; ++r) {
+      // a block has at least one token, so its max is finite
+      double l = ok ? exp(sc[r] - s_bm[r]) : 0.0;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off, 64);
+      if (lane == 0) red[wave][r] = l;
     }
     __syncthreads();
     if (threadIdx.x < kRowChunk && r0 + static_cast<int>(threadIdx.x) < a.rows) {
       const int r = threadIdx.x;
-      double m = red_m[0][r], l = red_l[0][r];
-      for (int w = 1; w < kTokBlock / 64; ++w) merge_ms(m, l, red_m[w][r], red_l[w][r]);
+      double l = red[0][r];
+      for (int w = 1; w < NWB; ++w) l += red[w][r];
       double* out = a.part + ((static_cast<size_t>(h) * a.nblk + blk) * a.rows + r0 + r) * 2;
-      out[0] = m;
+      out[0] = s_bm[r];
       out[1] = l;
     }
   }
