@@ -635,16 +635,17 @@ __global__ __launch_bounds__(256) void calib_cov_merge_kernel(CovArgs a) {
 // D - 1 rounds of D / 2 disjoint pairs (round-robin ordering: player 0
 // fixed, the others rotated).
 //
-// Phase 1 rotates A alone, in LDS: a round forms its rotations from the
-// current matrix, then applies J^T A J one 2 x 2 block at a time (blocks
-// (ki, kj) and (kj, ki) from one task, so A stays exactly symmetric).  A pair
+// Phase 1 rotates A alone, in LDS, keeping its upper triangle only: a
+// round forms its rotations from the current matrix, then applies J^T A J
+// one 2 x 2 block (ki, kj), ki <= kj, at a time.  A pair
 // whose off-diagonal entry is negligible (against its diagonal, or below
 // the rounding noise of the whole matrix) is set to zero without a rotation;
 // the sweeps end when one rotates nothing (at most kJacobiSweeps).  Each
 // round's rotations (c, s) go to a log in the workspace; a round that
 // rotates no pair skips the update.
 // Phase 2 replays the log on V = I (V^T kept in LDS where A was):
-// V <- V J round by round with phase 1's own (c, s).
+// V <- V J round by round with phase 1's own (c, s); a wavefront takes one
+// pair at a time, its lanes on contiguous columns.
 template <int D>
 constexpr int jacobi_threads() { return D == 128 ? 512 : 256; }
 
@@ -672,6 +673,10 @@ __device__ __forceinline__ void block_task(int e, int& ki, int& kj) {
   }
 }
 
+// Phase 1 keeps entry (x, y) of the symmetric A at (min, max) only.
+template <int LD>
+__device__ __forceinline__ int upper(int x, int y) { return min(x, y) * LD + max(x, y); }
+
 // Barrier for LDS traffic only: the log's global stores stay in flight.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
@@ -685,8 +690,7 @@ __global__ __launch_bounds__(jacobi_threads<D>()) void calib_jacobi_kernel(const
   // densely (block_task) and dealt round robin, NAT per thread at most
   constexpr int NTASK = NP * (NP + 1) / 2;
   constexpr int NAT = (NTASK + NT - 1) / NT;
-  constexpr int NWT = NP * D / NT;    // (pair, column) tasks of V^T per thread
-  static_assert(NWT * NT == NP * D && NT >= D && D % NWT == 0, "tasks divide evenly");
+  static_assert(NT >= D, "one thread per eigenvalue at the end");
   constexpr double kNegligible = 0x1p-53;   // |a_pq| <= 2^-53 sqrt(|a_pp a_qq|): already diagonal to rounding
   __shared__ double A[D * LD];             // phase 1: A; phase 2: V^T (row j = column j of V)
   __shared__ double2 s_cs[NP];             // (c, s) of each pair
@@ -746,10 +750,7 @@ __global__ __launch_bounds__(jacobi_threads<D>()) void calib_jacobi_kernel(const
         log[(static_cast<size_t>(sweep) * (D - 1) + r) * NP + k] = double2{c, t * c};
         // a pair left alone gets the exact zero its own task would write
         // (the other tasks never touch entry (p, q))
-        if (t == 0.0) {
-          A[p * LD + q] = 0.0;
-          A[q * LD + p] = 0.0;
-        }
+        if (t == 0.0) A[p * LD + q] = 0.0;
         const bool any = __any(t != 0.0);   // (the pairs are all in wavefront 0)
         if (k == 0) s_rot[rc & 1] = any;
       }
@@ -766,10 +767,10 @@ __global__ __launch_bounds__(jacobi_threads<D>()) void calib_jacobi_kernel(const
           block_task<NP>(e, ki, kj);
           const int2 pqi = s_pq[ki], pqj = s_pq[kj];
           const int pi = pqi.x, qi = pqi.y, pj = pqj.x, qj = pqj.y;
-          blk[u][0] = A[pi * LD + pj];
-          blk[u][1] = A[pi * LD + qj];
-          blk[u][2] = A[qi * LD + pj];
-          blk[u][3] = A[qi * LD + qj];
+          blk[u][0] = A[upper<LD>(pi, pj)];
+          blk[u][1] = A[upper<LD>(pi, qj)];
+          blk[u][2] = A[upper<LD>(qi, pj)];
+          blk[u][3] = A[upper<LD>(qi, qj)];
         }
       }
 #pragma unroll
@@ -787,7 +788,6 @@ __global__ __launch_bounds__(jacobi_threads<D>()) void calib_jacobi_kernel(const
           A[pi * LD + pi] = a_pp - t * a_pq;
           A[qi * LD + qi] = a_qq + t * a_pq;
           A[pi * LD + qi] = 0.0;
-          A[qi * LD + pi] = 0.0;
           continue;
         }
         const double2 csi = s_cs[ki], csj = s_cs[kj];
@@ -797,14 +797,10 @@ __global__ __launch_bounds__(jacobi_threads<D>()) void calib_jacobi_kernel(const
         const double r_qp = si * a_pp + ci * a_qp, r_qq = si * a_pq + ci * a_qq;
         const double n_pp = cj * r_pp - sj * r_pq, n_pq = sj * r_pp + cj * r_pq;
         const double n_qp = cj * r_qp - sj * r_qq, n_qq = sj * r_qp + cj * r_qq;
-        A[pi * LD + pj] = n_pp;
-        A[pj * LD + pi] = n_pp;
-        A[pi * LD + qj] = n_pq;
-        A[qj * LD + pi] = n_pq;
-        A[qi * LD + pj] = n_qp;
-        A[pj * LD + qi] = n_qp;
-        A[qi * LD + qj] = n_qq;
-        A[qj * LD + qi] = n_qq;
+        A[upper<LD>(pi, pj)] = n_pp;
+        A[upper<LD>(pi, qj)] = n_pq;
+        A[upper<LD>(qi, pj)] = n_qp;
+        A[upper<LD>(qi, qj)] = n_qq;
       }
       lds_barrier();
     }
@@ -816,37 +812,48 @@ __global__ __launch_bounds__(jacobi_threads<D>()) void calib_jacobi_kernel(const
   __syncthreads();
 
   // ---- phase 2: V^T <- J^T V^T, replayed from the log, starting from I:
-  // thread = one pair k of every round and columns i0, i0 + D / NWT, ...;
-  // its (c, s) are read one round ahead, and a pair that was left alone
-  // (s = 0, c = 1) leaves its two rows as they are
+  // wavefront w takes pairs w, w + NWV, ... of every round, its lanes
+  // columns lane, lane + 64; the pairs' (c, s) are read one round ahead, and
+  // a pair that was left alone (s = 0, c = 1) leaves its rows as they are
   for (int e = tid; e < D * D; e += NT) A[(e / D) * LD + e % D] = (e / D == e % D) ? 1.0 : 0.0;
   {
-    constexpr int CS = D / NWT;                 // threads per pair, column stride
-    const int k = tid / CS, i0 = tid % CS;
+    constexpr int NWV = NT / 64;                // wavefronts
+    constexpr int PPW = NP / NWV;               // pairs per wavefront
+    constexpr int CPL = D / 64;                 // columns per lane
+    static_assert(PPW * NWV == NP && CPL * 64 == D, "pairs and columns divide evenly");
+    const int wave = tid >> 6, lane = tid & 63;
     const int rounds = sweeps * (D - 1);
-    double2 cs_next = rounds > 0 ? log[k] : double2{1.0, 0.0};
+    double2 cs_next[PPW];
+#pragma unroll
+    for (int u = 0; u < PPW; ++u) cs_next[u] = rounds > 0 ? log[wave + NWV * u] : double2{1.0, 0.0};
     int r = 0;
     for (int round = 0; round < rounds; ++round) {
-      const double2 cs = cs_next;
-      if (round + 1 < rounds) cs_next = log[static_cast<size_t>(round + 1) * NP + k];
-      int p, q;
-      jacobi_pair<D>(r, k, p, q);
-      r = r == D - 2 ? 0 : r + 1;
+      double2 cs[PPW];
+#pragma unroll
+      for (int u = 0; u < PPW; ++u) {
+        cs[u] = cs_next[u];
+        if (round + 1 < rounds) cs_next[u] = log[static_cast<size_t>(round + 1) * NP + wave + NWV * u];
+      }
       lds_barrier();   // the previous round's rows are written (the log loads stay in flight)
-      if (cs.y == 0.0) continue;
-      const int rp = p * LD, rq = q * LD;
-      const double c = cs.x, sn = cs.y;
-      double wx[NWT], wy[NWT];
 #pragma unroll
-      for (int u = 0; u < NWT; ++u) {
-        wx[u] = A[rp + i0 + u * CS];
-        wy[u] = A[rq + i0 + u * CS];
-      }
+      for (int u = 0; u < PPW; ++u) {
+        if (cs[u].y == 0.0) continue;   // a pair left alone: its rows stay as they are
+        int p, q;
+        jacobi_pair<D>(r, wave + NWV * u, p, q);
+        const double c = cs[u].x, sn = cs[u].y;
+        double wx[CPL], wy[CPL];
 #pragma unroll
-      for (int u = 0; u < NWT; ++u) {
-        A[rp + i0 + u * CS] = c * wx[u] - sn * wy[u];
-        A[rq + i0 + u * CS] = sn * wx[u] + c * wy[u];
+        for (int j = 0; j < CPL; ++j) {
+          wx[j] = A[p * LD + lane + 64 * j];
+          wy[j] = A[q * LD + lane + 64 * j];
+        }
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+          A[p * LD + lane + 64 * j] = c * wx[j] - sn * wy[j];
+          A[q * LD + lane + 64 * j] = sn * wx[j] + c * wy[j];
+        }
       }
+      r = r == D - 2 ? 0 : r + 1;
     }
   }
   __syncthreads();
