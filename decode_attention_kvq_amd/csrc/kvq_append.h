@@ -28,7 +28,11 @@
 // workgroup takes a ticket when done; the last one of a session advances its
 // length, so no workgroup can see the new length before it read the old one
 // (the fused step defers this to its merge, and also copies the open group's
-// blocks, statistics, norms and modality bytes to a record in shared memory).
+// blocks, statistics, norms and modality bytes to a record in shared memory;
+// with a record, the cache writes are left to the caller, which makes them
+// from the record after its last load: on this GPU one counter tracks
+// loads and stores alike, so a load issued after a store is waited for
+// together with it).
 //
 // Latency matters for the common one-position append, throughput for a
 // chunk: each role issues its global loads in at most two dependent rounds,
@@ -268,8 +272,8 @@ __device__ __forceinline__ void append_group(const AppendArgs& a, AppendSmem<D>&
     if (BITS == 2) {
       if (tid < D / 2) {
         const uint4 v = reinterpret_cast<const uint4*>(sm.k.kblk)[tid];
-        reinterpret_cast<uint4*>(a.k_codes + static_cast<size_t>(blk_) * 8 * D)[tid] = v;
         if (stage) reinterpret_cast<uint4*>(stage + kStageCodes)[tid] = v;
+        else reinterpret_cast<uint4*>(a.k_codes + static_cast<size_t>(blk_) * 8 * D)[tid] = v;
       }
     } else {
       uint32_t* dst = reinterpret_cast<uint32_t*>(a.k_codes + static_cast<size_t>(blk_) * 4 * BITS * D);
@@ -326,6 +330,10 @@ __device__ __forceinline__ void append_group(const AppendArgs& a, AppendSmem<D>&
         int* meta = reinterpret_cast<int*>(stage + kStageMeta);
         meta[0] = blk >= 0 ? 1 : 0;   // blocks stored (the page is mapped)
         meta[1] = s_end;              // positions of the group
+        meta[2] = t0;                 // its first position
+        meta[3] = s_first;            // its first new position
+        meta[4] = phys_of();
+        *reinterpret_cast<long long*>(stage + kStageBlock) = blk;
       }
 
       if (a.key_mode == KVQ_KEYS_PER_TOKEN) {
@@ -385,14 +393,10 @@ __device__ __forceinline__ void append_group(const AppendArgs& a, AppendSmem<D>&
         if (q == 0) {
           const uint16_t lo16 = f64_to_f16_rne(lo), hi16 = f64_to_f16_rne(hi);
           if (blk >= 0) {
-            uint16_t* st = a.k_stats + static_cast<size_t>(blk) * 2 * D;
+            uint16_t* st = stage ? reinterpret_cast<uint16_t*>(stage + kStageCodes + 16 * D)
+                                 : a.k_stats + static_cast<size_t>(blk) * 2 * D;
             st[c] = lo16;
             st[D + c] = hi16;
-            if (stage) {
-              uint16_t* sst = reinterpret_cast<uint16_t*>(stage + kStageCodes + 16 * D);
-              sst[c] = lo16;
-              sst[D + c] = hi16;
-            }
           }
           // LO and the per-channel factor (c3 - c0) / (HI - LO) (HI - LO is
           // exact in fp64); 0 marks HI == LO (every code 0).
@@ -433,7 +437,7 @@ __device__ __forceinline__ void append_group(const AppendArgs& a, AppendSmem<D>&
     // group 0 is the only reader of the tail and its reads are done (their
     // values were used above).
     const int open0 = (L_new / kGroupTokens) * kGroupTokens;
-    if (j == 0 && open0 < L_new) {
+    if (!stage && j == 0 && open0 < L_new) {
       const int start = max(open0, L_old);
       const int count = L_new - start;
       for (int idx = tid; idx < count * D; idx += kAppendThreads) {
@@ -577,10 +581,10 @@ __device__ __forceinline__ void append_group(const AppendArgs& a, AppendSmem<D>&
         }
         outw |= out << (8 * k);
       }
-      reinterpret_cast<uint32_t*>(vb)[tid] = outw;
       if (stage) reinterpret_cast<uint32_t*>(stage + kStageCodes + 8 * D)[tid] = outw;
+      else reinterpret_cast<uint32_t*>(vb)[tid] = outw;
     }
-    if (BITS != 2 && stored) {
+    if (BITS != 2 && stored && !stage) {
       auto vcode = [&](int t, int c) -> uint32_t {
         if (t < s_first) return sm.v.code[t][c];
         if (t < s_end) return sm.v.mod[t] < kModalities ? sm.v.code[t][c] : 0u;
@@ -589,7 +593,7 @@ __device__ __forceinline__ void append_group(const AppendArgs& a, AppendSmem<D>&
       for (int w = tid; w < BITS * D; w += kAppendThreads)
         reinterpret_cast<uint32_t*>(vb)[w] = pack_word<D, true>(BITS, w, vcode);
     }
-    if (stored && tid < kGroupTokens && tid >= s_first && tid < s_end) {
+    if (!stage && stored && tid < kGroupTokens && tid >= s_first && tid < s_end) {
       const int pos = (t0 + tid) % a.page_tokens;
       a.v_norms[(static_cast<size_t>(phys) * a.hkv + h) * a.page_tokens + pos] = f64_to_f16_rne(sm.v.n[tid]);
       if (h == 0) a.modality[static_cast<size_t>(phys) * a.page_tokens + pos] = sm.v.mod[tid];

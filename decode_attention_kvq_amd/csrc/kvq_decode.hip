@@ -1186,10 +1186,11 @@ struct StepSmem {
   app::AppendSmem<D> app;
   float q[8][D];                        // the KV head's query heads, rotated
   float sc[8][kGroupTokens];            // open group: scores (base 2), -inf where nothing is attended
-  float w[8][kGroupTokens];             // weights 2^(s - M) N
+  float w[8][kModalities][kGroupTokens];   // weights 2^(s - M) N of the positions of each modality (else 0)
   float nrm[kGroupTokens];
   int mod[kGroupTokens];
   int last;                             // the append's ticket flag (unused: the merge advances the lengths)
+  float lv[4];                          // the normalized levels
   __align__(16) uint8_t rec[stage_record_bytes(D)];   // the open group (kStage* layout)
 };
 
@@ -1214,6 +1215,15 @@ __device__ __forceinline__ void step_append_open_group(const DecodeArgs& a, cons
   constexpr int PS = kPartialHeader + kModalities * D;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = a.group;
+  // the four levels in shared memory: indexing the argument array by a
+  // code would be a memory load per use
+  if (tid < 4) sm.lv[tid] = a.level_f32[tid];
+  auto level = [&](uint32_t c) { return sm.lv[c]; };
+  // the new key row, for the raw tail (stored at the end with the cache
+  // writes): one 32-bit word per thread
+  constexpr int KW = D * (BF16 ? 2 : 4) / 4;
+  const uint32_t kraw = tid < KW
+      ? reinterpret_cast<const uint32_t*>(ap.k_new)[static_cast<size_t>(b * a.hkv + h) * KW + tid] : 0u;
   if (wave < 2) {
     // the KV head's query heads (16 lanes per head, head 4 w .. 4 w + 3 on wavefront w)
     constexpr int RCH = D / rotq::kLanes;
@@ -1239,7 +1249,7 @@ __device__ __forceinline__ void step_append_open_group(const DecodeArgs& a, cons
     for (int i = 0; i < OQ; ++i) {
       const float lo = f16_bits_to_f32(lohi[c0 + i]), hi = f16_bits_to_f32(lohi[D + c0 + i]);
       const uint32_t byte = rec[kStageCodes + key_code_byte<D>(t, c0 + (i & ~3))];
-      const float lvl = a.level_f32[(byte >> (2 * (i & 3))) & 3u];
+      const float lvl = level((byte >> (2 * (i & 3))) & 3u);
       kh[i] = (hi + lo) * 0.5f + (hi - lo) * 0.5f * lvl;
     }
     const bool live = meta.x != 0 && t < meta.y;
@@ -1268,7 +1278,11 @@ __device__ __forceinline__ void step_append_open_group(const DecodeArgs& a, cons
 #pragma unroll
     for (int m = 0; m < kModalities; ++m)
       if (__any(e > 0.f && md == m)) mk |= 1 << m;
-    if (lane < kGroupTokens) sm.w[wave][t] = e * sm.nrm[t];
+    if (lane < kGroupTokens) {
+      const float x = e * sm.nrm[t];
+#pragma unroll
+      for (int m = 0; m < kModalities; ++m) sm.w[wave][m][t] = md == m ? x : 0.f;
+    }
     float* part = a.partials + (static_cast<size_t>(h * G + wave) * a.pstride + slot) * PS;
     if (lane < kPartialHeader)
       part[lane] = lane == 0 ? mo : lane == 1 ? lsum : lane == 2 ? __int_as_float(mk) : 0.f;
@@ -1276,22 +1290,56 @@ __device__ __forceinline__ void step_append_open_group(const DecodeArgs& a, cons
   __syncthreads();
   {
     // value sums: channel c, query heads i = tid / D, + VG, ...
+    // (the channel's levels are decoded once; the modality split is in the
+    // weights, so the sums take no per-position branch or select)
     const int c = tid % D;
-    uint32_t vb[kGroupTokens / 4];
+    float lvl[kGroupTokens];
 #pragma unroll
-    for (int k = 0; k < kGroupTokens / 4; ++k) vb[k] = rec[kStageCodes + 8 * D + value_code_byte<D>(4 * k, c)];
+    for (int k = 0; k < kGroupTokens / 4; ++k) {
+      const uint32_t vb = rec[kStageCodes + 8 * D + value_code_byte<D>(4 * k, c)];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) lvl[4 * k + u] = level((vb >> (2 * u)) & 3u);
+    }
     for (int i = tid / D; i < G; i += VG) {
       float av[kModalities] = {0.f, 0.f, 0.f};
 #pragma unroll
-      for (int t = 0; t < kGroupTokens; ++t) {
-        const float x = sm.w[i][t] * a.level_f32[(vb[t >> 2] >> (2 * (t & 3))) & 3u];
-        const int md = sm.mod[t];
+      for (int t = 0; t < kGroupTokens; ++t)
 #pragma unroll
-        for (int m = 0; m < kModalities; ++m) av[m] += md == m ? x : 0.f;
-      }
+        for (int m = 0; m < kModalities; ++m) av[m] += sm.w[i][m][t] * lvl[t];
       float* part = a.partials + (static_cast<size_t>(h * G + i) * a.pstride + slot) * PS;
 #pragma unroll
       for (int m = 0; m < kModalities; ++m) part[kPartialHeader + m * D + c] = av[m];
+    }
+  }
+
+  // The append's cache writes, from the record, after the workgroup's last
+  // load: the group's key and value blocks and statistics, the new
+  // position's norm and modality byte, and its raw key in the tail when the
+  // group stays open.
+  {
+    const int* meta = reinterpret_cast<const int*>(rec + kStageMeta);
+    const int t0 = meta[2], s_first = meta[3], s_end = meta[1], phys = meta[4];
+    if (meta[0]) {
+      const long long blk = *reinterpret_cast<const long long*>(rec + kStageBlock);
+      const uint4* src = reinterpret_cast<const uint4*>(rec + kStageCodes);
+      if (tid < D / 2) {
+        reinterpret_cast<uint4*>(ap.k_codes + static_cast<size_t>(blk) * 8 * D)[tid] = src[tid];
+      } else if (tid < D) {
+        reinterpret_cast<uint4*>(ap.v_codes + static_cast<size_t>(blk) * 8 * D)[tid - D / 2] = src[tid];
+      } else if (tid < D + D / 4) {
+        reinterpret_cast<uint4*>(ap.k_stats + static_cast<size_t>(blk) * 2 * D)[tid - D] = src[tid];
+      }
+      if (tid >= s_first && tid < s_end) {
+        const int pos = (t0 + tid) % ap.page_tokens;
+        ap.v_norms[(static_cast<size_t>(phys) * ap.hkv + h) * ap.page_tokens + pos] =
+            reinterpret_cast<const uint16_t*>(rec + kStageNorms)[tid];
+        if (h == 0) ap.modality[static_cast<size_t>(phys) * ap.page_tokens + pos] = rec[kStageMods + tid];
+      }
+    }
+    const int L_old = t0 + s_first;
+    if (((L_old + 1) & (kGroupTokens - 1)) != 0 && tid < KW) {
+      const int sb = ap.b0 + b;
+      reinterpret_cast<uint32_t*>(ap.k_tail)[(static_cast<size_t>(sb * ap.hkv + h) * kGroupTokens + (L_old & 31)) * KW + tid] = kraw;
     }
   }
 }

@@ -58,7 +58,9 @@ struct AppendArgs {
 // workgroup that runs the step's append for one (session, KV head): written
 // by the append's key and value roles, then read for the open group's
 // partial.  Byte offsets:
-constexpr int kStageMeta = 0;      // int32 [0]: 1 if the group's page is mapped, [1]: positions in the group
+constexpr int kStageMeta = 0;      // int32 [0]: 1 if the group's page is mapped, [1]: positions in the group,
+                                   // [2]: its first position, [3]: its first new position, [4]: its page
+constexpr int kStageBlock = 24;    // int64: its 32-position block (-1: not stored)
 constexpr int kStageNorms = 64;    // 32 fp16 value norms
 constexpr int kStageMods = 128;    // 32 modality bytes
 constexpr int kStageCodes = 256;   // key block (8d bytes), value block (8d bytes), LO and HI rows (2d fp16 each)
