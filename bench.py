@@ -41,7 +41,7 @@ L80K = 81920
 # (FETCH_SIZE x 1.9998, WRITE_SIZE x 1.0); see profiles/decode_80k_hbm_bytes.md.
 # Valid only for the decode source the counters were taken on (SHA-256 of
 # kvq_decode.hip); otherwise `traffic` is reported as null.
-DECODE_TRAFFIC = {"kvq_decode_sha256": "d429d307260c14a50838913430052a9b2bd6b89673ba8ffc7f9c18801c1dad35",
+DECODE_TRAFFIC = {"kvq_decode_sha256": "1b954518339dceb77ea920193cd9d22d487022d8e0a9817d61240ffd57fb3814",
                   "bytes": 32901595}
 
 
