@@ -338,6 +338,14 @@ def main():
         extra["turboquant_baseline"] = turbo
         extra["wider_codes"] = {f"{b}bit": time_variant_decode(w, table, L0, R, n_dec, scale, bits=b)
                                 for b in (3, 4)}
+        # the same cache attended by 64 query heads (16 per KV head): the
+        # decode takes its wider-group partition kernel there
+        import dataclasses
+        w16 = dataclasses.replace(w, cfg=dataclasses.replace(w.cfg, n_q_heads=64),
+                                  q=np.ascontiguousarray(np.concatenate([w.q] * 3, axis=1)[:, :64]))
+        g16 = time_variant_decode(w16, table, L0, R, n_dec, scale)
+        g16["workload"] = "same 80K cache, 64 query heads (16 per KV head, the wider-group partition kernel)"
+        extra["gqa16_decode"] = g16
         del caches
         torch.cuda.empty_cache()
         extra["batched_paged_decode"] = time_batched_paged(max(3, R // 6))
