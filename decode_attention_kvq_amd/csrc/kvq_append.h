@@ -539,7 +539,11 @@ __device__ __forceinline__ void append_group(const AppendArgs& a, AppendSmem<D>&
 #pragma unroll
         for (int k = 0; k < KS; ++k) {
           const double av = static_cast<double>(sm.v.v[16 * mt + (lane & 15)][4 * k + (lane >> 4)]);
-          acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av, static_cast<double>(rb[k]), acc, 0, 0, 0);
+          // (opaque, so that the 32 conversions are not hoisted out of the
+          // tile loop as 64 more live registers)
+          float rk = rb[k];
+          asm volatile("" : "+v"(rk));
+          acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av, static_cast<double>(rk), acc, 0, 0, 0);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {

@@ -9,9 +9,13 @@ namespace kvq {
 namespace {
 
 using app::kAppendThreads;
+constexpr int kComputeUnits = 256;
 
-template <int D, bool BF16, int BITS>
-__global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
+// WIDE: a chunk with more workgroups than compute units; the register
+// budget then allows two workgroups per CU (a few registers spill, which a
+// one-position append, bound by its latency, would pay for).
+template <int D, bool BF16, int BITS, bool WIDE>
+__global__ __launch_bounds__(kAppendThreads, WIDE ? 4 : 1) void append_kernel(AppendArgs a) {
   __shared__ app::AppendSmem<D> sm;
   __shared__ int s_last;
   const int tid = threadIdx.x;
@@ -44,9 +48,16 @@ hipError_t launch_append_t(int nb, AppendArgs a, hipStream_t s) {
   const int rot_wgs = (a.rot_heads + kAppendThreads / rotq::kLanes - 1) / (kAppendThreads / rotq::kLanes);
   const int rot_x = (rot_wgs + a.hkv * nb - 1) / (a.hkv * nb);
   const dim3 grid(a.append_x + rot_x, a.hkv, nb);
-  if (a.bits == 4) hipLaunchKernelGGL((append_kernel<D, BF16, 4>), grid, dim3(kAppendThreads), 0, s, a);
-  else if (a.bits == 3) hipLaunchKernelGGL((append_kernel<D, BF16, 3>), grid, dim3(kAppendThreads), 0, s, a);
-  else hipLaunchKernelGGL((append_kernel<D, BF16, 2>), grid, dim3(kAppendThreads), 0, s, a);
+  const bool wide = static_cast<long long>(a.append_x) * a.hkv * nb > kComputeUnits;
+#define KVQ_APPEND(B)                                                                                   \
+  do {                                                                                                  \
+    if (wide) hipLaunchKernelGGL((append_kernel<D, BF16, B, true>), grid, dim3(kAppendThreads), 0, s, a);  \
+    else hipLaunchKernelGGL((append_kernel<D, BF16, B, false>), grid, dim3(kAppendThreads), 0, s, a);      \
+  } while (0)
+  if (a.bits == 4) KVQ_APPEND(4);
+  else if (a.bits == 3) KVQ_APPEND(3);
+  else KVQ_APPEND(2);
+#undef KVQ_APPEND
   return hipGetLastError();
 }
 
