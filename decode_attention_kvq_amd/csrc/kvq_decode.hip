@@ -1018,7 +1018,6 @@ template <int D, int BITS>
 __device__ __forceinline__ void sw_front(const ConsumerLoad<D, BITS>& cur, const SwSlot<D>* slot, int kg, int col,
                                          const uint2* tab, uint32_t lane_off, SwFront<D>& f) {
   constexpr int KT = D / 32;
-  constexpr int CT = D / 16;
   f.sc[0] = floatx4{0.f, 0.f, 0.f, 0.f};
   f.sc[1] = floatx4{0.f, 0.f, 0.f, 0.f};
   if constexpr (BITS != 2) {
