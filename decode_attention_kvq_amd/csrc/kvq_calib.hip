@@ -643,11 +643,38 @@ __global__ __launch_bounds__(256) void calib_cov_merge_kernel(CovArgs a) {
 // the sweeps end when one rotates nothing (at most kJacobiSweeps).  Each
 // round's rotations (c, s) go to a log in the workspace; a round that
 // rotates no pair skips the update.
-// Phase 2 replays the log on V = I (V^T kept in LDS where A was):
-// V <- V J round by round with phase 1's own (c, s); a wavefront takes one
-// pair at a time, its lanes on contiguous columns.
+// Phase 2 replays the log on V = I: V <- V J round by round with phase 1's
+// own (c, s).  The columns of V^T are independent under the rotations, so
+// the replay runs as many workgroups per matrix, each on a block of
+// kReplayCols columns of V^T (one lane per pair).  A last pass orders the
+// eigenvectors by eigenvalue and fixes their signs.
 template <int D>
 constexpr int jacobi_threads() { return D == 128 ? 512 : 256; }
+constexpr int kReplayCols = 8;     // columns of V^T per replay workgroup
+constexpr int kReplayChunk = 16;   // rounds of the log staged in LDS at a time
+
+// The eigenbasis workspace: the rotation log, then per matrix its round
+// count, its eigenvalues (unsorted) and V^T.
+struct EigLayout {
+  size_t log, rounds, lam, vt, total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+EigLayout eig_layout(int count, int d) {
+  EigLayout L;
+  size_t o = 0;
+  L.log = o;
+  o += align256(static_cast<size_t>(count) * kJacobiSweeps * (d - 1) * (d / 2) * 2 * sizeof(double));
+  L.rounds = o;
+  o += align256(static_cast<size_t>(count) * sizeof(int));
+  L.lam = o;
+  o += align256(static_cast<size_t>(count) * d * sizeof(double));
+  L.vt = o;
+  o += static_cast<size_t>(count) * d * d * sizeof(double);
+  L.total = o;
+  return L;
+}
 
 // Pair k of round r of the round-robin ordering, as (p, q) with p < q.
 template <int D>
@@ -681,8 +708,8 @@ __device__ __forceinline__ int upper(int x, int y) { return min(x, y) * LD + max
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <int D>
-__global__ __launch_bounds__(jacobi_threads<D>()) void calib_jacobi_kernel(const double* cov, float* rot,
-                                                                           double* evals, double* work) {
+__global__ __launch_bounds__(jacobi_threads<D>()) void calib_jacobi_kernel(const double* cov, double2* logs,
+                                                                           int* rounds_out, double* lam_out) {
   constexpr int NP = D / 2;
   constexpr int LD = D + 1;
   constexpr int NT = jacobi_threads<D>();
@@ -692,17 +719,16 @@ __global__ __launch_bounds__(jacobi_threads<D>()) void calib_jacobi_kernel(const
   constexpr int NAT = (NTASK + NT - 1) / NT;
   static_assert(NT >= D, "one thread per eigenvalue at the end");
   constexpr double kNegligible = 0x1p-53;   // |a_pq| <= 2^-53 sqrt(|a_pp a_qq|): already diagonal to rounding
-  __shared__ double A[D * LD];             // phase 1: A; phase 2: V^T (row j = column j of V)
+  __shared__ double A[D * LD];
   __shared__ double2 s_cs[NP];             // (c, s) of each pair
   __shared__ double s_t[NP];
   __shared__ int2 s_pq[NP];                // (p, q) of each pair
   __shared__ int s_changed;
-  __shared__ int s_rot[2];                 // phase 1: the round rotates some pair
-  __shared__ double s_lam[D];
+  __shared__ int s_rot[2];                 // the round rotates some pair
   __shared__ double s_sq[NT];
   const int mat = blockIdx.x, tid = threadIdx.x;
   const double* C = cov + static_cast<size_t>(mat) * D * D;
-  double2* log = reinterpret_cast<double2*>(work) + static_cast<size_t>(mat) * kJacobiSweeps * (D - 1) * NP;
+  double2* log = logs + static_cast<size_t>(mat) * kJacobiSweeps * (D - 1) * NP;
   double sq = 0.0;
   for (int e = tid; e < D * D; e += NT) {
     const int i = e / D, j = e % D;
@@ -807,55 +833,106 @@ __global__ __launch_bounds__(jacobi_threads<D>()) void calib_jacobi_kernel(const
     sweeps = sweep + 1;
     if (!s_changed) break;
   }
-  __syncthreads();   // the log is complete and visible to the workgroup
-  if (tid < D) s_lam[tid] = A[tid * LD + tid];
-  __syncthreads();
+  if (tid < D) lam_out[static_cast<size_t>(mat) * D + tid] = A[tid * LD + tid];
+  if (tid == 0) rounds_out[mat] = sweeps * (D - 1);
+}
 
-  // ---- phase 2: V^T <- J^T V^T, replayed from the log, starting from I:
-  // wavefront w takes pairs w, w + NWV, ... of every round, its lanes
-  // columns lane, lane + 64; the pairs' (c, s) are read one round ahead, and
-  // a pair that was left alone (s = 0, c = 1) leaves its rows as they are
-  for (int e = tid; e < D * D; e += NT) A[(e / D) * LD + e % D] = (e / D == e % D) ? 1.0 : 0.0;
-  {
-    constexpr int NWV = NT / 64;                // wavefronts
-    constexpr int PPW = NP / NWV;               // pairs per wavefront
-    constexpr int CPL = D / 64;                 // columns per lane
-    static_assert(PPW * NWV == NP && CPL * 64 == D, "pairs and columns divide evenly");
-    const int wave = tid >> 6, lane = tid & 63;
-    const int rounds = sweeps * (D - 1);
-    double2 cs_next[PPW];
+// Phase 2: V^T <- J^T V^T from the identity, on columns [cb W, (cb + 1) W)
+// of V^T (W = kReplayCols), one wavefront: lane k applies pair k of every
+// round (with two lanes per pair at d = 64, each on half the columns); a
+// pair that was left alone (s = 0, c = 1) leaves its rows as they are.  The
+// log is staged kReplayChunk rounds at a time through LDS, the next chunk's
+// loads in flight while the current one is applied.
+template <int D>
+__global__ __launch_bounds__(64) void calib_jacobi_replay_kernel(const double2* logs, const int* rounds_in,
+                                                                 double* vt) {
+  constexpr int NP = D / 2;
+  constexpr int W = kReplayCols;
+  constexpr int CB = D / W;              // column blocks per matrix
+  constexpr int LPP = 64 / NP;           // lanes per pair
+  constexpr int CPL = W / LPP;           // columns per lane
+  constexpr int LDB = W + 1;             // row stride in doubles
+  constexpr int CH = kReplayChunk;
+  constexpr int PRE = CH * NP / 64;      // log entries per lane per chunk
+  static_assert(LPP * NP == 64 && CPL * LPP == W && PRE * 64 == CH * NP, "replay shape");
+  __shared__ double V[D * LDB];
+  __shared__ double2 s_cs[2][CH * NP];
+  const int mat = blockIdx.x / CB, cb = blockIdx.x % CB;
+  const int lane = threadIdx.x, k = lane % NP, c0 = (lane / NP) * CPL;
+  const double2* log = logs + static_cast<size_t>(mat) * kJacobiSweeps * (D - 1) * NP;
+  const int rounds = rounds_in[mat];
+  for (int e = lane; e < D * W; e += 64) {
+    const int i = e / W, j = e % W;
+    V[i * LDB + j] = (i == cb * W + j) ? 1.0 : 0.0;
+  }
+  const int nch = (rounds + CH - 1) / CH;
+  double2 pre[PRE];
+  auto fetch = [&](int ch) {
 #pragma unroll
-    for (int u = 0; u < PPW; ++u) cs_next[u] = rounds > 0 ? log[wave + NWV * u] : double2{1.0, 0.0};
-    int r = 0;
-    for (int round = 0; round < rounds; ++round) {
-      double2 cs[PPW];
+    for (int u = 0; u < PRE; ++u) {
+      const int idx = u * 64 + lane;                   // (round in chunk) * NP + pair
+      const bool in = ch * CH + idx / NP < rounds;
+      pre[u] = in ? log[static_cast<size_t>(ch) * CH * NP + idx] : double2{1.0, 0.0};
+    }
+  };
+  auto stash = [&](int buf) {
 #pragma unroll
-      for (int u = 0; u < PPW; ++u) {
-        cs[u] = cs_next[u];
-        if (round + 1 < rounds) cs_next[u] = log[static_cast<size_t>(round + 1) * NP + wave + NWV * u];
-      }
-      lds_barrier();   // the previous round's rows are written (the log loads stay in flight)
-#pragma unroll
-      for (int u = 0; u < PPW; ++u) {
-        if (cs[u].y == 0.0) continue;   // a pair left alone: its rows stay as they are
+    for (int u = 0; u < PRE; ++u) s_cs[buf][u * 64 + lane] = pre[u];
+  };
+  if (nch > 0) {
+    fetch(0);
+    stash(0);
+  }
+  if (nch > 1) fetch(1);
+  lds_barrier();
+  int r = 0;   // round within the sweep: the pair ordering
+  for (int ch = 0; ch < nch; ++ch) {
+    const int buf = ch & 1;
+    const int nr = min(CH, rounds - ch * CH);
+    for (int i = 0; i < nr; ++i) {
+      const double2 cs = s_cs[buf][i * NP + k];
+      if (cs.y != 0.0) {
         int p, q;
-        jacobi_pair<D>(r, wave + NWV * u, p, q);
-        const double c = cs[u].x, sn = cs[u].y;
+        jacobi_pair<D>(r, k, p, q);
         double wx[CPL], wy[CPL];
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
-          wx[j] = A[p * LD + lane + 64 * j];
-          wy[j] = A[q * LD + lane + 64 * j];
+          wx[j] = V[p * LDB + c0 + j];
+          wy[j] = V[q * LDB + c0 + j];
         }
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
-          A[p * LD + lane + 64 * j] = c * wx[j] - sn * wy[j];
-          A[q * LD + lane + 64 * j] = sn * wx[j] + c * wy[j];
+          V[p * LDB + c0 + j] = cs.x * wx[j] - cs.y * wy[j];
+          V[q * LDB + c0 + j] = cs.y * wx[j] + cs.x * wy[j];
         }
       }
       r = r == D - 2 ? 0 : r + 1;
+      lds_barrier();   // the round's rows are written before the next reads them
     }
+    if (ch + 1 < nch) stash(buf ^ 1);   // chunk ch + 1 (its buffer held chunk ch - 1)
+    if (ch + 2 < nch) fetch(ch + 2);
+    lds_barrier();
   }
+  double* out = vt + static_cast<size_t>(mat) * D * D + cb * W;
+  for (int e = lane; e < D * W; e += 64) {
+    const int i = e / W, j = e % W;
+    out[static_cast<size_t>(i) * D + j] = V[i * LDB + j];
+  }
+}
+
+// The eigenvectors (rows of V^T) in decreasing eigenvalue order (ties by
+// index), each signed so that its largest-magnitude component (the first
+// of equal ones) is positive; rot[i][rank] = component i, as fp32.
+template <int D>
+__global__ __launch_bounds__(256) void calib_jacobi_finalize_kernel(const double* vt, const double* lam_in,
+                                                                    float* rot, double* evals) {
+  constexpr int LD = D + 1;
+  __shared__ double A[D * LD];
+  __shared__ double s_lam[D];
+  const int mat = blockIdx.x, tid = threadIdx.x;
+  const double* src = vt + static_cast<size_t>(mat) * D * D;
+  for (int e = tid; e < D * D; e += 256) A[(e / D) * LD + e % D] = src[e];
+  if (tid < D) s_lam[tid] = lam_in[static_cast<size_t>(mat) * D + tid];
   __syncthreads();
   if (tid < D) {
     const double lam = s_lam[tid];
@@ -901,8 +978,6 @@ kvq_status check_shape(const kvq_calib_shape* s) {
 
 bool dtype_ok(int32_t t) { return t == KVQ_F32 || t == KVQ_BF16; }
 
-size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
-
 CalibPlan plan_calib(const kvq_calib_shape* s) {
   CalibPlan p;
   const int d = s->head_dim, hkv = s->n_kv_heads, n = s->n_tokens;
@@ -922,8 +997,16 @@ CalibPlan plan_calib(const kvq_calib_shape* s) {
                 align256(static_cast<size_t>(hkv) * kCalibModalities * d * sizeof(double)) +
                 align256((static_cast<size_t>(n) + 4 + 3 * (static_cast<size_t>(n) / 1024 + 1)) * sizeof(int32_t)) +
                 align256(static_cast<size_t>(splits) * hkv * kCalibModalities * d * d * sizeof(double));
-  p.eig_bytes = static_cast<size_t>(3) * hkv * kJacobiSweeps * (d - 1) * (d / 2) * 2 * sizeof(double);
+  p.eig_bytes = eig_layout(3 * hkv, d).total;
   return p;
+}
+
+template <int D>
+void launch_eigenbasis(int count, const double* cov, double2* log, int* rounds, double* lam, double* vt, float* rot,
+                       double* evals, hipStream_t st) {
+  hipLaunchKernelGGL(calib_jacobi_kernel<D>, dim3(count), dim3(jacobi_threads<D>()), 0, st, cov, log, rounds, lam);
+  hipLaunchKernelGGL(calib_jacobi_replay_kernel<D>, dim3(count * (D / kReplayCols)), dim3(64), 0, st, log, rounds, vt);
+  hipLaunchKernelGGL(calib_jacobi_finalize_kernel<D>, dim3(count), dim3(256), 0, st, vt, lam, rot, evals);
 }
 
 template <int D>
@@ -981,8 +1064,8 @@ size_t kvq_calib_workspace_bytes(const kvq_calib_shape* shape) {
 
 size_t kvq_calib_eigenbasis_workspace_bytes(int32_t count, int32_t head_dim) {
   if (count < 0 || (head_dim != 64 && head_dim != 128)) return 0;
-  // the rotation log: (c, s) per (sweep, round, pair)
-  return static_cast<size_t>(count) * kJacobiSweeps * (head_dim - 1) * (head_dim / 2) * 2 * sizeof(double);
+  // the rotation log, (c, s) per (sweep, round, pair), and V^T per matrix
+  return eig_layout(count, head_dim).total;
 }
 
 kvq_status kvq_calib_contribution(const kvq_calib_shape* shape, const void* k, int32_t k_dtype, const void* q,
@@ -1064,14 +1147,16 @@ kvq_status kvq_calib_eigenbasis(int32_t count, int32_t head_dim, const double* c
   if (count == 0) return KVQ_OK;
   if (!cov || !rot || !eigenvalues) return KVQ_ERR_INVALID;
   if (!workspace || workspace_bytes < kvq_calib_eigenbasis_workspace_bytes(count, head_dim)) return KVQ_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return KVQ_ERR_INVALID;   // (c, s) pairs: 16-byte loads
   (void)hipGetLastError();
-  double* work = static_cast<double*>(workspace);
-  if (head_dim == 128)
-    hipLaunchKernelGGL(calib_jacobi_kernel<128>, dim3(count), dim3(jacobi_threads<128>()), 0, stream, cov, rot,
-                       eigenvalues, work);
-  else
-    hipLaunchKernelGGL(calib_jacobi_kernel<64>, dim3(count), dim3(jacobi_threads<64>()), 0, stream, cov, rot,
-                       eigenvalues, work);
+  const EigLayout L = eig_layout(count, head_dim);
+  char* w = static_cast<char*>(workspace);
+  double2* log = reinterpret_cast<double2*>(w + L.log);
+  int* rounds = reinterpret_cast<int*>(w + L.rounds);
+  double* lam = reinterpret_cast<double*>(w + L.lam);
+  double* vt = reinterpret_cast<double*>(w + L.vt);
+  if (head_dim == 128) launch_eigenbasis<128>(count, cov, log, rounds, lam, vt, rot, eigenvalues, stream);
+  else launch_eigenbasis<64>(count, cov, log, rounds, lam, vt, rot, eigenvalues, stream);
   return hipGetLastError() == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH;
 }
 

@@ -87,14 +87,18 @@ kvq_status kvq_calib_covariance(const kvq_calib_shape* shape, const void* v, int
 /*
  * kvq_calib_eigenbasis - eigenbasis of `count` symmetric d x d matrices
  * (Sec. 2 Method, value bullet: a modality-specific eigenbasis), by cyclic
- * Jacobi rotations in fp64 (one workgroup per matrix; at most 50 sweeps).
+ * Jacobi rotations in fp64 (one workgroup per matrix rotates it, at most 50
+ * sweeps, logging each round's rotations in the workspace; then d / 8
+ * workgroups per matrix accumulate the eigenvectors from the log, one block
+ * of columns each; three launches on `stream`).
  * cov: device [count][d][d] fp64, symmetric (only entries i <= j are read);
  * rot: device [count][d][d] fp32 output, rot[i][j] = component i of
  * eigenvector j (the kvq_params.rot layout when count = 3 * Hkv and cov
  * comes from kvq_calib_covariance); eigenvalues: device [count][d] fp64
- * output, decreasing.  A zero matrix gives the identity.
- * Errors: KVQ_ERR_INVALID (count < 0, null pointer), KVQ_ERR_UNSUPPORTED (d),
- * KVQ_ERR_WORKSPACE, KVQ_ERR_LAUNCH.
+ * output, decreasing.  A zero matrix gives the identity.  workspace: device,
+ * 16-byte aligned, kvq_calib_eigenbasis_workspace_bytes(count, d) bytes.
+ * Errors: KVQ_ERR_INVALID (count < 0, null pointer, workspace not 16-byte
+ * aligned), KVQ_ERR_UNSUPPORTED (d), KVQ_ERR_WORKSPACE, KVQ_ERR_LAUNCH.
  */
 kvq_status kvq_calib_eigenbasis(int32_t count, int32_t head_dim, const double* cov, float* rot,
                                 double* eigenvalues, void* workspace, size_t workspace_bytes,

@@ -244,7 +244,9 @@ def test_calibration_rejects_bad_arguments_without_launching():
         return L.KvqCalibShape(*[f[name] for name, _ in L.KvqCalibShape._fields_])
     good = shape()
     need = lib.kvq_calib_workspace_bytes(ctypes.byref(good))
-    eig_need = 6 * 50 * 127 * 64 * 16         # the Jacobi rotation log: (c, s) per (sweep, round, pair)
+    # the Jacobi rotation log, (c, s) per (sweep, round, pair); then, each region 256-byte aligned, the
+    # round counts, the eigenvalues and V^T of the 6 matrices
+    eig_need = 6 * 50 * 127 * 64 * 16 + 256 + 6 * 128 * 8 + 6 * 128 * 128 * 8
     assert need >= lib.kvq_calib_eigenbasis_workspace_bytes(6, 128) == eig_need
     assert lib.kvq_calib_workspace_bytes(ctypes.byref(shape(head_dim=96))) == 0
     assert lib.kvq_calib_eigenbasis_workspace_bytes(-1, 128) == 0
@@ -270,10 +272,11 @@ def test_calibration_rejects_bad_arguments_without_launching():
     assert cov(m=None) == L.KVQ_ERR_INVALID and cov(c=None) == L.KVQ_ERR_INVALID and cov(s=None) == L.KVQ_ERR_INVALID
     assert cov(nbytes=1) == L.KVQ_ERR_WORKSPACE
     assert cov(v=V(24)) == L.KVQ_ERR_INVALID                                      # v read in 16-byte pieces
-    eig = lambda count=6, d=128, c=V(8), r=V(8), e=V(8), ws=V(8), nbytes=need: lib.kvq_calib_eigenbasis(
+    eig = lambda count=6, d=128, c=V(8), r=V(8), e=V(8), ws=V(16), nbytes=need: lib.kvq_calib_eigenbasis(
         count, d, c, r, e, ws, nbytes, None)
     assert eig(count=-1) == L.KVQ_ERR_INVALID
     assert eig(d=32) == L.KVQ_ERR_UNSUPPORTED
     assert eig(r=None) == L.KVQ_ERR_INVALID
     assert eig(nbytes=eig_need - 1) == L.KVQ_ERR_WORKSPACE
+    assert eig(ws=V(24)) == L.KVQ_ERR_INVALID                                     # (c, s) read in 16-byte pieces
     assert eig(count=0, c=None, r=None, e=None) == L.KVQ_OK                       # nothing to do
