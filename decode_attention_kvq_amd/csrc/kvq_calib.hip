@@ -838,30 +838,40 @@ __global__ __launch_bounds__(jacobi_threads<D>()) void calib_jacobi_kernel(const
 }
 
 // Phase 2: V^T <- J^T V^T from the identity, on columns [cb W, (cb + 1) W)
-// of V^T (W = kReplayCols), one wavefront: lane k applies pair k of every
-// round (with two lanes per pair at d = 64, each on half the columns); a
-// pair that was left alone (s = 0, c = 1) leaves its rows as they are.  The
-// log is staged kReplayChunk rounds at a time through LDS, the next chunk's
-// loads in flight while the current one is applied.
+// of V^T (W = kReplayCols) per workgroup.  The columns do not interact, so
+// each of the replay_waves wavefronts takes W / replay_waves of them alone:
+// lane k applies pair k of every round (two lanes per pair at d = 64, each
+// on half the wavefront's columns), with no barrier between rounds; a pair
+// that was left alone (s = 0, c = 1) leaves its rows as they are.  The log
+// is staged kReplayChunk rounds at a time through LDS by the whole
+// workgroup, the next chunk's loads in flight while the current one is
+// applied.
 template <int D>
-__global__ __launch_bounds__(64) void calib_jacobi_replay_kernel(const double2* logs, const int* rounds_in,
-                                                                 double* vt) {
+constexpr int replay_waves() { return D == 128 ? 8 : 4; }   // one column per lane
+
+template <int D>
+__global__ __launch_bounds__(64 * replay_waves<D>()) void calib_jacobi_replay_kernel(const double2* logs,
+                                                                                     const int* rounds_in, double* vt) {
   constexpr int NP = D / 2;
   constexpr int W = kReplayCols;
+  constexpr int NT = 64 * replay_waves<D>();
   constexpr int CB = D / W;              // column blocks per matrix
+  constexpr int WW = W / replay_waves<D>();   // columns per wavefront
   constexpr int LPP = 64 / NP;           // lanes per pair
-  constexpr int CPL = W / LPP;           // columns per lane
+  constexpr int CPL = WW / LPP;          // columns per lane
   constexpr int LDB = W + 1;             // row stride in doubles
   constexpr int CH = kReplayChunk;
-  constexpr int PRE = CH * NP / 64;      // log entries per lane per chunk
-  static_assert(LPP * NP == 64 && CPL * LPP == W && PRE * 64 == CH * NP, "replay shape");
+  constexpr int PRE = CH * NP / NT;      // log entries per thread per chunk
+  static_assert(LPP * NP == 64 && CPL * LPP == WW && WW * replay_waves<D>() == W && PRE * NT == CH * NP,
+                "replay shape");
   __shared__ double V[D * LDB];
   __shared__ double2 s_cs[2][CH * NP];
   const int mat = blockIdx.x / CB, cb = blockIdx.x % CB;
-  const int lane = threadIdx.x, k = lane % NP, c0 = (lane / NP) * CPL;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int k = lane % NP, c0 = wave * WW + (lane / NP) * CPL;
   const double2* log = logs + static_cast<size_t>(mat) * kJacobiSweeps * (D - 1) * NP;
   const int rounds = rounds_in[mat];
-  for (int e = lane; e < D * W; e += 64) {
+  for (int e = tid; e < D * W; e += NT) {
     const int i = e / W, j = e % W;
     V[i * LDB + j] = (i == cb * W + j) ? 1.0 : 0.0;
   }
@@ -870,14 +880,14 @@ __global__ __launch_bounds__(64) void calib_jacobi_replay_kernel(const double2* 
   auto fetch = [&](int ch) {
 #pragma unroll
     for (int u = 0; u < PRE; ++u) {
-      const int idx = u * 64 + lane;                   // (round in chunk) * NP + pair
+      const int idx = u * NT + tid;                    // (round in chunk) * NP + pair
       const bool in = ch * CH + idx / NP < rounds;
       pre[u] = in ? log[static_cast<size_t>(ch) * CH * NP + idx] : double2{1.0, 0.0};
     }
   };
   auto stash = [&](int buf) {
 #pragma unroll
-    for (int u = 0; u < PRE; ++u) s_cs[buf][u * 64 + lane] = pre[u];
+    for (int u = 0; u < PRE; ++u) s_cs[buf][u * NT + tid] = pre[u];
   };
   if (nch > 0) {
     fetch(0);
@@ -885,15 +895,19 @@ __global__ __launch_bounds__(64) void calib_jacobi_replay_kernel(const double2* 
   }
   if (nch > 1) fetch(1);
   lds_barrier();
-  int r = 0;   // round within the sweep: the pair ordering
+  // pair k of round r is (x, y) = (k == 0 ? 0 : 1 + (k - 1 + r) mod (D - 1),
+  // 1 + (D - 2 - k + r) mod (D - 1)) (jacobi_pair), kept as two counters
+  int xm = (k + D - 2) % (D - 1), ym = (D - 2 - k) % (D - 1);
   for (int ch = 0; ch < nch; ++ch) {
     const int buf = ch & 1;
     const int nr = min(CH, rounds - ch * CH);
+    double2 cs = s_cs[buf][k];
     for (int i = 0; i < nr; ++i) {
-      const double2 cs = s_cs[buf][i * NP + k];
+      // the next round's (c, s), read ahead (the last one re-reads itself)
+      const double2 cs_next = s_cs[buf][min(i + 1, CH - 1) * NP + k];
+      const int x = k == 0 ? 0 : 1 + xm, y = 1 + ym;
+      const int p = min(x, y), q = max(x, y);
       if (cs.y != 0.0) {
-        int p, q;
-        jacobi_pair<D>(r, k, p, q);
         double wx[CPL], wy[CPL];
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
@@ -906,15 +920,21 @@ __global__ __launch_bounds__(64) void calib_jacobi_replay_kernel(const double2* 
           V[q * LDB + c0 + j] = cs.y * wx[j] + cs.x * wy[j];
         }
       }
-      r = r == D - 2 ? 0 : r + 1;
-      lds_barrier();   // the round's rows are written before the next reads them
+      xm = xm == D - 2 ? 0 : xm + 1;
+      ym = ym == D - 2 ? 0 : ym + 1;
+      // the round's rows are written before the wavefront's next reads
+      // (only this wavefront touches its columns)
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      cs = cs_next;
     }
-    if (ch + 1 < nch) stash(buf ^ 1);   // chunk ch + 1 (its buffer held chunk ch - 1)
+    // chunk ch + 1 into the buffer of chunk ch - 1, which every wavefront
+    // finished before the previous barrier
+    if (ch + 1 < nch) stash(buf ^ 1);
     if (ch + 2 < nch) fetch(ch + 2);
     lds_barrier();
   }
   double* out = vt + static_cast<size_t>(mat) * D * D + cb * W;
-  for (int e = lane; e < D * W; e += 64) {
+  for (int e = tid; e < D * W; e += NT) {
     const int i = e / W, j = e % W;
     out[static_cast<size_t>(i) * D + j] = V[i * LDB + j];
   }
@@ -1005,7 +1025,8 @@ template <int D>
 void launch_eigenbasis(int count, const double* cov, double2* log, int* rounds, double* lam, double* vt, float* rot,
                        double* evals, hipStream_t st) {
   hipLaunchKernelGGL(calib_jacobi_kernel<D>, dim3(count), dim3(jacobi_threads<D>()), 0, st, cov, log, rounds, lam);
-  hipLaunchKernelGGL(calib_jacobi_replay_kernel<D>, dim3(count * (D / kReplayCols)), dim3(64), 0, st, log, rounds, vt);
+  hipLaunchKernelGGL(calib_jacobi_replay_kernel<D>, dim3(count * (D / kReplayCols)), dim3(64 * replay_waves<D>()), 0, st,
+                     log, rounds, vt);
   hipLaunchKernelGGL(calib_jacobi_finalize_kernel<D>, dim3(count), dim3(256), 0, st, vt, lam, rot, evals);
 }
 
