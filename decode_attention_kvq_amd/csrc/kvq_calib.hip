@@ -649,7 +649,7 @@ __global__ __launch_bounds__(256) void calib_cov_merge_kernel(CovArgs a) {
 // kReplayCols columns of V^T (one lane per pair).  A last pass orders the
 // eigenvectors by eigenvalue and fixes their signs.
 template <int D>
-constexpr int jacobi_threads() { return D == 128 ? 512 : 256; }
+constexpr int jacobi_threads() { return D == 128 ? 1024 : 256; }
 constexpr int kReplayCols = 8;     // columns of V^T per replay workgroup
 constexpr int kReplayChunk = 16;   // rounds of the log staged in LDS at a time
 
