@@ -31,13 +31,36 @@ __global__ __launch_bounds__(kAppendThreads, WIDE ? 4 : 1) void append_kernel(Ap
     }
     return;   // no ticket: only the append's workgroups count
   }
-  // The value workgroups (the longer ones: a group's rotation R_m^T v) take
-  // the first grid columns, the key workgroups the rest, so that a chunk's
-  // value work is dispatched first and the short key work fills in behind it.
-  const int half = a.append_x / 2, x = blockIdx.x;
-  const int bx = x < half ? 2 * x + 1 : 2 * (x - half);
-  app::append_group<D, BF16, BITS>(a, sm, s_last, bx, blockIdx.y, blockIdx.z,
-                                   a.append_x * static_cast<int>(gridDim.y));
+  // Dispatch order (workgroups start in the order of their linear index):
+  // the value workgroups (the longer ones: a group's rotation R_m^T v) of
+  // every group but the last, over all (KV head, session) pairs, then their
+  // key workgroups, then both workgroups of the last group, which is empty
+  // when the chunk starts on a group boundary (the grid covers any start).
+  // A chunk with more workgroups than slots then leaves only those empty
+  // ones for a second round.
+  const int P = static_cast<int>(gridDim.y * gridDim.z);   // (KV head, session) pairs
+  const int G = a.append_x / 2;                              // groups the append may touch
+  const int i = static_cast<int>(blockIdx.x) + a.append_x * static_cast<int>(blockIdx.z * gridDim.y + blockIdx.y);
+  const int nmain = (G - 1) * P;
+  int grp, pair;
+  bool val;
+  if (i < nmain) {
+    val = true;
+    grp = i / P;
+    pair = i % P;
+  } else if (i < 2 * nmain) {
+    val = false;
+    grp = (i - nmain) / P;
+    pair = (i - nmain) % P;
+  } else {
+    const int j = i - 2 * nmain;
+    val = j < P;
+    grp = G - 1;
+    pair = j % P;
+  }
+  const int bx = 2 * grp + (val ? 1 : 0);
+  app::append_group<D, BF16, BITS>(a, sm, s_last, bx, pair % static_cast<int>(gridDim.y),
+                                   pair / static_cast<int>(gridDim.y), a.append_x * static_cast<int>(gridDim.y));
 }
 
 template <int D, bool BF16>
