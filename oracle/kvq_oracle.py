@@ -36,9 +36,10 @@ Readings where the pages are silent (each repeated in the design notes):
     stored norm is fp16(n); reconstruction is R_m (N / sqrt(d)) c[code].
   * Query head i uses KV head floor(i / G); scores use scale 1/sqrt(d) unless
     given; an empty context attends to nothing and yields zeros.
-  * Sparse page sets (a retained-page list or mask, as in the survey's paging
-    follow-on): positions outside the retained set are left out before the
-    softmax, exactly as if they had never been cached.
+  * Sparse page sets (a retained-page list or mask; OmniTide page, Sec. 6
+    OmniPage: an emptied page is skipped whole): positions outside the
+    retained set are left out before the softmax, exactly as if they had
+    never been cached.
   * TurboQuant baseline (Sec. 2 Method, TurboQuant bullet; Sec. 1 Problem
     bullet: one fixed scale per token rather than local ranges): a key is
     coded like a value, with the randomized Hadamard as its rotation:
