@@ -722,7 +722,7 @@ __global__ __launch_bounds__(jacobi_threads<D>()) void calib_jacobi_kernel(const
   __shared__ double A[D * LD];
   __shared__ double2 s_cs[NP];             // (c, s) of each pair
   __shared__ double s_t[NP];
-  __shared__ int2 s_pq[NP];                // (p, q) of each pair
+  __shared__ int s_pq[NP];                 // p | q << 16 of each pair
   __shared__ int s_changed;
   __shared__ int s_rot[2];                 // the round rotates some pair
   __shared__ double s_sq[NT];
@@ -770,7 +770,7 @@ __global__ __launch_bounds__(jacobi_threads<D>()) void calib_jacobi_kernel(const
           s_changed = 1;
         }
         const double c = 1.0 / sqrt(1.0 + t * t);
-        s_pq[k] = int2{p, q};
+        s_pq[k] = p | (q << 16);
         s_cs[k] = double2{c, t * c};
         s_t[k] = t;
         log[(static_cast<size_t>(sweep) * (D - 1) + r) * NP + k] = double2{c, t * c};
@@ -783,20 +783,24 @@ __global__ __launch_bounds__(jacobi_threads<D>()) void calib_jacobi_kernel(const
       lds_barrier();
       // a round that rotates nothing leaves every other entry as it is
       if (!s_rot[rc++ & 1]) continue;
-      // this round's tasks touch disjoint entries: all loads, then all stores
+      // this round's tasks touch disjoint entries: all loads (their
+      // addresses kept), then all stores
       double blk[NAT][4];
+      int adr[NAT][4];
 #pragma unroll
       for (int u = 0; u < NAT; ++u) {
         const int e = tid + u * NT;
         if (e < NTASK) {
           int ki, kj;
           block_task<NP>(e, ki, kj);
-          const int2 pqi = s_pq[ki], pqj = s_pq[kj];
-          const int pi = pqi.x, qi = pqi.y, pj = pqj.x, qj = pqj.y;
-          blk[u][0] = A[upper<LD>(pi, pj)];
-          blk[u][1] = A[upper<LD>(pi, qj)];
-          blk[u][2] = A[upper<LD>(qi, pj)];
-          blk[u][3] = A[upper<LD>(qi, qj)];
+          const int pqi = s_pq[ki], pqj = s_pq[kj];
+          const int pi = pqi & 0xFFFF, qi = pqi >> 16, pj = pqj & 0xFFFF, qj = pqj >> 16;
+          adr[u][0] = upper<LD>(pi, pj);
+          adr[u][1] = upper<LD>(pi, qj);
+          adr[u][2] = upper<LD>(qi, pj);
+          adr[u][3] = upper<LD>(qi, qj);
+#pragma unroll
+          for (int x = 0; x < 4; ++x) blk[u][x] = A[adr[u][x]];
         }
       }
 #pragma unroll
@@ -805,15 +809,14 @@ __global__ __launch_bounds__(jacobi_threads<D>()) void calib_jacobi_kernel(const
         if (e >= NTASK) continue;
         int ki, kj;
         block_task<NP>(e, ki, kj);
-        const int2 pqi = s_pq[ki], pqj = s_pq[kj];
-        const int pi = pqi.x, qi = pqi.y, pj = pqj.x, qj = pqj.y;
         const double a_pp = blk[u][0], a_pq = blk[u][1], a_qp = blk[u][2], a_qq = blk[u][3];
         if (ki == kj) {
-          // the rotated pair itself: exact zero off the diagonal
+          // the rotated pair itself (entries (p, p), (p, q), (q, q)): exact
+          // zero off the diagonal
           const double t = s_t[ki];
-          A[pi * LD + pi] = a_pp - t * a_pq;
-          A[qi * LD + qi] = a_qq + t * a_pq;
-          A[pi * LD + qi] = 0.0;
+          A[adr[u][0]] = a_pp - t * a_pq;
+          A[adr[u][3]] = a_qq + t * a_pq;
+          A[adr[u][1]] = 0.0;
           continue;
         }
         const double2 csi = s_cs[ki], csj = s_cs[kj];
@@ -823,10 +826,10 @@ __global__ __launch_bounds__(jacobi_threads<D>()) void calib_jacobi_kernel(const
         const double r_qp = si * a_pp + ci * a_qp, r_qq = si * a_pq + ci * a_qq;
         const double n_pp = cj * r_pp - sj * r_pq, n_pq = sj * r_pp + cj * r_pq;
         const double n_qp = cj * r_qp - sj * r_qq, n_qq = sj * r_qp + cj * r_qq;
-        A[upper<LD>(pi, pj)] = n_pp;
-        A[upper<LD>(pi, qj)] = n_pq;
-        A[upper<LD>(qi, pj)] = n_qp;
-        A[upper<LD>(qi, qj)] = n_qq;
+        A[adr[u][0]] = n_pp;
+        A[adr[u][1]] = n_pq;
+        A[adr[u][2]] = n_qp;
+        A[adr[u][3]] = n_qq;
       }
       lds_barrier();
     }
