@@ -41,7 +41,7 @@ L80K = 81920
 # (FETCH_SIZE x 1.9998, WRITE_SIZE x 1.0); see profiles/decode_80k_hbm_bytes.md.
 # Valid only for the decode source the counters were taken on (SHA-256 of
 # kvq_decode.hip); otherwise `traffic` is reported as null.
-DECODE_TRAFFIC = {"kvq_decode_sha256": "ca5e7bf75dd3b29ee9e7bb6cb0474b3025fdaa7c5921d02476fc649ca11fc497",
+DECODE_TRAFFIC = {"kvq_decode_sha256": "d1b0765908da56527c072c3d9237c7f75f1e9a006eb40feabb38db8ded1b3fcd",
                   "bytes": 32901595}
 
 

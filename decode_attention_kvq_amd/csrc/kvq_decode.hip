@@ -1971,6 +1971,193 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
   }
 }
 
+// Merge for few partials per query head (every session's partitions plus
+// the step's slot at most kMergeHeadsSplits): workgroup (session, KV head,
+// row block) takes every query head of the group, so the rows of the three
+// inverse value rotations are loaded once for the G heads (the per-head
+// merge loads them once per head, which dominates when each head has only a
+// few partials to reduce).  Every load (rotation rows, headers, accumulator
+// blocks) is issued before the first reduction; per head the partials are
+// rescaled to the head's max and summed per modality in partition order,
+// then out = sum_m R_m A_m / l for the block's rows.  The workgroups of one
+// key sit on the XCD key mod 8, as in the per-head merge.
+constexpr int kMergeHeadsSplits = 8;
+
+template <int D, bool ASYM, bool STEP = false>
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_heads_kernel(DecodeArgs a) {
+  constexpr int PS = kPartialHeader + kModalities * D;
+  constexpr int F4 = D / 4;                        // float4 per accumulator block
+  constexpr int RB = MergeShape<D>::RB;
+  constexpr int RR = MergeShape<D>::RR;
+  constexpr int QT = kMergeThreads / RR;           // threads per output row
+  constexpr int JQ = D / QT;                       // columns of R per thread
+  constexpr int SM = kMergeHeadsSplits;
+  constexpr int NIT = kMaxGroupHeads * kModalities * F4;   // (head, modality, float4) items at most
+  constexpr int NI = (NIT + kMergeThreads - 1) / kMergeThreads;
+  static_assert(JQ % 4 == 0 && QT == 16, "one output row per 16-lane row");
+  static_assert(!(STEP && ASYM), "the fused step takes a symmetric codebook");
+  __shared__ float s_hm[kMaxGroupHeads][SM];
+  __shared__ float s_hl[kMaxGroupHeads][SM];
+  __shared__ float s_hs[kMaxGroupHeads][SM][kModalities];
+  __shared__ uint8_t s_mk[kMaxGroupHeads][SM];
+  __shared__ float s_e[kMaxGroupHeads][SM];
+  __shared__ float s_l[kMaxGroupHeads];
+  __shared__ float s_sm[kMaxGroupHeads][kModalities];
+  __shared__ float s_A[kMaxGroupHeads][kModalities][D];
+
+  const int x = blockIdx.x % kXcds, y = blockIdx.x / kXcds;
+  const int keys = a.batch * a.hkv;
+  const int key = (y / RB) * kXcds + x;            // b * Hkv + h
+  const int rb = y % RB;
+  if (key >= keys) return;
+  const int h = key % a.hkv, b = key / a.hkv, G = a.group;
+  const int tid = threadIdx.x;
+  int slot0, S;
+  if (a.ntab > 0) {
+    slot0 = a.tab_start[b];
+    S = a.tab_start[b + 1] - slot0;
+  } else {
+    slot0 = b * (a.splits + a.step);
+    S = a.splits + a.step;
+  }
+  auto head_partials = [&](int gq) {
+    return a.partials + (static_cast<size_t>(h * G + gq) * a.pstride + slot0) * PS;
+  };
+
+  // Rotation rows: row rb RR + tid / QT, columns [q JQ, (q+1) JQ) of all three R_m.
+  const int rloc = tid / QT, q = tid % QT;
+  const int row = rb * RR + rloc;
+  float4 R[kModalities][JQ / 4];
+#pragma unroll
+  for (int m = 0; m < kModalities; ++m) {
+    const float4* Rp = reinterpret_cast<const float4*>(
+        a.rot + ((static_cast<size_t>(h) * kModalities + m) * D + row) * D + q * JQ);
+#pragma unroll
+    for (int j4 = 0; j4 < JQ / 4; ++j4) R[m][j4] = Rp[j4];
+  }
+  // Accumulator blocks: item it = (head, modality, float4) of every split
+  // (indices past the last split re-read it: branch-free, all in flight).
+  const int nit = G * kModalities * F4;
+  float4 blk[NI][SM];
+#pragma unroll
+  for (int u = 0; u < NI; ++u) {
+    if (u * kMergeThreads >= nit) break;           // (uniform) no item of this round
+    const int it = min(tid + u * kMergeThreads, nit - 1);
+    const int gq = it / (kModalities * F4), m = (it / F4) % kModalities, f = it % F4;
+    const float* P = head_partials(gq);
+#pragma unroll
+    for (int sp = 0; sp < SM; ++sp)
+      blk[u][sp] = reinterpret_cast<const float4*>(P + static_cast<size_t>(min(sp, S - 1)) * PS + kPartialHeader +
+                                                   m * D)[f];
+  }
+  // Headers of (head, split) = (t / SM, t % SM).
+  for (int t = tid; t < G * SM; t += kMergeThreads) {
+    const int gq = t / SM, sp = t % SM;
+    float4 h0 = {-__builtin_inff(), 0.f, 0.f, 0.f}, h1 = {0.f, 0.f, 0.f, 0.f};
+    if (sp < S) {
+      const float4* hp = reinterpret_cast<const float4*>(head_partials(gq) + static_cast<size_t>(sp) * PS);
+      h0 = hp[0];
+      if constexpr (ASYM) h1 = hp[1];
+    }
+    s_hm[gq][sp] = h0.x;
+    s_hl[gq][sp] = h0.y;
+    s_mk[gq][sp] = static_cast<uint8_t>(h0.x == -__builtin_inff() ? 0 : __float_as_int(h0.z));
+    s_hs[gq][sp][0] = h1.x;
+    s_hs[gq][sp][1] = h1.y;
+    s_hs[gq][sp][2] = h1.z;
+  }
+  __syncthreads();
+  // Per head: its max, the splits' weights, l and (asymmetric codebook) the
+  // per-modality weight sums, in split order.
+  if (tid < G) {
+    const int gq = tid;
+    float M = -__builtin_inff();
+    for (int sp = 0; sp < S; ++sp) M = fmaxf(M, s_hm[gq][sp]);
+    float l = 0.f, sm[kModalities] = {0.f, 0.f, 0.f};
+    for (int sp = 0; sp < SM; ++sp) {
+      const float mv = s_hm[gq][sp];
+      const float e = (sp >= S || mv == -__builtin_inff()) ? 0.f : exp2f(mv - M);
+      s_e[gq][sp] = e;
+      l += e * s_hl[gq][sp];
+      if constexpr (ASYM) {
+        const int pm = s_mk[gq][sp];
+#pragma unroll
+        for (int m = 0; m < kModalities; ++m) sm[m] += (pm >> m) & 1 ? e * s_hs[gq][sp][m] : 0.f;
+      }
+    }
+    s_l[gq] = l;
+#pragma unroll
+    for (int m = 0; m < kModalities; ++m) s_sm[gq][m] = sm[m];
+  }
+  __syncthreads();
+  // Weighted sums of the accumulator blocks, in split order (absent
+  // modalities are selected away, never multiplied: their blocks hold stale
+  // data).
+#pragma unroll
+  for (int u = 0; u < NI; ++u) {
+    const int it = tid + u * kMergeThreads;
+    if (it < nit) {
+      const int gq = it / (kModalities * F4), m = (it / F4) % kModalities, f = it % F4;
+      float4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int sp = 0; sp < SM; ++sp) {
+        const bool p = sp < S && ((s_mk[gq][sp] >> m) & 1);
+        const float e = s_e[gq][sp];
+        acc.x += p ? e * blk[u][sp].x : 0.f;
+        acc.y += p ? e * blk[u][sp].y : 0.f;
+        acc.z += p ? e * blk[u][sp].z : 0.f;
+        acc.w += p ? e * blk[u][sp].w : 0.f;
+      }
+      *reinterpret_cast<float4*>(&s_A[gq][m][4 * f]) = acc;
+    }
+  }
+  __syncthreads();
+  if constexpr (STEP) {
+    // one workgroup per session advances its length (nothing else in this
+    // launch reads it)
+    if (tid == 0 && rb == 0 && h == 0) a.step_len[b] += 1;
+  }
+  // out[row] = (chalf sum_m R_m A_m + cmid sum_m S_m rowsum(R_m)) / (sqrt(d) l), per head
+  float rsum[kModalities] = {0.f, 0.f, 0.f};
+  if constexpr (ASYM) {
+#pragma unroll
+    for (int m = 0; m < kModalities; ++m) {
+      float rm = 0.f;
+#pragma unroll
+      for (int j4 = 0; j4 < JQ / 4; ++j4) rm += R[m][j4].x + R[m][j4].y + R[m][j4].z + R[m][j4].w;
+      rsum[m] = row16_sum(rm);
+    }
+  }
+  for (int gq = 0; gq < G; ++gq) {
+    float acc = 0.f;
+#pragma unroll
+    for (int m = 0; m < kModalities; ++m) {
+      float am = 0.f;
+#pragma unroll
+      for (int j4 = 0; j4 < JQ / 4; ++j4) {
+        const float* A = &s_A[gq][m][q * JQ + 4 * j4];
+        const float4 r = R[m][j4];
+        am += r.x * A[0] + r.y * A[1] + r.z * A[2] + r.w * A[3];
+      }
+      acc += am;
+    }
+    acc = row16_sum(acc);
+    if (q == 0) {
+      float rs = 0.f;
+      if constexpr (ASYM)
+#pragma unroll
+        for (int m = 0; m < kModalities; ++m) rs += s_sm[gq][m] * rsum[m];
+      const float l = s_l[gq];
+      const float o = (l > 0.f) ? (a.chalf * acc + a.cmid * rs) * (a.value_scale / l) : 0.f;
+      const size_t head = static_cast<size_t>(b) * a.hq + h * G + gq;
+      if (a.out_bf16)
+        static_cast<uint16_t*>(a.out)[head * D + row] = f32_to_bf16_rne(o);
+      else
+        static_cast<float*>(a.out)[head * D + row] = o;
+    }
+  }
+}
+
 // Grid of a partition launch (see the plan in DecodeArgs).
 dim3 partition_grid(int batch, const DecodeArgs& a) {
   return a.ntab > 0 ? dim3(a.pstride, a.hkv, 1) : dim3(a.splits + a.step, a.hkv, batch);
@@ -2014,11 +2201,19 @@ void launch_partition_sw(int batch, const DecodeArgs& a, hipStream_t s) {
   else launch_partition_sw_bits<D, SLOTS, 2>(batch, a, s);
 }
 
-// Merge grid: per (session, KV head) key, group * RB workgroups, all on the
-// XCD key mod 8 (see decode_merge_kernel).
+// Merge grid: per (session, KV head) key, group * RB workgroups (RB with few
+// partials per head, decode_merge_heads_kernel), all on the XCD key mod 8
+// (see decode_merge_kernel).
 template <int D, bool ASYM, bool STEP>
 void launch_merge(int batch, const DecodeArgs& a, hipStream_t s) {
   const int keys = a.hkv * batch;
+  if (a.splits + a.step <= kMergeHeadsSplits) {
+    // few partials per head: one workgroup per (key, row block) for all heads
+    const int rows = ((keys + kXcds - 1) / kXcds) * MergeShape<D>::RB;
+    hipLaunchKernelGGL((decode_merge_heads_kernel<D, ASYM, STEP>), dim3(kXcds * rows), dim3(kMergeThreads), 0, s,
+                       a);
+    return;
+  }
   const int per_key = a.group * MergeShape<D>::RB;
   const int rows = ((keys + kXcds - 1) / kXcds) * per_key;
   hipLaunchKernelGGL((decode_merge_kernel<D, ASYM, STEP>), dim3(kXcds * rows), dim3(kMergeThreads), 0, s, a);

@@ -101,6 +101,40 @@ def test_append_and_decode_parity(cfg_id, kw):
     assert worst <= h.ATTN_TOL
 
 
+# An asymmetric codebook (c0 + c3 != 0): the decode then carries the
+# codebook's midpoint through the per-modality weight sums of the partials.
+ASYM_CODEBOOK = np.array([-1.2, -0.35, 0.55, 1.8], dtype=np.float32)
+ASYM_CASES = [
+    (0, dict(length=1500)),                          # a few partitions per head: the all-heads merge
+    (3, dict(batch=3, len_range=(200, 500))),         # a ragged batch, all-heads merge
+    (2, dict(length=20000)),                         # 64 partitions per head: the per-head merge
+    (3, dict(batch=3, len_range=(700, 2600))),        # a ragged batch, per-head merge
+    (1, dict(length=3001, n_q_heads=32)),            # 16 heads per KV head: the one-role partition kernel
+    (1, dict(length=1000, n_q_heads=32)),            # the same with few partitions: all-heads merge, 16 heads
+]
+
+
+@pytest.mark.parametrize("cfg_id,kw", ASYM_CASES, ids=[f"asym-{_case_id(c, kw)}-{i}" for i, (c, kw) in enumerate(ASYM_CASES)])
+def test_asymmetric_codebook_parity(cfg_id, kw):
+    import dataclasses
+    import decode_attention_kvq_amd as K
+    h = H()
+    w = dataclasses.replace(generate(cfg_id, **kw), codebook=ASYM_CODEBOOK.copy())
+    _say(f"asymmetric codebook cfg{cfg_id} {kw} lengths={w.lengths.tolist()}")
+    cfg, params, cache = h.build(w)
+    total, mism = h.check_codes(w, cfg, cache, range(w.cfg.batch))
+    _say(f"codes: {total} elements, {mism} boundary mismatches")
+    scale = h.default_scale(w)
+    q_rot = K.kvq_rotate_query(cfg, params, h.query_tensor(w))
+    out = K.kvq_decode_attention(cfg, cache, params, q_rot, scale).cpu().numpy()
+    ref = h.oracle_decode_over_gpu_codes(w, cfg, cache, O.as_f64(w.q, w.dtype), range(w.cfg.batch), scale)
+    worst = 0.0
+    for b in range(w.cfg.batch):
+        worst = max(worst, float(h.normwise_rel_err(out[b].astype(np.float64), ref[b]).max()))
+    _say(f"decode worst normwise rel err {worst:.3e}")
+    assert worst <= h.ATTN_TOL
+
+
 FUSED_CASES = [
     # (cfg_id, overrides, positions appended, first session, query dtype)
     (0, dict(length=700), 1, 0, None),
