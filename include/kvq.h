@@ -16,7 +16,11 @@
  *
  * Conventions shared by every entry point
  *   - All pointers named "device" are HIP device memory owned by the caller;
- *     the library allocates nothing and keeps no global state.
+ *     the library allocates nothing and keeps no global state, apart from
+ *     the static device array of kvq_decode_attention_noalloc (see there).
+ *   - Keys, values, queries and the value bases must be finite: a NaN or an
+ *     infinity gives unspecified codes and outputs (nothing on the device
+ *     checks for them).
  *   - Every call is asynchronous on the given stream (0 = null stream).  No
  *     call synchronises.
  *   - Arguments are validated on the host before anything is launched; a
