@@ -81,8 +81,9 @@ def test_decode_accuracy_does_not_depend_on_the_value_scale(cfg_id, kw, factor):
     assert err <= h.ATTN_TOL
 
 
-@pytest.mark.parametrize("cfg_id,kw", [(1, dict(length=3001)), (1, dict(length=2100, n_q_heads=32))],
-                         ids=["G8", "G16"])
+@pytest.mark.parametrize("cfg_id,kw", [(1, dict(length=3001)), (1, dict(length=2100, n_q_heads=32)),
+                                       (1, dict(length=1000))],
+                         ids=["G8", "G16", "G8-few-partials"])
 def test_bf16_output_is_the_fp32_output_rounded(cfg_id, kw):
     """out_dtype = bf16 writes the fp32 result rounded to nearest even, bit for
     bit; against the oracle it is then within the bar plus bf16's own
